@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the Bole tree-verify hot path on one MI355X.
+
+Workload: the hybrid layer stack. There are 64 sequences, each with one best-first
+draft tree of 32 nodes, and 8 linear-recurrence layers of 32 heads (d_k=128, d_v=64).
+q/k/v are bf16; the scalar gate and the committed state H0 are fp32.
+
+One step:
+  1. bole_tree_verify for layers 0..7, in order, as a forward pass would call them;
+  2. bole_commit_path for layers 0..7: each layer's accepted path goes into its H0 in
+     place.
+All inputs are resident in HBM before the timed region starts. The 8 layers hold
+1 GB, four times the 256 MB last-level cache, so every layer is read cold.
+
+The program prints one JSON line:
+  - value: draft nodes verified through the whole stack per second;
+  - roofline: for the dominant kernel, its algorithmic bytes per launch over its
+    average launch time (HIP events on the launch stream), against the 8 TB/s HBM peak;
+  - cpu_baseline: the fp64 CPU oracle timed on this host on whole steps of the same
+    workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "tree-verify draft nodes/s + achieved HBM GB/s (B=64, 32 heads, N=32)"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time for the oracle baseline (whole steps)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 512 MiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def verify_bytes(wl, s_f=2):
+    """Algorithmic HBM bytes of one verify launch (one layer): H0 read once, every
+    node's q, k, v, gate read once, out written once, plus parent and offsets."""
+    B, H, dk, dv, T = wl.batch, wl.heads, wl.d_k, wl.d_v, wl.total_nodes
+    s_g = 4 * (dk if wl.vector_gate else 1)
+    return (4 * B * H * dk * dv + T * H * ((2 * dk + dv) * s_f + s_g) + 4 * T * H * dv
+            + 4 * T + 4 * (B + 1))
+
+
+def commit_bytes(wl, s_f=2):
+    """Algorithmic HBM bytes of one commit launch: for each sequence with an accepted
+    path (L > 0), H0 read and written once and the path's k, v, gate read once."""
+    H, dk, dv = wl.heads, wl.d_k, wl.d_v
+    s_g = 4 * (dk if wl.vector_gate else 1)
+    tot = 0
+    for b in range(wl.batch):
+        L = int(wl.accepted_len[b])
+        if L > 0:
+            tot += H * (8 * dk * dv + L * ((dk + dv) * s_f + s_g))
+    return tot + 4 * wl.batch * (wl.max_path + 1) + 4 * wl.total_nodes + 4 * (wl.batch + 1)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(verify and commit shard by sequence or head with no communication); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from tree_speculative_decoding_02_amd import bole
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.make_config(5)
+    L = len(wl.layers)
+    print(f"[bench] workload {wl.name}: B={wl.batch} layers={L} H={wl.heads} d_k={wl.d_k} "
+          f"d_v={wl.d_v} T={wl.total_nodes}", file=sys.stderr, flush=True)
+    g = lambda t: t.to(dev)
+    parent = torch.from_numpy(wl.parent).to(dev)
+    offs = torch.from_numpy(wl.node_offsets).to(dev)
+    acc_idx = torch.from_numpy(wl.accepted_idx).to(dev)
+    acc_len = torch.from_numpy(wl.accepted_len).to(dev)
+    layers = [dict(H0=g(l.H0), q=g(l.q), k=g(l.k), v=g(l.v), gate=g(l.gate)) for l in wl.layers]
+    outs = [torch.empty((wl.total_nodes, wl.heads, wl.d_v), dtype=torch.float32, device=dev)
+            for _ in range(L)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(record=None):
+        for l in range(L):
+            x = layers[l]
+            if record is not None:
+                record["v"][l][0].record(stream)
+            bole.bole_tree_verify(x["H0"], x["q"], x["k"], x["v"], x["gate"], parent, offs,
+                                  out=outs[l], stream=stream)
+            if record is not None:
+                record["v"][l][1].record(stream)
+        for l in range(L):
+            x = layers[l]
+            if record is not None:
+                record["c"][l][0].record(stream)
+            bole.bole_commit_path(x["H0"], x["k"], x["v"], x["gate"], parent, offs, acc_idx,
+                                  acc_len, stream=stream)
+            if record is not None:
+                record["c"][l][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    records = [{"v": [(ev(), ev()) for _ in range(L)], "c": [(ev(), ev()) for _ in range(L)]}
+               for _ in range(args.steps)]
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(records[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = t_start.elapsed_time(t_end)
+    v_ms = [r["v"][l][0].elapsed_time(r["v"][l][1]) for r in records for l in range(L)]
+    c_ms = [r["c"][l][0].elapsed_time(r["c"][l][1]) for r in records for l in range(L)]
+    ms_per_step = gpu_ms / args.steps
+    nodes = wl.total_nodes
+    vb, cb = verify_bytes(wl), commit_bytes(wl)
+    v_us, c_us = 1e3 * float(np.mean(v_ms)), 1e3 * float(np.mean(c_ms))
+    v_gbs, c_gbs = vb / (v_us * 1e3), cb / (c_us * 1e3)
+    kernels = {
+        "verify": {"avg_us": v_us, "median_us": 1e3 * float(np.median(v_ms)),
+                   "bytes_per_launch": vb, "GB_s": v_gbs, "frac_hbm_peak": v_gbs / HBM_PEAK_GBS,
+                   "launches_per_step": L, "nodes_per_s_per_layer": nodes / (v_us * 1e-6)},
+        "commit": {"avg_us": c_us, "median_us": 1e3 * float(np.median(c_ms)),
+                   "bytes_per_launch": cb, "GB_s": c_gbs, "frac_hbm_peak": c_gbs / HBM_PEAK_GBS,
+                   "launches_per_step": L},
+    }
+    dom = "verify" if v_us >= c_us else "commit"
+    kd = kernels[dom]
+    naive = wl.heads * wl.total_nodes * wl.d_k * wl.d_v * 4
+    bole_transient = sum(int(layers[0][n].numel() * layers[0][n].element_size())
+                         for n in ("k", "v", "gate"))
+    result = {
+        "metric": METRIC,
+        "value": nodes / (ms_per_step * 1e-3),
+        "unit": "draft nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "hybrid_stack: 64 sequences x 8 linear-recurrence layers x 32 "
+                               "heads, d_k=128, d_v=64, 32-node best-first draft trees, bf16 "
+                               "q/k/v, fp32 scalar gate and state; verify all layers, then "
+                               "commit each layer's accepted path in place",
+                   "batch": wl.batch, "layers": L, "heads": wl.heads, "d_k": wl.d_k,
+                   "d_v": wl.d_v, "nodes_per_tree": 32, "parallelism": "single_gpu"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kd["GB_s"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["GB_s"] / HBM_PEAK_GBS,
+                     "traffic": None},
+        "kernels": kernels,
+        "hbm_GB_s_step": L * (vb + cb) / (ms_per_step * 1e6),
+        "wall_ms_per_step": 1e3 * wall / args.steps,
+        "transient_bytes_per_layer": {"naive_state_per_node": naive,
+                                      "bole_factors": bole_transient,
+                                      "reduction": 1.0 - bole_transient / naive},
+    }
+
+    if args.copy_calibration:
+        n = 512 * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": 4 * n, "write": 4 * n}
+        del src, dst
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, min_seconds):
+    """fp64 CPU oracle (serial walk per node) on whole steps of the same workload:
+    verify of all 8 layers then commit of all 8 layers, repeated until at least
+    min_seconds have passed. Inputs are widened to fp64 before the clock starts."""
+    import numpy as np
+
+    import oracle
+    lays = [[oracle.f64(t) for t in (l.H0, l.q, l.k, l.v, l.gate)] for l in wl.layers]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for H0, q, k, v, gate in lays:
+            oracle.verify_serial(H0, q, k, v, gate, wl.parent, wl.node_offsets, False)
+        for H0, q, k, v, gate in lays:
+            oracle.commit_serial(H0, k, v, gate, wl.parent, wl.node_offsets, wl.accepted_idx,
+                                 wl.accepted_len, False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": reps * wl.total_nodes / el, "unit": "draft nodes/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{reps} whole step(s) of the same workload (8-layer verify + commit, "
+                      f"{wl.total_nodes} nodes x {wl.heads} heads per layer), fp64, "
+                      f"{el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

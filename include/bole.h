@@ -1,0 +1,187 @@
+/*
+ * bole.h - C ABI of the MI355X (gfx950) library for Bole-style tree verification of
+ * linear-recurrence layers, and for the commit of the accepted path.
+ *
+ * Method: "Bole: Efficient Tree Speculation for Hybrid-Attention Language Models", as
+ * summarised on the llm-wiki page about Bole.
+ *  - Section 1, "Tree-Structured Closed Form": the per-token recurrence
+ *    h_{t+1} = S_t h_t + u_t unrolls into a chain of factor products. Every draft node
+ *    can therefore be verified in parallel, with no serial walk down the branches.
+ *  - Section 2, "Token-Level Factor Encoding": each draft node stores only its own
+ *    token factor, and after verification only the accepted path's state is rebuilt.
+ *
+ * Here, for the Mamba-2 / GLA / RWKV-6 family, a draft node i carries:
+ *  - a gate: a scalar decay a_i per head (S_i = a_i I), or one decay per key channel
+ *    g_i (S_i = diag(g_i), scaling the d_k rows of the state);
+ *  - a rank-one update u_i = k_i v_i^T;
+ *  - a query q_i.
+ * Its state is H_i = S_i H_parent(i) + k_i v_i^T. A node whose parent is -1 hangs
+ * directly off the committed state H_0. Its output, taken after its own update, is
+ *     o_i = H_i^T q_i = D_i (H_0^T q_i) + sum_{j on path(i)} D_{j->i} (q_i . k_j) v_j
+ * for a scalar gate, where D_i is the product of the gates on the root-to-i path and
+ * D_{j->i} the product over the nodes after j on that path (D_{i->i} = 1). For a vector
+ * gate the same holds channel by channel:
+ *     o_i = H_0^T (G_i * q_i) + sum_j (sum_c q_i[c] k_j[c] G_i[c] / G_j[c]) v_j.
+ *
+ * Memory layouts. Everything is row-major, contiguous, and in device memory unless
+ * stated otherwise:
+ *   H0    float [B][H][d_k][d_v]   committed state, one matrix per (sequence, head)
+ *   q, k  [T][H][d_k]              factor_dtype (bf16 or fp32)
+ *   v     [T][H][d_v]              factor_dtype
+ *   gate  float [T][H] (BOLE_GATE_SCALAR) or [T][H][d_k] (BOLE_GATE_VECTOR).
+ *         It holds the decay itself: finite and > 0, typically in (0, 1].
+ *   out   float [T][H][d_v]
+ *   parent       int32 [T]      tree-local parent index, -1 for a root. parent[i] < i
+ *                               is required (topological order). Forests are allowed.
+ *   node_offsets int32 [B + 1]  tree b owns packed rows node_offsets[b] ..
+ *                               node_offsets[b+1]-1, at most 64 of them.
+ *   accepted_idx int32 [B][max_path]  tree-local accepted path, root first
+ *   accepted_len int32 [B]
+ * Rows that belong to no tree are neither read nor written.
+ *
+ * Ownership. The caller owns every buffer. The library allocates nothing, keeps no
+ * pointer after a call returns, and needs no workspace. Every call is asynchronous on
+ * the given stream and does not synchronise. Calls are reentrant across streams.
+ *
+ * Errors.
+ *  - Problems visible on the host (null pointers, sizes out of range, unsupported
+ *    combinations) are reported by the return value before anything is launched.
+ *  - Problems in tree data are only visible on the device. They are reported per tree
+ *    in the optional tree_status[B] output, as BOLE_TREE_* codes:
+ *      - for a tree with a bad size, nothing is written;
+ *      - verify fills the rows of a bad-parent tree with NaN;
+ *      - commit leaves the state of any bad tree untouched.
+ */
+#ifndef BOLE_H
+#define BOLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BOLE_API __attribute__((visibility("default")))
+
+/* Host-side result of every call. */
+typedef enum {
+    BOLE_OK = 0,
+    BOLE_ERR_INVALID_VALUE = 1, /* null pointer, negative size, bad enum value */
+    BOLE_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels cover */
+    BOLE_ERR_HIP = 3            /* a HIP launch reported an error */
+} bole_status_t;
+
+/* Per-tree device-side status written to tree_status[b]. */
+enum {
+    BOLE_TREE_OK = 0,
+    BOLE_TREE_BAD_SIZE = 1,   /* offsets unordered, outside [0, T], or more than 64 nodes */
+    BOLE_TREE_BAD_PARENT = 2, /* some node i has parent[i] < -1 or parent[i] >= i */
+    BOLE_TREE_BAD_PATH = 3    /* commit: length outside [0, max_path], an index outside
+                                 the tree, or not a chain that starts at a root */
+};
+
+typedef enum { BOLE_DTYPE_BF16 = 0, BOLE_DTYPE_F32 = 1 } bole_dtype_t;
+typedef enum { BOLE_GATE_SCALAR = 0, BOLE_GATE_VECTOR = 1 } bole_gate_kind_t;
+
+/* Flags (bole_dims_t.flags). */
+enum {
+    BOLE_FLAG_FORCE_GENERIC = 1 /* use the plain vector-ALU kernels even where the
+                                   matrix-core kernels apply (testing, odd shapes) */
+};
+
+/* Same type as hipStream_t; NULL is the default stream. */
+typedef struct ihipStream_t *bole_stream_t;
+
+typedef struct {
+    int32_t batch;        /* B >= 0 trees (one per sequence) */
+    int32_t heads;        /* H >= 1 */
+    int32_t d_k;          /* key width = state rows, 1..256 */
+    int32_t d_v;          /* value width = state columns, 1..256 */
+    int32_t total_nodes;  /* T >= 0, rows of the packed node arrays */
+    int32_t max_path;     /* commit: row stride of accepted_idx, 0..64 */
+    int32_t factor_dtype; /* bole_dtype_t of q, k, v */
+    int32_t gate_kind;    /* bole_gate_kind_t */
+    int32_t flags;        /* BOLE_FLAG_* */
+} bole_dims_t;
+
+/* Per-node factors that a commit gathers along the accepted path (section 2 of the
+ * Bole summary: the factors (S_i, u_i) are all that is kept per node). */
+typedef struct {
+    const void *k;                /* [T][H][d_k] factor_dtype */
+    const void *v;                /* [T][H][d_v] factor_dtype */
+    const float *gate;            /* [T][H] or [T][H][d_k] */
+    const int32_t *parent;        /* [T] */
+    const int32_t *node_offsets;  /* [B + 1] */
+} bole_factors_t;
+
+/* Maximum number of nodes in one tree (one 64-lane wavefront, one 64-bit mask). */
+BOLE_API int32_t bole_max_tree_nodes(void);
+
+/* Human-readable name of a status value (static string, never NULL). */
+BOLE_API const char *bole_status_string(bole_status_t status);
+
+/* Host-only check of a dims descriptor, the same check every entry point runs first.
+ * `op` is 0 for verify, 1 for commit, 2 for prepare. Touches no device. */
+BOLE_API bole_status_t bole_check_dims(const bole_dims_t *dims, int32_t op);
+
+/*
+ * Tree verification: the closed form of the Bole summary page, section 1
+ * ("Tree-Structured Closed Form").
+ * Writes out[i] = H_i^T q_i for every node of every tree, all nodes in parallel.
+ * H0 is read once per (sequence, head) and never written. No per-node state is ever
+ * materialised: only the per-node factors are read.
+ * out must not alias any input.
+ * tree_status (device int32[B], may be NULL) receives one BOLE_TREE_* code per tree.
+ * Returns BOLE_ERR_INVALID_VALUE or BOLE_ERR_UNSUPPORTED without launching anything.
+ */
+BOLE_API bole_status_t bole_tree_verify(const float *H0, const void *q, const void *k, const void *v,
+                               const float *gate, const int32_t *parent,
+                               const int32_t *node_offsets, float *out,
+                               const bole_dims_t *dims, int32_t *tree_status,
+                               bole_stream_t stream);
+
+/*
+ * Accepted-path commit: the restore step of the Bole summary page, section 2
+ * ("Token-Level Factor Encoding").
+ * For each tree b with accepted_len[b] = L > 0, and path p_1..p_L
+ * (= accepted_idx[b][0..L-1]):
+ *     H0[b,h] <- S_{p_L}...S_{p_1} H0[b,h] + sum_m (S_{p_L}...S_{p_{m+1}}) k_{p_m} v_{p_m}^T
+ * This is done in place, for every head. The result is the state after the accepted
+ * tokens. A length of 0 leaves H0 untouched.
+ * `factors` is a host struct of device pointers. accepted_idx and accepted_len are
+ * device arrays.
+ * path_nodes (device int32[B][max_path], may be NULL) receives the packed row of each
+ * applied node (node_offsets[b] + accepted_idx[b][m]), and -1 elsewhere and for bad
+ * trees.
+ * tree_status (device int32[B], may be NULL) receives BOLE_TREE_* codes.
+ * Must be stream-ordered after any verify that reads the same H0.
+ */
+BOLE_API bole_status_t bole_commit_path(float *H0, const bole_factors_t *factors,
+                               const int32_t *accepted_idx, const int32_t *accepted_len,
+                               const bole_dims_t *dims, int32_t *path_nodes,
+                               int32_t *tree_status, bole_stream_t stream);
+
+/*
+ * Tree topology preprocessor: the same per-tree pass that verify and commit run
+ * internally, exported on its own.
+ * Per node:
+ *   depth  (int32 [T])  number of nodes on the root-to-node path;
+ *   mask   (uint64 [T]) bit j set when tree-local node j is on that path;
+ *   cumlog (float [T][H], or [T][H][d_k] for vector gates) sum of log(gate) over the
+ *          path, root first.
+ * Any output pointer may be NULL to skip that output. gate may be NULL when cumlog is
+ * NULL.
+ * For a bad-parent tree, depth, mask and cumlog are written as 0. For a bad-size tree,
+ * nothing is written.
+ */
+BOLE_API bole_status_t bole_tree_prepare(const int32_t *parent, const int32_t *node_offsets,
+                                const float *gate, const bole_dims_t *dims, int32_t *depth,
+                                uint64_t *mask, float *cumlog, int32_t *tree_status,
+                                bole_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BOLE_H */

@@ -30,6 +30,8 @@ def configure(lib):
                                          _p, _p, _p, _p, _p, _p, _p, _p, _p]
     lib.oracle_commit_serial.argtypes = [_i64, _i64, _i64, _i64, _i64, _int, _p, _p, _p,
                                          _p, _p, _p, _p, _p, _i64, _p, _p]
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = _int
     for f in (lib.oracle_topology, lib.oracle_cumlog, lib.oracle_verify_serial,
               lib.oracle_commit_serial):
         f.restype = _int
@@ -43,6 +45,11 @@ def _load():
             _build.build()
         _lib = configure(ctypes.CDLL(_build.LIB))
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
 
 
 def f64(x) -> np.ndarray:

@@ -45,6 +45,7 @@
  *       not a chain that starts at a root.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -52,6 +53,9 @@
 #define OR_MAX_TREE 64
 
 enum { OR_OK = 0, OR_BAD_SIZE = 1, OR_BAD_PARENT = 2, OR_BAD_PATH = 3 };
+
+/* Number of OpenMP threads the parallel loops below use. */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* Structural check of tree b: size first, then every parent link. */
 static int or_tree_check(int64_t b, const int32_t *node_offsets, int64_t total_nodes,

@@ -1,0 +1,101 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point that
+include/bole.h declares, and rejects bad host-visible arguments before launching."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch  # noqa: F401  (the binding loads libbole.so into torch's HIP runtime)
+
+from tree_speculative_decoding_02_amd import bole
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "bole.h")).read()
+    return re.findall(r"BOLE_API\s+[\w\s\*]+?\b(bole_\w+)\s*\(", src)
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert set(names) == set(bole.EXPORTED)
+    for want in ("bole_tree_verify", "bole_commit_path", "bole_tree_prepare"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", bole.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(bole.lib, name)
+    # nothing but the C ABI and HIP's own kernel handles is visible
+    leaked = [s for s in exported if "launch_" in s]
+    assert not leaked, leaked
+
+
+def _dims(**kw):
+    d = bole.make_dims(4, 8, 128, 64, 100, torch.bfloat16, False, 8)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("op", [0, 1, 2])
+def test_check_dims_accepts_valid(op):
+    assert bole.lib.bole_check_dims(ctypes.byref(_dims()), op) == bole.BOLE_OK
+
+
+@pytest.mark.parametrize("field,value,op,want", [
+    ("heads", 0, 0, 1), ("batch", -1, 0, 1), ("d_k", 0, 0, 1), ("d_v", -3, 1, 1),
+    ("total_nodes", -1, 2, 1), ("factor_dtype", 7, 0, 1), ("gate_kind", 2, 0, 1),
+    ("flags", 8, 0, 1), ("max_path", -1, 1, 1), ("d_k", 257, 0, 2), ("d_v", 512, 1, 2),
+    ("max_path", 65, 1, 2),
+])
+def test_check_dims_rejects(field, value, op, want):
+    assert bole.lib.bole_check_dims(ctypes.byref(_dims(**{field: value})), op) == want
+
+
+def test_vector_gate_width_limit():
+    d = _dims(gate_kind=bole.BOLE_GATE_VECTOR, d_k=256)
+    assert bole.lib.bole_check_dims(ctypes.byref(d), 0) == bole.BOLE_ERR_UNSUPPORTED
+    assert bole.lib.bole_check_dims(ctypes.byref(d), 1) == bole.BOLE_OK
+
+
+def test_null_dims_and_pointers_rejected_without_launch():
+    L = bole.lib
+    assert L.bole_check_dims(None, 0) == bole.BOLE_ERR_INVALID_VALUE
+    args = [None] * 8
+    assert L.bole_tree_verify(*args, None, None, None) == bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_tree_verify(*args, ctypes.byref(_dims()), None, None) == \
+        bole.BOLE_ERR_INVALID_VALUE
+    # an empty batch is a valid no-op
+    assert L.bole_tree_verify(*args, ctypes.byref(_dims(batch=0)), None, None) == bole.BOLE_OK
+    f = bole.bole_factors_t()
+    assert L.bole_commit_path(None, ctypes.byref(f), None, None, ctypes.byref(_dims()), None,
+                              None, None) == bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_commit_path(None, None, None, None, ctypes.byref(_dims(batch=0)), None, None,
+                              None) == bole.BOLE_OK
+    assert L.bole_tree_prepare(None, None, None, ctypes.byref(_dims()), None, None, None, None,
+                               None) == bole.BOLE_ERR_INVALID_VALUE
+
+
+def test_status_strings_and_limits():
+    assert bole.lib.bole_max_tree_nodes() == bole.MAX_TREE_NODES == 64
+    for code, name in [(0, b"BOLE_OK"), (1, b"BOLE_ERR_INVALID_VALUE"),
+                       (2, b"BOLE_ERR_UNSUPPORTED"), (3, b"BOLE_ERR_HIP")]:
+        assert bole.lib.bole_status_string(code) == name
+    assert bole.lib.bole_status_string(99) == b"BOLE_ERR_UNKNOWN"
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package never imports, loads or names the oracle."""
+    pkg = os.path.join(ROOT, "tree_speculative_decoding_02_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.lower(), fn

@@ -1,0 +1,200 @@
+"""Thin ctypes binding over libbole.so, using the C function names of include/bole.h.
+
+Only argument marshalling happens here: dtype, device and shape checks, building the
+dims descriptor, and passing data pointers plus torch's current HIP stream. Every step
+of verify, commit and prepare runs in the library's HIP kernels. If the library is
+missing, importing this module fails: there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch  # must be imported before libbole.so: the two share torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbole.so")
+
+BOLE_OK, BOLE_ERR_INVALID_VALUE, BOLE_ERR_UNSUPPORTED, BOLE_ERR_HIP = 0, 1, 2, 3
+BOLE_TREE_OK, BOLE_TREE_BAD_SIZE, BOLE_TREE_BAD_PARENT, BOLE_TREE_BAD_PATH = 0, 1, 2, 3
+BOLE_DTYPE_BF16, BOLE_DTYPE_F32 = 0, 1
+BOLE_GATE_SCALAR, BOLE_GATE_VECTOR = 0, 1
+BOLE_FLAG_FORCE_GENERIC = 1
+MAX_TREE_NODES = 64
+
+EXPORTED = ("bole_max_tree_nodes", "bole_status_string", "bole_check_dims", "bole_tree_verify",
+            "bole_commit_path", "bole_tree_prepare")
+
+
+class bole_dims_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("d_k", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("total_nodes", ctypes.c_int32),
+                ("max_path", ctypes.c_int32), ("factor_dtype", ctypes.c_int32),
+                ("gate_kind", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class bole_factors_t(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("parent", ctypes.c_void_p), ("node_offsets", ctypes.c_void_p)]
+
+
+class BoleError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                          "(hipcc, gfx950) before using the HIP path")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32 = ctypes.c_void_p, ctypes.c_int32
+    D = ctypes.POINTER(bole_dims_t)
+    lib.bole_max_tree_nodes.restype = I32
+    lib.bole_max_tree_nodes.argtypes = []
+    lib.bole_status_string.restype = ctypes.c_char_p
+    lib.bole_status_string.argtypes = [ctypes.c_int]
+    lib.bole_check_dims.restype = ctypes.c_int
+    lib.bole_check_dims.argtypes = [D, I32]
+    lib.bole_tree_verify.restype = ctypes.c_int
+    lib.bole_tree_verify.argtypes = [P, P, P, P, P, P, P, P, D, P, P]
+    lib.bole_commit_path.restype = ctypes.c_int
+    lib.bole_commit_path.argtypes = [P, ctypes.POINTER(bole_factors_t), P, P, D, P, P, P]
+    lib.bole_tree_prepare.restype = ctypes.c_int
+    lib.bole_tree_prepare.argtypes = [P, P, P, D, P, P, P, P, P]
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int, what: str):
+    if status != BOLE_OK:
+        raise BoleError(f"{what}: {lib.bole_status_string(status).decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def make_dims(batch, heads, d_k, d_v, total_nodes, factor_dtype, vector_gate, max_path=0,
+              force_generic=False) -> bole_dims_t:
+    fd = {torch.bfloat16: BOLE_DTYPE_BF16, torch.float32: BOLE_DTYPE_F32}.get(factor_dtype)
+    if fd is None:
+        raise TypeError(f"factor dtype must be bfloat16 or float32, got {factor_dtype}")
+    return bole_dims_t(batch, heads, d_k, d_v, total_nodes, max_path, fd,
+                       BOLE_GATE_VECTOR if vector_gate else BOLE_GATE_SCALAR,
+                       BOLE_FLAG_FORCE_GENERIC if force_generic else 0)
+
+
+def _factor_dims(H0, q_or_k, v, gate, parent, node_offsets):
+    dev = H0.device
+    _need(H0, "H0", torch.float32)
+    if H0.dim() != 4:
+        raise ValueError("H0 must be [B, H, d_k, d_v]")
+    B, Hh, d_k, d_v = H0.shape
+    _need(q_or_k, "k", device=dev)
+    _need(v, "v", q_or_k.dtype, dev)
+    _need(gate, "gate", torch.float32, dev)
+    _need(parent, "parent", torch.int32, dev)
+    _need(node_offsets, "node_offsets", torch.int32, dev)
+    T = q_or_k.shape[0]
+    if tuple(q_or_k.shape) != (T, Hh, d_k) or tuple(v.shape) != (T, Hh, d_v):
+        raise ValueError("factor shapes must be [T, H, d_k] and [T, H, d_v]")
+    if tuple(parent.shape) != (T,) or tuple(node_offsets.shape) != (B + 1,):
+        raise ValueError("parent must be [T] and node_offsets [B + 1]")
+    if tuple(gate.shape) == (T, Hh):
+        vector_gate = False
+    elif tuple(gate.shape) == (T, Hh, d_k):
+        vector_gate = True
+    else:
+        raise ValueError("gate must be [T, H] (scalar) or [T, H, d_k] (vector)")
+    return B, Hh, d_k, d_v, T, vector_gate
+
+
+def bole_tree_verify(H0, q, k, v, gate, parent, node_offsets, out=None, tree_status=None,
+                     stream=None, force_generic=False):
+    """out[T, H, d_v] (fp32) = H_i^T q_i for every node, by the parallel closed form."""
+    B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
+    _need(q, "q", k.dtype, H0.device)
+    if tuple(q.shape) != tuple(k.shape):
+        raise ValueError("q must have the shape of k")
+    if out is None:
+        out = torch.empty((T, Hh, d_v), dtype=torch.float32, device=H0.device)
+    _need(out, "out", torch.float32, H0.device)
+    if tuple(out.shape) != (T, Hh, d_v):
+        raise ValueError("out must be [T, H, d_v]")
+    if tree_status is not None:
+        _need(tree_status, "tree_status", torch.int32, H0.device)
+        if tree_status.numel() < B:
+            raise ValueError("tree_status needs B entries")
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, force_generic)
+    _check(lib.bole_tree_verify(_ptr(H0), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(parent),
+                                _ptr(node_offsets), _ptr(out), ctypes.byref(dims),
+                                _ptr(tree_status), _stream(stream)), "bole_tree_verify")
+    return out
+
+
+def bole_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepted_len,
+                     path_nodes=None, tree_status=None, stream=None):
+    """Commits each tree's accepted path into H0 in place; returns H0."""
+    B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
+    _need(accepted_idx, "accepted_idx", torch.int32, H0.device)
+    _need(accepted_len, "accepted_len", torch.int32, H0.device)
+    if accepted_idx.dim() != 2 or accepted_idx.shape[0] != B or tuple(accepted_len.shape) != (B,):
+        raise ValueError("accepted_idx must be [B, max_path] and accepted_len [B]")
+    max_path = accepted_idx.shape[1]
+    for t, name in ((path_nodes, "path_nodes"), (tree_status, "tree_status")):
+        if t is not None:
+            _need(t, name, torch.int32, H0.device)
+    if path_nodes is not None and tuple(path_nodes.shape) != (B, max_path):
+        raise ValueError("path_nodes must be [B, max_path]")
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, max_path)
+    f = bole_factors_t(k.data_ptr(), v.data_ptr(), gate.data_ptr(), parent.data_ptr(),
+                       node_offsets.data_ptr())
+    _check(lib.bole_commit_path(_ptr(H0), ctypes.byref(f), _ptr(accepted_idx),
+                                _ptr(accepted_len), ctypes.byref(dims), _ptr(path_nodes),
+                                _ptr(tree_status), _stream(stream)), "bole_commit_path")
+    return H0
+
+
+def bole_tree_prepare(parent, node_offsets, heads=1, d_k=1, gate=None, want_cumlog=False,
+                      tree_status=None, stream=None):
+    """Topology export: (depth int32[T], mask int64[T] holding the uint64 bits,
+    cumlog float32 [T, H] / [T, H, d_k] or None)."""
+    _need(parent, "parent", torch.int32)
+    dev = parent.device
+    _need(node_offsets, "node_offsets", torch.int32, dev)
+    T, B = parent.shape[0], node_offsets.shape[0] - 1
+    vec = gate is not None and gate.dim() == 3
+    if want_cumlog:
+        _need(gate, "gate", torch.float32, dev)
+        heads = gate.shape[1]
+        d_k = gate.shape[2] if vec else d_k
+    depth = torch.zeros(T, dtype=torch.int32, device=dev)
+    mask = torch.zeros(T, dtype=torch.int64, device=dev)
+    cum = None
+    if want_cumlog:
+        cum = torch.zeros(tuple(gate.shape), dtype=torch.float32, device=dev)
+    if tree_status is not None:
+        _need(tree_status, "tree_status", torch.int32, dev)
+    dims = make_dims(B, heads, d_k, 1, T, torch.float32, vec)
+    _check(lib.bole_tree_prepare(_ptr(parent), _ptr(node_offsets), _ptr(gate), ctypes.byref(dims),
+                                 _ptr(depth), _ptr(mask), _ptr(cum), _ptr(tree_status),
+                                 _stream(None)), "bole_tree_prepare")
+    return depth, mask, cum

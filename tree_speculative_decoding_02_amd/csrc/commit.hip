@@ -1,0 +1,170 @@
+// commit.hip - in-place commit of each tree's accepted path into the committed state.
+//
+// This is the restore step of the Bole summary page, section 2 ("Token-Level Factor
+// Encoding"): after verification, only the accepted path's state is rebuilt, from the
+// per-node factors, on top of H_0. For path p_1..p_L of tree b and every head:
+//     H_0 <- S_{p_L} ... S_{p_1} H_0 + sum_m (S_{p_L} ... S_{p_{m+1}}) k_{p_m} v_{p_m}^T
+// Each thread keeps a slice of H_0 in registers and applies the L rank-one steps
+// H <- S_m H + k_m v_m^T in path order, so H_0 is read once and written once. The path
+// factors are staged in LDS in chunks of 16 nodes.
+//
+// One 256-thread workgroup per (sequence, head). Wavefront 0 first validates the tree
+// (size, parent links) and the path (length in [0, max_path], indices inside the tree,
+// each node the child of the previous one, the first a root). A bad tree keeps its
+// state; a tree with L = 0 costs no state traffic.
+#include "bole_device.h"
+#include "launch.h"
+
+namespace bole {
+
+constexpr int kCommitThreads = 256;
+constexpr int kPathChunk = 16;   // path nodes staged in LDS at a time
+constexpr int kRegFloats = 64;   // state floats held per thread per pass
+
+template <typename TF, bool VEC, int W>
+__global__ __launch_bounds__(kCommitThreads) void commit_kernel(
+    float *__restrict__ H0, const TF *__restrict__ k, const TF *__restrict__ v,
+    const float *__restrict__ gate, const int32_t *__restrict__ parent,
+    const int32_t *__restrict__ node_offsets, const int32_t *__restrict__ accepted_idx,
+    const int32_t *__restrict__ accepted_len, int32_t *__restrict__ path_nodes,
+    int32_t *__restrict__ tree_status, int H, int DK, int DV, int T, int max_path) {
+    __shared__ int s_row[kMaxTree];  // packed row of each path node
+    __shared__ int s_len;
+    extern __shared__ float s_f[];   // [kPathChunk][(VEC ? 2 : 1) * DK + DV] staged factors
+    const int unit = blockIdx.x;
+    const int b = unit / H, h = unit - b * H;
+    const int tid = threadIdx.x;
+
+    if (tid < 64) {
+        const TreeRange tr = tree_range(node_offsets, b, T);
+        int st = tr.status;
+        int len = 0, x = -1;
+        if (st == BOLE_TREE_OK) st = wave_topology(parent + tr.lo, tr.n).bad;
+        if (st == BOLE_TREE_OK) {
+            len = accepted_len[b];
+            if (len < 0 || len > max_path) {
+                st = BOLE_TREE_BAD_PATH;
+            } else {
+                x = tid < len ? accepted_idx[(size_t)b * max_path + tid] : -1;
+                const int prev_raw = __shfl(x, tid > 0 ? tid - 1 : 0, 64);
+                const int prev = tid == 0 ? -1 : prev_raw;
+                bool bad = false;
+                if (tid < len) bad = x < 0 || x >= tr.n || parent[tr.lo + x] != prev;
+                if (__any(bad)) st = BOLE_TREE_BAD_PATH;
+            }
+        }
+        const bool ok = st == BOLE_TREE_OK;
+        const int row = (ok && tid < len) ? tr.lo + x : -1;
+        s_row[tid] = row;
+        if (tid == 0) s_len = ok ? len : 0;
+        if (h == 0) {
+            if (tid == 0 && tree_status) tree_status[b] = st;
+            if (path_nodes && tid < max_path) path_nodes[(size_t)b * max_path + tid] = row;
+        }
+    }
+    __syncthreads();
+    const int len = s_len;
+    if (len == 0) return;
+
+    const int FW = (VEC ? 2 : 1) * DK + DV;   // staged floats per path node
+    const int GPR = DV / W;                    // W-wide groups per state row
+    const int G = DK * GPR;                    // groups per state
+    constexpr int PER = kRegFloats / W;        // groups per thread per pass
+    float *Hu = H0 + (size_t)unit * DK * DV;
+
+    for (int g0 = 0; g0 < G; g0 += kCommitThreads * PER) {
+        float reg[PER][W];
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int g = g0 + s * kCommitThreads + tid;
+            if (g < G) {
+                if (W == 4) {
+                    const float4 t = *reinterpret_cast<const float4 *>(Hu + (size_t)g * 4);
+                    reg[s][0] = t.x; reg[s][1] = t.y; reg[s][2] = t.z; reg[s][3] = t.w;
+                } else {
+                    reg[s][0] = Hu[g];
+                }
+            }
+        }
+        for (int m0 = 0; m0 < len; m0 += kPathChunk) {
+            const int mc = min(kPathChunk, len - m0);
+            __syncthreads();
+            for (int idx = tid; idx < mc * FW; idx += kCommitThreads) {
+                const int mm = idx / FW, f = idx - mm * FW;
+                const size_t row = (size_t)s_row[m0 + mm];
+                float val;
+                if (f < DK)
+                    val = to_f32(k[(row * H + h) * DK + f]);
+                else if (VEC && f < 2 * DK)
+                    val = gate[(row * H + h) * DK + (f - DK)];
+                else
+                    val = to_f32(v[(row * H + h) * DV + (f - (VEC ? 2 : 1) * DK)]);
+                s_f[idx] = val;
+            }
+            __syncthreads();
+            for (int mm = 0; mm < mc; ++mm) {
+                const float *fk = s_f + mm * FW;
+                const float *fg = fk + DK;
+                const float *fv = fk + (VEC ? 2 : 1) * DK;
+                const float a = VEC ? 0.f : gate[(size_t)s_row[m0 + mm] * H + h];
+#pragma unroll
+                for (int s = 0; s < PER; ++s) {
+                    const int g = g0 + s * kCommitThreads + tid;
+                    if (g < G) {
+                        const int r = g / GPR, c = (g - r * GPR) * W;
+                        const float kr = fk[r];
+                        const float sr = VEC ? fg[r] : a;
+#pragma unroll
+                        for (int e = 0; e < W; ++e) reg[s][e] = sr * reg[s][e] + kr * fv[c + e];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int g = g0 + s * kCommitThreads + tid;
+            if (g < G) {
+                if (W == 4) {
+                    *reinterpret_cast<float4 *>(Hu + (size_t)g * 4) =
+                        make_float4(reg[s][0], reg[s][1], reg[s][2], reg[s][3]);
+                } else {
+                    Hu[g] = reg[s][0];
+                }
+            }
+        }
+    }
+}
+
+template <typename TF, bool VEC>
+static void launch_w(float *H0, const bole_factors_t &f, const int32_t *accepted_idx,
+                     const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
+                     int32_t *tree_status, hipStream_t stream) {
+    const dim3 grid((unsigned)d.batch * (unsigned)d.heads), block(kCommitThreads);
+    const size_t lds = sizeof(float) * kPathChunk * ((VEC ? 2 : 1) * d.d_k + d.d_v);
+    const TF *k = static_cast<const TF *>(f.k), *v = static_cast<const TF *>(f.v);
+    const bool vec4 = (d.d_v % 4 == 0) && (reinterpret_cast<uintptr_t>(H0) % 16 == 0);
+    if (vec4)
+        commit_kernel<TF, VEC, 4><<<grid, block, lds, stream>>>(
+            H0, k, v, f.gate, f.parent, f.node_offsets, accepted_idx, accepted_len, path_nodes,
+            tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path);
+    else
+        commit_kernel<TF, VEC, 1><<<grid, block, lds, stream>>>(
+            H0, k, v, f.gate, f.parent, f.node_offsets, accepted_idx, accepted_len, path_nodes,
+            tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path);
+}
+
+hipError_t launch_commit(float *H0, const bole_factors_t &f, const int32_t *accepted_idx,
+                         const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
+                         int32_t *tree_status, hipStream_t stream) {
+    const bool vec = d.gate_kind == BOLE_GATE_VECTOR;
+    if (d.factor_dtype == BOLE_DTYPE_F32) {
+        if (vec) launch_w<float, true>(H0, f, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
+        else launch_w<float, false>(H0, f, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
+    } else {
+        if (vec) launch_w<__bf16, true>(H0, f, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
+        else launch_w<__bf16, false>(H0, f, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace bole
