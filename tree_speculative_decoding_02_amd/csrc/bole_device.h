@@ -26,6 +26,7 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
     return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
 }
 
+// Value of x in lane src (src must be wave-uniform; a compile-time constant is best).
 __device__ __forceinline__ float readlane_f(float x, int src_uniform) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src_uniform));
 }
@@ -64,16 +65,18 @@ struct WaveTopo {
     int bad;
 };
 
-__device__ __forceinline__ WaveTopo wave_topology(const int32_t *par, int n) {
+// Same, from the parent index already loaded by lane i (any value for lanes >= n).
+// Doubling stops as soon as every lane's pointer has passed a root, so a tree of depth
+// d costs ceil(log2 d) rounds.
+__device__ __forceinline__ WaveTopo wave_topology_p(int p_loaded, int n) {
     const int lane = lane_id();
-    const int p = lane < n ? par[lane] : -1;
+    const int p = lane < n ? p_loaded : -1;
     const bool bad_lane = lane < n && (p < -1 || p >= lane);
     WaveTopo t;
     t.bad = __any(bad_lane) ? BOLE_TREE_BAD_PARENT : BOLE_TREE_OK;
     uint64_t m = (lane < n && !t.bad) ? (1ull << lane) : 0ull;
     int anc = (lane < n && !t.bad) ? p : -1;
-#pragma unroll
-    for (int r = 0; r < 6; ++r) {
+    for (int r = 0; r < 6 && __any(anc >= 0); ++r) {
         const int src = anc < 0 ? lane : anc;
         const uint64_t m_up = shfl_u64(m, src);
         const int anc_up = __shfl(anc, src, 64);
@@ -87,17 +90,48 @@ __device__ __forceinline__ WaveTopo wave_topology(const int32_t *par, int n) {
     return t;
 }
 
-// Cumulative log-decay of lane i's node: sum of lg[j] over the set bits j of `mask`,
-// taken in ascending j. Because parent[i] < i, ascending index along a path is root
-// first, so every caller sums in the same fixed order. lg lives in lane j.
-// n is wave-uniform.
-__device__ __forceinline__ float wave_cumlog(uint64_t mask, float lg, int n) {
-    float acc = 0.f;
-    for (int j = 0; j < n; ++j) {
-        const float x = readlane_f(lg, j);
-        if ((mask >> j) & 1ull) acc += x;
+__device__ __forceinline__ WaveTopo wave_topology(const int32_t *par, int n) {
+    const int lane = lane_id();
+    return wave_topology_p(lane < n ? par[lane] : -1, n);
+}
+
+// Topology and cumulative log-decay in one doubling pass. Lane i starts from its own
+// log-gate lg; each round adds the sum held by the lane its pointer names, then jumps
+// the pointer. After the last round, `L` is the sum of lg over every node on the
+// root-to-i path. The summation order is a fixed binary tree over the path (the same
+// on every call), so the result is deterministic.
+struct WaveTopoL {
+    uint64_t mask;
+    int depth;
+    int bad;
+    float L;
+};
+
+__device__ __forceinline__ WaveTopoL wave_topology_cumlog(int p_loaded, float lg, int n) {
+    const int lane = lane_id();
+    const int p = lane < n ? p_loaded : -1;
+    const bool bad_lane = lane < n && (p < -1 || p >= lane);
+    WaveTopoL t;
+    t.bad = __any(bad_lane) ? BOLE_TREE_BAD_PARENT : BOLE_TREE_OK;
+    const bool live = lane < n && !t.bad;
+    uint64_t m = live ? (1ull << lane) : 0ull;
+    float acc = live ? lg : 0.f;
+    int anc = live ? p : -1;
+    for (int r = 0; r < 6 && __any(anc >= 0); ++r) {
+        const int src = anc < 0 ? lane : anc;
+        const uint64_t m_up = shfl_u64(m, src);
+        const float acc_up = __shfl(acc, src, 64);
+        const int anc_up = __shfl(anc, src, 64);
+        if (anc >= 0) {
+            m |= m_up;
+            acc += acc_up;
+            anc = anc_up;
+        }
     }
-    return acc;
+    t.mask = m;
+    t.depth = __popcll(m);
+    t.L = acc;
+    return t;
 }
 
 template <typename T>

@@ -6,12 +6,20 @@
 //     H_0 <- S_{p_L} ... S_{p_1} H_0 + sum_m (S_{p_L} ... S_{p_{m+1}}) k_{p_m} v_{p_m}^T
 // Each thread keeps a slice of H_0 in registers and applies the L rank-one steps
 // H <- S_m H + k_m v_m^T in path order, so H_0 is read once and written once. The path
-// factors are staged in LDS in chunks of 16 nodes.
+// factors are staged in LDS (as fp32) in chunks of 16 nodes.
 //
-// One 256-thread workgroup per (sequence, head). Wavefront 0 first validates the tree
-// (size, parent links) and the path (length in [0, max_path], indices inside the tree,
-// each node the child of the previous one, the first a root). A bad tree keeps its
-// state; a tree with L = 0 costs no state traffic.
+// One 256-thread workgroup per (sequence, head). The kernel is a stream: its cost is
+// the state's round trip through HBM plus a short chain of dependent loads, so it is
+// built for occupancy (few registers, little LDS) and a short chain:
+//   1. tree offsets and path length (scalar loads);
+//   2. the thread's state slice, every parent of the tree and the path indices, all
+//      issued together;
+//   3. wavefront 0 validates everything with cross-lane operations on what it already
+//      holds: tree size, parent links (-1 <= parent[i] < i), path length in
+//      [0, max_path], path indices inside the tree, each node the child of the previous
+//      one, the first a root;
+//   4. the path's factors are staged, the state is updated and stored.
+// A bad tree keeps its state. A tree with L = 0 costs no state traffic.
 #include "bole_device.h"
 #include "launch.h"
 
@@ -19,7 +27,7 @@ namespace bole {
 
 constexpr int kCommitThreads = 256;
 constexpr int kPathChunk = 16;   // path nodes staged in LDS at a time
-constexpr int kRegFloats = 64;   // state floats held per thread per pass
+constexpr int kRegFloats = 32;   // state floats held per thread per pass
 
 template <typename TF, bool VEC, int W>
 __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
@@ -28,34 +36,72 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
     const int32_t *__restrict__ node_offsets, const int32_t *__restrict__ accepted_idx,
     const int32_t *__restrict__ accepted_len, int32_t *__restrict__ path_nodes,
     int32_t *__restrict__ tree_status, int H, int DK, int DV, int T, int max_path) {
-    __shared__ int s_row[kMaxTree];  // packed row of each path node
+    __shared__ int s_row[kMaxTree];         // packed row of each path node
+    __shared__ float s_a[kMaxTree];         // scalar gate of each path node
     __shared__ int s_len;
-    extern __shared__ float s_f[];   // [kPathChunk][(VEC ? 2 : 1) * DK + DV] staged factors
+    extern __shared__ float s_f[];          // [kPathChunk][(VEC ? 2 : 1) * DK + DV] staged factors
     const int unit = blockIdx.x;
     const int b = unit / H, h = unit - b * H;
     const int tid = threadIdx.x;
 
+    const int FW = (VEC ? 2 : 1) * DK + DV;   // staged floats per path node
+    const int GPR = DV / W;                    // W-wide groups per state row
+    const int G = DK * GPR;                    // groups per state
+    constexpr int PER = kRegFloats / W;        // groups per thread per pass
+    float *Hu = H0 + (size_t)unit * DK * DV;
+
+    // ---- 1, 2: offsets and length, then everything that depends only on them
+    const TreeRange tr = tree_range(node_offsets, b, T);
+    const int len_raw = accepted_len[b];
+    const bool likely = tr.status == BOLE_TREE_OK && len_raw > 0 && len_raw <= max_path &&
+                        len_raw <= tr.n;
+    float reg[PER][W];
+    if (likely) {
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int g = s * kCommitThreads + tid;
+            if (g < G) {
+                if (W == 4) {
+                    const float4 t = *reinterpret_cast<const float4 *>(Hu + (size_t)g * 4);
+                    reg[s][0] = t.x; reg[s][1] = t.y; reg[s][2] = t.z; reg[s][3] = t.w;
+                } else {
+                    reg[s][0] = Hu[g];
+                }
+            }
+        }
+    }
+
+    // ---- 3: validation by wavefront 0, lane = tree node / path position
     if (tid < 64) {
-        const TreeRange tr = tree_range(node_offsets, b, T);
         int st = tr.status;
         int len = 0, x = -1;
-        if (st == BOLE_TREE_OK) st = wave_topology(parent + tr.lo, tr.n).bad;
-        if (st == BOLE_TREE_OK) {
-            len = accepted_len[b];
-            if (len < 0 || len > max_path) {
+        if (st == BOLE_TREE_OK && tr.n > 0) {
+            const int n = tr.n;
+            const int p = tid < n ? parent[tr.lo + tid] : -1;
+            const bool len_ok = len_raw >= 0 && len_raw <= max_path;
+            const int xr = (len_ok && tid < len_raw) ? accepted_idx[(size_t)b * max_path + tid] : -1;
+            if (__any(tid < n && (p < -1 || p >= tid))) {
+                st = BOLE_TREE_BAD_PARENT;
+            } else if (!len_ok) {
                 st = BOLE_TREE_BAD_PATH;
             } else {
-                x = tid < len ? accepted_idx[(size_t)b * max_path + tid] : -1;
+                len = len_raw;
+                x = xr;
+                // parent of node x (held by lane x) and the previous path node
+                const int px = __shfl(p, (x >= 0 && x < n) ? x : 0, 64);
                 const int prev_raw = __shfl(x, tid > 0 ? tid - 1 : 0, 64);
                 const int prev = tid == 0 ? -1 : prev_raw;
-                bool bad = false;
-                if (tid < len) bad = x < 0 || x >= tr.n || parent[tr.lo + x] != prev;
+                const bool bad = tid < len && (x < 0 || x >= n || px != prev);
                 if (__any(bad)) st = BOLE_TREE_BAD_PATH;
             }
+        } else if (st == BOLE_TREE_OK) {
+            // empty tree: only a zero-length path is valid
+            if (len_raw != 0) st = BOLE_TREE_BAD_PATH;
         }
         const bool ok = st == BOLE_TREE_OK;
         const int row = (ok && tid < len) ? tr.lo + x : -1;
         s_row[tid] = row;
+        if (!VEC) s_a[tid] = row >= 0 ? gate[(size_t)row * H + h] : 1.f;
         if (tid == 0) s_len = ok ? len : 0;
         if (h == 0) {
             if (tid == 0 && tree_status) tree_status[b] = st;
@@ -66,25 +112,29 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
     const int len = s_len;
     if (len == 0) return;
 
-    const int FW = (VEC ? 2 : 1) * DK + DV;   // staged floats per path node
-    const int GPR = DV / W;                    // W-wide groups per state row
-    const int G = DK * GPR;                    // groups per state
-    constexpr int PER = kRegFloats / W;        // groups per thread per pass
-    float *Hu = H0 + (size_t)unit * DK * DV;
-
+    // ---- 4: stage factors, update, store
     for (int g0 = 0; g0 < G; g0 += kCommitThreads * PER) {
-        float reg[PER][W];
+        if (g0 > 0) {
+#pragma unroll
+            for (int s = 0; s < PER; ++s) {
+                const int g = g0 + s * kCommitThreads + tid;
+                if (g < G) {
+                    if (W == 4) {
+                        const float4 t = *reinterpret_cast<const float4 *>(Hu + (size_t)g * 4);
+                        reg[s][0] = t.x; reg[s][1] = t.y; reg[s][2] = t.z; reg[s][3] = t.w;
+                    } else {
+                        reg[s][0] = Hu[g];
+                    }
+                }
+            }
+        }
+        // state row and first column of each group this thread holds (fixed for the pass)
+        int rr[PER], cc[PER];
 #pragma unroll
         for (int s = 0; s < PER; ++s) {
             const int g = g0 + s * kCommitThreads + tid;
-            if (g < G) {
-                if (W == 4) {
-                    const float4 t = *reinterpret_cast<const float4 *>(Hu + (size_t)g * 4);
-                    reg[s][0] = t.x; reg[s][1] = t.y; reg[s][2] = t.z; reg[s][3] = t.w;
-                } else {
-                    reg[s][0] = Hu[g];
-                }
-            }
+            rr[s] = g / GPR;
+            cc[s] = (g - rr[s] * GPR) * W;
         }
         for (int m0 = 0; m0 < len; m0 += kPathChunk) {
             const int mc = min(kPathChunk, len - m0);
@@ -106,16 +156,15 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
                 const float *fk = s_f + mm * FW;
                 const float *fg = fk + DK;
                 const float *fv = fk + (VEC ? 2 : 1) * DK;
-                const float a = VEC ? 0.f : gate[(size_t)s_row[m0 + mm] * H + h];
+                const float a = VEC ? 0.f : s_a[m0 + mm];
 #pragma unroll
                 for (int s = 0; s < PER; ++s) {
                     const int g = g0 + s * kCommitThreads + tid;
                     if (g < G) {
-                        const int r = g / GPR, c = (g - r * GPR) * W;
-                        const float kr = fk[r];
-                        const float sr = VEC ? fg[r] : a;
+                        const float kr = fk[rr[s]];
+                        const float sr = VEC ? fg[rr[s]] : a;
 #pragma unroll
-                        for (int e = 0; e < W; ++e) reg[s][e] = sr * reg[s][e] + kr * fv[c + e];
+                        for (int e = 0; e < W; ++e) reg[s][e] = sr * reg[s][e] + kr * fv[cc[s] + e];
                     }
                 }
             }

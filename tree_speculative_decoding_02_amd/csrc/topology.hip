@@ -1,9 +1,11 @@
 // topology.hip - the tree-topology preprocessor exported as bole_tree_prepare.
 //
 // One 64-lane workgroup per tree; lane i is tree-local node i. It writes depth,
-// the ancestor-or-self mask and the root-first cumulative log-decay. These come from
-// the same wave_topology / wave_cumlog device functions that the verify and commit
-// kernels run inline, so this export shows bit for bit what those kernels use.
+// the ancestor-or-self mask and the cumulative log-decay. Depth and mask come from
+// the same pointer-doubling device code that the verify and commit kernels run
+// inline, so this export shows bit for bit the topology those kernels use. The scalar
+// cumulative log-decay is the same doubling sum that the generic verify kernel uses
+// (the matrix-core kernel keeps the same sum in base 2).
 #include "bole_device.h"
 #include "launch.h"
 
@@ -22,7 +24,8 @@ __global__ __launch_bounds__(64) void prepare_kernel(
         return;
     }
     const int lo = tr.lo, n = tr.n;
-    const WaveTopo t = wave_topology(parent + lo, n);
+    const int p_raw = lane < n ? parent[lo + lane] : -1;
+    const WaveTopo t = wave_topology_p(p_raw, n);
     if (lane == 0 && tree_status) tree_status[b] = t.bad;
     if (lane < n) {
         if (depth) depth[lo + lane] = t.depth;
@@ -32,7 +35,7 @@ __global__ __launch_bounds__(64) void prepare_kernel(
     for (int h = 0; h < H; ++h) {
         if (!VEC) {
             const float lg = (lane < n && !t.bad) ? logf(gate[(size_t)(lo + lane) * H + h]) : 0.f;
-            const float L = wave_cumlog(t.mask, lg, n);
+            const float L = wave_topology_cumlog(p_raw, lg, n).L;
             if (lane < n) cumlog[(size_t)(lo + lane) * H + h] = L;
         } else {
             for (int c = 0; c < DK; ++c) {

@@ -43,14 +43,13 @@ __global__ __launch_bounds__(256) void verify_generic_kernel(
     }
     const int lo = tr.lo, n = tr.n;
     if (tid < 64) {
-        const WaveTopo t = wave_topology(parent + lo, n);
+        const int p_raw = tid < n ? parent[lo + tid] : -1;
+        const float lg =
+            (!VEC && tid < n) ? logf(gate[(size_t)(lo + tid) * H + h]) : 0.f;
+        const WaveTopoL t = wave_topology_cumlog(p_raw, lg, n);
         if (tid == 0) s_bad = t.bad;
         s_mask[tid] = t.mask;
-        if (!VEC) {
-            const float lg =
-                (tid < n && !t.bad) ? logf(gate[(size_t)(lo + tid) * H + h]) : 0.f;
-            s_L[tid] = wave_cumlog(t.mask, lg, n);
-        }
+        s_L[tid] = t.L;
     }
     __syncthreads();
     const int bad = s_bad;
