@@ -105,7 +105,7 @@ def main():
             if record is not None:
                 record["v"][l][0].record(stream)
             bole.bole_tree_verify(x["H0"], x["q"], x["k"], x["v"], x["gate"], parent, offs,
-                                  out=outs[l], stream=stream)
+                                  out=outs[l], stream=stream, trees_le_32=True)
             if record is not None:
                 record["v"][l][1].record(stream)
         for l in range(L):
@@ -113,7 +113,7 @@ def main():
             if record is not None:
                 record["c"][l][0].record(stream)
             bole.bole_commit_path(x["H0"], x["k"], x["v"], x["gate"], parent, offs, acc_idx,
-                                  acc_len, stream=stream)
+                                  acc_len, stream=stream, trees_le_32=True)
             if record is not None:
                 record["c"][l][1].record(stream)
 

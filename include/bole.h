@@ -75,7 +75,8 @@ typedef enum {
 /* Per-tree device-side status written to tree_status[b]. */
 enum {
     BOLE_TREE_OK = 0,
-    BOLE_TREE_BAD_SIZE = 1,   /* offsets unordered, outside [0, T], or more than 64 nodes */
+    BOLE_TREE_BAD_SIZE = 1,   /* offsets unordered, outside [0, T], or more than 64 nodes
+                                 (32 under BOLE_FLAG_TREES_LE_32) */
     BOLE_TREE_BAD_PARENT = 2, /* some node i has parent[i] < -1 or parent[i] >= i */
     BOLE_TREE_BAD_PATH = 3    /* commit: length outside [0, max_path], an index outside
                                  the tree, or not a chain that starts at a root */
@@ -86,8 +87,12 @@ typedef enum { BOLE_GATE_SCALAR = 0, BOLE_GATE_VECTOR = 1 } bole_gate_kind_t;
 
 /* Flags (bole_dims_t.flags). */
 enum {
-    BOLE_FLAG_FORCE_GENERIC = 1 /* use the plain vector-ALU kernels even where the
-                                   matrix-core kernels apply (testing, odd shapes) */
+    BOLE_FLAG_FORCE_GENERIC = 1, /* use the plain vector-ALU kernels even where the
+                                    matrix-core kernels apply (testing, odd shapes) */
+    BOLE_FLAG_TREES_LE_32 = 2    /* the caller's tree budget is at most 32 nodes: only the
+                                    kernels for such trees are launched, and a tree with
+                                    more nodes is reported BOLE_TREE_BAD_SIZE (verify and
+                                    commit alike) and left untouched */
 };
 
 /* Same type as hipStream_t; NULL is the default stream. */

@@ -47,12 +47,14 @@ def _dims(**kw):
 @pytest.mark.parametrize("op", [0, 1, 2])
 def test_check_dims_accepts_valid(op):
     assert bole.lib.bole_check_dims(ctypes.byref(_dims()), op) == bole.BOLE_OK
+    for flags in (1, 2, 3):
+        assert bole.lib.bole_check_dims(ctypes.byref(_dims(flags=flags)), op) == bole.BOLE_OK
 
 
 @pytest.mark.parametrize("field,value,op,want", [
     ("heads", 0, 0, 1), ("batch", -1, 0, 1), ("d_k", 0, 0, 1), ("d_v", -3, 1, 1),
     ("total_nodes", -1, 2, 1), ("factor_dtype", 7, 0, 1), ("gate_kind", 2, 0, 1),
-    ("flags", 8, 0, 1), ("max_path", -1, 1, 1), ("d_k", 257, 0, 2), ("d_v", 512, 1, 2),
+    ("flags", 8, 0, 1), ("flags", 4, 1, 1), ("max_path", -1, 1, 1), ("d_k", 257, 0, 2), ("d_v", 512, 1, 2),
     ("max_path", 65, 1, 2),
 ])
 def test_check_dims_rejects(field, value, op, want):

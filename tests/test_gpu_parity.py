@@ -43,25 +43,26 @@ def to_dev(wl, layer=0):
                 acc_len=torch.from_numpy(wl.accepted_len).to(d))
 
 
-def gpu_verify(bole, t, force_generic=False):
+def gpu_verify(bole, t, force_generic=False, trees_le_32=False):
     B = t["offs"].numel() - 1
     status = torch.full((max(B, 1),), -7, dtype=torch.int32, device=dev())
     out = torch.full((t["q"].shape[0], t["H0"].shape[1], t["H0"].shape[3]), 12345.0,
                      dtype=torch.float32, device=dev())
     bole.bole_tree_verify(t["H0"], t["q"], t["k"], t["v"], t["gate"], t["parent"], t["offs"],
                           out=out, tree_status=status[:B] if B else None,
-                          force_generic=force_generic)
+                          force_generic=force_generic, trees_le_32=trees_le_32)
     torch.cuda.synchronize()
     return out.double().cpu().numpy(), status[:B].cpu().numpy()
 
 
-def gpu_commit(bole, t):
+def gpu_commit(bole, t, trees_le_32=False):
     B = t["offs"].numel() - 1
     H = t["H0"].clone()
     status = torch.full((max(B, 1),), -7, dtype=torch.int32, device=dev())
     pn = torch.full(tuple(t["acc_idx"].shape), -7, dtype=torch.int32, device=dev())
     bole.bole_commit_path(H, t["k"], t["v"], t["gate"], t["parent"], t["offs"], t["acc_idx"],
-                          t["acc_len"], path_nodes=pn, tree_status=status[:B])
+                          t["acc_len"], path_nodes=pn, tree_status=status[:B],
+                          trees_le_32=trees_le_32)
     torch.cuda.synchronize()
     return H.double().cpu().numpy(), pn.cpu().numpy(), status[:B].cpu().numpy()
 
@@ -75,18 +76,18 @@ def oracle_layer(wl, layer=0):
     return out, st, H, pn, cst
 
 
-def check_workload(bole, wl, layer=0, paths=("auto", "generic")):
+def check_workload(bole, wl, layer=0, paths=("auto", "generic"), trees_le_32=False):
     tol = TOL[wl.factor_dtype]
     t = to_dev(wl, layer)
     ref, st, Href, pnref, cstref = oracle_layer(wl, layer)
     report = {}
     for path in paths:
-        out, gst = gpu_verify(bole, t, force_generic=(path == "generic"))
+        out, gst = gpu_verify(bole, t, force_generic=(path == "generic"), trees_le_32=trees_le_32)
         assert gst.tolist() == st.tolist(), (wl.name, path)
         err = rel_err_rows(out, ref)
         report[path] = err
         assert err <= tol, f"{wl.name} verify[{path}] rel err {err:.3e} > {tol:g}"
-    H, pn, cst = gpu_commit(bole, t)
+    H, pn, cst = gpu_commit(bole, t, trees_le_32=trees_le_32)
     assert cst.tolist() == cstref.tolist(), wl.name
     np.testing.assert_array_equal(pn, pnref)
     herr = rel_err_states(H, Href)
@@ -106,6 +107,33 @@ def test_config_parity(bole, cid):
     print(f"config {cid} {wl.name}: " + ", ".join(f"{k} {v:.2e}" for k, v in rep.items()))
 
 
+@pytest.mark.parametrize("cid", [2, 5])
+def test_config_parity_tree_budget_32(bole, cid):
+    """Same bars with the caller's tree budget declared as <= 32 nodes (the launch
+    configuration of the benchmark)."""
+    wl = W.make_config(cid, n_layers=1)
+    assert wl.tree_sizes.max() <= 32
+    check_workload(bole, wl, trees_le_32=True)
+
+
+def test_tree_budget_32_rejects_bigger_trees(bole):
+    """Under the <= 32 budget a 33-node tree is BAD_SIZE in verify and commit, and is
+    left untouched; the other trees are unaffected."""
+    wl = W.make_random(12, batch=3, heads=2, d_k=128, d_v=64, sizes=[32, 33, 5])
+    t = to_dev(wl)
+    ref, st, Href, _, cstref = oracle_layer(wl)
+    for path in ("auto", "generic"):
+        out, gst = gpu_verify(bole, t, force_generic=(path == "generic"), trees_le_32=True)
+        assert gst.tolist() == [0, 1, 0]
+        assert (out[32:65] == 12345.0).all()
+        keep = np.r_[0:32, 65:70]
+        assert rel_err_rows(out[keep], ref[keep]) <= 2e-3
+    H, pn, cst = gpu_commit(bole, t, trees_le_32=True)
+    assert cst.tolist() == [0, 1, 0]
+    np.testing.assert_array_equal(H[1], wl.layers[0].H0.double().numpy()[1])
+    assert rel_err_states(H[[0, 2]], Href[[0, 2]]) <= 2e-3
+
+
 def test_config5_all_layers_commit_in_place(bole):
     """Bench workload: 8 layers, verify then commit in place in every layer; sampled
     sequences checked against the oracle layer by layer."""
@@ -113,11 +141,11 @@ def test_config5_all_layers_commit_in_place(bole):
     sample = [0, 1, 17, 40, 63]
     for layer in range(len(wl.layers)):
         t = to_dev(wl, layer)
-        out, st = gpu_verify(bole, t)
+        out, st = gpu_verify(bole, t, trees_le_32=True)
         assert (st == 0).all()
         H = t["H0"]
         bole.bole_commit_path(H, t["k"], t["v"], t["gate"], t["parent"], t["offs"],
-                              t["acc_idx"], t["acc_len"])
+                              t["acc_idx"], t["acc_len"], trees_le_32=True)
         torch.cuda.synchronize()
         sub = subset(wl, layer, sample)
         ref, _, Href, _, _ = oracle_layer(sub)

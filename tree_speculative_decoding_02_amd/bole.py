@@ -18,6 +18,7 @@ BOLE_TREE_OK, BOLE_TREE_BAD_SIZE, BOLE_TREE_BAD_PARENT, BOLE_TREE_BAD_PATH = 0, 
 BOLE_DTYPE_BF16, BOLE_DTYPE_F32 = 0, 1
 BOLE_GATE_SCALAR, BOLE_GATE_VECTOR = 0, 1
 BOLE_FLAG_FORCE_GENERIC = 1
+BOLE_FLAG_TREES_LE_32 = 2
 MAX_TREE_NODES = 64
 
 EXPORTED = ("bole_max_tree_nodes", "bole_status_string", "bole_check_dims", "bole_tree_verify",
@@ -93,13 +94,14 @@ def _need(t, name, dtype=None, device=None):
 
 
 def make_dims(batch, heads, d_k, d_v, total_nodes, factor_dtype, vector_gate, max_path=0,
-              force_generic=False) -> bole_dims_t:
+              force_generic=False, trees_le_32=False) -> bole_dims_t:
     fd = {torch.bfloat16: BOLE_DTYPE_BF16, torch.float32: BOLE_DTYPE_F32}.get(factor_dtype)
     if fd is None:
         raise TypeError(f"factor dtype must be bfloat16 or float32, got {factor_dtype}")
+    flags = (BOLE_FLAG_FORCE_GENERIC if force_generic else 0) | \
+        (BOLE_FLAG_TREES_LE_32 if trees_le_32 else 0)
     return bole_dims_t(batch, heads, d_k, d_v, total_nodes, max_path, fd,
-                       BOLE_GATE_VECTOR if vector_gate else BOLE_GATE_SCALAR,
-                       BOLE_FLAG_FORCE_GENERIC if force_generic else 0)
+                       BOLE_GATE_VECTOR if vector_gate else BOLE_GATE_SCALAR, flags)
 
 
 def _factor_dims(H0, q_or_k, v, gate, parent, node_offsets):
@@ -128,8 +130,10 @@ def _factor_dims(H0, q_or_k, v, gate, parent, node_offsets):
 
 
 def bole_tree_verify(H0, q, k, v, gate, parent, node_offsets, out=None, tree_status=None,
-                     stream=None, force_generic=False):
-    """out[T, H, d_v] (fp32) = H_i^T q_i for every node, by the parallel closed form."""
+                     stream=None, force_generic=False, trees_le_32=False):
+    """out[T, H, d_v] (fp32) = H_i^T q_i for every node, by the parallel closed form.
+    trees_le_32: the caller's tree budget is at most 32 nodes (larger trees are reported
+    BOLE_TREE_BAD_SIZE and left untouched)."""
     B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
     _need(q, "q", k.dtype, H0.device)
     if tuple(q.shape) != tuple(k.shape):
@@ -143,7 +147,7 @@ def bole_tree_verify(H0, q, k, v, gate, parent, node_offsets, out=None, tree_sta
         _need(tree_status, "tree_status", torch.int32, H0.device)
         if tree_status.numel() < B:
             raise ValueError("tree_status needs B entries")
-    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, force_generic)
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, force_generic, trees_le_32)
     _check(lib.bole_tree_verify(_ptr(H0), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(parent),
                                 _ptr(node_offsets), _ptr(out), ctypes.byref(dims),
                                 _ptr(tree_status), _stream(stream)), "bole_tree_verify")
@@ -151,7 +155,7 @@ def bole_tree_verify(H0, q, k, v, gate, parent, node_offsets, out=None, tree_sta
 
 
 def bole_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepted_len,
-                     path_nodes=None, tree_status=None, stream=None):
+                     path_nodes=None, tree_status=None, stream=None, trees_le_32=False):
     """Commits each tree's accepted path into H0 in place; returns H0."""
     B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
     _need(accepted_idx, "accepted_idx", torch.int32, H0.device)
@@ -164,7 +168,7 @@ def bole_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepte
             _need(t, name, torch.int32, H0.device)
     if path_nodes is not None and tuple(path_nodes.shape) != (B, max_path):
         raise ValueError("path_nodes must be [B, max_path]")
-    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, max_path)
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, max_path, trees_le_32=trees_le_32)
     f = bole_factors_t(k.data_ptr(), v.data_ptr(), gate.data_ptr(), parent.data_ptr(),
                        node_offsets.data_ptr())
     _check(lib.bole_commit_path(_ptr(H0), ctypes.byref(f), _ptr(accepted_idx),

@@ -36,7 +36,7 @@ bole_status_t bole_check_dims(const bole_dims_t *d, int32_t op) {
         return BOLE_ERR_INVALID_VALUE;
     if (d->gate_kind != BOLE_GATE_SCALAR && d->gate_kind != BOLE_GATE_VECTOR)
         return BOLE_ERR_INVALID_VALUE;
-    if (d->flags & ~BOLE_FLAG_FORCE_GENERIC) return BOLE_ERR_INVALID_VALUE;
+    if (d->flags & ~(BOLE_FLAG_FORCE_GENERIC | BOLE_FLAG_TREES_LE_32)) return BOLE_ERR_INVALID_VALUE;
     if (op == kOpCommit && d->max_path < 0) return BOLE_ERR_INVALID_VALUE;
     if (d->d_k > 256 || d->d_v > 256) return BOLE_ERR_UNSUPPORTED;
     if (op == kOpVerify && d->gate_kind == BOLE_GATE_VECTOR && d->d_k > 128)

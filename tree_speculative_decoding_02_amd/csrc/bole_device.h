@@ -38,15 +38,21 @@ struct TreeRange {
     int status;
 };
 
-__device__ __forceinline__ TreeRange tree_range(const int32_t *node_offsets, int b, int T) {
+// max_n: the largest valid tree (kMaxTree, or 32 under BOLE_FLAG_TREES_LE_32).
+__device__ __forceinline__ TreeRange tree_range(const int32_t *node_offsets, int b, int T,
+                                                int max_n = kMaxTree) {
     const int lo = node_offsets[b];
     const int hi = node_offsets[b + 1];
     TreeRange r;
     r.lo = lo;
     r.n = hi - lo;
-    r.status = (lo < 0 || hi < lo || hi > T || hi - lo > kMaxTree) ? BOLE_TREE_BAD_SIZE
-                                                                    : BOLE_TREE_OK;
+    r.status = (lo < 0 || hi < lo || hi > T || hi - lo > max_n) ? BOLE_TREE_BAD_SIZE
+                                                                 : BOLE_TREE_OK;
     return r;
+}
+
+__host__ __device__ __forceinline__ int max_tree_nodes(int32_t flags) {
+    return (flags & BOLE_FLAG_TREES_LE_32) ? 32 : kMaxTree;
 }
 
 // Topology of the tree whose tree-local parent array is par[0 .. n-1], computed by

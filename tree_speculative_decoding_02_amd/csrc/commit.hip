@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
     const float *__restrict__ gate, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, const int32_t *__restrict__ accepted_idx,
     const int32_t *__restrict__ accepted_len, int32_t *__restrict__ path_nodes,
-    int32_t *__restrict__ tree_status, int H, int DK, int DV, int T, int max_path) {
+    int32_t *__restrict__ tree_status, int H, int DK, int DV, int T, int max_path, int max_n) {
     __shared__ int s_row[kMaxTree];         // packed row of each path node
     __shared__ float s_a[kMaxTree];         // scalar gate of each path node
     __shared__ int s_len;
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
     float *Hu = H0 + (size_t)unit * DK * DV;
 
     // ---- 1, 2: offsets and length, then everything that depends only on them
-    const TreeRange tr = tree_range(node_offsets, b, T);
+    const TreeRange tr = tree_range(node_offsets, b, T, max_n);
     const int len_raw = accepted_len[b];
     const bool likely = tr.status == BOLE_TREE_OK && len_raw > 0 && len_raw <= max_path &&
                         len_raw <= tr.n;
@@ -195,11 +195,11 @@ static void launch_w(float *H0, const bole_factors_t &f, const int32_t *accepted
     if (vec4)
         commit_kernel<TF, VEC, 4><<<grid, block, lds, stream>>>(
             H0, k, v, f.gate, f.parent, f.node_offsets, accepted_idx, accepted_len, path_nodes,
-            tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path);
+            tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags));
     else
         commit_kernel<TF, VEC, 1><<<grid, block, lds, stream>>>(
             H0, k, v, f.gate, f.parent, f.node_offsets, accepted_idx, accepted_len, path_nodes,
-            tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path);
+            tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags));
 }
 
 hipError_t launch_commit(float *H0, const bole_factors_t &f, const int32_t *accepted_idx,

@@ -15,10 +15,11 @@ template <bool VEC>
 __global__ __launch_bounds__(64) void prepare_kernel(
     const int32_t *__restrict__ parent, const int32_t *__restrict__ node_offsets,
     const float *__restrict__ gate, int32_t *__restrict__ depth, uint64_t *__restrict__ mask,
-    float *__restrict__ cumlog, int32_t *__restrict__ tree_status, int H, int DK, int T) {
+    float *__restrict__ cumlog, int32_t *__restrict__ tree_status, int H, int DK, int T,
+    int max_n) {
     const int b = blockIdx.x;
     const int lane = lane_id();
-    const TreeRange tr = tree_range(node_offsets, b, T);
+    const TreeRange tr = tree_range(node_offsets, b, T, max_n);
     if (tr.status != BOLE_TREE_OK) {
         if (lane == 0 && tree_status) tree_status[b] = tr.status;
         return;
@@ -58,11 +59,11 @@ hipError_t launch_prepare(const int32_t *parent, const int32_t *node_offsets, co
     if (d.gate_kind == BOLE_GATE_VECTOR)
         prepare_kernel<true><<<grid, block, 0, stream>>>(parent, node_offsets, gate, depth, mask,
                                                          cumlog, tree_status, d.heads, d.d_k,
-                                                         d.total_nodes);
+                                                         d.total_nodes, max_tree_nodes(d.flags));
     else
         prepare_kernel<false><<<grid, block, 0, stream>>>(parent, node_offsets, gate, depth, mask,
                                                           cumlog, tree_status, d.heads, d.d_k,
-                                                          d.total_nodes);
+                                                          d.total_nodes, max_tree_nodes(d.flags));
     return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void verify_generic_kernel(
     const float *__restrict__ H0, const TF *__restrict__ q, const TF *__restrict__ k,
     const TF *__restrict__ v, const float *__restrict__ gate, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, float *__restrict__ out,
-    int32_t *__restrict__ tree_status, int H, int DK, int DV, int T) {
+    int32_t *__restrict__ tree_status, int H, int DK, int DV, int T, int max_n) {
     __shared__ uint64_t s_mask[kMaxTree];
     __shared__ float s_L[kMaxTree];
     __shared__ float s_W[kMaxTree][kMaxTree + 1];
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void verify_generic_kernel(
     const int unit = blockIdx.x;
     const int b = unit / H, h = unit - b * H;
     const int tid = threadIdx.x;
-    const TreeRange tr = tree_range(node_offsets, b, T);
+    const TreeRange tr = tree_range(node_offsets, b, T, max_n);
     if (tr.status != BOLE_TREE_OK) {
         if (h == 0 && tid == 0 && tree_status) tree_status[b] = tr.status;
         return;
@@ -119,11 +119,11 @@ static hipError_t launch_typed(const float *H0, const void *q, const void *k, co
         const size_t lds = sizeof(float) * kMaxTree * d.d_k;
         verify_generic_kernel<TF, true><<<grid, block, lds, stream>>>(
             H0, qt, kt, vt, gate, parent, node_offsets, out, tree_status, d.heads, d.d_k, d.d_v,
-            d.total_nodes);
+            d.total_nodes, max_tree_nodes(d.flags));
     } else {
         verify_generic_kernel<TF, false><<<grid, block, 0, stream>>>(
             H0, qt, kt, vt, gate, parent, node_offsets, out, tree_status, d.heads, d.d_k, d.d_v,
-            d.total_nodes);
+            d.total_nodes, max_tree_nodes(d.flags));
     }
     return hipGetLastError();
 }

@@ -89,17 +89,17 @@ __device__ __forceinline__ void wait_vmem_le() {
 //     refill its buffer with chunk c+2, then run its MFMAs.
 // A second row tile (33..64 nodes) repeats the pass. Its H_0 chunks come from L2,
 // and its ancestor tile-0 operands come from direct loads.
-template <int DK, int DV>
-__global__ __launch_bounds__((DV < 64 ? DV : 64) / 32 * 64, 2) void verify_mfma_scalar_kernel(
+template <int DK, int DV, bool BIG>
+__global__ __launch_bounds__((DV < 64 ? DV : 64) / 32 * 64, BIG ? 2 : 4) void verify_mfma_scalar_kernel(
     const float *__restrict__ H0, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     const __bf16 *__restrict__ v, const float *__restrict__ gate,
     const int32_t *__restrict__ parent, const int32_t *__restrict__ node_offsets,
-    float *__restrict__ out, int32_t *__restrict__ tree_status, int H, int T, int U) {
+    float *__restrict__ out, int32_t *__restrict__ tree_status, int H, int T, int U, int max_n) {
     constexpr int KS = DK / 16;                    // K-steps of Q.H0 and K.Q^T
     constexpr int NCH = DK / 32;                   // 32-row H_0 chunks (two K-steps each)
     constexpr int NW = (DV < 64 ? DV : 64) / 32;   // waves per workgroup
     constexpr int G = DV / (32 * NW);              // column groups per unit
-    __shared__ float s_h0[NW][2][32 * 32];         // per wave: two 32-row chunks of its slice
+    __shared__ float s_h0[NW][NCH][32 * 32];       // per wave: its whole H_0 slice, by 32-row chunk
     __shared__ __bf16 s_v[NW][32 * 32];            // per wave: V rows of the tile, row j at [32 j]
 
     const int lane = lane_id();
@@ -121,10 +121,17 @@ __global__ __launch_bounds__((DV < 64 ? DV : 64) / 32 * 64, 2) void verify_mfma_
     const int c0 = __builtin_amdgcn_readfirstlane((cg * NW + wave) * 32);
     const bool writer = tree_status != nullptr && h == 0 && cg == 0 && threadIdx.x == 0;
 
-    const TreeRange tr = tree_range(node_offsets, b, T);
-    if (tr.status != BOLE_TREE_OK) {
-        if (writer) tree_status[b] = tr.status;
-        return;
+    // BIG instantiation: trees of 33..64 nodes only (everything else, status included, is
+    // the small instantiation's); small instantiation: every other tree.
+    const TreeRange tr = tree_range(node_offsets, b, T, BIG ? kMaxTree : max_n);
+    if (BIG) {
+        if (tr.status != BOLE_TREE_OK || tr.n <= 32) return;
+    } else {
+        if (tr.status != BOLE_TREE_OK) {
+            if (writer) tree_status[b] = tr.status;
+            return;
+        }
+        if (tr.n > 32) return;  // launched alongside the BIG instantiation
     }
     const int lo = tr.lo, n = tr.n;
     if (n == 0) {
@@ -140,7 +147,7 @@ __global__ __launch_bounds__((DV < 64 ? DV : 64) / 32 * 64, 2) void verify_mfma_
     const __bf16 *vu = v + (size_t)lo * rv + (size_t)h * DV + c0;
     float *ou = out + (size_t)lo * rv + (size_t)h * DV + c0;
     const float *hu = H0 + (size_t)unit * DK * DV + c0;
-    float *lh0 = s_h0[wave][0], *lh1 = s_h0[wave][1];
+
     __bf16 *lv = s_v[wave];
     // H_0 chunk c (rows 32c .. 32c+31 of the slice): instruction s moves rows 32c + 8s ..
     // +7; lane l takes row 32c + 8s + l/8, columns 4(l%8) .. +3
@@ -157,15 +164,19 @@ __global__ __launch_bounds__((DV < 64 ? DV : 64) / 32 * 64, 2) void verify_mfma_
     const float g_raw = gate[(size_t)lo * H + h + (uint32_t)min(lane, last) * (uint32_t)H];
 
     WaveTopoL topo;
-    const int ntile = (n + 31) >> 5;
+    constexpr int ntile = BIG ? 2 : 1;
     for (int it = 0; it < ntile; ++it) {
-        // ---- 1. issue: Q fragments, V rows and the first two H_0 chunks (the vmcnt
-        // waits below count the younger DMAs, so the order matters)
-        bf16x8 qf[KS];
+        // ---- 1. issue everything this tile needs at once: Q and K fragments (registers),
+        // V rows and the whole H_0 slice (DMA into LDS). Nothing later waits on a load
+        // that depends on another load.
+        bf16x8 qf[KS], kf[KS];
         {
             const uint32_t qo = (uint32_t)min(32 * it + col, last) * rq + qoff_half;
 #pragma unroll
-            for (int t = 0; t < KS; ++t) qf[t] = load16(qu + (qo + 16 * t));
+            for (int t = 0; t < KS; ++t) {
+                qf[t] = load16(qu + (qo + 16 * t));
+                kf[t] = load16(ku + (qo + 16 * t));
+            }
         }
         {
             // V rows 32it .. 32it+31: instruction s moves 16 rows, lane l takes row
@@ -174,8 +185,10 @@ __global__ __launch_bounds__((DV < 64 ? DV : 64) / 32 * 64, 2) void verify_mfma_
             for (int s = 0; s < 2; ++s)
                 dma16(vu + ((uint32_t)min(32 * it + 16 * s + (lane >> 2), last) * rv + 8 * (lane & 3)), lv + 512 * s);
         }
-        dma_chunk(0, lh0);
-        if (NCH > 1) dma_chunk(1, lh1);
+        if (it == 0) {
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) dma_chunk(c, s_h0[wave][c]);
+        }
 
         // ---- 2. topology and decay, once, while the loads fly
         if (it == 0) {
@@ -198,32 +211,22 @@ __global__ __launch_bounds__((DV < 64 ? DV : 64) / 32 * 64, 2) void verify_mfma_
             return half ? v1 : v0;
         };
 
-        // ---- 3. H0 term chunk by chunk through the LDS double buffer:
-        // acc = Q_it . H0 slice, H0 split into bf16 hi + lo
+        // ---- 3. H0 term over the resident slice: acc = Q_it . H0 slice, H0 split into
+        // bf16 hi + lo
         f32x16 acc;
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+        wait_all_memory();
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            float *buf = (c & 1) ? lh1 : lh0;
-            if (c + 1 < NCH) wait_vmem_le<4>();  // only chunk c+1's DMA may still fly
-            else wait_vmem_le<0>();
-            float hv[2][8];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) hv[t][e] = buf[(16 * t + 8 * half + e) * 32 + col];
-            if (c + 2 < NCH) {
-                wait_lds_reads();
-                dma_chunk(c + 2, buf);
-            }
+            const float *buf = s_h0[wave][c];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 bf16x8 bh, bl;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     __bf16 xh, xl;
-                    split_bf16(hv[t][e], xh, xl);
+                    split_bf16(buf[(16 * t + 8 * half + e) * 32 + col], xh, xl);
                     bh[e] = xh;
                     bl[e] = xl;
                 }
@@ -251,25 +254,19 @@ __global__ __launch_bounds__((DV < 64 ? DV : 64) / 32 * 64, 2) void verify_mfma_
                         vf[st][e] = lv[(16 * st + 8 * (e >> 2) + 4 * half + (e & 3)) * 32 + col];
             } else {
 #pragma unroll
+                for (int t = 0; t < KS; ++t) kf[t] = load16(ku + (ko + 16 * t));
+#pragma unroll
                 for (int st = 0; st < 2; ++st)
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         vf[st][e] = vu[(uint32_t)(32 * jt + 16 * st + 8 * (e >> 2) + 4 * half + (e & 3)) * rv + ooff];
             }
-            // S^T tile: A = K rows j = 32jt + col, B = Q fragments of tile it; K comes in
-            // two halves to keep the register peak low
+            // S^T tile: A = K rows j = 32jt + col, B = Q fragments of tile it
             f32x16 s;
 #pragma unroll
             for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-            for (int hk = 0; hk < 2; ++hk) {
-                bf16x8 kf[KS / 2];
-#pragma unroll
-                for (int t = 0; t < KS / 2; ++t)
-                    kf[t] = load16(ku + (ko + 16 * (t + hk * KS / 2)));
-#pragma unroll
-                for (int t = 0; t < KS / 2; ++t) s = mfma32(kf[t], qf[t + hk * KS / 2], s);
-            }
+            for (int t = 0; t < KS; ++t) s = mfma32(kf[t], qf[t], s);
             // W^T in accumulator layout: element e pairs node i with
             // j = 32jt + 8(e/4) + 4half + e%4; non-ancestors are selected to 0
             float w[16];
@@ -334,9 +331,14 @@ static void launch_shape(const float *H0, const __bf16 *q, const __bf16 *k, cons
     const unsigned U = (unsigned)d.batch * (unsigned)d.heads;
     // G > 1: ceil(U / 8) slots of 8 units, each slot G column groups wide
     const unsigned grid = G == 1 ? U : ((U + 7) / 8) * 8 * G;
-    verify_mfma_scalar_kernel<DK, DV><<<dim3(grid), dim3(NW * 64), 0, stream>>>(
+    const int max_n = max_tree_nodes(d.flags);
+    verify_mfma_scalar_kernel<DK, DV, false><<<dim3(grid), dim3(NW * 64), 0, stream>>>(
         H0, q, k, v, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
-        (int)U);
+        (int)U, max_n);
+    if (max_n > 32)
+        verify_mfma_scalar_kernel<DK, DV, true><<<dim3(grid), dim3(NW * 64), 0, stream>>>(
+            H0, q, k, v, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
+            (int)U, max_n);
 }
 
 template <int DK>
