@@ -15,7 +15,9 @@ All inputs are resident in HBM before the timed region starts. The 8 layers hold
 The program prints one JSON line:
   - value: draft nodes verified through the whole stack per second;
   - roofline: for the dominant kernel, its algorithmic bytes per launch over its
-    average launch time (HIP events on the launch stream), against the 8 TB/s HBM peak;
+    average launch time, against the 8 TB/s HBM peak. The launch time is taken with HIP
+    events on the launch stream around each step's group of 8 launches of that kernel,
+    divided by 8 (the launches of a group run back to back);
   - cpu_baseline: the fp64 CPU oracle timed on this host on whole steps of the same
     workload.
 """
@@ -27,6 +29,38 @@ import time
 
 METRIC = "tree-verify draft nodes/s + achieved HBM GB/s (B=64, 32 heads, N=32)"
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+_CSRC = os.path.join(ROOT, "tree_speculative_decoding_02_amd", "csrc")
+# sources that determine each kernel's memory traffic
+KERNEL_SOURCES = {
+    "verify": [os.path.join(_CSRC, f) for f in ("verify_mfma.hip", "bole_device.h", "launch.h")],
+    "commit": [os.path.join(_CSRC, f) for f in ("commit.hip", "bole_device.h", "launch.h")],
+}
+# FETCH_SIZE / WRITE_SIZE record of the last counter runs (calibrated bytes per launch)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_commit_hybrid_stack_hbm_traffic.md")
+
+
+def source_hash(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch from the committed counter record, or None when there is no
+    record or the kernel's sources changed after the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            line = next(l for l in f if l.startswith("TRAFFIC_JSON "))
+        rec = json.loads(line[len("TRAFFIC_JSON "):])["kernels"][kernel]
+    except (OSError, StopIteration, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec["traffic_bytes"]
 
 
 def parse():
@@ -39,7 +73,8 @@ def parse():
                     help="minimum CPU time for the oracle baseline (whole steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain 512 MiB device copy (counter calibration)")
+                    help="also run a plain 512 MiB device copy (counter calibration), then "
+                         "time it five times")
     return ap.parse_args()
 
 
@@ -99,29 +134,31 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def step(record=None):
-        for l in range(L):
-            x = layers[l]
-            if record is not None:
-                record["v"][l][0].record(stream)
-            bole.bole_tree_verify(x["H0"], x["q"], x["k"], x["v"], x["gate"], parent, offs,
-                                  out=outs[l], stream=stream, trees_le_32=True)
-            if record is not None:
-                record["v"][l][1].record(stream)
-        for l in range(L):
-            x = layers[l]
-            if record is not None:
-                record["c"][l][0].record(stream)
-            bole.bole_commit_path(x["H0"], x["k"], x["v"], x["gate"], parent, offs, acc_idx,
-                                  acc_len, stream=stream, trees_le_32=True)
-            if record is not None:
-                record["c"][l][1].record(stream)
+    # arguments are checked and marshalled once; the timed loop only enqueues launches
+    vlaunch = [bole.bind_tree_verify(x["H0"], x["q"], x["k"], x["v"], x["gate"], parent, offs,
+                                     outs[l], stream=stream, trees_le_32=True)
+               for l, x in enumerate(layers)]
+    claunch = [bole.bind_commit_path(x["H0"], x["k"], x["v"], x["gate"], parent, offs, acc_idx,
+                                     acc_len, stream=stream, trees_le_32=True) for x in layers]
+
+    def step(rec=None):
+        # rec = (start, verify group done, commit group done): one event pair per kernel
+        # group, since an event between two launches costs the stream several microseconds
+        if rec is not None:
+            rec[0].record(stream)
+        for f in vlaunch:
+            f()
+        if rec is not None:
+            rec[1].record(stream)
+        for f in claunch:
+            f()
+        if rec is not None:
+            rec[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    records = [{"v": [(ev(), ev()) for _ in range(L)], "c": [(ev(), ev()) for _ in range(L)]}
-               for _ in range(args.steps)]
+    records = [(ev(), ev(), ev()) for _ in range(args.steps)]
     t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -132,8 +169,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     gpu_ms = t_start.elapsed_time(t_end)
-    v_ms = [r["v"][l][0].elapsed_time(r["v"][l][1]) for r in records for l in range(L)]
-    c_ms = [r["c"][l][0].elapsed_time(r["c"][l][1]) for r in records for l in range(L)]
+    # average launch duration of each kernel = its group's span / launches in the group
+    v_ms = [r[0].elapsed_time(r[1]) / L for r in records]
+    c_ms = [r[1].elapsed_time(r[2]) / L for r in records]
     ms_per_step = gpu_ms / args.steps
     nodes = wl.total_nodes
     vb, cb = verify_bytes(wl), commit_bytes(wl)
@@ -173,7 +211,7 @@ def main():
                    "d_v": wl.d_v, "nodes_per_tree": 32, "parallelism": "single_gpu"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": kd["GB_s"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["GB_s"] / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": recorded_traffic(dom)},
         "kernels": kernels,
         "hbm_GB_s_step": L * (vb + cb) / (ms_per_step * 1e6),
         "wall_ms_per_step": 1e3 * wall / args.steps,
@@ -189,7 +227,15 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = {"read": 4 * n, "write": 4 * n}
+        # the same copy timed: a practical read+write streaming rate for comparison
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        result["copy_calibration"] = {"read_bytes": 4 * n, "write_bytes": 4 * n,
+                                      "GB_s": 5 * 8 * n / (a.elapsed_time(b) * 1e6)}
         del src, dst
 
     if not args.no_cpu_baseline:

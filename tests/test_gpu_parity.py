@@ -281,6 +281,33 @@ def test_determinism(bole):
     np.testing.assert_array_equal(Ha, Hb)
 
 
+def test_bound_launchers_match_calls(bole):
+    """bind_tree_verify / bind_commit_path launch exactly what the plain calls launch:
+    bit-identical outputs, and a bound commit called twice applies the path twice."""
+    wl = W.make_config(2)
+    t = to_dev(wl)
+    ref, _ = gpu_verify(bole, t)
+    out = torch.empty((t["q"].shape[0], t["H0"].shape[1], t["H0"].shape[3]),
+                      dtype=torch.float32, device=dev())
+    f = bole.bind_tree_verify(t["H0"], t["q"], t["k"], t["v"], t["gate"], t["parent"],
+                              t["offs"], out)
+    f()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.double().cpu().numpy(), ref)
+    H1, _, _ = gpu_commit(bole, t)
+    H = t["H0"].clone()
+    c = bole.bind_commit_path(H, t["k"], t["v"], t["gate"], t["parent"], t["offs"],
+                              t["acc_idx"], t["acc_len"])
+    c()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(H.double().cpu().numpy(), H1)
+    t2 = dict(t, H0=H.clone())
+    H2, _, _ = gpu_commit(bole, t2)
+    c()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(H.double().cpu().numpy(), H2)
+
+
 def test_resume_verify_commit_verify(bole):
     """verify(next tree) on the GPU-committed state equals the oracle's verify of the
     accepted path with the next tree hung below it, on the old state."""

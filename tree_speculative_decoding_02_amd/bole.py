@@ -154,6 +154,64 @@ def bole_tree_verify(H0, q, k, v, gate, parent, node_offsets, out=None, tree_sta
     return out
 
 
+class _Bound:
+    """A launch whose arguments were checked and marshalled once; calling it enqueues the
+    same C call again (the tensors are kept alive by the object)."""
+
+    def __init__(self, fn, what, args, keep):
+        self._fn, self._what, self._args, self._keep = fn, what, args, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != BOLE_OK:
+            _check(st, self._what)
+
+
+def bind_tree_verify(H0, q, k, v, gate, parent, node_offsets, out, tree_status=None,
+                     stream=None, force_generic=False, trees_le_32=False):
+    """Same checks as bole_tree_verify, done once; returns a callable that launches the
+    verify on these buffers each time it is called (for tight launch loops)."""
+    B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
+    _need(q, "q", k.dtype, H0.device)
+    _need(out, "out", torch.float32, H0.device)
+    if tuple(q.shape) != tuple(k.shape) or tuple(out.shape) != (T, Hh, d_v):
+        raise ValueError("q must have the shape of k and out must be [T, H, d_v]")
+    if tree_status is not None:
+        _need(tree_status, "tree_status", torch.int32, H0.device)
+        if tree_status.numel() < B:
+            raise ValueError("tree_status needs B entries")
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, force_generic, trees_le_32)
+    args = (_ptr(H0), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(parent), _ptr(node_offsets),
+            _ptr(out), ctypes.byref(dims), _ptr(tree_status), _stream(stream))
+    return _Bound(lib.bole_tree_verify, "bole_tree_verify", args,
+                  (H0, q, k, v, gate, parent, node_offsets, out, tree_status, dims))
+
+
+def bind_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepted_len,
+                     path_nodes=None, tree_status=None, stream=None, trees_le_32=False):
+    """Same checks as bole_commit_path, done once; returns a callable that commits into
+    H0 in place each time it is called."""
+    B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
+    _need(accepted_idx, "accepted_idx", torch.int32, H0.device)
+    _need(accepted_len, "accepted_len", torch.int32, H0.device)
+    if accepted_idx.dim() != 2 or accepted_idx.shape[0] != B or tuple(accepted_len.shape) != (B,):
+        raise ValueError("accepted_idx must be [B, max_path] and accepted_len [B]")
+    max_path = accepted_idx.shape[1]
+    for t, name in ((path_nodes, "path_nodes"), (tree_status, "tree_status")):
+        if t is not None:
+            _need(t, name, torch.int32, H0.device)
+    if path_nodes is not None and tuple(path_nodes.shape) != (B, max_path):
+        raise ValueError("path_nodes must be [B, max_path]")
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, max_path, trees_le_32=trees_le_32)
+    f = bole_factors_t(k.data_ptr(), v.data_ptr(), gate.data_ptr(), parent.data_ptr(),
+                       node_offsets.data_ptr())
+    args = (_ptr(H0), ctypes.byref(f), _ptr(accepted_idx), _ptr(accepted_len),
+            ctypes.byref(dims), _ptr(path_nodes), _ptr(tree_status), _stream(stream))
+    return _Bound(lib.bole_commit_path, "bole_commit_path", args,
+                  (H0, k, v, gate, parent, node_offsets, accepted_idx, accepted_len, path_nodes,
+                   tree_status, dims, f))
+
+
 def bole_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepted_len,
                      path_nodes=None, tree_status=None, stream=None, trees_le_32=False):
     """Commits each tree's accepted path into H0 in place; returns H0."""
