@@ -190,6 +190,9 @@ EDGE = [
     ("extreme_gates_scalar", dict(batch=4, heads=2, d_k=128, d_v=64, sizes=[64, 64, 30, 10], kind="deep", gate_shift=6.0, max_path=64)),
     ("extreme_gates_vector", dict(batch=3, heads=2, d_k=64, d_v=64, sizes=[64, 20, 64], kind="deep", vector_gate=True, gate_shift=6.0, max_path=64)),
     ("single_nodes", dict(batch=6, heads=5, d_k=128, d_v=64, sizes=[1] * 6)),
+    ("dk128_dv32", dict(batch=4, heads=3, d_k=128, d_v=32)),
+    ("dk64_dv64", dict(batch=4, heads=3, d_k=64, d_v=64, sizes=[32, 17, 16, 5])),
+    ("trees_up_to_32", dict(batch=8, heads=4, d_k=128, d_v=64, sizes=[16, 15, 9, 3, 17, 24, 31, 32])),
 ]
 
 
@@ -198,6 +201,27 @@ def test_edge_parity(bole, name, kw):
     wl = W.make_random(zlib.crc32(name.encode()) % 10000, **kw)
     rep = check_workload(bole, wl)
     print(f"{name}: " + ", ".join(f"{k} {v:.2e}" for k, v in rep.items()))
+
+
+def test_misaligned_pointers_use_the_generic_kernel(bole):
+    """q and v one element off a 16-byte boundary: the matrix-core kernels need 16-byte
+    rows, so the call takes the vector-ALU kernel, bit-identical to a forced generic
+    call on aligned copies, and within the bf16 bar of the oracle."""
+    wl = W.make_random(77, batch=3, heads=2, d_k=128, d_v=64)
+    t = to_dev(wl)
+
+    def shifted(x):
+        y = torch.empty(x.numel() + 1, dtype=x.dtype, device=x.device)[1:].view(x.shape)
+        y.copy_(x)
+        assert y.data_ptr() % 16 != 0
+        return y
+
+    a, sa = gpu_verify(bole, dict(t, q=shifted(t["q"]), v=shifted(t["v"])))
+    b, sb = gpu_verify(bole, t, force_generic=True)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(sa, sb)
+    ref, _, _, _, _ = oracle_layer(wl)
+    assert rel_err_rows(a, ref) <= TOL[torch.bfloat16]
 
 
 def test_bad_trees(bole):

@@ -61,7 +61,7 @@ bole_status_t bole_tree_verify(const float *H0, const void *q, const void *k, co
                               parent == nullptr || out == nullptr))
         return BOLE_ERR_INVALID_VALUE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (bole::verify_mfma_applies(d, q, k))
+    if (bole::verify_mfma_applies(d, H0, q, k, v, out))
         return from_hip(bole::launch_verify_mfma(H0, q, k, v, gate, parent, node_offsets, out, d,
                                                  tree_status, s));
     return from_hip(bole::launch_verify_generic(H0, q, k, v, gate, parent, node_offsets, out, d,

@@ -20,7 +20,8 @@ hipError_t launch_verify_generic(const float *H0, const void *q, const void *k, 
                                  int32_t *tree_status, hipStream_t stream);
 
 // True when the matrix-core verify kernel covers this request.
-bool verify_mfma_applies(const bole_dims_t &d, const void *q, const void *k);
+bool verify_mfma_applies(const bole_dims_t &d, const void *H0, const void *q, const void *k,
+                         const void *v, const void *out);
 
 hipError_t launch_verify_mfma(const float *H0, const void *q, const void *k, const void *v,
                               const float *gate, const int32_t *parent,
