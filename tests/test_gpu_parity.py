@@ -193,6 +193,10 @@ EDGE = [
     ("dk128_dv32", dict(batch=4, heads=3, d_k=128, d_v=32)),
     ("dk64_dv64", dict(batch=4, heads=3, d_k=64, d_v=64, sizes=[32, 17, 16, 5])),
     ("trees_up_to_32", dict(batch=8, heads=4, d_k=128, d_v=64, sizes=[16, 15, 9, 3, 17, 24, 31, 32])),
+    # long accepted paths: commit stages the path's factors in several rounds
+    ("long_paths_bf16", dict(batch=4, heads=2, d_k=128, d_v=64, sizes=[64, 48, 40, 33], kind="chain", max_path=64)),
+    ("long_paths_fp32", dict(batch=4, heads=2, d_k=128, d_v=64, sizes=[64, 40, 24, 20], kind="chain", factor_dtype=torch.float32, max_path=64)),
+    ("long_paths_vector", dict(batch=4, heads=2, d_k=128, d_v=128, sizes=[64, 48, 30, 12], kind="chain", vector_gate=True, max_path=64)),
 ]
 
 

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
         for (int s = 0; s < PER; ++s) {
             const int g = s * kCommitThreads + tid;
             if (g < G) {
-                if (W == 4) {
+                if constexpr (W == 4) {
                     const float4 t = *reinterpret_cast<const float4 *>(Hu + (size_t)g * 4);
                     reg[s][0] = t.x; reg[s][1] = t.y; reg[s][2] = t.z; reg[s][3] = t.w;
                 } else {
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
             for (int s = 0; s < PER; ++s) {
                 const int g = g0 + s * kCommitThreads + tid;
                 if (g < G) {
-                    if (W == 4) {
+                    if constexpr (W == 4) {
                         const float4 t = *reinterpret_cast<const float4 *>(Hu + (size_t)g * 4);
                         reg[s][0] = t.x; reg[s][1] = t.y; reg[s][2] = t.z; reg[s][3] = t.w;
                     } else {
@@ -173,13 +173,207 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
         for (int s = 0; s < PER; ++s) {
             const int g = g0 + s * kCommitThreads + tid;
             if (g < G) {
-                if (W == 4) {
+                if constexpr (W == 4) {
                     *reinterpret_cast<float4 *>(Hu + (size_t)g * 4) =
                         make_float4(reg[s][0], reg[s][1], reg[s][2], reg[s][3]);
                 } else {
                     Hu[g] = reg[s][0];
                 }
             }
+        }
+    }
+}
+
+// Streaming commit for the common shapes: d_v/4 a power of two that divides 256 (so a
+// thread's state rows are r0 + 16s-style strides and its columns are fixed), 16-byte
+// factor rows. Two dependent rounds of memory instead of three:
+//   round 1: tree offsets and path length (scalar), and the path indices the thread's
+//            factor chunks and validation need (per lane);
+//   round 2: the state slice (non-temporal), the path's factor rows as 16-byte chunks,
+//            the tree's parent links and the path's scalar gates, all at once.
+// Validation then runs on values already in registers, the factors go to LDS as fp32,
+// and the state is updated in registers and stored (non-temporal). Up to 16 path nodes
+// are staged per round; longer paths stage the rest afterwards.
+constexpr int kStageNodes = 16;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <typename TF, bool VEC>
+__global__ __launch_bounds__(kCommitThreads) void commit_stream_kernel(
+    float *__restrict__ H0, const TF *__restrict__ k, const TF *__restrict__ v,
+    const float *__restrict__ gate, const int32_t *__restrict__ parent,
+    const int32_t *__restrict__ node_offsets, const int32_t *__restrict__ accepted_idx,
+    const int32_t *__restrict__ accepted_len, int32_t *__restrict__ path_nodes,
+    int32_t *__restrict__ tree_status, int H, int DK, int DV, int T, int max_path, int max_n,
+    int gpr_log2) {
+    constexpr int E = 16 / sizeof(TF);   // factor elements per 16-byte chunk
+    constexpr int PER = kRegFloats / 4;  // float4 state groups per thread per pass
+    __shared__ int s_row[kMaxTree];
+    __shared__ float s_a[kMaxTree];
+    __shared__ int s_len;
+    extern __shared__ __attribute__((aligned(16))) float s_f[];  // [kStageNodes][FW]: k, (gate), v rows
+    const int unit = blockIdx.x;
+    const int b = unit / H, h = unit - b * H;
+    const int tid = threadIdx.x;
+    const int FW = (VEC ? 2 : 1) * DK + DV;
+    const int CK = DK / E, CG = VEC ? DK / 4 : 0, CV = DV / E;
+    const int CPN = CK + CG + CV;        // chunks per path node
+    float *Hu = H0 + (size_t)unit * DK * DV;
+    const int G = DK * DV / 4;           // float4 groups of the state
+
+    // ---- round 1
+    const TreeRange tr = tree_range(node_offsets, b, T, max_n);
+    const int len_raw = accepted_len[b];
+    const int m0 = tid / CPN, m1 = (tid + kCommitThreads) / CPN;  // nodes of my two chunks
+    const int32_t *acc_b = accepted_idx + (size_t)b * max_path;
+    const int x0 = m0 < max_path ? acc_b[m0] : 0;
+    const int x1 = m1 < max_path ? acc_b[m1] : 0;
+    const int xl = (tid < 64 && tid < max_path) ? acc_b[tid] : -1;
+
+    // ---- round 2
+    const bool likely = tr.status == BOLE_TREE_OK && len_raw > 0 && len_raw <= max_path &&
+                        len_raw <= tr.n;
+    const int n = tr.n;
+    f32x4v reg[PER];
+    const int rs = kCommitThreads >> gpr_log2;             // state rows between groups
+    const int r0 = tid >> gpr_log2;                        // row of group 0
+    const int cc = (tid & ((1 << gpr_log2) - 1)) * 4;      // first column (fixed)
+    if (likely) {
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int g = s * kCommitThreads + tid;
+            if (g < G) reg[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(Hu) + g);
+        }
+    }
+    // factor chunks of the first S1 path nodes, two chunks per thread at most (clamped
+    // rows: validated below); later nodes are staged kStageNodes at a time
+    const int S1 = min(kStageNodes, 2 * kCommitThreads / CPN);
+    const int L0 = likely ? min(len_raw, S1) : 0;
+    auto chunk_src = [&](int c, int x) -> const void * {
+        const int m = c / CPN, part = c - m * CPN;
+        (void)m;
+        const size_t row = (size_t)(tr.lo + min(max(x, 0), n - 1)) * H + h;
+        if (part < CK) return k + row * DK + part * E;
+        if (VEC && part < CK + CG) return gate + row * DK + (part - CK) * 4;
+        return v + row * DV + (part - CK - CG) * E;
+    };
+    uint4 raw0 = {0, 0, 0, 0}, raw1 = {0, 0, 0, 0};
+    const int c0 = tid, c1 = tid + kCommitThreads;
+    if (c0 < L0 * CPN) raw0 = *reinterpret_cast<const uint4 *>(chunk_src(c0, x0));
+    if (c1 < L0 * CPN) raw1 = *reinterpret_cast<const uint4 *>(chunk_src(c1, x1));
+
+    // validation by wavefront 0 (lane = tree node / path position)
+    if (tid < 64) {
+        int st = tr.status;
+        int len = 0, x = -1;
+        float a = 1.f;
+        if (st == BOLE_TREE_OK && n > 0) {
+            const int p = tid < n ? parent[tr.lo + tid] : -1;
+            const bool len_ok = len_raw >= 0 && len_raw <= max_path;
+            const int xr = (len_ok && tid < len_raw) ? xl : -1;
+            if (!VEC && len_ok && tid < len_raw)
+                a = gate[(size_t)(tr.lo + min(max(xr, 0), n - 1)) * H + h];
+            if (__any(tid < n && (p < -1 || p >= tid))) {
+                st = BOLE_TREE_BAD_PARENT;
+            } else if (!len_ok) {
+                st = BOLE_TREE_BAD_PATH;
+            } else {
+                len = len_raw;
+                x = xr;
+                const int px = __shfl(p, (x >= 0 && x < n) ? x : 0, 64);
+                const int prev_raw = __shfl(x, tid > 0 ? tid - 1 : 0, 64);
+                const int prev = tid == 0 ? -1 : prev_raw;
+                const bool bad = tid < len && (x < 0 || x >= n || px != prev);
+                if (__any(bad)) st = BOLE_TREE_BAD_PATH;
+            }
+        } else if (st == BOLE_TREE_OK) {
+            if (len_raw != 0) st = BOLE_TREE_BAD_PATH;  // empty tree: only L = 0 is valid
+        }
+        const bool ok = st == BOLE_TREE_OK;
+        const int row = (ok && tid < len) ? tr.lo + x : -1;
+        s_row[tid] = row;
+        s_a[tid] = a;
+        if (tid == 0) s_len = ok ? len : 0;
+        if (h == 0) {
+            if (tid == 0 && tree_status) tree_status[b] = st;
+            if (path_nodes && tid < max_path) path_nodes[(size_t)b * max_path + tid] = row;
+        }
+    }
+    // factors -> LDS as fp32
+    auto put = [&](int c, const uint4 &raw) {
+        const int m = c / CPN, part = c - m * CPN;
+        float *dst = s_f + m * FW;
+        if (part < CK) {
+            dst += part * E;
+        } else if (VEC && part < CK + CG) {
+            dst += DK + (part - CK) * 4;
+            *reinterpret_cast<uint4 *>(dst) = raw;
+            return;
+        } else {
+            dst += (VEC ? 2 : 1) * DK + (part - CK - CG) * E;
+        }
+        if (E == 8) {
+            const __bf16 *e = reinterpret_cast<const __bf16 *>(&raw);
+            *reinterpret_cast<float4 *>(dst) = make_float4(to_f32(e[0]), to_f32(e[1]), to_f32(e[2]), to_f32(e[3]));
+            *reinterpret_cast<float4 *>(dst + 4) = make_float4(to_f32(e[4]), to_f32(e[5]), to_f32(e[6]), to_f32(e[7]));
+        } else {
+            *reinterpret_cast<uint4 *>(dst) = raw;
+        }
+    };
+    if (c0 < L0 * CPN) put(c0, raw0);
+    if (c1 < L0 * CPN) put(c1, raw1);
+    __syncthreads();
+    const int len = s_len;
+    if (len == 0) return;
+
+    for (int g0 = 0; g0 < G; g0 += kCommitThreads * PER) {
+        const int rbase = (g0 >> gpr_log2) + r0;
+        if (g0 > 0) {
+#pragma unroll
+            for (int s = 0; s < PER; ++s) {
+                const int g = g0 + s * kCommitThreads + tid;
+                if (g < G) reg[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(Hu) + g);
+            }
+        }
+        for (int m0s = 0; m0s < len;) {
+            const int mc = m0s == 0 ? min(S1, len) : min(kStageNodes, len - m0s);
+            if (m0s > 0 || g0 > 0) {
+                // stage path nodes m0s .. m0s+mc-1 (the first group is staged above)
+                __syncthreads();
+                for (int c = tid; c < mc * CPN; c += kCommitThreads) {
+                    const int m = c / CPN, part = c - m * CPN;
+                    const size_t row = (size_t)s_row[m0s + m] * H + h;
+                    const void *src;
+                    if (part < CK) src = k + row * DK + part * E;
+                    else if (VEC && part < CK + CG) src = gate + row * DK + (part - CK) * 4;
+                    else src = v + row * DV + (part - CK - CG) * E;
+                    put(c, *reinterpret_cast<const uint4 *>(src));
+                }
+                __syncthreads();
+            }
+            for (int mm = 0; mm < mc; ++mm) {
+                const float *fk = s_f + mm * FW;
+                const float *fg = fk + DK;
+                const float4 vv = *reinterpret_cast<const float4 *>(fk + (VEC ? 2 : 1) * DK + cc);
+                const float a = s_a[m0s + mm];
+#pragma unroll
+                for (int s = 0; s < PER; ++s) {
+                    const int r = rbase + s * rs;
+                    if (g0 + s * kCommitThreads + tid < G) {
+                        const float kr = fk[r];
+                        const float sr = VEC ? fg[r] : a;
+                        reg[s].x = sr * reg[s].x + kr * vv.x;
+                        reg[s].y = sr * reg[s].y + kr * vv.y;
+                        reg[s].z = sr * reg[s].z + kr * vv.z;
+                        reg[s].w = sr * reg[s].w + kr * vv.w;
+                    }
+                }
+            }
+            m0s += mc;
+        }
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int g = g0 + s * kCommitThreads + tid;
+            if (g < G) __builtin_nontemporal_store(reg[s], reinterpret_cast<f32x4v *>(Hu) + g);
         }
     }
 }
@@ -192,7 +386,19 @@ static void launch_w(float *H0, const bole_factors_t &f, const int32_t *accepted
     const size_t lds = sizeof(float) * kPathChunk * ((VEC ? 2 : 1) * d.d_k + d.d_v);
     const TF *k = static_cast<const TF *>(f.k), *v = static_cast<const TF *>(f.v);
     const bool vec4 = (d.d_v % 4 == 0) && (reinterpret_cast<uintptr_t>(H0) % 16 == 0);
-    if (vec4)
+    // streaming kernel: d_v/4 a power of two dividing the block, 16-byte factor rows
+    const int gpr = d.d_v / 4;
+    constexpr int E = 16 / sizeof(TF);
+    const uintptr_t fa = reinterpret_cast<uintptr_t>(f.k) | reinterpret_cast<uintptr_t>(f.v) |
+                         (VEC ? reinterpret_cast<uintptr_t>(f.gate) : 0);
+    if (vec4 && gpr > 0 && (gpr & (gpr - 1)) == 0 && kCommitThreads % gpr == 0 &&
+        d.d_k % E == 0 && d.d_v % E == 0 && fa % 16 == 0) {
+        const size_t slds = sizeof(float) * kStageNodes * ((VEC ? 2 : 1) * d.d_k + d.d_v);
+        commit_stream_kernel<TF, VEC><<<grid, block, slds, stream>>>(
+            H0, k, v, f.gate, f.parent, f.node_offsets, accepted_idx, accepted_len, path_nodes,
+            tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags),
+            __builtin_ctz((unsigned)gpr));
+    } else if (vec4)
         commit_kernel<TF, VEC, 4><<<grid, block, lds, stream>>>(
             H0, k, v, f.gate, f.parent, f.node_offsets, accepted_idx, accepted_len, path_nodes,
             tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags));
