@@ -33,7 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 _CSRC = os.path.join(ROOT, "tree_speculative_decoding_02_amd", "csrc")
 # sources that determine each kernel's memory traffic
 KERNEL_SOURCES = {
-    "verify": [os.path.join(_CSRC, f) for f in ("verify_mfma.hip", "bole_device.h", "launch.h")],
+    "verify": [os.path.join(_CSRC, f) for f in ("verify_mfma.hip", "mfma_util.h", "bole_device.h",
+                                                  "launch.h")],
     "commit": [os.path.join(_CSRC, f) for f in ("commit.hip", "bole_device.h", "launch.h")],
 }
 # FETCH_SIZE / WRITE_SIZE record of the last counter runs (calibrated bytes per launch)

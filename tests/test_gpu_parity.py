@@ -228,13 +228,14 @@ def test_misaligned_pointers_use_the_generic_kernel(bole):
     assert rel_err_rows(a, ref) <= TOL[torch.bfloat16]
 
 
-def test_bad_trees(bole):
+@pytest.mark.parametrize("vector_gate", [False, True], ids=["scalar_gate", "vector_gate"])
+def test_bad_trees(bole, vector_gate):
     """Device-detected errors: status codes match the oracle bit for bit, bad-parent
     rows are NaN, bad-size rows untouched, committed states of bad trees unchanged."""
     sizes = [3, 2, 3, 2, 1]
     parent = np.array([-1, 0, 0,    -1, 1,    -1, 0, 1,    -1, 0,    -1], np.int32)
     offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
-    wl = W.make_random(5, batch=5, heads=2, d_k=128, d_v=64, sizes=sizes)
+    wl = W.make_random(5, batch=5, heads=2, d_k=128, d_v=64, sizes=sizes, vector_gate=vector_gate)
     wl.parent = parent
     wl.node_offsets = offs
     # tree 2 commits a path that is not a chain, tree 4 a too-long path
@@ -264,13 +265,14 @@ def test_bad_trees(bole):
     assert rel_err_states(H, Href) <= 2e-3
 
     # bad sizes: a 65-node tree and unordered offsets; nothing written for them
-    wl2 = W.make_random(6, batch=3, heads=2, d_k=128, d_v=64, sizes=[65, 3, 4], kind="star")
+    wl2 = W.make_random(6, batch=3, heads=2, d_k=128, d_v=64, sizes=[65, 3, 4], kind="star",
+                        vector_gate=vector_gate)
     t2 = to_dev(wl2)
     for path in ("auto", "generic"):
         out, gst = gpu_verify(bole, t2, force_generic=(path == "generic"))
         _, ost = oracle.verify_serial(wl2.layers[0].H0, wl2.layers[0].q, wl2.layers[0].k,
                                       wl2.layers[0].v, wl2.layers[0].gate, wl2.parent,
-                                      wl2.node_offsets, False)
+                                      wl2.node_offsets, vector_gate)
         assert gst.tolist() == ost.tolist() == [1, 0, 0]
         assert (out[:65] == 12345.0).all()
     t2["offs"] = torch.tensor([0, 65, 60, 72], dtype=torch.int32, device=dev())

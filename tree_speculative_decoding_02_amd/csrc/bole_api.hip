@@ -64,6 +64,9 @@ bole_status_t bole_tree_verify(const float *H0, const void *q, const void *k, co
     if (bole::verify_mfma_applies(d, H0, q, k, v, out))
         return from_hip(bole::launch_verify_mfma(H0, q, k, v, gate, parent, node_offsets, out, d,
                                                  tree_status, s));
+    if (bole::verify_vec_applies(d, H0, q, k, v, gate, out))
+        return from_hip(bole::launch_verify_vec(H0, q, k, v, gate, parent, node_offsets, out, d,
+                                                tree_status, s));
     return from_hip(bole::launch_verify_generic(H0, q, k, v, gate, parent, node_offsets, out, d,
                                                 tree_status, s));
 }
