@@ -15,13 +15,21 @@
 //    LG_i - LG_j <= 0, so no factor can overflow.
 //
 // One 256-thread workgroup per (sequence, head, 64-column group), trees of up to 64
-// nodes. Everything the tree needs is staged in LDS by DMA (the H_0 column slice, the
-// gate, K and V rows); wavefront 0 builds the topology. Then:
-//  1. gate -> log2 -> root-first cumulative sums LG, one tree level at a time;
-//  2. pair weights w_ij for every ancestor pair, four lanes per node;
-//  3. H_0 term, one 16-node tile per wavefront (v_mfma_f32_16x16x32_bf16), B operands
-//     read from LDS as 16-byte rows (lane (n, g) takes columns 4n .. 4n+3);
-//  4. the intra term accumulated into the same registers, the rows stored.
+// nodes. Every input is staged through registers with plain 16-byte loads issued in the
+// order of use (parent, gate, K, query channels, Q fragments, then H_0 and V), so the
+// H_0 and V loads stay in flight while the first phases compute, and each phase waits
+// only for what it reads:
+//  1. wavefront 0 builds the topology; the gate and K rows go to LDS;
+//  2. gate -> log2 -> root-first cumulative sums LG by pointer doubling: each thread
+//     keeps its own entries in registers, and round r adds the sum held at the node's
+//     2^r-th ancestor (ceil(log2 depth) rounds, one barrier pair each);
+//  3. pair weights w_ij for every ancestor pair, four lanes per node; each wavefront
+//     then builds its decayed-query operands (hi + lo) for one 16-node tile;
+//  4. H_0 and V go to LDS, H_0 reusing the space of the LG and K tables;
+//  5. H_0 term (v_mfma_f32_16x16x32_bf16, B operands read as 16-byte rows: lane (n, g)
+//     takes columns CPL*n ..), the intra term accumulated into the same registers, and
+//     the rows stored.
+// About 72 KB of LDS at d_k = 128, so two workgroups share a CU.
 #include "bole_device.h"
 #include "launch.h"
 #include "mfma_util.h"
@@ -42,15 +50,26 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     constexpr int G = DV / CW;              // column groups per unit
     constexpr int KT = DK / 32;             // k-steps of the 16x16x32 products
     constexpr int CH = DK / 4;              // channels per lane in the pair weights
+    // 16-byte pieces per thread of each staged table
+    constexpr int GP = DK / 4, GPT = N * GP / kVecThreads;    // gate rows, fp32
+    constexpr int KP = DK / 8, KPT = N * KP / kVecThreads;    // K rows, bf16
+    constexpr int HP = CW / 4, HPT = DK * HP / kVecThreads;   // H_0 slice, fp32
+    constexpr int VP = CW / 8, VPT = N * VP / kVecThreads;    // V rows, bf16
+    static_assert(GPT >= 1 && KPT >= 1 && HPT >= 1 && VPT >= 1, "staging split");
     typedef float hvec __attribute__((ext_vector_type(CPL)));
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
-    __shared__ __attribute__((aligned(16))) float s_h0[DK * CW];  // row d at [CW d]
-    __shared__ __attribute__((aligned(16))) float s_lg[N * DK];   // gate -> LG, node i at [DK i]
-    __shared__ __attribute__((aligned(16))) __bf16 s_k[N * DK];   // K rows
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    // phase A: LG (N x DK fp32) then K (N x DK bf16); phase B: the H_0 slice (DK x CW fp32)
+    constexpr int kBig = (N * DK + N * DK / 2) > DK * CW ? (N * DK + N * DK / 2) : DK * CW;
+    __shared__ __attribute__((aligned(16))) float s_big[kBig];
     __shared__ __attribute__((aligned(16))) __bf16 s_v[N * CW];   // V rows, the group's columns
     __shared__ float s_w[N * N];                                   // w_ij at [N i + j]
     __shared__ uint64_t s_mask[N];
-    __shared__ int s_par[N], s_depth[N], s_info[2];                // info: status, max depth
+    __shared__ int s_anc[6][N];                                    // 2^r-th ancestor (or -1)
+    __shared__ int s_info[2];                                      // status, doubling rounds
+    float *s_lg = s_big;
+    __bf16 *s_k = reinterpret_cast<__bf16 *>(s_big + N * DK);
+    float *s_h0 = s_big;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     int unit, cg;
@@ -85,65 +104,80 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     const __bf16 *vu = v + (size_t)lo * rv + (size_t)h * DV + c0;
     float *ou = out + (size_t)lo * rv + (size_t)h * DV + c0;
     const float *hu = H0 + (size_t)unit * DK * DV + c0;
-
-    // ---- 1. stage everything by DMA; each wavefront issues every fourth instruction.
-    // A table of R rows x P 16-byte pieces moves 64/P rows per instruction; lane l takes
-    // row (64/P)s + l/P, piece l%P. Node rows past the tree repeat its last row.
-    {
-        constexpr int HP = CW / 4;  // H_0: fp32 pieces per row
-        for (int s = wave; s < DK * HP / 64; s += 4) {
-            const int r = (64 / HP) * s + lane / HP;
-            dma16_stream(hu + ((uint32_t)r * DV + 4 * (lane % HP)), s_h0 + 256 * s);
-        }
-        constexpr int GP = DK / 4;  // gate: fp32 pieces per row
-        for (int s = wave; s < N * GP / 64; s += 4) {
-            const int r = (64 / GP) * s + lane / GP;
-            dma16_stream(gu + ((uint32_t)min(r, last) * rq + 4 * (lane % GP)), s_lg + 256 * s);
-        }
-        constexpr int KP = DK / 8;  // K: bf16 pieces per row
-        for (int s = wave; s < N * KP / 64; s += 4) {
-            const int r = (64 / KP) * s + lane / KP;
-            dma16_stream(ku + ((uint32_t)min(r, last) * rq + 8 * (lane % KP)), s_k + 512 * s);
-        }
-        constexpr int VP = CW / 8;  // V: bf16 pieces per row
-        for (int s = wave; s < N * VP / 64; s += 4) {
-            const int r = (64 / VP) * s + lane / VP;
-            dma16_stream(vu + ((uint32_t)min(r, last) * rv + 8 * (lane % VP)), s_v + 512 * s);
-        }
-    }
-    // Q fragments of the H_0 term: wavefront = node tile, lane (n, g): row 16*wave + n,
-    // channels 32t + 8g .. +7
     const int n16 = lane & 15, g4 = lane >> 4;
-    bf16x8 qf[KT];
+    const int pi = tid >> 2, psub = tid & 3;  // pair-weight node and channel quarter
+
+    // ---- issue every load, in order of use. Piece P = tid + 256u of a table with PP
+    // pieces per row is row P / PP, piece P % PP (rows past the tree repeat its last row).
+    const int p_raw = wave == 0 ? parent[lo + min(lane, last)] : -1;
+    u32x4 rg[GPT], rk[KPT], rh[HPT], rvv[VPT];
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
-        qf[t] = load16_stream(qu + ((uint32_t)min(16 * wave + n16, last) * rq + 32 * t + 8 * g4));
-    // query channels of the pair weights: node tid/4, channels CH*(tid%4) .. +CH-1
-    const int pi = tid >> 2, psub = tid & 3;
-    bf16x8 qp[CH / 8];
+    for (int u = 0; u < GPT; ++u) {
+        const int P = tid + kVecThreads * u;
+        rg[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+            gu + ((uint32_t)min(P / GP, last) * rq + 4 * (P % GP))));
+    }
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        const int P = tid + kVecThreads * u;
+        rk[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+            ku + ((uint32_t)min(P / KP, last) * rq + 8 * (P % KP))));
+    }
+    bf16x8 qp[CH / 8];  // query channels CH*psub .. of node pi
 #pragma unroll
     for (int u = 0; u < CH / 8; ++u)
         qp[u] = load16(qu + ((uint32_t)min(pi, last) * rq + CH * psub + 8 * u));
-
-    // ---- topology, wavefront 0
-    if (wave == 0) {
-        const int p = parent[lo + min(lane, last)];
-        const WaveTopo topo = wave_topology_p(p, n);
-        s_mask[lane] = topo.mask;
-        s_par[lane] = lane < n ? p : -1;
-        s_depth[lane] = topo.depth;
-        // max depth over the wave: a butterfly of maxima
-        int md = topo.depth;
+    bf16x8 qf[KT];      // Q fragments: row 16*wave + n, channels 32t + 8g .. +7
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) md = max(md, __shfl_xor(md, o, 64));
+    for (int t = 0; t < KT; ++t)
+        qf[t] = load16(qu + ((uint32_t)min(16 * wave + n16, last) * rq + 32 * t + 8 * g4));
+#pragma unroll
+    for (int u = 0; u < HPT; ++u) {
+        const int P = tid + kVecThreads * u;
+        rh[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+            hu + ((uint32_t)(P / HP) * DV + 4 * (P % HP))));
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        const int P = tid + kVecThreads * u;
+        rvv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+            vu + ((uint32_t)min(P / VP, last) * rv + 8 * (P % VP))));
+    }
+
+    // ---- 1. topology and doubling pointers (wavefront 0); log2 of the gate rows and
+    // the K rows to LDS; W cleared
+    if (wave == 0) {
+        const WaveTopo topo = wave_topology_p(p_raw, n);
+        s_mask[lane] = topo.mask;
+        int a = (lane < n && !topo.bad) ? p_raw : -1;
+        int rounds = 0;
+        for (int r = 0; r < 6 && __any(a >= 0); ++r) {
+            s_anc[r][lane] = a;
+            rounds = r + 1;
+            const int up = __shfl(a, a >= 0 ? a : lane, 64);
+            a = a >= 0 ? up : -1;
+        }
         if (lane == 0) {
             s_info[0] = topo.bad;
-            s_info[1] = md;
+            s_info[1] = rounds;
         }
         if (writer) tree_status[b] = topo.bad;
     }
+    float4 lgv[GPT];  // this thread's gate entries: row (tid + 256u) / GP, channels 4*(.. % GP)
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) {
+        const int P = tid + kVecThreads * u;
+        const float4 x = __builtin_bit_cast(float4, rg[u]);
+        lgv[u] = make_float4(__builtin_amdgcn_logf(x.x), __builtin_amdgcn_logf(x.y),
+                             __builtin_amdgcn_logf(x.z), __builtin_amdgcn_logf(x.w));
+        *reinterpret_cast<float4 *>(s_lg + (P / GP) * DK + 4 * (P % GP)) = lgv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        const int P = tid + kVecThreads * u;
+        *reinterpret_cast<u32x4 *>(s_k + (P / KP) * DK + 8 * (P % KP)) = rk[u];
+    }
     for (int e = tid; e < N * N; e += kVecThreads) s_w[e] = 0.f;
-    wait_all_memory();
     __syncthreads();
 
     if (s_info[0] != BOLE_TREE_OK) {
@@ -152,14 +186,27 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         return;
     }
 
-    // ---- 2. LG: log2 of every gate entry of the tree, then root-first sums by level
-    for (int e = tid; e < n * DK; e += kVecThreads) s_lg[e] = __builtin_amdgcn_logf(s_lg[e]);
-    __syncthreads();
-    const int max_depth = s_info[1];
-    for (int d = 2; d <= max_depth; ++d) {
-        for (int e = tid; e < n * DK; e += kVecThreads) {
-            const int i = e / DK;
-            if (s_depth[i] == d) s_lg[e] += s_lg[s_par[i] * DK + (e - i * DK)];
+    // ---- 2. LG by pointer doubling: after round r an entry holds the sum over the
+    // node's 2^{r+1} nearest path nodes (or its whole path)
+    const int rounds = s_info[1];
+    for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+        for (int u = 0; u < GPT; ++u) {
+            const int P = tid + kVecThreads * u;
+            const int a = s_anc[r][P / GP];
+            if (a >= 0) {
+                const float4 x = *reinterpret_cast<const float4 *>(s_lg + a * DK + 4 * (P % GP));
+                lgv[u].x += x.x;
+                lgv[u].y += x.y;
+                lgv[u].z += x.z;
+                lgv[u].w += x.w;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < GPT; ++u) {
+            const int P = tid + kVecThreads * u;
+            *reinterpret_cast<float4 *>(s_lg + (P / GP) * DK + 4 * (P % GP)) = lgv[u];
         }
         __syncthreads();
     }
@@ -167,8 +214,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     // ---- 3. pair weights w_ij = sum_c q_i[c] k_j[c] 2^{LG_i[c] - LG_j[c]}, j on path(i);
     // four lanes per node, CH channels each, summed across the four
     {
-        const bool live = pi < n;
-        const uint64_t mi = live ? s_mask[pi] : 0ull;
+        const uint64_t mi = pi < n ? s_mask[pi] : 0ull;
         float qv[CH], li[CH];
 #pragma unroll
         for (int u = 0; u < CH / 8; ++u)
@@ -206,28 +252,46 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
             if (psub == 0) s_w[pi * N + j] = acc;
         }
     }
+    // decayed-query operands of node tile `wave`: 2^{LG_i[c]} q_i[c], split hi + lo
+    bf16x8 ah[KT], al[KT];
+    {
+        const int qi = min(16 * wave + n16, last);
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const float *lgq = s_lg + qi * DK + 32 * t + 8 * g4;
+            const float4 x0 = *reinterpret_cast<const float4 *>(lgq);
+            const float4 x1 = *reinterpret_cast<const float4 *>(lgq + 4);
+            const float lq[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                __bf16 xh, xl;
+                split_bf16(static_cast<float>(qf[t][e]) * __builtin_amdgcn_exp2f(lq[e]), xh, xl);
+                ah[t][e] = xh;
+                al[t][e] = xl;
+            }
+        }
+    }
+    __syncthreads();  // LG and K are dead: the H_0 slice takes their space
+
+    // ---- 4. H_0 and V to LDS
+#pragma unroll
+    for (int u = 0; u < HPT; ++u) {
+        const int P = tid + kVecThreads * u;
+        *reinterpret_cast<u32x4 *>(s_h0 + (P / HP) * CW + 4 * (P % HP)) = rh[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        const int P = tid + kVecThreads * u;
+        *reinterpret_cast<u32x4 *>(s_v + (P / VP) * CW + 8 * (P % VP)) = rvv[u];
+    }
     __syncthreads();
 
-    // ---- 4. H_0 term for node tile `wave`: A = decayed query (hi + lo), B = H_0 rows
-    // 32t + 8g + e, columns CPL*n + c (hi + lo)
+    // ---- 5. H_0 term for node tile `wave`, then the intra term, then the rows
     f32x4 acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int qi = min(16 * wave + n16, last);
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-        const float *lgq = s_lg + qi * DK + 32 * t + 8 * g4;
-        const float4 x0 = *reinterpret_cast<const float4 *>(lgq);
-        const float4 x1 = *reinterpret_cast<const float4 *>(lgq + 4);
-        const float lq[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        bf16x8 ah, al;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            __bf16 xh, xl;
-            split_bf16(static_cast<float>(qf[t][e]) * __builtin_amdgcn_exp2f(lq[e]), xh, xl);
-            ah[e] = xh;
-            al[e] = xl;
-        }
         bf16x8 bh[CPL], bl[CPL];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -242,14 +306,11 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         }
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            acc[c] = mfma16_bf16(ah, bh[c], acc[c]);
-            acc[c] = mfma16_bf16(ah, bl[c], acc[c]);
-            acc[c] = mfma16_bf16(al, bh[c], acc[c]);
+            acc[c] = mfma16_bf16(ah[t], bh[c], acc[c]);
+            acc[c] = mfma16_bf16(ah[t], bl[c], acc[c]);
+            acc[c] = mfma16_bf16(al[t], bh[c], acc[c]);
         }
     }
-
-    // ---- 5. intra term into the same registers (node 16*wave + 4g + r, columns
-    // CPL*n + c), then the rows
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = 16 * wave + 4 * g4 + r;
