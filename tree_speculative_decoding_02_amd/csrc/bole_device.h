@@ -16,7 +16,6 @@ namespace bole {
 constexpr int kMaxTree = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 

@@ -7,12 +7,6 @@ namespace bole {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8(l/32)+e], B[8(l/32)+e][l%32], and
-// C rows 8(e/4) + 4(l/32) + e%4 of column l%32.
-__device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
 // fp32 x -> bf16 hi + bf16 lo with x ~= hi + lo (relative error about 2^-17).
 __device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo) {
     hi = static_cast<__bf16>(x);
@@ -46,10 +40,6 @@ __device__ __forceinline__ void dma16_stream(const void *src, void *lds_wave_bas
 
 // Waits until every memory operation this wave issued (DMA into LDS included) is done.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
-
-// Waits until this wave's LDS reads have returned (the LDS may then be overwritten by
-// DMA); vector-memory and export counters are left alone.
-__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], and
 // C rows 4(l/16) + r of column l%16.
