@@ -41,7 +41,7 @@ namespace bole {
 //
 // Intra-tree term on the same products:
 //  - S^T tile (jt, it) = K_jt . Q_it^T over d_k, for every ancestor tile jt <= it; K
-//    comes from LDS (DMA, 16-byte pieces XOR-swizzled by row so the fragment reads are
+//    comes from LDS (16-byte pieces XOR-swizzled by row so the fragment reads are
 //    conflict-free), Q from registers;
 //  - the accumulator layout (lane (n, g) holds j = 16jt + 4g + r for node i = 16it + n)
 //    is used in place as the A operand of W.V over a pair of ancestor tiles (2p, 2p+1):
@@ -122,20 +122,26 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
         for (int t = 0; t < KT; ++t)
             qf[it][t] = load16_stream(
                 qu + ((uint32_t)min(32 * wave + 16 * it + n16, last) * rq + 32 * t + 8 * g));
-    // K rows -> LDS: instruction s fills slots 64s .. 64s+63, i.e. rows (64/PPR)s ..; lane
-    // l fills slot 64s + l = row j, slot-in-row l % PPR, with piece (l % PPR) ^ (j % PPR).
-    // The wavefronts of the workgroup take every NWT-th instruction.
+    // K and V rows go to LDS through registers (plain loads, so every later wait counts
+    // exactly what it needs: no LDS instruction has to wait for the H_0 loads). K: load
+    // s fills LDS slots 64s .. 64s+63, i.e. rows (64/PPR)s ..; lane l fills slot 64s + l
+    // = row j, slot-in-row l % PPR, with piece (l % PPR) ^ (j % PPR). V: lane l of load s
+    // takes row (64/VPR)s + l/VPR, piece l % VPR. The wavefronts of the workgroup take
+    // every NWT-th load.
+    constexpr int KL = NN * PPR / 64 / NWT, VL = NN * VPR / 64 / NWT;
+    bf16x8 kst[KL], vst[VL];
 #pragma unroll
-    for (int s = wave; s < NN * PPR / 64; s += NWT) {
+    for (int u = 0; u < KL; ++u) {
+        const int s = wave + NWT * u;
         const int j = (64 / PPR) * s + lane / PPR;
         const int pc = (lane % PPR) ^ (j % PPR);
-        dma16_stream(ku + ((uint32_t)min(j, last) * rq + 8 * pc), s_k + 64 * s);
+        kst[u] = load16_stream(ku + ((uint32_t)min(j, last) * rq + 8 * pc));
     }
-    // V rows -> LDS: lane l of instruction s takes row (64/VPR)s + l/VPR, piece l % VPR
 #pragma unroll
-    for (int s = wave; s < NN * VPR / 64; s += NWT) {
+    for (int u = 0; u < VL; ++u) {
+        const int s = wave + NWT * u;
         const int j = (64 / VPR) * s + lane / VPR;
-        dma16_stream(vu + ((uint32_t)min(j, last) * rv + 8 * (lane % VPR)), s_v + 512 * s);
+        vst[u] = load16_stream(vu + ((uint32_t)min(j, last) * rv + 8 * (lane % VPR)));
     }
     // H_0 slice: load s = 8t + e, lane (n, g): row 32t + 8g + e, columns CPL*n .. +CPL-1
     hvec hreg[HS];
@@ -144,12 +150,17 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
         hreg[s] = __builtin_nontemporal_load(reinterpret_cast<const hvec *>(
             hu + ((uint32_t)(32 * (s >> 3) + 8 * g + (s & 7)) * DV + CPL * n16)));
 
+#pragma unroll
+    for (int u = 0; u < KL; ++u) s_k[64 * (wave + NWT * u) + lane] = kst[u];
+#pragma unroll
+    for (int u = 0; u < VL; ++u)
+        *reinterpret_cast<bf16x8 *>(s_v + 512 * (wave + NWT * u) + 8 * lane) = vst[u];
+
     // ---- 2. topology and base-2 cumulative decay, lane = node (every wavefront)
     const float lg2 = lane < n ? __builtin_amdgcn_logf(g_raw) : 0.f;
     const WaveTopoL topo = wave_topology_cumlog(p_raw, lg2, n);
     if (writer) tree_status[b] = topo.bad;
     if (topo.bad) {
-        wait_all_memory();  // no DMA may still target this workgroup's LDS after exit
         for (int i = 32 * wave + g; i < min(n, 32 * wave + 32); i += 4)
 #pragma unroll
             for (int c = 0; c < CPL; ++c) ou[(uint32_t)i * rv + CPL * n16 + c] = __builtin_nanf("");
@@ -193,9 +204,8 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
             for (int c = 0; c < CPL; ++c) acc[it][c][r] *= sc;
         }
 
-    // ---- 4. intra-tree term, one node tile and one ancestor tile pair at a time (the K
-    // and V rows of every wavefront's DMA must have landed)
-    wait_all_memory();
+    // ---- 4. intra-tree term, one node tile and one ancestor tile pair at a time (with
+    // two wavefronts, each needs the other's K and V rows)
     if (NWT > 1) __syncthreads();
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
