@@ -195,30 +195,37 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
 // and the state is updated in registers and stored (non-temporal). Up to 16 path nodes
 // are staged per round; longer paths stage the rest afterwards.
 constexpr int kStageNodes = 16;
+constexpr unsigned kCommitTargetBlocks = 1024;  // small batches split states to about this many
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-template <typename TF, bool VEC>
+template <typename TF, bool VEC, bool SLICED>
 __global__ __launch_bounds__(kCommitThreads) void commit_stream_kernel(
     float *__restrict__ H0, const TF *__restrict__ k, const TF *__restrict__ v,
     const float *__restrict__ gate, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, const int32_t *__restrict__ accepted_idx,
     const int32_t *__restrict__ accepted_len, int32_t *__restrict__ path_nodes,
     int32_t *__restrict__ tree_status, int H, int DK, int DV, int T, int max_path, int max_n,
-    int gpr_log2) {
+    int gpr_log2, int slices, int slice_groups) {
     constexpr int E = 16 / sizeof(TF);   // factor elements per 16-byte chunk
     constexpr int PER = kRegFloats / 4;  // float4 state groups per thread per pass
     __shared__ int s_row[kMaxTree];
     __shared__ float s_a[kMaxTree];
     __shared__ int s_len;
     extern __shared__ __attribute__((aligned(16))) float s_f[];  // [kStageNodes][FW]: k, (gate), v rows
-    const int unit = blockIdx.x;
+    // workgroup = (unit, slice): the slice is a run of slice_groups float4 groups of the
+    // unit's state (whole state when slices == 1)
+    const int unit = SLICED ? (int)blockIdx.x / slices : (int)blockIdx.x;
+    const int slice = SLICED ? (int)blockIdx.x - unit * slices : 0;
     const int b = unit / H, h = unit - b * H;
     const int tid = threadIdx.x;
     const int FW = (VEC ? 2 : 1) * DK + DV;
     const int CK = DK / E, CG = VEC ? DK / 4 : 0, CV = DV / E;
     const int CPN = CK + CG + CV;        // chunks per path node
-    float *Hu = H0 + (size_t)unit * DK * DV;
-    const int G = DK * DV / 4;           // float4 groups of the state
+    // this slice: groups gbeg .. gbeg + G - 1 of the state, i.e. rows from row0 on
+    const int gbeg = SLICED ? slice * slice_groups : 0;
+    const int G = SLICED ? min(DK * DV / 4 - gbeg, slice_groups) : DK * DV / 4;
+    const int row0 = SLICED ? gbeg >> gpr_log2 : 0;
+    float *Hu = H0 + (size_t)unit * DK * DV + (size_t)gbeg * 4;
 
     // ---- round 1
     const TreeRange tr = tree_range(node_offsets, b, T, max_n);
@@ -235,7 +242,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_stream_kernel(
     const int n = tr.n;
     f32x4v reg[PER];
     const int rs = kCommitThreads >> gpr_log2;             // state rows between groups
-    const int r0 = tid >> gpr_log2;                        // row of group 0
+    const int r0 = tid >> gpr_log2;                        // row of group 0 (of a pass)
     const int cc = (tid & ((1 << gpr_log2) - 1)) * 4;      // first column (fixed)
     if (likely) {
 #pragma unroll
@@ -293,7 +300,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_stream_kernel(
         s_row[tid] = row;
         s_a[tid] = a;
         if (tid == 0) s_len = ok ? len : 0;
-        if (h == 0) {
+        if (h == 0 && slice == 0) {
             if (tid == 0 && tree_status) tree_status[b] = st;
             if (path_nodes && tid < max_path) path_nodes[(size_t)b * max_path + tid] = row;
         }
@@ -351,9 +358,9 @@ __global__ __launch_bounds__(kCommitThreads) void commit_stream_kernel(
                 __syncthreads();
             }
             for (int mm = 0; mm < mc; ++mm) {
-                const float *fk = s_f + mm * FW;
+                const float *fk = s_f + mm * FW + row0;  // k and gate rows of this slice
                 const float *fg = fk + DK;
-                const float4 vv = *reinterpret_cast<const float4 *>(fk + (VEC ? 2 : 1) * DK + cc);
+                const float4 vv = *reinterpret_cast<const float4 *>(s_f + mm * FW + (VEC ? 2 : 1) * DK + cc);
                 const float a = s_a[m0s + mm];
 #pragma unroll
                 for (int s = 0; s < PER; ++s) {
@@ -394,10 +401,21 @@ static void launch_w(float *H0, const bole_factors_t &f, const int32_t *accepted
     if (vec4 && gpr > 0 && (gpr & (gpr - 1)) == 0 && kCommitThreads % gpr == 0 &&
         d.d_k % E == 0 && d.d_v % E == 0 && fa % 16 == 0) {
         const size_t slds = sizeof(float) * kStageNodes * ((VEC ? 2 : 1) * d.d_k + d.d_v);
-        commit_stream_kernel<TF, VEC><<<grid, block, slds, stream>>>(
+        // state slices per unit: one pass per workgroup, and about kCommitTargetBlocks
+        // workgroups in all when the batch is small
+        const unsigned U = (unsigned)d.batch * (unsigned)d.heads;
+        const int G = d.d_k * d.d_v / 4, per_pass = kCommitThreads * kRegFloats / 4;
+        int slices = (G + per_pass - 1) / per_pass;
+        const int want = (int)((kCommitTargetBlocks + U - 1) / U);
+        slices = max(slices, min(want, G / kCommitThreads));
+        int sg = (G + slices - 1) / slices;
+        sg = (sg + kCommitThreads - 1) / kCommitThreads * kCommitThreads;
+        slices = (G + sg - 1) / sg;
+        auto kern = slices > 1 ? commit_stream_kernel<TF, VEC, true> : commit_stream_kernel<TF, VEC, false>;
+        kern<<<dim3(U * (unsigned)slices), block, slds, stream>>>(
             H0, k, v, f.gate, f.parent, f.node_offsets, accepted_idx, accepted_len, path_nodes,
             tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags),
-            __builtin_ctz((unsigned)gpr));
+            __builtin_ctz((unsigned)gpr), slices, sg);
     } else if (vec4)
         commit_kernel<TF, VEC, 4><<<grid, block, lds, stream>>>(
             H0, k, v, f.gate, f.parent, f.node_offsets, accepted_idx, accepted_len, path_nodes,
