@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time for the oracle baseline (whole steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config-sweep", action="store_true",
+                    help="instead of the benchmark, time verify and commit on each of the five "
+                         "workloads (one JSON line each)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration), then "
                          "time it five times")
@@ -118,6 +121,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.config_sweep:
+        config_sweep(dev)
+        return
     wl = W.make_config(5)
     L = len(wl.layers)
     print(f"[bench] workload {wl.name}: B={wl.batch} layers={L} H={wl.heads} d_k={wl.d_k} "
@@ -242,6 +248,56 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def config_sweep(dev, reps=20):
+    """Verify and commit on each workload, one layer: the layer's state is copied into 8
+    buffers and the 8 launches of one kind are timed with one event pair (divided by 8).
+    No flags: a caller without a known tree budget takes the general launch."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from tree_speculative_decoding_02_amd import bole
+    stream = torch.cuda.current_stream()
+    names = {1: "tiny_fp32", 2: "mamba2_scalar", 3: "gla_vector", 4: "ragged_large_batch",
+             5: "hybrid_stack_one_layer"}
+    for cid in (1, 2, 3, 4, 5):
+        wl = W.make_config(cid, n_layers=1) if cid == 5 else W.make_config(cid)
+        lay = wl.layers[0]
+        g = lambda t: t.to(dev)
+        Hs = [g(lay.H0) for _ in range(8)]
+        q, k, v, gate = g(lay.q), g(lay.k), g(lay.v), g(lay.gate)
+        par, offs = g(torch.from_numpy(wl.parent)), g(torch.from_numpy(wl.node_offsets))
+        ai, al = g(torch.from_numpy(wl.accepted_idx)), g(torch.from_numpy(wl.accepted_len))
+        out = torch.empty((wl.total_nodes, wl.heads, wl.d_v), dtype=torch.float32, device=dev)
+        launches = {"verify": [bole.bind_tree_verify(H, q, k, v, gate, par, offs, out,
+                                                     stream=stream) for H in Hs],
+                    "commit": [bole.bind_commit_path(H, k, v, gate, par, offs, ai, al,
+                                                     stream=stream) for H in Hs]}
+        s_f = 2 if lay.q.dtype == torch.bfloat16 else 4
+        nbytes = {"verify": verify_bytes(wl, s_f), "commit": commit_bytes(wl, s_f)}
+        rec = {"kind": "config_sweep", "config": cid, "workload": names[cid], "batch": wl.batch,
+               "heads": wl.heads, "d_k": wl.d_k, "d_v": wl.d_v, "total_nodes": wl.total_nodes,
+               "vector_gate": bool(wl.vector_gate), "factor_dtype": str(lay.q.dtype)}
+        for name, fs in launches.items():
+            for _ in range(3):
+                for f in fs:
+                    f()
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            for a, b in evs:
+                a.record(stream)
+                for f in fs:
+                    f()
+                b.record(stream)
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 / len(fs) for a, b in evs]))
+            gbs = nbytes[name] / (us * 1e3)
+            rec[name] = {"median_us": us, "bytes": nbytes[name], "GB_s": gbs,
+                         "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+        print(json.dumps(rec), flush=True)
 
 
 def cpu_baseline(wl, min_seconds):
