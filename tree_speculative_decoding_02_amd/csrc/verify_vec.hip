@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     __shared__ uint64_t s_mask[N];
     __shared__ int s_anc[6][N];                                    // 2^r-th ancestor (or -1)
     __shared__ int s_info[2];                                      // status, doubling rounds
+    __shared__ float s_red[4][2];                                  // per wave: min, max of LG
     float *s_lg = s_big;
     __bf16 *s_k = reinterpret_cast<__bf16 *>(s_big + N * DK);
     float *s_h0 = s_big;
@@ -211,9 +212,36 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         __syncthreads();
     }
 
-    // ---- 3. pair weights w_ij = sum_c q_i[c] k_j[c] 2^{LG_i[c] - LG_j[c]}, j on path(i);
-    // four lanes per node, CH channels each, summed across the four
-    {
+    // ---- LG range of the tree. With M its midpoint, q_i 2^{LG_i - M} and k_j 2^{M - LG_j}
+    // stay within 2^{+-60} when the range is at most 120, and w_ij is then their dot
+    // product: the intra term runs on matrix cores. Otherwise (very deep or very strongly
+    // decayed trees) each ancestor pair is summed with its exact exponent.
+    float lmin = 3.0e38f, lmax = -3.0e38f;
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) {
+        if ((tid + kVecThreads * u) / GP < n) {
+            lmin = fminf(lmin, fminf(fminf(lgv[u].x, lgv[u].y), fminf(lgv[u].z, lgv[u].w)));
+            lmax = fmaxf(lmax, fmaxf(fmaxf(lgv[u].x, lgv[u].y), fmaxf(lgv[u].z, lgv[u].w)));
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        lmin = fminf(lmin, __shfl_xor(lmin, o, 64));
+        lmax = fmaxf(lmax, __shfl_xor(lmax, o, 64));
+    }
+    if (lane == 0) {
+        s_red[wave][0] = lmin;
+        s_red[wave][1] = lmax;
+    }
+    __syncthreads();
+    const float lo_lg = fminf(fminf(s_red[0][0], s_red[1][0]), fminf(s_red[2][0], s_red[3][0]));
+    const float hi_lg = fmaxf(fmaxf(s_red[0][1], s_red[1][1]), fmaxf(s_red[2][1], s_red[3][1]));
+    const float M = 0.5f * (lo_lg + hi_lg);
+    const bool factored = hi_lg - lo_lg <= 120.f && M >= -100.f;
+
+    // ---- 3 (exact path). pair weights w_ij = sum_c q_i[c] k_j[c] 2^{LG_i[c] - LG_j[c]},
+    // j on path(i); four lanes per node, CH channels each, summed across the four
+    if (!factored) {
         const uint64_t mi = pi < n ? s_mask[pi] : 0ull;
         float qv[CH], li[CH];
 #pragma unroll
@@ -252,7 +280,9 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
             if (psub == 0) s_w[pi * N + j] = acc;
         }
     }
-    // decayed-query operands of node tile `wave`: 2^{LG_i[c]} q_i[c], split hi + lo
+    // query operands of node tile `wave`: 2^{LG_i[c] - off} q_i[c], split hi + lo, with
+    // off = M on the factored path (the H_0 term is scaled back by 2^M) and 0 otherwise
+    const float off = factored ? M : 0.f;
     bf16x8 ah[KT], al[KT];
     {
         const int qi = min(16 * wave + n16, last);
@@ -265,11 +295,76 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 __bf16 xh, xl;
-                split_bf16(static_cast<float>(qf[t][e]) * __builtin_amdgcn_exp2f(lq[e]), xh, xl);
+                split_bf16(static_cast<float>(qf[t][e]) * __builtin_amdgcn_exp2f(lq[e] - off), xh, xl);
                 ah[t][e] = xh;
                 al[t][e] = xl;
             }
         }
+    }
+    // ---- 3 (factored path). S^T tiles (jt, it = wave) = B_jt . A_it^T over channels, with
+    // B_j = k_j 2^{M - LG_j} (split hi + lo; three products), masked to ancestors. Their
+    // accumulator layout (lane (n, g) holds j = 16jt + 4g + r for node i = 16it + n) is the
+    // A operand of W.V over the ancestor tile pair (2p, 2p+1): contraction index 8g + e
+    // stands for node 32p + 4g + e (e < 4) or 32p + 16 + 4g + e - 4 (e >= 4).
+    bf16x8 wh[2], wl[2];
+    if (factored) {
+        // B_j = k_j 2^{M - LG_j}, once per entry: each thread rewrites its own LG entries
+        // in place once every wavefront has read LG for its query operands
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < GPT; ++u) {
+            const int P = tid + kVecThreads * u;
+            const int row = P / GP, c = 4 * (P % GP);
+            const __bf16 *kr = s_k + row * DK + c;
+            const float4 bj = make_float4(
+                static_cast<float>(kr[0]) * __builtin_amdgcn_exp2f(M - lgv[u].x),
+                static_cast<float>(kr[1]) * __builtin_amdgcn_exp2f(M - lgv[u].y),
+                static_cast<float>(kr[2]) * __builtin_amdgcn_exp2f(M - lgv[u].z),
+                static_cast<float>(kr[3]) * __builtin_amdgcn_exp2f(M - lgv[u].w));
+            *reinterpret_cast<float4 *>(s_lg + row * DK + c) = bj;
+        }
+        __syncthreads();
+        const uint64_t mi = s_mask[16 * wave + n16];
+        float w[4][4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            f32x4 st = {0.f, 0.f, 0.f, 0.f};
+            if (jt <= wave) {
+                const int j = min(16 * jt + n16, N - 1);
+#pragma unroll
+                for (int t = 0; t < KT; ++t) {
+                    const float *bj = s_lg + j * DK + 32 * t + 8 * g4;
+                    const float4 x0 = *reinterpret_cast<const float4 *>(bj);
+                    const float4 x1 = *reinterpret_cast<const float4 *>(bj + 4);
+                    const float bv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    bf16x8 bh, bl;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        __bf16 xh, xl;
+                        split_bf16(bv[e], xh, xl);
+                        bh[e] = xh;
+                        bl[e] = xl;
+                    }
+                    st = mfma16_bf16(bh, ah[t], st);
+                    st = mfma16_bf16(bh, al[t], st);
+                    st = mfma16_bf16(bl, ah[t], st);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * jt + 4 * g4 + r;
+                w[jt][r] = (jt <= wave && ((mi >> j) & 1ull)) ? st[r] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                __bf16 xh, xl;
+                split_bf16(e < 4 ? w[2 * p][e] : w[2 * p + 1][e - 4], xh, xl);
+                wh[p][e] = xh;
+                wl[p][e] = xl;
+            }
     }
     __syncthreads();  // LG and K are dead: the H_0 slice takes their space
 
@@ -311,11 +406,34 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
             acc[c] = mfma16_bf16(al[t], bh[c], acc[c]);
         }
     }
+    if (factored) {
+        const float sc = __builtin_amdgcn_exp2f(M);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] *= sc;
+        // W.V: V operand for column tile c, element e = V[32p + j(e)][CPL*n + c]
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            if (2 * p > wave) break;
+            bf16x8 vb[CPL];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = 32 * p + (e < 4 ? 4 * g4 + e : 12 + 4 * g4 + e);
+                const vvec x = *reinterpret_cast<const vvec *>(s_v + j * CW + CPL * n16);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) vb[c][e] = x[c];
+            }
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                acc[c] = mfma16_bf16(wh[p], vb[c], acc[c]);
+                acc[c] = mfma16_bf16(wl[p], vb[c], acc[c]);
+            }
+        }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = 16 * wave + 4 * g4 + r;
         if (i >= n) continue;
-        uint64_t rest = s_mask[i];
+        uint64_t rest = factored ? 0ull : s_mask[i];
         while (rest) {
             const int j = __ffsll((unsigned long long)rest) - 1;
             rest &= rest - 1;
