@@ -25,8 +25,9 @@ namespace bole {
 // One kernel template, two instantiations: NWT = 1 takes trees of 1..32 nodes (and the
 // status of every tree except those of 33..64 nodes), NWT = 2 takes trees of 33..64 and
 // is launched only when the batch may hold them. A workgroup of NWT wavefronts works on
-// one (sequence, head, 64-column group); wavefront w owns nodes 32w .. 32w+31 as two
-// 16-node tiles. 16x16 matrix-core tiles throughout: lane = (n, g) with n = lane % 16,
+// one (sequence, head, 64-column group): every wavefront covers all 32 NWT nodes as
+// 16-node tiles, and wavefront w the columns w*CW/NWT .. of the group, so H_0 is read
+// once. 16x16 matrix-core tiles throughout: lane = (n, g) with n = lane % 16,
 // g = lane / 16.
 //
 // H_0 term, all v_mfma_f32_16x16x32_bf16. The H_0 slice is loaded straight into
@@ -58,8 +59,10 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     const int32_t *__restrict__ parent, const int32_t *__restrict__ node_offsets,
     float *__restrict__ out, int32_t *__restrict__ tree_status, int H, int T, int U, int max_n) {
     constexpr int NN = 32 * NWT;            // node rows staged
+    constexpr int NT = 2 * NWT;             // 16-node tiles per wavefront
     constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
-    constexpr int CPL = CW / 16;            // columns per lane: 4 (2 when d_v = 32)
+    constexpr int CPW = CW / NWT;           // state columns per wavefront
+    constexpr int CPL = CPW / 16;           // columns per lane: 4, 2 or 1
     constexpr int G = DV / CW;              // column groups per unit
     constexpr int KT = DK / 32;             // k-steps of the bf16 products
     constexpr int HS = DK / 4;              // 16-byte H_0 loads per lane (4 rows each)
@@ -85,6 +88,7 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     }
     const int b = unit / H, h = unit - b * H;
     const int c0 = cg * CW;
+    const int cw0 = wave * CPW;             // the wave's first column within the group
     const bool writer = tree_status != nullptr && h == 0 && cg == 0 && threadIdx.x == 0;
 
     const TreeRange tr = tree_range(node_offsets, b, T, NWT == 1 ? max_n : kMaxTree);
@@ -114,14 +118,14 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     const uint32_t node = (uint32_t)min(lane, last);
     const int p_raw = parent[lo + node];
     const float g_raw = gate[(size_t)lo * H + h + node * (uint32_t)H];
-    // Q fragments of the wave's tiles: row 32w + 16it + n, elements 32t + 8g .. +7
-    bf16x8 qf[2][KT];
+    // Q fragments of the tiles: row 16it + n, elements 32t + 8g .. +7
+    bf16x8 qf[NT][KT];
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+    for (int it = 0; it < NT; ++it)
 #pragma unroll
         for (int t = 0; t < KT; ++t)
             qf[it][t] = load16_stream(
-                qu + ((uint32_t)min(32 * wave + 16 * it + n16, last) * rq + 32 * t + 8 * g));
+                qu + ((uint32_t)min(16 * it + n16, last) * rq + 32 * t + 8 * g));
     // K and V rows go to LDS through registers (plain loads, so every later wait counts
     // exactly what it needs: no LDS instruction has to wait for the H_0 loads). K: load
     // s fills LDS slots 64s .. 64s+63, i.e. rows (64/PPR)s ..; lane l fills slot 64s + l
@@ -143,12 +147,12 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
         const int j = (64 / VPR) * s + lane / VPR;
         vst[u] = load16_stream(vu + ((uint32_t)min(j, last) * rv + 8 * (lane % VPR)));
     }
-    // H_0 slice: load s = 8t + e, lane (n, g): row 32t + 8g + e, columns CPL*n .. +CPL-1
+    // H_0 slice: load s = 8t + e, lane (n, g): row 32t + 8g + e, columns cw0 + CPL*n ..
     hvec hreg[HS];
 #pragma unroll
     for (int s = 0; s < HS; ++s)
         hreg[s] = __builtin_nontemporal_load(reinterpret_cast<const hvec *>(
-            hu + ((uint32_t)(32 * (s >> 3) + 8 * g + (s & 7)) * DV + CPL * n16)));
+            hu + ((uint32_t)(32 * (s >> 3) + 8 * g + (s & 7)) * DV + cw0 + CPL * n16)));
 
 #pragma unroll
     for (int u = 0; u < KL; ++u) s_k[64 * (wave + NWT * u) + lane] = kst[u];
@@ -161,18 +165,19 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     const WaveTopoL topo = wave_topology_cumlog(p_raw, lg2, n);
     if (writer) tree_status[b] = topo.bad;
     if (topo.bad) {
-        for (int i = 32 * wave + g; i < min(n, 32 * wave + 32); i += 4)
+        for (int i = g; i < n; i += 4)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) ou[(uint32_t)i * rv + CPL * n16 + c] = __builtin_nanf("");
+            for (int c = 0; c < CPL; ++c)
+                ou[(uint32_t)i * rv + cw0 + CPL * n16 + c] = __builtin_nanf("");
         return;
     }
     const float L2 = topo.L;
 
     // ---- 3. H_0 term: over the 8 loads of k-step t, lane (n, g) holds rows 32t + 8g + e
     // of columns CPL*n + c: the B operand for column tile c; A is the Q fragment.
-    f32x4 acc[2][CPL];
+    f32x4 acc[NT][CPL];
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+    for (int it = 0; it < NT; ++it)
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[it][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -188,18 +193,18 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
                 bl[e] = xl;
             }
 #pragma unroll
-            for (int it = 0; it < 2; ++it) {
+            for (int it = 0; it < NT; ++it) {
                 acc[it][c] = mfma16_bf16(qf[it][t], bh, acc[it][c]);
                 acc[it][c] = mfma16_bf16(qf[it][t], bl, acc[it][c]);
             }
         }
     }
-    // row scale 2^{L_i}, node 32w + 16it + 4g + r
+    // row scale 2^{L_i}, node 16it + 4g + r
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+    for (int it = 0; it < NT; ++it)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float sc = __builtin_amdgcn_exp2f(__shfl(L2, 32 * wave + 16 * it + 4 * g + r, 64));
+            const float sc = __builtin_amdgcn_exp2f(__shfl(L2, 16 * it + 4 * g + r, 64));
 #pragma unroll
             for (int c = 0; c < CPL; ++c) acc[it][c][r] *= sc;
         }
@@ -208,8 +213,8 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     // two wavefronts, each needs the other's K and V rows)
     if (NWT > 1) __syncthreads();
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int ti = 2 * wave + it;             // global node tile
+    for (int it = 0; it < NT; ++it) {
+        const int ti = it;                        // node tile
         const int i = 16 * ti + n16;              // node of this lane's column
         const uint64_t mi = shfl_u64(topo.mask, i);
         const float Li = __shfl(L2, i, 64);
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int j = 32 * p + (e < 4 ? 4 * g + e : 12 + 4 * g + e);
-                const vvec x = *reinterpret_cast<const vvec *>(s_v + j * CW + CPL * n16);
+                const vvec x = *reinterpret_cast<const vvec *>(s_v + j * CW + cw0 + CPL * n16);
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) vb[c][e] = x[c];
             }
@@ -261,17 +266,17 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
         }
     }
 
-    // ---- 5. store: node 32w + 16it + 4g + r, columns CPL*n .. +CPL-1
+    // ---- 5. store: node 16it + 4g + r, columns cw0 + CPL*n .. +CPL-1
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+    for (int it = 0; it < NT; ++it)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = 32 * wave + 16 * it + 4 * g + r;
+            const int i = 16 * it + 4 * g + r;
             hvec o;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) o[c] = acc[it][c][r];
             if (i < n)
-                __builtin_nontemporal_store(o, reinterpret_cast<hvec *>(ou + ((uint32_t)i * rv + CPL * n16)));
+                __builtin_nontemporal_store(o, reinterpret_cast<hvec *>(ou + ((uint32_t)i * rv + cw0 + CPL * n16)));
         }
 }
 
