@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time for the oracle baseline (whole steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-naive", action="store_true",
+                    help="skip timing the naive serial-walk baseline")
     ap.add_argument("--config-sweep", action="store_true",
                     help="instead of the benchmark, time verify and commit on each of the five "
                          "workloads (one JSON line each)")
@@ -226,6 +228,35 @@ def main():
                                       "bole_factors": bole_transient,
                                       "reduction": 1.0 - bole_transient / naive},
     }
+
+    # the naive serial walk on layer 0 (one materialised state per node): the baseline the
+    # closed form is measured against, timed after the benchmark proper
+    if not args.no_naive:
+        x = layers[0]
+        torch.cuda.synchronize()
+        m0 = torch.cuda.memory_allocated(dev)
+        states = torch.empty((wl.total_nodes, wl.heads, wl.d_k, wl.d_v), dtype=torch.float32,
+                             device=dev)
+        states_bytes = torch.cuda.memory_allocated(dev) - m0
+        nout = torch.empty_like(outs[0])
+        naive = lambda: bole.bole_tree_verify_naive(x["H0"], x["q"], x["k"], x["v"], x["gate"],
+                                                    parent, offs, out=nout, states=states,
+                                                    stream=stream)
+        naive()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(5):
+            naive()
+        b.record(stream)
+        torch.cuda.synchronize()
+        n_us = a.elapsed_time(b) * 1e3 / 5
+        result["naive_serial_walk"] = {
+            "avg_us_per_layer": n_us, "closed_form_speedup": n_us / v_us,
+            "states_bytes_measured": states_bytes,
+            "what": "bole_tree_verify_naive: every node's state materialised in tree order, "
+                    "layer 0 of the same workload, 5 launches"}
+        del states, nout
 
     if args.copy_calibration:
         n = 512 * 2 ** 20 // 4

@@ -147,6 +147,22 @@ BOLE_API bole_status_t bole_tree_verify(const float *H0, const void *q, const vo
                                bole_stream_t stream);
 
 /*
+ * Baseline: the naive serial walk that the closed form replaces (Bole summary page,
+ * section 1). Every node's state is materialised, in tree order:
+ *     H_i = S_i H_parent(i) + k_i v_i^T   (H_parent = H0 for a root),   out[i] = H_i^T q_i.
+ * states (device float [T][H][d_k][d_v], caller-owned: T * H * d_k * d_v floats)
+ * receives every H_i; this is the transient memory the closed form avoids. Inputs,
+ * outputs, tree_status and errors follow bole_tree_verify (bad-parent trees get NaN rows
+ * and no states; bad-size trees are not touched). It exists to measure the closed form
+ * against and is not a fast path.
+ */
+BOLE_API bole_status_t bole_tree_verify_naive(const float *H0, const void *q, const void *k,
+                               const void *v, const float *gate, const int32_t *parent,
+                               const int32_t *node_offsets, float *out, float *states,
+                               const bole_dims_t *dims, int32_t *tree_status,
+                               bole_stream_t stream);
+
+/*
  * Accepted-path commit: the restore step of the Bole summary page, section 2
  * ("Token-Level Factor Encoding").
  * For each tree b with accepted_len[b] = L > 0, and path p_1..p_L

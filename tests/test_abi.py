@@ -83,6 +83,11 @@ def test_null_dims_and_pointers_rejected_without_launch():
                               None) == bole.BOLE_OK
     assert L.bole_tree_prepare(None, None, None, ctypes.byref(_dims()), None, None, None, None,
                                None) == bole.BOLE_ERR_INVALID_VALUE
+    # the serial-walk baseline needs its states buffer like any other output
+    assert L.bole_tree_verify_naive(*([None] * 9), ctypes.byref(_dims()), None, None) == \
+        bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_tree_verify_naive(*([None] * 9), ctypes.byref(_dims(batch=0)), None, None) == \
+        bole.BOLE_OK
 
 
 def test_status_strings_and_limits():

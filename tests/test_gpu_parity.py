@@ -338,6 +338,72 @@ def test_bound_launchers_match_calls(bole):
     np.testing.assert_array_equal(H.double().cpu().numpy(), H2)
 
 
+NAIVE_CASES = [
+    ("config1_tiny_fp32", lambda: W.make_config(1)),
+    ("config2_mamba2", lambda: W.make_config(2)),
+    ("vector_gate", lambda: W.make_random(31, batch=3, heads=2, d_k=128, d_v=128, kind="bestfirst",
+                                          vector_gate=True)),
+    ("fp32_odd_dims", lambda: W.make_random(32, batch=3, heads=3, d_k=40, d_v=24,
+                                            factor_dtype=torch.float32)),
+    ("trees_to_64", lambda: W.make_random(33, batch=4, heads=2, d_k=64, d_v=64,
+                                          sizes=[64, 33, 1, 0], kind="deep", max_path=64)),
+]
+
+
+@pytest.mark.parametrize("name,make", NAIVE_CASES, ids=[c[0] for c in NAIVE_CASES])
+def test_naive_serial_walk_matches_oracle(bole, name, make):
+    """The baseline serial walk (one materialised state per node) against the oracle."""
+    wl = make()
+    t = to_dev(wl)
+    B = wl.batch
+    status = torch.full((B,), -7, dtype=torch.int32, device=dev())
+    out, states = bole.bole_tree_verify_naive(t["H0"], t["q"], t["k"], t["v"], t["gate"],
+                                              t["parent"], t["offs"], tree_status=status)
+    torch.cuda.synchronize()
+    ref, st = oracle.verify_serial(wl.layers[0].H0, wl.layers[0].q, wl.layers[0].k,
+                                   wl.layers[0].v, wl.layers[0].gate, wl.parent, wl.node_offsets,
+                                   wl.vector_gate)
+    assert status.cpu().numpy().tolist() == st.tolist()
+    assert rel_err_rows(out.double().cpu().numpy(), ref) <= TOL[wl.factor_dtype]
+    assert tuple(states.shape) == (wl.total_nodes, wl.heads, wl.d_k, wl.d_v)
+
+
+def test_naive_states_equal_committed_states(bole):
+    """The state the serial walk materialises at the last node of each accepted path is
+    the state the commit kernel writes into H0 (same fp32 recurrence)."""
+    wl = W.make_config(2)
+    t = to_dev(wl)
+    _, states = bole.bole_tree_verify_naive(t["H0"], t["q"], t["k"], t["v"], t["gate"],
+                                            t["parent"], t["offs"])
+    H, pn, _ = gpu_commit(bole, t)
+    S = states.double().cpu().numpy()
+    H0 = wl.layers[0].H0.double().numpy()
+    checked = 0
+    for b in range(wl.batch):
+        L = int(wl.accepted_len[b])
+        if L == 0:
+            np.testing.assert_array_equal(H[b], H0[b])
+            continue
+        end = int(pn[b, L - 1])
+        np.testing.assert_allclose(H[b], S[end], rtol=1e-5, atol=1e-6)
+        checked += 1
+    assert checked > 0
+
+
+def test_naive_bad_trees(bole):
+    sizes = [3, 2]
+    wl = W.make_random(5, batch=2, heads=2, d_k=64, d_v=32, sizes=sizes)
+    wl.parent = np.array([-1, 0, 0, -1, 1], np.int32)   # tree 1: node 1 is its own parent
+    t = to_dev(wl)
+    status = torch.full((2,), -7, dtype=torch.int32, device=dev())
+    out, _ = bole.bole_tree_verify_naive(t["H0"], t["q"], t["k"], t["v"], t["gate"], t["parent"],
+                                         t["offs"], tree_status=status)
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0, 2]
+    o = out.cpu().numpy()
+    assert np.isnan(o[3:5]).all() and np.isfinite(o[0:3]).all()
+
+
 def test_resume_verify_commit_verify(bole):
     """verify(next tree) on the GPU-committed state equals the oracle's verify of the
     accepted path with the next tree hung below it, on the old state."""

@@ -2,7 +2,7 @@
 layers. The compute lives in libbole.so (HIP kernels behind the C ABI of include/bole.h);
 ``bole`` is its thin Python binding."""
 from .bole import (bind_commit_path, bind_tree_verify, bole_commit_path, bole_tree_prepare,
-                   bole_tree_verify, BoleError, MAX_TREE_NODES)
+                   bole_tree_verify, bole_tree_verify_naive, BoleError, MAX_TREE_NODES)
 
 __all__ = ["bind_commit_path", "bind_tree_verify", "bole_commit_path", "bole_tree_prepare",
-           "bole_tree_verify", "BoleError", "MAX_TREE_NODES"]
+           "bole_tree_verify", "bole_tree_verify_naive", "BoleError", "MAX_TREE_NODES"]

@@ -22,7 +22,7 @@ BOLE_FLAG_TREES_LE_32 = 2
 MAX_TREE_NODES = 64
 
 EXPORTED = ("bole_max_tree_nodes", "bole_status_string", "bole_check_dims", "bole_tree_verify",
-            "bole_commit_path", "bole_tree_prepare")
+            "bole_tree_verify_naive", "bole_commit_path", "bole_tree_prepare")
 
 
 class bole_dims_t(ctypes.Structure):
@@ -56,6 +56,8 @@ def _load():
     lib.bole_check_dims.argtypes = [D, I32]
     lib.bole_tree_verify.restype = ctypes.c_int
     lib.bole_tree_verify.argtypes = [P, P, P, P, P, P, P, P, D, P, P]
+    lib.bole_tree_verify_naive.restype = ctypes.c_int
+    lib.bole_tree_verify_naive.argtypes = [P, P, P, P, P, P, P, P, P, D, P, P]
     lib.bole_commit_path.restype = ctypes.c_int
     lib.bole_commit_path.argtypes = [P, ctypes.POINTER(bole_factors_t), P, P, D, P, P, P]
     lib.bole_tree_prepare.restype = ctypes.c_int
@@ -152,6 +154,35 @@ def bole_tree_verify(H0, q, k, v, gate, parent, node_offsets, out=None, tree_sta
                                 _ptr(node_offsets), _ptr(out), ctypes.byref(dims),
                                 _ptr(tree_status), _stream(stream)), "bole_tree_verify")
     return out
+
+
+def bole_tree_verify_naive(H0, q, k, v, gate, parent, node_offsets, out=None, states=None,
+                           tree_status=None, stream=None, trees_le_32=False):
+    """Baseline serial walk: out[T, H, d_v] as bole_tree_verify, with every node's state
+    written to states[T, H, d_k, d_v] (fp32, allocated here when None). Returns
+    (out, states)."""
+    B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
+    _need(q, "q", k.dtype, H0.device)
+    if tuple(q.shape) != tuple(k.shape):
+        raise ValueError("q must have the shape of k")
+    if out is None:
+        out = torch.empty((T, Hh, d_v), dtype=torch.float32, device=H0.device)
+    if states is None:
+        states = torch.empty((T, Hh, d_k, d_v), dtype=torch.float32, device=H0.device)
+    _need(out, "out", torch.float32, H0.device)
+    _need(states, "states", torch.float32, H0.device)
+    if tuple(out.shape) != (T, Hh, d_v) or tuple(states.shape) != (T, Hh, d_k, d_v):
+        raise ValueError("out must be [T, H, d_v] and states [T, H, d_k, d_v]")
+    if tree_status is not None:
+        _need(tree_status, "tree_status", torch.int32, H0.device)
+        if tree_status.numel() < B:
+            raise ValueError("tree_status needs B entries")
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, trees_le_32=trees_le_32)
+    _check(lib.bole_tree_verify_naive(_ptr(H0), _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                                      _ptr(parent), _ptr(node_offsets), _ptr(out), _ptr(states),
+                                      ctypes.byref(dims), _ptr(tree_status), _stream(stream)),
+           "bole_tree_verify_naive")
+    return out, states
 
 
 class _Bound:

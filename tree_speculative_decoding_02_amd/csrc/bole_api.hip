@@ -71,6 +71,23 @@ bole_status_t bole_tree_verify(const float *H0, const void *q, const void *k, co
                                                 tree_status, s));
 }
 
+bole_status_t bole_tree_verify_naive(const float *H0, const void *q, const void *k,
+                                     const void *v, const float *gate, const int32_t *parent,
+                                     const int32_t *node_offsets, float *out, float *states,
+                                     const bole_dims_t *dims, int32_t *tree_status,
+                                     bole_stream_t stream) {
+    const bole_status_t st = bole_check_dims(dims, kOpVerify);
+    if (st != BOLE_OK) return st;
+    const bole_dims_t &d = *dims;
+    if (d.batch == 0) return BOLE_OK;
+    if (H0 == nullptr || node_offsets == nullptr) return BOLE_ERR_INVALID_VALUE;
+    if (d.total_nodes > 0 && (q == nullptr || k == nullptr || v == nullptr || gate == nullptr ||
+                              parent == nullptr || out == nullptr || states == nullptr))
+        return BOLE_ERR_INVALID_VALUE;
+    return from_hip(bole::launch_verify_naive(H0, q, k, v, gate, parent, node_offsets, out, states,
+                                              d, tree_status, reinterpret_cast<hipStream_t>(stream)));
+}
+
 bole_status_t bole_commit_path(float *H0, const bole_factors_t *factors,
                                const int32_t *accepted_idx, const int32_t *accepted_len,
                                const bole_dims_t *dims, int32_t *path_nodes,

@@ -37,6 +37,11 @@ hipError_t launch_verify_vec(const float *H0, const void *q, const void *k, cons
                              const int32_t *node_offsets, float *out, const bole_dims_t &d,
                              int32_t *tree_status, hipStream_t stream);
 
+hipError_t launch_verify_naive(const float *H0, const void *q, const void *k, const void *v,
+                               const float *gate, const int32_t *parent,
+                               const int32_t *node_offsets, float *out, float *states,
+                               const bole_dims_t &d, int32_t *tree_status, hipStream_t stream);
+
 hipError_t launch_commit(float *H0, const bole_factors_t &f, const int32_t *accepted_idx,
                          const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
                          int32_t *tree_status, hipStream_t stream);
