@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time for the oracle baseline (whole steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lazy", action="store_true",
+                    help="skip timing the lazy-commit form of the decode loop")
     ap.add_argument("--no-naive", action="store_true",
                     help="skip timing the naive serial-walk baseline")
     ap.add_argument("--config-sweep", action="store_true",
@@ -104,6 +106,14 @@ def commit_bytes(wl, s_f=2):
         if L > 0:
             tot += H * (8 * dk * dv + L * ((dk + dv) * s_f + s_g))
     return tot + 4 * wl.batch * (wl.max_path + 1) + 4 * wl.total_nodes + 4 * (wl.batch + 1)
+
+
+def lazy_bytes(wl, s_f=2):
+    """Algorithmic HBM bytes of one lazy launch (the previous step's commit folded into this
+    step's verify): verify's and commit's bytes, less the second read of H_0 that the
+    two-pass form makes for every (sequence, head) with a non-empty path."""
+    with_path = int((wl.accepted_len > 0).sum())
+    return verify_bytes(wl, s_f) + commit_bytes(wl, s_f) - 4 * wl.heads * wl.d_k * wl.d_v * with_path
 
 
 def main():
@@ -228,6 +238,38 @@ def main():
                                       "bole_factors": bole_transient,
                                       "reduction": 1.0 - bole_transient / naive},
     }
+
+    # the same decode loop with each step's commit folded into the next step's verify: per
+    # layer, one launch commits the previous step's accepted path into H_0 and verifies this
+    # step's tree against the result (the previous step here is the same synthetic batch)
+    if not args.no_lazy:
+        llaunch = [bole.bind_tree_verify_lazy_commit(
+            x["H0"], (x["k"], x["v"], x["gate"], parent, offs), acc_idx, acc_len, x["q"], x["k"],
+            x["v"], x["gate"], parent, offs, outs[l], stream=stream, trees_le_32=True,
+            prev_trees_le_32=True) for l, x in enumerate(layers)]
+        for _ in range(args.warmup):
+            for f in llaunch:
+                f()
+        torch.cuda.synchronize()
+        lrec = [(ev(), ev()) for _ in range(args.steps)]
+        for s in range(args.steps):
+            lrec[s][0].record(stream)
+            for f in llaunch:
+                f()
+            lrec[s][1].record(stream)
+        torch.cuda.synchronize()
+        l_ms = [a.elapsed_time(b) for a, b in lrec]
+        lb = lazy_bytes(wl)
+        l_us = 1e3 * float(np.mean(l_ms)) / L
+        result["lazy_commit"] = {
+            "ms_per_step": float(np.mean(l_ms)), "value": nodes / (float(np.mean(l_ms)) * 1e-3),
+            "unit": "draft nodes/s", "avg_us_per_launch": l_us,
+            "median_us_per_launch": 1e3 * float(np.median(l_ms)) / L, "bytes_per_launch": lb,
+            "GB_s": lb / (l_us * 1e3), "frac_hbm_peak": lb / (l_us * 1e3) / HBM_PEAK_GBS,
+            "launches_per_step": L, "speedup_vs_two_pass": ms_per_step / float(np.mean(l_ms)),
+            "what": "bole_tree_verify_lazy_commit per layer: the previous step's commit and "
+                    "this step's verify in one pass over H_0 (same work per step in steady "
+                    "state: one commit and one verify per layer)"}
 
     # the naive serial walk on layer 0 (one materialised state per node): the baseline the
     # closed form is measured against, timed after the benchmark proper

@@ -147,6 +147,30 @@ BOLE_API bole_status_t bole_tree_verify(const float *H0, const void *q, const vo
                                bole_stream_t stream);
 
 /*
+ * Lazy commit: the previous step's accepted-path commit folded into this step's verify,
+ * so that one pass over H0 serves both. The accepted path of a step is known only after
+ * that step's verify, so its commit can ride on the next step's verify; H0 is then read
+ * once and written once per step instead of read twice and written once.
+ * The result is exactly that of
+ *     bole_commit_path(H0, prev, prev_accepted_idx, prev_accepted_len, prev_dims,
+ *                      prev_path_nodes, prev_tree_status, stream);
+ *     bole_tree_verify(H0, q, k, v, gate, parent, node_offsets, out, dims, tree_status,
+ *                      stream);
+ * and every argument follows those two calls. prev_dims describes the previous step
+ * (its total_nodes, max_path and flags); batch, heads, d_k, d_v, factor_dtype and
+ * gate_kind must equal those of dims (else BOLE_ERR_INVALID_VALUE). On exit H0 holds
+ * the state after the previous step's accepted tokens: the state the next call, or a
+ * final bole_commit_path of the last step, starts from. Shapes the one-pass kernel does
+ * not cover run as the two calls above.
+ */
+BOLE_API bole_status_t bole_tree_verify_lazy_commit(
+    float *H0, const bole_factors_t *prev, const int32_t *prev_accepted_idx,
+    const int32_t *prev_accepted_len, const bole_dims_t *prev_dims, int32_t *prev_path_nodes,
+    int32_t *prev_tree_status, const void *q, const void *k, const void *v, const float *gate,
+    const int32_t *parent, const int32_t *node_offsets, float *out, const bole_dims_t *dims,
+    int32_t *tree_status, bole_stream_t stream);
+
+/*
  * Baseline: the naive serial walk that the closed form replaces (Bole summary page,
  * section 1). Every node's state is materialised, in tree order:
  *     H_i = S_i H_parent(i) + k_i v_i^T   (H_parent = H0 for a root),   out[i] = H_i^T q_i.

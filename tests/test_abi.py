@@ -90,6 +90,27 @@ def test_null_dims_and_pointers_rejected_without_launch():
         bole.BOLE_OK
 
 
+
+def test_lazy_commit_checks_both_steps_without_launch():
+    L = bole.lib
+    f = bole.bole_factors_t()
+
+    def call(d, pd, H0=None, prev=None):
+        return L.bole_tree_verify_lazy_commit(H0, prev, None, None, pd, None, None, None, None,
+                                              None, None, None, None, None, d, None, None)
+    assert call(None, ctypes.byref(_dims())) == bole.BOLE_ERR_INVALID_VALUE
+    assert call(ctypes.byref(_dims()), None) == bole.BOLE_ERR_INVALID_VALUE
+    # the previous step must describe the same layer
+    for field, value in (("heads", 4), ("d_v", 128), ("gate_kind", bole.BOLE_GATE_VECTOR),
+                         ("factor_dtype", bole.BOLE_DTYPE_F32), ("batch", 3)):
+        assert call(ctypes.byref(_dims()), ctypes.byref(_dims(**{field: value}))) == \
+            bole.BOLE_ERR_INVALID_VALUE, field
+    assert call(ctypes.byref(_dims(batch=0)), ctypes.byref(_dims(batch=0))) == bole.BOLE_OK
+    # a non-empty batch needs its buffers; nothing is launched before the check fails
+    assert call(ctypes.byref(_dims()), ctypes.byref(_dims()), prev=ctypes.byref(f)) == \
+        bole.BOLE_ERR_INVALID_VALUE
+
+
 def test_status_strings_and_limits():
     assert bole.lib.bole_max_tree_nodes() == bole.MAX_TREE_NODES == 64
     for code, name in [(0, b"BOLE_OK"), (1, b"BOLE_ERR_INVALID_VALUE"),

@@ -404,6 +404,190 @@ def test_naive_bad_trees(bole):
     assert np.isnan(o[3:5]).all() and np.isfinite(o[0:3]).all()
 
 
+LAZY_CASES = [
+    # (name, shared kwargs, previous-step kwargs, current-step kwargs)
+    ("scalar_dv64", dict(batch=6, heads=4, d_k=128, d_v=64), dict(sizes=[32, 20, 1, 0, 32, 9]),
+     dict(sizes=[32, 32, 5, 17, 0, 32])),
+    ("scalar_dv128_groups", dict(batch=4, heads=3, d_k=128, d_v=128), dict(kind="bestfirst"),
+     dict(kind="random")),
+    ("scalar_dk64_dv32", dict(batch=5, heads=2, d_k=64, d_v=32), dict(), dict()),
+    ("big_trees_long_paths", dict(batch=4, heads=2, d_k=128, d_v=64, max_path=64),
+     dict(sizes=[64, 48, 40, 33], kind="chain"), dict(sizes=[64, 12, 33, 30], kind="deep")),
+    ("vector_gate_fallback", dict(batch=3, heads=2, d_k=128, d_v=128, vector_gate=True), dict(),
+     dict()),
+    ("fp32_fallback", dict(batch=3, heads=2, d_k=64, d_v=64, factor_dtype=torch.float32), dict(),
+     dict()),
+]
+
+
+def _lazy_pair(name, shared, prev_kw, cur_kw):
+    seed = zlib.crc32(name.encode()) % 10000
+    wp = W.make_random(seed, **shared, **prev_kw)
+    wc = W.make_random(seed + 1, **shared, **cur_kw)
+    return wp, wc
+
+
+@pytest.mark.parametrize("name,shared,prev_kw,cur_kw", LAZY_CASES, ids=[c[0] for c in LAZY_CASES])
+def test_lazy_commit_equals_commit_then_verify(bole, name, shared, prev_kw, cur_kw):
+    """One pass (previous step's commit folded into this step's verify) against the two
+    calls it replaces, and both against the oracle's commit followed by verify."""
+    wp, wc = _lazy_pair(name, shared, prev_kw, cur_kw)
+    tp, tc = to_dev(wp), to_dev(wc)
+    B = wp.batch
+    # the two calls
+    H_a = tp["H0"].clone()
+    pst_a = torch.full((B,), -7, dtype=torch.int32, device=dev())
+    pn_a = torch.full(tuple(tp["acc_idx"].shape), -7, dtype=torch.int32, device=dev())
+    bole.bole_commit_path(H_a, tp["k"], tp["v"], tp["gate"], tp["parent"], tp["offs"],
+                          tp["acc_idx"], tp["acc_len"], path_nodes=pn_a, tree_status=pst_a)
+    st_a = torch.full((B,), -7, dtype=torch.int32, device=dev())
+    out_a = bole.bole_tree_verify(H_a, tc["q"], tc["k"], tc["v"], tc["gate"], tc["parent"],
+                                  tc["offs"], tree_status=st_a)
+    # one pass
+    H_b = tp["H0"].clone()
+    pst_b = torch.full((B,), -7, dtype=torch.int32, device=dev())
+    pn_b = torch.full(tuple(tp["acc_idx"].shape), -7, dtype=torch.int32, device=dev())
+    st_b = torch.full((B,), -7, dtype=torch.int32, device=dev())
+    out_b = bole.bole_tree_verify_lazy_commit(
+        H_b, (tp["k"], tp["v"], tp["gate"], tp["parent"], tp["offs"]), tp["acc_idx"], tp["acc_len"],
+        tc["q"], tc["k"], tc["v"], tc["gate"], tc["parent"], tc["offs"], prev_path_nodes=pn_b,
+        prev_tree_status=pst_b, tree_status=st_b)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(pst_b.cpu().numpy(), pst_a.cpu().numpy())
+    np.testing.assert_array_equal(pn_b.cpu().numpy(), pn_a.cpu().numpy())
+    np.testing.assert_array_equal(st_b.cpu().numpy(), st_a.cpu().numpy())
+    Ha, Hb = H_a.double().cpu().numpy(), H_b.double().cpu().numpy()
+    assert rel_err_states(Hb, Ha) <= 1e-6
+    oa, ob = out_a.double().cpu().numpy(), out_b.double().cpu().numpy()
+    assert rel_err_rows(ob, oa) <= 1e-5
+    # the oracle: commit the previous path, verify the current tree on the result
+    lp, lc = wp.layers[0], wc.layers[0]
+    Href, _, _ = oracle.commit_serial(lp.H0, lp.k, lp.v, lp.gate, wp.parent, wp.node_offsets,
+                                      wp.accepted_idx, wp.accepted_len, wp.vector_gate)
+    ref, _ = oracle.verify_serial(Href, lc.q, lc.k, lc.v, lc.gate, wc.parent, wc.node_offsets,
+                                  wc.vector_gate)
+    tol = TOL[wp.factor_dtype]
+    assert rel_err_states(Hb, Href) <= tol
+    assert rel_err_rows(ob, ref) <= tol
+
+
+def _lazy_vs_separate(bole, tp, tc, prev_trees_le_32=False):
+    """Runs the previous step's commit and this step's verify as two calls and as one;
+    returns both results as (H, out, prev status, prev path nodes, status) numpy tuples."""
+    B = tp["offs"].numel() - 1
+    res = []
+    for lazy in (False, True):
+        H = tp["H0"].clone()
+        pst = torch.full((B,), -7, dtype=torch.int32, device=dev())
+        pn = torch.full(tuple(tp["acc_idx"].shape), -7, dtype=torch.int32, device=dev())
+        st = torch.full((B,), -7, dtype=torch.int32, device=dev())
+        out = torch.full((tc["q"].shape[0], tc["H0"].shape[1], tc["H0"].shape[3]), 12345.0,
+                         dtype=torch.float32, device=dev())
+        if lazy:
+            bole.bole_tree_verify_lazy_commit(
+                H, (tp["k"], tp["v"], tp["gate"], tp["parent"], tp["offs"]), tp["acc_idx"],
+                tp["acc_len"], tc["q"], tc["k"], tc["v"], tc["gate"], tc["parent"], tc["offs"],
+                out=out, prev_path_nodes=pn, prev_tree_status=pst, tree_status=st,
+                prev_trees_le_32=prev_trees_le_32)
+        else:
+            bole.bole_commit_path(H, tp["k"], tp["v"], tp["gate"], tp["parent"], tp["offs"],
+                                  tp["acc_idx"], tp["acc_len"], path_nodes=pn, tree_status=pst,
+                                  trees_le_32=prev_trees_le_32)
+            bole.bole_tree_verify(H, tc["q"], tc["k"], tc["v"], tc["gate"], tc["parent"],
+                                  tc["offs"], out=out, tree_status=st)
+        torch.cuda.synchronize()
+        res.append(tuple(x.cpu().numpy() for x in (H, out, pst, pn, st)))
+    return res
+
+
+def test_lazy_commit_bad_trees(bole):
+    """Bad previous trees and paths (bad parent, path not a chain, path too long, path on
+    an empty tree, a tree over the size budget) and bad current trees: the one-pass form
+    reports the same statuses and path rows as the two calls, leaves the same states
+    untouched and writes the same NaN rows."""
+    sizes = [3, 2, 3, 2, 1, 0, 4]
+    wp = W.make_random(15, batch=7, heads=2, d_k=128, d_v=64, sizes=sizes)
+    wp.parent = np.array([-1, 0, 0, -1, 1, -1, 0, 1, -1, 0, -1, -1, 0, 1, 2], np.int32)
+    wp.node_offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    wp.accepted_idx[:] = -1
+    wp.accepted_len[:] = [2, 1, 2, 0, 17, 1, 3]
+    wp.accepted_idx[0, :2] = [0, 2]
+    wp.accepted_idx[1, :1] = [0]
+    wp.accepted_idx[2, :2] = [0, 2]       # parent[2] == 1 in tree 2: not a chain
+    wp.accepted_idx[4, :1] = [0]
+    wp.accepted_idx[5, :1] = [0]          # a path on an empty tree
+    wp.accepted_idx[6, :3] = [0, 1, 2]
+    cur_sizes = [4, 3, 40, 2, 5, 1, 6]
+    wc = W.make_random(16, batch=7, heads=2, d_k=128, d_v=64, sizes=cur_sizes)
+    wc.parent = wc.parent.copy()
+    wc.parent[wc.node_offsets[3] + 1] = 1     # current tree 3: a node its own parent
+    tp, tc = to_dev(wp), to_dev(wc)
+    (Ha, oa, psa, pna, sa), (Hb, ob, psb, pnb, sb) = _lazy_vs_separate(bole, tp, tc)
+    assert psa.tolist() == [0, 2, 3, 0, 3, 3, 0]
+    assert sa.tolist() == [0, 0, 0, 2, 0, 0, 0]
+    np.testing.assert_array_equal(psb, psa)
+    np.testing.assert_array_equal(pnb, pna)
+    np.testing.assert_array_equal(sb, sa)
+    H0 = wp.layers[0].H0.numpy()
+    for b in (1, 2, 4, 5):
+        np.testing.assert_array_equal(Hb[b], H0[b])
+    assert rel_err_states(Hb, Ha) <= 1e-6
+    bad = np.arange(wc.node_offsets[3], wc.node_offsets[4])
+    assert np.isnan(ob[bad]).all() and np.isnan(oa[bad]).all()
+    good = np.setdiff1d(np.arange(ob.shape[0]), bad)
+    assert rel_err_rows(ob[good].astype(np.float64), oa[good].astype(np.float64)) <= 1e-5
+
+    # a previous tree over the <= 32 budget, and unordered previous offsets
+    wp2 = W.make_random(17, batch=3, heads=2, d_k=128, d_v=64, sizes=[33, 3, 4])
+    wc2 = W.make_random(18, batch=3, heads=2, d_k=128, d_v=64, sizes=[5, 64, 2])
+    tp2, tc2 = to_dev(wp2), to_dev(wc2)
+    (Ha, oa, psa, pna, sa), (Hb, ob, psb, pnb, sb) = _lazy_vs_separate(bole, tp2, tc2,
+                                                                      prev_trees_le_32=True)
+    assert psa[0] == 1 and psb.tolist() == psa.tolist()
+    np.testing.assert_array_equal(pnb, pna)
+    np.testing.assert_array_equal(Hb[0], wp2.layers[0].H0.numpy()[0])
+    assert rel_err_states(Hb, Ha) <= 1e-6 and rel_err_rows(ob, oa) <= 1e-5
+    tp2["offs"] = torch.tensor([0, 33, 30, 40], dtype=torch.int32, device=dev())
+    (Ha, oa, psa, pna, sa), (Hb, ob, psb, pnb, sb) = _lazy_vs_separate(bole, tp2, tc2)
+    _, _, ost = oracle.commit_serial(wp2.layers[0].H0, wp2.layers[0].k, wp2.layers[0].v,
+                                     wp2.layers[0].gate, wp2.parent,
+                                     np.array([0, 33, 30, 40], np.int32), wp2.accepted_idx,
+                                     wp2.accepted_len, False)
+    assert psa.tolist() == ost.tolist() == [0, 1, 2] and psb.tolist() == psa.tolist()
+    np.testing.assert_array_equal(pnb, pna)
+    assert rel_err_states(Hb, Ha) <= 1e-6 and rel_err_rows(ob, oa) <= 1e-5
+
+
+def test_lazy_commit_decode_loop(bole):
+    """Three steps run eagerly (verify, commit, verify, commit, ...) and lazily (verify,
+    then verify with the previous commit folded in, and a final commit)."""
+    shared = dict(batch=8, heads=4, d_k=128, d_v=64)
+    steps = [W.make_random(700 + i, **shared) for i in range(3)]
+    ts = [to_dev(w) for w in steps]
+    H_e = ts[0]["H0"].clone()
+    outs_e = []
+    for t in ts:
+        outs_e.append(bole.bole_tree_verify(H_e, t["q"], t["k"], t["v"], t["gate"], t["parent"],
+                                            t["offs"]))
+        bole.bole_commit_path(H_e, t["k"], t["v"], t["gate"], t["parent"], t["offs"],
+                              t["acc_idx"], t["acc_len"])
+    H_l = ts[0]["H0"].clone()
+    outs_l = [bole.bole_tree_verify(H_l, ts[0]["q"], ts[0]["k"], ts[0]["v"], ts[0]["gate"],
+                                    ts[0]["parent"], ts[0]["offs"])]
+    for i in (1, 2):
+        p, t = ts[i - 1], ts[i]
+        outs_l.append(bole.bole_tree_verify_lazy_commit(
+            H_l, (p["k"], p["v"], p["gate"], p["parent"], p["offs"]), p["acc_idx"], p["acc_len"],
+            t["q"], t["k"], t["v"], t["gate"], t["parent"], t["offs"]))
+    t = ts[2]
+    bole.bole_commit_path(H_l, t["k"], t["v"], t["gate"], t["parent"], t["offs"], t["acc_idx"],
+                          t["acc_len"])
+    torch.cuda.synchronize()
+    for oe, ol in zip(outs_e, outs_l):
+        assert rel_err_rows(ol.double().cpu().numpy(), oe.double().cpu().numpy()) <= 1e-5
+    assert rel_err_states(H_l.double().cpu().numpy(), H_e.double().cpu().numpy()) <= 1e-6
+
+
 def test_resume_verify_commit_verify(bole):
     """verify(next tree) on the GPU-committed state equals the oracle's verify of the
     accepted path with the next tree hung below it, on the old state."""

@@ -22,7 +22,8 @@ BOLE_FLAG_TREES_LE_32 = 2
 MAX_TREE_NODES = 64
 
 EXPORTED = ("bole_max_tree_nodes", "bole_status_string", "bole_check_dims", "bole_tree_verify",
-            "bole_tree_verify_naive", "bole_commit_path", "bole_tree_prepare")
+            "bole_tree_verify_lazy_commit", "bole_tree_verify_naive", "bole_commit_path",
+            "bole_tree_prepare")
 
 
 class bole_dims_t(ctypes.Structure):
@@ -56,6 +57,9 @@ def _load():
     lib.bole_check_dims.argtypes = [D, I32]
     lib.bole_tree_verify.restype = ctypes.c_int
     lib.bole_tree_verify.argtypes = [P, P, P, P, P, P, P, P, D, P, P]
+    lib.bole_tree_verify_lazy_commit.restype = ctypes.c_int
+    lib.bole_tree_verify_lazy_commit.argtypes = [P, ctypes.POINTER(bole_factors_t), P, P, D, P, P,
+                                                 P, P, P, P, P, P, P, D, P, P]
     lib.bole_tree_verify_naive.restype = ctypes.c_int
     lib.bole_tree_verify_naive.argtypes = [P, P, P, P, P, P, P, P, P, D, P, P]
     lib.bole_commit_path.restype = ctypes.c_int
@@ -185,6 +189,62 @@ def bole_tree_verify_naive(H0, q, k, v, gate, parent, node_offsets, out=None, st
     return out, states
 
 
+def _lazy_args(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate, parent,
+               node_offsets, out, prev_path_nodes, prev_tree_status, tree_status, stream,
+               trees_le_32, prev_trees_le_32):
+    pk, pv, pgate, pparent, poffs = prev
+    B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
+    pB, pH, pdk, pdv, pT, pvec = _factor_dims(H0, pk, pv, pgate, pparent, poffs)
+    if pk.dtype != k.dtype or pvec != vec:
+        raise ValueError("the previous step's factors must match this step's dtype and gate kind")
+    _need(q, "q", k.dtype, H0.device)
+    if tuple(q.shape) != tuple(k.shape):
+        raise ValueError("q must have the shape of k")
+    _need(prev_accepted_idx, "prev_accepted_idx", torch.int32, H0.device)
+    _need(prev_accepted_len, "prev_accepted_len", torch.int32, H0.device)
+    if (prev_accepted_idx.dim() != 2 or prev_accepted_idx.shape[0] != B
+            or tuple(prev_accepted_len.shape) != (B,)):
+        raise ValueError("prev_accepted_idx must be [B, max_path] and prev_accepted_len [B]")
+    max_path = prev_accepted_idx.shape[1]
+    if out is None:
+        out = torch.empty((T, Hh, d_v), dtype=torch.float32, device=H0.device)
+    _need(out, "out", torch.float32, H0.device)
+    if tuple(out.shape) != (T, Hh, d_v):
+        raise ValueError("out must be [T, H, d_v]")
+    for t, name in ((prev_path_nodes, "prev_path_nodes"), (prev_tree_status, "prev_tree_status"),
+                    (tree_status, "tree_status")):
+        if t is not None:
+            _need(t, name, torch.int32, H0.device)
+    if prev_path_nodes is not None and tuple(prev_path_nodes.shape) != (B, max_path):
+        raise ValueError("prev_path_nodes must be [B, max_path]")
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, trees_le_32=trees_le_32)
+    pdims = make_dims(B, Hh, d_k, d_v, pT, k.dtype, vec, max_path, trees_le_32=prev_trees_le_32)
+    f = bole_factors_t(pk.data_ptr(), pv.data_ptr(), pgate.data_ptr(), pparent.data_ptr(),
+                       poffs.data_ptr())
+    args = (_ptr(H0), ctypes.byref(f), _ptr(prev_accepted_idx), _ptr(prev_accepted_len),
+            ctypes.byref(pdims), _ptr(prev_path_nodes), _ptr(prev_tree_status), _ptr(q), _ptr(k),
+            _ptr(v), _ptr(gate), _ptr(parent), _ptr(node_offsets), _ptr(out), ctypes.byref(dims),
+            _ptr(tree_status), _stream(stream))
+    keep = (H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate, parent, node_offsets,
+            out, prev_path_nodes, prev_tree_status, tree_status, dims, pdims, f)
+    return out, args, keep
+
+
+def bole_tree_verify_lazy_commit(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate,
+                                 parent, node_offsets, out=None, prev_path_nodes=None,
+                                 prev_tree_status=None, tree_status=None, stream=None,
+                                 trees_le_32=False, prev_trees_le_32=False):
+    """Commits the previous step's accepted path into H0 and verifies this step's tree
+    against the result, in one pass over H0. prev = (k, v, gate, parent, node_offsets)
+    of the previous step. Same result as bole_commit_path(previous step) followed by
+    bole_tree_verify(this step); returns out."""
+    out, args, _ = _lazy_args(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate,
+                              parent, node_offsets, out, prev_path_nodes, prev_tree_status,
+                              tree_status, stream, trees_le_32, prev_trees_le_32)
+    _check(lib.bole_tree_verify_lazy_commit(*args), "bole_tree_verify_lazy_commit")
+    return out
+
+
 class _Bound:
     """A launch whose arguments were checked and marshalled once; calling it enqueues the
     same C call again (the tensors are kept alive by the object)."""
@@ -241,6 +301,18 @@ def bind_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepte
     return _Bound(lib.bole_commit_path, "bole_commit_path", args,
                   (H0, k, v, gate, parent, node_offsets, accepted_idx, accepted_len, path_nodes,
                    tree_status, dims, f))
+
+
+def bind_tree_verify_lazy_commit(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate,
+                                 parent, node_offsets, out, prev_path_nodes=None,
+                                 prev_tree_status=None, tree_status=None, stream=None,
+                                 trees_le_32=False, prev_trees_le_32=False):
+    """Same checks as bole_tree_verify_lazy_commit, done once; returns a callable that
+    launches it on these buffers each time it is called."""
+    _, args, keep = _lazy_args(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate,
+                               parent, node_offsets, out, prev_path_nodes, prev_tree_status,
+                               tree_status, stream, trees_le_32, prev_trees_le_32)
+    return _Bound(lib.bole_tree_verify_lazy_commit, "bole_tree_verify_lazy_commit", args, keep)
 
 
 def bole_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepted_len,

@@ -37,6 +37,21 @@ hipError_t launch_verify_vec(const float *H0, const void *q, const void *k, cons
                              const int32_t *node_offsets, float *out, const bole_dims_t &d,
                              int32_t *tree_status, hipStream_t stream);
 
+// True when the one-pass lazy commit + verify kernel covers this pair of steps.
+bool verify_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const float *H0,
+                         const void *q, const void *k, const void *v, const void *out,
+                         const bole_factors_t &prev);
+
+hipError_t launch_verify_lazy_commit(float *H0, const bole_factors_t &prev,
+                                     const int32_t *prev_accepted_idx,
+                                     const int32_t *prev_accepted_len, const bole_dims_t &pd,
+                                     int32_t *prev_path_nodes, int32_t *prev_tree_status,
+                                     const void *q, const void *k, const void *v,
+                                     const float *gate, const int32_t *parent,
+                                     const int32_t *node_offsets, float *out,
+                                     const bole_dims_t &d, int32_t *tree_status,
+                                     hipStream_t stream);
+
 hipError_t launch_verify_naive(const float *H0, const void *q, const void *k, const void *v,
                                const float *gate, const int32_t *parent,
                                const int32_t *node_offsets, float *out, float *states,

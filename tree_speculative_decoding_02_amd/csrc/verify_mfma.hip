@@ -52,12 +52,25 @@ namespace bole {
 // Both terms land in one accumulator layout: lane (n, g) holds node 16it + 4g + r,
 // state columns 4n .. 4n+3 across its four tiles, stored as one 16-byte write per row.
 // Read-once and write-once streams carry the non-temporal cache policy.
-template <int DK, int DV, int NWT>
+// The previous step's factors and accepted path, for the lazy-commit form (LAZY): the
+// kernel first applies that path to H_0 in registers and writes the committed state
+// back, then verifies this step's tree against it.
+struct LazyCommit {
+    const __bf16 *k, *v;
+    const float *gate;
+    const int32_t *parent, *node_offsets, *accepted_idx, *accepted_len;
+    int32_t *path_nodes, *tree_status;
+    int T, max_path, max_n;
+};
+
+template <int DK, int DV, int NWT, bool LAZY>
 __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
-    const float *__restrict__ H0, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
+    const float *__restrict__ H0c, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     const __bf16 *__restrict__ v, const float *__restrict__ gate,
     const int32_t *__restrict__ parent, const int32_t *__restrict__ node_offsets,
-    float *__restrict__ out, int32_t *__restrict__ tree_status, int H, int T, int U, int max_n) {
+    float *__restrict__ out, int32_t *__restrict__ tree_status, int H, int T, int U, int max_n,
+    LazyCommit lc) {
+    static_assert(!LAZY || NWT == 1, "the lazy commit runs in the one-wavefront instantiation");
     constexpr int NN = 32 * NWT;            // node rows staged
     constexpr int NT = 2 * NWT;             // 16-node tiles per wavefront
     constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
@@ -72,6 +85,10 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
     __shared__ bf16x8 s_k[NN * PPR];        // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR)
     __shared__ __bf16 s_v[NN * CW];         // V rows of the group's columns, row j at [CW j]
+    // lazy commit: k rows and v rows (group columns) of up to kLazyStage path nodes
+    constexpr int kLazyStage = LAZY ? 8 : 1;
+    __shared__ __bf16 s_pk[kLazyStage * DK], s_pv[kLazyStage * CW];
+    float *H0 = const_cast<float *>(H0c);   // written only by the lazy commit
 
     const int lane = lane_id();
     const int wave = NWT == 1 ? 0 : (int)(threadIdx.x >> 6);
@@ -92,40 +109,65 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     const bool writer = tree_status != nullptr && h == 0 && cg == 0 && threadIdx.x == 0;
 
     const TreeRange tr = tree_range(node_offsets, b, T, NWT == 1 ? max_n : kMaxTree);
+    bool do_verify = true;
     if (NWT == 1) {
         if (tr.status != BOLE_TREE_OK) {
             if (writer) tree_status[b] = tr.status;
-            return;
-        }
-        if (tr.n > 32) return;  // the NWT = 2 instantiation's
-        if (tr.n == 0) {
+            do_verify = false;
+        } else if (tr.n > 32) {
+            do_verify = false;  // the NWT = 2 instantiation's
+        } else if (tr.n == 0) {
             if (writer) tree_status[b] = BOLE_TREE_OK;
-            return;
+            do_verify = false;
         }
     } else {
-        if (tr.status != BOLE_TREE_OK || tr.n <= 32) return;
+        if (tr.status != BOLE_TREE_OK || tr.n <= 32) do_verify = false;
     }
-    const int lo = tr.lo, n = tr.n;
+    // the previous step's path: plausible from its length and offsets alone (validated
+    // below, once its parent links and indices are in)
+    TreeRange ptr = {0, 0, BOLE_TREE_OK};
+    int plen_raw = 0;
+    bool plikely = false;
+    if constexpr (LAZY) {
+        ptr = tree_range(lc.node_offsets, b, lc.T, lc.max_n);
+        plen_raw = lc.accepted_len[b];
+        plikely = ptr.status == BOLE_TREE_OK && plen_raw > 0 && plen_raw <= lc.max_path &&
+                  plen_raw <= ptr.n;
+    }
+    if (!LAZY && !do_verify) return;
+    const int lo = do_verify ? tr.lo : 0, n = do_verify ? tr.n : 1;
     const int last = n - 1;
     const uint32_t rq = (uint32_t)H * DK, rv = (uint32_t)H * DV;
     const __bf16 *qu = q + (size_t)lo * rq + (size_t)h * DK;
     const __bf16 *ku = k + (size_t)lo * rq + (size_t)h * DK;
     const __bf16 *vu = v + (size_t)lo * rv + (size_t)h * DV + c0;
     float *ou = out + (size_t)lo * rv + (size_t)h * DV + c0;
-    const float *hu = H0 + (size_t)unit * DK * DV + c0;
+    float *hu = H0 + (size_t)unit * DK * DV + c0;
 
     // ---- 1. issue every load
+    // lazy commit, first: the path indices this lane's factor chunks and the validation
+    // need (a chunk is 16 bytes of a path node's k row or of its v row's group columns)
+    constexpr int LCK = DK / 8, LCV = CW / 8, LCPN = LCK + LCV;  // chunks per path node
+    constexpr int LCH = LAZY ? (kLazyStage * LCPN + 63) / 64 : 1;  // chunks per lane
+    int lx[LCH];
+    int lpx = -1, lpp = -1;  // lane = path position: accepted index; lane = node: parent
+    if constexpr (LAZY) {
+        const int32_t *acc_b = lc.accepted_idx + (size_t)b * lc.max_path;
+#pragma unroll
+        for (int u = 0; u < LCH; ++u) {
+            const int m = (lane + 64 * u) / LCPN;
+            lx[u] = (plikely && m < plen_raw) ? acc_b[m] : 0;
+        }
+        if (ptr.status == BOLE_TREE_OK && ptr.n > 0) {
+            lpp = lane < ptr.n ? lc.parent[ptr.lo + lane] : -1;
+            if (lane < plen_raw && plen_raw <= lc.max_path) lpx = acc_b[lane];
+        }
+    }
     const uint32_t node = (uint32_t)min(lane, last);
-    const int p_raw = parent[lo + node];
-    const float g_raw = gate[(size_t)lo * H + h + node * (uint32_t)H];
+    const int p_raw = do_verify ? parent[lo + node] : -1;
+    const float g_raw = do_verify ? gate[(size_t)lo * H + h + node * (uint32_t)H] : 1.f;
     // Q fragments of the tiles: row 16it + n, elements 32t + 8g .. +7
     bf16x8 qf[NT][KT];
-#pragma unroll
-    for (int it = 0; it < NT; ++it)
-#pragma unroll
-        for (int t = 0; t < KT; ++t)
-            qf[it][t] = load16_stream(
-                qu + ((uint32_t)min(16 * it + n16, last) * rq + 32 * t + 8 * g));
     // K and V rows go to LDS through registers (plain loads, so every later wait counts
     // exactly what it needs: no LDS instruction has to wait for the H_0 loads). K: load
     // s fills LDS slots 64s .. 64s+63, i.e. rows (64/PPR)s ..; lane l fills slot 64s + l
@@ -134,31 +176,120 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     // every NWT-th load.
     constexpr int KL = NN * PPR / 64 / NWT, VL = NN * VPR / 64 / NWT;
     bf16x8 kst[KL], vst[VL];
+    if (do_verify) {
 #pragma unroll
-    for (int u = 0; u < KL; ++u) {
-        const int s = wave + NWT * u;
-        const int j = (64 / PPR) * s + lane / PPR;
-        const int pc = (lane % PPR) ^ (j % PPR);
-        kst[u] = load16_stream(ku + ((uint32_t)min(j, last) * rq + 8 * pc));
-    }
+        for (int it = 0; it < NT; ++it)
 #pragma unroll
-    for (int u = 0; u < VL; ++u) {
-        const int s = wave + NWT * u;
-        const int j = (64 / VPR) * s + lane / VPR;
-        vst[u] = load16_stream(vu + ((uint32_t)min(j, last) * rv + 8 * (lane % VPR)));
+            for (int t = 0; t < KT; ++t)
+                qf[it][t] = load16_stream(
+                    qu + ((uint32_t)min(16 * it + n16, last) * rq + 32 * t + 8 * g));
+#pragma unroll
+        for (int u = 0; u < KL; ++u) {
+            const int s = wave + NWT * u;
+            const int j = (64 / PPR) * s + lane / PPR;
+            const int pc = (lane % PPR) ^ (j % PPR);
+            kst[u] = load16_stream(ku + ((uint32_t)min(j, last) * rq + 8 * pc));
+        }
+#pragma unroll
+        for (int u = 0; u < VL; ++u) {
+            const int s = wave + NWT * u;
+            const int j = (64 / VPR) * s + lane / VPR;
+            vst[u] = load16_stream(vu + ((uint32_t)min(j, last) * rv + 8 * (lane % VPR)));
+        }
     }
     // H_0 slice: load s = 8t + e, lane (n, g): row 32t + 8g + e, columns cw0 + CPL*n ..
     hvec hreg[HS];
+    if (do_verify || plikely) {
 #pragma unroll
-    for (int s = 0; s < HS; ++s)
-        hreg[s] = __builtin_nontemporal_load(reinterpret_cast<const hvec *>(
-            hu + ((uint32_t)(32 * (s >> 3) + 8 * g + (s & 7)) * DV + cw0 + CPL * n16)));
+        for (int s = 0; s < HS; ++s)
+            hreg[s] = __builtin_nontemporal_load(reinterpret_cast<const hvec *>(
+                hu + ((uint32_t)(32 * (s >> 3) + 8 * g + (s & 7)) * DV + cw0 + CPL * n16)));
+    }
+    if (do_verify) {
+#pragma unroll
+        for (int u = 0; u < KL; ++u) s_k[64 * (wave + NWT * u) + lane] = kst[u];
+#pragma unroll
+        for (int u = 0; u < VL; ++u)
+            *reinterpret_cast<bf16x8 *>(s_v + 512 * (wave + NWT * u) + 8 * lane) = vst[u];
+    }
 
+    // ---- lazy commit: validate the previous path, stage its factors, update H_0 in
+    // registers, write it back (same rules and outputs as bole_commit_path)
+    if constexpr (LAZY) {
+        int st = ptr.status, plen = 0;
+        float pa = 1.f;  // lane m: scalar gate of path node m
+        if (st == BOLE_TREE_OK && ptr.n > 0) {
+            const int pn = ptr.n;
+            const bool len_ok = plen_raw >= 0 && plen_raw <= lc.max_path;
+            const int x = lane < plen_raw ? lpx : -1;
+            if (__any(lane < pn && (lpp < -1 || lpp >= lane))) {
+                st = BOLE_TREE_BAD_PARENT;
+            } else if (!len_ok) {
+                st = BOLE_TREE_BAD_PATH;
+            } else {
+                const int px = __shfl(lpp, (x >= 0 && x < pn) ? x : 0, 64);
+                const int prev_raw = __shfl(x, lane > 0 ? lane - 1 : 0, 64);
+                const int prev = lane == 0 ? -1 : prev_raw;
+                const bool bad = lane < plen_raw && (x < 0 || x >= pn || px != prev);
+                if (__any(bad)) st = BOLE_TREE_BAD_PATH;
+                else plen = plen_raw;
+            }
+            if (plen > 0 && lane < plen) pa = lc.gate[(size_t)(ptr.lo + x) * H + h];
+            const int row = (st == BOLE_TREE_OK && lane < plen) ? ptr.lo + x : -1;
+            if (h == 0 && cg == 0) {
+                if (lane == 0 && lc.tree_status) lc.tree_status[b] = st;
+                if (lc.path_nodes && lane < lc.max_path) lc.path_nodes[(size_t)b * lc.max_path + lane] = row;
+            }
+        } else {
+            if (st == BOLE_TREE_OK && plen_raw != 0) st = BOLE_TREE_BAD_PATH;  // empty tree
+            if (h == 0 && cg == 0) {
+                if (lane == 0 && lc.tree_status) lc.tree_status[b] = st;
+                if (lc.path_nodes && lane < lc.max_path) lc.path_nodes[(size_t)b * lc.max_path + lane] = -1;
+            }
+        }
+        if (plen > 0) {
+            // stage kLazyStage path nodes at a time: chunk c of the stage is node c / LCPN
+            for (int m0 = 0; m0 < plen; m0 += kLazyStage) {
+                const int mc = min(kLazyStage, plen - m0);
 #pragma unroll
-    for (int u = 0; u < KL; ++u) s_k[64 * (wave + NWT * u) + lane] = kst[u];
+                for (int u = 0; u < LCH; ++u) {
+                    const int c = lane + 64 * u;
+                    const int m = c / LCPN, part = c - m * LCPN;
+                    // every lane takes part in the shuffle; only m < mc use the result
+                    const int xs = __shfl(lpx, min(m0 + m, 63), 64);
+                    if (m < mc) {
+                        const int xm = m0 == 0 ? lx[u] : xs;
+                        const size_t prow = (size_t)(ptr.lo + min(max(xm, 0), ptr.n - 1)) * H + h;
+                        if (part < LCK)
+                            *reinterpret_cast<bf16x8 *>(s_pk + m * DK + 8 * part) =
+                                load16(lc.k + prow * DK + 8 * part);
+                        else
+                            *reinterpret_cast<bf16x8 *>(s_pv + m * CW + 8 * (part - LCK)) =
+                                load16(lc.v + prow * DV + c0 + 8 * (part - LCK));
+                    }
+                }
+                for (int m = 0; m < mc; ++m) {
+                    const float a = readlane_f(pa, m0 + m);
+                    const vvec vv = *reinterpret_cast<const vvec *>(s_pv + m * CW + cw0 + CPL * n16);
 #pragma unroll
-    for (int u = 0; u < VL; ++u)
-        *reinterpret_cast<bf16x8 *>(s_v + 512 * (wave + NWT * u) + 8 * lane) = vst[u];
+                    for (int t = 0; t < KT; ++t) {
+                        const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(s_pk + m * DK + 32 * t + 8 * g);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+#pragma unroll
+                            for (int c = 0; c < CPL; ++c)
+                                hreg[8 * t + e][c] = a * hreg[8 * t + e][c] +
+                                                     static_cast<float>(kk[e]) * static_cast<float>(vv[c]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < HS; ++s)
+                __builtin_nontemporal_store(hreg[s], reinterpret_cast<hvec *>(
+                    hu + ((uint32_t)(32 * (s >> 3) + 8 * g + (s & 7)) * DV + cw0 + CPL * n16)));
+        }
+        if (!do_verify) return;
+    }
 
     // ---- 2. topology and base-2 cumulative decay, lane = node (every wavefront)
     const float lg2 = lane < n ? __builtin_amdgcn_logf(g_raw) : 0.f;
@@ -303,33 +434,40 @@ template <int DK, int DV>
 static void launch_shape(const float *H0, const __bf16 *q, const __bf16 *k, const __bf16 *v,
                          const float *gate, const int32_t *parent, const int32_t *node_offsets,
                          float *out, const bole_dims_t &d, int32_t *tree_status,
-                         hipStream_t stream) {
+                         hipStream_t stream, const LazyCommit *lazy) {
     const unsigned U = (unsigned)d.batch * (unsigned)d.heads;
     const int max_n = max_tree_nodes(d.flags);
     // one workgroup per (unit, 64-column group); G > 1: ceil(U / 8) slots of 8 units, each
     // slot G column groups wide, so the groups of a unit share an XCD
     constexpr int G = DV < 64 ? 1 : DV / 64;
     const unsigned grid = G == 1 ? U : ((U + 7) / 8) * 8 * G;
-    verify_mfma_tree_kernel<DK, DV, 1><<<dim3(grid), dim3(64), 0, stream>>>(
-        H0, q, k, v, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
-        (int)U, max_n);
-    if (max_n > 32)
-        verify_mfma_tree_kernel<DK, DV, 2><<<dim3(grid), dim3(128), 0, stream>>>(
+    const LazyCommit none = {};
+    if (lazy)
+        verify_mfma_tree_kernel<DK, DV, 1, true><<<dim3(grid), dim3(64), 0, stream>>>(
             H0, q, k, v, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
-            (int)U, max_n);
+            (int)U, max_n, *lazy);
+    else
+        verify_mfma_tree_kernel<DK, DV, 1, false><<<dim3(grid), dim3(64), 0, stream>>>(
+            H0, q, k, v, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
+            (int)U, max_n, none);
+    if (max_n > 32)
+        verify_mfma_tree_kernel<DK, DV, 2, false><<<dim3(grid), dim3(128), 0, stream>>>(
+            H0, q, k, v, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
+            (int)U, max_n, none);
 }
 
 template <int DK>
 static void launch_dk(const float *H0, const void *q, const void *k, const void *v,
                       const float *gate, const int32_t *parent, const int32_t *node_offsets,
-                      float *out, const bole_dims_t &d, int32_t *tree_status, hipStream_t stream) {
+                      float *out, const bole_dims_t &d, int32_t *tree_status, hipStream_t stream,
+                      const LazyCommit *lazy) {
     const __bf16 *qb = static_cast<const __bf16 *>(q), *kb = static_cast<const __bf16 *>(k),
                  *vb = static_cast<const __bf16 *>(v);
     switch (d.d_v) {
-        case 32: launch_shape<DK, 32>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream); break;
-        case 64: launch_shape<DK, 64>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream); break;
-        case 128: launch_shape<DK, 128>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream); break;
-        case 256: launch_shape<DK, 256>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream); break;
+        case 32: launch_shape<DK, 32>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream, lazy); break;
+        case 64: launch_shape<DK, 64>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream, lazy); break;
+        case 128: launch_shape<DK, 128>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream, lazy); break;
+        case 256: launch_shape<DK, 256>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream, lazy); break;
         default: break;
     }
 }
@@ -339,9 +477,52 @@ hipError_t launch_verify_mfma(const float *H0, const void *q, const void *k, con
                               const int32_t *node_offsets, float *out, const bole_dims_t &d,
                               int32_t *tree_status, hipStream_t stream) {
     if (d.d_k == 64)
-        launch_dk<64>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, stream);
+        launch_dk<64>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, stream, nullptr);
     else
-        launch_dk<128>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, stream);
+        launch_dk<128>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, stream, nullptr);
+    return hipGetLastError();
+}
+
+bool verify_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const float *H0,
+                         const void *q, const void *k, const void *v, const void *out,
+                         const bole_factors_t &prev) {
+    if (!verify_mfma_applies(d, H0, q, k, v, out)) return false;
+    // the previous step's factors: same layout and shapes, 16-byte rows
+    if (pd.factor_dtype != d.factor_dtype || pd.gate_kind != d.gate_kind || pd.d_k != d.d_k ||
+        pd.d_v != d.d_v || pd.heads != d.heads || pd.batch != d.batch)
+        return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(prev.k) | reinterpret_cast<uintptr_t>(prev.v);
+    if (a % 16 != 0) return false;
+    const uint64_t row_elems = (uint64_t)pd.heads * (uint64_t)(pd.d_k > pd.d_v ? pd.d_k : pd.d_v);
+    return row_elems * kMaxTree < (1ull << 31);
+}
+
+hipError_t launch_verify_lazy_commit(float *H0, const bole_factors_t &prev,
+                                     const int32_t *prev_accepted_idx,
+                                     const int32_t *prev_accepted_len, const bole_dims_t &pd,
+                                     int32_t *prev_path_nodes, int32_t *prev_tree_status,
+                                     const void *q, const void *k, const void *v,
+                                     const float *gate, const int32_t *parent,
+                                     const int32_t *node_offsets, float *out,
+                                     const bole_dims_t &d, int32_t *tree_status,
+                                     hipStream_t stream) {
+    LazyCommit lz;
+    lz.k = static_cast<const __bf16 *>(prev.k);
+    lz.v = static_cast<const __bf16 *>(prev.v);
+    lz.gate = prev.gate;
+    lz.parent = prev.parent;
+    lz.node_offsets = prev.node_offsets;
+    lz.accepted_idx = prev_accepted_idx;
+    lz.accepted_len = prev_accepted_len;
+    lz.path_nodes = prev_path_nodes;
+    lz.tree_status = prev_tree_status;
+    lz.T = pd.total_nodes;
+    lz.max_path = pd.max_path;
+    lz.max_n = max_tree_nodes(pd.flags);
+    if (d.d_k == 64)
+        launch_dk<64>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, stream, &lz);
+    else
+        launch_dk<128>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, stream, &lz);
     return hipGetLastError();
 }
 
