@@ -3,21 +3,25 @@
 
 Workload: the hybrid layer stack. There are 64 sequences, each with one best-first
 draft tree of 32 nodes, and 8 linear-recurrence layers of 32 heads (d_k=128, d_v=64).
-q/k/v are bf16; the scalar gate and the committed state H0 are fp32.
+q/k/v are bf16; the scalar gate and the committed state H0 are fp32. The 8 layers see
+the same draft tokens, so they share the trees and the accepted paths.
 
-One step:
-  1. bole_tree_verify for layers 0..7, in order, as a forward pass would call them;
-  2. bole_commit_path for layers 0..7: each layer's accepted path goes into its H0 in
-     place.
-All inputs are resident in HBM before the timed region starts. The 8 layers hold
-1 GB, four times the 256 MB last-level cache, so every layer is read cold.
+One decode step does, for every layer, one accepted-path commit and one tree verify. The
+headline step runs them as the decode loop would in steady state: one launch for the
+8-layer stack (bole_tree_verify_lazy_commit_layers) that commits the previous step's
+accepted path into each layer's H0 and verifies this step's tree against the result, so
+H0 is read once and written once per step. The previous step is the same synthetic
+batch (same trees, paths and factors), so every timed step does exactly one commit and
+one verify per layer. The same work as two passes (bole_tree_verify_layers, then
+bole_commit_path_layers: H0 read twice, written once) is timed beside it. All inputs are
+resident in HBM before the timed region starts. The 8 layers hold 1 GB, four times the
+256 MB last-level cache, so every layer is read cold.
 
 The program prints one JSON line:
-  - value: draft nodes verified through the whole stack per second;
-  - roofline: for the dominant kernel, its algorithmic bytes per launch over its
-    average launch time, against the 8 TB/s HBM peak. The launch time is taken with HIP
-    events on the launch stream around each step's group of 8 launches of that kernel,
-    divided by 8 (the launches of a group run back to back);
+  - value: draft nodes verified (and committed) through the whole stack per second;
+  - roofline: for the step's kernel, its algorithmic bytes per launch over its average
+    launch time (HIP events on the launch stream around each launch), against the
+    8 TB/s HBM peak;
   - cpu_baseline: the fp64 CPU oracle timed on this host on whole steps of the same
     workload.
 """
@@ -32,13 +36,15 @@ HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 _CSRC = os.path.join(ROOT, "tree_speculative_decoding_02_amd", "csrc")
 # sources that determine each kernel's memory traffic
+_VERIFY_SOURCES = [os.path.join(_CSRC, f) for f in ("verify_mfma.hip", "mfma_util.h",
+                                                   "bole_device.h", "launch.h")]
 KERNEL_SOURCES = {
-    "verify": [os.path.join(_CSRC, f) for f in ("verify_mfma.hip", "mfma_util.h", "bole_device.h",
-                                                  "launch.h")],
+    "lazy": _VERIFY_SOURCES,
+    "verify": _VERIFY_SOURCES,
     "commit": [os.path.join(_CSRC, f) for f in ("commit.hip", "bole_device.h", "launch.h")],
 }
 # FETCH_SIZE / WRITE_SIZE record of the last counter runs (calibrated bytes per launch)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_commit_hybrid_stack_hbm_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hybrid_stack_hbm_traffic.md")
 
 
 def source_hash(paths):
@@ -73,8 +79,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time for the oracle baseline (whole steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-lazy", action="store_true",
-                    help="skip timing the lazy-commit form of the decode loop")
+    ap.add_argument("--per-layer-forms", action="store_true",
+                    help="also time both forms with one launch per layer (the same kernels "
+                         "as the stacked forms, so leave it off in profiled runs)")
     ap.add_argument("--no-naive", action="store_true",
                     help="skip timing the naive serial-walk baseline")
     ap.add_argument("--config-sweep", action="store_true",
@@ -109,9 +116,9 @@ def commit_bytes(wl, s_f=2):
 
 
 def lazy_bytes(wl, s_f=2):
-    """Algorithmic HBM bytes of one lazy launch (the previous step's commit folded into this
-    step's verify): verify's and commit's bytes, less the second read of H_0 that the
-    two-pass form makes for every (sequence, head) with a non-empty path."""
+    """Algorithmic HBM bytes of one layer of a lazy launch (the previous step's commit
+    folded into this step's verify): verify's and commit's bytes, less the second read of
+    H_0 that the two-pass form makes for every (sequence, head) with a non-empty path."""
     with_path = int((wl.accepted_len > 0).sum())
     return verify_bytes(wl, s_f) + commit_bytes(wl, s_f) - 4 * wl.heads * wl.d_k * wl.d_v * with_path
 
@@ -145,67 +152,76 @@ def main():
     offs = torch.from_numpy(wl.node_offsets).to(dev)
     acc_idx = torch.from_numpy(wl.accepted_idx).to(dev)
     acc_len = torch.from_numpy(wl.accepted_len).to(dev)
-    layers = [dict(H0=g(l.H0), q=g(l.q), k=g(l.k), v=g(l.v), gate=g(l.gate)) for l in wl.layers]
-    outs = [torch.empty((wl.total_nodes, wl.heads, wl.d_v), dtype=torch.float32, device=dev)
-            for _ in range(L)]
+    layers = []
+    for l in wl.layers:
+        y = dict(H0=g(l.H0), q=g(l.q), k=g(l.k), v=g(l.v), gate=g(l.gate),
+                 out=torch.empty((wl.total_nodes, wl.heads, wl.d_v), dtype=torch.float32,
+                                 device=dev))
+        y.update(prev_k=y["k"], prev_v=y["v"], prev_gate=y["gate"])  # previous step: same batch
+        layers.append(y)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
-
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    kw = dict(stream=stream, trees_le_32=True)
 
-    # arguments are checked and marshalled once; the timed loop only enqueues launches
-    vlaunch = [bole.bind_tree_verify(x["H0"], x["q"], x["k"], x["v"], x["gate"], parent, offs,
-                                     outs[l], stream=stream, trees_le_32=True)
-               for l, x in enumerate(layers)]
-    claunch = [bole.bind_commit_path(x["H0"], x["k"], x["v"], x["gate"], parent, offs, acc_idx,
-                                     acc_len, stream=stream, trees_le_32=True) for x in layers]
+    # arguments are checked and marshalled once; the timed loops only enqueue launches
+    lazy = bole.bind_tree_verify_lazy_commit_layers(layers, parent, offs, acc_idx, acc_len, parent,
+                                                    offs, prev_trees_le_32=True, **kw)
+    vstack = bole.bind_tree_verify_layers(layers, parent, offs, **kw)
+    cstack = bole.bind_commit_path_layers(layers, parent, offs, acc_idx, acc_len, **kw)
 
-    def step(rec=None):
-        # rec = (start, verify group done, commit group done): one event pair per kernel
-        # group, since an event between two launches costs the stream several microseconds
-        if rec is not None:
-            rec[0].record(stream)
-        for f in vlaunch:
-            f()
-        if rec is not None:
-            rec[1].record(stream)
-        for f in claunch:
-            f()
-        if rec is not None:
-            rec[2].record(stream)
+    def timed(groups, steps, warmup):
+        """Runs `steps` steps of the launch groups; returns (ms per step from one event
+        pair around all steps, per-group span of each step in ms, wall seconds)."""
+        for _ in range(warmup):
+            for grp in groups:
+                for f in grp:
+                    f()
+        torch.cuda.synchronize()
+        recs = [[ev() for _ in range(len(groups) + 1)] for _ in range(steps)]
+        t0, t1 = ev(), ev()
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        t0.record(stream)
+        for r in recs:
+            # one event pair per launch group: an event between two launches costs the
+            # stream several microseconds
+            r[0].record(stream)
+            for j, grp in enumerate(groups):
+                for f in grp:
+                    f()
+                r[j + 1].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        spans = np.array([[r[j].elapsed_time(r[j + 1]) for j in range(len(groups))] for r in recs])
+        return t0.elapsed_time(t1) / steps, spans, wall
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    records = [(ev(), ev(), ev()) for _ in range(args.steps)]
-    t_start, t_end = ev(), ev()
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t_start.record(stream)
-    for s in range(args.steps):
-        step(records[s])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    gpu_ms = t_start.elapsed_time(t_end)
-    # average launch duration of each kernel = its group's span / launches in the group
-    v_ms = [r[0].elapsed_time(r[1]) / L for r in records]
-    c_ms = [r[1].elapsed_time(r[2]) / L for r in records]
-    ms_per_step = gpu_ms / args.steps
+    # headline: the lazy step, one launch for the stack
+    ms_per_step, l_spans, wall = timed([[lazy]], args.steps, args.warmup)
+    # the same work in two passes, one launch each for the stack
+    tp_ms, tp_spans, _ = timed([[vstack], [cstack]], args.steps, args.warmup)
+
     nodes = wl.total_nodes
-    vb, cb = verify_bytes(wl), commit_bytes(wl)
-    v_us, c_us = 1e3 * float(np.mean(v_ms)), 1e3 * float(np.mean(c_ms))
-    v_gbs, c_gbs = vb / (v_us * 1e3), cb / (c_us * 1e3)
+    lb, vb, cb = lazy_bytes(wl), verify_bytes(wl), commit_bytes(wl)
+
+    def kernel_rec(span_ms, nbytes, what):
+        us = 1e3 * float(np.mean(span_ms))
+        gbs = L * nbytes / (us * 1e3)
+        return {"avg_us_per_launch": us, "median_us_per_launch": 1e3 * float(np.median(span_ms)),
+                "layers_per_launch": L, "avg_us_per_layer": us / L,
+                "bytes_per_launch": L * nbytes, "bytes_per_layer": nbytes, "GB_s": gbs,
+                "frac_hbm_peak": gbs / HBM_PEAK_GBS, "what": what}
+
     kernels = {
-        "verify": {"avg_us": v_us, "median_us": 1e3 * float(np.median(v_ms)),
-                   "bytes_per_launch": vb, "GB_s": v_gbs, "frac_hbm_peak": v_gbs / HBM_PEAK_GBS,
-                   "launches_per_step": L, "nodes_per_s_per_layer": nodes / (v_us * 1e-6)},
-        "commit": {"avg_us": c_us, "median_us": 1e3 * float(np.median(c_ms)),
-                   "bytes_per_launch": cb, "GB_s": c_gbs, "frac_hbm_peak": c_gbs / HBM_PEAK_GBS,
-                   "launches_per_step": L},
+        "lazy": kernel_rec(l_spans[:, 0], lb, "verify_mfma_tree_kernel<128,64,1,lazy>: previous "
+                           "path committed into H0, this tree verified, 8 layers"),
+        "verify": kernel_rec(tp_spans[:, 0], vb, "verify_mfma_tree_kernel<128,64,1>: two-pass "
+                             "form, verify of 8 layers"),
+        "commit": kernel_rec(tp_spans[:, 1], cb, "commit_stream_kernel<bf16,scalar>: two-pass "
+                             "form, commit of 8 layers"),
     }
-    dom = "verify" if v_us >= c_us else "commit"
-    kd = kernels[dom]
+    kd = kernels["lazy"]
     naive = wl.heads * wl.total_nodes * wl.d_k * wl.d_v * 4
     bole_transient = sum(int(layers[0][n].numel() * layers[0][n].element_size())
                          for n in ("k", "v", "gate"))
@@ -224,52 +240,42 @@ def main():
         "data": "synthetic",
         "config": {"workload": "hybrid_stack: 64 sequences x 8 linear-recurrence layers x 32 "
                                "heads, d_k=128, d_v=64, 32-node best-first draft trees, bf16 "
-                               "q/k/v, fp32 scalar gate and state; verify all layers, then "
-                               "commit each layer's accepted path in place",
+                               "q/k/v, fp32 scalar gate and state; per step and layer one "
+                               "accepted-path commit and one tree verify, run as one launch "
+                               "for the stack that commits the previous step's path and "
+                               "verifies this step's tree in one pass over H0",
                    "batch": wl.batch, "layers": L, "heads": wl.heads, "d_k": wl.d_k,
-                   "d_v": wl.d_v, "nodes_per_tree": 32, "parallelism": "single_gpu"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kd["GB_s"],
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["GB_s"] / HBM_PEAK_GBS,
-                     "traffic": recorded_traffic(dom)},
+                   "d_v": wl.d_v, "nodes_per_tree": 32, "step_form": "lazy_commit_stacked",
+                   "parallelism": "single_gpu"},
+        "roofline": {"bound": "hbm", "kernel": "lazy", "achieved": kd["GB_s"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["frac_hbm_peak"],
+                     "traffic": recorded_traffic("lazy")},
         "kernels": kernels,
-        "hbm_GB_s_step": L * (vb + cb) / (ms_per_step * 1e6),
+        "forms": {
+            "lazy_commit_stacked": {"ms_per_step": ms_per_step,
+                                    "value": nodes / (ms_per_step * 1e-3), "launches_per_step": 1},
+            "two_pass_stacked": {"ms_per_step": tp_ms, "value": nodes / (tp_ms * 1e-3),
+                                 "launches_per_step": 2},
+        },
+        "hbm_GB_s_step": L * lb / (ms_per_step * 1e6),
         "wall_ms_per_step": 1e3 * wall / args.steps,
         "transient_bytes_per_layer": {"naive_state_per_node": naive,
                                       "bole_factors": bole_transient,
                                       "reduction": 1.0 - bole_transient / naive},
     }
-
-    # the same decode loop with each step's commit folded into the next step's verify: per
-    # layer, one launch commits the previous step's accepted path into H_0 and verifies this
-    # step's tree against the result (the previous step here is the same synthetic batch)
-    if not args.no_lazy:
-        llaunch = [bole.bind_tree_verify_lazy_commit(
-            x["H0"], (x["k"], x["v"], x["gate"], parent, offs), acc_idx, acc_len, x["q"], x["k"],
-            x["v"], x["gate"], parent, offs, outs[l], stream=stream, trees_le_32=True,
-            prev_trees_le_32=True) for l, x in enumerate(layers)]
-        for _ in range(args.warmup):
-            for f in llaunch:
-                f()
-        torch.cuda.synchronize()
-        lrec = [(ev(), ev()) for _ in range(args.steps)]
-        for s in range(args.steps):
-            lrec[s][0].record(stream)
-            for f in llaunch:
-                f()
-            lrec[s][1].record(stream)
-        torch.cuda.synchronize()
-        l_ms = [a.elapsed_time(b) for a, b in lrec]
-        lb = lazy_bytes(wl)
-        l_us = 1e3 * float(np.mean(l_ms)) / L
-        result["lazy_commit"] = {
-            "ms_per_step": float(np.mean(l_ms)), "value": nodes / (float(np.mean(l_ms)) * 1e-3),
-            "unit": "draft nodes/s", "avg_us_per_launch": l_us,
-            "median_us_per_launch": 1e3 * float(np.median(l_ms)) / L, "bytes_per_launch": lb,
-            "GB_s": lb / (l_us * 1e3), "frac_hbm_peak": lb / (l_us * 1e3) / HBM_PEAK_GBS,
-            "launches_per_step": L, "speedup_vs_two_pass": ms_per_step / float(np.mean(l_ms)),
-            "what": "bole_tree_verify_lazy_commit per layer: the previous step's commit and "
-                    "this step's verify in one pass over H_0 (same work per step in steady "
-                    "state: one commit and one verify per layer)"}
+    if args.per_layer_forms:
+        v1 = [bole.bind_tree_verify(y["H0"], y["q"], y["k"], y["v"], y["gate"], parent, offs,
+                                    y["out"], **kw) for y in layers]
+        c1 = [bole.bind_commit_path(y["H0"], y["k"], y["v"], y["gate"], parent, offs, acc_idx,
+                                    acc_len, **kw) for y in layers]
+        l1 = [bole.bind_tree_verify_lazy_commit(
+            y["H0"], (y["k"], y["v"], y["gate"], parent, offs), acc_idx, acc_len, y["q"], y["k"],
+            y["v"], y["gate"], parent, offs, y["out"], prev_trees_le_32=True, **kw) for y in layers]
+        for name, groups in (("lazy_commit_per_layer", [l1]), ("two_pass_per_layer", [v1, c1])):
+            ms, _, _ = timed(groups, args.steps, args.warmup)
+            result["forms"][name] = {"ms_per_step": ms, "value": nodes / (ms * 1e-3),
+                                     "launches_per_step": L * len(groups)}
+    v_us = kernels["verify"]["avg_us_per_layer"]
 
     # the naive serial walk on layer 0 (one materialised state per node): the baseline the
     # closed form is measured against, timed after the benchmark proper
@@ -280,7 +286,7 @@ def main():
         states = torch.empty((wl.total_nodes, wl.heads, wl.d_k, wl.d_v), dtype=torch.float32,
                              device=dev)
         states_bytes = torch.cuda.memory_allocated(dev) - m0
-        nout = torch.empty_like(outs[0])
+        nout = torch.empty_like(x["out"])
         naive = lambda: bole.bole_tree_verify_naive(x["H0"], x["q"], x["k"], x["v"], x["gate"],
                                                     parent, offs, out=nout, states=states,
                                                     stream=stream)

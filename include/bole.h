@@ -120,6 +120,22 @@ typedef struct {
     const int32_t *node_offsets;  /* [B + 1] */
 } bole_factors_t;
 
+/* One layer of a stack of linear-recurrence layers. The layers of a stack see the same
+ * draft tokens, so they verify the same trees and commit the same accepted paths; only
+ * each layer's state and per-node factors are its own. Every pointer follows the layouts
+ * above, with the same dims for every layer. A host struct of device pointers. */
+typedef struct {
+    float *H0;              /* [B][H][d_k][d_v] this layer's committed state */
+    const void *q;          /* [T][H][d_k] this step's factors */
+    const void *k;          /* [T][H][d_k] */
+    const void *v;          /* [T][H][d_v] */
+    const float *gate;      /* [T][H] or [T][H][d_k] */
+    float *out;             /* [T][H][d_v] verify output; unused by commit */
+    const void *prev_k;     /* lazy commit only: the previous step's k, v and gate, */
+    const void *prev_v;     /* laid out by that step's tree; NULL elsewhere */
+    const float *prev_gate;
+} bole_layer_t;
+
 /* Maximum number of nodes in one tree (one 64-lane wavefront, one 64-bit mask). */
 BOLE_API int32_t bole_max_tree_nodes(void);
 
@@ -169,6 +185,46 @@ BOLE_API bole_status_t bole_tree_verify_lazy_commit(
     int32_t *prev_tree_status, const void *q, const void *k, const void *v, const float *gate,
     const int32_t *parent, const int32_t *node_offsets, float *out, const bole_dims_t *dims,
     int32_t *tree_status, bole_stream_t stream);
+
+/*
+ * Layer stacks: the calls above for num_layers >= 1 layers that share their trees (and
+ * paths), in as few launches as the kernels allow. The matrix-core kernels take up to
+ * 16 layers per launch (blockIdx.y = layer), so that the workgroups of one layer's tail
+ * overlap the next layer's, instead of one launch, ramp and drain per layer. `layers` is
+ * a host array of num_layers entries. Each call's result is exactly that of the
+ * single-layer call on every layer in turn:
+ *  - bole_tree_verify_layers: bole_tree_verify(layer.H0, layer.q, layer.k, layer.v,
+ *    layer.gate, parent, node_offsets, layer.out, dims, tree_status, stream);
+ *  - bole_commit_path_layers: bole_commit_path(layer.H0, {layer.k, layer.v, layer.gate,
+ *    parent, node_offsets}, accepted_idx, accepted_len, dims, path_nodes, tree_status,
+ *    stream);
+ *  - bole_tree_verify_lazy_commit_layers: bole_tree_verify_lazy_commit(layer.H0,
+ *    {layer.prev_k, layer.prev_v, layer.prev_gate, prev_parent, prev_node_offsets},
+ *    prev_accepted_idx, prev_accepted_len, prev_dims, prev_path_nodes, prev_tree_status,
+ *    layer.q, layer.k, layer.v, layer.gate, parent, node_offsets, layer.out, dims,
+ *    tree_status, stream).
+ * The per-tree outputs (tree_status, path_nodes, ...) depend on the trees alone and are
+ * written once. Layers must not overlap in H0 (commit, lazy commit) or out (verify,
+ * lazy commit); two layers with the same H0 or out pointer, num_layers < 1 or a NULL
+ * layers array give BOLE_ERR_INVALID_VALUE.
+ */
+BOLE_API bole_status_t bole_tree_verify_layers(const bole_layer_t *layers, int32_t num_layers,
+                               const int32_t *parent, const int32_t *node_offsets,
+                               const bole_dims_t *dims, int32_t *tree_status,
+                               bole_stream_t stream);
+
+BOLE_API bole_status_t bole_commit_path_layers(const bole_layer_t *layers, int32_t num_layers,
+                               const int32_t *parent, const int32_t *node_offsets,
+                               const int32_t *accepted_idx, const int32_t *accepted_len,
+                               const bole_dims_t *dims, int32_t *path_nodes,
+                               int32_t *tree_status, bole_stream_t stream);
+
+BOLE_API bole_status_t bole_tree_verify_lazy_commit_layers(
+    const bole_layer_t *layers, int32_t num_layers, const int32_t *prev_parent,
+    const int32_t *prev_node_offsets, const int32_t *prev_accepted_idx,
+    const int32_t *prev_accepted_len, const bole_dims_t *prev_dims, int32_t *prev_path_nodes,
+    int32_t *prev_tree_status, const int32_t *parent, const int32_t *node_offsets,
+    const bole_dims_t *dims, int32_t *tree_status, bole_stream_t stream);
 
 /*
  * Baseline: the naive serial walk that the closed form replaces (Bole summary page,

@@ -111,6 +111,32 @@ def test_lazy_commit_checks_both_steps_without_launch():
         bole.BOLE_ERR_INVALID_VALUE
 
 
+
+def test_layer_stacks_checked_without_launch():
+    L = bole.lib
+    d = _dims(max_path=8)
+    one = (bole.bole_layer_t * 1)()
+    assert L.bole_tree_verify_layers(None, 1, None, None, ctypes.byref(d), None, None) == \
+        bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_tree_verify_layers(one, 0, None, None, ctypes.byref(d), None, None) == \
+        bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_tree_verify_layers(one, 1, None, None, ctypes.byref(_dims(batch=0)), None,
+                                     None) == bole.BOLE_OK
+    # two layers on one state (commit) or one output (verify) are rejected; the pointers
+    # below are never dereferenced
+    two = (bole.bole_layer_t * 2)()
+    for e in two:
+        e.H0, e.q, e.k, e.v, e.gate = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000
+    two[0].out, two[1].out = 0x6000, 0x6000
+    assert L.bole_tree_verify_layers(two, 2, 0x7000, 0x8000, ctypes.byref(d), None, None) == \
+        bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_commit_path_layers(two, 2, 0x7000, 0x8000, 0x9000, 0xa000, ctypes.byref(d),
+                                     None, None, None) == bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_tree_verify_lazy_commit_layers(
+        two, 2, 0x7000, 0x8000, 0x9000, 0xa000, ctypes.byref(d), None, None, 0x7000, 0x8000,
+        ctypes.byref(d), None, None) == bole.BOLE_ERR_INVALID_VALUE
+
+
 def test_status_strings_and_limits():
     assert bole.lib.bole_max_tree_nodes() == bole.MAX_TREE_NODES == 64
     for code, name in [(0, b"BOLE_OK"), (1, b"BOLE_ERR_INVALID_VALUE"),

@@ -588,6 +588,140 @@ def test_lazy_commit_decode_loop(bole):
     assert rel_err_states(H_l.double().cpu().numpy(), H_e.double().cpu().numpy()) <= 1e-6
 
 
+def _stack(seed, n_layers, **kw):
+    """A workload whose tree and paths are shared by n_layers layers of independent
+    factors and states (drawn with the same shapes from further seeds)."""
+    wl = W.make_random(seed, **kw)
+    kw = dict(kw, sizes=np.diff(wl.node_offsets).tolist())   # the same tree sizes
+    lays = [wl.layers[0]] + [W.make_random(seed + 1000 * (i + 1), **kw).layers[0]
+                             for i in range(n_layers - 1)]
+    assert all(l.k.shape == wl.layers[0].k.shape for l in lays)
+    return wl, lays
+
+
+def _dev_layers(lays, prev_lays=None):
+    d = dev()
+    out = []
+    for i, l in enumerate(lays):
+        y = dict(H0=l.H0.to(d), q=l.q.to(d), k=l.k.to(d), v=l.v.to(d), gate=l.gate.to(d))
+        if prev_lays is not None:
+            p = prev_lays[i]
+            y.update(prev_k=p.k.to(d), prev_v=p.v.to(d), prev_gate=p.gate.to(d))
+        out.append(y)
+    return out
+
+
+def _tree_dev(wl):
+    d = dev()
+    return dict(parent=torch.from_numpy(wl.parent).to(d), offs=torch.from_numpy(wl.node_offsets).to(d),
+                acc_idx=torch.from_numpy(wl.accepted_idx).to(d),
+                acc_len=torch.from_numpy(wl.accepted_len).to(d))
+
+
+LAYER_CASES = [
+    # (name, layers, make_random kwargs)
+    ("mfma_dv64", 3, dict(batch=6, heads=4, d_k=128, d_v=64)),
+    ("mfma_dv128_big_trees", 2, dict(batch=4, heads=2, d_k=128, d_v=128,
+                                     sizes=[64, 20, 40, 0], max_path=64, kind="deep")),
+    ("seventeen_layers", 17, dict(batch=3, heads=2, d_k=64, d_v=32)),
+    ("vector_gate", 3, dict(batch=3, heads=2, d_k=128, d_v=64, vector_gate=True)),
+    ("fp32", 2, dict(batch=3, heads=2, d_k=64, d_v=64, factor_dtype=torch.float32)),
+]
+
+
+@pytest.mark.parametrize("name,n_layers,kw", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_layer_stack_equals_layer_by_layer(bole, name, n_layers, kw):
+    """Verify, commit and lazy commit of a stack in one call: the same outputs, states and
+    per-tree outputs as the single-layer calls on each layer (same kernels, so bit for
+    bit), and the lazy stack within tolerance of the oracle."""
+    seed = zlib.crc32(name.encode()) % 10000
+    wp, lp = _stack(seed, n_layers, **kw)
+    wc, lc = _stack(seed + 1, n_layers, **kw)
+    tp, tc = _tree_dev(wp), _tree_dev(wc)
+    B = wp.batch
+
+    def status():
+        return torch.full((B,), -7, dtype=torch.int32, device=dev())
+
+    # verify: stack vs layer by layer
+    ys = _dev_layers(lc)
+    st_s = status()
+    outs = bole.bole_tree_verify_layers(ys, tc["parent"], tc["offs"], tree_status=st_s)
+    for y, o in zip(ys, outs):
+        st_1 = status()
+        o1 = bole.bole_tree_verify(y["H0"], y["q"], y["k"], y["v"], y["gate"], tc["parent"],
+                                   tc["offs"], tree_status=st_1)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o1)
+        assert torch.equal(st_s, st_1)
+
+    # commit: stack vs layer by layer
+    ys = _dev_layers(lp)
+    ref = [y["H0"].clone() for y in ys]
+    pn_s, st_s = torch.full(tuple(tp["acc_idx"].shape), -7, dtype=torch.int32, device=dev()), status()
+    bole.bole_commit_path_layers(ys, tp["parent"], tp["offs"], tp["acc_idx"], tp["acc_len"],
+                                 path_nodes=pn_s, tree_status=st_s)
+    for y, H in zip(ys, ref):
+        pn_1, st_1 = torch.empty_like(pn_s), status()
+        bole.bole_commit_path(H, y["k"], y["v"], y["gate"], tp["parent"], tp["offs"],
+                              tp["acc_idx"], tp["acc_len"], path_nodes=pn_1, tree_status=st_1)
+        torch.cuda.synchronize()
+        assert torch.equal(y["H0"], H)
+        assert torch.equal(pn_s, pn_1) and torch.equal(st_s, st_1)
+
+    # lazy commit: stack vs layer by layer, and the stack against the oracle
+    ys = _dev_layers(lc, lp)
+    ref = [y["H0"].clone() for y in ys]
+    pst_s, st_s = status(), status()
+    pn_s = torch.full(tuple(tp["acc_idx"].shape), -7, dtype=torch.int32, device=dev())
+    outs = bole.bole_tree_verify_lazy_commit_layers(
+        ys, tp["parent"], tp["offs"], tp["acc_idx"], tp["acc_len"], tc["parent"], tc["offs"],
+        prev_path_nodes=pn_s, prev_tree_status=pst_s, tree_status=st_s)
+    torch.cuda.synchronize()
+    for i, (y, H, o) in enumerate(zip(ys, ref, outs)):
+        pst_1, st_1 = status(), status()
+        pn_1 = torch.empty_like(pn_s)
+        o1 = bole.bole_tree_verify_lazy_commit(
+            H, (y["prev_k"], y["prev_v"], y["prev_gate"], tp["parent"], tp["offs"]),
+            tp["acc_idx"], tp["acc_len"], y["q"], y["k"], y["v"], y["gate"], tc["parent"],
+            tc["offs"], prev_path_nodes=pn_1, prev_tree_status=pst_1, tree_status=st_1)
+        torch.cuda.synchronize()
+        assert torch.equal(y["H0"], H) and torch.equal(o, o1)
+        assert torch.equal(pst_s, pst_1) and torch.equal(st_s, st_1) and torch.equal(pn_s, pn_1)
+        if i < 3:
+            # the stack's states start from the current layers' H0
+            Href, _, _ = oracle.commit_serial(lc[i].H0, lp[i].k, lp[i].v, lp[i].gate, wp.parent,
+                                              wp.node_offsets, wp.accepted_idx, wp.accepted_len,
+                                              wp.vector_gate)
+            oref, _ = oracle.verify_serial(Href, lc[i].q, lc[i].k, lc[i].v, lc[i].gate,
+                                           wc.parent, wc.node_offsets, wc.vector_gate)
+            tol = TOL[wp.factor_dtype]
+            assert rel_err_states(y["H0"].double().cpu().numpy(), Href) <= tol
+            assert rel_err_rows(o.double().cpu().numpy(), oref) <= tol
+
+
+def test_layer_stack_with_a_misaligned_layer(bole):
+    """A layer whose factor rows are not 16-byte aligned sends its chunk to the kernels
+    that take any alignment; every layer still matches the oracle."""
+    wc, lc = _stack(321, 3, batch=4, heads=2, d_k=128, d_v=64)
+    tc = _tree_dev(wc)
+    ys = _dev_layers(lc)
+    # layer 1: q, k, v copied into buffers offset by one bf16 element
+    for name in ("q", "k", "v"):
+        t = ys[1][name]
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=dev())
+        view = buf[1:].view(t.shape)
+        view.copy_(t)
+        ys[1][name] = view
+    assert ys[1]["k"].data_ptr() % 16 != 0
+    outs = bole.bole_tree_verify_layers(ys, tc["parent"], tc["offs"])
+    torch.cuda.synchronize()
+    for l, o in zip(lc, outs):
+        ref, _ = oracle.verify_serial(l.H0, l.q, l.k, l.v, l.gate, wc.parent, wc.node_offsets,
+                                      False)
+        assert rel_err_rows(o.double().cpu().numpy(), ref) <= TOL[torch.bfloat16]
+
+
 def test_resume_verify_commit_verify(bole):
     """verify(next tree) on the GPU-committed state equals the oracle's verify of the
     accepted path with the next tree hung below it, on the old state."""

@@ -22,7 +22,8 @@ BOLE_FLAG_TREES_LE_32 = 2
 MAX_TREE_NODES = 64
 
 EXPORTED = ("bole_max_tree_nodes", "bole_status_string", "bole_check_dims", "bole_tree_verify",
-            "bole_tree_verify_lazy_commit", "bole_tree_verify_naive", "bole_commit_path",
+            "bole_tree_verify_lazy_commit", "bole_tree_verify_layers", "bole_commit_path_layers",
+            "bole_tree_verify_lazy_commit_layers", "bole_tree_verify_naive", "bole_commit_path",
             "bole_tree_prepare")
 
 
@@ -36,6 +37,13 @@ class bole_dims_t(ctypes.Structure):
 class bole_factors_t(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("parent", ctypes.c_void_p), ("node_offsets", ctypes.c_void_p)]
+
+
+class bole_layer_t(ctypes.Structure):
+    _fields_ = [("H0", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("prev_k", ctypes.c_void_p), ("prev_v", ctypes.c_void_p),
+                ("prev_gate", ctypes.c_void_p)]
 
 
 class BoleError(RuntimeError):
@@ -60,6 +68,13 @@ def _load():
     lib.bole_tree_verify_lazy_commit.restype = ctypes.c_int
     lib.bole_tree_verify_lazy_commit.argtypes = [P, ctypes.POINTER(bole_factors_t), P, P, D, P, P,
                                                  P, P, P, P, P, P, P, D, P, P]
+    LP = ctypes.POINTER(bole_layer_t)
+    lib.bole_tree_verify_layers.restype = ctypes.c_int
+    lib.bole_tree_verify_layers.argtypes = [LP, I32, P, P, D, P, P]
+    lib.bole_commit_path_layers.restype = ctypes.c_int
+    lib.bole_commit_path_layers.argtypes = [LP, I32, P, P, P, P, D, P, P, P]
+    lib.bole_tree_verify_lazy_commit_layers.restype = ctypes.c_int
+    lib.bole_tree_verify_lazy_commit_layers.argtypes = [LP, I32, P, P, P, P, D, P, P, P, P, D, P, P]
     lib.bole_tree_verify_naive.restype = ctypes.c_int
     lib.bole_tree_verify_naive.argtypes = [P, P, P, P, P, P, P, P, P, D, P, P]
     lib.bole_commit_path.restype = ctypes.c_int
@@ -336,6 +351,172 @@ def bole_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepte
                                 _ptr(accepted_len), ctypes.byref(dims), _ptr(path_nodes),
                                 _ptr(tree_status), _stream(stream)), "bole_commit_path")
     return H0
+
+
+# ---- layer stacks: a layer is a dict with H0, q, k, v, gate, and as needed out (verify;
+# allocated when missing) and prev_k, prev_v, prev_gate (lazy commit). All layers share
+# the shapes of the first and the trees passed beside them.
+
+def _layers_args(layers, parent, node_offsets, verify, prev_parent=None, prev_node_offsets=None):
+    if len(layers) < 1:
+        raise ValueError("need at least one layer")
+    y0 = layers[0]
+    dims = _factor_dims(y0["H0"], y0["k"], y0["v"], y0["gate"], parent, node_offsets)
+    B, Hh, d_k, d_v, T, vec = dims
+    pT = None
+    arr = (bole_layer_t * len(layers))()
+    keep = [layers, arr]
+    for i, y in enumerate(layers):
+        H0, k, v, gate = y["H0"], y["k"], y["v"], y["gate"]
+        if _factor_dims(H0, k, v, gate, parent, node_offsets) != dims or k.dtype != y0["k"].dtype:
+            raise ValueError(f"layer {i} does not match layer 0's shapes and dtypes")
+        e = arr[i]
+        e.H0, e.k, e.v, e.gate = H0.data_ptr(), k.data_ptr(), v.data_ptr(), gate.data_ptr()
+        if verify:
+            q = y["q"]
+            _need(q, "q", k.dtype, H0.device)
+            if tuple(q.shape) != tuple(k.shape):
+                raise ValueError("q must have the shape of k")
+            if y.get("out") is None:
+                y["out"] = torch.empty((T, Hh, d_v), dtype=torch.float32, device=H0.device)
+            _need(y["out"], "out", torch.float32, H0.device)
+            if tuple(y["out"].shape) != (T, Hh, d_v):
+                raise ValueError("out must be [T, H, d_v]")
+            e.q, e.out = q.data_ptr(), y["out"].data_ptr()
+        if prev_parent is not None:
+            pk, pv, pg = y["prev_k"], y["prev_v"], y["prev_gate"]
+            pd = _factor_dims(H0, pk, pv, pg, prev_parent, prev_node_offsets)
+            if pk.dtype != k.dtype or pd[5] != vec:
+                raise ValueError("the previous step's factors must match this step's dtype "
+                                 "and gate kind")
+            pT = pd[4]
+            e.prev_k, e.prev_v, e.prev_gate = pk.data_ptr(), pv.data_ptr(), pg.data_ptr()
+    return arr, dims, pT, keep
+
+
+def _status_arg(t, name, B, dev):
+    if t is not None:
+        _need(t, name, torch.int32, dev)
+        if t.numel() < B:
+            raise ValueError(f"{name} needs B entries")
+    return _ptr(t)
+
+
+def _path_args(accepted_idx, accepted_len, path_nodes, B, dev, what=""):
+    _need(accepted_idx, what + "accepted_idx", torch.int32, dev)
+    _need(accepted_len, what + "accepted_len", torch.int32, dev)
+    if accepted_idx.dim() != 2 or accepted_idx.shape[0] != B or tuple(accepted_len.shape) != (B,):
+        raise ValueError(f"{what}accepted_idx must be [B, max_path] and {what}accepted_len [B]")
+    max_path = accepted_idx.shape[1]
+    if path_nodes is not None:
+        _need(path_nodes, what + "path_nodes", torch.int32, dev)
+        if tuple(path_nodes.shape) != (B, max_path):
+            raise ValueError(f"{what}path_nodes must be [B, max_path]")
+    return max_path
+
+
+def _verify_layers_call(layers, parent, node_offsets, tree_status, stream, force_generic,
+                        trees_le_32):
+    arr, (B, Hh, d_k, d_v, T, vec), _, keep = _layers_args(layers, parent, node_offsets, True)
+    dev = layers[0]["H0"].device
+    dims = make_dims(B, Hh, d_k, d_v, T, layers[0]["k"].dtype, vec, 0, force_generic, trees_le_32)
+    args = (arr, len(layers), _ptr(parent), _ptr(node_offsets), ctypes.byref(dims),
+            _status_arg(tree_status, "tree_status", B, dev), _stream(stream))
+    return args, keep + [parent, node_offsets, tree_status, dims]
+
+
+def bole_tree_verify_layers(layers, parent, node_offsets, tree_status=None, stream=None,
+                            force_generic=False, trees_le_32=False):
+    """bole_tree_verify on every layer of a stack that shares the trees, in as few
+    launches as the kernels allow; returns the list of outs."""
+    args, _ = _verify_layers_call(layers, parent, node_offsets, tree_status, stream,
+                                  force_generic, trees_le_32)
+    _check(lib.bole_tree_verify_layers(*args), "bole_tree_verify_layers")
+    return [y["out"] for y in layers]
+
+
+def bind_tree_verify_layers(layers, parent, node_offsets, tree_status=None, stream=None,
+                            force_generic=False, trees_le_32=False):
+    args, keep = _verify_layers_call(layers, parent, node_offsets, tree_status, stream,
+                                     force_generic, trees_le_32)
+    return _Bound(lib.bole_tree_verify_layers, "bole_tree_verify_layers", args, keep)
+
+
+def _commit_layers_call(layers, parent, node_offsets, accepted_idx, accepted_len, path_nodes,
+                        tree_status, stream, trees_le_32):
+    arr, (B, Hh, d_k, d_v, T, vec), _, keep = _layers_args(layers, parent, node_offsets, False)
+    dev = layers[0]["H0"].device
+    max_path = _path_args(accepted_idx, accepted_len, path_nodes, B, dev)
+    dims = make_dims(B, Hh, d_k, d_v, T, layers[0]["k"].dtype, vec, max_path,
+                     trees_le_32=trees_le_32)
+    args = (arr, len(layers), _ptr(parent), _ptr(node_offsets), _ptr(accepted_idx),
+            _ptr(accepted_len), ctypes.byref(dims), _ptr(path_nodes),
+            _status_arg(tree_status, "tree_status", B, dev), _stream(stream))
+    return args, keep + [parent, node_offsets, accepted_idx, accepted_len, path_nodes,
+                         tree_status, dims]
+
+
+def bole_commit_path_layers(layers, parent, node_offsets, accepted_idx, accepted_len,
+                            path_nodes=None, tree_status=None, stream=None, trees_le_32=False):
+    """bole_commit_path of each layer's k, v, gate along the shared accepted paths."""
+    args, _ = _commit_layers_call(layers, parent, node_offsets, accepted_idx, accepted_len,
+                                  path_nodes, tree_status, stream, trees_le_32)
+    _check(lib.bole_commit_path_layers(*args), "bole_commit_path_layers")
+
+
+def bind_commit_path_layers(layers, parent, node_offsets, accepted_idx, accepted_len,
+                            path_nodes=None, tree_status=None, stream=None, trees_le_32=False):
+    args, keep = _commit_layers_call(layers, parent, node_offsets, accepted_idx, accepted_len,
+                                     path_nodes, tree_status, stream, trees_le_32)
+    return _Bound(lib.bole_commit_path_layers, "bole_commit_path_layers", args, keep)
+
+
+def _lazy_layers_call(layers, prev_parent, prev_node_offsets, prev_accepted_idx,
+                      prev_accepted_len, parent, node_offsets, prev_path_nodes, prev_tree_status,
+                      tree_status, stream, trees_le_32, prev_trees_le_32):
+    arr, (B, Hh, d_k, d_v, T, vec), pT, keep = _layers_args(
+        layers, parent, node_offsets, True, prev_parent, prev_node_offsets)
+    dev = layers[0]["H0"].device
+    max_path = _path_args(prev_accepted_idx, prev_accepted_len, prev_path_nodes, B, dev, "prev_")
+    fd = layers[0]["k"].dtype
+    dims = make_dims(B, Hh, d_k, d_v, T, fd, vec, 0, trees_le_32=trees_le_32)
+    pdims = make_dims(B, Hh, d_k, d_v, pT, fd, vec, max_path, trees_le_32=prev_trees_le_32)
+    args = (arr, len(layers), _ptr(prev_parent), _ptr(prev_node_offsets), _ptr(prev_accepted_idx),
+            _ptr(prev_accepted_len), ctypes.byref(pdims), _ptr(prev_path_nodes),
+            _status_arg(prev_tree_status, "prev_tree_status", B, dev), _ptr(parent),
+            _ptr(node_offsets), ctypes.byref(dims), _status_arg(tree_status, "tree_status", B, dev),
+            _stream(stream))
+    return args, keep + [prev_parent, prev_node_offsets, prev_accepted_idx, prev_accepted_len,
+                         parent, node_offsets, prev_path_nodes, prev_tree_status, tree_status,
+                         dims, pdims]
+
+
+def bole_tree_verify_lazy_commit_layers(layers, prev_parent, prev_node_offsets,
+                                        prev_accepted_idx, prev_accepted_len, parent,
+                                        node_offsets, prev_path_nodes=None, prev_tree_status=None,
+                                        tree_status=None, stream=None, trees_le_32=False,
+                                        prev_trees_le_32=False):
+    """bole_tree_verify_lazy_commit on every layer of a stack (each layer's prev_k,
+    prev_v, prev_gate along the shared previous path, then its verify); returns the outs."""
+    args, _ = _lazy_layers_call(layers, prev_parent, prev_node_offsets, prev_accepted_idx,
+                                prev_accepted_len, parent, node_offsets, prev_path_nodes,
+                                prev_tree_status, tree_status, stream, trees_le_32,
+                                prev_trees_le_32)
+    _check(lib.bole_tree_verify_lazy_commit_layers(*args), "bole_tree_verify_lazy_commit_layers")
+    return [y["out"] for y in layers]
+
+
+def bind_tree_verify_lazy_commit_layers(layers, prev_parent, prev_node_offsets,
+                                        prev_accepted_idx, prev_accepted_len, parent,
+                                        node_offsets, prev_path_nodes=None, prev_tree_status=None,
+                                        tree_status=None, stream=None, trees_le_32=False,
+                                        prev_trees_le_32=False):
+    args, keep = _lazy_layers_call(layers, prev_parent, prev_node_offsets, prev_accepted_idx,
+                                   prev_accepted_len, parent, node_offsets, prev_path_nodes,
+                                   prev_tree_status, tree_status, stream, trees_le_32,
+                                   prev_trees_le_32)
+    return _Bound(lib.bole_tree_verify_lazy_commit_layers, "bole_tree_verify_lazy_commit_layers",
+                  args, keep)
 
 
 def bole_tree_prepare(parent, node_offsets, heads=1, d_k=1, gate=None, want_cumlog=False,

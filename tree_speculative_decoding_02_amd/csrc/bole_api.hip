@@ -12,19 +12,103 @@ enum { kOpVerify = 0, kOpCommit = 1, kOpPrepare = 2 };
 
 bole_status_t from_hip(hipError_t e) { return e == hipSuccess ? BOLE_OK : BOLE_ERR_HIP; }
 
-// Verify kernel choice for checked arguments: matrix cores when they cover the request.
-hipError_t dispatch_verify(const float *H0, const void *q, const void *k, const void *v,
-                           const float *gate, const int32_t *parent, const int32_t *node_offsets,
-                           float *out, const bole_dims_t &d, int32_t *tree_status,
-                           hipStream_t s) {
-    if (bole::verify_mfma_applies(d, H0, q, k, v, out))
-        return bole::launch_verify_mfma(H0, q, k, v, gate, parent, node_offsets, out, d,
-                                        tree_status, s);
-    if (bole::verify_vec_applies(d, H0, q, k, v, gate, out))
-        return bole::launch_verify_vec(H0, q, k, v, gate, parent, node_offsets, out, d,
-                                       tree_status, s);
-    return bole::launch_verify_generic(H0, q, k, v, gate, parent, node_offsets, out, d,
-                                       tree_status, s);
+using bole::kLayersPerLaunch;
+
+// Verify of checked layers, kLayersPerLaunch at a time: matrix cores when they cover
+// every layer of the chunk, else the vector-gate or plain kernel layer by layer. Per-tree
+// outputs come from the first launch only.
+hipError_t dispatch_verify(const bole_layer_t *layers, int num_layers, const int32_t *parent,
+                           const int32_t *node_offsets, const bole_dims_t &d,
+                           int32_t *tree_status, hipStream_t s) {
+    for (int l0 = 0; l0 < num_layers; l0 += kLayersPerLaunch) {
+        const bole_layer_t *ch = layers + l0;
+        const int nl = num_layers - l0 < kLayersPerLaunch ? num_layers - l0 : kLayersPerLaunch;
+        int32_t *ts = l0 == 0 ? tree_status : nullptr;
+        hipError_t e = hipSuccess;
+        if (bole::verify_mfma_applies(d, ch, nl)) {
+            e = bole::launch_verify_mfma(ch, nl, parent, node_offsets, d, ts, s);
+        } else {
+            for (int l = 0; l < nl && e == hipSuccess; ++l) {
+                const bole_layer_t &y = ch[l];
+                int32_t *tl = l == 0 ? ts : nullptr;
+                e = bole::verify_vec_applies(d, y.H0, y.q, y.k, y.v, y.gate, y.out)
+                        ? bole::launch_verify_vec(y.H0, y.q, y.k, y.v, y.gate, parent,
+                                                  node_offsets, y.out, d, tl, s)
+                        : bole::launch_verify_generic(y.H0, y.q, y.k, y.v, y.gate, parent,
+                                                      node_offsets, y.out, d, tl, s);
+            }
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t dispatch_commit(const bole_layer_t *layers, int num_layers, const int32_t *parent,
+                           const int32_t *node_offsets, const int32_t *accepted_idx,
+                           const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
+                           int32_t *tree_status, hipStream_t s) {
+    for (int l0 = 0; l0 < num_layers; l0 += kLayersPerLaunch) {
+        const int nl = num_layers - l0 < kLayersPerLaunch ? num_layers - l0 : kLayersPerLaunch;
+        const hipError_t e = bole::launch_commit(layers + l0, nl, parent, node_offsets,
+                                                 accepted_idx, accepted_len, d,
+                                                 l0 == 0 ? path_nodes : nullptr,
+                                                 l0 == 0 ? tree_status : nullptr, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// One pass per chunk where the lazy kernel covers it; elsewhere the previous step's
+// commit (on prev_k, prev_v, prev_gate) then this step's verify, chunk by chunk.
+hipError_t dispatch_lazy(const bole_layer_t *layers, int num_layers, const bole::PrevPath &prev,
+                         const bole_dims_t &pd, const int32_t *parent, const int32_t *node_offsets,
+                         const bole_dims_t &d, int32_t *tree_status, hipStream_t s) {
+    for (int l0 = 0; l0 < num_layers; l0 += kLayersPerLaunch) {
+        const bole_layer_t *ch = layers + l0;
+        const int nl = num_layers - l0 < kLayersPerLaunch ? num_layers - l0 : kLayersPerLaunch;
+        bole::PrevPath pp = prev;
+        if (l0 > 0) pp.path_nodes = pp.tree_status = nullptr;
+        int32_t *ts = l0 == 0 ? tree_status : nullptr;
+        hipError_t e;
+        if (bole::verify_lazy_applies(d, pd, ch, nl)) {
+            e = bole::launch_verify_lazy_commit(ch, nl, pp, pd, parent, node_offsets, d, ts, s);
+        } else {
+            bole_layer_t pl[kLayersPerLaunch];
+            for (int l = 0; l < nl; ++l) {
+                pl[l] = ch[l];
+                pl[l].k = ch[l].prev_k;
+                pl[l].v = ch[l].prev_v;
+                pl[l].gate = ch[l].prev_gate;
+            }
+            e = bole::launch_commit(pl, nl, pp.parent, pp.node_offsets, pp.accepted_idx,
+                                    pp.accepted_len, pd, pp.path_nodes, pp.tree_status, s);
+            if (e == hipSuccess) e = dispatch_verify(ch, nl, parent, node_offsets, d, ts, s);
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Host-visible checks shared by the entry points. `need_out`: verify outputs; `distinct`:
+// which per-layer buffer must differ between layers (0 none, 1 H0, 2 out, 3 both).
+bool layers_ok(const bole_layer_t *layers, int num_layers, const bole_dims_t &d, bool verify,
+               bool prev, const bole_dims_t *pd, int distinct) {
+    if (layers == nullptr || num_layers < 1) return false;
+    for (int l = 0; l < num_layers; ++l) {
+        const bole_layer_t &y = layers[l];
+        if (y.H0 == nullptr) return false;
+        if (d.total_nodes > 0 && (y.k == nullptr || y.v == nullptr || y.gate == nullptr))
+            return false;
+        if (verify && d.total_nodes > 0 && (y.q == nullptr || y.out == nullptr)) return false;
+        if (prev && pd->total_nodes > 0 &&
+            (y.prev_k == nullptr || y.prev_v == nullptr || y.prev_gate == nullptr))
+            return false;
+        for (int m = 0; m < l; ++m) {
+            if ((distinct & 1) && layers[m].H0 == y.H0) return false;
+            if ((distinct & 2) && y.out != nullptr && layers[m].out == y.out) return false;
+        }
+    }
+    return true;
 }
 
 }  // namespace
@@ -62,21 +146,58 @@ bole_status_t bole_check_dims(const bole_dims_t *d, int32_t op) {
     return BOLE_OK;
 }
 
+bole_status_t bole_tree_verify_layers(const bole_layer_t *layers, int32_t num_layers,
+                                      const int32_t *parent, const int32_t *node_offsets,
+                                      const bole_dims_t *dims, int32_t *tree_status,
+                                      bole_stream_t stream) {
+    const bole_status_t st = bole_check_dims(dims, kOpVerify);
+    if (st != BOLE_OK) return st;
+    const bole_dims_t &d = *dims;
+    if (layers == nullptr || num_layers < 1) return BOLE_ERR_INVALID_VALUE;
+    if (d.batch == 0) return BOLE_OK;
+    if (node_offsets == nullptr || (d.total_nodes > 0 && parent == nullptr) ||
+        !layers_ok(layers, num_layers, d, true, false, nullptr, 2))
+        return BOLE_ERR_INVALID_VALUE;
+    return from_hip(dispatch_verify(layers, num_layers, parent, node_offsets, d, tree_status,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
 bole_status_t bole_tree_verify(const float *H0, const void *q, const void *k, const void *v,
                                const float *gate, const int32_t *parent,
                                const int32_t *node_offsets, float *out,
                                const bole_dims_t *dims, int32_t *tree_status,
                                bole_stream_t stream) {
-    const bole_status_t st = bole_check_dims(dims, kOpVerify);
+    const bole_layer_t y = {const_cast<float *>(H0), q, k, v, gate, out, nullptr, nullptr, nullptr};
+    return bole_tree_verify_layers(&y, 1, parent, node_offsets, dims, tree_status, stream);
+}
+
+bole_status_t bole_tree_verify_lazy_commit_layers(
+    const bole_layer_t *layers, int32_t num_layers, const int32_t *prev_parent,
+    const int32_t *prev_node_offsets, const int32_t *prev_accepted_idx,
+    const int32_t *prev_accepted_len, const bole_dims_t *prev_dims, int32_t *prev_path_nodes,
+    int32_t *prev_tree_status, const int32_t *parent, const int32_t *node_offsets,
+    const bole_dims_t *dims, int32_t *tree_status, bole_stream_t stream) {
+    bole_status_t st = bole_check_dims(dims, kOpVerify);
     if (st != BOLE_OK) return st;
-    const bole_dims_t &d = *dims;
-    if (d.batch == 0) return BOLE_OK;
-    if (H0 == nullptr || node_offsets == nullptr) return BOLE_ERR_INVALID_VALUE;
-    if (d.total_nodes > 0 && (q == nullptr || k == nullptr || v == nullptr || gate == nullptr ||
-                              parent == nullptr || out == nullptr))
+    st = bole_check_dims(prev_dims, kOpCommit);
+    if (st != BOLE_OK) return st;
+    const bole_dims_t &d = *dims, &pd = *prev_dims;
+    // both steps describe the same layers: only the trees and the path may differ
+    if (pd.batch != d.batch || pd.heads != d.heads || pd.d_k != d.d_k || pd.d_v != d.d_v ||
+        pd.factor_dtype != d.factor_dtype || pd.gate_kind != d.gate_kind)
         return BOLE_ERR_INVALID_VALUE;
-    return from_hip(dispatch_verify(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status,
-                                    reinterpret_cast<hipStream_t>(stream)));
+    if (layers == nullptr || num_layers < 1) return BOLE_ERR_INVALID_VALUE;
+    if (d.batch == 0) return BOLE_OK;
+    if (node_offsets == nullptr || prev_node_offsets == nullptr || prev_accepted_len == nullptr)
+        return BOLE_ERR_INVALID_VALUE;
+    if ((d.total_nodes > 0 && parent == nullptr) || (pd.total_nodes > 0 && prev_parent == nullptr))
+        return BOLE_ERR_INVALID_VALUE;
+    if (pd.max_path > 0 && prev_accepted_idx == nullptr) return BOLE_ERR_INVALID_VALUE;
+    if (!layers_ok(layers, num_layers, d, true, true, &pd, 3)) return BOLE_ERR_INVALID_VALUE;
+    const bole::PrevPath prev = {prev_parent, prev_node_offsets, prev_accepted_idx,
+                                 prev_accepted_len, prev_path_nodes, prev_tree_status};
+    return from_hip(dispatch_lazy(layers, num_layers, prev, pd, parent, node_offsets, d,
+                                  tree_status, reinterpret_cast<hipStream_t>(stream)));
 }
 
 bole_status_t bole_tree_verify_lazy_commit(
@@ -85,36 +206,17 @@ bole_status_t bole_tree_verify_lazy_commit(
     int32_t *prev_tree_status, const void *q, const void *k, const void *v, const float *gate,
     const int32_t *parent, const int32_t *node_offsets, float *out, const bole_dims_t *dims,
     int32_t *tree_status, bole_stream_t stream) {
-    bole_status_t st = bole_check_dims(dims, kOpVerify);
-    if (st != BOLE_OK) return st;
-    st = bole_check_dims(prev_dims, kOpCommit);
-    if (st != BOLE_OK) return st;
-    const bole_dims_t &d = *dims, &pd = *prev_dims;
-    // both steps describe the same layer: only the trees and the path may differ
-    if (pd.batch != d.batch || pd.heads != d.heads || pd.d_k != d.d_k || pd.d_v != d.d_v ||
-        pd.factor_dtype != d.factor_dtype || pd.gate_kind != d.gate_kind)
-        return BOLE_ERR_INVALID_VALUE;
-    if (d.batch == 0) return BOLE_OK;
-    if (H0 == nullptr || node_offsets == nullptr || prev == nullptr ||
-        prev->node_offsets == nullptr || prev_accepted_len == nullptr)
-        return BOLE_ERR_INVALID_VALUE;
-    if (d.total_nodes > 0 && (q == nullptr || k == nullptr || v == nullptr || gate == nullptr ||
-                              parent == nullptr || out == nullptr))
-        return BOLE_ERR_INVALID_VALUE;
-    if (pd.max_path > 0 && prev_accepted_idx == nullptr) return BOLE_ERR_INVALID_VALUE;
-    if (pd.total_nodes > 0 && (prev->k == nullptr || prev->v == nullptr ||
-                               prev->gate == nullptr || prev->parent == nullptr))
-        return BOLE_ERR_INVALID_VALUE;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (bole::verify_lazy_applies(d, pd, H0, q, k, v, out, *prev))
-        return from_hip(bole::launch_verify_lazy_commit(
-            H0, *prev, prev_accepted_idx, prev_accepted_len, pd, prev_path_nodes,
-            prev_tree_status, q, k, v, gate, parent, node_offsets, out, d, tree_status, s));
-    // every other shape: the two steps as separate launches, in stream order
-    const hipError_t e = bole::launch_commit(H0, *prev, prev_accepted_idx, prev_accepted_len, pd,
-                                             prev_path_nodes, prev_tree_status, s);
-    if (e != hipSuccess) return from_hip(e);
-    return from_hip(dispatch_verify(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, s));
+    if (prev == nullptr) {
+        // the dims checks still come first, as in every entry point
+        bole_status_t st = bole_check_dims(dims, kOpVerify);
+        if (st == BOLE_OK) st = bole_check_dims(prev_dims, kOpCommit);
+        return st != BOLE_OK ? st : (dims->batch == 0 ? BOLE_OK : BOLE_ERR_INVALID_VALUE);
+    }
+    const bole_layer_t y = {H0, q, k, v, gate, out, prev->k, prev->v, prev->gate};
+    return bole_tree_verify_lazy_commit_layers(&y, 1, prev->parent, prev->node_offsets,
+                                               prev_accepted_idx, prev_accepted_len, prev_dims,
+                                               prev_path_nodes, prev_tree_status, parent,
+                                               node_offsets, dims, tree_status, stream);
 }
 
 bole_status_t bole_tree_verify_naive(const float *H0, const void *q, const void *k,
@@ -134,23 +236,38 @@ bole_status_t bole_tree_verify_naive(const float *H0, const void *q, const void 
                                               d, tree_status, reinterpret_cast<hipStream_t>(stream)));
 }
 
+bole_status_t bole_commit_path_layers(const bole_layer_t *layers, int32_t num_layers,
+                                      const int32_t *parent, const int32_t *node_offsets,
+                                      const int32_t *accepted_idx, const int32_t *accepted_len,
+                                      const bole_dims_t *dims, int32_t *path_nodes,
+                                      int32_t *tree_status, bole_stream_t stream) {
+    const bole_status_t st = bole_check_dims(dims, kOpCommit);
+    if (st != BOLE_OK) return st;
+    const bole_dims_t &d = *dims;
+    if (layers == nullptr || num_layers < 1) return BOLE_ERR_INVALID_VALUE;
+    if (d.batch == 0) return BOLE_OK;
+    if (node_offsets == nullptr || accepted_len == nullptr) return BOLE_ERR_INVALID_VALUE;
+    if (d.max_path > 0 && accepted_idx == nullptr) return BOLE_ERR_INVALID_VALUE;
+    if ((d.total_nodes > 0 && parent == nullptr) ||
+        !layers_ok(layers, num_layers, d, false, false, nullptr, 1))
+        return BOLE_ERR_INVALID_VALUE;
+    return from_hip(dispatch_commit(layers, num_layers, parent, node_offsets, accepted_idx,
+                                    accepted_len, d, path_nodes, tree_status,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
 bole_status_t bole_commit_path(float *H0, const bole_factors_t *factors,
                                const int32_t *accepted_idx, const int32_t *accepted_len,
                                const bole_dims_t *dims, int32_t *path_nodes,
                                int32_t *tree_status, bole_stream_t stream) {
-    const bole_status_t st = bole_check_dims(dims, kOpCommit);
-    if (st != BOLE_OK) return st;
-    const bole_dims_t &d = *dims;
-    if (d.batch == 0) return BOLE_OK;
-    if (H0 == nullptr || factors == nullptr || factors->node_offsets == nullptr ||
-        accepted_len == nullptr)
-        return BOLE_ERR_INVALID_VALUE;
-    if (d.max_path > 0 && accepted_idx == nullptr) return BOLE_ERR_INVALID_VALUE;
-    if (d.total_nodes > 0 && (factors->k == nullptr || factors->v == nullptr ||
-                              factors->gate == nullptr || factors->parent == nullptr))
-        return BOLE_ERR_INVALID_VALUE;
-    return from_hip(bole::launch_commit(H0, *factors, accepted_idx, accepted_len, d, path_nodes,
-                                        tree_status, reinterpret_cast<hipStream_t>(stream)));
+    if (factors == nullptr) {
+        const bole_status_t st = bole_check_dims(dims, kOpCommit);
+        return st != BOLE_OK ? st : (dims->batch == 0 ? BOLE_OK : BOLE_ERR_INVALID_VALUE);
+    }
+    const bole_layer_t y = {H0, nullptr, factors->k, factors->v, factors->gate, nullptr,
+                            nullptr, nullptr, nullptr};
+    return bole_commit_path_layers(&y, 1, factors->parent, factors->node_offsets, accepted_idx,
+                                   accepted_len, dims, path_nodes, tree_status, stream);
 }
 
 bole_status_t bole_tree_prepare(const int32_t *parent, const int32_t *node_offsets,

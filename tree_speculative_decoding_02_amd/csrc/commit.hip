@@ -198,14 +198,20 @@ constexpr int kStageNodes = 16;
 constexpr unsigned kCommitTargetBlocks = 1024;  // small batches split states to about this many
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+// Layer blockIdx.y of the table (its H0, k, v, gate); the layers share trees and paths,
+// and layer 0 writes the per-tree outputs.
 template <typename TF, bool VEC, bool SLICED>
 __global__ __launch_bounds__(kCommitThreads) void commit_stream_kernel(
-    float *__restrict__ H0, const TF *__restrict__ k, const TF *__restrict__ v,
-    const float *__restrict__ gate, const int32_t *__restrict__ parent,
+    const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, const int32_t *__restrict__ accepted_idx,
     const int32_t *__restrict__ accepted_len, int32_t *__restrict__ path_nodes,
     int32_t *__restrict__ tree_status, int H, int DK, int DV, int T, int max_path, int max_n,
     int gpr_log2, int slices, int slice_groups) {
+    const bole_layer_t &ly = lt.l[blockIdx.y];
+    float *const H0 = ly.H0;
+    const TF *const k = static_cast<const TF *>(ly.k);
+    const TF *const v = static_cast<const TF *>(ly.v);
+    const float *const gate = ly.gate;
     constexpr int E = 16 / sizeof(TF);   // factor elements per 16-byte chunk
     constexpr int PER = kRegFloats / 4;  // float4 state groups per thread per pass
     __shared__ int s_row[kMaxTree];
@@ -300,7 +306,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_stream_kernel(
         s_row[tid] = row;
         s_a[tid] = a;
         if (tid == 0) s_len = ok ? len : 0;
-        if (h == 0 && slice == 0) {
+        if (h == 0 && slice == 0 && blockIdx.y == 0) {
             if (tid == 0 && tree_status) tree_status[b] = st;
             if (path_nodes && tid < max_path) path_nodes[(size_t)b * max_path + tid] = row;
         }
@@ -386,23 +392,28 @@ __global__ __launch_bounds__(kCommitThreads) void commit_stream_kernel(
 }
 
 template <typename TF, bool VEC>
-static void launch_w(float *H0, const bole_factors_t &f, const int32_t *accepted_idx,
+static void launch_w(const bole_layer_t *layers, int nl, const int32_t *parent,
+                     const int32_t *node_offsets, const int32_t *accepted_idx,
                      const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
                      int32_t *tree_status, hipStream_t stream) {
-    const dim3 grid((unsigned)d.batch * (unsigned)d.heads), block(kCommitThreads);
-    const size_t lds = sizeof(float) * kPathChunk * ((VEC ? 2 : 1) * d.d_k + d.d_v);
-    const TF *k = static_cast<const TF *>(f.k), *v = static_cast<const TF *>(f.v);
-    const bool vec4 = (d.d_v % 4 == 0) && (reinterpret_cast<uintptr_t>(H0) % 16 == 0);
-    // streaming kernel: d_v/4 a power of two dividing the block, 16-byte factor rows
+    const dim3 block(kCommitThreads);
+    // streaming kernel: d_v/4 a power of two dividing the block, 16-byte state and factor
+    // rows in every layer
     const int gpr = d.d_v / 4;
     constexpr int E = 16 / sizeof(TF);
-    const uintptr_t fa = reinterpret_cast<uintptr_t>(f.k) | reinterpret_cast<uintptr_t>(f.v) |
-                         (VEC ? reinterpret_cast<uintptr_t>(f.gate) : 0);
-    if (vec4 && gpr > 0 && (gpr & (gpr - 1)) == 0 && kCommitThreads % gpr == 0 &&
-        d.d_k % E == 0 && d.d_v % E == 0 && fa % 16 == 0) {
+    bool vec4 = d.d_v % 4 == 0, aligned = true;
+    for (int l = 0; l < nl; ++l) {
+        vec4 = vec4 && reinterpret_cast<uintptr_t>(layers[l].H0) % 16 == 0;
+        const uintptr_t fa = reinterpret_cast<uintptr_t>(layers[l].k) |
+                             reinterpret_cast<uintptr_t>(layers[l].v) |
+                             (VEC ? reinterpret_cast<uintptr_t>(layers[l].gate) : 0);
+        aligned = aligned && fa % 16 == 0;
+    }
+    if (vec4 && aligned && gpr > 0 && (gpr & (gpr - 1)) == 0 && kCommitThreads % gpr == 0 &&
+        d.d_k % E == 0 && d.d_v % E == 0) {
         const size_t slds = sizeof(float) * kStageNodes * ((VEC ? 2 : 1) * d.d_k + d.d_v);
         // state slices per unit: one pass per workgroup, and about kCommitTargetBlocks
-        // workgroups in all when the batch is small
+        // workgroups per layer when the batch is small
         const unsigned U = (unsigned)d.batch * (unsigned)d.heads;
         const int G = d.d_k * d.d_v / 4, per_pass = kCommitThreads * kRegFloats / 4;
         int slices = (G + per_pass - 1) / per_pass;
@@ -411,31 +422,44 @@ static void launch_w(float *H0, const bole_factors_t &f, const int32_t *accepted
         int sg = (G + slices - 1) / slices;
         sg = (sg + kCommitThreads - 1) / kCommitThreads * kCommitThreads;
         slices = (G + sg - 1) / sg;
+        LayerTable lt = {};
+        for (int l = 0; l < nl; ++l) lt.l[l] = layers[l];
         auto kern = slices > 1 ? commit_stream_kernel<TF, VEC, true> : commit_stream_kernel<TF, VEC, false>;
-        kern<<<dim3(U * (unsigned)slices), block, slds, stream>>>(
-            H0, k, v, f.gate, f.parent, f.node_offsets, accepted_idx, accepted_len, path_nodes,
-            tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags),
+        kern<<<dim3(U * (unsigned)slices, (unsigned)nl), block, slds, stream>>>(
+            lt, parent, node_offsets, accepted_idx, accepted_len, path_nodes, tree_status,
+            d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags),
             __builtin_ctz((unsigned)gpr), slices, sg);
-    } else if (vec4)
-        commit_kernel<TF, VEC, 4><<<grid, block, lds, stream>>>(
-            H0, k, v, f.gate, f.parent, f.node_offsets, accepted_idx, accepted_len, path_nodes,
-            tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags));
-    else
-        commit_kernel<TF, VEC, 1><<<grid, block, lds, stream>>>(
-            H0, k, v, f.gate, f.parent, f.node_offsets, accepted_idx, accepted_len, path_nodes,
-            tree_status, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags));
+        return;
+    }
+    // any other shape or alignment: one launch per layer
+    const dim3 grid((unsigned)d.batch * (unsigned)d.heads);
+    const size_t lds = sizeof(float) * kPathChunk * ((VEC ? 2 : 1) * d.d_k + d.d_v);
+    for (int l = 0; l < nl; ++l) {
+        const bole_layer_t &y = layers[l];
+        const TF *k = static_cast<const TF *>(y.k), *v = static_cast<const TF *>(y.v);
+        int32_t *pn = l == 0 ? path_nodes : nullptr, *ts = l == 0 ? tree_status : nullptr;
+        if (d.d_v % 4 == 0 && reinterpret_cast<uintptr_t>(y.H0) % 16 == 0)
+            commit_kernel<TF, VEC, 4><<<grid, block, lds, stream>>>(
+                y.H0, k, v, y.gate, parent, node_offsets, accepted_idx, accepted_len, pn, ts,
+                d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags));
+        else
+            commit_kernel<TF, VEC, 1><<<grid, block, lds, stream>>>(
+                y.H0, k, v, y.gate, parent, node_offsets, accepted_idx, accepted_len, pn, ts,
+                d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags));
+    }
 }
 
-hipError_t launch_commit(float *H0, const bole_factors_t &f, const int32_t *accepted_idx,
+hipError_t launch_commit(const bole_layer_t *layers, int nl, const int32_t *parent,
+                         const int32_t *node_offsets, const int32_t *accepted_idx,
                          const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
                          int32_t *tree_status, hipStream_t stream) {
     const bool vec = d.gate_kind == BOLE_GATE_VECTOR;
     if (d.factor_dtype == BOLE_DTYPE_F32) {
-        if (vec) launch_w<float, true>(H0, f, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
-        else launch_w<float, false>(H0, f, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
+        if (vec) launch_w<float, true>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
+        else launch_w<float, false>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
     } else {
-        if (vec) launch_w<__bf16, true>(H0, f, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
-        else launch_w<__bf16, false>(H0, f, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
+        if (vec) launch_w<__bf16, true>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
+        else launch_w<__bf16, false>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
     }
     return hipGetLastError();
 }

@@ -10,6 +10,19 @@ namespace bole {
 
 constexpr int kMaxTreeNodesHost = 64;  // nodes per tree: one wavefront, one 64-bit mask
 
+// Layers of one launch (blockIdx.y = layer), passed by value as a kernel argument: the
+// kernels read their layer's pointers from the argument segment, no table in memory.
+constexpr int kLayersPerLaunch = 16;
+struct LayerTable {
+    bole_layer_t l[kLayersPerLaunch];
+};
+
+// The previous step's tree and accepted path, shared by the layers of a lazy commit.
+struct PrevPath {
+    const int32_t *parent, *node_offsets, *accepted_idx, *accepted_len;
+    int32_t *path_nodes, *tree_status;
+};
+
 hipError_t launch_prepare(const int32_t *parent, const int32_t *node_offsets, const float *gate,
                           const bole_dims_t &d, int32_t *depth, uint64_t *mask, float *cumlog,
                           int32_t *tree_status, hipStream_t stream);
@@ -19,13 +32,14 @@ hipError_t launch_verify_generic(const float *H0, const void *q, const void *k, 
                                  const int32_t *node_offsets, float *out, const bole_dims_t &d,
                                  int32_t *tree_status, hipStream_t stream);
 
-// True when the matrix-core verify kernel covers this request.
-bool verify_mfma_applies(const bole_dims_t &d, const void *H0, const void *q, const void *k,
-                         const void *v, const void *out);
+// Launchers below take nl <= kLayersPerLaunch layers sharing their trees; statuses and
+// path rows are written once.
 
-hipError_t launch_verify_mfma(const float *H0, const void *q, const void *k, const void *v,
-                              const float *gate, const int32_t *parent,
-                              const int32_t *node_offsets, float *out, const bole_dims_t &d,
+// True when the matrix-core verify kernel covers this request (every layer).
+bool verify_mfma_applies(const bole_dims_t &d, const bole_layer_t *layers, int nl);
+
+hipError_t launch_verify_mfma(const bole_layer_t *layers, int nl, const int32_t *parent,
+                              const int32_t *node_offsets, const bole_dims_t &d,
                               int32_t *tree_status, hipStream_t stream);
 
 // True when the matrix-core vector-gate verify kernel covers this request.
@@ -38,26 +52,22 @@ hipError_t launch_verify_vec(const float *H0, const void *q, const void *k, cons
                              int32_t *tree_status, hipStream_t stream);
 
 // True when the one-pass lazy commit + verify kernel covers this pair of steps.
-bool verify_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const float *H0,
-                         const void *q, const void *k, const void *v, const void *out,
-                         const bole_factors_t &prev);
+bool verify_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const bole_layer_t *layers,
+                         int nl);
 
-hipError_t launch_verify_lazy_commit(float *H0, const bole_factors_t &prev,
-                                     const int32_t *prev_accepted_idx,
-                                     const int32_t *prev_accepted_len, const bole_dims_t &pd,
-                                     int32_t *prev_path_nodes, int32_t *prev_tree_status,
-                                     const void *q, const void *k, const void *v,
-                                     const float *gate, const int32_t *parent,
-                                     const int32_t *node_offsets, float *out,
-                                     const bole_dims_t &d, int32_t *tree_status,
-                                     hipStream_t stream);
+hipError_t launch_verify_lazy_commit(const bole_layer_t *layers, int nl, const PrevPath &prev,
+                                     const bole_dims_t &pd, const int32_t *parent,
+                                     const int32_t *node_offsets, const bole_dims_t &d,
+                                     int32_t *tree_status, hipStream_t stream);
 
 hipError_t launch_verify_naive(const float *H0, const void *q, const void *k, const void *v,
                                const float *gate, const int32_t *parent,
                                const int32_t *node_offsets, float *out, float *states,
                                const bole_dims_t &d, int32_t *tree_status, hipStream_t stream);
 
-hipError_t launch_commit(float *H0, const bole_factors_t &f, const int32_t *accepted_idx,
+// Commit of each layer's k, v, gate along the shared accepted paths.
+hipError_t launch_commit(const bole_layer_t *layers, int nl, const int32_t *parent,
+                         const int32_t *node_offsets, const int32_t *accepted_idx,
                          const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
                          int32_t *tree_status, hipStream_t stream);
 

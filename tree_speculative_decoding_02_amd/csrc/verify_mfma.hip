@@ -52,24 +52,22 @@ namespace bole {
 // Both terms land in one accumulator layout: lane (n, g) holds node 16it + 4g + r,
 // state columns 4n .. 4n+3 across its four tiles, stored as one 16-byte write per row.
 // Read-once and write-once streams carry the non-temporal cache policy.
-// The previous step's factors and accepted path, for the lazy-commit form (LAZY): the
-// kernel first applies that path to H_0 in registers and writes the committed state
-// back, then verifies this step's tree against it.
+// The previous step's tree and accepted path, for the lazy-commit form (LAZY): the kernel
+// first applies that path (with the layer's prev_k, prev_v, prev_gate) to H_0 in
+// registers and writes the committed state back, then verifies this step's tree against it.
 struct LazyCommit {
-    const __bf16 *k, *v;
-    const float *gate;
     const int32_t *parent, *node_offsets, *accepted_idx, *accepted_len;
     int32_t *path_nodes, *tree_status;
     int T, max_path, max_n;
 };
 
+// Layer blockIdx.y of the table; every layer runs the same trees. Per-tree outputs
+// (statuses, path rows) are written by layer 0 only.
 template <int DK, int DV, int NWT, bool LAZY>
 __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
-    const float *__restrict__ H0c, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
-    const __bf16 *__restrict__ v, const float *__restrict__ gate,
-    const int32_t *__restrict__ parent, const int32_t *__restrict__ node_offsets,
-    float *__restrict__ out, int32_t *__restrict__ tree_status, int H, int T, int U, int max_n,
-    LazyCommit lc) {
+    const LayerTable lt, const int32_t *__restrict__ parent,
+    const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
+    int U, int max_n, LazyCommit lc) {
     static_assert(!LAZY || NWT == 1, "the lazy commit runs in the one-wavefront instantiation");
     constexpr int NN = 32 * NWT;            // node rows staged
     constexpr int NT = 2 * NWT;             // 16-node tiles per wavefront
@@ -88,7 +86,13 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     // lazy commit: k rows and v rows (group columns) of up to kLazyStage path nodes
     constexpr int kLazyStage = LAZY ? 8 : 1;
     __shared__ __bf16 s_pk[kLazyStage * DK], s_pv[kLazyStage * CW];
-    float *H0 = const_cast<float *>(H0c);   // written only by the lazy commit
+    const bole_layer_t &ly = lt.l[blockIdx.y];
+    float *const H0 = ly.H0;                // written only by the lazy commit
+    const __bf16 *const q = static_cast<const __bf16 *>(ly.q);
+    const __bf16 *const k = static_cast<const __bf16 *>(ly.k);
+    const __bf16 *const v = static_cast<const __bf16 *>(ly.v);
+    const float *const gate = ly.gate;
+    float *const out = ly.out;
 
     const int lane = lane_id();
     const int wave = NWT == 1 ? 0 : (int)(threadIdx.x >> 6);
@@ -106,7 +110,8 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     const int b = unit / H, h = unit - b * H;
     const int c0 = cg * CW;
     const int cw0 = wave * CPW;             // the wave's first column within the group
-    const bool writer = tree_status != nullptr && h == 0 && cg == 0 && threadIdx.x == 0;
+    const bool first = blockIdx.y == 0 && h == 0 && cg == 0;  // writes the per-tree outputs
+    const bool writer = tree_status != nullptr && first && threadIdx.x == 0;
 
     const TreeRange tr = tree_range(node_offsets, b, T, NWT == 1 ? max_n : kMaxTree);
     bool do_verify = true;
@@ -205,6 +210,27 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
             hreg[s] = __builtin_nontemporal_load(reinterpret_cast<const hvec *>(
                 hu + ((uint32_t)(32 * (s >> 3) + 8 * g + (s & 7)) * DV + cw0 + CPL * n16)));
     }
+    // lazy commit: the factor chunks of the first kLazyStage path nodes, issued behind
+    // H_0 (their indices were loaded first) and held in registers until the path is
+    // validated; rows clamped into the tree, which the offsets check keeps inside [0, T)
+    bf16x8 pf[LCH];
+    if constexpr (LAZY) {
+        if (plikely) {
+            const int mc0 = min(kLazyStage, plen_raw);
+#pragma unroll
+            for (int u = 0; u < LCH; ++u) {
+                const int c = lane + 64 * u;
+                const int m = c / LCPN, part = c - m * LCPN;
+                if (m < mc0) {
+                    const size_t prow = (size_t)(ptr.lo + min(max(lx[u], 0), ptr.n - 1)) * H + h;
+                    pf[u] = part < LCK
+                                ? load16(static_cast<const __bf16 *>(ly.prev_k) + prow * DK + 8 * part)
+                                : load16(static_cast<const __bf16 *>(ly.prev_v) + prow * DV + c0 +
+                                         8 * (part - LCK));
+                }
+            }
+        }
+    }
     if (do_verify) {
 #pragma unroll
         for (int u = 0; u < KL; ++u) s_k[64 * (wave + NWT * u) + lane] = kst[u];
@@ -234,15 +260,15 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
                 if (__any(bad)) st = BOLE_TREE_BAD_PATH;
                 else plen = plen_raw;
             }
-            if (plen > 0 && lane < plen) pa = lc.gate[(size_t)(ptr.lo + x) * H + h];
+            if (plen > 0 && lane < plen) pa = ly.prev_gate[(size_t)(ptr.lo + x) * H + h];
             const int row = (st == BOLE_TREE_OK && lane < plen) ? ptr.lo + x : -1;
-            if (h == 0 && cg == 0) {
+            if (first) {
                 if (lane == 0 && lc.tree_status) lc.tree_status[b] = st;
                 if (lc.path_nodes && lane < lc.max_path) lc.path_nodes[(size_t)b * lc.max_path + lane] = row;
             }
         } else {
             if (st == BOLE_TREE_OK && plen_raw != 0) st = BOLE_TREE_BAD_PATH;  // empty tree
-            if (h == 0 && cg == 0) {
+            if (first) {
                 if (lane == 0 && lc.tree_status) lc.tree_status[b] = st;
                 if (lc.path_nodes && lane < lc.max_path) lc.path_nodes[(size_t)b * lc.max_path + lane] = -1;
             }
@@ -258,14 +284,20 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
                     // every lane takes part in the shuffle; only m < mc use the result
                     const int xs = __shfl(lpx, min(m0 + m, 63), 64);
                     if (m < mc) {
-                        const int xm = m0 == 0 ? lx[u] : xs;
-                        const size_t prow = (size_t)(ptr.lo + min(max(xm, 0), ptr.n - 1)) * H + h;
+                        bf16x8 chunk;
+                        if (m0 == 0) {
+                            chunk = pf[u];  // prefetched: plen == plen_raw here
+                        } else {
+                            const size_t prow = (size_t)(ptr.lo + min(max(xs, 0), ptr.n - 1)) * H + h;
+                            chunk = part < LCK
+                                        ? load16(static_cast<const __bf16 *>(ly.prev_k) + prow * DK + 8 * part)
+                                        : load16(static_cast<const __bf16 *>(ly.prev_v) + prow * DV +
+                                                 c0 + 8 * (part - LCK));
+                        }
                         if (part < LCK)
-                            *reinterpret_cast<bf16x8 *>(s_pk + m * DK + 8 * part) =
-                                load16(lc.k + prow * DK + 8 * part);
+                            *reinterpret_cast<bf16x8 *>(s_pk + m * DK + 8 * part) = chunk;
                         else
-                            *reinterpret_cast<bf16x8 *>(s_pv + m * CW + 8 * (part - LCK)) =
-                                load16(lc.v + prow * DV + c0 + 8 * (part - LCK));
+                            *reinterpret_cast<bf16x8 *>(s_pv + m * CW + 8 * (part - LCK)) = chunk;
                     }
                 }
                 for (int m = 0; m < mc; ++m) {
@@ -411,17 +443,11 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
         }
 }
 
-bool verify_mfma_applies(const bole_dims_t &d, const void *H0, const void *q, const void *k,
-                         const void *v, const void *out) {
+static bool shape_ok(const bole_dims_t &d) {
     if (d.flags & BOLE_FLAG_FORCE_GENERIC) return false;
     if (d.factor_dtype != BOLE_DTYPE_BF16 || d.gate_kind != BOLE_GATE_SCALAR) return false;
     if (d.d_k != 64 && d.d_k != 128) return false;
     if (d.d_v != 32 && d.d_v != 64 && d.d_v != 128 && d.d_v != 256) return false;
-    // 16-byte loads of H_0, q, k, v rows and 16-byte stores of out rows
-    const uintptr_t a = reinterpret_cast<uintptr_t>(H0) | reinterpret_cast<uintptr_t>(q) |
-                        reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
-                        reinterpret_cast<uintptr_t>(out);
-    if (a % 16 != 0) return false;
     // per-tree element offsets (64 rows of one head's rows, and one H_0 slice) are 32-bit
     const uint64_t row_elems = (uint64_t)d.heads * (uint64_t)(d.d_k > d.d_v ? d.d_k : d.d_v);
     if (row_elems * kMaxTree >= (1ull << 31)) return false;
@@ -430,99 +456,99 @@ bool verify_mfma_applies(const bole_dims_t &d, const void *H0, const void *q, co
     return ((uint64_t)d.batch * (uint64_t)d.heads + 8) * groups < (1ull << 30);
 }
 
+bool verify_mfma_applies(const bole_dims_t &d, const bole_layer_t *layers, int nl) {
+    if (!shape_ok(d)) return false;
+    // 16-byte loads of H_0, q, k, v rows and 16-byte stores of out rows
+    for (int l = 0; l < nl; ++l) {
+        const bole_layer_t &y = layers[l];
+        const uintptr_t a = reinterpret_cast<uintptr_t>(y.H0) | reinterpret_cast<uintptr_t>(y.q) |
+                            reinterpret_cast<uintptr_t>(y.k) | reinterpret_cast<uintptr_t>(y.v) |
+                            reinterpret_cast<uintptr_t>(y.out);
+        if (a % 16 != 0) return false;
+    }
+    return true;
+}
+
 template <int DK, int DV>
-static void launch_shape(const float *H0, const __bf16 *q, const __bf16 *k, const __bf16 *v,
-                         const float *gate, const int32_t *parent, const int32_t *node_offsets,
-                         float *out, const bole_dims_t &d, int32_t *tree_status,
+static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *parent,
+                         const int32_t *node_offsets, const bole_dims_t &d, int32_t *tree_status,
                          hipStream_t stream, const LazyCommit *lazy) {
     const unsigned U = (unsigned)d.batch * (unsigned)d.heads;
     const int max_n = max_tree_nodes(d.flags);
-    // one workgroup per (unit, 64-column group); G > 1: ceil(U / 8) slots of 8 units, each
-    // slot G column groups wide, so the groups of a unit share an XCD
+    // one workgroup per (unit, 64-column group, layer): G > 1: ceil(U / 8) slots of 8
+    // units, each slot G column groups wide, so the groups of a unit share an XCD
     constexpr int G = DV < 64 ? 1 : DV / 64;
-    const unsigned grid = G == 1 ? U : ((U + 7) / 8) * 8 * G;
+    const dim3 grid(G == 1 ? U : ((U + 7) / 8) * 8 * G, (unsigned)nl);
+    LayerTable lt = {};
+    for (int l = 0; l < nl; ++l) lt.l[l] = layers[l];
     const LazyCommit none = {};
     if (lazy)
-        verify_mfma_tree_kernel<DK, DV, 1, true><<<dim3(grid), dim3(64), 0, stream>>>(
-            H0, q, k, v, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
-            (int)U, max_n, *lazy);
+        verify_mfma_tree_kernel<DK, DV, 1, true><<<grid, dim3(64), 0, stream>>>(
+            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, *lazy);
     else
-        verify_mfma_tree_kernel<DK, DV, 1, false><<<dim3(grid), dim3(64), 0, stream>>>(
-            H0, q, k, v, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
-            (int)U, max_n, none);
+        verify_mfma_tree_kernel<DK, DV, 1, false><<<grid, dim3(64), 0, stream>>>(
+            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, none);
     if (max_n > 32)
-        verify_mfma_tree_kernel<DK, DV, 2, false><<<dim3(grid), dim3(128), 0, stream>>>(
-            H0, q, k, v, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
-            (int)U, max_n, none);
+        verify_mfma_tree_kernel<DK, DV, 2, false><<<grid, dim3(128), 0, stream>>>(
+            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, none);
 }
 
 template <int DK>
-static void launch_dk(const float *H0, const void *q, const void *k, const void *v,
-                      const float *gate, const int32_t *parent, const int32_t *node_offsets,
-                      float *out, const bole_dims_t &d, int32_t *tree_status, hipStream_t stream,
-                      const LazyCommit *lazy) {
-    const __bf16 *qb = static_cast<const __bf16 *>(q), *kb = static_cast<const __bf16 *>(k),
-                 *vb = static_cast<const __bf16 *>(v);
+static void launch_dk(const bole_layer_t *layers, int nl, const int32_t *parent,
+                      const int32_t *node_offsets, const bole_dims_t &d, int32_t *tree_status,
+                      hipStream_t stream, const LazyCommit *lazy) {
     switch (d.d_v) {
-        case 32: launch_shape<DK, 32>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream, lazy); break;
-        case 64: launch_shape<DK, 64>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream, lazy); break;
-        case 128: launch_shape<DK, 128>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream, lazy); break;
-        case 256: launch_shape<DK, 256>(H0, qb, kb, vb, gate, parent, node_offsets, out, d, tree_status, stream, lazy); break;
+        case 32: launch_shape<DK, 32>(layers, nl, parent, node_offsets, d, tree_status, stream, lazy); break;
+        case 64: launch_shape<DK, 64>(layers, nl, parent, node_offsets, d, tree_status, stream, lazy); break;
+        case 128: launch_shape<DK, 128>(layers, nl, parent, node_offsets, d, tree_status, stream, lazy); break;
+        case 256: launch_shape<DK, 256>(layers, nl, parent, node_offsets, d, tree_status, stream, lazy); break;
         default: break;
     }
 }
 
-hipError_t launch_verify_mfma(const float *H0, const void *q, const void *k, const void *v,
-                              const float *gate, const int32_t *parent,
-                              const int32_t *node_offsets, float *out, const bole_dims_t &d,
+hipError_t launch_verify_mfma(const bole_layer_t *layers, int nl, const int32_t *parent,
+                              const int32_t *node_offsets, const bole_dims_t &d,
                               int32_t *tree_status, hipStream_t stream) {
     if (d.d_k == 64)
-        launch_dk<64>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, stream, nullptr);
+        launch_dk<64>(layers, nl, parent, node_offsets, d, tree_status, stream, nullptr);
     else
-        launch_dk<128>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, stream, nullptr);
+        launch_dk<128>(layers, nl, parent, node_offsets, d, tree_status, stream, nullptr);
     return hipGetLastError();
 }
 
-bool verify_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const float *H0,
-                         const void *q, const void *k, const void *v, const void *out,
-                         const bole_factors_t &prev) {
-    if (!verify_mfma_applies(d, H0, q, k, v, out)) return false;
+bool verify_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const bole_layer_t *layers,
+                         int nl) {
+    if (!verify_mfma_applies(d, layers, nl)) return false;
     // the previous step's factors: same layout and shapes, 16-byte rows
     if (pd.factor_dtype != d.factor_dtype || pd.gate_kind != d.gate_kind || pd.d_k != d.d_k ||
         pd.d_v != d.d_v || pd.heads != d.heads || pd.batch != d.batch)
         return false;
-    const uintptr_t a = reinterpret_cast<uintptr_t>(prev.k) | reinterpret_cast<uintptr_t>(prev.v);
-    if (a % 16 != 0) return false;
-    const uint64_t row_elems = (uint64_t)pd.heads * (uint64_t)(pd.d_k > pd.d_v ? pd.d_k : pd.d_v);
-    return row_elems * kMaxTree < (1ull << 31);
+    for (int l = 0; l < nl; ++l) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(layers[l].prev_k) |
+                            reinterpret_cast<uintptr_t>(layers[l].prev_v);
+        if (a % 16 != 0) return false;
+    }
+    return true;
 }
 
-hipError_t launch_verify_lazy_commit(float *H0, const bole_factors_t &prev,
-                                     const int32_t *prev_accepted_idx,
-                                     const int32_t *prev_accepted_len, const bole_dims_t &pd,
-                                     int32_t *prev_path_nodes, int32_t *prev_tree_status,
-                                     const void *q, const void *k, const void *v,
-                                     const float *gate, const int32_t *parent,
-                                     const int32_t *node_offsets, float *out,
-                                     const bole_dims_t &d, int32_t *tree_status,
-                                     hipStream_t stream) {
+hipError_t launch_verify_lazy_commit(const bole_layer_t *layers, int nl, const PrevPath &prev,
+                                     const bole_dims_t &pd, const int32_t *parent,
+                                     const int32_t *node_offsets, const bole_dims_t &d,
+                                     int32_t *tree_status, hipStream_t stream) {
     LazyCommit lz;
-    lz.k = static_cast<const __bf16 *>(prev.k);
-    lz.v = static_cast<const __bf16 *>(prev.v);
-    lz.gate = prev.gate;
     lz.parent = prev.parent;
     lz.node_offsets = prev.node_offsets;
-    lz.accepted_idx = prev_accepted_idx;
-    lz.accepted_len = prev_accepted_len;
-    lz.path_nodes = prev_path_nodes;
-    lz.tree_status = prev_tree_status;
+    lz.accepted_idx = prev.accepted_idx;
+    lz.accepted_len = prev.accepted_len;
+    lz.path_nodes = prev.path_nodes;
+    lz.tree_status = prev.tree_status;
     lz.T = pd.total_nodes;
     lz.max_path = pd.max_path;
     lz.max_n = max_tree_nodes(pd.flags);
     if (d.d_k == 64)
-        launch_dk<64>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, stream, &lz);
+        launch_dk<64>(layers, nl, parent, node_offsets, d, tree_status, stream, &lz);
     else
-        launch_dk<128>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, stream, &lz);
+        launch_dk<128>(layers, nl, parent, node_offsets, d, tree_status, stream, &lz);
     return hipGetLastError();
 }
 
