@@ -230,6 +230,23 @@ def make_config(cid: int, n_layers: Optional[int] = None) -> Workload:
                     acc_len, layers, recipe)
 
 
+def make_marginals(seed: int, batch: int, depth: int, vocab: int, logit_std: float = 2.0,
+                   grid: Optional[float] = None) -> np.ndarray:
+    """Synthetic drafter output for the tree builder: for each sequence and position
+    k = 1..depth, q_k = softmax(logits), logits ~ N(0, logit_std) over the vocabulary
+    (the shape of a block-diffusion drafter's position-wise marginals). float32
+    [batch][depth][vocab]. grid: round every probability down to a multiple of it (many
+    exact ties, for tie-order tests)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x7ee5]))
+    z = rng.normal(0.0, logit_std, size=(batch, depth, vocab))
+    z -= z.max(axis=-1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=-1, keepdims=True)
+    if grid is not None:
+        p = np.floor(p / grid) * grid
+    return p.astype(np.float32)
+
+
 def random_tree(rng: np.random.Generator, n: int, kind: str) -> np.ndarray:
     """Tree-local parent array of n nodes, parent[i] < i. Kinds: 'random' (uniform
     parent in [-1, i)), 'chain', 'star' (all roots), 'bestfirst', 'deep' (mostly chains)."""
