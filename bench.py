@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--per-layer-forms", action="store_true",
                     help="also time both forms with one launch per layer (the same kernels "
                          "as the stacked forms, so leave it off in profiled runs)")
+    ap.add_argument("--no-builder", action="store_true",
+                    help="skip timing the draft-tree builder")
     ap.add_argument("--no-naive", action="store_true",
                     help="skip timing the naive serial-walk baseline")
     ap.add_argument("--config-sweep", action="store_true",
@@ -276,6 +278,28 @@ def main():
             result["forms"][name] = {"ms_per_step": ms, "value": nodes / (ms * 1e-3),
                                      "launches_per_step": L * len(groups)}
     v_us = kernels["verify"]["avg_us_per_layer"]
+
+    # the draft-tree builder on the same batch: 64 sequences x 8 drafted positions over a
+    # 128256-token vocabulary (Llama-3.1's), best-first up to 64 nodes, controller on the
+    # speedup model's cost C(N) = T_draft/T_AR + 1 + alpha N (alpha = 0.05, in AR steps)
+    if not args.no_builder:
+        Bb, Db, Vb, nb = wl.batch, 8, 128256, 64
+        marg = torch.from_numpy(W.make_marginals(2024, Bb, Db, Vb)).to(dev)
+        cost = torch.tensor([0.1 + 1.0 + 0.05 * n for n in range(1, nb + 1)], dtype=torch.float32,
+                            device=dev)
+        build = bole.bind_build_tree(marg, cost, 1.0, n_max=nb, stream=stream)
+        b_ms, b_spans, _ = timed([[build]], args.steps, args.warmup)
+        b_us = 1e3 * float(np.mean(b_spans[:, 0]))
+        b_bytes = Bb * Db * Vb * 4   # the marginals, read once; the rest is < 0.1 %
+        torch.cuda.synchronize()
+        n_kept = build.out["node_offsets"][-1].item()
+        result["tree_builder"] = {
+            "avg_us_per_call": b_us, "median_us_per_call": 1e3 * float(np.median(b_spans[:, 0])),
+            "bytes_per_call": b_bytes, "GB_s": b_bytes / (b_us * 1e3),
+            "frac_hbm_peak": b_bytes / (b_us * 1e3) / HBM_PEAK_GBS, "nodes_kept": n_kept,
+            "what": "bole_build_tree: top-64 per position, best-first tree, budget controller "
+                    "and packing for 64 sequences x 8 positions x 128256 tokens (3 launches)"}
+        del marg
 
     # the naive serial walk on layer 0 (one materialised state per node): the baseline the
     # closed form is measured against, timed after the benchmark proper

@@ -281,6 +281,65 @@ BOLE_API bole_status_t bole_tree_prepare(const int32_t *parent, const int32_t *n
                                 uint64_t *mask, float *cumlog, int32_t *tree_status,
                                 bole_stream_t stream);
 
+/*
+ * Draft-tree construction and budget control: the BASTION summary page, sections 1-3.
+ *  - Path score (section 1): node i at depth d(i) with path tokens x_i1..x_id scores
+ *    rho(i) = prod_k q_k(x_ik), q_k being the drafter's position-wise marginal of
+ *    position k.
+ *  - Best-first expansion (section 2): the tree grows by repeatedly inserting the valid
+ *    node (its parent already in the tree; depth-1 nodes hang off the verified context)
+ *    with the highest rho. Each product is fp32(rho(parent) * q); ties go to the earlier
+ *    source (the context first, then tree nodes in insertion order), and among one
+ *    parent's children to the lower token id.
+ *  - Budget controller (section 3): with A_hat(N) the fp32 sum of the first N scores in
+ *    insertion order, S(N) = fp32(fp32(A_hat(N) * l_ar) / cost[N - 1]). The tree grows from
+ *    N = 1 and keeps the first N with S(N + 1) < S(N), else all n_max nodes (or all
+ *    nodes that exist). BOLE_BUILD_FIXED_BUDGET keeps n_max nodes without the test.
+ *
+ * Inputs:
+ *   marginals float [B][depth][vocab]  q_k for positions k = 1..depth (probabilities,
+ *                                      finite and >= 0; NaN is not allowed)
+ *   cost      float [n_max]            cost[N - 1] = C(N), the caller's estimate of one
+ *                                      step's time with an N-node tree (draft + verify),
+ *                                      > 0; may be NULL with BOLE_BUILD_FIXED_BUDGET and
+ *                                      speedup NULL
+ *   l_ar                               L_AR, the autoregressive time per token, > 0 (same
+ *                                      unit as cost)
+ *   workspace                          device scratch of at least
+ *                                      bole_build_tree_workspace_size(dims) bytes,
+ *                                      16-byte aligned, owned by the caller; contents on
+ *                                      entry do not matter
+ * Outputs (device):
+ *   node_offsets int32 [B + 1]   packed layout of the kept trees (as bole_tree_verify
+ *                                takes it)
+ *   parent int32 [B * n_max]     tree-local parent (-1 for depth 1), insertion order, so
+ *                                parent[i] < i; rows past node_offsets[B] are not written
+ *   token  int32 [B * n_max]     vocabulary index of each node
+ *   rho    float [B * n_max]     path score of each node (may be NULL)
+ *   speedup float [B]            S(N) at the kept size (may be NULL)
+ * Host errors (BOLE_ERR_INVALID_VALUE / BOLE_ERR_UNSUPPORTED) are returned before any
+ * launch: depth outside 1..32, n_max outside 1..64, vocab < 1, a short or misaligned
+ * workspace, missing pointers, l_ar not > 0.
+ */
+enum { BOLE_BUILD_FIXED_BUDGET = 1 };
+
+typedef struct {
+    int32_t batch;  /* B >= 0 sequences */
+    int32_t depth;  /* drafted positions per sequence, 1..32 */
+    int32_t vocab;  /* vocabulary size, >= 1 */
+    int32_t n_max;  /* tree budget cap, 1..64 */
+    int32_t flags;  /* BOLE_BUILD_* */
+} bole_build_dims_t;
+
+/* Workspace bytes bole_build_tree needs for these dims (0 for invalid dims). */
+BOLE_API size_t bole_build_tree_workspace_size(const bole_build_dims_t *dims);
+
+BOLE_API bole_status_t bole_build_tree(const float *marginals, const float *cost, float l_ar,
+                               void *workspace, size_t workspace_bytes,
+                               const bole_build_dims_t *dims, int32_t *node_offsets,
+                               int32_t *parent, int32_t *token, float *rho, float *speedup,
+                               bole_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

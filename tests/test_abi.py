@@ -137,6 +137,33 @@ def test_layer_stacks_checked_without_launch():
         ctypes.byref(d), None, None) == bole.BOLE_ERR_INVALID_VALUE
 
 
+
+def test_build_tree_checked_without_launch():
+    L = bole.lib
+    BD = bole.bole_build_dims_t
+    for bad in (BD(4, 0, 100, 8, 0), BD(4, 33, 100, 8, 0), BD(4, 8, 100, 65, 0),
+                BD(4, 8, 0, 8, 0), BD(4, 8, 100, 0, 0), BD(4, 8, 100, 8, 2)):
+        assert L.bole_build_tree_workspace_size(ctypes.byref(bad)) == 0
+    d = BD(4, 8, 1000, 16, 0)
+    need = L.bole_build_tree_workspace_size(ctypes.byref(d))
+    assert need > 4 * 8 * 64 * 8
+    args = lambda **kw: dict(dict(m=0x1000, cost=0x2000, l_ar=1.0, ws=0x3000, wsb=need,
+                                   offs=0x4000, par=0x5000, tok=0x6000), **kw)
+
+    def call(dims, **kw):
+        a = args(**kw)
+        return L.bole_build_tree(a["m"], a["cost"], a["l_ar"], a["ws"], a["wsb"],
+                                 ctypes.byref(dims), a["offs"], a["par"], a["tok"], None, None,
+                                 None)
+    assert call(d, wsb=need - 1) == bole.BOLE_ERR_INVALID_VALUE      # short workspace
+    assert call(d, ws=0x3008) == bole.BOLE_ERR_INVALID_VALUE        # misaligned workspace
+    assert call(d, l_ar=0.0) == bole.BOLE_ERR_INVALID_VALUE
+    assert call(d, cost=None) == bole.BOLE_ERR_INVALID_VALUE
+    assert call(d, m=None) == bole.BOLE_ERR_INVALID_VALUE
+    assert call(BD(4, 33, 1000, 16, 0)) == bole.BOLE_ERR_UNSUPPORTED
+    assert call(BD(0, 8, 1000, 16, 0)) == bole.BOLE_OK                # empty batch
+
+
 def test_status_strings_and_limits():
     assert bole.lib.bole_max_tree_nodes() == bole.MAX_TREE_NODES == 64
     for code, name in [(0, b"BOLE_OK"), (1, b"BOLE_ERR_INVALID_VALUE"),

@@ -24,7 +24,8 @@ MAX_TREE_NODES = 64
 EXPORTED = ("bole_max_tree_nodes", "bole_status_string", "bole_check_dims", "bole_tree_verify",
             "bole_tree_verify_lazy_commit", "bole_tree_verify_layers", "bole_commit_path_layers",
             "bole_tree_verify_lazy_commit_layers", "bole_tree_verify_naive", "bole_commit_path",
-            "bole_tree_prepare")
+            "bole_tree_prepare", "bole_build_tree_workspace_size", "bole_build_tree")
+BOLE_BUILD_FIXED_BUDGET = 1
 
 
 class bole_dims_t(ctypes.Structure):
@@ -44,6 +45,11 @@ class bole_layer_t(ctypes.Structure):
                 ("v", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("prev_k", ctypes.c_void_p), ("prev_v", ctypes.c_void_p),
                 ("prev_gate", ctypes.c_void_p)]
+
+
+class bole_build_dims_t(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("depth", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("n_max", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class BoleError(RuntimeError):
@@ -75,6 +81,11 @@ def _load():
     lib.bole_commit_path_layers.argtypes = [LP, I32, P, P, P, P, D, P, P, P]
     lib.bole_tree_verify_lazy_commit_layers.restype = ctypes.c_int
     lib.bole_tree_verify_lazy_commit_layers.argtypes = [LP, I32, P, P, P, P, D, P, P, P, P, D, P, P]
+    BD = ctypes.POINTER(bole_build_dims_t)
+    lib.bole_build_tree_workspace_size.restype = ctypes.c_size_t
+    lib.bole_build_tree_workspace_size.argtypes = [BD]
+    lib.bole_build_tree.restype = ctypes.c_int
+    lib.bole_build_tree.argtypes = [P, P, ctypes.c_float, P, ctypes.c_size_t, BD, P, P, P, P, P, P]
     lib.bole_tree_verify_naive.restype = ctypes.c_int
     lib.bole_tree_verify_naive.argtypes = [P, P, P, P, P, P, P, P, P, D, P, P]
     lib.bole_commit_path.restype = ctypes.c_int
@@ -517,6 +528,60 @@ def bind_tree_verify_lazy_commit_layers(layers, prev_parent, prev_node_offsets,
                                    prev_trees_le_32)
     return _Bound(lib.bole_tree_verify_lazy_commit_layers, "bole_tree_verify_lazy_commit_layers",
                   args, keep)
+
+
+# ---- draft-tree construction (best-first expansion and budget controller)
+
+def _build_call(marginals, cost, l_ar, n_max, fixed, workspace, out, stream):
+    _need(marginals, "marginals", torch.float32)
+    dev = marginals.device
+    if marginals.dim() != 3:
+        raise ValueError("marginals must be [B, depth, vocab]")
+    B, D, V = marginals.shape
+    if cost is not None:
+        _need(cost, "cost", torch.float32, dev)
+        if cost.numel() < n_max:
+            raise ValueError("cost needs n_max entries")
+    dims = bole_build_dims_t(B, D, V, n_max, BOLE_BUILD_FIXED_BUDGET if fixed else 0)
+    need = lib.bole_build_tree_workspace_size(ctypes.byref(dims))
+    if need == 0:
+        raise ValueError("unsupported tree-build dims (depth 1..32, n_max 1..64, vocab >= 1)")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", device=dev)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    if out is None:
+        cap = max(B * n_max, 1)
+        out = {"node_offsets": torch.empty(B + 1, dtype=torch.int32, device=dev),
+               "parent": torch.empty(cap, dtype=torch.int32, device=dev),
+               "token": torch.empty(cap, dtype=torch.int32, device=dev),
+               "rho": torch.empty(cap, dtype=torch.float32, device=dev),
+               "speedup": torch.empty(max(B, 1), dtype=torch.float32, device=dev) if cost is not None else None}
+    args = (_ptr(marginals), _ptr(cost), ctypes.c_float(l_ar), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), ctypes.byref(dims),
+            _ptr(out["node_offsets"]), _ptr(out["parent"]), _ptr(out["token"]), _ptr(out.get("rho")),
+            _ptr(out.get("speedup")), _stream(stream))
+    return args, out, (marginals, cost, workspace, out, dims)
+
+
+def bole_build_tree(marginals, cost, l_ar=1.0, n_max=64, fixed=False, workspace=None, out=None,
+                    stream=None):
+    """Best-first draft trees from position-wise marginals [B, depth, vocab] (fp32
+    probabilities) with the budget controller over cost[n_max] (C(N) at N - 1) and L_AR.
+    Returns a dict of device tensors: node_offsets [B + 1], and parent, token, rho (packed,
+    capacity B * n_max; node_offsets[B] of them are written), speedup [B]."""
+    args, out, _ = _build_call(marginals, cost, l_ar, n_max, fixed, workspace, out, stream)
+    _check(lib.bole_build_tree(*args), "bole_build_tree")
+    return out
+
+
+def bind_build_tree(marginals, cost, l_ar=1.0, n_max=64, fixed=False, workspace=None, out=None,
+                    stream=None):
+    args, out, keep = _build_call(marginals, cost, l_ar, n_max, fixed, workspace, out, stream)
+    bound = _Bound(lib.bole_build_tree, "bole_build_tree", args, keep)
+    bound.out = out
+    return bound
 
 
 def bole_tree_prepare(parent, node_offsets, heads=1, d_k=1, gate=None, want_cumlog=False,

@@ -285,4 +285,34 @@ bole_status_t bole_tree_prepare(const int32_t *parent, const int32_t *node_offse
                                          tree_status, reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t bole_build_tree_workspace_size(const bole_build_dims_t *dims) {
+    if (dims == nullptr || !bole::build_dims_ok(*dims)) return 0;
+    return bole::build_workspace_bytes(*dims);
+}
+
+bole_status_t bole_build_tree(const float *marginals, const float *cost, float l_ar,
+                              void *workspace, size_t workspace_bytes,
+                              const bole_build_dims_t *dims, int32_t *node_offsets,
+                              int32_t *parent, int32_t *token, float *rho, float *speedup,
+                              bole_stream_t stream) {
+    if (dims == nullptr) return BOLE_ERR_INVALID_VALUE;
+    const bole_build_dims_t &d = *dims;
+    if (d.batch < 0 || d.vocab < 1 || d.n_max < 1 || d.depth < 1 ||
+        (d.flags & ~BOLE_BUILD_FIXED_BUDGET))
+        return BOLE_ERR_INVALID_VALUE;
+    if (!bole::build_dims_ok(d)) return BOLE_ERR_UNSUPPORTED;
+    if (d.batch == 0) return BOLE_OK;
+    const bool fixed = (d.flags & BOLE_BUILD_FIXED_BUDGET) != 0;
+    if (marginals == nullptr || node_offsets == nullptr || parent == nullptr || token == nullptr)
+        return BOLE_ERR_INVALID_VALUE;
+    if (cost == nullptr && (!fixed || speedup != nullptr)) return BOLE_ERR_INVALID_VALUE;
+    if (!fixed && !(l_ar > 0.f && l_ar < 3.4e38f)) return BOLE_ERR_INVALID_VALUE;
+    if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 ||
+        workspace_bytes < bole::build_workspace_bytes(d))
+        return BOLE_ERR_INVALID_VALUE;
+    return from_hip(bole::launch_build_tree(marginals, cost, l_ar, workspace, d, node_offsets,
+                                            parent, token, rho, speedup,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -71,4 +71,12 @@ hipError_t launch_commit(const bole_layer_t *layers, int nl, const int32_t *pare
                          const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
                          int32_t *tree_status, hipStream_t stream);
 
+// Draft-tree construction (tree_build.hip).
+bool build_dims_ok(const bole_build_dims_t &d);
+size_t build_workspace_bytes(const bole_build_dims_t &d);
+hipError_t launch_build_tree(const float *marginals, const float *cost, float l_ar,
+                             void *workspace, const bole_build_dims_t &d, int32_t *node_offsets,
+                             int32_t *parent, int32_t *token, float *rho, float *speedup,
+                             hipStream_t stream);
+
 }  // namespace bole

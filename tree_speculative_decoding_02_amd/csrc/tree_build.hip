@@ -1,0 +1,432 @@
+// tree_build.hip - draft-tree construction from a block drafter's position-wise
+// marginals and the online budget controller (BASTION summary page: section 1 path
+// score, section 2 best-first expansion, section 3 budget controller).
+//
+// Three launches:
+//  1. topk_slice_kernel: the top 64 entries of every (sequence, position) row, per
+//     vocabulary slice of kSliceElems, ordered by (probability desc, index asc). The only
+//     HBM-heavy step: it reads the marginals once.
+//  2. build_kernel: one wavefront per sequence merges its slices' lists per position,
+//     grows the best-first tree (lane = candidate source) and runs the controller.
+//  3. pack_kernel: one workgroup scans the kept sizes into node_offsets and packs the
+//     trees.
+// Only the top 64 tokens of a position can ever be used: one parent's children are
+// inserted in rank order and a tree has at most 64 nodes.
+#include "bole_device.h"
+#include "launch.h"
+
+namespace bole {
+
+constexpr int kTopK = 64;
+constexpr int kBuildThreads = 256;
+constexpr int kPerThread = 64;                           // register-resident keys per thread
+constexpr int kSliceElems = kBuildThreads * kPerThread;  // 16384
+constexpr int kGatherCap = 1024;                         // candidates sorted in LDS
+constexpr int kMaxDepth = 32;
+constexpr int kMaxBudget = 64;
+
+// Orderable key of a float: a larger float has a larger key; 0 marks "no element".
+__device__ __forceinline__ uint32_t f2key(float f) {
+    const uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);  // -0 ranks as +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// rank order: larger key first, then lower index
+__device__ __forceinline__ bool better(uint32_t ka, int ia, uint32_t kb, int ib) {
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+// One compare-exchange step of a 64-lane bitonic network: the lower lane of each pair
+// keeps the better element when `desc`, the worse otherwise.
+__device__ __forceinline__ void bitonic_step(uint32_t &k, int &i, int j, bool desc) {
+    const int lane = lane_id();
+    const uint32_t pk = __shfl_xor(k, j, 64);
+    const int pi = __shfl_xor(i, j, 64);
+    const bool keep_better = ((lane & j) == 0) == desc;
+    const bool pb = better(pk, pi, k, i);
+    if (keep_better ? pb : !pb) {
+        k = pk;
+        i = pi;
+    }
+}
+
+// Sorts the 64 lane values in rank order (lane 0 the best).
+__device__ __forceinline__ void wave_sort64(uint32_t &k, int &i) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+        for (int j = size >> 1; j > 0; j >>= 1) bitonic_step(k, i, j, (lane & size) == 0);
+}
+
+// (k, i) sorted in rank order across lanes; merges another sorted list (nk, ni) and
+// keeps the best 64, sorted.
+__device__ __forceinline__ void wave_merge64(uint32_t &k, int &i, uint32_t nk, int ni) {
+    const int lane = lane_id();
+    const uint32_t rk = __shfl(nk, 63 - lane, 64);
+    const int ri = __shfl(ni, 63 - lane, 64);
+    if (better(rk, ri, k, i)) {
+        k = rk;
+        i = ri;
+    }
+#pragma unroll
+    for (int j = 32; j > 0; j >>= 1) bitonic_step(k, i, j, true);
+}
+
+// ---- 1. top 64 of one vocabulary slice of one (sequence, position) row
+//
+// Thread t holds elements lo + (j * 256 + t) * W + c (j < kPerThread / W, c < W) as keys.
+// A threshold theta that at least 64 elements reach is the smallest over the four
+// wavefronts of the wavefront's 16th largest thread maximum; the elements >= theta are
+// gathered in LDS and sorted, and the first 64 kept. If more than kGatherCap elements
+// reach theta (many equal values), 64 rounds of block-wide extraction of the best
+// remaining element give the same list exactly.
+template <int W>
+__global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
+    const float *__restrict__ marginals, uint2 *__restrict__ lists, int V, int S) {
+    constexpr int J = kPerThread / W;
+    __shared__ uint32_t s_k[kGatherCap];
+    __shared__ int s_i[kGatherCap];
+    __shared__ uint32_t s_theta[4];
+    __shared__ int s_cnt;
+    __shared__ uint32_t s_rk[4];
+    __shared__ int s_ri[4];
+    const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
+    const size_t row = blockIdx.x / S;
+    const int slice = blockIdx.x - (int)row * S;
+    const int lo = slice * kSliceElems;
+    const float *src = marginals + row * (size_t)V;
+    uint2 *dst = lists + (size_t)blockIdx.x * kTopK;
+
+    uint32_t key[J][W];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int e = lo + (j * kBuildThreads + t) * W;
+        if (W == 4 && e + 3 < V) {
+            typedef float f4 __attribute__((ext_vector_type(4)));
+            const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(src + e));
+#pragma unroll
+            for (int c = 0; c < W; ++c) key[j][c] = f2key(x[c]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < W; ++c)
+                key[j][c] = e + c < V && e + c < lo + kSliceElems ? f2key(__builtin_nontemporal_load(src + e + c)) : 0u;
+        }
+    }
+    auto index_of = [&](int j, int c) { return lo + (j * kBuildThreads + t) * W + c; };
+
+    // threshold
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int c = 0; c < W; ++c) mx = max(mx, key[j][c]);
+    {
+        uint32_t k = mx;
+        int i = lane;
+        wave_sort64(k, i);
+        const uint32_t th = __shfl(k, 15, 64);
+        if (lane == 0) s_theta[wave] = th;
+    }
+    if (t == 0) s_cnt = 0;
+    __syncthreads();
+    const uint32_t theta = min(min(s_theta[0], s_theta[1]), min(s_theta[2], s_theta[3]));
+
+    // gather (one LDS atomic per wavefront and element slot)
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int c = 0; c < W; ++c) {
+            const bool take = key[j][c] != 0u && key[j][c] >= theta;
+            const uint64_t m = __ballot(take);
+            if (m) {
+                int base = 0;
+                if (lane == __builtin_ctzll(m)) base = atomicAdd(&s_cnt, __popcll(m));
+                base = __shfl(base, __builtin_ctzll(m), 64);
+                const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                            (uint32_t)(m >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                if (take && slot < kGatherCap) {
+                    s_k[slot] = key[j][c];
+                    s_i[slot] = index_of(j, c);
+                }
+            }
+        }
+    __syncthreads();
+    const int cnt = s_cnt;
+
+    if (cnt <= kGatherCap) {
+        int P = kTopK;
+        while (P < cnt) P <<= 1;
+        for (int x = cnt + t; x < P; x += kBuildThreads) {
+            s_k[x] = 0u;
+            s_i[x] = 0x7fffffff;
+        }
+        __syncthreads();
+        // bitonic sort of P entries in rank order
+        for (int size = 2; size <= P; size <<= 1)
+            for (int jj = size >> 1; jj > 0; jj >>= 1) {
+                for (int p = t; p < P / 2; p += kBuildThreads) {
+                    const int a = 2 * jj * (p / jj) + (p % jj), b2 = a + jj;
+                    const bool desc = (a & size) == 0;
+                    const bool bb = better(s_k[b2], s_i[b2], s_k[a], s_i[a]);
+                    if (desc ? bb : !bb && !(s_k[b2] == s_k[a] && s_i[b2] == s_i[a])) {
+                        const uint32_t tk = s_k[a];
+                        const int ti = s_i[a];
+                        s_k[a] = s_k[b2];
+                        s_i[a] = s_i[b2];
+                        s_k[b2] = tk;
+                        s_i[b2] = ti;
+                    }
+                }
+                __syncthreads();
+            }
+        if (t < kTopK) dst[t] = make_uint2(s_k[t], (uint32_t)s_i[t]);
+        return;
+    }
+
+    // many ties: extract the best remaining element 64 times
+    for (int r = 0; r < kTopK; ++r) {
+        uint32_t bk = 0u;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int c = 0; c < W; ++c)
+                if (better(key[j][c], index_of(j, c), bk, bi)) {
+                    bk = key[j][c];
+                    bi = index_of(j, c);
+                }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const uint32_t pk = __shfl_xor(bk, off, 64);
+            const int pi = __shfl_xor(bi, off, 64);
+            if (better(pk, pi, bk, bi)) {
+                bk = pk;
+                bi = pi;
+            }
+        }
+        if (lane == 0) {
+            s_rk[wave] = bk;
+            s_ri[wave] = bi;
+        }
+        __syncthreads();
+        bk = s_rk[0];
+        bi = s_ri[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+            if (better(s_rk[w], s_ri[w], bk, bi)) {
+                bk = s_rk[w];
+                bi = s_ri[w];
+            }
+        __syncthreads();
+        if (t == 0) dst[r] = make_uint2(bk, (uint32_t)(bk ? bi : 0x7fffffff));
+        if (bk != 0u) {
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+#pragma unroll
+                for (int c = 0; c < W; ++c)
+                    if (index_of(j, c) == bi) key[j][c] = 0u;
+        }
+    }
+}
+
+// ---- 2. best-first tree and controller, one wavefront per sequence
+//
+// Lane l < n is tree node l as a candidate source (its depth, next child rank, score);
+// lane 63 is the verified context, whose children are the depth-1 tokens. Each step every
+// source offers its best child not yet inserted, score fp32(rho_source * q); the best
+// offer (score desc, source asc with the context as -1) becomes node n. Node n's outputs
+// are kept in lane n's output registers (which do not alias the context's state in
+// lane 63).
+__global__ __launch_bounds__(64) void build_kernel(
+    const uint2 *__restrict__ lists, const float *__restrict__ cost, float l_ar, int D, int S,
+    int n_max, int fixed, int32_t *__restrict__ n_nodes, int32_t *__restrict__ par_out,
+    int32_t *__restrict__ tok_out, float *__restrict__ rho_out, float *__restrict__ speedup) {
+    __shared__ float s_val[kMaxDepth][kTopK];
+    __shared__ int s_tok[kMaxDepth][kTopK];
+    __shared__ uint32_t s_key[kMaxDepth][kTopK];
+    const int lane = lane_id();
+    const int b = blockIdx.x;
+
+    for (int d = 0; d < D; ++d) {
+        const uint2 *l0 = lists + ((size_t)b * D + d) * S * kTopK;
+        uint2 e = l0[lane];
+        uint32_t k = e.x;
+        int i = (int)e.y;
+        for (int s = 1; s < S; ++s) {
+            const uint2 x = l0[(size_t)s * kTopK + lane];
+            wave_merge64(k, i, x.x, (int)x.y);
+        }
+        s_key[d][lane] = k;
+        s_val[d][lane] = key2f(k);
+        s_tok[d][lane] = i;
+    }
+    __syncthreads();
+
+    // source state (lane 63: the context) and node outputs
+    int src_depth = 0, src_rank = 0;
+    float src_rho = 1.f;
+    int o_par = -1, o_tok = 0;
+    float o_rho = 0.f;
+    int n = 0;
+    for (; n < n_max; ++n) {
+        const bool is_src = lane < n || lane == 63;
+        float sc = -1.f;
+        if (is_src && src_depth < D && src_rank < kTopK && s_key[src_depth][src_rank] != 0u)
+            sc = __fmul_rn(src_rho, s_val[src_depth][src_rank]);
+        int who = lane == 63 ? -1 : lane;
+        if (sc < 0.f) who = 0x7fffffff;
+        float bs = sc;
+        int bw = who;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ps = __shfl_xor(bs, off, 64);
+            const int pw = __shfl_xor(bw, off, 64);
+            if (ps > bs || (ps == bs && pw < bw)) {
+                bs = ps;
+                bw = pw;
+            }
+        }
+        if (bs < 0.f) break;  // no source offers a child (wave-uniform)
+        const int wl = bw < 0 ? 63 : bw;  // the winning source's lane
+        const int wd = __shfl(src_depth, wl, 64), wr = __shfl(src_rank, wl, 64);
+        if (lane == wl) ++src_rank;
+        if (lane == n) {
+            o_par = bw < 0 ? -1 : bw;
+            o_tok = s_tok[wd][wr];
+            o_rho = bs;
+            if (n < 63) {
+                src_depth = wd + 1;
+                src_rank = 0;
+                src_rho = bs;
+            }
+        }
+    }
+    const int built = n;
+
+    // controller: A_hat summed in insertion order, S(N) = A_hat(N) * L_AR / C(N)
+    int keep = built;
+    float s_keep = 0.f;
+    if (built > 0 && cost != nullptr) {
+        float A = 0.f, s_prev = 0.f;
+        bool stopped = false;
+        for (int N = 1; N <= built; ++N) {
+            A = __fadd_rn(A, __shfl(o_rho, N - 1, 64));
+            const float sN = __fdiv_rn(__fmul_rn(A, l_ar), cost[N - 1]);
+            if (N > 1 && !fixed && sN < s_prev) {
+                keep = N - 1;
+                stopped = true;
+                break;
+            }
+            s_prev = sN;
+        }
+        s_keep = s_prev;  // S at the kept size
+        (void)stopped;
+    }
+    if (lane < keep) {
+        par_out[(size_t)b * n_max + lane] = o_par;
+        tok_out[(size_t)b * n_max + lane] = o_tok;
+        rho_out[(size_t)b * n_max + lane] = o_rho;
+    }
+    if (lane == 0) {
+        n_nodes[b] = keep;
+        if (speedup) speedup[b] = s_keep;
+    }
+}
+
+// ---- 3. node_offsets and packed trees, one workgroup
+constexpr int kPackThreads = 1024;
+
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(
+    const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ par_in,
+    const int32_t *__restrict__ tok_in, const float *__restrict__ rho_in, int B, int n_max,
+    int32_t *__restrict__ node_offsets, int32_t *__restrict__ parent, int32_t *__restrict__ token,
+    float *__restrict__ rho) {
+    __shared__ int s_part[kPackThreads];
+    const int t = threadIdx.x;
+    const int per = (B + kPackThreads - 1) / kPackThreads;
+    const int b0 = min(B, t * per), b1 = min(B, b0 + per);
+    int sum = 0;
+    for (int b = b0; b < b1; ++b) sum += n_nodes[b];
+    s_part[t] = sum;
+    __syncthreads();
+    // inclusive scan of the per-thread sums (Hillis-Steele)
+    for (int off = 1; off < kPackThreads; off <<= 1) {
+        const int x = t >= off ? s_part[t - off] : 0;
+        __syncthreads();
+        s_part[t] += x;
+        __syncthreads();
+    }
+    int off = s_part[t] - sum;
+    for (int b = b0; b < b1; ++b) {
+        node_offsets[b] = off;
+        const int n = n_nodes[b];
+        for (int j = 0; j < n; ++j) {
+            parent[off + j] = par_in[(size_t)b * n_max + j];
+            token[off + j] = tok_in[(size_t)b * n_max + j];
+            if (rho) rho[off + j] = rho_in[(size_t)b * n_max + j];
+        }
+        off += n;
+    }
+    if (t == kPackThreads - 1) node_offsets[B] = s_part[t];
+}
+
+// ---- host side
+struct BuildLayout {
+    size_t lists, n_nodes, par, tok, rho, total;
+    int S;
+};
+
+static BuildLayout build_layout(const bole_build_dims_t &d) {
+    BuildLayout L;
+    L.S = (d.vocab + kSliceElems - 1) / kSliceElems;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t B = (size_t)d.batch;
+    L.lists = 0;
+    L.n_nodes = al(B * d.depth * L.S * kTopK * sizeof(uint2));
+    L.par = L.n_nodes + al(B * sizeof(int32_t));
+    L.tok = L.par + al(B * d.n_max * sizeof(int32_t));
+    L.rho = L.tok + al(B * d.n_max * sizeof(int32_t));
+    L.total = L.rho + al(B * d.n_max * sizeof(float));
+    return L;
+}
+
+bool build_dims_ok(const bole_build_dims_t &d) {
+    if (d.batch < 0 || d.depth < 1 || d.depth > kMaxDepth || d.vocab < 1 || d.n_max < 1 ||
+        d.n_max > kMaxBudget || (d.flags & ~BOLE_BUILD_FIXED_BUDGET))
+        return false;
+    const uint64_t S = ((uint64_t)d.vocab + kSliceElems - 1) / kSliceElems;
+    return (uint64_t)d.batch * d.depth * S < (1ull << 31);
+}
+
+size_t build_workspace_bytes(const bole_build_dims_t &d) { return build_layout(d).total; }
+
+hipError_t launch_build_tree(const float *marginals, const float *cost, float l_ar,
+                             void *workspace, const bole_build_dims_t &d, int32_t *node_offsets,
+                             int32_t *parent, int32_t *token, float *rho, float *speedup,
+                             hipStream_t stream) {
+    const BuildLayout L = build_layout(d);
+    char *ws = static_cast<char *>(workspace);
+    uint2 *lists = reinterpret_cast<uint2 *>(ws + L.lists);
+    int32_t *nn = reinterpret_cast<int32_t *>(ws + L.n_nodes);
+    int32_t *par = reinterpret_cast<int32_t *>(ws + L.par);
+    int32_t *tok = reinterpret_cast<int32_t *>(ws + L.tok);
+    float *rh = reinterpret_cast<float *>(ws + L.rho);
+    const unsigned rows = (unsigned)d.batch * (unsigned)d.depth * (unsigned)L.S;
+    const bool vec = d.vocab % 4 == 0 && reinterpret_cast<uintptr_t>(marginals) % 16 == 0;
+    if (vec)
+        topk_slice_kernel<4><<<dim3(rows), dim3(kBuildThreads), 0, stream>>>(marginals, lists, d.vocab, L.S);
+    else
+        topk_slice_kernel<1><<<dim3(rows), dim3(kBuildThreads), 0, stream>>>(marginals, lists, d.vocab, L.S);
+    build_kernel<<<dim3((unsigned)d.batch), dim3(64), 0, stream>>>(
+        lists, cost, l_ar, d.depth, L.S, d.n_max, (d.flags & BOLE_BUILD_FIXED_BUDGET) ? 1 : 0,
+        nn, par, tok, rh, speedup);
+    pack_kernel<<<dim3(1), dim3(kPackThreads), 0, stream>>>(nn, par, tok, rh, d.batch, d.n_max,
+                                                          node_offsets, parent, token, rho);
+    return hipGetLastError();
+}
+
+}  // namespace bole
