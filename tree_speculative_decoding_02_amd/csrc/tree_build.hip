@@ -27,8 +27,10 @@ constexpr int kMaxBudget = 64;
 
 // Orderable key of a float: a larger float has a larger key; 0 marks "no element".
 __device__ __forceinline__ uint32_t f2key(float f) {
-    const uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);  // -0 ranks as +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    uint32_t u = __float_as_uint(f);
+    u = u == 0x80000000u ? 0u : u;                          // -0 ranks as +0
+    const uint32_t neg = (uint32_t)((int32_t)u >> 31);      // all ones for a negative
+    return u ^ (neg | 0x80000000u);                         // flip all bits, or the sign bit
 }
 __device__ __forceinline__ float key2f(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
@@ -80,9 +82,9 @@ __device__ __forceinline__ void wave_merge64(uint32_t &k, int &i, uint32_t nk, i
 // Thread t holds elements lo + (j * 256 + t) * W + c (j < kPerThread / W, c < W) as keys.
 // A threshold theta that at least 64 elements reach is the smallest over the four
 // wavefronts of the wavefront's 16th largest thread maximum; the elements >= theta are
-// gathered in LDS and sorted, and the first 64 kept. If more than kGatherCap elements
-// reach theta (many equal values), 64 rounds of block-wide extraction of the best
-// remaining element give the same list exactly.
+// gathered in LDS and each one's rank among them counted, the first 64 kept. If more
+// than kGatherCap elements reach theta (many equal values), 64 rounds of block-wide
+// extraction of the best remaining element give the same list exactly.
 template <int W>
 __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
     const float *__restrict__ marginals, uint2 *__restrict__ lists, int V, int S) {
@@ -100,22 +102,31 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
     const float *src = marginals + row * (size_t)V;
     uint2 *dst = lists + (size_t)blockIdx.x * kTopK;
 
-    uint32_t key[J][W];
+    // every load issued before any is used: addresses clamped into the row, keys of
+    // elements outside the slice or the row masked to 0 afterwards (in place)
+    typedef uint32_t uv __attribute__((ext_vector_type(W)));
+    uv key[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int e = lo + (j * kBuildThreads + t) * W;
-        if (W == 4 && e + 3 < V) {
-            typedef float f4 __attribute__((ext_vector_type(4)));
-            const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(src + e));
+        key[j] = __builtin_nontemporal_load(reinterpret_cast<const uv *>(src + (uint32_t)min(e, V - W)));
+    }
+    if (lo + kSliceElems <= V) {  // a whole slice (all but the last of a row)
 #pragma unroll
-            for (int c = 0; c < W; ++c) key[j][c] = f2key(x[c]);
-        } else {
+        for (int j = 0; j < J; ++j)
 #pragma unroll
-            for (int c = 0; c < W; ++c)
-                key[j][c] = e + c < V && e + c < lo + kSliceElems ? f2key(__builtin_nontemporal_load(src + e + c)) : 0u;
+            for (int c = 0; c < W; ++c) key[j][c] = f2key(__uint_as_float(key[j][c]));
+    } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = lo + (j * kBuildThreads + t) * W;
+#pragma unroll
+            for (int c = 0; c < W; ++c) {
+                const uint32_t k = f2key(__uint_as_float(key[j][c]));
+                key[j][c] = e + c < V ? k : 0u;
+            }
         }
     }
-    auto index_of = [&](int j, int c) { return lo + (j * kBuildThreads + t) * W + c; };
 
     // threshold
     uint32_t mx = 0;
@@ -124,10 +135,13 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
 #pragma unroll
         for (int c = 0; c < W; ++c) mx = max(mx, key[j][c]);
     {
-        uint32_t k = mx;
-        int i = lane;
-        wave_sort64(k, i);
-        const uint32_t th = __shfl(k, 15, 64);
+        // the wavefront's 16th largest thread maximum, bit by bit: the largest th with
+        // at least 16 maxima >= th
+        uint32_t th = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = th | (1u << bit);
+            if (__popcll(__ballot(mx >= cand)) >= 16) th = cand;
+        }
         if (lane == 0) s_theta[wave] = th;
     }
     if (t == 0) s_cnt = 0;
@@ -136,7 +150,11 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
 
     // gather (one LDS atomic per wavefront and element slot)
 #pragma unroll
-    for (int j = 0; j < J; ++j)
+    for (int j = 0; j < J; ++j) {
+        // the slab's first index, recomputed per slab (the empty asm keeps the compiler
+        // from holding all 64 indices in registers)
+        int sbase = lo + (j * kBuildThreads + t) * W;
+        asm volatile("" : "+v"(sbase));
 #pragma unroll
         for (int c = 0; c < W; ++c) {
             const bool take = key[j][c] != 0u && key[j][c] >= theta;
@@ -150,55 +168,50 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
                 if (take && slot < kGatherCap) {
                     s_k[slot] = key[j][c];
-                    s_i[slot] = index_of(j, c);
+                    s_i[slot] = sbase + c;
                 }
             }
         }
+    }
     __syncthreads();
     const int cnt = s_cnt;
 
     if (cnt <= kGatherCap) {
-        int P = kTopK;
-        while (P < cnt) P <<= 1;
-        for (int x = cnt + t; x < P; x += kBuildThreads) {
-            s_k[x] = 0u;
-            s_i[x] = 0x7fffffff;
+        // each candidate's rank is the number of better candidates ((key, index) pairs
+        // are distinct, so ranks are too); ranks below 64 are written in place
+        for (int x = t; x < cnt; x += kBuildThreads) {
+            const uint32_t kx = s_k[x];
+            const int ix = s_i[x];
+            int rank = 0;
+            for (int y = 0; y < cnt; ++y) rank += better(s_k[y], s_i[y], kx, ix) ? 1 : 0;
+            if (rank < kTopK) dst[rank] = make_uint2(kx, (uint32_t)ix);
         }
-        __syncthreads();
-        // bitonic sort of P entries in rank order
-        for (int size = 2; size <= P; size <<= 1)
-            for (int jj = size >> 1; jj > 0; jj >>= 1) {
-                for (int p = t; p < P / 2; p += kBuildThreads) {
-                    const int a = 2 * jj * (p / jj) + (p % jj), b2 = a + jj;
-                    const bool desc = (a & size) == 0;
-                    const bool bb = better(s_k[b2], s_i[b2], s_k[a], s_i[a]);
-                    if (desc ? bb : !bb && !(s_k[b2] == s_k[a] && s_i[b2] == s_i[a])) {
-                        const uint32_t tk = s_k[a];
-                        const int ti = s_i[a];
-                        s_k[a] = s_k[b2];
-                        s_i[a] = s_i[b2];
-                        s_k[b2] = tk;
-                        s_i[b2] = ti;
-                    }
-                }
-                __syncthreads();
-            }
-        if (t < kTopK) dst[t] = make_uint2(s_k[t], (uint32_t)s_i[t]);
+        for (int r = cnt + t; r < kTopK; r += kBuildThreads) dst[r] = make_uint2(0u, 0x7fffffffu);
         return;
     }
 
-    // many ties: extract the best remaining element 64 times
+    // many ties: 64 rounds, each taking the best element not yet taken. The keys are
+    // read again from memory (an element is taken when it ranks at or above the last
+    // one taken), so no register holds them across the rounds.
+    uint32_t lk = 0xffffffffu;  // last taken (key, index); everything better is taken
+    int li = -1;
     for (int r = 0; r < kTopK; ++r) {
         uint32_t bk = 0u;
         int bi = 0x7fffffff;
+        for (int j = 0; j < J; ++j) {
+            const int e = lo + (j * kBuildThreads + t) * W;
+            const uv x = *reinterpret_cast<const uv *>(src + min(e, V - W));
 #pragma unroll
-        for (int j = 0; j < J; ++j)
-#pragma unroll
-            for (int c = 0; c < W; ++c)
-                if (better(key[j][c], index_of(j, c), bk, bi)) {
-                    bk = key[j][c];
-                    bi = index_of(j, c);
+            for (int c = 0; c < W; ++c) {
+                const uint32_t k = e + c < V ? f2key(__uint_as_float(x[c])) : 0u;
+                const int ix = e + c;
+                // not yet taken: ranks strictly after (lk, li)
+                if (better(lk, li, k, ix) && better(k, ix, bk, bi)) {
+                    bk = k;
+                    bi = ix;
                 }
+            }
+        }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
             const uint32_t pk = __shfl_xor(bk, off, 64);
@@ -223,14 +236,34 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
             }
         __syncthreads();
         if (t == 0) dst[r] = make_uint2(bk, (uint32_t)(bk ? bi : 0x7fffffff));
-        if (bk != 0u) {
-#pragma unroll
-            for (int j = 0; j < J; ++j)
-#pragma unroll
-                for (int c = 0; c < W; ++c)
-                    if (index_of(j, c) == bi) key[j][c] = 0u;
-        }
+        lk = bk;
+        li = bi;
     }
+}
+
+// Best (score desc, who asc) over the wavefront, in every lane. DPP reduction toward lane
+// 63 (row_shr 1, 2, 4, 8 within each row of 16, then row_bcast 15 and 31 across rows);
+// lanes whose DPP source is outside the row or masked keep the identity (-inf, INT_MAX).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_dpp_step(float &s, int &w) {
+    const float ps = __int_as_float(__builtin_amdgcn_update_dpp(
+        (int)0xff800000, __float_as_int(s), CTRL, ROW_MASK, 0xf, false));
+    const int pw = __builtin_amdgcn_update_dpp(0x7fffffff, w, CTRL, ROW_MASK, 0xf, false);
+    if (ps > s || (ps == s && pw < w)) {
+        s = ps;
+        w = pw;
+    }
+}
+
+__device__ __forceinline__ void wave_argmax(float &s, int &w) {
+    argmax_dpp_step<0x111, 0xf>(s, w);  // row_shr:1
+    argmax_dpp_step<0x112, 0xf>(s, w);  // row_shr:2
+    argmax_dpp_step<0x114, 0xf>(s, w);  // row_shr:4
+    argmax_dpp_step<0x118, 0xf>(s, w);  // row_shr:8
+    argmax_dpp_step<0x142, 0xa>(s, w);  // row_bcast:15 into rows 1 and 3
+    argmax_dpp_step<0x143, 0xc>(s, w);  // row_bcast:31 into rows 2 and 3
+    s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
+    w = __builtin_amdgcn_readlane(w, 63);
 }
 
 // ---- 2. best-first tree and controller, one wavefront per sequence
@@ -241,30 +274,46 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
 // offer (score desc, source asc with the context as -1) becomes node n. Node n's outputs
 // are kept in lane n's output registers (which do not alias the context's state in
 // lane 63).
-__global__ __launch_bounds__(64) void build_kernel(
+__global__ __launch_bounds__(256) void build_kernel(
     const uint2 *__restrict__ lists, const float *__restrict__ cost, float l_ar, int D, int S,
     int n_max, int fixed, int32_t *__restrict__ n_nodes, int32_t *__restrict__ par_out,
     int32_t *__restrict__ tok_out, float *__restrict__ rho_out, float *__restrict__ speedup) {
     __shared__ float s_val[kMaxDepth][kTopK];
     __shared__ int s_tok[kMaxDepth][kTopK];
     __shared__ uint32_t s_key[kMaxDepth][kTopK];
-    const int lane = lane_id();
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int b = blockIdx.x;
 
-    for (int d = 0; d < D; ++d) {
+    // per-position candidate lists: wavefront w merges positions w, w + 4, ..., loading
+    // up to 8 slice lists at a time
+    constexpr int kBatch = 8;
+    for (int d = wave; d < D; d += 4) {
         const uint2 *l0 = lists + ((size_t)b * D + d) * S * kTopK;
-        uint2 e = l0[lane];
-        uint32_t k = e.x;
-        int i = (int)e.y;
-        for (int s = 1; s < S; ++s) {
-            const uint2 x = l0[(size_t)s * kTopK + lane];
-            wave_merge64(k, i, x.x, (int)x.y);
+        uint32_t k = 0u;
+        int i = 0x7fffffff;
+        for (int s0 = 0; s0 < S; s0 += kBatch) {
+            uint2 x[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                x[u] = s0 + u < S ? l0[(size_t)(s0 + u) * kTopK + lane] : make_uint2(0u, 0x7fffffffu);
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (s0 + u == 0) {
+                    k = x[u].x;
+                    i = (int)x[u].y;
+                } else if (s0 + u < S) {
+                    wave_merge64(k, i, x[u].x, (int)x[u].y);
+                }
+            }
         }
         s_key[d][lane] = k;
         s_val[d][lane] = key2f(k);
         s_tok[d][lane] = i;
     }
     __syncthreads();
+    if (wave != 0) return;
+    // C(N) for N = lane + 1
+    const float c_lane = (cost != nullptr && lane < n_max) ? cost[lane] : 1.f;
 
     // source state (lane 63: the context) and node outputs
     int src_depth = 0, src_rank = 0;
@@ -281,18 +330,11 @@ __global__ __launch_bounds__(64) void build_kernel(
         if (sc < 0.f) who = 0x7fffffff;
         float bs = sc;
         int bw = who;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ps = __shfl_xor(bs, off, 64);
-            const int pw = __shfl_xor(bw, off, 64);
-            if (ps > bs || (ps == bs && pw < bw)) {
-                bs = ps;
-                bw = pw;
-            }
-        }
+        wave_argmax(bs, bw);
         if (bs < 0.f) break;  // no source offers a child (wave-uniform)
         const int wl = bw < 0 ? 63 : bw;  // the winning source's lane
-        const int wd = __shfl(src_depth, wl, 64), wr = __shfl(src_rank, wl, 64);
+        const int wd = __builtin_amdgcn_readlane(src_depth, wl);
+        const int wr = __builtin_amdgcn_readlane(src_rank, wl);
         if (lane == wl) ++src_rank;
         if (lane == n) {
             o_par = bw < 0 ? -1 : bw;
@@ -314,8 +356,9 @@ __global__ __launch_bounds__(64) void build_kernel(
         float A = 0.f, s_prev = 0.f;
         bool stopped = false;
         for (int N = 1; N <= built; ++N) {
-            A = __fadd_rn(A, __shfl(o_rho, N - 1, 64));
-            const float sN = __fdiv_rn(__fmul_rn(A, l_ar), cost[N - 1]);
+            A = __fadd_rn(A, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(o_rho), N - 1)));
+            const float cN = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c_lane), N - 1));
+            const float sN = __fdiv_rn(__fmul_rn(A, l_ar), cN);
             if (N > 1 && !fixed && sN < s_prev) {
                 keep = N - 1;
                 stopped = true;
@@ -363,15 +406,21 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
     int off = s_part[t] - sum;
     for (int b = b0; b < b1; ++b) {
         node_offsets[b] = off;
-        const int n = n_nodes[b];
-        for (int j = 0; j < n; ++j) {
-            parent[off + j] = par_in[(size_t)b * n_max + j];
-            token[off + j] = tok_in[(size_t)b * n_max + j];
-            if (rho) rho[off + j] = rho_in[(size_t)b * n_max + j];
-        }
-        off += n;
+        off += n_nodes[b];
     }
     if (t == kPackThreads - 1) node_offsets[B] = s_part[t];
+    __syncthreads();  // node_offsets written by this workgroup, read back below
+    // every (sequence, node) slot in parallel
+    const int total = B * n_max;
+    for (int x = t; x < total; x += kPackThreads) {
+        const int b = x / n_max, j = x - b * n_max;
+        if (j < n_nodes[b]) {
+            const int o = node_offsets[b] + j;
+            parent[o] = par_in[x];
+            token[o] = tok_in[x];
+            if (rho) rho[o] = rho_in[x];
+        }
+    }
 }
 
 // ---- host side
@@ -421,7 +470,7 @@ hipError_t launch_build_tree(const float *marginals, const float *cost, float l_
         topk_slice_kernel<4><<<dim3(rows), dim3(kBuildThreads), 0, stream>>>(marginals, lists, d.vocab, L.S);
     else
         topk_slice_kernel<1><<<dim3(rows), dim3(kBuildThreads), 0, stream>>>(marginals, lists, d.vocab, L.S);
-    build_kernel<<<dim3((unsigned)d.batch), dim3(64), 0, stream>>>(
+    build_kernel<<<dim3((unsigned)d.batch), dim3(256), 0, stream>>>(
         lists, cost, l_ar, d.depth, L.S, d.n_max, (d.flags & BOLE_BUILD_FIXED_BUDGET) ? 1 : 0,
         nn, par, tok, rh, speedup);
     pack_kernel<<<dim3(1), dim3(kPackThreads), 0, stream>>>(nn, par, tok, rh, d.batch, d.n_max,
