@@ -1,0 +1,133 @@
+"""Tree acceptance: which draft nodes the target model accepts, and its next token.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke entry and the benchmark's CPU-baseline leg
+are its only callers; the GPU library never imports, loads or calls it.
+
+It follows the LLM Primer chapter 9 walkthrough, section 9.1: the target scores every
+drafted position in one pass, the longest prefix it agrees with is accepted, and at the
+first disagreement the target's own choice is committed. With sampling, a token x drafted
+from q is accepted with probability min(1, p(x) / q(x)); otherwise the token comes from
+the normalised residual (p - q)+. That keeps the output distributed exactly as the
+target's.
+
+On a tree (the reading taken where the pages are silent):
+  - the walk starts at the verified context and descends one accepted node at a time;
+  - greedy (temperature 0): the target's choice at a node is its argmax (lowest token id
+    on ties); the child carrying that token is accepted (the lowest-index one if several),
+    and when no child carries it, that token is the next (bonus) token;
+  - sampling: the children of the current node are tested in index order, each against
+    the residual distributions the children rejected before it left: x is accepted when
+    u * q_res(x) < p_res(x); on a rejection p_res <- (p_res - q_res)+ renormalised, and x
+    leaves q_res, which is renormalised (siblings are distinct tokens, drawn without
+    replacement). When every child is rejected, or the node has none, the bonus token is
+    drawn from p_res by inverse CDF with the tree's bonus uniform. On a chain this is the
+    section 9.1 rule exactly.
+  - at most max_path nodes are accepted; the bonus is then drawn at the last one.
+
+Arithmetic: residuals are fp64, kept unnormalised with their totals Zp, Zq: the test is
+u * rq(x) * Zp < rp(x) * Zq; a rejection sets rp <- max(rp / Zp - rq / Zq, 0),
+Zp <- sum(rp), Zq <- Zq - rq(x), rq(x) <- 0. At a node reached fresh rp = p, rq = q (the
+fp32 rows, widened) and Zp = Zq = 1. The bonus is the smallest y with
+sum_{y' <= y} rp(y') > u * sum(rp) (the last y if rounding leaves none). Each call also
+returns the smallest relative decision margin it met, so that a test can tell a genuine
+mismatch from a comparison that a different summation order may flip.
+"""
+import numpy as np
+
+GREEDY, SAMPLE = 0, 1
+# per-tree status codes (same values as the C header's BOLE_TREE_*)
+TREE_OK, TREE_BAD_SIZE, TREE_BAD_PARENT, TREE_BAD_TOKEN = 0, 1, 2, 4
+
+
+def _rel(a, b):
+    m = max(abs(a), abs(b))
+    return abs(a - b) / m if m > 0 else 0.0
+
+
+def accept_tree(p_ctx, q_ctx, p_node, q_node, parent, token, lo, n, u_node, u_bonus, mode,
+                max_path):
+    """One tree: rows lo .. lo + n - 1 of the packed node arrays. p_ctx, q_ctx are the
+    rows at the verified context; p_node[lo + i], q_node[lo + i] the rows after node i.
+    Returns (accepted tree-local indices, bonus token, smallest relative margin)."""
+    kids = {-1: []}
+    for i in range(n):
+        kids.setdefault(i, [])
+        kids.setdefault(int(parent[lo + i]), []).append(i)
+    path, cur, margin = [], -1, np.inf
+    while True:
+        prow = np.asarray(p_ctx if cur < 0 else p_node[lo + cur], np.float64)
+        room = len(path) < max_path
+        if mode == GREEDY:
+            y = int(np.argmax(prow))
+            hit = [c for c in kids[cur] if int(token[lo + c]) == y]
+            if hit and room:
+                path.append(hit[0])
+                cur = hit[0]
+                continue
+            return path, y, margin
+        rp = prow.copy()
+        rq = np.asarray(q_ctx if cur < 0 else q_node[lo + cur], np.float64).copy()
+        Zp = Zq = 1.0
+        fresh, nxt = True, None
+        for c in (kids[cur] if room else []):
+            x = int(token[lo + c])
+            lhs = float(u_node[lo + c]) * rq[x] * Zp
+            rhs = rp[x] * Zq
+            margin = min(margin, _rel(lhs, rhs))
+            if lhs < rhs:
+                nxt = c
+                break
+            rp = np.maximum(rp / Zp - rq / Zq, 0.0)
+            Zp = float(rp.sum())
+            Zq = Zq - rq[x]
+            rq[x] = 0.0
+            fresh = False
+        if nxt is not None:
+            path.append(nxt)
+            cur = nxt
+            continue
+        total = float(rp.sum()) if fresh else Zp
+        t = float(u_bonus) * total
+        cs = np.cumsum(rp)
+        y = min(int(np.searchsorted(cs, t, side="right")), rp.shape[0] - 1)
+        if t > 0:
+            margin = min(margin, float(np.abs(cs - t).min()) / t)
+        return path, y, margin
+
+
+def accept_trees(p_ctx, q_ctx, p_node, q_node, parent, token, node_offsets, u_node, u_bonus,
+                 mode, max_path):
+    """A packed batch. Returns dict of accepted_idx [B][max_path] (-1 padded),
+    accepted_len [B], bonus [B], status [B], margin [B]. A tree whose offsets are out of
+    order or outside [0, T] or hold more than 64 nodes gets BAD_SIZE, a parent outside
+    [-1, i) BAD_PARENT, a token outside [0, V) BAD_TOKEN; such trees accept nothing and
+    get bonus -1."""
+    B = len(node_offsets) - 1
+    T = len(parent)
+    V = np.asarray(p_ctx).shape[-1]
+    idx = np.full((B, max_path), -1, np.int32)
+    ln = np.zeros(B, np.int32)
+    bonus = np.full(B, -1, np.int32)
+    status = np.zeros(B, np.int32)
+    margin = np.full(B, np.inf)
+    for b in range(B):
+        lo, hi = int(node_offsets[b]), int(node_offsets[b + 1])
+        if lo < 0 or hi < lo or hi > T or hi - lo > 64:
+            status[b] = TREE_BAD_SIZE
+            continue
+        n = hi - lo
+        if any(not (-1 <= int(parent[lo + i]) < i) for i in range(n)):
+            status[b] = TREE_BAD_PARENT
+            continue
+        if any(not (0 <= int(token[lo + i]) < V) for i in range(n)):
+            status[b] = TREE_BAD_TOKEN
+            continue
+        path, y, m = accept_tree(p_ctx[b], q_ctx[b] if q_ctx is not None else None, p_node,
+                                 q_node, parent, token, lo, n, u_node, u_bonus[b], mode,
+                                 max_path)
+        idx[b, :len(path)] = path
+        ln[b] = len(path)
+        bonus[b] = y
+        margin[b] = m
+    return {"accepted_idx": idx, "accepted_len": ln, "bonus": bonus, "status": status,
+            "margin": margin}
