@@ -78,8 +78,9 @@ enum {
     BOLE_TREE_BAD_SIZE = 1,   /* offsets unordered, outside [0, T], or more than 64 nodes
                                  (32 under BOLE_FLAG_TREES_LE_32) */
     BOLE_TREE_BAD_PARENT = 2, /* some node i has parent[i] < -1 or parent[i] >= i */
-    BOLE_TREE_BAD_PATH = 3    /* commit: length outside [0, max_path], an index outside
+    BOLE_TREE_BAD_PATH = 3,   /* commit: length outside [0, max_path], an index outside
                                  the tree, or not a chain that starts at a root */
+    BOLE_TREE_BAD_TOKEN = 4   /* accept: a node's token outside [0, vocab) */
 };
 
 typedef enum { BOLE_DTYPE_BF16 = 0, BOLE_DTYPE_F32 = 1 } bole_dtype_t;
@@ -338,6 +339,59 @@ BOLE_API bole_status_t bole_build_tree(const float *marginals, const float *cost
                                void *workspace, size_t workspace_bytes,
                                const bole_build_dims_t *dims, int32_t *node_offsets,
                                int32_t *parent, int32_t *token, float *rho, float *speedup,
+                               bole_stream_t stream);
+
+/*
+ * Tree acceptance: the LLM Primer chapter 9 walkthrough, section 9.1. The target model
+ * scores every drafted node in one pass; the walk from the verified context accepts the
+ * longest path the target agrees with, and the target's own next token at the first
+ * disagreement (the bonus token) is returned beside it.
+ *  - BOLE_ACCEPT_GREEDY: at each node the target's choice is the argmax of its row
+ *    (lowest token id on ties). The child carrying it is accepted (the lowest-index
+ *    child if several); when none does, that token is the bonus.
+ *  - BOLE_ACCEPT_SAMPLE: a drafted token x is accepted with probability
+ *    min(1, p(x) / q(x)), else the bonus is drawn from the normalised residual (p - q)+,
+ *    which keeps the output distributed as the target's. Siblings (distinct tokens,
+ *    drafted without replacement) are tested in index order, each against the residuals
+ *    the rejected ones before it left: p_res <- (p_res - q_res)+ renormalised, and the
+ *    rejected token leaves q_res, renormalised. x is accepted when
+ *    u_node[x's node] * q_res(x) < p_res(x). The bonus is the smallest y whose
+ *    cumulative p_res exceeds u_bonus[b] (inverse CDF). Residuals are fp64; draws that
+ *    fall within rounding of a boundary may differ from a different summation order.
+ * At most max_path nodes are accepted; the bonus is then taken at the last of them.
+ *
+ * Inputs (device, fp32 probability rows, each finite, >= 0 and summing to 1):
+ *   p_ctx [B][V], q_ctx [B][V]    target / draft distribution at the verified context
+ *   p_node [T][V], q_node [T][V]  the same after each draft node (q: the distribution
+ *                                 its children were drafted from)
+ *   parent [T], token [T], node_offsets [B + 1]   the packed trees (as verify takes them)
+ *   u_node [T], u_bonus [B]       uniforms in [0, 1) (sampling)
+ *   q_ctx, q_node, u_node, u_bonus may be NULL for greedy.
+ *   workspace: bole_tree_accept_workspace_size(dims) bytes, 8-byte aligned (0 for greedy).
+ * Outputs (device): accepted_idx [B][max_path] (tree-local, root first, -1 after the
+ * path), accepted_len [B], bonus [B] (-1 for a bad tree), tree_status [B] (may be NULL:
+ * BOLE_TREE_BAD_SIZE, BAD_PARENT or BAD_TOKEN; a bad tree accepts nothing). accepted_idx
+ * and accepted_len feed bole_commit_path directly.
+ */
+enum { BOLE_ACCEPT_GREEDY = 0, BOLE_ACCEPT_SAMPLE = 1 };
+
+typedef struct {
+    int32_t batch;        /* B >= 0 */
+    int32_t total_nodes;  /* T >= 0 */
+    int32_t vocab;        /* V >= 1 */
+    int32_t max_path;     /* 1..64, row stride of accepted_idx */
+    int32_t mode;         /* BOLE_ACCEPT_* */
+} bole_accept_dims_t;
+
+BOLE_API size_t bole_tree_accept_workspace_size(const bole_accept_dims_t *dims);
+
+BOLE_API bole_status_t bole_tree_accept(const float *p_ctx, const float *p_node,
+                               const float *q_ctx, const float *q_node,
+                               const int32_t *parent, const int32_t *token,
+                               const int32_t *node_offsets, const float *u_node,
+                               const float *u_bonus, void *workspace, size_t workspace_bytes,
+                               const bole_accept_dims_t *dims, int32_t *accepted_idx,
+                               int32_t *accepted_len, int32_t *bonus, int32_t *tree_status,
                                bole_stream_t stream);
 
 #ifdef __cplusplus

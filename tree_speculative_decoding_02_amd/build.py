@@ -12,7 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "bole")
 LIB = os.path.join(HERE, "libbole.so")
 SOURCES = ["bole_api.hip", "topology.hip", "verify_generic.hip", "verify_mfma.hip", "verify_vec.hip",
-           "verify_naive.hip", "commit.hip", "tree_build.hip"]
+           "verify_naive.hip", "commit.hip", "tree_build.hip",
+           "tree_accept.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions stay off: the compiler would otherwise form them from
