@@ -84,6 +84,8 @@ def parse():
                          "as the stacked forms, so leave it off in profiled runs)")
     ap.add_argument("--no-builder", action="store_true",
                     help="skip timing the draft-tree builder")
+    ap.add_argument("--no-accept", action="store_true",
+                    help="skip timing tree acceptance")
     ap.add_argument("--no-naive", action="store_true",
                     help="skip timing the naive serial-walk baseline")
     ap.add_argument("--config-sweep", action="store_true",
@@ -300,6 +302,62 @@ def main():
             "what": "bole_build_tree: top-64 per position, best-first tree, budget controller "
                     "and packing for 64 sequences x 8 positions x 128256 tokens (3 launches)"}
         del marg
+
+    # tree acceptance on the same trees: target and draft rows over a 128256-token
+    # vocabulary for the context and every node (synthetic, generated on the GPU: draft
+    # logits N(0, 2), target = draft + N(0, 1) with the first child's token raised by 8
+    # at 70 % of the nodes; each node's children carry the draft row's top tokens)
+    if not args.no_accept:
+        Va = 128256
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(2025)
+        T = wl.total_nodes
+        zq = torch.randn((T + wl.batch, Va), generator=gen, device=dev) * 2.0
+        top = torch.topk(zq, 64, dim=1).indices.cpu().numpy()
+        par_np, offs_np = wl.parent, wl.node_offsets
+        tok_np = np.zeros(T, np.int32)
+        boost = torch.zeros_like(zq)
+        rng = np.random.default_rng(2025)
+        for b in range(wl.batch):
+            lo, hi = int(offs_np[b]), int(offs_np[b + 1])
+            for cur in [-1] + list(range(hi - lo)):
+                kids = [i for i in range(hi - lo) if par_np[lo + i] == cur]
+                row = T + b if cur < 0 else lo + cur
+                for r, c in enumerate(kids):
+                    tok_np[lo + c] = top[row, r]
+                if kids and rng.random() < 0.7:
+                    boost[row, int(tok_np[lo + kids[0]])] = 8.0
+        zp = zq + torch.randn(zq.shape, generator=gen, device=dev) + boost
+        del boost
+        pr, qr = torch.softmax(zp, dim=1), torch.softmax(zq, dim=1)
+        del zp, zq
+        p_node, p_ctx = pr[:T].contiguous(), pr[T:].contiguous()
+        q_node, q_ctx = qr[:T].contiguous(), qr[T:].contiguous()
+        del pr, qr
+        tok = torch.from_numpy(tok_np).to(dev)
+        u_node = torch.rand(T, generator=gen, device=dev)
+        u_bonus = torch.rand(wl.batch, generator=gen, device=dev)
+        acc = {}
+        for mode in ("greedy", "sample"):
+            f = bole.bind_tree_accept(p_ctx, p_node, parent, tok, offs, wl.max_path,
+                                      sample=mode == "sample", q_ctx=q_ctx, q_node=q_node,
+                                      u_node=u_node, u_bonus=u_bonus, stream=stream)
+            _, spans, _ = timed([[f]], args.steps, args.warmup)
+            torch.cuda.synchronize()
+            lens = f.out["accepted_len"][:wl.batch].cpu().numpy()
+            us = 1e3 * float(np.mean(spans[:, 0]))
+            rec = {"avg_us_per_call": us, "median_us_per_call": 1e3 * float(np.median(spans[:, 0])),
+                   "mean_accepted_len": float(lens.mean())}
+            if mode == "greedy":
+                # the walk reads one target row per visited node (the path and its end)
+                nb = int((lens + 1).sum()) * Va * 4
+                rec.update({"bytes_per_call": nb, "GB_s": nb / (us * 1e3),
+                            "frac_hbm_peak": nb / (us * 1e3) / HBM_PEAK_GBS})
+            acc[mode] = rec
+        acc["what"] = ("bole_tree_accept on the benchmark's 64 trees of 32 nodes, target and "
+                       "draft rows over 128256 tokens")
+        result["tree_accept"] = acc
+        del p_node, p_ctx, q_node, q_ctx
 
     # the naive serial walk on layer 0 (one materialised state per node): the baseline the
     # closed form is measured against, timed after the benchmark proper

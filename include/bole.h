@@ -366,8 +366,8 @@ BOLE_API bole_status_t bole_build_tree(const float *marginals, const float *cost
  *                                 its children were drafted from)
  *   parent [T], token [T], node_offsets [B + 1]   the packed trees (as verify takes them)
  *   u_node [T], u_bonus [B]       uniforms in [0, 1) (sampling)
- *   q_ctx, q_node, u_node, u_bonus may be NULL for greedy.
- *   workspace: bole_tree_accept_workspace_size(dims) bytes, 8-byte aligned (0 for greedy).
+ *   q_ctx, q_node, u_node, u_bonus may be NULL for greedy. No workspace: the residuals
+ *   are recomputed from the rows (same fp64 operations, same order) instead of stored.
  * Outputs (device): accepted_idx [B][max_path] (tree-local, root first, -1 after the
  * path), accepted_len [B], bonus [B] (-1 for a bad tree), tree_status [B] (may be NULL:
  * BOLE_TREE_BAD_SIZE, BAD_PARENT or BAD_TOKEN; a bad tree accepts nothing). accepted_idx
@@ -383,14 +383,12 @@ typedef struct {
     int32_t mode;         /* BOLE_ACCEPT_* */
 } bole_accept_dims_t;
 
-BOLE_API size_t bole_tree_accept_workspace_size(const bole_accept_dims_t *dims);
-
 BOLE_API bole_status_t bole_tree_accept(const float *p_ctx, const float *p_node,
                                const float *q_ctx, const float *q_node,
                                const int32_t *parent, const int32_t *token,
                                const int32_t *node_offsets, const float *u_node,
-                               const float *u_bonus, void *workspace, size_t workspace_bytes,
-                               const bole_accept_dims_t *dims, int32_t *accepted_idx,
+                               const float *u_bonus, const bole_accept_dims_t *dims,
+                               int32_t *accepted_idx,
                                int32_t *accepted_len, int32_t *bonus, int32_t *tree_status,
                                bole_stream_t stream);
 

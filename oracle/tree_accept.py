@@ -24,13 +24,20 @@ On a tree (the reading taken where the pages are silent):
     section 9.1 rule exactly.
   - at most max_path nodes are accepted; the bonus is then drawn at the last one.
 
-Arithmetic: residuals are fp64, kept unnormalised with their totals Zp, Zq: the test is
-u * rq(x) * Zp < rp(x) * Zq; a rejection sets rp <- max(rp / Zp - rq / Zq, 0),
-Zp <- sum(rp), Zq <- Zq - rq(x), rq(x) <- 0. At a node reached fresh rp = p, rq = q (the
-fp32 rows, widened) and Zp = Zq = 1. The bonus is the smallest y with
-sum_{y' <= y} rp(y') > u * sum(rp) (the last y if rounding leaves none). Each call also
-returns the smallest relative decision margin it met, so that a test can tell a genuine
-mismatch from a comparison that a different summation order may flip.
+Arithmetic (fp64). The residuals are kept unnormalised with their totals Zp, Zq:
+p_res = rp / Zp, q_res = rq / Zq; the test is u * rq(x) * Zp < rp(x) * Zq. A rejection of
+x replaces rp by max(rp / Zp - rq / Zq, 0) and removes x from rq. Because a clamp at 0
+never releases (each step subtracts a non-negative amount), after k rejections
+    rp(y) = max(p(y) * A - q(y) * C, 0),     rq(y) = q(y) (0 for rejected tokens),
+where a fresh node starts from A = 1, C = 0, Zp = Zq = 1, and each rejection of x sets
+A <- A / Zp, C <- C / Zp + 1 / Zq, Zq <- Zq - q(x), Zp <- sum_y rp(y) (the new rp). A
+rejected token's value is <= 0 there already, so the same formula holds for it. This is
+exactly the step-by-step residual in real arithmetic, and it is how both sides evaluate
+it: the products and the difference are separately rounded fp64 operations. The bonus
+is the smallest y with sum_{y' <= y} rp(y') > u * total, total = sum(p) at a fresh node,
+else Zp (the last y if rounding leaves none). Each call also returns the smallest
+relative decision margin it met, so that a test can tell a genuine mismatch from a
+comparison that a different summation order may flip.
 """
 import numpy as np
 
@@ -65,22 +72,23 @@ def accept_tree(p_ctx, q_ctx, p_node, q_node, parent, token, lo, n, u_node, u_bo
                 cur = hit[0]
                 continue
             return path, y, margin
-        rp = prow.copy()
-        rq = np.asarray(q_ctx if cur < 0 else q_node[lo + cur], np.float64).copy()
-        Zp = Zq = 1.0
+        qrow = np.asarray(q_ctx if cur < 0 else q_node[lo + cur], np.float64)
+        A, C, Zp, Zq = 1.0, 0.0, 1.0, 1.0
+        rp = prow
         fresh, nxt = True, None
         for c in (kids[cur] if room else []):
             x = int(token[lo + c])
-            lhs = float(u_node[lo + c]) * rq[x] * Zp
-            rhs = rp[x] * Zq
+            rpx = max(prow[x] * A - qrow[x] * C, 0.0)
+            lhs = float(u_node[lo + c]) * qrow[x] * Zp
+            rhs = rpx * Zq
             margin = min(margin, _rel(lhs, rhs))
             if lhs < rhs:
                 nxt = c
                 break
-            rp = np.maximum(rp / Zp - rq / Zq, 0.0)
+            A, C = A / Zp, C / Zp + 1.0 / Zq
+            Zq = Zq - qrow[x]
+            rp = np.maximum(prow * A - qrow * C, 0.0)
             Zp = float(rp.sum())
-            Zq = Zq - rq[x]
-            rq[x] = 0.0
             fresh = False
         if nxt is not None:
             path.append(nxt)

@@ -168,22 +168,14 @@ def test_build_tree_checked_without_launch():
 def test_tree_accept_checked_without_launch():
     L = bole.lib
     AD = bole.bole_accept_dims_t
-    for bad in (AD(4, 10, 0, 8, 0), AD(4, 10, 100, 0, 0), AD(4, 10, 100, 65, 0),
-                AD(4, 10, 100, 8, 2), AD(-1, 10, 100, 8, 0)):
-        assert L.bole_tree_accept_workspace_size(ctypes.byref(bad)) == 0
-    assert L.bole_tree_accept_workspace_size(ctypes.byref(AD(4, 10, 100, 8, 0))) == 0
-    need = L.bole_tree_accept_workspace_size(ctypes.byref(AD(4, 10, 100, 8, 1)))
-    assert need == 2 * 4 * 100 * 8
     P = 0x1000
 
-    def call(d, ws=P, wsb=need, q=P):
-        return L.bole_tree_accept(P, P, q, q, P, P, P, P, P, ws, wsb, ctypes.byref(d), P, P, P,
-                                  None, None)
-    s = AD(4, 10, 100, 8, 1)
-    assert call(s, wsb=need - 8) == bole.BOLE_ERR_INVALID_VALUE
-    assert call(s, ws=P + 4) == bole.BOLE_ERR_INVALID_VALUE
-    assert call(s, q=None) == bole.BOLE_ERR_INVALID_VALUE
-    assert call(AD(4, 10, 100, 65, 0)) == bole.BOLE_ERR_INVALID_VALUE
+    def call(d, q=P):
+        return L.bole_tree_accept(P, P, q, q, P, P, P, P, P, ctypes.byref(d), P, P, P, None, None)
+    for bad in (AD(4, 10, 0, 8, 0), AD(4, 10, 100, 0, 0), AD(4, 10, 100, 65, 0),
+                AD(4, 10, 100, 8, 2), AD(-1, 10, 100, 8, 0)):
+        assert call(bad) == bole.BOLE_ERR_INVALID_VALUE
+    assert call(AD(4, 10, 100, 8, 1), q=None) == bole.BOLE_ERR_INVALID_VALUE
     assert call(AD(0, 10, 100, 8, 1)) == bole.BOLE_OK
 
 

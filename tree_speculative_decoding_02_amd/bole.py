@@ -25,7 +25,7 @@ EXPORTED = ("bole_max_tree_nodes", "bole_status_string", "bole_check_dims", "bol
             "bole_tree_verify_lazy_commit", "bole_tree_verify_layers", "bole_commit_path_layers",
             "bole_tree_verify_lazy_commit_layers", "bole_tree_verify_naive", "bole_commit_path",
             "bole_tree_prepare", "bole_build_tree_workspace_size", "bole_build_tree",
-            "bole_tree_accept_workspace_size", "bole_tree_accept")
+            "bole_tree_accept")
 BOLE_ACCEPT_GREEDY, BOLE_ACCEPT_SAMPLE = 0, 1
 BOLE_BUILD_FIXED_BUDGET = 1
 
@@ -94,11 +94,8 @@ def _load():
     lib.bole_build_tree.restype = ctypes.c_int
     lib.bole_build_tree.argtypes = [P, P, ctypes.c_float, P, ctypes.c_size_t, BD, P, P, P, P, P, P]
     AD = ctypes.POINTER(bole_accept_dims_t)
-    lib.bole_tree_accept_workspace_size.restype = ctypes.c_size_t
-    lib.bole_tree_accept_workspace_size.argtypes = [AD]
     lib.bole_tree_accept.restype = ctypes.c_int
-    lib.bole_tree_accept.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, AD, P, P, P, P,
-                                     P]
+    lib.bole_tree_accept.argtypes = [P, P, P, P, P, P, P, P, P, AD, P, P, P, P, P]
     lib.bole_tree_verify_naive.restype = ctypes.c_int
     lib.bole_tree_verify_naive.argtypes = [P, P, P, P, P, P, P, P, P, D, P, P]
     lib.bole_commit_path.restype = ctypes.c_int
@@ -600,7 +597,7 @@ def bind_build_tree(marginals, cost, l_ar=1.0, n_max=64, fixed=False, workspace=
 # ---- tree acceptance
 
 def _accept_call(p_ctx, p_node, parent, token, node_offsets, max_path, sample, q_ctx, q_node,
-                 u_node, u_bonus, workspace, out, stream):
+                 u_node, u_bonus, out, stream):
     _need(p_ctx, "p_ctx", torch.float32)
     dev = p_ctx.device
     if p_ctx.dim() != 2:
@@ -621,42 +618,35 @@ def _accept_call(p_ctx, p_node, parent, token, node_offsets, max_path, sample, q
             if tuple(t.shape) != shape:
                 raise ValueError(f"{name} must be {list(shape)}")
     dims = bole_accept_dims_t(B, T, V, max_path, BOLE_ACCEPT_SAMPLE if sample else BOLE_ACCEPT_GREEDY)
-    need = lib.bole_tree_accept_workspace_size(ctypes.byref(dims))
-    if sample and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if out is None:
         out = {"accepted_idx": torch.empty((max(B, 1), max_path), dtype=torch.int32, device=dev),
                "accepted_len": torch.empty(max(B, 1), dtype=torch.int32, device=dev),
                "bonus": torch.empty(max(B, 1), dtype=torch.int32, device=dev),
                "status": torch.empty(max(B, 1), dtype=torch.int32, device=dev)}
     args = (_ptr(p_ctx), _ptr(p_node), _ptr(q_ctx), _ptr(q_node), _ptr(parent), _ptr(token),
-            _ptr(node_offsets), _ptr(u_node), _ptr(u_bonus), _ptr(workspace), wsb,
-            ctypes.byref(dims), _ptr(out["accepted_idx"]), _ptr(out["accepted_len"]),
+            _ptr(node_offsets), _ptr(u_node), _ptr(u_bonus), ctypes.byref(dims), _ptr(out["accepted_idx"]), _ptr(out["accepted_len"]),
             _ptr(out["bonus"]), _ptr(out["status"]), _stream(stream))
-    keep = (p_ctx, p_node, parent, token, node_offsets, q_ctx, q_node, u_node, u_bonus,
-            workspace, out, dims)
+    keep = (p_ctx, p_node, parent, token, node_offsets, q_ctx, q_node, u_node, u_bonus, out,
+            dims)
     return args, out, keep
 
 
 def bole_tree_accept(p_ctx, p_node, parent, token, node_offsets, max_path, sample=False,
-                     q_ctx=None, q_node=None, u_node=None, u_bonus=None, workspace=None,
-                     out=None, stream=None):
+                     q_ctx=None, q_node=None, u_node=None, u_bonus=None, out=None, stream=None):
     """Accepted path and bonus token per tree: greedy longest match against the target's
     argmax, or (sample=True) min(1, p/q) acceptance with residual resampling. Returns a
     dict of device tensors accepted_idx [B, max_path], accepted_len [B], bonus [B],
     status [B]."""
     args, out, _ = _accept_call(p_ctx, p_node, parent, token, node_offsets, max_path, sample,
-                                q_ctx, q_node, u_node, u_bonus, workspace, out, stream)
+                                q_ctx, q_node, u_node, u_bonus, out, stream)
     _check(lib.bole_tree_accept(*args), "bole_tree_accept")
     return out
 
 
 def bind_tree_accept(p_ctx, p_node, parent, token, node_offsets, max_path, sample=False,
-                     q_ctx=None, q_node=None, u_node=None, u_bonus=None, workspace=None,
-                     out=None, stream=None):
+                     q_ctx=None, q_node=None, u_node=None, u_bonus=None, out=None, stream=None):
     args, out, keep = _accept_call(p_ctx, p_node, parent, token, node_offsets, max_path, sample,
-                                   q_ctx, q_node, u_node, u_bonus, workspace, out, stream)
+                                   q_ctx, q_node, u_node, u_bonus, out, stream)
     bound = _Bound(lib.bole_tree_accept, "bole_tree_accept", args, keep)
     bound.out = out
     return bound

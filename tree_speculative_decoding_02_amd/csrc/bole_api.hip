@@ -321,16 +321,11 @@ static bool accept_dims_ok(const bole_accept_dims_t &d) {
            (d.mode == BOLE_ACCEPT_GREEDY || d.mode == BOLE_ACCEPT_SAMPLE);
 }
 
-size_t bole_tree_accept_workspace_size(const bole_accept_dims_t *dims) {
-    if (dims == nullptr || !accept_dims_ok(*dims)) return 0;
-    return bole::accept_workspace_bytes(*dims);
-}
-
 bole_status_t bole_tree_accept(const float *p_ctx, const float *p_node, const float *q_ctx,
                                const float *q_node, const int32_t *parent, const int32_t *token,
                                const int32_t *node_offsets, const float *u_node,
-                               const float *u_bonus, void *workspace, size_t workspace_bytes,
-                               const bole_accept_dims_t *dims, int32_t *accepted_idx,
+                               const float *u_bonus, const bole_accept_dims_t *dims,
+                               int32_t *accepted_idx,
                                int32_t *accepted_len, int32_t *bonus, int32_t *tree_status,
                                bole_stream_t stream) {
     if (dims == nullptr || !accept_dims_ok(*dims)) return BOLE_ERR_INVALID_VALUE;
@@ -345,15 +340,12 @@ bole_status_t bole_tree_accept(const float *p_ctx, const float *p_node, const fl
         if (q_ctx == nullptr || u_bonus == nullptr ||
             (d.total_nodes > 0 && (q_node == nullptr || u_node == nullptr)))
             return BOLE_ERR_INVALID_VALUE;
-        if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 8 != 0 ||
-            workspace_bytes < bole::accept_workspace_bytes(d))
-            return BOLE_ERR_INVALID_VALUE;
     }
     // row offsets (T + B rows of V) fit the kernels' 64-bit element offsets
     if ((uint64_t)(d.total_nodes + (int64_t)d.batch) * (uint64_t)d.vocab >= (1ull << 62))
         return BOLE_ERR_UNSUPPORTED;
     return from_hip(bole::launch_tree_accept(p_ctx, p_node, q_ctx, q_node, parent, token,
-                                             node_offsets, u_node, u_bonus, workspace, d,
+                                             node_offsets, u_node, u_bonus, d,
                                              accepted_idx, accepted_len, bonus, tree_status,
                                              reinterpret_cast<hipStream_t>(stream)));
 }

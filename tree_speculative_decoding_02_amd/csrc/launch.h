@@ -80,12 +80,11 @@ hipError_t launch_build_tree(const float *marginals, const float *cost, float l_
                              hipStream_t stream);
 
 // Tree acceptance (tree_accept.hip).
-size_t accept_workspace_bytes(const bole_accept_dims_t &d);
 hipError_t launch_tree_accept(const float *p_ctx, const float *p_node, const float *q_ctx,
                               const float *q_node, const int32_t *parent, const int32_t *token,
                               const int32_t *node_offsets, const float *u_node,
-                              const float *u_bonus, void *workspace,
-                              const bole_accept_dims_t &d, int32_t *accepted_idx,
+                              const float *u_bonus, const bole_accept_dims_t &d,
+                              int32_t *accepted_idx,
                               int32_t *accepted_len, int32_t *bonus, int32_t *tree_status,
                               hipStream_t stream);
 

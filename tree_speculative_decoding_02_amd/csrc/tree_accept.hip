@@ -9,24 +9,71 @@
 // thread.
 //  - greedy: the target's argmax (lowest id on ties) picks the child, else is the bonus;
 //  - sampling: children in index order, each tested against the residuals left by the
-//    rejected ones before it: accept x when u * rq(x) * Zp < rp(x) * Zq; a rejection
-//    writes rp <- max(rp / Zp - rq / Zq, 0) (fp64, into the workspace) with Zp its sum,
-//    Zq <- Zq - rq(x), rq(x) <- 0. The bonus is drawn from rp by inverse CDF.
+//    rejected ones before it. With rp = p_res * Zp and rq = q_res * Zq unnormalised, x is
+//    accepted when u * rq(x) * Zp < rp(x) * Zq. The residuals are never stored: after k
+//    rejections rp(y) = max(p(y) A - q(y) C, 0) (a clamp at 0 never releases, so the
+//    step-by-step residual has this closed form), with A, C, Zq updated per rejection of
+//    x as A <- A / Zp, C <- C / Zp + 1 / Zq, Zq <- Zq - q(x), and Zp the sum of the new
+//    rp: one pass over the node's two fp32 rows. The bonus is drawn from rp by inverse
+//    CDF. fp64 throughout, products and differences separately rounded.
 #include "bole_device.h"
 #include "launch.h"
 
 namespace bole {
 
-constexpr int kAcceptThreads = 256;
+constexpr int kAcceptThreads = 1024;
+constexpr int kAcceptBatch = 16;  // loads in flight per thread in a pass
 constexpr int kAcceptWaves = kAcceptThreads / 64;
 
 struct AcceptArgs {
     const float *p_ctx, *p_node, *q_ctx, *q_node, *u_node, *u_bonus;
     const int32_t *parent, *token, *node_offsets;
-    double *rp_ws, *rq_ws;  // [B][V] each (sampling only)
     int32_t *accepted_idx, *accepted_len, *bonus, *tree_status;
     int B, T, V, max_path, mode;
+    bool vec;  // fp32 rows are 16-byte aligned (V % 4 == 0 and aligned bases)
 };
+
+// Calls f(y, value) for the elements of an fp32 row this thread owns, in increasing y.
+// Loads are issued kAcceptBatch at a time before any is used.
+template <typename F>
+__device__ __forceinline__ void row_pass(const float *row, int V, bool vec, F f) {
+    const int t = threadIdx.x;
+    if (vec) {
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        constexpr int step = 4 * kAcceptThreads;
+        for (int y0 = 4 * t; y0 < V; y0 += step * kAcceptBatch) {
+            f4 x[kAcceptBatch];
+#pragma unroll
+            for (int u = 0; u < kAcceptBatch; ++u) {
+                const int y = y0 + u * step;
+                x[u] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(row + min(y, V - 4)));
+            }
+#pragma unroll
+            for (int u = 0; u < kAcceptBatch; ++u) {
+                const int y = y0 + u * step;
+                if (y < V) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) f(y + c, x[u][c]);
+                }
+            }
+        }
+    } else {
+        for (int y0 = t; y0 < V; y0 += kAcceptThreads * kAcceptBatch) {
+            float x[kAcceptBatch];
+#pragma unroll
+            for (int u = 0; u < kAcceptBatch; ++u)
+                x[u] = row[min(y0 + u * kAcceptThreads, V - 1)];
+#pragma unroll
+            for (int u = 0; u < kAcceptBatch; ++u)
+                if (y0 + u * kAcceptThreads < V) f(y0 + u * kAcceptThreads, x[u]);
+        }
+    }
+}
+
+// rp(y) = max(p(y) A - q(y) C, 0), each product and the difference rounded on its own
+__device__ __forceinline__ double residual(float p, float q, double A, double C) {
+    return fmax(__dsub_rn(__dmul_rn((double)p, A), __dmul_rn((double)q, C)), 0.0);
+}
 
 __device__ __forceinline__ double block_sum_d(double x, double *s_red) {
 #pragma unroll
@@ -80,8 +127,6 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
         return;
     }
 
-    double *rp = a.rp_ws ? a.rp_ws + (size_t)b * V : nullptr;
-    double *rq = a.rq_ws ? a.rq_ws + (size_t)b * V : nullptr;
     int cur = -1, len = 0, bonus = -1;
     while (true) {
         const float *prow = cur < 0 ? a.p_ctx + (size_t)b * V : a.p_node + (size_t)(lo + cur) * V;
@@ -93,13 +138,12 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
             // ---- greedy: argmax of the target row
             float bv = -__builtin_huge_valf();
             int bi = 0x7fffffff;
-            for (int y = t; y < V; y += kAcceptThreads) {
-                const float x = prow[y];
+            row_pass(prow, V, a.vec, [&](int y, float x) {
                 if (x > bv) {  // y increases: a tie keeps the earlier id
                     bv = x;
                     bi = y;
                 }
-            }
+            });
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) {
                 const float pv = __shfl_xor(bv, off, 64);
@@ -145,49 +189,52 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
 
         // ---- sampling
         const float *qrow = cur < 0 ? a.q_ctx + (size_t)b * V : a.q_node + (size_t)(lo + cur) * V;
-        double Zp = 1.0, Zq = 1.0;
-        bool fresh = true;
+        double A = 1.0, C = 0.0, Zp = 1.0, Zq = 1.0;
+        int k = 0;  // rejections at this node
         int acc = -1;
         for (uint64_t m = room ? kids : 0ull; m; m &= m - 1) {
             const int c = __builtin_ctzll(m);
             const int x = s_tok[c];
             const double u = (double)a.u_node[lo + c];
-            // rp, rq of the previous rejection pass are visible after its barrier
-            const double rpx = fresh ? (double)prow[x] : rp[x];
-            const double rqx = fresh ? (double)qrow[x] : rq[x];
-            if (u * rqx * Zp < rpx * Zq) {
+            const float px = prow[x], qx = qrow[x];
+            const double rpx = residual(px, qx, A, C);
+            if (__dmul_rn(__dmul_rn(u, (double)qx), Zp) < __dmul_rn(rpx, Zq)) {
                 acc = c;
                 break;
             }
-            __syncthreads();  // every thread has read rp[x], rq[x] before the pass rewrites them
-            // reject x: one fp64 pass writes the new residual and sums it
+            // reject x: new coefficients, then one pass over both rows for the new Zp
+            A = A / Zp;
+            C = C / Zp + 1.0 / Zq;
+            Zq = Zq - (double)qx;
             double part = 0.0;
-            for (int y = t; y < V; y += kAcceptThreads) {
-                const double py = fresh ? (double)prow[y] : rp[y];
-                const double qy = fresh ? (double)qrow[y] : rq[y];
-                const double r = fmax(py / Zp - qy / Zq, 0.0);
-                rp[y] = r;
-                part += r;
-                // the thread that reads rq[x] zeroes it (no other thread touches it)
-                if (fresh || y == x) rq[y] = y == x ? 0.0 : qy;
+            for (int y0 = t; y0 < V; y0 += kAcceptThreads * kAcceptBatch) {
+                float py[kAcceptBatch], qy[kAcceptBatch];
+#pragma unroll
+                for (int u2 = 0; u2 < kAcceptBatch; ++u2) {
+                    const int y = min(y0 + u2 * kAcceptThreads, V - 1);
+                    py[u2] = __builtin_nontemporal_load(prow + y);
+                    qy[u2] = __builtin_nontemporal_load(qrow + y);
+                }
+#pragma unroll
+                for (int u2 = 0; u2 < kAcceptBatch; ++u2)
+                    if (y0 + u2 * kAcceptThreads < V) part += residual(py[u2], qy[u2], A, C);
             }
-            Zp = block_sum_d(part, s_red);  // includes a barrier: the pass is visible
-            Zq = Zq - rqx;
-            fresh = false;
+            Zp = block_sum_d(part, s_red);
+            ++k;
         }
         if (acc >= 0) {
             if (t == 0) a.accepted_idx[(size_t)b * a.max_path + len] = acc;
             ++len;
             cur = acc;
-            __syncthreads();  // rp / rq are rewritten by the next node's passes
             continue;
         }
         // bonus: smallest y with cumsum(rp)[y] > u * total; thread t owns a contiguous
         // chunk, the chunk sums are scanned in thread order
-        const int C = (V + kAcceptThreads - 1) / kAcceptThreads;
-        const int y0 = min(V, t * C), y1 = min(V, y0 + C);
+        const int chunk = (V + kAcceptThreads - 1) / kAcceptThreads;
+        const int y0 = min(V, t * chunk), y1 = min(V, y0 + chunk);
         double cs = 0.0;
-        for (int y = y0; y < y1; ++y) cs += fresh ? (double)prow[y] : rp[y];
+#pragma unroll 8
+        for (int y = y0; y < y1; ++y) cs += k == 0 ? (double)prow[y] : residual(prow[y], qrow[y], A, C);
         s_scan[t] = cs;
         __syncthreads();
         for (int off = 1; off < kAcceptThreads; off <<= 1) {
@@ -196,14 +243,14 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
             s_scan[t] += v;
             __syncthreads();
         }
-        const double total = fresh ? s_scan[kAcceptThreads - 1] : Zp;
+        const double total = k == 0 ? s_scan[kAcceptThreads - 1] : Zp;
         const double thr = (double)a.u_bonus[b] * total;
         if (t == 0) s_pick = V - 1;
         __syncthreads();
         double run = t > 0 ? s_scan[t - 1] : 0.0;  // exclusive prefix of this chunk
         if (run <= thr) {
             for (int y = y0; y < y1; ++y) {
-                run += fresh ? (double)prow[y] : rp[y];
+                run += k == 0 ? (double)prow[y] : residual(prow[y], qrow[y], A, C);
                 if (run > thr) {
                     atomicMin(&s_pick, y);
                     break;
@@ -224,16 +271,10 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
     for (int m = len + t; m < a.max_path; m += kAcceptThreads) a.accepted_idx[(size_t)b * a.max_path + m] = -1;
 }
 
-size_t accept_workspace_bytes(const bole_accept_dims_t &d) {
-    if (d.mode != BOLE_ACCEPT_SAMPLE) return 0;
-    return 2 * (size_t)d.batch * (size_t)d.vocab * sizeof(double);
-}
-
 hipError_t launch_tree_accept(const float *p_ctx, const float *p_node, const float *q_ctx,
                               const float *q_node, const int32_t *parent, const int32_t *token,
                               const int32_t *node_offsets, const float *u_node,
-                              const float *u_bonus, void *workspace,
-                              const bole_accept_dims_t &d, int32_t *accepted_idx,
+                              const float *u_bonus, const bole_accept_dims_t &d, int32_t *accepted_idx,
                               int32_t *accepted_len, int32_t *bonus, int32_t *tree_status,
                               hipStream_t stream) {
     AcceptArgs a;
@@ -246,8 +287,6 @@ hipError_t launch_tree_accept(const float *p_ctx, const float *p_node, const flo
     a.parent = parent;
     a.token = token;
     a.node_offsets = node_offsets;
-    a.rp_ws = d.mode == BOLE_ACCEPT_SAMPLE ? static_cast<double *>(workspace) : nullptr;
-    a.rq_ws = a.rp_ws ? a.rp_ws + (size_t)d.batch * d.vocab : nullptr;
     a.accepted_idx = accepted_idx;
     a.accepted_len = accepted_len;
     a.bonus = bonus;
@@ -257,6 +296,8 @@ hipError_t launch_tree_accept(const float *p_ctx, const float *p_node, const flo
     a.V = d.vocab;
     a.max_path = d.max_path;
     a.mode = d.mode;
+    a.vec = d.vocab % 4 == 0 &&
+            ((reinterpret_cast<uintptr_t>(p_ctx) | reinterpret_cast<uintptr_t>(p_node)) % 16) == 0;
     tree_accept_kernel<<<dim3((unsigned)d.batch), dim3(kAcceptThreads), 0, stream>>>(a);
     return hipGetLastError();
 }
