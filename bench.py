@@ -37,11 +37,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 _CSRC = os.path.join(ROOT, "tree_speculative_decoding_02_amd", "csrc")
 # sources that determine each kernel's memory traffic
 _VERIFY_SOURCES = [os.path.join(_CSRC, f) for f in ("verify_mfma.hip", "mfma_util.h",
-                                                   "bole_device.h", "launch.h")]
+                                                   "bole_device.h")]
 KERNEL_SOURCES = {
     "lazy": _VERIFY_SOURCES,
     "verify": _VERIFY_SOURCES,
-    "commit": [os.path.join(_CSRC, f) for f in ("commit.hip", "bole_device.h", "launch.h")],
+    "commit": [os.path.join(_CSRC, f) for f in ("commit.hip", "bole_device.h")],
+    "topk": [os.path.join(_CSRC, f) for f in ("tree_build.hip", "bole_device.h")],
 }
 # FETCH_SIZE / WRITE_SIZE record of the last counter runs (calibrated bytes per launch)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hybrid_stack_hbm_traffic.md")
@@ -299,6 +300,7 @@ def main():
             "avg_us_per_call": b_us, "median_us_per_call": 1e3 * float(np.median(b_spans[:, 0])),
             "bytes_per_call": b_bytes, "GB_s": b_bytes / (b_us * 1e3),
             "frac_hbm_peak": b_bytes / (b_us * 1e3) / HBM_PEAK_GBS, "nodes_kept": n_kept,
+            "topk_kernel_traffic": recorded_traffic("topk"),
             "what": "bole_build_tree: top-64 per position, best-first tree, budget controller "
                     "and packing for 64 sequences x 8 positions x 128256 tokens (3 launches)"}
         del marg
