@@ -4,14 +4,16 @@
 //
 // Three launches:
 //  1. topk_slice_kernel: the top 64 entries of every (sequence, position) row, per
-//     vocabulary slice of kSliceElems, ordered by (probability desc, index asc). The only
-//     HBM-heavy step: it reads the marginals once.
+//     vocabulary slice, ordered by (probability desc, index asc). The only HBM-heavy
+//     step: it streams the marginals once.
 //  2. build_kernel: one wavefront per sequence merges its slices' lists per position,
 //     grows the best-first tree (lane = candidate source) and runs the controller.
 //  3. pack_kernel: one workgroup scans the kept sizes into node_offsets and packs the
 //     trees.
 // Only the top 64 tokens of a position can ever be used: one parent's children are
 // inserted in rank order and a tree has at most 64 nodes.
+#include <algorithm>
+
 #include "bole_device.h"
 #include "launch.h"
 
@@ -19,22 +21,14 @@ namespace bole {
 
 constexpr int kTopK = 64;
 constexpr int kBuildThreads = 256;
-constexpr int kPerThread = 64;                           // register-resident keys per thread
-constexpr int kSliceElems = kBuildThreads * kPerThread;  // 16384
 constexpr int kGatherCap = 1024;                         // candidates sorted in LDS
 constexpr int kMaxDepth = 32;
 constexpr int kMaxBudget = 64;
 
-// Orderable key of a float: a larger float has a larger key; 0 marks "no element".
-__device__ __forceinline__ uint32_t f2key(float f) {
-    uint32_t u = __float_as_uint(f);
-    u = u == 0x80000000u ? 0u : u;                          // -0 ranks as +0
-    const uint32_t neg = (uint32_t)((int32_t)u >> 31);      // all ones for a negative
-    return u ^ (neg | 0x80000000u);                         // flip all bits, or the sign bit
-}
-__device__ __forceinline__ float key2f(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
+// Orderable key of a probability (finite, >= 0): its bits without the sign, plus one. A
+// larger value has a larger key, -0 ranks as +0, and key 0 marks "no element".
+__device__ __forceinline__ uint32_t bits2key(uint32_t u) { return (u & 0x7fffffffu) + 1u; }
+__device__ __forceinline__ float key2f(uint32_t k) { return __uint_as_float(k - 1u); }
 // rank order: larger key first, then lower index
 __device__ __forceinline__ bool better(uint32_t ka, int ia, uint32_t kb, int ib) {
     return ka > kb || (ka == kb && ia < ib);
@@ -79,164 +73,247 @@ __device__ __forceinline__ void wave_merge64(uint32_t &k, int &i, uint32_t nk, i
 
 // ---- 1. top 64 of one vocabulary slice of one (sequence, position) row
 //
-// Thread t holds elements lo + (j * 256 + t) * W + c (j < kPerThread / W, c < W) as keys.
-// A threshold theta that at least 64 elements reach is the smallest over the four
-// wavefronts of the wavefront's 16th largest thread maximum; the elements >= theta are
-// gathered in LDS and each one's rank among them counted, the first 64 kept. If more
-// than kGatherCap elements reach theta (many equal values), 64 rounds of block-wide
-// extraction of the best remaining element give the same list exactly.
+// The workgroup streams its slice [lo, hi) in chunks of kChunk elements, the next chunk's
+// loads in flight while the current one is filtered: thread t holds elements
+// c0 + (j * 256 + t) * W + c (j < kChunkPerThread / W, c < W) as orderable keys. Only
+// elements at or above a running threshold theta are gathered into an LDS candidate
+// buffer. theta starts as the smallest, over the wavefronts, of the wavefront's 16th
+// largest thread maximum in the first chunk (at least 64 elements reach it), and rises
+// after the first chunk and whenever the buffer passes half full: it becomes the exact
+// 64th largest buffered key (a 32-step bitwise search) and the candidates below it are
+// dropped. theta never
+// exceeds the 64th largest key seen so far, so the buffer always holds the top 64. The
+// last step counts each candidate's rank and writes ranks below 64 in place. If one
+// chunk leaves more than kGatherCap candidates (many equal values at theta), 64 rounds
+// of block-wide extraction over the slice, read again, give the same list.
+constexpr int kChunkPerThread = 16;
+constexpr int kChunk = kBuildThreads * kChunkPerThread;  // 4096 elements
+
 template <int W>
 __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
-    const float *__restrict__ marginals, uint2 *__restrict__ lists, int V, int S) {
-    constexpr int J = kPerThread / W;
-    __shared__ uint32_t s_k[kGatherCap];
-    __shared__ int s_i[kGatherCap];
-    __shared__ uint32_t s_theta[4];
-    __shared__ int s_cnt;
+    const float *__restrict__ marginals, uint2 *__restrict__ lists, int V, int S, int slice_len) {
+    constexpr int J = kChunkPerThread / W;
+    typedef uint32_t uv __attribute__((ext_vector_type(W)));
+    __shared__ uint32_t s_k[2][kGatherCap];
+    __shared__ int s_i[2][kGatherCap];
+    __shared__ int s_cnt[2];
+    __shared__ uint32_t s_th4[4];
+    __shared__ int s_wc[2][4];
     __shared__ uint32_t s_rk[4];
     __shared__ int s_ri[4];
     const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
     const size_t row = blockIdx.x / S;
     const int slice = blockIdx.x - (int)row * S;
-    const int lo = slice * kSliceElems;
+    const int lo = slice * slice_len, hi = min(V, lo + slice_len);
     const float *src = marginals + row * (size_t)V;
     uint2 *dst = lists + (size_t)blockIdx.x * kTopK;
 
-    // every load issued before any is used: addresses clamped into the row, keys of
-    // elements outside the slice or the row masked to 0 afterwards (in place)
-    typedef uint32_t uv __attribute__((ext_vector_type(W)));
-    uv key[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int e = lo + (j * kBuildThreads + t) * W;
-        key[j] = __builtin_nontemporal_load(reinterpret_cast<const uv *>(src + (uint32_t)min(e, V - W)));
-    }
-    if (lo + kSliceElems <= V) {  // a whole slice (all but the last of a row)
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-#pragma unroll
-            for (int c = 0; c < W; ++c) key[j][c] = f2key(__uint_as_float(key[j][c]));
-    } else {
+    // a chunk's raw bits (addresses clamped into the row)
+    auto load = [&](int c0, uv (&x)[J]) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int e = lo + (j * kBuildThreads + t) * W;
-#pragma unroll
-            for (int c = 0; c < W; ++c) {
-                const uint32_t k = f2key(__uint_as_float(key[j][c]));
-                key[j][c] = e + c < V ? k : 0u;
-            }
+            const int e = c0 + (j * kBuildThreads + t) * W;
+            x[j] = __builtin_nontemporal_load(reinterpret_cast<const uv *>(src + (uint32_t)min(e, V - W)));
         }
-    }
-
-    // threshold
-    uint32_t mx = 0;
+    };
+    // the keys of a chunk in place (0 outside the slice: only the last chunk masks), and
+    // the thread's largest
+    auto keys = [&](int c0, uv (&x)[J]) -> uint32_t {
+        uint32_t mx = 0u;
+        if (c0 + kChunk <= hi) {
 #pragma unroll
-    for (int j = 0; j < J; ++j)
+            for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int c = 0; c < W; ++c) mx = max(mx, key[j][c]);
-    {
-        // the wavefront's 16th largest thread maximum, bit by bit: the largest th with
-        // at least 16 maxima >= th
-        uint32_t th = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = th | (1u << bit);
-            if (__popcll(__ballot(mx >= cand)) >= 16) th = cand;
-        }
-        if (lane == 0) s_theta[wave] = th;
-    }
-    if (t == 0) s_cnt = 0;
-    __syncthreads();
-    const uint32_t theta = min(min(s_theta[0], s_theta[1]), min(s_theta[2], s_theta[3]));
-
-    // gather (one LDS atomic per wavefront and element slot)
+                for (int c = 0; c < W; ++c) {
+                    x[j][c] = bits2key(x[j][c]);
+                    mx = max(mx, x[j][c]);
+                }
+        } else {
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        // the slab's first index, recomputed per slab (the empty asm keeps the compiler
-        // from holding all 64 indices in registers)
-        int sbase = lo + (j * kBuildThreads + t) * W;
-        asm volatile("" : "+v"(sbase));
+            for (int j = 0; j < J; ++j) {
+                const int e = c0 + (j * kBuildThreads + t) * W;
 #pragma unroll
-        for (int c = 0; c < W; ++c) {
-            const bool take = key[j][c] != 0u && key[j][c] >= theta;
-            const uint64_t m = __ballot(take);
-            if (m) {
-                int base = 0;
-                if (lane == __builtin_ctzll(m)) base = atomicAdd(&s_cnt, __popcll(m));
-                base = __shfl(base, __builtin_ctzll(m), 64);
-                const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                            (uint32_t)(m >> 32),
-                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                if (take && slot < kGatherCap) {
-                    s_k[slot] = key[j][c];
-                    s_i[slot] = sbase + c;
+                for (int c = 0; c < W; ++c) {
+                    x[j][c] = e + c < hi ? bits2key(x[j][c]) : 0u;
+                    mx = max(mx, x[j][c]);
                 }
             }
         }
+        return mx;
+    };
+
+    int buf = 0;
+    if (t == 0) s_cnt[0] = 0;
+    uv A[J], B2[J];  // two chunk buffers, alternating
+    load(lo, A);
+    if (lo + kChunk < hi) load(lo + kChunk, B2);
+    uint32_t mx0 = keys(lo, A);
+    {
+        // the wavefront's 16th largest thread maximum in the first chunk, bit by bit
+        uint32_t th = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = th | (1u << bit);
+            if (__popcll(__ballot(mx0 >= cand)) >= 16) th = cand;
+        }
+        if (lane == 0) s_th4[wave] = th;
     }
     __syncthreads();
-    const int cnt = s_cnt;
+    // >= 1: a key at or above it is never the empty key
+    uint32_t theta = max(1u, min(min(s_th4[0], s_th4[1]), min(s_th4[2], s_th4[3])));
 
-    if (cnt <= kGatherCap) {
+    bool overflow = false;
+    // filters one chunk (keys already formed): gather, then compact when the buffer is
+    // half full (or past 2 x 64 at the slice's end); false when the buffer overflowed
+    auto filter = [&](int c0, uv (&x)[J], uint32_t mx) -> bool {
+        if (__ballot(mx >= theta)) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                int sbase = c0 + (j * kBuildThreads + t) * W;
+                asm volatile("" : "+v"(sbase));  // recomputed per slab, not held in registers
+#pragma unroll
+                for (int c = 0; c < W; ++c) {
+                    const bool take = x[j][c] >= theta;
+                    const uint64_t m = __ballot(take);
+                    if (m) {
+                        const int first = __builtin_ctzll(m);
+                        int base = 0;
+                        if (lane == first) base = atomicAdd(&s_cnt[buf], __popcll(m));
+                        base = __builtin_amdgcn_readlane(base, first);
+                        const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                                    (uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        if (take && slot < kGatherCap) {
+                            s_k[buf][slot] = x[j][c];
+                            s_i[buf][slot] = sbase + c;
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        const int cnt = s_cnt[buf];
+        if (cnt > kGatherCap) return false;
+        if (cnt > kGatherCap / 2 || (c0 == lo && cnt > kTopK) ||
+            (c0 + kChunk >= hi && cnt > 2 * kTopK)) {
+            // theta <- the exact 64th largest buffered key; keep the candidates >= it
+            uint32_t bk[kGatherCap / kBuildThreads];
+#pragma unroll
+            for (int r = 0; r < kGatherCap / kBuildThreads; ++r) {
+                const int x2 = t + r * kBuildThreads;
+                bk[r] = x2 < cnt ? s_k[buf][x2] : 0u;
+            }
+            uint32_t th = 0u;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand = th | (1u << bit);
+                int wc = 0;
+#pragma unroll
+                for (int r = 0; r < kGatherCap / kBuildThreads; ++r) wc += __popcll(__ballot(bk[r] >= cand));
+                if (lane == 0) s_wc[bit & 1][wave] = wc;
+                __syncthreads();
+                if (s_wc[bit & 1][0] + s_wc[bit & 1][1] + s_wc[bit & 1][2] + s_wc[bit & 1][3] >= kTopK)
+                    th = cand;
+            }
+            theta = max(theta, th);
+            if (t == 0) s_cnt[buf ^ 1] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < kGatherCap / kBuildThreads; ++r) {
+                const int x2 = t + r * kBuildThreads;
+                const bool keep = x2 < cnt && bk[r] >= theta;
+                const uint64_t m = __ballot(keep);
+                if (m) {
+                    const int first = __builtin_ctzll(m);
+                    int base = 0;
+                    if (lane == first) base = atomicAdd(&s_cnt[buf ^ 1], __popcll(m));
+                    base = __builtin_amdgcn_readlane(base, first);
+                    const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                                (uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    if (keep) {
+                        s_k[buf ^ 1][slot] = bk[r];
+                        s_i[buf ^ 1][slot] = s_i[buf][x2];
+                    }
+                }
+            }
+            __syncthreads();
+            buf ^= 1;
+        }
+        return true;
+    };
+
+    for (int c0 = lo; c0 < hi; c0 += 2 * kChunk) {
+        // chunk c0 in A (keys formed), chunk c0 + kChunk in flight in B2
+        if (!filter(c0, A, mx0)) {
+            overflow = true;
+            break;
+        }
+        const int c1 = c0 + kChunk;
+        if (c1 >= hi) break;
+        if (c1 + kChunk < hi) load(c1 + kChunk, A);
+        const uint32_t mx1 = keys(c1, B2);
+        if (!filter(c1, B2, mx1)) {
+            overflow = true;
+            break;
+        }
+        if (c1 + kChunk >= hi) break;
+        if (c1 + 2 * kChunk < hi) load(c1 + 2 * kChunk, B2);
+        mx0 = keys(c1 + kChunk, A);
+    }
+
+    if (!overflow) {
         // each candidate's rank is the number of better candidates ((key, index) pairs
         // are distinct, so ranks are too); ranks below 64 are written in place
+        const int cnt = s_cnt[buf];
         for (int x = t; x < cnt; x += kBuildThreads) {
-            const uint32_t kx = s_k[x];
-            const int ix = s_i[x];
+            const uint32_t kx = s_k[buf][x];
+            const int ix = s_i[buf][x];
             int rank = 0;
-            for (int y = 0; y < cnt; ++y) rank += better(s_k[y], s_i[y], kx, ix) ? 1 : 0;
+            for (int y = 0; y < cnt; ++y) rank += better(s_k[buf][y], s_i[buf][y], kx, ix) ? 1 : 0;
             if (rank < kTopK) dst[rank] = make_uint2(kx, (uint32_t)ix);
         }
         for (int r = cnt + t; r < kTopK; r += kBuildThreads) dst[r] = make_uint2(0u, 0x7fffffffu);
         return;
     }
 
-    // many ties: 64 rounds, each taking the best element not yet taken. The keys are
-    // read again from memory (an element is taken when it ranks at or above the last
-    // one taken), so no register holds them across the rounds.
-    uint32_t lk = 0xffffffffu;  // last taken (key, index); everything better is taken
+    // many ties: 64 rounds, each taking the best element not yet taken (ranking after the
+    // last one taken), over the slice read again
+    uint32_t lk = 0xffffffffu;
     int li = -1;
     for (int r = 0; r < kTopK; ++r) {
-        uint32_t bk = 0u;
+        uint32_t bk2 = 0u;
         int bi = 0x7fffffff;
-        for (int j = 0; j < J; ++j) {
-            const int e = lo + (j * kBuildThreads + t) * W;
-            const uv x = *reinterpret_cast<const uv *>(src + min(e, V - W));
-#pragma unroll
-            for (int c = 0; c < W; ++c) {
-                const uint32_t k = e + c < V ? f2key(__uint_as_float(x[c])) : 0u;
-                const int ix = e + c;
-                // not yet taken: ranks strictly after (lk, li)
-                if (better(lk, li, k, ix) && better(k, ix, bk, bi)) {
-                    bk = k;
-                    bi = ix;
-                }
+        for (int e = lo + t; e < hi; e += kBuildThreads) {
+            const uint32_t k = bits2key(__float_as_uint(src[e]));
+            if (better(lk, li, k, e) && better(k, e, bk2, bi)) {
+                bk2 = k;
+                bi = e;
             }
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
-            const uint32_t pk = __shfl_xor(bk, off, 64);
+            const uint32_t pk = __shfl_xor(bk2, off, 64);
             const int pi = __shfl_xor(bi, off, 64);
-            if (better(pk, pi, bk, bi)) {
-                bk = pk;
+            if (better(pk, pi, bk2, bi)) {
+                bk2 = pk;
                 bi = pi;
             }
         }
         if (lane == 0) {
-            s_rk[wave] = bk;
+            s_rk[wave] = bk2;
             s_ri[wave] = bi;
         }
         __syncthreads();
-        bk = s_rk[0];
+        bk2 = s_rk[0];
         bi = s_ri[0];
 #pragma unroll
         for (int w = 1; w < 4; ++w)
-            if (better(s_rk[w], s_ri[w], bk, bi)) {
-                bk = s_rk[w];
+            if (better(s_rk[w], s_ri[w], bk2, bi)) {
+                bk2 = s_rk[w];
                 bi = s_ri[w];
             }
         __syncthreads();
-        if (t == 0) dst[r] = make_uint2(bk, (uint32_t)(bk ? bi : 0x7fffffff));
-        lk = bk;
+        if (t == 0) dst[r] = make_uint2(bk2, (uint32_t)(bk2 ? bi : 0x7fffffff));
+        lk = bk2;
         li = bi;
     }
 }
@@ -426,12 +503,25 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
 // ---- host side
 struct BuildLayout {
     size_t lists, n_nodes, par, tok, rho, total;
-    int S;
+    int S, slice_len;
 };
+
+// Slices per row: about 2048 workgroups in all, each slice at least 8192 elements and a
+// multiple of the chunk.
+static void slices_for(const bole_build_dims_t &d, int &S, int &slice_len) {
+    const int64_t rows = (int64_t)d.batch * d.depth;
+    const int64_t by_grid = rows > 0 ? (2048 + rows - 1) / rows : 1;
+    const int64_t by_size = ((int64_t)d.vocab + 8191) / 8192;
+    const int64_t want = std::max<int64_t>(1, std::min(by_grid, by_size));
+    int64_t len = ((int64_t)d.vocab + want - 1) / want;
+    len = (len + kChunk - 1) / kChunk * kChunk;
+    slice_len = (int)len;
+    S = (int)(((int64_t)d.vocab + len - 1) / len);
+}
 
 static BuildLayout build_layout(const bole_build_dims_t &d) {
     BuildLayout L;
-    L.S = (d.vocab + kSliceElems - 1) / kSliceElems;
+    slices_for(d, L.S, L.slice_len);
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t B = (size_t)d.batch;
     L.lists = 0;
@@ -447,7 +537,8 @@ bool build_dims_ok(const bole_build_dims_t &d) {
     if (d.batch < 0 || d.depth < 1 || d.depth > kMaxDepth || d.vocab < 1 || d.n_max < 1 ||
         d.n_max > kMaxBudget || (d.flags & ~BOLE_BUILD_FIXED_BUDGET))
         return false;
-    const uint64_t S = ((uint64_t)d.vocab + kSliceElems - 1) / kSliceElems;
+    int S, len;
+    slices_for(d, S, len);
     return (uint64_t)d.batch * d.depth * S < (1ull << 31);
 }
 
@@ -467,9 +558,9 @@ hipError_t launch_build_tree(const float *marginals, const float *cost, float l_
     const unsigned rows = (unsigned)d.batch * (unsigned)d.depth * (unsigned)L.S;
     const bool vec = d.vocab % 4 == 0 && reinterpret_cast<uintptr_t>(marginals) % 16 == 0;
     if (vec)
-        topk_slice_kernel<4><<<dim3(rows), dim3(kBuildThreads), 0, stream>>>(marginals, lists, d.vocab, L.S);
+        topk_slice_kernel<4><<<dim3(rows), dim3(kBuildThreads), 0, stream>>>(marginals, lists, d.vocab, L.S, L.slice_len);
     else
-        topk_slice_kernel<1><<<dim3(rows), dim3(kBuildThreads), 0, stream>>>(marginals, lists, d.vocab, L.S);
+        topk_slice_kernel<1><<<dim3(rows), dim3(kBuildThreads), 0, stream>>>(marginals, lists, d.vocab, L.S, L.slice_len);
     build_kernel<<<dim3((unsigned)d.batch), dim3(256), 0, stream>>>(
         lists, cost, l_ar, d.depth, L.S, d.n_max, (d.flags & BOLE_BUILD_FIXED_BUDGET) ? 1 : 0,
         nn, par, tok, rh, speedup);
