@@ -311,34 +311,10 @@ def main():
     # at 70 % of the nodes; each node's children carry the draft row's top tokens)
     if not args.no_accept:
         Va = 128256
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(2025)
-        T = wl.total_nodes
-        zq = torch.randn((T + wl.batch, Va), generator=gen, device=dev) * 2.0
-        top = torch.topk(zq, 64, dim=1).indices.cpu().numpy()
-        par_np, offs_np = wl.parent, wl.node_offsets
-        tok_np = np.zeros(T, np.int32)
-        boost = torch.zeros_like(zq)
-        rng = np.random.default_rng(2025)
-        for b in range(wl.batch):
-            lo, hi = int(offs_np[b]), int(offs_np[b + 1])
-            for cur in [-1] + list(range(hi - lo)):
-                kids = [i for i in range(hi - lo) if par_np[lo + i] == cur]
-                row = T + b if cur < 0 else lo + cur
-                for r, c in enumerate(kids):
-                    tok_np[lo + c] = top[row, r]
-                if kids and rng.random() < 0.7:
-                    boost[row, int(tok_np[lo + kids[0]])] = 8.0
-        zp = zq + torch.randn(zq.shape, generator=gen, device=dev) + boost
-        del boost
-        pr, qr = torch.softmax(zp, dim=1), torch.softmax(zq, dim=1)
-        del zp, zq
-        p_node, p_ctx = pr[:T].contiguous(), pr[T:].contiguous()
-        q_node, q_ctx = qr[:T].contiguous(), qr[T:].contiguous()
-        del pr, qr
-        tok = torch.from_numpy(tok_np).to(dev)
-        u_node = torch.rand(T, generator=gen, device=dev)
-        u_bonus = torch.rand(wl.batch, generator=gen, device=dev)
+        ai = W.make_accept_inputs(wl.parent, wl.node_offsets, Va, 2025, dev)
+        p_ctx, p_node, q_ctx, q_node = ai["p_ctx"], ai["p_node"], ai["q_ctx"], ai["q_node"]
+        tok, u_node, u_bonus = ai["token"], ai["u_node"], ai["u_bonus"]
+        del ai
         acc = {}
         for mode in ("greedy", "sample"):
             f = bole.bind_tree_accept(p_ctx, p_node, parent, tok, offs, wl.max_path,

@@ -1,0 +1,111 @@
+"""Parity at the benchmark's full sizes, in the launch configurations bench.py times, on
+outputs the oracle computes for sampled sequences:
+  - the lazy step: bole_tree_verify_lazy_commit_layers over the 8-layer stack (64
+    sequences x 32 heads, d_k=128, d_v=64, 32-node trees, tree budget <= 32), two steps
+    in a row as the benchmark loop runs them (the previous step is the same batch);
+  - the tree builder on 64 sequences x 8 positions x 128256 tokens (every output);
+  - tree acceptance on the benchmark's trees over 128256 tokens (sampled trees)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import tree_accept as TA
+from oracle import tree_build as TB
+import workloads as W
+from tests.helpers import rel_err_rows, rel_err_states
+from tests.test_gpu_parity import subset
+
+pytestmark = pytest.mark.gpu
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def bole():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tree_speculative_decoding_02_amd import bole as b
+    return b
+
+
+def test_lazy_stack_benchmark_configuration(bole):
+    wl = W.make_config(5)
+    g = lambda x: x.to(dev())
+    parent, offs = g(torch.from_numpy(wl.parent)), g(torch.from_numpy(wl.node_offsets))
+    acc_idx, acc_len = g(torch.from_numpy(wl.accepted_idx)), g(torch.from_numpy(wl.accepted_len))
+    layers = []
+    for l in wl.layers:
+        y = dict(H0=g(l.H0), q=g(l.q), k=g(l.k), v=g(l.v), gate=g(l.gate),
+                 out=torch.empty((wl.total_nodes, wl.heads, wl.d_v), dtype=torch.float32,
+                                 device=dev()))
+        y.update(prev_k=y["k"], prev_v=y["v"], prev_gate=y["gate"])
+        layers.append(y)
+    step = bole.bind_tree_verify_lazy_commit_layers(layers, parent, offs, acc_idx, acc_len, parent,
+                                                    offs, trees_le_32=True, prev_trees_le_32=True)
+    sample = [0, 1, 17, 40, 63]
+    rows = np.concatenate([np.arange(wl.node_offsets[b], wl.node_offsets[b + 1]) for b in sample])
+    subs = [subset(wl, l, sample) for l in range(len(wl.layers))]
+    H = [s.layers[0].H0.double().numpy() for s in subs]   # the oracle's states, per layer
+    for it in range(2):
+        step()
+        torch.cuda.synchronize()
+        for l, s in enumerate(subs):
+            lay = s.layers[0]
+            H[l], _, _ = oracle.commit_serial(H[l], lay.k, lay.v, lay.gate, s.parent,
+                                              s.node_offsets, s.accepted_idx, s.accepted_len,
+                                              False)
+            ref, _ = oracle.verify_serial(H[l], lay.q, lay.k, lay.v, lay.gate, s.parent,
+                                          s.node_offsets, False)
+            out = layers[l]["out"].double().cpu().numpy()[rows]
+            Hg = layers[l]["H0"].double().cpu().numpy()[sample]
+            assert rel_err_rows(out, ref) <= 2e-3, (it, l)
+            assert rel_err_states(Hg, H[l]) <= 2e-3, (it, l)
+
+
+def test_build_tree_benchmark_size(bole):
+    m = W.make_marginals(2024, 64, 8, 128256)
+    cost = np.array([0.1 + 1.0 + 0.05 * n for n in range(1, 65)], np.float32)
+    out = bole.bole_build_tree(torch.from_numpy(m).to(dev()), torch.from_numpy(cost).to(dev()),
+                               1.0, n_max=64)
+    torch.cuda.synchronize()
+    ref = TB.build_trees(m, cost, 1.0, 64)
+    offs = out["node_offsets"].cpu().numpy()
+    np.testing.assert_array_equal(offs, ref["node_offsets"])
+    T = int(offs[-1])
+    for k in ("parent", "token", "rho"):
+        np.testing.assert_array_equal(out[k][:T].cpu().numpy(), ref[k], err_msg=k)
+    np.testing.assert_array_equal(out["speedup"].cpu().numpy(), ref["speedup"])
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_accept_benchmark_size(bole, mode):
+    wl = W.make_config(5, n_layers=1)
+    V = 128256
+    ai = W.make_accept_inputs(wl.parent, wl.node_offsets, V, 2025, dev())
+    parent = torch.from_numpy(wl.parent).to(dev())
+    offs = torch.from_numpy(wl.node_offsets).to(dev())
+    out = bole.bole_tree_accept(ai["p_ctx"], ai["p_node"], parent, ai["token"], offs, wl.max_path,
+                                sample=mode == "sample", q_ctx=ai["q_ctx"], q_node=ai["q_node"],
+                                u_node=ai["u_node"], u_bonus=ai["u_bonus"])
+    torch.cuda.synchronize()
+    tok = ai["token"].cpu().numpy()
+    u_node = ai["u_node"].cpu().numpy()
+    u_bonus = ai["u_bonus"].cpu().numpy()
+    lens = out["accepted_len"].cpu().numpy()
+    assert lens.max() >= 3
+    for b in [0, 1, 17, 40, 63]:
+        lo, hi = int(wl.node_offsets[b]), int(wl.node_offsets[b + 1])
+        pn = ai["p_node"][lo:hi].cpu().numpy()
+        qn = ai["q_node"][lo:hi].cpu().numpy()
+        path, y, margin = TA.accept_tree(ai["p_ctx"][b].cpu().numpy(), ai["q_ctx"][b].cpu().numpy(),
+                                         pn, qn, wl.parent[lo:hi], tok[lo:hi], 0, hi - lo,
+                                         u_node[lo:hi], u_bonus[b],
+                                         TA.SAMPLE if mode == "sample" else TA.GREEDY, wl.max_path)
+        if mode == "sample" and margin <= 1e-9:
+            continue
+        assert int(lens[b]) == len(path), b
+        assert out["accepted_idx"][b, :len(path)].cpu().tolist() == path, b
+        assert int(out["bonus"][b]) == y, b

@@ -247,6 +247,47 @@ def make_marginals(seed: int, batch: int, depth: int, vocab: int, logit_std: flo
     return p.astype(np.float32)
 
 
+def make_accept_inputs(parent: np.ndarray, node_offsets: np.ndarray, vocab: int, seed: int,
+                       device, agree: float = 0.7):
+    """Synthetic target and draft rows for tree acceptance, built on `device` with a seeded
+    torch generator: draft logits N(0, 2) for every node and for each tree's verified
+    context; each node's children carry the draft row's top tokens in order; target
+    logits = draft + N(0, 1), with the first child's token raised by 8 at a fraction
+    `agree` of the nodes (so that paths of several nodes are accepted); uniforms U[0, 1).
+    Returns a dict of tensors: p_ctx, q_ctx [B, V], p_node, q_node [T, V], token [T],
+    u_node [T], u_bonus [B] (float32 / int32)."""
+    T, B = int(parent.shape[0]), int(node_offsets.shape[0]) - 1
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    zq = torch.randn((T + B, vocab), generator=gen, device=device) * 2.0
+    top = torch.topk(zq, min(64, vocab), dim=1).indices.cpu().numpy()
+    tok = np.zeros(T, np.int32)
+    rng = np.random.default_rng(seed)
+    raise_at = []
+    for b in range(B):
+        lo, hi = int(node_offsets[b]), int(node_offsets[b + 1])
+        for cur in [-1] + list(range(hi - lo)):
+            kids = [i for i in range(hi - lo) if parent[lo + i] == cur]
+            row = T + b if cur < 0 else lo + cur
+            for r, c in enumerate(kids):
+                tok[lo + c] = top[row, r]
+            if kids and rng.random() < agree:
+                raise_at.append((row, int(tok[lo + kids[0]])))
+    zp = zq + torch.randn(zq.shape, generator=gen, device=device)
+    if raise_at:
+        ri = torch.tensor([r for r, _ in raise_at], device=device)
+        ci = torch.tensor([c for _, c in raise_at], device=device)
+        zp[ri, ci] += 8.0
+    p, q = torch.softmax(zp, dim=1), torch.softmax(zq, dim=1)
+    del zp, zq
+    out = {"p_node": p[:T].contiguous(), "p_ctx": p[T:].contiguous(),
+           "q_node": q[:T].contiguous(), "q_ctx": q[T:].contiguous(),
+           "token": torch.from_numpy(tok).to(device),
+           "u_node": torch.rand(T, generator=gen, device=device),
+           "u_bonus": torch.rand(B, generator=gen, device=device)}
+    return out
+
+
 def random_tree(rng: np.random.Generator, n: int, kind: str) -> np.ndarray:
     """Tree-local parent array of n nodes, parent[i] < i. Kinds: 'random' (uniform
     parent in [-1, i)), 'chain', 'star' (all roots), 'bestfirst', 'deep' (mostly chains)."""
