@@ -9,7 +9,10 @@
 //
 // One launch for trees of 1..32 nodes (one wavefront per sequence, head and 64-column
 // group) and, only when the batch may hold larger trees, one for trees of 33..64 nodes
-// (two wavefronts). H_0 goes from HBM straight into MFMA operand registers with
+// (two wavefronts); each launch covers up to 16 layers that share the trees
+// (blockIdx.y = layer). The LAZY instantiation first applies the previous step's accepted
+// path to H_0 (section 2's restore) and writes it back, in the same pass over H_0.
+// H_0 goes from HBM straight into MFMA operand registers with
 // row-contiguous 16-byte loads, so a wavefront needs only 12 KB of LDS (K and V) and
 // eight of them fit on a CU: the whole benchmark batch is in flight at once. fp32
 // operands (H_0, W) are split into bf16 hi + lo (two products, about 16 mantissa bits),
