@@ -283,14 +283,21 @@ def main():
     v_us = kernels["verify"]["avg_us_per_layer"]
 
     # the draft-tree builder on the same batch: 64 sequences x 8 drafted positions over a
-    # 128256-token vocabulary (Llama-3.1's), best-first up to 64 nodes, controller on the
-    # speedup model's cost C(N) = T_draft/T_AR + 1 + alpha N (alpha = 0.05, in AR steps)
+    # 128256-token vocabulary (Llama-3.1's), best-first up to 64 nodes, with the budget
+    # controller's cost C(N) from this GPU: the lazy step of the same stack is timed at
+    # tree sizes N, the roofline form T(N) = t0 + t1 N fitted to it, L_AR = T(1) (one node
+    # per sequence is an autoregressive step through these layers) and
+    # C(N) = T_draft + T(N) with T_draft = 0.1 L_AR
     if not args.no_builder:
         Bb, Db, Vb, nb = wl.batch, 8, 128256, 64
+        calib = calibrate_verify_cost(bole, W, wl, dev, stream, timed)
+        t0, t1 = calib["fit_us"]["t0"], calib["fit_us"]["t1"]
+        l_ar = t0 + t1
+        result["controller_calibration"] = calib
         marg = torch.from_numpy(W.make_marginals(2024, Bb, Db, Vb)).to(dev)
-        cost = torch.tensor([0.1 + 1.0 + 0.05 * n for n in range(1, nb + 1)], dtype=torch.float32,
-                            device=dev)
-        build = bole.bind_build_tree(marg, cost, 1.0, n_max=nb, stream=stream)
+        cost = torch.tensor([0.1 * l_ar + t0 + t1 * n for n in range(1, nb + 1)],
+                            dtype=torch.float32, device=dev)
+        build = bole.bind_build_tree(marg, cost, l_ar, n_max=nb, stream=stream)
         b_ms, b_spans, _ = timed([[build]], args.steps, args.warmup)
         b_us = 1e3 * float(np.mean(b_spans[:, 0]))
         b_bytes = Bb * Db * Vb * 4   # the marginals, read once; the rest is < 0.1 %
@@ -387,6 +394,38 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def calibrate_verify_cost(bole, W, wl, dev, stream, timed, sizes=(1, 4, 8, 16, 32, 64)):
+    """The lazy step of the benchmark's stack (64 sequences, 8 layers x 32 heads,
+    d_k=128, d_v=64) timed with every tree of N nodes, for each N in `sizes`; the
+    least-squares line T(N) = t0 + t1 N through the times (us per step)."""
+    import numpy as np
+    import torch
+    ts = []
+    for n in sizes:
+        w = W.make_random(900 + n, batch=wl.batch, heads=wl.heads, d_k=wl.d_k, d_v=wl.d_v,
+                          sizes=[n] * wl.batch, kind="bestfirst", max_path=wl.max_path)
+        lay = w.layers[0]
+        g = lambda x: x.to(dev)
+        par, offs = g(torch.from_numpy(w.parent)), g(torch.from_numpy(w.node_offsets))
+        ai, al = g(torch.from_numpy(w.accepted_idx)), g(torch.from_numpy(w.accepted_len))
+        q, k, v, gate = g(lay.q), g(lay.k), g(lay.v), g(lay.gate)
+        layers = [dict(H0=g(lay.H0).clone(), q=q, k=k, v=v, gate=gate, prev_k=k, prev_v=v,
+                       prev_gate=gate,
+                       out=torch.empty((w.total_nodes, w.heads, w.d_v), dtype=torch.float32,
+                                       device=dev)) for _ in range(len(wl.layers))]
+        step = bole.bind_tree_verify_lazy_commit_layers(
+            layers, par, offs, ai, al, par, offs, stream=stream, trees_le_32=n <= 32,
+            prev_trees_le_32=n <= 32)
+        ms, _, _ = timed([[step]], 20, 3)
+        ts.append(1e3 * ms)
+        del layers, step
+    A = np.stack([np.ones(len(sizes)), np.array(sizes, float)], axis=1)
+    (t0, t1), *_ = np.linalg.lstsq(A, np.array(ts), rcond=None)
+    return {"N": list(sizes), "T_us": ts, "fit_us": {"t0": float(t0), "t1": float(t1)},
+            "what": "lazy step of the 8-layer stack with every tree of N nodes; "
+                    "C(N) = 0.1 L_AR + t0 + t1 N, L_AR = t0 + t1"}
 
 
 def config_sweep(dev, reps=20):
