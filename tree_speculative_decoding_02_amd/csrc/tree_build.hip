@@ -318,29 +318,31 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
     }
 }
 
-// Best (score desc, who asc) over the wavefront, in every lane. DPP reduction toward lane
-// 63 (row_shr 1, 2, 4, 8 within each row of 16, then row_bcast 15 and 31 across rows);
-// lanes whose DPP source is outside the row or masked keep the identity (-inf, INT_MAX).
+// Best offer over the wavefront, in every lane. An offer is packed into one 64-bit key
+// that is larger when better: the high word is the score's bits + 1 (scores are >= +0,
+// so this orders them; 0 means no offer), the low word is ~(source + 1) (the context is
+// source -1), so equal scores go to the earlier source. DPP reduction toward lane 63
+// (row_shr 1, 2, 4, 8 within each row of 16, then row_bcast 15 and 31 across rows);
+// lanes whose DPP source is outside the row or masked keep key 0.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void argmax_dpp_step(float &s, int &w) {
-    const float ps = __int_as_float(__builtin_amdgcn_update_dpp(
-        (int)0xff800000, __float_as_int(s), CTRL, ROW_MASK, 0xf, false));
-    const int pw = __builtin_amdgcn_update_dpp(0x7fffffff, w, CTRL, ROW_MASK, 0xf, false);
-    if (ps > s || (ps == s && pw < w)) {
-        s = ps;
-        w = pw;
-    }
+__device__ __forceinline__ void keymax_dpp_step(uint32_t &hi, uint32_t &lo) {
+    const uint32_t ph = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t pl = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, ROW_MASK, 0xf, false);
+    const uint64_t p = ((uint64_t)ph << 32) | pl, m = ((uint64_t)hi << 32) | lo;
+    const bool take = p > m;
+    hi = take ? ph : hi;
+    lo = take ? pl : lo;
 }
 
-__device__ __forceinline__ void wave_argmax(float &s, int &w) {
-    argmax_dpp_step<0x111, 0xf>(s, w);  // row_shr:1
-    argmax_dpp_step<0x112, 0xf>(s, w);  // row_shr:2
-    argmax_dpp_step<0x114, 0xf>(s, w);  // row_shr:4
-    argmax_dpp_step<0x118, 0xf>(s, w);  // row_shr:8
-    argmax_dpp_step<0x142, 0xa>(s, w);  // row_bcast:15 into rows 1 and 3
-    argmax_dpp_step<0x143, 0xc>(s, w);  // row_bcast:31 into rows 2 and 3
-    s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
-    w = __builtin_amdgcn_readlane(w, 63);
+__device__ __forceinline__ void wave_keymax(uint32_t &hi, uint32_t &lo) {
+    keymax_dpp_step<0x111, 0xf>(hi, lo);  // row_shr:1
+    keymax_dpp_step<0x112, 0xf>(hi, lo);  // row_shr:2
+    keymax_dpp_step<0x114, 0xf>(hi, lo);  // row_shr:4
+    keymax_dpp_step<0x118, 0xf>(hi, lo);  // row_shr:8
+    keymax_dpp_step<0x142, 0xa>(hi, lo);  // row_bcast:15 into rows 1 and 3
+    keymax_dpp_step<0x143, 0xc>(hi, lo);  // row_bcast:31 into rows 2 and 3
+    hi = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
+    lo = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
 }
 
 // ---- 2. best-first tree and controller, one wavefront per sequence
@@ -357,7 +359,6 @@ __global__ __launch_bounds__(256) void build_kernel(
     int32_t *__restrict__ tok_out, float *__restrict__ rho_out, float *__restrict__ speedup) {
     __shared__ float s_val[kMaxDepth][kTopK];
     __shared__ int s_tok[kMaxDepth][kTopK];
-    __shared__ uint32_t s_key[kMaxDepth][kTopK];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int b = blockIdx.x;
 
@@ -383,8 +384,7 @@ __global__ __launch_bounds__(256) void build_kernel(
                 }
             }
         }
-        s_key[d][lane] = k;
-        s_val[d][lane] = key2f(k);
+        s_val[d][lane] = k ? key2f(k) : -1.f;  // -1: no candidate of this rank
         s_tok[d][lane] = i;
     }
     __syncthreads();
@@ -392,35 +392,52 @@ __global__ __launch_bounds__(256) void build_kernel(
     // C(N) for N = lane + 1
     const float c_lane = (cost != nullptr && lane < n_max) ? cost[lane] : 1.f;
 
-    // source state (lane 63: the context) and node outputs
+    // source state (lane 63: the context): depth, rank and score of its next child, the
+    // value of that child (cur) and of the one after it (nxt), so that no LDS read sits
+    // on a step's critical path: only a winning lane refills nxt, and it is needed only
+    // when that lane wins again. A new node's first two candidates come from the
+    // per-position registers f0, f1 (lane d: the two best of position d + 1).
+    const float f0 = lane < D ? s_val[lane][0] : -1.f;
+    const float f1 = lane < D ? s_val[lane][1] : -1.f;
     int src_depth = 0, src_rank = 0;
     float src_rho = 1.f;
-    int o_par = -1, o_tok = 0;
+    float cur = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f0), 0));
+    float nxt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f1), 0));
+    int o_par = -1, o_d = 0, o_r = 0;  // node outputs: parent, the candidate's position and rank
     float o_rho = 0.f;
     int n = 0;
     for (; n < n_max; ++n) {
         const bool is_src = lane < n || lane == 63;
-        float sc = -1.f;
-        if (is_src && src_depth < D && src_rank < kTopK && s_key[src_depth][src_rank] != 0u)
-            sc = __fmul_rn(src_rho, s_val[src_depth][src_rank]);
-        int who = lane == 63 ? -1 : lane;
-        if (sc < 0.f) who = 0x7fffffff;
-        float bs = sc;
-        int bw = who;
-        wave_argmax(bs, bw);
-        if (bs < 0.f) break;  // no source offers a child (wave-uniform)
+        const bool offer = is_src && cur >= 0.f;
+        const float sc = __fmul_rn(src_rho, cur);
+        uint32_t khi = offer ? __float_as_uint(sc) + 1u : 0u;
+        uint32_t klo = ~(uint32_t)((lane == 63 ? -1 : lane) + 1);
+        wave_keymax(khi, klo);
+        if (khi == 0u) break;  // no source offers a child (wave-uniform)
+        const float bs = __uint_as_float(khi - 1u);
+        const int bw = (int)(~klo) - 1;  // the winning source: -1 for the context
         const int wl = bw < 0 ? 63 : bw;  // the winning source's lane
         const int wd = __builtin_amdgcn_readlane(src_depth, wl);
         const int wr = __builtin_amdgcn_readlane(src_rank, wl);
-        if (lane == wl) ++src_rank;
+        if (lane == wl) {
+            ++src_rank;
+            cur = nxt;
+            nxt = src_rank + 1 < kTopK ? s_val[src_depth][src_rank + 1] : -1.f;
+        }
+        const int dn = wd + 1;  // the new node's depth; its children are at position dn + 1
+        const float g0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f0), dn < D ? dn : 0));
+        const float g1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f1), dn < D ? dn : 0));
         if (lane == n) {
             o_par = bw < 0 ? -1 : bw;
-            o_tok = s_tok[wd][wr];
+            o_d = wd;
+            o_r = wr;
             o_rho = bs;
             if (n < 63) {
-                src_depth = wd + 1;
+                src_depth = dn;
                 src_rank = 0;
                 src_rho = bs;
+                cur = dn < D ? g0 : -1.f;
+                nxt = dn < D ? g1 : -1.f;
             }
         }
     }
@@ -448,7 +465,7 @@ __global__ __launch_bounds__(256) void build_kernel(
     }
     if (lane < keep) {
         par_out[(size_t)b * n_max + lane] = o_par;
-        tok_out[(size_t)b * n_max + lane] = o_tok;
+        tok_out[(size_t)b * n_max + lane] = s_tok[o_d][o_r];
         rho_out[(size_t)b * n_max + lane] = o_rho;
     }
     if (lane == 0) {
