@@ -29,9 +29,10 @@ constexpr int kMaxBudget = 64;
 // larger value has a larger key, -0 ranks as +0, and key 0 marks "no element".
 __device__ __forceinline__ uint32_t bits2key(uint32_t u) { return (u & 0x7fffffffu) + 1u; }
 __device__ __forceinline__ float key2f(uint32_t k) { return __uint_as_float(k - 1u); }
-// rank order: larger key first, then lower index
+// rank order: larger key first, then lower index (indices are >= 0): one 64-bit compare
+// of (key, ~index), with no branches
 __device__ __forceinline__ bool better(uint32_t ka, int ia, uint32_t kb, int ib) {
-    return ka > kb || (ka == kb && ia < ib);
+    return (((uint64_t)ka << 32) | (uint32_t)~ia) > (((uint64_t)kb << 32) | (uint32_t)~ib);
 }
 
 // One compare-exchange step of a 64-lane bitonic network: the lower lane of each pair
