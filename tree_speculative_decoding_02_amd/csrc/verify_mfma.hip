@@ -9,10 +9,10 @@
 //
 // One launch for trees of 1..32 nodes (one wavefront per sequence, head and 64-column
 // group) and, only when the batch may hold larger trees, one for trees of 33..64 nodes
-// (two wavefronts); each launch covers up to 16 layers that share the trees
-// (blockIdx.y = layer). The LAZY instantiation first applies the previous step's accepted
-// path to H_0 (section 2's restore) and writes it back, in the same pass over H_0.
-// H_0 goes from HBM straight into MFMA operand registers with
+// (two wavefronts that split H_0's rows); each launch covers up to 16 layers that share
+// the trees (blockIdx.y = layer). The LAZY instantiation first applies the previous
+// step's accepted path to H_0 (section 2's restore) and writes it back, in the same pass
+// over H_0. H_0 goes from HBM straight into MFMA operand registers with
 // row-contiguous 16-byte loads, so a wavefront needs only 12 KB of LDS (K and V) and
 // eight of them fit on a CU: the whole benchmark batch is in flight at once. fp32
 // operands (H_0, W) are split into bf16 hi + lo (two products, about 16 mantissa bits),
@@ -25,21 +25,17 @@
 
 namespace bole {
 
-// One kernel template, two instantiations: NWT = 1 takes trees of 1..32 nodes (and the
-// status of every tree except those of 33..64 nodes), NWT = 2 takes trees of 33..64 and
-// is launched only when the batch may hold them. A workgroup of NWT wavefronts works on
-// one (sequence, head, 64-column group): every wavefront covers all 32 NWT nodes as
-// 16-node tiles, and wavefront w the columns w*CW/NWT .. of the group, so H_0 is read
-// once. 16x16 matrix-core tiles throughout: lane = (n, g) with n = lane % 16,
-// g = lane / 16.
+// Trees of 1..32 nodes (and the status of every tree except those of 33..64 nodes, which
+// the two-wavefront kernel below takes): one wavefront per (sequence, head, 64-column
+// group) covers the tree's 32 node rows as two 16-node tiles. 16x16 matrix-core tiles
+// throughout: lane = (n, g) with n = lane % 16, g = lane / 16.
 //
 // H_0 term, all v_mfma_f32_16x16x32_bf16. The H_0 slice is loaded straight into
 // registers with row-contiguous 16-byte loads: load s = 8t + e gives lane (n, g) row
 // 32t + 8g + e, columns 4n .. 4n+3, and one load instruction covers 4 full rows. Over
 // the 8 loads of k-step t, lane (n, g) then holds rows 32t + 8g .. +7 of each of its
 // columns: exactly the B operand of a 16x16x32 product whose output column n stands
-// for state column 4n + c. H_0 never goes through LDS (with NWT = 2 each wavefront
-// loads the slice; the second read is served by L2). It is split bf16 hi + lo (two
+// for state column 4n + c. H_0 never goes through LDS. It is split bf16 hi + lo (two
 // products, about 16 mantissa bits); the A operand is the bf16 Q fragment of the same
 // k-step, shared with the intra-tree term.
 //
@@ -66,17 +62,15 @@ struct LazyCommit {
 
 // Layer blockIdx.y of the table; every layer runs the same trees. Per-tree outputs
 // (statuses, path rows) are written by layer 0 only.
-template <int DK, int DV, int NWT, bool LAZY>
-__global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
+template <int DK, int DV, bool LAZY>
+__global__ __launch_bounds__(64, 2) void verify_mfma_tree_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
     int U, int max_n, LazyCommit lc) {
-    static_assert(!LAZY || NWT == 1, "the lazy commit runs in the one-wavefront instantiation");
-    constexpr int NN = 32 * NWT;            // node rows staged
-    constexpr int NT = 2 * NWT;             // 16-node tiles per wavefront
+    constexpr int NN = 32;                  // node rows staged
+    constexpr int NT = 2;                   // 16-node tiles
     constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
-    constexpr int CPW = CW / NWT;           // state columns per wavefront
-    constexpr int CPL = CPW / 16;           // columns per lane: 4, 2 or 1
+    constexpr int CPL = CW / 16;            // columns per lane: 4 or 2
     constexpr int G = DV / CW;              // column groups per unit
     constexpr int KT = DK / 32;             // k-steps of the bf16 products
     constexpr int HS = DK / 4;              // 16-byte H_0 loads per lane (4 rows each)
@@ -98,7 +92,6 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     float *const out = ly.out;
 
     const int lane = lane_id();
-    const int wave = NWT == 1 ? 0 : (int)(threadIdx.x >> 6);
     const int n16 = lane & 15, g = lane >> 4;
     int unit, cg;
     if (G == 1) {
@@ -112,24 +105,19 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     }
     const int b = unit / H, h = unit - b * H;
     const int c0 = cg * CW;
-    const int cw0 = wave * CPW;             // the wave's first column within the group
     const bool first = blockIdx.y == 0 && h == 0 && cg == 0;  // writes the per-tree outputs
     const bool writer = tree_status != nullptr && first && threadIdx.x == 0;
 
-    const TreeRange tr = tree_range(node_offsets, b, T, NWT == 1 ? max_n : kMaxTree);
+    const TreeRange tr = tree_range(node_offsets, b, T, max_n);
     bool do_verify = true;
-    if (NWT == 1) {
-        if (tr.status != BOLE_TREE_OK) {
-            if (writer) tree_status[b] = tr.status;
-            do_verify = false;
-        } else if (tr.n > 32) {
-            do_verify = false;  // the NWT = 2 instantiation's
-        } else if (tr.n == 0) {
-            if (writer) tree_status[b] = BOLE_TREE_OK;
-            do_verify = false;
-        }
-    } else {
-        if (tr.status != BOLE_TREE_OK || tr.n <= 32) do_verify = false;
+    if (tr.status != BOLE_TREE_OK) {
+        if (writer) tree_status[b] = tr.status;
+        do_verify = false;
+    } else if (tr.n > 32) {
+        do_verify = false;  // the two-wavefront kernel's
+    } else if (tr.n == 0) {
+        if (writer) tree_status[b] = BOLE_TREE_OK;
+        do_verify = false;
     }
     // the previous step's path: plausible from its length and offsets alone (validated
     // below, once its parent links and indices are in)
@@ -180,9 +168,8 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     // exactly what it needs: no LDS instruction has to wait for the H_0 loads). K: load
     // s fills LDS slots 64s .. 64s+63, i.e. rows (64/PPR)s ..; lane l fills slot 64s + l
     // = row j, slot-in-row l % PPR, with piece (l % PPR) ^ (j % PPR). V: lane l of load s
-    // takes row (64/VPR)s + l/VPR, piece l % VPR. The wavefronts of the workgroup take
-    // every NWT-th load.
-    constexpr int KL = NN * PPR / 64 / NWT, VL = NN * VPR / 64 / NWT;
+    // takes row (64/VPR)s + l/VPR, piece l % VPR.
+    constexpr int KL = NN * PPR / 64, VL = NN * VPR / 64;
     bf16x8 kst[KL], vst[VL];
     if (do_verify) {
 #pragma unroll
@@ -193,25 +180,25 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
                     qu + ((uint32_t)min(16 * it + n16, last) * rq + 32 * t + 8 * g));
 #pragma unroll
         for (int u = 0; u < KL; ++u) {
-            const int s = wave + NWT * u;
+            const int s = u;
             const int j = (64 / PPR) * s + lane / PPR;
             const int pc = (lane % PPR) ^ (j % PPR);
             kst[u] = load16_stream(ku + ((uint32_t)min(j, last) * rq + 8 * pc));
         }
 #pragma unroll
         for (int u = 0; u < VL; ++u) {
-            const int s = wave + NWT * u;
+            const int s = u;
             const int j = (64 / VPR) * s + lane / VPR;
             vst[u] = load16_stream(vu + ((uint32_t)min(j, last) * rv + 8 * (lane % VPR)));
         }
     }
-    // H_0 slice: load s = 8t + e, lane (n, g): row 32t + 8g + e, columns cw0 + CPL*n ..
+    // H_0 slice: load s = 8t + e, lane (n, g): row 32t + 8g + e, columns CPL*n ..
     hvec hreg[HS];
     if (do_verify || plikely) {
 #pragma unroll
         for (int s = 0; s < HS; ++s)
             hreg[s] = __builtin_nontemporal_load(reinterpret_cast<const hvec *>(
-                hu + ((uint32_t)(32 * (s >> 3) + 8 * g + (s & 7)) * DV + cw0 + CPL * n16)));
+                hu + ((uint32_t)(32 * (s >> 3) + 8 * g + (s & 7)) * DV + CPL * n16)));
     }
     // lazy commit: the factor chunks of the first kLazyStage path nodes, issued behind
     // H_0 (their indices were loaded first) and held in registers until the path is
@@ -236,10 +223,10 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
     }
     if (do_verify) {
 #pragma unroll
-        for (int u = 0; u < KL; ++u) s_k[64 * (wave + NWT * u) + lane] = kst[u];
+        for (int u = 0; u < KL; ++u) s_k[64 * u + lane] = kst[u];
 #pragma unroll
         for (int u = 0; u < VL; ++u)
-            *reinterpret_cast<bf16x8 *>(s_v + 512 * (wave + NWT * u) + 8 * lane) = vst[u];
+            *reinterpret_cast<bf16x8 *>(s_v + 512 * u + 8 * lane) = vst[u];
     }
 
     // ---- lazy commit: validate the previous path, stage its factors, update H_0 in
@@ -305,7 +292,7 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
                 }
                 for (int m = 0; m < mc; ++m) {
                     const float a = readlane_f(pa, m0 + m);
-                    const vvec vv = *reinterpret_cast<const vvec *>(s_pv + m * CW + cw0 + CPL * n16);
+                    const vvec vv = *reinterpret_cast<const vvec *>(s_pv + m * CW + CPL * n16);
 #pragma unroll
                     for (int t = 0; t < KT; ++t) {
                         const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(s_pk + m * DK + 32 * t + 8 * g);
@@ -321,7 +308,7 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
 #pragma unroll
             for (int s = 0; s < HS; ++s)
                 __builtin_nontemporal_store(hreg[s], reinterpret_cast<hvec *>(
-                    hu + ((uint32_t)(32 * (s >> 3) + 8 * g + (s & 7)) * DV + cw0 + CPL * n16)));
+                    hu + ((uint32_t)(32 * (s >> 3) + 8 * g + (s & 7)) * DV + CPL * n16)));
         }
         if (!do_verify) return;
     }
@@ -334,7 +321,7 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
         for (int i = g; i < n; i += 4)
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-                ou[(uint32_t)i * rv + cw0 + CPL * n16 + c] = __builtin_nanf("");
+                ou[(uint32_t)i * rv + CPL * n16 + c] = __builtin_nanf("");
         return;
     }
     const float L2 = topo.L;
@@ -375,9 +362,7 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
             for (int c = 0; c < CPL; ++c) acc[it][c][r] *= sc;
         }
 
-    // ---- 4. intra-tree term, one node tile and one ancestor tile pair at a time (with
-    // two wavefronts, each needs the other's K and V rows)
-    if (NWT > 1) __syncthreads();
+    // ---- 4. intra-tree term, one node tile and one ancestor tile pair at a time
 #pragma unroll
     for (int it = 0; it < NT; ++it) {
         const int ti = it;                        // node tile
@@ -385,7 +370,7 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
         const uint64_t mi = shfl_u64(topo.mask, i);
         const float Li = __shfl(L2, i, 64);
 #pragma unroll
-        for (int p = 0; p < NWT; ++p) {           // ancestor tile pair (2p, 2p+1)
+        for (int p = 0; p < NN / 32; ++p) {       // ancestor tile pair (2p, 2p+1)
             if (2 * p > ti) break;                // wave-uniform: nothing above the diagonal
             float w[8];
 #pragma unroll
@@ -420,7 +405,7 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int j = 32 * p + (e < 4 ? 4 * g + e : 12 + 4 * g + e);
-                const vvec x = *reinterpret_cast<const vvec *>(s_v + j * CW + cw0 + CPL * n16);
+                const vvec x = *reinterpret_cast<const vvec *>(s_v + j * CW + CPL * n16);
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) vb[c][e] = x[c];
             }
@@ -432,7 +417,7 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
         }
     }
 
-    // ---- 5. store: node 16it + 4g + r, columns cw0 + CPL*n .. +CPL-1
+    // ---- 5. store: node 16it + 4g + r, columns CPL*n .. +CPL-1
 #pragma unroll
     for (int it = 0; it < NT; ++it)
 #pragma unroll
@@ -442,7 +427,271 @@ __global__ __launch_bounds__(64 * NWT, 2) void verify_mfma_tree_kernel(
 #pragma unroll
             for (int c = 0; c < CPL; ++c) o[c] = acc[it][c][r];
             if (i < n)
-                __builtin_nontemporal_store(o, reinterpret_cast<hvec *>(ou + ((uint32_t)i * rv + cw0 + CPL * n16)));
+                __builtin_nontemporal_store(o, reinterpret_cast<hvec *>(ou + ((uint32_t)i * rv + CPL * n16)));
+        }
+}
+
+// Trees of up to 64 nodes on two wavefronts that split H_0's rows: wavefront w loads
+// rows [DK/2 w, DK/2 (w+1)) of the slice (all CW columns, 16-byte loads as above) and
+// forms the H_0 term of every node tile over those rows; the two halves meet in LDS,
+// where each wavefront hands the other the partial sums of the other's node tiles (node
+// tiles 2w, 2w+1 belong to wavefront w). H_0 is read once, with the same full-width row
+// loads as the one-wavefront kernel, and each wavefront then finishes the intra-tree
+// term and the store of its own node tiles. Node tiles past the tree are skipped
+// (wave-uniform); K and V rows are staged per pair of tiles, clamped into the tree, so
+// every V row that a masked (zero) weight meets is finite. Trees with fewer than min_n
+// nodes are left to the one-wavefront kernel (min_n = 33), or taken here as well
+// (min_n = 1, which also writes the status of empty and out-of-range trees).
+template <int DK, int DV>
+__global__ __launch_bounds__(128, 2) void verify_mfma_ksplit_kernel(
+    const LayerTable lt, const int32_t *__restrict__ parent,
+    const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
+    int U, int max_n, int min_n) {
+    constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
+    constexpr int CPL = CW / 16;            // columns per lane: 4 or 2
+    constexpr int G = DV / CW;              // column groups per unit
+    constexpr int KT = DK / 32;             // k-steps of the bf16 products
+    constexpr int KH = KT / 2;              // k-steps of H_0 rows per wavefront
+    constexpr int HSW = 8 * KH;             // H_0 loads per lane (4 rows each per wavefront)
+    constexpr int PPR = DK / 8;             // 16-byte pieces per K row
+    constexpr int VPR = CW / 8;             // 16-byte pieces per V row
+    constexpr int NN = 64;
+    typedef float hvec __attribute__((ext_vector_type(CPL)));
+    typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
+    __shared__ bf16x8 s_k[NN * PPR];        // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR)
+    __shared__ __bf16 s_v[NN * CW];         // V rows of the group's columns, row j at [CW j]
+    __shared__ f32x4 s_x[2][2 * CPL * 64];  // s_x[w]: wavefront w's partials for the other's tiles
+    const bole_layer_t &ly = lt.l[blockIdx.y];
+    const __bf16 *const q = static_cast<const __bf16 *>(ly.q);
+    const __bf16 *const k = static_cast<const __bf16 *>(ly.k);
+    const __bf16 *const v = static_cast<const __bf16 *>(ly.v);
+    const float *const gate = ly.gate;
+    float *const out = ly.out;
+
+    const int lane = lane_id();
+    const int w = (int)(threadIdx.x >> 6);
+    const int n16 = lane & 15, g = lane >> 4;
+    int unit, cg;
+    if (G == 1) {
+        unit = blockIdx.x;
+        cg = 0;
+    } else {
+        const int slot = blockIdx.x >> 3;
+        cg = slot % G;
+        unit = (slot / G) * 8 + (blockIdx.x & 7);
+        if (unit >= U) return;
+    }
+    const int b = unit / H, h = unit - b * H;
+    const int c0 = cg * CW;
+    const bool first = blockIdx.y == 0 && h == 0 && cg == 0;
+    const bool writer = tree_status != nullptr && first && threadIdx.x == 0;
+    const bool all_sizes = min_n <= 1;      // this launch owns every tree's status
+
+    const TreeRange tr = tree_range(node_offsets, b, T, max_n);
+    if (tr.status != BOLE_TREE_OK) {
+        if (writer && all_sizes) tree_status[b] = tr.status;
+        return;
+    }
+    const int n = tr.n;
+    if (n == 0) {
+        if (writer && all_sizes) tree_status[b] = BOLE_TREE_OK;
+        return;
+    }
+    if (n < min_n) return;
+    const int lo = tr.lo, last = n - 1;
+    const int ntl = (n + 15) >> 4;          // node tiles holding nodes
+    const int rows = n > 32 ? 64 : 32;      // K and V rows staged (whole tile pairs)
+    const uint32_t rq = (uint32_t)H * DK, rv = (uint32_t)H * DV;
+    const __bf16 *qu = q + (size_t)lo * rq + (size_t)h * DK;
+    const __bf16 *ku = k + (size_t)lo * rq + (size_t)h * DK;
+    const __bf16 *vu = v + (size_t)lo * rv + (size_t)h * DV + c0;
+    float *ou = out + (size_t)lo * rv + (size_t)h * DV + c0;
+    const float *hu = ly.H0 + (size_t)unit * DK * DV + c0;
+
+    // ---- 1. issue every load. Relative node tile r: r < 2 is own tile 2w + r, r >= 2
+    // the other wavefront's tile 2(1 - w) + r - 2.
+    const uint32_t node = (uint32_t)min(lane, last);
+    const int p_raw = parent[lo + node];
+    const float g_raw = gate[(size_t)lo * H + h + node * (uint32_t)H];
+    // qa[r][tl]: Q fragment of relative tile r at this wavefront's k-step w*KH + tl;
+    // qb[r][tl]: own tile r at the other wavefront's k-step (1 - w)*KH + tl
+    bf16x8 qa[4][KH], qb[2][KH];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int ti = r < 2 ? 2 * w + r : 2 * (1 - w) + r - 2;
+        const __bf16 *qrow = qu + (uint32_t)min(16 * ti + n16, last) * rq + 8 * g;
+#pragma unroll
+        for (int tl = 0; tl < KH; ++tl) {
+            qa[r][tl] = bf16x8{};
+            if (ti < ntl) qa[r][tl] = load16_stream(qrow + 32 * (w * KH + tl));
+            if (r < 2) {
+                qb[r][tl] = bf16x8{};
+                if (ti < ntl) qb[r][tl] = load16_stream(qrow + 32 * ((1 - w) * KH + tl));
+            }
+        }
+    }
+    // K: load s = w + 2u fills LDS slots 64s .. 64s+63 (rows (64/PPR)s ..); V: load s,
+    // rows (64/VPR)s + lane/VPR. Only rows below `rows` are staged.
+    constexpr int KL = NN * PPR / 128, VL = NN * VPR / 128;
+    bf16x8 kst[KL], vst[VL];
+#pragma unroll
+    for (int u = 0; u < KL; ++u) {
+        const int s = w + 2 * u;
+        const int j = (64 / PPR) * s + lane / PPR;
+        const int pc = (lane % PPR) ^ (j % PPR);
+        if ((64 / PPR) * s < rows) kst[u] = load16_stream(ku + ((uint32_t)min(j, last) * rq + 8 * pc));
+    }
+#pragma unroll
+    for (int u = 0; u < VL; ++u) {
+        const int s = w + 2 * u;
+        const int j = (64 / VPR) * s + lane / VPR;
+        if ((64 / VPR) * s < rows)
+            vst[u] = load16_stream(vu + ((uint32_t)min(j, last) * rv + 8 * (lane % VPR)));
+    }
+    // H_0 rows of this wavefront: load s = 8tl + e, lane (n, g): row 32(w*KH + tl) + 8g + e
+    hvec hreg[HSW];
+#pragma unroll
+    for (int s = 0; s < HSW; ++s)
+        hreg[s] = __builtin_nontemporal_load(reinterpret_cast<const hvec *>(
+            hu + ((uint32_t)(32 * (w * KH + (s >> 3)) + 8 * g + (s & 7)) * DV + CPL * n16)));
+#pragma unroll
+    for (int u = 0; u < KL; ++u)
+        if ((64 / PPR) * (w + 2 * u) < rows) s_k[64 * (w + 2 * u) + lane] = kst[u];
+#pragma unroll
+    for (int u = 0; u < VL; ++u)
+        if ((64 / VPR) * (w + 2 * u) < rows)
+            *reinterpret_cast<bf16x8 *>(s_v + 512 * (w + 2 * u) + 8 * lane) = vst[u];
+
+    // ---- 2. topology and base-2 cumulative decay (both wavefronts, same result)
+    const float lg2 = lane < n ? __builtin_amdgcn_logf(g_raw) : 0.f;
+    const WaveTopoL topo = wave_topology_cumlog(p_raw, lg2, n);
+    if (writer) tree_status[b] = topo.bad;
+    if (topo.bad) {
+        for (int i = g + 4 * w; i < n; i += 8)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) ou[(uint32_t)i * rv + CPL * n16 + c] = __builtin_nanf("");
+        return;
+    }
+    const float L2 = topo.L;
+
+    // ---- 3. H_0 term over this wavefront's rows, for every node tile in the tree
+    f32x4 acc[4][CPL];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tl = 0; tl < KH; ++tl) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            bf16x8 bh, bl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                __bf16 xh, xl;
+                split_bf16(hreg[8 * tl + e][c], xh, xl);
+                bh[e] = xh;
+                bl[e] = xl;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ti = r < 2 ? 2 * w + r : 2 * (1 - w) + r - 2;
+                if (ti < ntl) {
+                    acc[r][c] = mfma16_bf16(qa[r][tl], bh, acc[r][c]);
+                    acc[r][c] = mfma16_bf16(qa[r][tl], bl, acc[r][c]);
+                }
+            }
+        }
+    }
+    // hand over the other wavefront's partials (same accumulator layout in both), take ours
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+        if (2 * (1 - w) + r < ntl)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) s_x[w][(r * CPL + c) * 64 + lane] = acc[2 + r][c];
+    __syncthreads();  // also publishes both halves of K and V
+    if (2 * w >= ntl) return;  // no node tile of this wavefront's in the tree
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+        if (2 * w + r < ntl)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[r][c] += s_x[1 - w][(r * CPL + c) * 64 + lane];
+    // row scale 2^{L_i}, node 16ti + 4g + rr
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const float sc = __builtin_amdgcn_exp2f(__shfl(L2, 16 * (2 * w + r) + 4 * g + rr, 64));
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[r][c][rr] *= sc;
+        }
+
+    // ---- 4. intra-tree term for own node tiles, one ancestor tile pair at a time
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int ti = 2 * w + r;               // node tile (wave-uniform)
+        if (ti >= ntl) break;
+        const int i = 16 * ti + n16;            // node of this lane's column
+        const uint64_t mi = shfl_u64(topo.mask, i);
+        const float Li = __shfl(L2, i, 64);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {           // ancestor tile pair (2p, 2p+1)
+            if (2 * p > ti) break;
+            float wv[8];
+#pragma unroll
+            for (int hlf = 0; hlf < 2; ++hlf) {
+                const int jt = 2 * p + hlf;
+                f32x4 st = {0.f, 0.f, 0.f, 0.f};
+                if (jt <= ti) {
+#pragma unroll
+                    for (int t = 0; t < KT; ++t) {
+                        const int j = 16 * jt + n16, pc = 4 * t + g;
+                        const bf16x8 qq = (t / KH == w) ? qa[r][t % KH] : qb[r][t % KH];
+                        st = mfma16_bf16(s_k[j * PPR + (pc ^ (j % PPR))], qq, st);
+                    }
+                }
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int j = 16 * jt + 4 * g + rr;
+                    const bool anc = jt <= ti && ((mi >> j) & 1ull);
+                    const float d = __builtin_amdgcn_exp2f(Li - __shfl(L2, j, 64));
+                    wv[4 * hlf + rr] = anc ? st[rr] * d : 0.f;
+                }
+            }
+            bf16x8 wh, wl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                __bf16 xh, xl;
+                split_bf16(wv[e], xh, xl);
+                wh[e] = xh;
+                wl[e] = xl;
+            }
+            bf16x8 vb[CPL];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = 32 * p + (e < 4 ? 4 * g + e : 12 + 4 * g + e);
+                const vvec x = *reinterpret_cast<const vvec *>(s_v + j * CW + CPL * n16);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) vb[c][e] = x[c];
+            }
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                acc[r][c] = mfma16_bf16(wh, vb[c], acc[r][c]);
+                acc[r][c] = mfma16_bf16(wl, vb[c], acc[r][c]);
+            }
+        }
+    }
+
+    // ---- 5. store own node tiles: node 16ti + 4g + rr, columns CPL*n ..
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int i = 16 * (2 * w + r) + 4 * g + rr;
+            hvec o;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) o[c] = acc[r][c][rr];
+            if (i < n)
+                __builtin_nontemporal_store(o, reinterpret_cast<hvec *>(ou + ((uint32_t)i * rv + CPL * n16)));
         }
 }
 
@@ -486,14 +735,14 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
     for (int l = 0; l < nl; ++l) lt.l[l] = layers[l];
     const LazyCommit none = {};
     if (lazy)
-        verify_mfma_tree_kernel<DK, DV, 1, true><<<grid, dim3(64), 0, stream>>>(
+        verify_mfma_tree_kernel<DK, DV, true><<<grid, dim3(64), 0, stream>>>(
             lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, *lazy);
     else
-        verify_mfma_tree_kernel<DK, DV, 1, false><<<grid, dim3(64), 0, stream>>>(
+        verify_mfma_tree_kernel<DK, DV, false><<<grid, dim3(64), 0, stream>>>(
             lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, none);
     if (max_n > 32)
-        verify_mfma_tree_kernel<DK, DV, 2, false><<<grid, dim3(128), 0, stream>>>(
-            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, none);
+        verify_mfma_ksplit_kernel<DK, DV><<<grid, dim3(128), 0, stream>>>(
+            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, 33);
 }
 
 template <int DK>
