@@ -311,6 +311,37 @@ def test_determinism(bole):
     np.testing.assert_array_equal(Ha, Hb)
 
 
+def test_large_trees_are_ordered_on_the_callers_stream(bole):
+    """Trees of 33..64 nodes are verified by a second launch; work queued on the caller's
+    stream after the call must see every row of both. On a side torch stream: verify, copy
+    out and the statuses on that stream, then synchronise that stream alone. The copies
+    equal a fully synchronised call bit for bit, and sampled sequences match the oracle."""
+    sizes = [64, 3, 64, 40, 17, 64, 33, 1] * 8
+    wl = W.make_random(41, batch=len(sizes), heads=8, d_k=128, d_v=64, sizes=sizes)
+    t = to_dev(wl)
+    ref, ref_status = gpu_verify(bole, t)
+    s = torch.cuda.Stream()
+    B = len(sizes)
+    for _ in range(3):
+        with torch.cuda.stream(s):
+            out = torch.full(ref.shape, float("nan"), dtype=torch.float32, device=dev())
+            status = torch.full((B,), -7, dtype=torch.int32, device=dev())
+            bole.bole_tree_verify(t["H0"], t["q"], t["k"], t["v"], t["gate"], t["parent"],
+                                  t["offs"], out=out, tree_status=status, stream=s)
+            out_copy, status_copy = out.clone(), status.clone()
+        s.synchronize()
+        np.testing.assert_array_equal(out_copy.double().cpu().numpy(), ref)
+        np.testing.assert_array_equal(status_copy.cpu().numpy(), ref_status)
+    assert (ref_status == 0).all()
+    sample = [0, 2, 3, 6]
+    sub = subset(wl, 0, sample)
+    lay = sub.layers[0]
+    want, _ = oracle.verify_serial(lay.H0.double().numpy(), lay.q, lay.k, lay.v, lay.gate,
+                                   sub.parent, sub.node_offsets, False)
+    rows = np.concatenate([np.arange(wl.node_offsets[b], wl.node_offsets[b + 1]) for b in sample])
+    assert rel_err_rows(ref[rows], want) <= TOL[torch.bfloat16]
+
+
 def test_bound_launchers_match_calls(bole):
     """bind_tree_verify / bind_commit_path launch exactly what the plain calls launch:
     bit-identical outputs, and a bound commit called twice applies the path twice."""
