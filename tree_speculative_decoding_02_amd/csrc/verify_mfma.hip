@@ -443,7 +443,7 @@ __global__ __launch_bounds__(64, 2) void verify_mfma_tree_kernel(
 // nodes are left to the one-wavefront kernel (min_n = 33), or taken here as well
 // (min_n = 1, which also writes the status of empty and out-of-range trees).
 template <int DK, int DV>
-__global__ __launch_bounds__(128, 2) void verify_mfma_ksplit_kernel(
+__global__ __launch_bounds__(128, 3) void verify_mfma_ksplit_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
     int U, int max_n, int min_n) {
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(128, 2) void verify_mfma_ksplit_kernel(
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
     __shared__ bf16x8 s_k[NN * PPR];        // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR)
     __shared__ __bf16 s_v[NN * CW];         // V rows of the group's columns, row j at [CW j]
-    __shared__ f32x4 s_x[2][2 * CPL * 64];  // s_x[w]: wavefront w's partials for the other's tiles
+    __shared__ f32x4 s_x[2 * CPL * 64];     // partials handed from one wavefront to the other
     const bole_layer_t &ly = lt.l[blockIdx.y];
     const __bf16 *const q = static_cast<const __bf16 *>(ly.q);
     const __bf16 *const k = static_cast<const __bf16 *>(ly.k);
@@ -514,7 +514,8 @@ __global__ __launch_bounds__(128, 2) void verify_mfma_ksplit_kernel(
     const int p_raw = parent[lo + node];
     const float g_raw = gate[(size_t)lo * H + h + node * (uint32_t)H];
     // qa[r][tl]: Q fragment of relative tile r at this wavefront's k-step w*KH + tl;
-    // qb[r][tl]: own tile r at the other wavefront's k-step (1 - w)*KH + tl
+    // qb[r][tl] (loaded after the H_0 term, which does not need it): own tile r at the
+    // other wavefront's k-step (1 - w)*KH + tl
     bf16x8 qa[4][KH], qb[2][KH];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -524,10 +525,6 @@ __global__ __launch_bounds__(128, 2) void verify_mfma_ksplit_kernel(
         for (int tl = 0; tl < KH; ++tl) {
             qa[r][tl] = bf16x8{};
             if (ti < ntl) qa[r][tl] = load16_stream(qrow + 32 * (w * KH + tl));
-            if (r < 2) {
-                qb[r][tl] = bf16x8{};
-                if (ti < ntl) qb[r][tl] = load16_stream(qrow + 32 * ((1 - w) * KH + tl));
-            }
         }
     }
     // K: load s = w + 2u fills LDS slots 64s .. 64s+63 (rows (64/PPR)s ..); V: load s,
@@ -602,19 +599,38 @@ __global__ __launch_bounds__(128, 2) void verify_mfma_ksplit_kernel(
             }
         }
     }
-    // hand over the other wavefront's partials (same accumulator layout in both), take ours
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-        if (2 * (1 - w) + r < ntl)
+    for (int r = 0; r < 2; ++r) {
+        const int ti = 2 * w + r;
+        const __bf16 *qrow = qu + (uint32_t)min(16 * ti + n16, last) * rq + 8 * g;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) s_x[w][(r * CPL + c) * 64 + lane] = acc[2 + r][c];
-    __syncthreads();  // also publishes both halves of K and V
+        for (int tl = 0; tl < KH; ++tl) {
+            qb[r][tl] = bf16x8{};
+            if (ti < ntl) qb[r][tl] = load16_stream(qrow + 32 * ((1 - w) * KH + tl));
+        }
+    }
+    // hand the other wavefront its partials (same accumulator layout in both) and take
+    // ours, through one region in two phases: wavefront 1 hands over tiles 0 and 1, then
+    // wavefront 0 tiles 2 and 3
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+        const int src = 1 - ph;               // the wavefront writing in this phase
+        if (w == src)
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                if (2 * ph + r < ntl)
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) s_x[(r * CPL + c) * 64 + lane] = acc[2 + r][c];
+        __syncthreads();  // (the first also publishes both halves of K and V)
+        if (w != src)
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                if (2 * ph + r < ntl)
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) acc[r][c] += s_x[(r * CPL + c) * 64 + lane];
+        if (ph == 0) __syncthreads();  // read before the second phase overwrites
+    }
     if (2 * w >= ntl) return;  // no node tile of this wavefront's in the tree
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-        if (2 * w + r < ntl)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[r][c] += s_x[1 - w][(r * CPL + c) * 64 + lane];
     // row scale 2^{L_i}, node 16ti + 4g + rr
 #pragma unroll
     for (int r = 0; r < 2; ++r)
