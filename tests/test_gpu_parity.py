@@ -193,6 +193,12 @@ EDGE = [
     ("dk128_dv32", dict(batch=4, heads=3, d_k=128, d_v=32)),
     ("dk64_dv64", dict(batch=4, heads=3, d_k=64, d_v=64, sizes=[32, 17, 16, 5])),
     ("trees_up_to_32", dict(batch=8, heads=4, d_k=128, d_v=64, sizes=[16, 15, 9, 3, 17, 24, 31, 32])),
+    # trees of 33..64 nodes around the 16-node tile boundaries (the row-split kernel skips
+    # node tiles past the tree), with d_k = 64 (one k-step per wavefront) and d_v = 128
+    # (two column groups)
+    ("big_tree_tiles_dk64", dict(batch=5, heads=3, d_k=64, d_v=64, sizes=[33, 48, 49, 64, 47], kind="deep", max_path=64)),
+    ("big_tree_tiles_dv128", dict(batch=5, heads=2, d_k=128, d_v=128, sizes=[33, 48, 49, 64, 17])),
+    ("big_tree_tiles_dv32", dict(batch=4, heads=3, d_k=128, d_v=32, sizes=[64, 33, 50, 2], kind="bestfirst")),
     # long accepted paths: commit stages the path's factors in several rounds
     ("long_paths_bf16", dict(batch=4, heads=2, d_k=128, d_v=64, sizes=[64, 48, 40, 33], kind="chain", max_path=64)),
     ("long_paths_fp32", dict(batch=4, heads=2, d_k=128, d_v=64, sizes=[64, 40, 24, 20], kind="chain", factor_dtype=torch.float32, max_path=64)),
