@@ -14,8 +14,10 @@
 //    rejections rp(y) = max(p(y) A - q(y) C, 0) (a clamp at 0 never releases, so the
 //    step-by-step residual has this closed form), with A, C, Zq updated per rejection of
 //    x as A <- A / Zp, C <- C / Zp + 1 / Zq, Zq <- Zq - q(x), and Zp the sum of the new
-//    rp: one pass over the node's two fp32 rows. The bonus is drawn from rp by inverse
-//    CDF. fp64 throughout, products and differences separately rounded.
+//    rp: one pass over the node's two fp32 rows (16-byte loads). The bonus is drawn from
+//    rp by inverse CDF over tiles of 4 elements per thread: per-wavefront tile sums,
+//    walked in order until the running sum passes the threshold, then a block-wide prefix
+//    sum inside that tile. fp64 throughout, products and differences separately rounded.
 #include "bole_device.h"
 #include "launch.h"
 
@@ -30,8 +32,21 @@ struct AcceptArgs {
     const int32_t *parent, *token, *node_offsets;
     int32_t *accepted_idx, *accepted_len, *bonus, *tree_status;
     int B, T, V, max_path, mode;
-    bool vec;  // fp32 rows are 16-byte aligned (V % 4 == 0 and aligned bases)
+    bool vec;   // target rows are 16-byte aligned (V % 4 == 0 and aligned bases)
+    bool vecq;  // so are the draft rows
 };
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Elements y .. y+3 of an fp32 row (y a multiple of 4; values past V are unspecified):
+// one 16-byte load when the row allows it.
+__device__ __forceinline__ f4 load4(const float *row, int y, int V, bool vec) {
+    if (vec) return __builtin_nontemporal_load(reinterpret_cast<const f4 *>(row + min(y, V - 4)));
+    f4 x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = row[min(y + c, V - 1)];
+    return x;
+}
 
 // Calls f(y, value) for the elements of an fp32 row this thread owns, in increasing y.
 // Loads are issued kAcceptBatch at a time before any is used.
@@ -70,6 +85,30 @@ __device__ __forceinline__ void row_pass(const float *row, int V, bool vec, F f)
     }
 }
 
+// Calls f(y, p(y), q(y)) for the elements of two fp32 rows this thread owns, in
+// increasing y; kAcceptBatch / 4 16-byte loads of each row in flight.
+template <typename F>
+__device__ __forceinline__ void row_pass2(const float *prow, const float *qrow, int V, bool vec,
+                                          F f) {
+    constexpr int NB = kAcceptBatch / 4;
+    constexpr int step = 4 * kAcceptThreads;
+    for (int y0 = 4 * threadIdx.x; y0 < V; y0 += step * NB) {
+        f4 px[NB], qx[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            px[u] = load4(prow, y0 + u * step, V, vec);
+            qx[u] = load4(qrow, y0 + u * step, V, vec);
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int y = y0 + u * step;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (y + c < V) f(y + c, px[u][c], qx[u][c]);
+        }
+    }
+}
+
 // rp(y) = max(p(y) A - q(y) C, 0), each product and the difference rounded on its own
 __device__ __forceinline__ double residual(float p, float q, double A, double C) {
     return fmax(__dsub_rn(__dmul_rn((double)p, A), __dmul_rn((double)q, C)), 0.0);
@@ -88,9 +127,34 @@ __device__ __forceinline__ double block_sum_d(double x, double *s_red) {
     return t;
 }
 
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Inclusive prefix sum over the wavefront's lanes, in lane order.
+__device__ __forceinline__ double wave_scan_d(double x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// The bonus search works on tiles of kTile elements, 4 per thread; tile sums are formed
+// per wavefront and kept for kTileGroup tiles at a time.
+constexpr int kTile = 4 * kAcceptThreads;
+constexpr int kTileGroup = 32;
+constexpr int kTileBatch = kAcceptBatch / 4;
+
 __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs a) {
     __shared__ double s_red[kAcceptWaves];
-    __shared__ double s_scan[kAcceptThreads];
+    __shared__ double s_tw[kAcceptWaves][kTileGroup];
+    __shared__ double s_before;
+    __shared__ int s_tile;
     __shared__ float s_bv[kAcceptWaves];
     __shared__ int s_bi[kAcceptWaves];
     __shared__ int s_par[kMaxTree], s_tok[kMaxTree];
@@ -207,18 +271,8 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
             C = C / Zp + 1.0 / Zq;
             Zq = Zq - (double)qx;
             double part = 0.0;
-            for (int y0 = t; y0 < V; y0 += kAcceptThreads * kAcceptBatch) {
-                float py[kAcceptBatch], qy[kAcceptBatch];
-#pragma unroll
-                for (int u2 = 0; u2 < kAcceptBatch; ++u2) {
-                    const int y = min(y0 + u2 * kAcceptThreads, V - 1);
-                    py[u2] = __builtin_nontemporal_load(prow + y);
-                    qy[u2] = __builtin_nontemporal_load(qrow + y);
-                }
-#pragma unroll
-                for (int u2 = 0; u2 < kAcceptBatch; ++u2)
-                    if (y0 + u2 * kAcceptThreads < V) part += residual(py[u2], qy[u2], A, C);
-            }
+            row_pass2(prow, qrow, V, a.vec && a.vecq,
+                      [&](int, float py, float qy) { part += residual(py, qy, A, C); });
             Zp = block_sum_d(part, s_red);
             ++k;
         }
@@ -228,37 +282,104 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
             cur = acc;
             continue;
         }
-        // bonus: smallest y with cumsum(rp)[y] > u * total; thread t owns a contiguous
-        // chunk, the chunk sums are scanned in thread order
-        const int chunk = (V + kAcceptThreads - 1) / kAcceptThreads;
-        const int y0 = min(V, t * chunk), y1 = min(V, y0 + chunk);
-        double cs = 0.0;
-#pragma unroll 8
-        for (int y = y0; y < y1; ++y) cs += k == 0 ? (double)prow[y] : residual(prow[y], qrow[y], A, C);
-        s_scan[t] = cs;
-        __syncthreads();
-        for (int off = 1; off < kAcceptThreads; off <<= 1) {
-            const double v = t >= off ? s_scan[t - off] : 0.0;
-            __syncthreads();
-            s_scan[t] += v;
-            __syncthreads();
+        // bonus: smallest y with cumsum(rp)[y] > u * total (total = sum(p) at a fresh
+        // node, else Zp). Tiles of kTile elements in order: per-wavefront tile sums, and
+        // thread 0 walks the tile sums until the running sum passes the threshold; inside
+        // that tile, a block-wide prefix sum in thread order finds the element.
+        const bool withq = k > 0;
+        auto rval = [&](float p, float q) -> double { return withq ? residual(p, q, A, C) : (double)p; };
+        double total = Zp;
+        if (!withq) {
+            double part = 0.0;
+            row_pass(prow, V, a.vec, [&](int, float x) { part += (double)x; });
+            total = block_sum_d(part, s_red);
         }
-        const double total = k == 0 ? s_scan[kAcceptThreads - 1] : Zp;
         const double thr = (double)a.u_bonus[b] * total;
-        if (t == 0) s_pick = V - 1;
-        __syncthreads();
-        double run = t > 0 ? s_scan[t - 1] : 0.0;  // exclusive prefix of this chunk
-        if (run <= thr) {
-            for (int y = y0; y < y1; ++y) {
-                run += k == 0 ? (double)prow[y] : residual(prow[y], qrow[y], A, C);
-                if (run > thr) {
-                    atomicMin(&s_pick, y);
-                    break;
+        const int ntiles = (V + kTile - 1) / kTile;
+        if (t == 0) {
+            s_before = 0.0;
+            s_tile = -1;
+            s_pick = V - 1;  // the last y if rounding leaves no crossing
+        }
+        int tile = -1;
+        for (int g0 = 0; g0 < ntiles; g0 += kTileGroup) {
+            const int gn = min(kTileGroup, ntiles - g0);
+            for (int j0 = 0; j0 < gn; j0 += kTileBatch) {
+                f4 pv[kTileBatch], qv[kTileBatch];
+#pragma unroll
+                for (int u = 0; u < kTileBatch; ++u) {
+                    const int y = (g0 + j0 + u) * kTile + 4 * t;
+                    pv[u] = load4(prow, y, V, a.vec);
+                    qv[u] = withq ? load4(qrow, y, V, a.vecq) : f4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int u = 0; u < kTileBatch; ++u) {
+                    if (j0 + u >= gn) break;  // uniform
+                    const int y = (g0 + j0 + u) * kTile + 4 * t;
+                    double sv = 0.0;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (y + c < V) sv += rval(pv[u][c], qv[u][c]);
+                    sv = wave_sum_d(sv);
+                    if (lane == 0) s_tw[wave][j0 + u] = sv;
                 }
             }
-        } else if (cs > 0.0) {
-            atomicMin(&s_pick, y0);  // the first chunk past the threshold, should rounding
-        }                            // hide the crossing from the chunk before it
+            __syncthreads();
+            if (t == 0) {
+                double run = s_before;
+                for (int jj = 0; jj < gn; ++jj) {
+                    double S = 0.0;
+                    for (int w = 0; w < kAcceptWaves; ++w) S += s_tw[w][jj];
+                    if (run + S > thr) {
+                        s_tile = g0 + jj;
+                        break;
+                    }
+                    run += S;
+                }
+                s_before = run;  // the sum over the tiles before the crossing one
+            }
+            __syncthreads();
+            tile = s_tile;
+            if (tile >= 0) break;  // uniform
+        }
+        if (tile >= 0) {
+            const int y = tile * kTile + 4 * t;
+            const f4 pv = load4(prow, y, V, a.vec);
+            const f4 qv = withq ? load4(qrow, y, V, a.vecq) : f4{0.f, 0.f, 0.f, 0.f};
+            double e[4], sv = 0.0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                e[c] = y + c < V ? rval(pv[c], qv[c]) : 0.0;
+                sv += e[c];
+            }
+            const double incl = wave_scan_d(sv);
+            double wex = __shfl_up(incl, 1, 64);
+            if (lane == 0) wex = 0.0;
+            if (lane == 63) s_red[wave] = incl;
+            __syncthreads();
+            double run = s_before;
+            for (int w = 0; w < wave; ++w) run += s_red[w];
+            run += wex;  // the sum over every element before this thread's first
+            if (run <= thr) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    run += e[c];
+                    if (run > thr) {
+                        atomicMin(&s_pick, y + c);
+                        break;
+                    }
+                }
+            } else {
+                // the crossing fell before this thread, hidden by rounding from the one
+                // holding it: its first positive element
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (e[c] > 0.0) {
+                        atomicMin(&s_pick, y + c);
+                        break;
+                    }
+            }
+        }
         __syncthreads();
         bonus = s_pick;
         break;
@@ -298,6 +419,8 @@ hipError_t launch_tree_accept(const float *p_ctx, const float *p_node, const flo
     a.mode = d.mode;
     a.vec = d.vocab % 4 == 0 &&
             ((reinterpret_cast<uintptr_t>(p_ctx) | reinterpret_cast<uintptr_t>(p_node)) % 16) == 0;
+    a.vecq = d.vocab % 4 == 0 && q_ctx && q_node &&
+             ((reinterpret_cast<uintptr_t>(q_ctx) | reinterpret_cast<uintptr_t>(q_node)) % 16) == 0;
     tree_accept_kernel<<<dim3((unsigned)d.batch), dim3(kAcceptThreads), 0, stream>>>(a);
     return hipGetLastError();
 }
