@@ -440,7 +440,9 @@ def calibrate_verify_cost(bole, W, wl, dev, stream, timed, sizes=(1, 4, 8, 16, 3
 def config_sweep(dev, reps=20):
     """Verify and commit on each workload, one layer: the layer's state is copied into 8
     buffers and the 8 launches of one kind are timed with one event pair (divided by 8).
-    No flags: a caller without a known tree budget takes the general launch."""
+    No flags: a caller without a known tree budget takes the general launch. Workloads
+    whose trees have at most 32 nodes are also timed as a caller with that budget runs
+    them (BOLE_FLAG_TREES_LE_32: one launch), under "verify_budget32"."""
     import numpy as np
     import torch
 
@@ -464,6 +466,10 @@ def config_sweep(dev, reps=20):
                                                      stream=stream) for H in Hs]}
         s_f = 2 if lay.q.dtype == torch.bfloat16 else 4
         nbytes = {"verify": verify_bytes(wl, s_f), "commit": commit_bytes(wl, s_f)}
+        if int(np.diff(wl.node_offsets).max()) <= 32:
+            launches["verify_budget32"] = [bole.bind_tree_verify(
+                H, q, k, v, gate, par, offs, out, stream=stream, trees_le_32=True) for H in Hs]
+            nbytes["verify_budget32"] = nbytes["verify"]
         rec = {"kind": "config_sweep", "config": cid, "workload": names[cid], "batch": wl.batch,
                "heads": wl.heads, "d_k": wl.d_k, "d_v": wl.d_v, "total_nodes": wl.total_nodes,
                "vector_gate": bool(wl.vector_gate), "factor_dtype": str(lay.q.dtype)}
