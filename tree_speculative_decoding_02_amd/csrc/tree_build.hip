@@ -80,14 +80,15 @@ __device__ __forceinline__ void wave_merge64(uint32_t &k, int &i, uint32_t nk, i
 // elements at or above a running threshold theta are gathered into an LDS candidate
 // buffer. theta starts as the smallest, over the wavefronts, of the wavefront's 16th
 // largest thread maximum in the first chunk (at least 64 elements reach it), and rises
-// after the first chunk and whenever the buffer passes half full: it becomes the exact
-// 64th largest buffered key (a 32-step bitwise search) and the candidates below it are
-// dropped. theta never
-// exceeds the 64th largest key seen so far, so the buffer always holds the top 64. The
+// after the first chunk and whenever the buffer passes half full: it becomes the 64th
+// largest buffered key resolved to its top kThetaBits bits (a bitwise search, one barrier
+// a bit), and the candidates below it are dropped. theta never exceeds the 64th largest
+// key seen so far, so the buffer always holds the top 64. The
 // last step counts each candidate's rank and writes ranks below 64 in place. If one
 // chunk leaves more than kGatherCap candidates (many equal values at theta), 64 rounds
 // of block-wide extraction over the slice, read again, give the same list.
 constexpr int kChunkPerThread = 16;
+constexpr int kThetaBits = 16;  // key bits resolved by a compaction's threshold search
 constexpr int kChunk = kBuildThreads * kChunkPerThread;  // 4096 elements
 
 template <int W>
@@ -196,7 +197,10 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
         if (cnt > kGatherCap) return false;
         if (cnt > kGatherCap / 2 || (c0 == lo && cnt > kTopK) ||
             (c0 + kChunk >= hi && cnt > 2 * kTopK)) {
-            // theta <- the exact 64th largest buffered key; keep the candidates >= it
+            // theta <- the 64th largest buffered key, resolved to its top kThetaBits bits
+            // (so never above it: the buffer keeps the top 64, plus the few keys that share
+            // that prefix below them; the final ranks are exact either way); keep the
+            // candidates >= it
             uint32_t bk[kGatherCap / kBuildThreads];
 #pragma unroll
             for (int r = 0; r < kGatherCap / kBuildThreads; ++r) {
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
                 bk[r] = x2 < cnt ? s_k[buf][x2] : 0u;
             }
             uint32_t th = 0u;
-            for (int bit = 31; bit >= 0; --bit) {
+            for (int bit = 31; bit >= 32 - kThetaBits; --bit) {
                 const uint32_t cand = th | (1u << bit);
                 int wc = 0;
 #pragma unroll
