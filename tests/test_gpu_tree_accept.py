@@ -89,6 +89,10 @@ CASES = [
     ("vocab_32000", 8, 32000, [32] * 8, "bestfirst", 16),
     ("ragged_random", 12, 3000, [0, 1, 5, 64, 33, 2, 17, 8, 9, 40, 3, 12], "random", 64),
     ("truncated_paths", 6, 200, [20] * 6, "chain", 3),
+    # more than 32 tiles of 4096 tokens: the bonus search carries its running sum from
+    # one group of tile sums to the next (16-byte loads, and element loads for an odd V)
+    ("two_tile_groups", 4, 150000, [12] * 4, "deep", 16),
+    ("two_tile_groups_unaligned", 4, 140001, [12] * 4, "chain", 16),
 ]
 
 
@@ -105,6 +109,24 @@ def test_accept_matches_oracle(bole, mode, name, B, V, sizes, kind, max_path):
         np.testing.assert_array_equal(got[k][clear], ref[k][clear], err_msg=k)
     # several nodes accepted somewhere: the walk really descends
     assert ref["accepted_len"].max() >= (3 if max_path >= 3 else max_path)
+
+
+@pytest.mark.parametrize("V", [150000, 140001])
+def test_sampled_bonus_past_the_first_tile_group(bole, V):
+    """Bonus uniforms near 1 put every crossing past the first 32 tiles of 4096 tokens,
+    so the bonus search must carry its running sum into the next group of tile sums.
+    Bit-exact against the oracle where the decision margins are clear."""
+    B = 5
+    c = make_case(77 + V % 7, B, V, [10] * B, "chain")
+    c["u_bonus"] = np.array([0.9990, 0.9995, 0.99995, 0.9999, 0.99999], np.float32)
+    got, ref = run(bole, c, 16, True)
+    np.testing.assert_array_equal(got["status"], ref["status"])
+    clear = ref["margin"] > 1e-9
+    assert clear.sum() >= B - 1, ref["margin"]
+    for k in ("accepted_idx", "accepted_len", "bonus"):
+        np.testing.assert_array_equal(got[k][clear], ref[k][clear], err_msg=k)
+    # the drawn tokens lie in the second group of tiles for most trees
+    assert (ref["bonus"] >= 32 * 4096).sum() >= 3, ref["bonus"]
 
 
 def test_accept_bad_trees(bole):
