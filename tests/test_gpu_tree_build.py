@@ -60,6 +60,10 @@ CASES = [
     ("budget_17", 6, 4, 5000, 17, {}, 0.02),
     ("many_ties", 4, 5, 20000, 64, dict(grid=2.0 ** -12), 0.05),
     ("flat_logits_many_ties", 2, 3, 50000, 64, dict(logit_std=0.0), 0.05),
+    # nearly flat rows: the top keys lie within the threshold search's 16-bit resolution,
+    # so compactions keep many candidates (and may take the block-wide extraction path)
+    ("near_flat_logits", 2, 3, 60000, 64, dict(logit_std=0.002), 0.05),
+    ("slightly_flat_logits", 2, 3, 60000, 64, dict(logit_std=0.05), 0.05),
     ("vocab_10", 3, 3, 10, 64, {}, 0.01),
     ("vocab_1_chain", 2, 5, 1, 64, {}, 0.01),
     ("large_batch_pack", 2500, 2, 64, 8, {}, 0.05),
