@@ -323,31 +323,31 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
     }
 }
 
-// Best offer over the wavefront, in every lane. An offer is packed into one 64-bit key
-// that is larger when better: the high word is the score's bits + 1 (scores are >= +0,
-// so this orders them; 0 means no offer), the low word is ~(source + 1) (the context is
-// source -1), so equal scores go to the earlier source. DPP reduction toward lane 63
-// (row_shr 1, 2, 4, 8 within each row of 16, then row_bcast 15 and 31 across rows);
-// lanes whose DPP source is outside the row or masked keep key 0.
+// Best offer over the wavefront. An offer's key is the score's bits + 1 (scores are
+// >= +0, so this orders them; 0 means no offer). The largest key comes from a DPP maximum
+// toward lane 63 (row_shr 1, 2, 4, 8 within each row of 16, then row_bcast 15 and 31
+// across rows; lanes whose DPP source is outside the row or masked contribute 0); equal
+// scores go to the earlier source, the context (source -1, lane 63) first, by a ballot.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void keymax_dpp_step(uint32_t &hi, uint32_t &lo) {
-    const uint32_t ph = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, ROW_MASK, 0xf, false);
-    const uint32_t pl = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, ROW_MASK, 0xf, false);
-    const uint64_t p = ((uint64_t)ph << 32) | pl, m = ((uint64_t)hi << 32) | lo;
-    const bool take = p > m;
-    hi = take ? ph : hi;
-    lo = take ? pl : lo;
+__device__ __forceinline__ void max_dpp_step(uint32_t &x) {
+    const uint32_t p = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, false);
+    x = max(x, p);
 }
 
-__device__ __forceinline__ void wave_keymax(uint32_t &hi, uint32_t &lo) {
-    keymax_dpp_step<0x111, 0xf>(hi, lo);  // row_shr:1
-    keymax_dpp_step<0x112, 0xf>(hi, lo);  // row_shr:2
-    keymax_dpp_step<0x114, 0xf>(hi, lo);  // row_shr:4
-    keymax_dpp_step<0x118, 0xf>(hi, lo);  // row_shr:8
-    keymax_dpp_step<0x142, 0xa>(hi, lo);  // row_bcast:15 into rows 1 and 3
-    keymax_dpp_step<0x143, 0xc>(hi, lo);  // row_bcast:31 into rows 2 and 3
-    hi = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
-    lo = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+// The best key (wave-uniform) and its source's lane: lane 63 when the context offers
+// it, else the lowest lane that does.
+__device__ __forceinline__ uint32_t wave_bestkey(uint32_t key, int &best_lane) {
+    uint32_t x = key;
+    max_dpp_step<0x111, 0xf>(x);  // row_shr:1
+    max_dpp_step<0x112, 0xf>(x);  // row_shr:2
+    max_dpp_step<0x114, 0xf>(x);  // row_shr:4
+    max_dpp_step<0x118, 0xf>(x);  // row_shr:8
+    max_dpp_step<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    max_dpp_step<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+    const uint32_t best = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    const uint64_t at = __ballot(key == best);
+    best_lane = (at >> 63) ? 63 : __builtin_ctzll(at);
+    return best;
 }
 
 // ---- 2. best-first tree and controller, one wavefront per sequence
@@ -415,13 +415,12 @@ __global__ __launch_bounds__(256) void build_kernel(
         const bool is_src = lane < n || lane == 63;
         const bool offer = is_src && cur >= 0.f;
         const float sc = __fmul_rn(src_rho, cur);
-        uint32_t khi = offer ? __float_as_uint(sc) + 1u : 0u;
-        uint32_t klo = ~(uint32_t)((lane == 63 ? -1 : lane) + 1);
-        wave_keymax(khi, klo);
-        if (khi == 0u) break;  // no source offers a child (wave-uniform)
-        const float bs = __uint_as_float(khi - 1u);
-        const int bw = (int)(~klo) - 1;  // the winning source: -1 for the context
-        const int wl = bw < 0 ? 63 : bw;  // the winning source's lane
+        const uint32_t key = offer ? __float_as_uint(sc) + 1u : 0u;
+        int wl;  // the winning source's lane
+        const uint32_t best = wave_bestkey(key, wl);
+        if (best == 0u) break;  // no source offers a child (wave-uniform)
+        const float bs = __uint_as_float(best - 1u);
+        const int bw = wl == 63 ? -1 : wl;  // the winning source: -1 for the context
         const int wd = __builtin_amdgcn_readlane(src_depth, wl);
         const int wr = __builtin_amdgcn_readlane(src_rank, wl);
         if (lane == wl) {
