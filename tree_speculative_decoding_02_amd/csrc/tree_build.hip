@@ -447,25 +447,23 @@ __global__ __launch_bounds__(256) void build_kernel(
     }
     const int built = n;
 
-    // controller: A_hat summed in insertion order, S(N) = A_hat(N) * L_AR / C(N)
+    // controller: A_hat summed in insertion order, S(N) = A_hat(N) * L_AR / C(N). The sum
+    // runs serially (its order fixes the rounding); lane N - 1 keeps A_hat(N), and every
+    // S(N) is then formed at once. The tree keeps N - 1 nodes at the first N > 1 with
+    // S(N) < S(N - 1) (all of them under a fixed budget).
     int keep = built;
     float s_keep = 0.f;
     if (built > 0 && cost != nullptr) {
-        float A = 0.f, s_prev = 0.f;
-        bool stopped = false;
+        float A = 0.f, a_lane = 0.f;
         for (int N = 1; N <= built; ++N) {
             A = __fadd_rn(A, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(o_rho), N - 1)));
-            const float cN = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c_lane), N - 1));
-            const float sN = __fdiv_rn(__fmul_rn(A, l_ar), cN);
-            if (N > 1 && !fixed && sN < s_prev) {
-                keep = N - 1;
-                stopped = true;
-                break;
-            }
-            s_prev = sN;
+            if (lane == N - 1) a_lane = A;
         }
-        s_keep = s_prev;  // S at the kept size
-        (void)stopped;
+        const float s_lane = __fdiv_rn(__fmul_rn(a_lane, l_ar), c_lane);  // S(lane + 1)
+        const float s_before = __shfl_up(s_lane, 1, 64);                   // S(lane)
+        const uint64_t drop = __ballot(!fixed && lane >= 1 && lane < built && s_lane < s_before);
+        if (drop) keep = __builtin_ctzll(drop);  // S(keep + 1) < S(keep): keep nodes 0 .. keep - 1
+        s_keep = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lane), keep - 1));  // S at the kept size
     }
     if (lane < keep) {
         par_out[(size_t)b * n_max + lane] = o_par;
