@@ -439,14 +439,13 @@ __global__ __launch_bounds__(64, 2) void verify_mfma_tree_kernel(
 // loads as the one-wavefront kernel, and each wavefront then finishes the intra-tree
 // term and the store of its own node tiles. Node tiles past the tree are skipped
 // (wave-uniform); K and V rows are staged per pair of tiles, clamped into the tree, so
-// every V row that a masked (zero) weight meets is finite. Trees with fewer than min_n
-// nodes are left to the one-wavefront kernel (min_n = 33), or taken here as well
-// (min_n = 1, which also writes the status of empty and out-of-range trees).
+// every V row that a masked (zero) weight meets is finite. Every other tree, and the
+// status of out-of-range trees, is the one-wavefront kernel's.
 template <int DK, int DV>
 __global__ __launch_bounds__(128, 3) void verify_mfma_ksplit_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
-    int U, int max_n, int min_n) {
+    int U, int max_n) {
     constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
     constexpr int CPL = CW / 16;            // columns per lane: 4 or 2
     constexpr int G = DV / CW;              // column groups per unit
@@ -485,19 +484,10 @@ __global__ __launch_bounds__(128, 3) void verify_mfma_ksplit_kernel(
     const int c0 = cg * CW;
     const bool first = blockIdx.y == 0 && h == 0 && cg == 0;
     const bool writer = tree_status != nullptr && first && threadIdx.x == 0;
-    const bool all_sizes = min_n <= 1;      // this launch owns every tree's status
 
     const TreeRange tr = tree_range(node_offsets, b, T, max_n);
-    if (tr.status != BOLE_TREE_OK) {
-        if (writer && all_sizes) tree_status[b] = tr.status;
-        return;
-    }
+    if (tr.status != BOLE_TREE_OK || tr.n <= 32) return;
     const int n = tr.n;
-    if (n == 0) {
-        if (writer && all_sizes) tree_status[b] = BOLE_TREE_OK;
-        return;
-    }
-    if (n < min_n) return;
     const int lo = tr.lo, last = n - 1;
     const int ntl = (n + 15) >> 4;          // node tiles holding nodes
     const int rows = n > 32 ? 64 : 32;      // K and V rows staged (whole tile pairs)
@@ -758,7 +748,7 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
             lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, none);
     if (max_n > 32)
         verify_mfma_ksplit_kernel<DK, DV><<<grid, dim3(128), 0, stream>>>(
-            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, 33);
+            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n);
 }
 
 template <int DK>
