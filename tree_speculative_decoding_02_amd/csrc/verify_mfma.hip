@@ -62,8 +62,18 @@ struct LazyCommit {
 
 // Layer blockIdx.y of the table; every layer runs the same trees. Per-tree outputs
 // (statuses, path rows) are written by layer 0 only.
-template <int DK, int DV, bool LAZY>
-__global__ __launch_bounds__(64, 2) void verify_mfma_tree_kernel(
+template <int DK, int DV>
+constexpr int ksplit_smem_bytes();
+template <int DK, int DV>
+__device__ __forceinline__ void ksplit_body(const bole_layer_t, const int32_t *, const int32_t *,
+                                            int32_t *, int, int, int, int, char *);
+
+// FUSED: every tree size in one launch, for a caller without a budget of 32 nodes. A
+// workgroup of two wavefronts takes a tree of 33..64 nodes with the row-split body (below)
+// and one of up to 32 nodes on its first wavefront (the second exits); both leave at once,
+// and wave-uniformly, for the trees they do not take, and share one LDS buffer.
+template <int DK, int DV, bool LAZY, bool FUSED>
+__global__ __launch_bounds__(FUSED ? 128 : 64, 2) void verify_mfma_tree_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
     int U, int max_n, LazyCommit lc) {
@@ -78,12 +88,26 @@ __global__ __launch_bounds__(64, 2) void verify_mfma_tree_kernel(
     constexpr int VPR = CW / 8;             // 16-byte pieces per V row (of this group's columns)
     typedef float hvec __attribute__((ext_vector_type(CPL)));
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
-    __shared__ bf16x8 s_k[NN * PPR];        // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR)
-    __shared__ __bf16 s_v[NN * CW];         // V rows of the group's columns, row j at [CW j]
-    // lazy commit: k rows and v rows (group columns) of up to kLazyStage path nodes
+    static_assert(!(LAZY && FUSED), "trees of 33..64 nodes follow a lazy commit in their own launch");
+    // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR); V rows of the group's columns,
+    // row j at [CW j]; lazy commit: k rows and v rows (group columns) of up to kLazyStage
+    // path nodes. FUSED: K and V in the buffer the row-split body uses.
     constexpr int kLazyStage = LAZY ? 8 : 1;
+    constexpr int kFusedBytes = FUSED ? (NN * PPR * 16 + NN * CW * 2 > ksplit_smem_bytes<DK, DV>()
+                                             ? NN * PPR * 16 + NN * CW * 2
+                                             : ksplit_smem_bytes<DK, DV>())
+                                      : 16;
+    __shared__ __align__(16) char s_fused[kFusedBytes];
+    __shared__ bf16x8 s_k_own[FUSED ? 1 : NN * PPR];
+    __shared__ __bf16 s_v_own[FUSED ? 8 : NN * CW];
     __shared__ __bf16 s_pk[kLazyStage * DK], s_pv[kLazyStage * CW];
+    bf16x8 *const s_k = FUSED ? reinterpret_cast<bf16x8 *>(s_fused) : s_k_own;
+    __bf16 *const s_v = FUSED ? reinterpret_cast<__bf16 *>(s_fused + NN * PPR * 16) : s_v_own;
     const bole_layer_t &ly = lt.l[blockIdx.y];
+    if constexpr (FUSED) {
+        ksplit_body<DK, DV>(ly, parent, node_offsets, tree_status, H, T, U, max_n, s_fused);
+        if (threadIdx.x >= 64) return;
+    }
     float *const H0 = ly.H0;                // written only by the lazy commit
     const __bf16 *const q = static_cast<const __bf16 *>(ly.q);
     const __bf16 *const k = static_cast<const __bf16 *>(ly.k);
@@ -442,10 +466,16 @@ __global__ __launch_bounds__(64, 2) void verify_mfma_tree_kernel(
 // every V row that a masked (zero) weight meets is finite. Every other tree, and the
 // status of out-of-range trees, is the one-wavefront kernel's.
 template <int DK, int DV>
-__global__ __launch_bounds__(128, 3) void verify_mfma_ksplit_kernel(
-    const LayerTable lt, const int32_t *__restrict__ parent,
+constexpr int ksplit_smem_bytes() {
+    return 64 * (DK / 8) * 16 + 64 * (DV < 64 ? DV : 64) * 2 + 2 * ((DV < 64 ? DV : 64) / 16) * 64 * 16;
+}
+
+// Both wavefronts of a 128-thread workgroup; smem holds ksplit_smem_bytes bytes.
+template <int DK, int DV>
+__device__ __forceinline__ void ksplit_body(
+    const bole_layer_t ly, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
-    int U, int max_n) {
+    int U, int max_n, char *smem) {
     constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
     constexpr int CPL = CW / 16;            // columns per lane: 4 or 2
     constexpr int G = DV / CW;              // column groups per unit
@@ -457,10 +487,11 @@ __global__ __launch_bounds__(128, 3) void verify_mfma_ksplit_kernel(
     constexpr int NN = 64;
     typedef float hvec __attribute__((ext_vector_type(CPL)));
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
-    __shared__ bf16x8 s_k[NN * PPR];        // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR)
-    __shared__ __bf16 s_v[NN * CW];         // V rows of the group's columns, row j at [CW j]
-    __shared__ f32x4 s_x[2 * CPL * 64];     // partials handed from one wavefront to the other
-    const bole_layer_t &ly = lt.l[blockIdx.y];
+    // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR); V rows of the group's columns,
+    // row j at [CW j]; partials handed from one wavefront to the other
+    bf16x8 *const s_k = reinterpret_cast<bf16x8 *>(smem);
+    __bf16 *const s_v = reinterpret_cast<__bf16 *>(s_k + NN * PPR);
+    f32x4 *const s_x = reinterpret_cast<f32x4 *>(s_v + NN * CW);
     const __bf16 *const q = static_cast<const __bf16 *>(ly.q);
     const __bf16 *const k = static_cast<const __bf16 *>(ly.k);
     const __bf16 *const v = static_cast<const __bf16 *>(ly.v);
@@ -468,7 +499,7 @@ __global__ __launch_bounds__(128, 3) void verify_mfma_ksplit_kernel(
     float *const out = ly.out;
 
     const int lane = lane_id();
-    const int w = (int)(threadIdx.x >> 6);
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
     const int n16 = lane & 15, g = lane >> 4;
     int unit, cg;
     if (G == 1) {
@@ -701,6 +732,15 @@ __global__ __launch_bounds__(128, 3) void verify_mfma_ksplit_kernel(
         }
 }
 
+template <int DK, int DV>
+__global__ __launch_bounds__(128, 3) void verify_mfma_ksplit_kernel(
+    const LayerTable lt, const int32_t *__restrict__ parent,
+    const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
+    int U, int max_n) {
+    __shared__ __align__(16) char smem[ksplit_smem_bytes<DK, DV>()];
+    ksplit_body<DK, DV>(lt.l[blockIdx.y], parent, node_offsets, tree_status, H, T, U, max_n, smem);
+}
+
 static bool shape_ok(const bole_dims_t &d) {
     if (d.flags & BOLE_FLAG_FORCE_GENERIC) return false;
     if (d.factor_dtype != BOLE_DTYPE_BF16 || d.gate_kind != BOLE_GATE_SCALAR) return false;
@@ -740,15 +780,20 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
     LayerTable lt = {};
     for (int l = 0; l < nl; ++l) lt.l[l] = layers[l];
     const LazyCommit none = {};
-    if (lazy)
-        verify_mfma_tree_kernel<DK, DV, true><<<grid, dim3(64), 0, stream>>>(
+    if (lazy) {
+        // the large trees of this step are verified against the state this launch commits
+        verify_mfma_tree_kernel<DK, DV, true, false><<<grid, dim3(64), 0, stream>>>(
             lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, *lazy);
-    else
-        verify_mfma_tree_kernel<DK, DV, false><<<grid, dim3(64), 0, stream>>>(
+        if (max_n > 32)
+            verify_mfma_ksplit_kernel<DK, DV><<<grid, dim3(128), 0, stream>>>(
+                lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n);
+    } else if (max_n > 32) {
+        verify_mfma_tree_kernel<DK, DV, false, true><<<grid, dim3(128), 0, stream>>>(
             lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, none);
-    if (max_n > 32)
-        verify_mfma_ksplit_kernel<DK, DV><<<grid, dim3(128), 0, stream>>>(
-            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n);
+    } else {
+        verify_mfma_tree_kernel<DK, DV, false, false><<<grid, dim3(64), 0, stream>>>(
+            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, max_n, none);
+    }
 }
 
 template <int DK>
