@@ -7,10 +7,11 @@
 // L_i is the root-first sum of log2 a over path(i). Only per-node factors are read
 // (section 2, "Token-Level Factor Encoding"); no per-node state exists anywhere.
 //
-// One launch for trees of 1..32 nodes (one wavefront per sequence, head and 64-column
-// group) and, only when the batch may hold larger trees, one for trees of 33..64 nodes
-// (two wavefronts that split H_0's rows); each launch covers up to 16 layers that share
-// the trees (blockIdx.y = layer). The LAZY instantiation first applies the previous
+// Trees of 1..32 nodes take one wavefront per sequence, head and 64-column group; trees
+// of 33..64 nodes take two wavefronts that split H_0's rows. A batch that may hold larger
+// trees runs both in one fused launch (after a lazy commit, the larger trees take a launch
+// of their own); each launch covers up to 16 layers that share the trees
+// (blockIdx.y = layer). The LAZY instantiation first applies the previous
 // step's accepted path to H_0 (section 2's restore) and writes it back, in the same pass
 // over H_0. H_0 goes from HBM straight into MFMA operand registers with
 // row-contiguous 16-byte loads, so a wavefront needs only 12 KB of LDS (K and V) and
