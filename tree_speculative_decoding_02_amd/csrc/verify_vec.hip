@@ -38,6 +38,18 @@ namespace bole {
 
 constexpr int kVecThreads = 256;
 
+// One step of a wavefront-wide running minimum and maximum over DPP lane moves: lanes
+// that the move gives no source keep their own values (the identities +inf and -inf).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void range_dpp_step(float &mn, float &mx) {
+    const int pinf = __builtin_bit_cast(int, __builtin_inff());
+    const int ninf = __builtin_bit_cast(int, -__builtin_inff());
+    mn = fminf(mn, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                 pinf, __builtin_bit_cast(int, mn), CTRL, ROW_MASK, 0xf, false)));
+    mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                 ninf, __builtin_bit_cast(int, mx), CTRL, ROW_MASK, 0xf, false)));
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     const float *__restrict__ H0, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
@@ -191,11 +203,13 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     // node's 2^{r+1} nearest path nodes (or its whole path)
     const int rounds = s_info[1];
     for (int r = 0; r < rounds; ++r) {
+        bool moved[GPT];  // entries whose 2^r-th ancestor exists; only they change
 #pragma unroll
         for (int u = 0; u < GPT; ++u) {
             const int P = tid + kVecThreads * u;
             const int a = s_anc[r][P / GP];
-            if (a >= 0) {
+            moved[u] = a >= 0;
+            if (moved[u]) {
                 const float4 x = *reinterpret_cast<const float4 *>(s_lg + a * DK + 4 * (P % GP));
                 lgv[u].x += x.x;
                 lgv[u].y += x.y;
@@ -207,16 +221,17 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
 #pragma unroll
         for (int u = 0; u < GPT; ++u) {
             const int P = tid + kVecThreads * u;
-            *reinterpret_cast<float4 *>(s_lg + (P / GP) * DK + 4 * (P % GP)) = lgv[u];
+            if (moved[u])
+                *reinterpret_cast<float4 *>(s_lg + (P / GP) * DK + 4 * (P % GP)) = lgv[u];
         }
-        __syncthreads();
+        if (r + 1 < rounds) __syncthreads();  // the last round's barrier is the range's
     }
 
     // ---- LG range of the tree. With M its midpoint, q_i 2^{LG_i - M} and k_j 2^{M - LG_j}
     // stay within 2^{+-60} when the range is at most 120, and w_ij is then their dot
     // product: the intra term runs on matrix cores. Otherwise (very deep or very strongly
     // decayed trees) each ancestor pair is summed with its exact exponent.
-    float lmin = 3.0e38f, lmax = -3.0e38f;
+    float lmin = __builtin_inff(), lmax = -__builtin_inff();
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
         if ((tid + kVecThreads * u) / GP < n) {
@@ -224,12 +239,13 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
             lmax = fmaxf(lmax, fmaxf(fmaxf(lgv[u].x, lgv[u].y), fmaxf(lgv[u].z, lgv[u].w)));
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        lmin = fminf(lmin, __shfl_xor(lmin, o, 64));
-        lmax = fmaxf(lmax, __shfl_xor(lmax, o, 64));
-    }
-    if (lane == 0) {
+    range_dpp_step<0x111, 0xf>(lmin, lmax);  // row_shr:1
+    range_dpp_step<0x112, 0xf>(lmin, lmax);  // row_shr:2
+    range_dpp_step<0x114, 0xf>(lmin, lmax);  // row_shr:4
+    range_dpp_step<0x118, 0xf>(lmin, lmax);  // row_shr:8
+    range_dpp_step<0x142, 0xa>(lmin, lmax);  // row_bcast:15 into rows 1 and 3
+    range_dpp_step<0x143, 0xc>(lmin, lmax);  // row_bcast:31 into rows 2 and 3
+    if (lane == 63) {  // lane 63 holds the wavefront's minimum and maximum
         s_red[wave][0] = lmin;
         s_red[wave][1] = lmax;
     }
