@@ -324,20 +324,32 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     // stands for node 32p + 4g + e (e < 4) or 32p + 16 + 4g + e - 4 (e >= 4).
     bf16x8 wh[2], wl[2];
     if (factored) {
-        // B_j = k_j 2^{M - LG_j}, once per entry: each thread rewrites its own LG entries
-        // in place once every wavefront has read LG for its query operands
+        // B_j = k_j 2^{M - LG_j}, split hi + lo once per entry, into two bf16 tables that
+        // take the LG table's space once every wavefront has read LG for its query
+        // operands. Their 16-byte chunks are swizzled by row (chunk ^ row mod NCH), so the
+        // tile reads below (16 rows, one chunk each) fall on distinct banks.
+        constexpr int NCH = DK / 8;
+        typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+        __bf16 *s_bh = reinterpret_cast<__bf16 *>(s_big);
+        __bf16 *s_bl = s_bh + N * DK;
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < GPT; ++u) {
             const int P = tid + kVecThreads * u;
             const int row = P / GP, c = 4 * (P % GP);
-            const __bf16 *kr = s_k + row * DK + c;
-            const float4 bj = make_float4(
-                static_cast<float>(kr[0]) * __builtin_amdgcn_exp2f(M - lgv[u].x),
-                static_cast<float>(kr[1]) * __builtin_amdgcn_exp2f(M - lgv[u].y),
-                static_cast<float>(kr[2]) * __builtin_amdgcn_exp2f(M - lgv[u].z),
-                static_cast<float>(kr[3]) * __builtin_amdgcn_exp2f(M - lgv[u].w));
-            *reinterpret_cast<float4 *>(s_lg + row * DK + c) = bj;
+            const b4 kk = *reinterpret_cast<const b4 *>(s_k + row * DK + c);
+            const float lg[4] = {lgv[u].x, lgv[u].y, lgv[u].z, lgv[u].w};
+            b4 hh, ll;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                __bf16 xh, xl;
+                split_bf16(static_cast<float>(kk[e]) * __builtin_amdgcn_exp2f(M - lg[e]), xh, xl);
+                hh[e] = xh;
+                ll[e] = xl;
+            }
+            const int at = row * DK + 8 * ((c >> 3) ^ (row & (NCH - 1))) + (c & 7);
+            *reinterpret_cast<b4 *>(s_bh + at) = hh;
+            *reinterpret_cast<b4 *>(s_bl + at) = ll;
         }
         __syncthreads();
         const uint64_t mi = s_mask[16 * wave + n16];
@@ -346,21 +358,11 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         for (int jt = 0; jt < 4; ++jt) {
             f32x4 st = {0.f, 0.f, 0.f, 0.f};
             if (jt <= wave) {
-                const int j = min(16 * jt + n16, N - 1);
+                const int j = 16 * jt + n16;
 #pragma unroll
                 for (int t = 0; t < KT; ++t) {
-                    const float *bj = s_lg + j * DK + 32 * t + 8 * g4;
-                    const float4 x0 = *reinterpret_cast<const float4 *>(bj);
-                    const float4 x1 = *reinterpret_cast<const float4 *>(bj + 4);
-                    const float bv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                    bf16x8 bh, bl;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        __bf16 xh, xl;
-                        split_bf16(bv[e], xh, xl);
-                        bh[e] = xh;
-                        bl[e] = xl;
-                    }
+                    const int at = j * DK + 8 * ((4 * t + g4) ^ (j & (NCH - 1)));
+                    const bf16x8 bh = load16(s_bh + at), bl = load16(s_bl + at);
                     st = mfma16_bf16(bh, ah[t], st);
                     st = mfma16_bf16(bh, al[t], st);
                     st = mfma16_bf16(bl, ah[t], st);
