@@ -203,6 +203,12 @@ EDGE = [
     ("long_paths_bf16", dict(batch=4, heads=2, d_k=128, d_v=64, sizes=[64, 48, 40, 33], kind="chain", max_path=64)),
     ("long_paths_fp32", dict(batch=4, heads=2, d_k=128, d_v=64, sizes=[64, 40, 24, 20], kind="chain", factor_dtype=torch.float32, max_path=64)),
     ("long_paths_vector", dict(batch=4, heads=2, d_k=128, d_v=128, sizes=[64, 48, 30, 12], kind="chain", vector_gate=True, max_path=64)),
+    # vector gates at every width the matrix-core kernel takes: d_k = 64 (two k-steps and
+    # eight 16-byte chunks per factor row), d_v = 32 (one column group narrower than 64)
+    # and d_v = 256 (four column groups), with ragged tree sizes across the 16-node tiles
+    ("vector_gate_dk64_dv128", dict(batch=4, heads=3, d_k=64, d_v=128, sizes=[64, 17, 33, 1], vector_gate=True, kind="bestfirst")),
+    ("vector_gate_dk128_dv32", dict(batch=4, heads=3, d_k=128, d_v=32, sizes=[48, 64, 5, 31], vector_gate=True, kind="deep", max_path=64)),
+    ("vector_gate_dk64_dv256", dict(batch=3, heads=2, d_k=64, d_v=256, sizes=[64, 49, 16], vector_gate=True, kind="bestfirst")),
 ]
 
 
