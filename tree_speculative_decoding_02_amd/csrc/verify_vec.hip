@@ -16,7 +16,7 @@
 //
 // One 256-thread workgroup per (sequence, head, 64-column group), trees of up to 64
 // nodes. Every input is staged through registers with plain 16-byte loads issued in the
-// order of use (parent, gate, K, query channels, Q fragments, then H_0 and V), so the
+// order of use (parent, gate, K, Q fragments, then H_0 and V), so the
 // H_0 and V loads stay in flight while the first phases compute, and each phase waits
 // only for what it reads:
 //  1. wavefront 0 builds the topology; the gate and K rows go to LDS;
@@ -136,10 +136,6 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         rk[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
             ku + ((uint32_t)min(P / KP, last) * rq + 8 * (P % KP))));
     }
-    bf16x8 qp[CH / 8];  // query channels CH*psub .. of node pi
-#pragma unroll
-    for (int u = 0; u < CH / 8; ++u)
-        qp[u] = load16(qu + ((uint32_t)min(pi, last) * rq + CH * psub + 8 * u));
     bf16x8 qf[KT];      // Q fragments: row 16*wave + n, channels 32t + 8g .. +7
 #pragma unroll
     for (int t = 0; t < KT; ++t)
@@ -259,6 +255,10 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     // j on path(i); four lanes per node, CH channels each, summed across the four
     if (!factored) {
         const uint64_t mi = pi < n ? s_mask[pi] : 0ull;
+        bf16x8 qp[CH / 8];  // query channels CH*psub .. of node pi, loaded only on this path
+#pragma unroll
+        for (int u = 0; u < CH / 8; ++u)
+            qp[u] = load16(qu + ((uint32_t)min(pi, last) * rq + CH * psub + 8 * u));
         float qv[CH], li[CH];
 #pragma unroll
         for (int u = 0; u < CH / 8; ++u)
