@@ -65,13 +65,14 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     // 16-byte pieces per thread of each staged table
     constexpr int GP = DK / 4, GPT = N * GP / kVecThreads;    // gate rows, fp32
     constexpr int KP = DK / 8, KPT = N * KP / kVecThreads;    // K rows, bf16
-    constexpr int HP = CW / 4, HPT = DK * HP / kVecThreads;   // H_0 slice, fp32
+    constexpr int HRG = DK / 8;                                // H_0 slice: 8-row groups
     constexpr int VP = CW / 8, VPT = N * VP / kVecThreads;    // V rows, bf16
-    static_assert(GPT >= 1 && KPT >= 1 && HPT >= 1 && VPT >= 1, "staging split");
+    static_assert(GPT >= 1 && KPT >= 1 && VPT >= 1 && HRG * 16 <= kVecThreads, "staging split");
     typedef float hvec __attribute__((ext_vector_type(CPL)));
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    // phase A: LG (N x DK fp32) then K (N x DK bf16); phase B: the H_0 slice (DK x CW fp32)
+    // phase A: LG (N x DK fp32) then K (N x DK bf16); phase B: the H_0 slice (DK x CW, as
+    // bf16 hi and lo tables)
     constexpr int kBig = (N * DK + N * DK / 2) > DK * CW ? (N * DK + N * DK / 2) : DK * CW;
     __shared__ __attribute__((aligned(16))) float s_big[kBig];
     __shared__ __attribute__((aligned(16))) __bf16 s_v[N * CW];   // V rows, the group's columns
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     __shared__ float s_red[4][2];                                  // per wave: min, max of LG
     float *s_lg = s_big;
     __bf16 *s_k = reinterpret_cast<__bf16 *>(s_big + N * DK);
-    float *s_h0 = s_big;
+    __bf16 *s_h0b = reinterpret_cast<__bf16 *>(s_big);  // H_0 slice, hi then lo tables
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     int unit, cg;
@@ -123,7 +124,8 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     // ---- issue every load, in order of use. Piece P = tid + 256u of a table with PP
     // pieces per row is row P / PP, piece P % PP (rows past the tree repeat its last row).
     const int p_raw = wave == 0 ? parent[lo + min(lane, last)] : -1;
-    u32x4 rg[GPT], rk[KPT], rh[HPT], rvv[VPT];
+    u32x4 rg[GPT], rk[KPT], rvv[VPT];
+    hvec rh[8];
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
         const int P = tid + kVecThreads * u;
@@ -140,11 +142,14 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
 #pragma unroll
     for (int t = 0; t < KT; ++t)
         qf[t] = load16(qu + ((uint32_t)min(16 * wave + n16, last) * rq + 32 * t + 8 * g4));
+    // H_0: thread (hrg, hn) = (tid / 16, tid % 16) loads rows 8 hrg .. 8 hrg + 7 of the
+    // slice, columns CPL*hn .. (the B-operand rows and columns of one lane)
+    const int hrg = tid >> 4, hn = tid & 15;
+    if (hrg < HRG) {
 #pragma unroll
-    for (int u = 0; u < HPT; ++u) {
-        const int P = tid + kVecThreads * u;
-        rh[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-            hu + ((uint32_t)(P / HP) * DV + 4 * (P % HP))));
+        for (int e = 0; e < 8; ++e)
+            rh[e] = __builtin_nontemporal_load(
+                reinterpret_cast<const hvec *>(hu + ((uint32_t)(8 * hrg + e) * DV + CPL * hn)));
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
@@ -386,11 +391,25 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     }
     __syncthreads();  // LG and K are dead: the H_0 slice takes their space
 
-    // ---- 4. H_0 and V to LDS
+    // ---- 4. H_0 and V to LDS. H_0 is split hi + lo once here, into two bf16 tables in
+    // B-operand order: the 16 bytes at [(rg CPL + c) 16 + n] hold rows 8rg .. 8rg + 7 of
+    // column CPL*n + c, so each product reads its operands with one 16-byte load per lane
+    // (the 16 lanes of a row group contiguous) and splits nothing.
+    if (hrg < HRG) {
 #pragma unroll
-    for (int u = 0; u < HPT; ++u) {
-        const int P = tid + kVecThreads * u;
-        *reinterpret_cast<u32x4 *>(s_h0 + (P / HP) * CW + 4 * (P % HP)) = rh[u];
+        for (int c = 0; c < CPL; ++c) {
+            bf16x8 hh, ll;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                __bf16 xh, xl;
+                split_bf16(rh[e][c], xh, xl);
+                hh[e] = xh;
+                ll[e] = xl;
+            }
+            const int at = ((hrg * CPL + c) * 16 + hn) * 8;
+            *reinterpret_cast<bf16x8 *>(s_h0b + at) = hh;
+            *reinterpret_cast<bf16x8 *>(s_h0b + DK * CW + at) = ll;
+        }
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
@@ -405,23 +424,13 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     for (int c = 0; c < CPL; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-        bf16x8 bh[CPL], bl[CPL];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const hvec row = *reinterpret_cast<const hvec *>(s_h0 + (32 * t + 8 * g4 + e) * CW + CPL * n16);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                __bf16 xh, xl;
-                split_bf16(row[c], xh, xl);
-                bh[c][e] = xh;
-                bl[c][e] = xl;
-            }
-        }
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            acc[c] = mfma16_bf16(ah[t], bh[c], acc[c]);
-            acc[c] = mfma16_bf16(ah[t], bl[c], acc[c]);
-            acc[c] = mfma16_bf16(al[t], bh[c], acc[c]);
+            const int at = (((4 * t + g4) * CPL + c) * 16 + n16) * 8;
+            const bf16x8 bh = load16(s_h0b + at), bl = load16(s_h0b + DK * CW + at);
+            acc[c] = mfma16_bf16(ah[t], bh, acc[c]);
+            acc[c] = mfma16_bf16(ah[t], bl, acc[c]);
+            acc[c] = mfma16_bf16(al[t], bh, acc[c]);
         }
     }
     if (factored) {
