@@ -159,7 +159,8 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     }
 
     // ---- 1. topology and doubling pointers (wavefront 0); log2 of the gate rows and
-    // the K rows to LDS; W cleared
+    // the K rows to LDS. W needs no clearing: the exact path writes every (node, path
+    // node) pair it later reads, and the factored path never reads it.
     if (wave == 0) {
         const WaveTopo topo = wave_topology_p(p_raw, n);
         s_mask[lane] = topo.mask;
@@ -191,7 +192,6 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         const int P = tid + kVecThreads * u;
         *reinterpret_cast<u32x4 *>(s_k + (P / KP) * DK + 8 * (P % KP)) = rk[u];
     }
-    for (int e = tid; e < N * N; e += kVecThreads) s_w[e] = 0.f;
     __syncthreads();
 
     if (s_info[0] != BOLE_TREE_OK) {
