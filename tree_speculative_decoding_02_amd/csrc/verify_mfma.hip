@@ -468,7 +468,7 @@ __global__ __launch_bounds__(FUSED ? 128 : 64, 2) void verify_mfma_tree_kernel(
 // status of out-of-range trees, is the one-wavefront kernel's.
 template <int DK, int DV>
 constexpr int ksplit_smem_bytes() {
-    return 64 * (DK / 8) * 16 + 64 * (DV < 64 ? DV : 64) * 2 + 2 * ((DV < 64 ? DV : 64) / 16) * 64 * 16;
+    return 64 * (DK / 8) * 16 + 64 * (DV < 64 ? DV : 64) * 2;
 }
 
 // Both wavefronts of a 128-thread workgroup; smem holds ksplit_smem_bytes bytes.
@@ -488,11 +488,13 @@ __device__ __forceinline__ void ksplit_body(
     constexpr int NN = 64;
     typedef float hvec __attribute__((ext_vector_type(CPL)));
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
-    // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR); V rows of the group's columns,
-    // row j at [CW j]; partials handed from one wavefront to the other
+    // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR); then one region used twice:
+    // first for the partials handed from one wavefront to the other, then for the V rows
+    // of the group's columns (row j at [CW j]). Both take 128 CW bytes.
+    static_assert(2 * CPL * 64 * sizeof(f32x4) == NN * CW * sizeof(__bf16), "shared region");
     bf16x8 *const s_k = reinterpret_cast<bf16x8 *>(smem);
-    __bf16 *const s_v = reinterpret_cast<__bf16 *>(s_k + NN * PPR);
-    f32x4 *const s_x = reinterpret_cast<f32x4 *>(s_v + NN * CW);
+    f32x4 *const s_x = reinterpret_cast<f32x4 *>(s_k + NN * PPR);
+    __bf16 *const s_v = reinterpret_cast<__bf16 *>(s_x);
     const __bf16 *const q = static_cast<const __bf16 *>(ly.q);
     const __bf16 *const k = static_cast<const __bf16 *>(ly.k);
     const __bf16 *const v = static_cast<const __bf16 *>(ly.v);
@@ -560,13 +562,6 @@ __device__ __forceinline__ void ksplit_body(
         const int pc = (lane % PPR) ^ (j % PPR);
         if ((64 / PPR) * s < rows) kst[u] = load16_stream(ku + ((uint32_t)min(j, last) * rq + 8 * pc));
     }
-#pragma unroll
-    for (int u = 0; u < VL; ++u) {
-        const int s = w + 2 * u;
-        const int j = (64 / VPR) * s + lane / VPR;
-        if ((64 / VPR) * s < rows)
-            vst[u] = load16_stream(vu + ((uint32_t)min(j, last) * rv + 8 * (lane % VPR)));
-    }
     // H_0 rows of this wavefront: load s = 8tl + e, lane (n, g): row 32(w*KH + tl) + 8g + e
     hvec hreg[HSW];
 #pragma unroll
@@ -576,10 +571,6 @@ __device__ __forceinline__ void ksplit_body(
 #pragma unroll
     for (int u = 0; u < KL; ++u)
         if ((64 / PPR) * (w + 2 * u) < rows) s_k[64 * (w + 2 * u) + lane] = kst[u];
-#pragma unroll
-    for (int u = 0; u < VL; ++u)
-        if ((64 / VPR) * (w + 2 * u) < rows)
-            *reinterpret_cast<bf16x8 *>(s_v + 512 * (w + 2 * u) + 8 * lane) = vst[u];
 
     // ---- 2. topology and base-2 cumulative decay (both wavefronts, same result)
     const float lg2 = lane < n ? __builtin_amdgcn_logf(g_raw) : 0.f;
@@ -631,6 +622,15 @@ __device__ __forceinline__ void ksplit_body(
             if (ti < ntl) qb[r][tl] = load16_stream(qrow + 32 * ((1 - w) * KH + tl));
         }
     }
+    // V rows, needed only by the intra-tree term and staged after the swap in the region
+    // the partials use: issued here, once H_0's registers are free
+#pragma unroll
+    for (int u = 0; u < VL; ++u) {
+        const int s = w + 2 * u;
+        const int j = (64 / VPR) * s + lane / VPR;
+        if ((64 / VPR) * s < rows)
+            vst[u] = load16_stream(vu + ((uint32_t)min(j, last) * rv + 8 * (lane % VPR)));
+    }
     // hand the other wavefront its partials (same accumulator layout in both) and take
     // ours, through one region in two phases: wavefront 1 hands over tiles 0 and 1, then
     // wavefront 0 tiles 2 and 3
@@ -643,15 +643,20 @@ __device__ __forceinline__ void ksplit_body(
                 if (2 * ph + r < ntl)
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) s_x[(r * CPL + c) * 64 + lane] = acc[2 + r][c];
-        __syncthreads();  // (the first also publishes both halves of K and V)
+        __syncthreads();  // (the first also publishes both halves of K)
         if (w != src)
 #pragma unroll
             for (int r = 0; r < 2; ++r)
                 if (2 * ph + r < ntl)
 #pragma unroll
                     for (int c = 0; c < CPL; ++c) acc[r][c] += s_x[(r * CPL + c) * 64 + lane];
-        if (ph == 0) __syncthreads();  // read before the second phase overwrites
+        __syncthreads();  // read before the second phase, then V, overwrite the region
     }
+#pragma unroll
+    for (int u = 0; u < VL; ++u)
+        if ((64 / VPR) * (w + 2 * u) < rows)
+            *reinterpret_cast<bf16x8 *>(s_v + 512 * (w + 2 * u) + 8 * lane) = vst[u];
+    __syncthreads();
     if (2 * w >= ntl) return;  // no node tile of this wavefront's in the tree
     // row scale 2^{L_i}, node 16ti + 4g + rr
 #pragma unroll
