@@ -213,6 +213,9 @@ EDGE = [
     # positive along a path, and the vector kernel's mid-range offset M with them
     ("growing_gates_scalar", dict(batch=4, heads=2, d_k=128, d_v=64, sizes=[64, 40, 33, 17], kind="chain", gate_scale=2.5, max_path=64)),
     ("growing_gates_vector", dict(batch=4, heads=2, d_k=128, d_v=128, sizes=[64, 40, 33, 17], kind="deep", vector_gate=True, gate_scale=2.5, max_path=64)),
+    # every gate exactly 1: no decay, every cumulative log-decay exactly 0
+    ("unit_gates_scalar", dict(batch=4, heads=2, d_k=128, d_v=64, sizes=[32, 64, 7, 40], kind="bestfirst", gate_value=1.0)),
+    ("unit_gates_vector", dict(batch=4, heads=2, d_k=128, d_v=128, sizes=[32, 64, 7, 40], kind="bestfirst", vector_gate=True, gate_value=1.0)),
 ]
 
 

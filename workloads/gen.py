@@ -139,7 +139,7 @@ def _cast(x: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
 
 
 def _layer(ss: np.random.SeedSequence, B, H, T, d_k, d_v, fdt, vector_gate, qkv_std, h0_std,
-           gate_shift=0.0, gate_scale=1.0) -> Layer:
+           gate_shift=0.0, gate_scale=1.0, gate_value=None) -> Layer:
     rq, rk, rv, rg, rh = (np.random.default_rng(s) for s in ss.spawn(5))
     q = _cast(rq.standard_normal((T, H, d_k)) * qkv_std, fdt)
     k = _cast(rk.standard_normal((T, H, d_k)) * qkv_std, fdt)
@@ -147,6 +147,8 @@ def _layer(ss: np.random.SeedSequence, B, H, T, d_k, d_v, fdt, vector_gate, qkv_
     gshape = (T, H, d_k) if vector_gate else (T, H)
     gate = _cast(gate_scale * np.exp(-softplus(rg.standard_normal(gshape) + gate_shift)),
                  torch.float32)
+    if gate_value is not None:  # every gate the same value (1.0: no decay at all)
+        gate = torch.full(gshape, float(gate_value), dtype=torch.float32)
     H0 = _cast(rh.standard_normal((B, H, d_k, d_v)) * h0_std, torch.float32)
     return Layer(H0=H0, q=q, k=k, v=v, gate=gate)
 
@@ -314,11 +316,12 @@ def make_random(seed: int, batch: int, heads: int, d_k: int, d_v: int,
                 sizes: Optional[Sequence[int]] = None, kind: str = "random",
                 vector_gate: bool = False, factor_dtype: torch.dtype = torch.bfloat16,
                 max_path: int = 16, gate_shift: float = 0.0, h0_std: float = 0.05,
-                gate_scale: float = 1.0) -> Workload:
+                gate_scale: float = 1.0, gate_value: Optional[float] = None) -> Workload:
     """Seeded workload with arbitrary shapes for parity and edge-case tests.
     ``sizes`` gives each tree's node count (default: uniform in [1, 64]). Gates are
     ``gate_scale * exp(-softplus(x + gate_shift))`` with x ~ N(0, 1): a scale above 1
-    gives gates above 1 as well (the state grows along a path)."""
+    gives gates above 1 as well (the state grows along a path). ``gate_value`` sets every
+    gate to one value instead."""
     root = np.random.SeedSequence(seed)
     tree_ss, acc_ss, lay_ss = root.spawn(3)
     trng = np.random.default_rng(tree_ss)
@@ -337,7 +340,7 @@ def make_random(seed: int, batch: int, heads: int, d_k: int, d_v: int,
         acc_len[b] = L
         acc_idx[b, :L] = branch[:L]
     lay = _layer(lay_ss, batch, heads, T, d_k, d_v, factor_dtype, vector_gate,
-                 1.0 / np.sqrt(d_k), h0_std, gate_shift, gate_scale)
+                 1.0 / np.sqrt(d_k), h0_std, gate_shift, gate_scale, gate_value)
     return Workload(f"random_{kind}_{seed}", batch, heads, d_k, d_v, vector_gate, factor_dtype,
                     parent, offs, np.concatenate(rhos) if rhos else np.zeros(0), acc_idx,
                     acc_len, [lay], f"random {kind} trees, seed {seed}")
