@@ -476,47 +476,83 @@ __global__ __launch_bounds__(256) void build_kernel(
     }
 }
 
-// ---- 3. node_offsets and packed trees, one workgroup
+// ---- 3. node_offsets and packed trees, one workgroup. The first slots' inputs do not
+// depend on the offsets, so their loads are issued before the scan; the scan is one
+// shuffle scan per wavefront plus one barrier; the offsets and counts of up to
+// kPackLdsSeqs sequences are kept in LDS for the scatter (beyond that, read back from
+// node_offsets, which this workgroup wrote before its barrier).
 constexpr int kPackThreads = 1024;
+constexpr int kPackPre = 4;          // slots per thread loaded ahead of the scan
+constexpr int kPackLdsSeqs = 4096;
 
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(
     const int32_t *__restrict__ n_nodes, const int32_t *__restrict__ par_in,
     const int32_t *__restrict__ tok_in, const float *__restrict__ rho_in, int B, int n_max,
     int32_t *__restrict__ node_offsets, int32_t *__restrict__ parent, int32_t *__restrict__ token,
     float *__restrict__ rho) {
-    __shared__ int s_part[kPackThreads];
-    const int t = threadIdx.x;
+    __shared__ int s_wave[kPackThreads / 64];
+    __shared__ int s_off[kPackLdsSeqs], s_cnt[kPackLdsSeqs];
+    const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
+    const int total = B * n_max;
+    int pp[kPackPre], pt[kPackPre];
+    float pr[kPackPre];
+#pragma unroll
+    for (int u = 0; u < kPackPre; ++u) {
+        const int x = t + kPackThreads * u;
+        pp[u] = 0;
+        pt[u] = 0;
+        pr[u] = 0.f;
+        if (x < total) {
+            pp[u] = par_in[x];
+            pt[u] = tok_in[x];
+            if (rho) pr[u] = rho_in[x];
+        }
+    }
     const int per = (B + kPackThreads - 1) / kPackThreads;
     const int b0 = min(B, t * per), b1 = min(B, b0 + per);
     int sum = 0;
     for (int b = b0; b < b1; ++b) sum += n_nodes[b];
-    s_part[t] = sum;
+    // inclusive scan of the per-thread sums within the wavefront, then over wavefronts
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_wave[wave] = incl;
     __syncthreads();
-    // inclusive scan of the per-thread sums (Hillis-Steele)
-    for (int off = 1; off < kPackThreads; off <<= 1) {
-        const int x = t >= off ? s_part[t - off] : 0;
-        __syncthreads();
-        s_part[t] += x;
-        __syncthreads();
-    }
-    int off = s_part[t] - sum;
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_wave[w];
+    int off = base + incl - sum;
     for (int b = b0; b < b1; ++b) {
+        const int c = n_nodes[b];
         node_offsets[b] = off;
-        off += n_nodes[b];
-    }
-    if (t == kPackThreads - 1) node_offsets[B] = s_part[t];
-    __syncthreads();  // node_offsets written by this workgroup, read back below
-    // every (sequence, node) slot in parallel
-    const int total = B * n_max;
-    for (int x = t; x < total; x += kPackThreads) {
-        const int b = x / n_max, j = x - b * n_max;
-        if (j < n_nodes[b]) {
-            const int o = node_offsets[b] + j;
-            parent[o] = par_in[x];
-            token[o] = tok_in[x];
-            if (rho) rho[o] = rho_in[x];
+        if (b < kPackLdsSeqs) {
+            s_off[b] = off;
+            s_cnt[b] = c;
         }
+        off += c;
     }
+    if (t == kPackThreads - 1) node_offsets[B] = base + incl;
+    __syncthreads();  // offsets and counts (LDS, and node_offsets) visible to the workgroup
+    // every (sequence, node) slot in parallel
+    auto put = [&](int x, int pv, int tv, float rv) {
+        const int b = x / n_max, j = x - b * n_max;
+        const int c = b < kPackLdsSeqs ? s_cnt[b] : n_nodes[b];
+        if (j < c) {
+            const int o = (b < kPackLdsSeqs ? s_off[b] : node_offsets[b]) + j;
+            parent[o] = pv;
+            token[o] = tv;
+            if (rho) rho[o] = rv;
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < kPackPre; ++u) {
+        const int x = t + kPackThreads * u;
+        if (x < total) put(x, pp[u], pt[u], pr[u]);
+    }
+    for (int x = t + kPackThreads * kPackPre; x < total; x += kPackThreads)
+        put(x, par_in[x], tok_in[x], rho ? rho_in[x] : 0.f);
 }
 
 // ---- host side
