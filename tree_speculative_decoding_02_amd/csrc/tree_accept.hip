@@ -49,12 +49,15 @@ __device__ __forceinline__ f4 load4(const float *row, int y, int V, bool vec) {
 }
 
 // Calls f(y, value) for the elements of an fp32 row this thread owns, in increasing y.
-// Loads are issued kAcceptBatch at a time before any is used.
+// Loads are issued kAcceptBatch at a time before any is used. Positions past the row
+// (y >= V) get the value `pad`, which must leave f's result unchanged (-inf for a maximum,
+// 0 for a sum): every loaded value is then used unconditionally, so the compiler keeps
+// the batch of loads in flight together instead of moving a load under a per-element
+// branch.
 template <typename F>
-__device__ __forceinline__ void row_pass(const float *row, int V, bool vec, F f) {
+__device__ __forceinline__ void row_pass(const float *row, int V, bool vec, F f, float pad) {
     const int t = threadIdx.x;
     if (vec) {
-        typedef float f4 __attribute__((ext_vector_type(4)));
         constexpr int step = 4 * kAcceptThreads;
         for (int y0 = 4 * t; y0 < V; y0 += step * kAcceptBatch) {
             f4 x[kAcceptBatch];
@@ -66,10 +69,8 @@ __device__ __forceinline__ void row_pass(const float *row, int V, bool vec, F f)
 #pragma unroll
             for (int u = 0; u < kAcceptBatch; ++u) {
                 const int y = y0 + u * step;
-                if (y < V) {
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) f(y + c, x[u][c]);
-                }
+                for (int c = 0; c < 4; ++c) f(y + c, y + c < V ? x[u][c] : pad);
             }
         }
     } else {
@@ -79,14 +80,17 @@ __device__ __forceinline__ void row_pass(const float *row, int V, bool vec, F f)
             for (int u = 0; u < kAcceptBatch; ++u)
                 x[u] = row[min(y0 + u * kAcceptThreads, V - 1)];
 #pragma unroll
-            for (int u = 0; u < kAcceptBatch; ++u)
-                if (y0 + u * kAcceptThreads < V) f(y0 + u * kAcceptThreads, x[u]);
+            for (int u = 0; u < kAcceptBatch; ++u) {
+                const int y = y0 + u * kAcceptThreads;
+                f(y, y < V ? x[u] : pad);
+            }
         }
     }
 }
 
 // Calls f(y, p(y), q(y)) for the elements of two fp32 rows this thread owns, in
-// increasing y; kAcceptBatch / 4 16-byte loads of each row in flight.
+// increasing y; kAcceptBatch / 4 16-byte loads of each row in flight. Positions past the
+// rows get p = q = 0 (f must then add nothing), for the reason given above.
 template <typename F>
 __device__ __forceinline__ void row_pass2(const float *prow, const float *qrow, int V, bool vec,
                                           F f) {
@@ -103,8 +107,10 @@ __device__ __forceinline__ void row_pass2(const float *prow, const float *qrow, 
         for (int u = 0; u < NB; ++u) {
             const int y = y0 + u * step;
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (y + c < V) f(y + c, px[u][c], qx[u][c]);
+            for (int c = 0; c < 4; ++c) {
+                const bool in = y + c < V;
+                f(y + c, in ? px[u][c] : 0.f, in ? qx[u][c] : 0.f);
+            }
         }
     }
 }
@@ -150,6 +156,9 @@ constexpr int kTile = 4 * kAcceptThreads;
 constexpr int kTileGroup = 32;
 constexpr int kTileBatch = kAcceptBatch / 4;
 
+// VP, VQ: the target rows (p), the draft rows (q) take 16-byte loads. As template
+// constants they leave no branch between the loads of a batch.
+template <bool VP, bool VQ>
 __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs a) {
     __shared__ double s_red[kAcceptWaves];
     __shared__ double s_tw[kAcceptWaves][kTileGroup];
@@ -202,12 +211,12 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
             // ---- greedy: argmax of the target row
             float bv = -__builtin_huge_valf();
             int bi = 0x7fffffff;
-            row_pass(prow, V, a.vec, [&](int y, float x) {
+            row_pass(prow, V, VP, [&](int y, float x) {
                 if (x > bv) {  // y increases: a tie keeps the earlier id
                     bv = x;
                     bi = y;
                 }
-            });
+            }, -__builtin_huge_valf());
 #pragma unroll
             for (int off = 32; off > 0; off >>= 1) {
                 const float pv = __shfl_xor(bv, off, 64);
@@ -271,7 +280,7 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
             C = C / Zp + 1.0 / Zq;
             Zq = Zq - (double)qx;
             double part = 0.0;
-            row_pass2(prow, qrow, V, a.vec && a.vecq,
+            row_pass2(prow, qrow, V, VP && VQ,
                       [&](int, float py, float qy) { part += residual(py, qy, A, C); });
             Zp = block_sum_d(part, s_red);
             ++k;
@@ -291,7 +300,7 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
         double total = Zp;
         if (!withq) {
             double part = 0.0;
-            row_pass(prow, V, a.vec, [&](int, float x) { part += (double)x; });
+            row_pass(prow, V, VP, [&](int, float x) { part += (double)x; }, 0.f);
             total = block_sum_d(part, s_red);
         }
         const double thr = (double)a.u_bonus[b] * total;
@@ -309,8 +318,8 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
 #pragma unroll
                 for (int u = 0; u < kTileBatch; ++u) {
                     const int y = (g0 + j0 + u) * kTile + 4 * t;
-                    pv[u] = load4(prow, y, V, a.vec);
-                    qv[u] = withq ? load4(qrow, y, V, a.vecq) : f4{0.f, 0.f, 0.f, 0.f};
+                    pv[u] = load4(prow, y, V, VP);
+                    qv[u] = withq ? load4(qrow, y, V, VQ) : f4{0.f, 0.f, 0.f, 0.f};
                 }
 #pragma unroll
                 for (int u = 0; u < kTileBatch; ++u) {
@@ -318,8 +327,8 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
                     const int y = (g0 + j0 + u) * kTile + 4 * t;
                     double sv = 0.0;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        if (y + c < V) sv += rval(pv[u][c], qv[u][c]);
+                    for (int c = 0; c < 4; ++c)  // past the row: + 0, exact
+                        sv += y + c < V ? rval(pv[u][c], qv[u][c]) : 0.0;
                     sv = wave_sum_d(sv);
                     if (lane == 0) s_tw[wave][j0 + u] = sv;
                 }
@@ -344,8 +353,8 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
         }
         if (tile >= 0) {
             const int y = tile * kTile + 4 * t;
-            const f4 pv = load4(prow, y, V, a.vec);
-            const f4 qv = withq ? load4(qrow, y, V, a.vecq) : f4{0.f, 0.f, 0.f, 0.f};
+            const f4 pv = load4(prow, y, V, VP);
+            const f4 qv = withq ? load4(qrow, y, V, VQ) : f4{0.f, 0.f, 0.f, 0.f};
             double e[4], sv = 0.0;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -421,7 +430,11 @@ hipError_t launch_tree_accept(const float *p_ctx, const float *p_node, const flo
             ((reinterpret_cast<uintptr_t>(p_ctx) | reinterpret_cast<uintptr_t>(p_node)) % 16) == 0;
     a.vecq = d.vocab % 4 == 0 && q_ctx && q_node &&
              ((reinterpret_cast<uintptr_t>(q_ctx) | reinterpret_cast<uintptr_t>(q_node)) % 16) == 0;
-    tree_accept_kernel<<<dim3((unsigned)d.batch), dim3(kAcceptThreads), 0, stream>>>(a);
+    const dim3 grid((unsigned)d.batch), block(kAcceptThreads);
+    if (a.vec && a.vecq) tree_accept_kernel<true, true><<<grid, block, 0, stream>>>(a);
+    else if (a.vec) tree_accept_kernel<true, false><<<grid, block, 0, stream>>>(a);
+    else if (a.vecq) tree_accept_kernel<false, true><<<grid, block, 0, stream>>>(a);
+    else tree_accept_kernel<false, false><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
 }
 
