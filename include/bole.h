@@ -80,7 +80,8 @@ enum {
     BOLE_TREE_BAD_PARENT = 2, /* some node i has parent[i] < -1 or parent[i] >= i */
     BOLE_TREE_BAD_PATH = 3,   /* commit: length outside [0, max_path], an index outside
                                  the tree, or not a chain that starts at a root */
-    BOLE_TREE_BAD_TOKEN = 4   /* accept: a node's token outside [0, vocab) */
+    BOLE_TREE_BAD_TOKEN = 4   /* accept: a node's token outside [0, vocab), or (sampling)
+                                 two siblings carrying the same token */
 };
 
 typedef enum { BOLE_DTYPE_BF16 = 0, BOLE_DTYPE_F32 = 1 } bole_dtype_t;
@@ -352,7 +353,8 @@ BOLE_API bole_status_t bole_build_tree(const float *marginals, const float *cost
  *  - BOLE_ACCEPT_SAMPLE: a drafted token x is accepted with probability
  *    min(1, p(x) / q(x)), else the bonus is drawn from the normalised residual (p - q)+,
  *    which keeps the output distributed as the target's. Siblings (distinct tokens,
- *    drafted without replacement) are tested in index order, each against the residuals
+ *    drafted without replacement; two siblings with one token make the tree
+ *    BOLE_TREE_BAD_TOKEN) are tested in index order, each against the residuals
  *    the rejected ones before it left: p_res <- (p_res - q_res)+ renormalised, and the
  *    rejected token leaves q_res, renormalised. x is accepted when
  *    u_node[x's node] * q_res(x) < p_res(x). The bonus is the smallest y whose

@@ -16,28 +16,24 @@ On a tree (the reading taken where the pages are silent):
     on ties); the child carrying that token is accepted (the lowest-index one if several),
     and when no child carries it, that token is the next (bonus) token;
   - sampling: the children of the current node are tested in index order, each against
-    the residual distributions the children rejected before it left: x is accepted when
-    u * q_res(x) < p_res(x); on a rejection p_res <- (p_res - q_res)+ renormalised, and x
-    leaves q_res, which is renormalised (siblings are distinct tokens, drawn without
-    replacement). When every child is rejected, or the node has none, the bonus token is
-    drawn from p_res by inverse CDF with the tree's bonus uniform. On a chain this is the
-    section 9.1 rule exactly.
+    the residual distributions the children rejected before it left. x is accepted when
+    u * q_res(x) < p_res(x) (probability min(1, p_res(x) / q_res(x))). On a rejection,
+    step by step:
+        p_res <- max(p_res - q_res, 0), renormalised to sum 1;
+        q_res[x] <- 0, q_res renormalised to sum 1
+    (siblings are distinct tokens, drawn from q without replacement, so the rejected
+    token leaves the draft distribution). When every child is rejected, or the node has
+    none, the bonus token is drawn from p_res by inverse CDF with the tree's bonus
+    uniform: the smallest y with sum_{y' <= y} p_res(y') > u * sum(p_res) (the last y if
+    rounding leaves none). On a chain this is the section 9.1 rule exactly.
+  - siblings with the same token are a malformed draft under sampling (the rule above
+    assumes drafts without replacement): such a tree is reported BAD_TOKEN;
   - at most max_path nodes are accepted; the bonus is then drawn at the last one.
 
-Arithmetic (fp64). The residuals are kept unnormalised with their totals Zp, Zq:
-p_res = rp / Zp, q_res = rq / Zq; the test is u * rq(x) * Zp < rp(x) * Zq. A rejection of
-x replaces rp by max(rp / Zp - rq / Zq, 0) and removes x from rq. Because a clamp at 0
-never releases (each step subtracts a non-negative amount), after k rejections
-    rp(y) = max(p(y) * A - q(y) * C, 0),     rq(y) = q(y) (0 for rejected tokens),
-where a fresh node starts from A = 1, C = 0, Zp = Zq = 1, and each rejection of x sets
-A <- A / Zp, C <- C / Zp + 1 / Zq, Zq <- Zq - q(x), Zp <- sum_y rp(y) (the new rp). A
-rejected token's value is <= 0 there already, so the same formula holds for it. This is
-exactly the step-by-step residual in real arithmetic, and it is how both sides evaluate
-it: the products and the difference are separately rounded fp64 operations. The bonus
-is the smallest y with sum_{y' <= y} rp(y') > u * total, total = sum(p) at a fresh node,
-else Zp (the last y if rounding leaves none). Each call also returns the smallest
-relative decision margin it met, so that a test can tell a genuine mismatch from a
-comparison that a different summation order may flip.
+Arithmetic: fp64 numpy arrays, the residuals held normalised, one step per rejection in
+the order above. Each call also returns the smallest relative decision margin it met
+(acceptance tests and the bonus threshold), so that a test can tell a genuine mismatch
+from a comparison that different rounding may flip.
 """
 import numpy as np
 
@@ -49,6 +45,12 @@ TREE_OK, TREE_BAD_SIZE, TREE_BAD_PARENT, TREE_BAD_TOKEN = 0, 1, 2, 4
 def _rel(a, b):
     m = max(abs(a), abs(b))
     return abs(a - b) / m if m > 0 else 0.0
+
+
+def _normalised(r):
+    """r / sum(r); a vector with nothing left stays all zero."""
+    s = float(r.sum())
+    return r / s if s > 0 else np.zeros_like(r)
 
 
 def accept_tree(p_ctx, q_ctx, p_node, q_node, parent, token, lo, n, u_node, u_bonus, mode,
@@ -73,31 +75,28 @@ def accept_tree(p_ctx, q_ctx, p_node, q_node, parent, token, lo, n, u_node, u_bo
                 continue
             return path, y, margin
         qrow = np.asarray(q_ctx if cur < 0 else q_node[lo + cur], np.float64)
-        A, C, Zp, Zq = 1.0, 0.0, 1.0, 1.0
-        rp = prow
-        fresh, nxt = True, None
+        p_res = prow.copy()   # the target row as given at a fresh node
+        q_res = qrow.copy()
+        nxt = None
         for c in (kids[cur] if room else []):
             x = int(token[lo + c])
-            rpx = max(prow[x] * A - qrow[x] * C, 0.0)
-            lhs = float(u_node[lo + c]) * qrow[x] * Zp
-            rhs = rpx * Zq
+            lhs = float(u_node[lo + c]) * q_res[x]
+            rhs = p_res[x]
             margin = min(margin, _rel(lhs, rhs))
             if lhs < rhs:
                 nxt = c
                 break
-            A, C = A / Zp, C / Zp + 1.0 / Zq
-            Zq = Zq - qrow[x]
-            rp = np.maximum(prow * A - qrow * C, 0.0)
-            Zp = float(rp.sum())
-            fresh = False
+            p_res = _normalised(np.maximum(p_res - q_res, 0.0))
+            q_res = q_res.copy()
+            q_res[x] = 0.0
+            q_res = _normalised(q_res)
         if nxt is not None:
             path.append(nxt)
             cur = nxt
             continue
-        total = float(rp.sum()) if fresh else Zp
-        t = float(u_bonus) * total
-        cs = np.cumsum(rp)
-        y = min(int(np.searchsorted(cs, t, side="right")), rp.shape[0] - 1)
+        t = float(u_bonus) * float(p_res.sum())
+        cs = np.cumsum(p_res)
+        y = min(int(np.searchsorted(cs, t, side="right")), p_res.shape[0] - 1)
         if t > 0:
             margin = min(margin, float(np.abs(cs - t).min()) / t)
         return path, y, margin
@@ -108,8 +107,8 @@ def accept_trees(p_ctx, q_ctx, p_node, q_node, parent, token, node_offsets, u_no
     """A packed batch. Returns dict of accepted_idx [B][max_path] (-1 padded),
     accepted_len [B], bonus [B], status [B], margin [B]. A tree whose offsets are out of
     order or outside [0, T] or hold more than 64 nodes gets BAD_SIZE, a parent outside
-    [-1, i) BAD_PARENT, a token outside [0, V) BAD_TOKEN; such trees accept nothing and
-    get bonus -1."""
+    [-1, i) BAD_PARENT, a token outside [0, V) BAD_TOKEN, and so do two siblings with the
+    same token under sampling; such trees accept nothing and get bonus -1."""
     B = len(node_offsets) - 1
     T = len(parent)
     V = np.asarray(p_ctx).shape[-1]
@@ -130,6 +129,11 @@ def accept_trees(p_ctx, q_ctx, p_node, q_node, parent, token, node_offsets, u_no
         if any(not (0 <= int(token[lo + i]) < V) for i in range(n)):
             status[b] = TREE_BAD_TOKEN
             continue
+        if mode == SAMPLE:
+            pairs = [(int(parent[lo + i]), int(token[lo + i])) for i in range(n)]
+            if len(set(pairs)) != n:
+                status[b] = TREE_BAD_TOKEN
+                continue
         path, y, m = accept_tree(p_ctx[b], q_ctx[b] if q_ctx is not None else None, p_node,
                                  q_node, parent, token, lo, n, u_node, u_bonus[b], mode,
                                  max_path)

@@ -162,3 +162,26 @@ def test_accepted_paths_feed_commit(bole):
     Hn = H.double().cpu().numpy()
     err = (np.abs(Hn - Href).reshape(12, -1).max(1) / np.abs(Href).reshape(12, -1).max(1)).max()
     assert err <= 2e-3
+
+
+def test_accept_duplicate_siblings(bole):
+    """Two siblings with one token: a bad tree under sampling (drafts are without
+    replacement), an ordinary tree under greedy acceptance; the other trees of the batch
+    are unaffected. Bit-exact against the oracle."""
+    c = make_case(21, 4, 300, [6, 6, 6, 6], "random")
+    c["token"] = c["token"].copy()
+    par = c["parent"]
+    lo = 6  # tree 1: give a later sibling the token of an earlier one
+    kids = {}
+    for i in range(6):
+        kids.setdefault(int(par[lo + i]), []).append(i)
+    sib = next(v for v in kids.values() if len(v) >= 2)
+    c["token"][lo + sib[-1]] = c["token"][lo + sib[0]]
+    for sample in (False, True):
+        print(f"[case] duplicate siblings sample={sample}", flush=True)
+        got, ref = run(bole, c, 8, sample)
+        assert ref["status"].tolist() == ([0, 4, 0, 0] if sample else [0, 0, 0, 0])
+        np.testing.assert_array_equal(got["status"], ref["status"])
+        clear = ref["margin"] > 1e-9 if sample else np.ones(4, bool)
+        for k in ("accepted_idx", "accepted_len", "bonus"):
+            np.testing.assert_array_equal(got[k][clear], ref[k][clear], err_msg=k)

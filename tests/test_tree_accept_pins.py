@@ -124,3 +124,124 @@ def test_batch_statuses():
     bad = TA.accept_trees(ctx, ctx, rows, rows, parent, token, np.array([0, 4, 2, 6], np.int32),
                           np.zeros(6, np.float32), np.full(3, 0.5, np.float32), TA.SAMPLE, 4)
     assert bad["status"].tolist()[1] == TA.TREE_BAD_SIZE
+
+
+def test_two_rejections_hand_worked():
+    """Exact rationals, worked by hand from the section 9.1 rule. p = (.3, .2, .3, .2),
+    q = (.1, .5, .3, .1); the root's children carry tokens 1 then 2 and both uniforms are
+    0.99, so both are rejected:
+      - token 1: 0.99 * 0.5 >= 0.2. p_res = (p - q)+ = (.2, 0, 0, .1) / .3 = (2/3, 0, 0, 1/3);
+        q_res = q without token 1 = (.1, 0, .3, .1) / .5 = (.2, 0, .6, .2);
+      - token 2: 0.99 * 0.6 >= 0. p_res = (2/3 - .2, 0, 0, 1/3 - .2)+ = (7/15, 0, 0, 2/15),
+        normalised (7/9, 0, 0, 2/9).
+    The bonus is therefore token 0 for u_bonus < 7/9 and token 3 above."""
+    p = np.array([0.3, 0.2, 0.3, 0.2])
+    q = np.array([0.1, 0.5, 0.3, 0.1])
+    parent = np.array([-1, -1], np.int32)
+    token = np.array([1, 2], np.int32)
+    u = np.array([0.99, 0.99])
+    z = np.zeros((2, 4))
+    for ub, want in ((0.0, 0), (0.7777, 0), (0.7778, 3), (0.999, 3)):
+        path, y, _ = TA.accept_tree(p, q, z, z, parent, token, 0, 2, u, ub, TA.SAMPLE, 8)
+        assert path == [] and y == want, (ub, y)
+    # a rule that forgets to take the rejected token out of q_res subtracts q_res(2) = .3
+    # and q_res(3) = .1 instead: p_res -> (17/24, 0, 0, 7/24), and u_bonus in
+    # (17/24, 7/9) would give token 3
+    for ub in (0.72, 0.75, 0.77):
+        path, y, _ = TA.accept_tree(p, q, z, z, parent, token, 0, 2, u, ub, TA.SAMPLE, 8)
+        assert y == 0, ub
+
+
+def _closed_form_walk(p, q, toks, u, ub):
+    """The residual in the closed form the acceptance kernel evaluates (kept here, in the
+    test, to show it equals the oracle's step-by-step residual): after k rejections
+    rp(y) = max(p(y) A - q(y) C, 0) unnormalised, with A <- A / Zp, C <- C / Zp + 1 / Zq,
+    Zq <- Zq - q(x) per rejection of x and Zp = sum(rp). Returns (accepted sibling or -1,
+    bonus, smallest relative margin)."""
+    A, C, Zp, Zq = 1.0, 0.0, 1.0, 1.0
+    rp = p.copy()
+    fresh, margin = True, np.inf
+    for c, x in enumerate(toks):
+        rpx = max(p[x] * A - q[x] * C, 0.0)
+        lhs, rhs = u[c] * q[x] * Zp, rpx * Zq
+        margin = min(margin, TA._rel(lhs, rhs))
+        if lhs < rhs:
+            return c, None, margin
+        A, C = A / Zp, C / Zp + 1.0 / Zq
+        Zq -= q[x]
+        rp = np.maximum(p * A - q * C, 0.0)
+        Zp = float(rp.sum())
+        fresh = False
+    total = float(rp.sum()) if fresh else Zp
+    cs = np.cumsum(rp)
+    t = ub * total
+    margin = min(margin, float(np.abs(cs - t).min()) / t)
+    return -1, min(int(np.searchsorted(cs, t, side="right")), len(p) - 1), margin
+
+
+def test_kernel_residual_form_equals_the_step_by_step_rule():
+    """The acceptance kernel keeps the residual in a closed form instead of stepping it.
+    In real arithmetic the two agree for siblings with distinct tokens (a clamp at 0 never
+    releases, and a rejected token's residual is 0 already). Here both walk the same
+    random sibling groups: every decision whose margin is clear agrees."""
+    rng = np.random.default_rng(42)
+    agree = 0
+    for trial in range(400):
+        V = int(rng.integers(3, 40))
+        k = int(rng.integers(1, min(V, 6) + 1))
+        p = rng.dirichlet(np.full(V, 0.5))
+        q = rng.dirichlet(np.full(V, 0.5))
+        toks = rng.choice(V, size=k, replace=False, p=q)
+        u = rng.random(k)
+        ub = float(rng.random())
+        parent = np.full(k, -1, np.int32)
+        z = np.zeros((k, V))
+        path, y, m = TA.accept_tree(p, q, z, z, parent, toks, 0, k, u, ub, TA.SAMPLE, 8)
+        c, yc, mc = _closed_form_walk(p, q, toks, u, ub)
+        if min(m, mc) <= 1e-9:
+            continue
+        agree += 1
+        assert (path[0] if path else -1) == c, trial
+        if c < 0:
+            assert y == yc, trial
+    assert agree >= 390
+
+
+def test_duplicate_siblings_are_a_bad_tree_under_sampling():
+    """Two siblings with the same token are not a draft without replacement. The closed
+    form would take q(x) out of Zq twice, the step-by-step rule subtracts q_res once more
+    without removing anything: the section 9.1 guarantee holds for neither, so the batch
+    call reports such a tree BAD_TOKEN under sampling. Greedy acceptance is well defined
+    on it (the lowest-index child carrying the argmax) and accepts as usual."""
+    V = 5
+    parent = np.array([-1, -1, 0, 0, 0], np.int32)
+    token = np.array([1, 3, 2, 4, 2], np.int32)       # nodes 2 and 4: same parent, token 2
+    rng = np.random.default_rng(1)
+    ctx = rng.dirichlet(np.ones(V), size=1).astype(np.float32)
+    rows = rng.dirichlet(np.ones(V), size=5).astype(np.float32)
+    offs = np.array([0, 5], np.int32)
+    u = np.full(5, 0.5, np.float32)
+    r = TA.accept_trees(ctx, ctx, rows, rows, parent, token, offs, u, np.full(1, 0.5, np.float32),
+                        TA.SAMPLE, 4)
+    assert r["status"].tolist() == [TA.TREE_BAD_TOKEN] and r["bonus"].tolist() == [-1]
+    g = TA.accept_trees(ctx, None, rows, None, parent, token, offs, None, np.zeros(1),
+                        TA.GREEDY, 4)
+    assert g["status"].tolist() == [TA.TREE_OK]
+    # the same token under different parents is fine
+    token2 = np.array([1, 3, 2, 4, 1], np.int32)
+    r2 = TA.accept_trees(ctx, ctx, rows, rows, parent, token2, offs, u, np.full(1, 0.5, np.float32),
+                         TA.SAMPLE, 4)
+    assert r2["status"].tolist() == [TA.TREE_OK]
+    # and the closed form really does differ from the step-by-step rule on duplicates:
+    # token 0 rejected twice, then token 1 (uniforms 0.99). Step by step, the second
+    # rejection of token 0 leaves p_res = (0, 1, 0), q_res = (0, .5, .5), and token 1 is
+    # accepted (0.99 * .5 < 1). The closed form takes q(0) out of Zq twice (Zq = -0.2),
+    # and its test 0.99 * .2 * .1 < .1 * (-0.2) rejects token 1.
+    p = np.array([0.1, 0.5, 0.4])
+    q = np.array([0.6, 0.2, 0.2])
+    z = np.zeros((3, 3))
+    u3 = np.array([0.99, 0.99, 0.99])
+    c_cf, _, _ = _closed_form_walk(p, q, [0, 0, 1], u3, 0.5)
+    path, _, _ = TA.accept_tree(p, q, z, z, np.full(3, -1, np.int32), np.array([0, 0, 1], np.int32),
+                                0, 3, u3, 0.5, TA.SAMPLE, 8)
+    assert path == [2] and c_cf == -1

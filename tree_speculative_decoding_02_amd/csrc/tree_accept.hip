@@ -9,12 +9,16 @@
 // thread.
 //  - greedy: the target's argmax (lowest id on ties) picks the child, else is the bonus;
 //  - sampling: children in index order, each tested against the residuals left by the
-//    rejected ones before it. With rp = p_res * Zp and rq = q_res * Zq unnormalised, x is
-//    accepted when u * rq(x) * Zp < rp(x) * Zq. The residuals are never stored: after k
-//    rejections rp(y) = max(p(y) A - q(y) C, 0) (a clamp at 0 never releases, so the
-//    step-by-step residual has this closed form), with A, C, Zq updated per rejection of
-//    x as A <- A / Zp, C <- C / Zp + 1 / Zq, Zq <- Zq - q(x), and Zp the sum of the new
-//    rp: one pass over the node's two fp32 rows (16-byte loads). The bonus is drawn from
+//    rejected ones before it: on a rejection of x, p_res <- (p_res - q_res)+ renormalised,
+//    and x leaves q_res, renormalised. With rp = p_res * Zp and rq = q_res * Zq
+//    unnormalised, x is accepted when u * rq(x) * Zp < rp(x) * Zq. The residuals are
+//    never stored: after k rejections rp(y) = max(p(y) A - q(y) C, 0), with A, C, Zq
+//    updated per rejection of x as A <- A / Zp, C <- C / Zp + 1 / Zq, Zq <- Zq - q(x), and
+//    Zp the sum of the new rp: one pass over the node's two fp32 rows (16-byte loads).
+//    This equals the step-by-step residual in real arithmetic because a clamp at 0 never
+//    releases and a rejected token's residual is already 0; it needs siblings with
+//    distinct tokens (drafts without replacement), so a tree with two siblings carrying
+//    one token is reported BOLE_TREE_BAD_TOKEN under sampling. The bonus is drawn from
 //    rp by inverse CDF over tiles of 4 elements per thread: per-wavefront tile sums,
 //    walked in order until the running sum passes the threshold, then a block-wide prefix
 //    sum inside that tile. fp64 throughout, products and differences separately rounded.
@@ -180,6 +184,16 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
         const int tk = lane < n ? a.token[tr.lo + lane] : 0;
         if (st == BOLE_TREE_OK && __any(lane < n && (p < -1 || p >= lane))) st = BOLE_TREE_BAD_PARENT;
         if (st == BOLE_TREE_OK && __any(lane < n && (tk < 0 || tk >= V))) st = BOLE_TREE_BAD_TOKEN;
+        if (st == BOLE_TREE_OK && a.mode == BOLE_ACCEPT_SAMPLE) {
+            // sampling tests siblings as drafts without replacement: two siblings with
+            // one token make a malformed tree
+            bool dup = false;
+            for (int j = 0; j < n; ++j) {  // n is wave-uniform
+                const int pj = __shfl(p, j, 64), tj = __shfl(tk, j, 64);
+                dup |= j < lane && lane < n && pj == p && tj == tk;
+            }
+            if (__any(dup)) st = BOLE_TREE_BAD_TOKEN;
+        }
         s_par[lane] = lane < n ? p : -2;
         s_tok[lane] = tk;
         if (lane == 0) {
