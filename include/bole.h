@@ -40,8 +40,10 @@
  * Rows that belong to no tree are neither read nor written.
  *
  * Ownership. The caller owns every buffer. The library allocates nothing, keeps no
- * pointer after a call returns, and needs no workspace. Every call is asynchronous on
- * the given stream and does not synchronise. Calls are reentrant across streams.
+ * pointer after a call returns, and verify, commit and prepare need no workspace
+ * (bole_workspace_bytes returns 0; the tree builder alone takes one). Every call except
+ * bole_read_status is asynchronous on the given stream and does not synchronise. Calls
+ * are reentrant across streams.
  *
  * Errors.
  *  - Problems visible on the host (null pointers, sizes out of range, unsupported
@@ -51,6 +53,11 @@
  *      - for a tree with a bad size, nothing is written;
  *      - verify fills the rows of a bad-parent tree with NaN;
  *      - commit leaves the state of any bad tree untouched.
+ *    bole_read_status copies the array to the host after the stream's work and returns
+ *    BOLE_ERR_BAD_TREE when any tree is bad.
+ *  - Gates are not checked unless BOLE_FLAG_VALIDATE_GATES is set: a gate outside its
+ *    domain (finite and > 0) then makes the tree BOLE_TREE_BAD_GATE, handled like a
+ *    bad-parent tree (NaN rows from verify, untouched state from commit).
  */
 #ifndef BOLE_H
 #define BOLE_H
@@ -69,7 +76,8 @@ typedef enum {
     BOLE_OK = 0,
     BOLE_ERR_INVALID_VALUE = 1, /* null pointer, negative size, bad enum value */
     BOLE_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels cover */
-    BOLE_ERR_HIP = 3            /* a HIP launch reported an error */
+    BOLE_ERR_HIP = 3,           /* a HIP launch, copy or synchronisation reported an error */
+    BOLE_ERR_BAD_TREE = 4       /* bole_read_status: at least one tree is not BOLE_TREE_OK */
 } bole_status_t;
 
 /* Per-tree device-side status written to tree_status[b]. */
@@ -80,8 +88,10 @@ enum {
     BOLE_TREE_BAD_PARENT = 2, /* some node i has parent[i] < -1 or parent[i] >= i */
     BOLE_TREE_BAD_PATH = 3,   /* commit: length outside [0, max_path], an index outside
                                  the tree, or not a chain that starts at a root */
-    BOLE_TREE_BAD_TOKEN = 4   /* accept: a node's token outside [0, vocab), or (sampling)
+    BOLE_TREE_BAD_TOKEN = 4,  /* accept: a node's token outside [0, vocab), or (sampling)
                                  two siblings carrying the same token */
+    BOLE_TREE_BAD_GATE = 5    /* under BOLE_FLAG_VALIDATE_GATES: a gate of one of the tree's
+                                 nodes (any layer, head or channel) is not finite and > 0 */
 };
 
 typedef enum { BOLE_DTYPE_BF16 = 0, BOLE_DTYPE_F32 = 1 } bole_dtype_t;
@@ -91,10 +101,22 @@ typedef enum { BOLE_GATE_SCALAR = 0, BOLE_GATE_VECTOR = 1 } bole_gate_kind_t;
 enum {
     BOLE_FLAG_FORCE_GENERIC = 1, /* use the plain vector-ALU kernels even where the
                                     matrix-core kernels apply (testing, odd shapes) */
-    BOLE_FLAG_TREES_LE_32 = 2    /* the caller's tree budget is at most 32 nodes: only the
+    BOLE_FLAG_TREES_LE_32 = 2,   /* the caller's tree budget is at most 32 nodes: only the
                                     kernels for such trees are launched, and a tree with
                                     more nodes is reported BOLE_TREE_BAD_SIZE (verify and
                                     commit alike) and left untouched */
+    BOLE_FLAG_VALIDATE_GATES = 4 /* check every gate of every tree's nodes (in every layer
+                                    of the call) against its domain, finite and > 0, on the
+                                    device. A structurally valid tree with a bad gate gets
+                                    BOLE_TREE_BAD_GATE: verify writes NaN over its rows in
+                                    every layer, commit keeps its state in every layer.
+                                    tree_status is then required (NULL gives
+                                    BOLE_ERR_INVALID_VALUE). It costs one extra read of the
+                                    gates (verify: after the verify kernels, plus a pass
+                                    that rewrites the rows of bad trees; commit: before the
+                                    commit kernels); the lazy calls run as commit then
+                                    verify under it. Without the flag a bad gate changes
+                                    only the values of its own tree's outputs and state. */
 };
 
 /* Same type as hipStream_t; NULL is the default stream. */
@@ -148,6 +170,25 @@ BOLE_API const char *bole_status_string(bole_status_t status);
  * `op` is 0 for verify, 1 for commit, 2 for prepare. Touches no device. */
 BOLE_API bole_status_t bole_check_dims(const bole_dims_t *dims, int32_t op);
 
+/* Scratch bytes that bole_tree_verify, bole_commit_path, their lazy and layer-stack forms
+ * and bole_tree_prepare need: always 0. Their kernels keep every intermediate (topology,
+ * cumulative decay, pair weights, partial sums) in registers and LDS, and per-tree
+ * statuses go to the caller's tree_status array. dims may be NULL. */
+BOLE_API size_t bole_workspace_bytes(const bole_dims_t *dims);
+
+/*
+ * Reads the per-tree statuses of earlier calls: a copy of tree_status[0 .. batch-1]
+ * (device int32, as written by any entry point) ordered after the work already on
+ * `stream`, then a synchronisation of `stream`. This is the one call that blocks the
+ * host. host_status (host int32[batch], may be NULL) receives the values. Returns
+ * BOLE_ERR_BAD_TREE if any value is not BOLE_TREE_OK, BOLE_OK if all are,
+ * BOLE_ERR_INVALID_VALUE for batch < 0 or a NULL tree_status with batch > 0, and
+ * BOLE_ERR_HIP if the copy or the synchronisation fails. Nothing is allocated: without
+ * host_status the values pass through a buffer on the stack, 256 at a time.
+ */
+BOLE_API bole_status_t bole_read_status(const int32_t *tree_status, int32_t batch,
+                                        int32_t *host_status, bole_stream_t stream);
+
 /*
  * Tree verification: the closed form of the Bole summary page, section 1
  * ("Tree-Structured Closed Form").
@@ -166,7 +207,10 @@ BOLE_API bole_status_t bole_tree_verify(const float *H0, const void *q, const vo
 
 /*
  * Lazy commit: the previous step's accepted-path commit folded into this step's verify,
- * so that one pass over H0 serves both. The accepted path of a step is known only after
+ * so that one pass over H0 serves both. The restore of the Bole summary page, section 2
+ * ("Token-Level Factor Encoding": after verification only the accepted path's state is
+ * rebuilt), followed by the closed form of section 1; the pages do not say when the
+ * restore runs, and nothing reads the committed state before the next step's verify. The accepted path of a step is known only after
  * that step's verify, so its commit can ride on the next step's verify; H0 is then read
  * once and written once per step instead of read twice and written once.
  * The result is exactly that of
@@ -190,7 +234,10 @@ BOLE_API bole_status_t bole_tree_verify_lazy_commit(
 
 /*
  * Layer stacks: the calls above for num_layers >= 1 layers that share their trees (and
- * paths), in as few launches as the kernels allow. The matrix-core kernels take up to
+ * paths), in as few launches as the kernels allow. The Bole summary page applies the
+ * closed form (section 1) and the restore (section 2) to every linear-recurrence layer of
+ * a hybrid model; its draft tokens, and so its trees and accepted paths, are the same in
+ * every layer. The matrix-core kernels take up to
  * 16 layers per launch (blockIdx.y = layer), so that the workgroups of one layer's tail
  * overlap the next layer's, instead of one launch, ramp and drain per layer. `layers` is
  * a host array of num_layers entries. Each call's result is exactly that of the
@@ -229,8 +276,10 @@ BOLE_API bole_status_t bole_tree_verify_lazy_commit_layers(
     const bole_dims_t *dims, int32_t *tree_status, bole_stream_t stream);
 
 /*
- * Baseline: the naive serial walk that the closed form replaces (Bole summary page,
- * section 1). Every node's state is materialised, in tree order:
+ * Baseline: the naive serial walk that the closed form replaces: the one-state-per-node
+ * approach of the Bole summary page's comparison with prior approaches (a full recurrent
+ * state kept for every draft node, each branch walked serially; section 1 states the
+ * recurrence it walks). Every node's state is materialised, in tree order:
  *     H_i = S_i H_parent(i) + k_i v_i^T   (H_parent = H0 for a root),   out[i] = H_i^T q_i.
  * states (device float [T][H][d_k][d_v], caller-owned: T * H * d_k * d_v floats)
  * receives every H_i; this is the transient memory the closed form avoids. Inputs,
@@ -267,7 +316,10 @@ BOLE_API bole_status_t bole_commit_path(float *H0, const bole_factors_t *factors
 
 /*
  * Tree topology preprocessor: the same per-tree pass that verify and commit run
- * internally, exported on its own.
+ * internally, exported on its own. It computes the two quantities the closed form of the
+ * Bole summary page, section 1, needs per node: which nodes lie on its root-to-node path
+ * (the ancestors j of the sum over the path) and the product of the gates along that
+ * path (D_i, kept as a sum of logarithms).
  * Per node:
  *   depth  (int32 [T])  number of nodes on the root-to-node path;
  *   mask   (uint64 [T]) bit j set when tree-local node j is on that path;

@@ -47,14 +47,14 @@ def _dims(**kw):
 @pytest.mark.parametrize("op", [0, 1, 2])
 def test_check_dims_accepts_valid(op):
     assert bole.lib.bole_check_dims(ctypes.byref(_dims()), op) == bole.BOLE_OK
-    for flags in (1, 2, 3):
+    for flags in range(1, 8):
         assert bole.lib.bole_check_dims(ctypes.byref(_dims(flags=flags)), op) == bole.BOLE_OK
 
 
 @pytest.mark.parametrize("field,value,op,want", [
     ("heads", 0, 0, 1), ("batch", -1, 0, 1), ("d_k", 0, 0, 1), ("d_v", -3, 1, 1),
     ("total_nodes", -1, 2, 1), ("factor_dtype", 7, 0, 1), ("gate_kind", 2, 0, 1),
-    ("flags", 8, 0, 1), ("flags", 4, 1, 1), ("max_path", -1, 1, 1), ("d_k", 257, 0, 2), ("d_v", 512, 1, 2),
+    ("flags", 8, 0, 1), ("flags", 12, 1, 1), ("max_path", -1, 1, 1), ("d_k", 257, 0, 2), ("d_v", 512, 1, 2),
     ("max_path", 65, 1, 2),
 ])
 def test_check_dims_rejects(field, value, op, want):
@@ -182,7 +182,8 @@ def test_tree_accept_checked_without_launch():
 def test_status_strings_and_limits():
     assert bole.lib.bole_max_tree_nodes() == bole.MAX_TREE_NODES == 64
     for code, name in [(0, b"BOLE_OK"), (1, b"BOLE_ERR_INVALID_VALUE"),
-                       (2, b"BOLE_ERR_UNSUPPORTED"), (3, b"BOLE_ERR_HIP")]:
+                       (2, b"BOLE_ERR_UNSUPPORTED"), (3, b"BOLE_ERR_HIP"),
+                       (4, b"BOLE_ERR_BAD_TREE")]:
         assert bole.lib.bole_status_string(code) == name
     assert bole.lib.bole_status_string(99) == b"BOLE_ERR_UNKNOWN"
 
@@ -195,3 +196,56 @@ def test_product_path_does_not_touch_the_oracle():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in text.lower(), fn
+
+
+def test_workspace_bytes_is_zero():
+    """Verify, commit and prepare keep everything in registers and LDS: no scratch for any
+    shape, flag or gate kind."""
+    L = bole.lib
+    assert L.bole_workspace_bytes(None) == 0
+    for kw in ({}, dict(gate_kind=bole.BOLE_GATE_VECTOR), dict(flags=7), dict(batch=4096),
+               dict(d_k=256, d_v=256), dict(factor_dtype=bole.BOLE_DTYPE_F32)):
+        assert L.bole_workspace_bytes(ctypes.byref(_dims(**kw))) == 0, kw
+    assert bole.bole_workspace_bytes() == 0
+
+
+def test_read_status_checked_without_device_work():
+    """Bad arguments are refused before any copy; an empty batch needs no copy."""
+    L = bole.lib
+    host = (ctypes.c_int32 * 4)()
+    assert L.bole_read_status(None, -1, host, None) == bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_read_status(None, 4, host, None) == bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_read_status(None, 0, None, None) == bole.BOLE_OK
+    assert L.bole_read_status(0x1000, 0, host, None) == bole.BOLE_OK
+
+
+def test_validate_gates_needs_tree_status():
+    """BOLE_FLAG_VALIDATE_GATES reports through tree_status: every entry point refuses a
+    NULL one under the flag, before launching (the pointers are never dereferenced)."""
+    L = bole.lib
+    v = _dims(flags=bole.BOLE_FLAG_VALIDATE_GATES)
+    P = [0x1000 * (i + 1) for i in range(9)]
+    assert L.bole_tree_verify(*P[:8], ctypes.byref(v), None, None) == bole.BOLE_ERR_INVALID_VALUE
+    f = bole.bole_factors_t(0x1000, 0x2000, 0x3000, 0x4000, 0x5000)
+    assert L.bole_commit_path(0x6000, ctypes.byref(f), 0x7000, 0x8000, ctypes.byref(v), None,
+                              None, None) == bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_tree_verify_naive(*P, ctypes.byref(v), None, None) == \
+        bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_tree_prepare(0x1000, 0x2000, 0x3000, ctypes.byref(v), None, None, None, None,
+                               None) == bole.BOLE_ERR_INVALID_VALUE
+    one = (bole.bole_layer_t * 1)()
+    e = one[0]
+    e.H0, e.q, e.k, e.v, e.gate, e.out = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000
+    e.prev_k, e.prev_v, e.prev_gate = 0x7000, 0x8000, 0x9000
+    assert L.bole_tree_verify_layers(one, 1, 0xa000, 0xb000, ctypes.byref(v), None, None) == \
+        bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_commit_path_layers(one, 1, 0xa000, 0xb000, 0xc000, 0xd000, ctypes.byref(v),
+                                     None, None, None) == bole.BOLE_ERR_INVALID_VALUE
+    plain = _dims()
+    # the previous step under the flag needs prev_tree_status, this step tree_status
+    assert L.bole_tree_verify_lazy_commit_layers(
+        one, 1, 0xa000, 0xb000, 0xc000, 0xd000, ctypes.byref(v), None, None, 0xa000, 0xb000,
+        ctypes.byref(plain), 0xe000, None) == bole.BOLE_ERR_INVALID_VALUE
+    assert L.bole_tree_verify_lazy_commit_layers(
+        one, 1, 0xa000, 0xb000, 0xc000, 0xd000, ctypes.byref(plain), None, 0xe000, 0xa000,
+        0xb000, ctypes.byref(v), None, None) == bole.BOLE_ERR_INVALID_VALUE

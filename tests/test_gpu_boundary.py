@@ -1,0 +1,195 @@
+"""GPU checks of the boundary's reporting calls: gate validation under
+BOLE_FLAG_VALIDATE_GATES (verify, commit, lazy commit, layer stacks, prepare) and
+bole_read_status, through the C ABI.
+
+A gate outside its domain (finite and > 0) voids its tree: the tree gets
+BOLE_TREE_BAD_GATE, verify writes NaN over its rows in every layer and commit keeps its
+state in every layer. Every other tree's results must equal those of the call without the
+flag bit for bit, and a tree already bad by structure keeps that status."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+BAD_GATE = 5
+
+
+@pytest.fixture(scope="module")
+def bole():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tree_speculative_decoding_02_amd import bole as b
+    return b
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def g(x):
+    return (torch.from_numpy(np.ascontiguousarray(x)) if isinstance(x, np.ndarray) else x).to(dev())
+
+
+def make(seed, vector_gate=False, n_layers=1, sizes=(12, 30, 7, 40, 20, 33), d_v=64):
+    wls = [W.make_random(seed + l, batch=len(sizes), heads=4, d_k=128, d_v=d_v, sizes=list(sizes),
+                         kind="random", vector_gate=vector_gate) for l in range(n_layers)]
+    # one set of trees and paths for every layer: take layer 0's
+    base = wls[0]
+    layers = []
+    for w in wls:
+        y = w.layers[0]
+        layers.append(dict(H0=g(y.H0), q=g(y.q), k=g(y.k), v=g(y.v), gate=g(y.gate).clone()))
+    return base, layers
+
+
+def spoil(layers, base, tree, layer, head, value, node=1):
+    """Sets one gate of tree `tree` (node `node`, every channel for vector gates)."""
+    row = int(base.node_offsets[tree]) + node
+    layers[layer]["gate"][row, head] = value
+
+
+@pytest.mark.parametrize("vector_gate", [False, True])
+def test_verify_validate_gates(bole, vector_gate):
+    base, layers = make(31, vector_gate, n_layers=3)
+    B = base.batch
+    par, offs = g(base.parent), g(base.node_offsets)
+    spoil(layers, base, 1, 0, 2, 0.0)               # a zero gate
+    spoil(layers, base, 3, 2, 0, float("nan"))      # NaN, in the last layer only
+    spoil(layers, base, 4, 1, 3, -0.5)              # negative
+    spoil(layers, base, 5, 1, 1, float("inf"))      # infinite
+    ref = [dict(y, out=None) for y in layers]
+    st_ref = torch.full((B,), -1, dtype=torch.int32, device=dev())
+    bole.bole_tree_verify_layers(ref, par, offs, tree_status=st_ref)
+    got = [dict(y, out=None) for y in layers]
+    st = torch.full((B,), -1, dtype=torch.int32, device=dev())
+    print(f"[case] verify validate vector_gate={vector_gate}", flush=True)
+    bole.bole_tree_verify_layers(got, par, offs, tree_status=st, validate_gates=True)
+    torch.cuda.synchronize()
+    assert st_ref.cpu().tolist() == [0] * B
+    assert st.cpu().tolist() == [0, BAD_GATE, 0, BAD_GATE, BAD_GATE, BAD_GATE]
+    o = base.node_offsets
+    for l in range(3):
+        a, r = got[l]["out"].cpu(), ref[l]["out"].cpu()
+        for b in range(B):
+            rows = slice(int(o[b]), int(o[b + 1]))
+            if b in (1, 3, 4, 5):
+                assert torch.isnan(a[rows]).all(), (l, b)
+            else:
+                assert torch.equal(a[rows], r[rows]), (l, b)
+    # the single-layer call and the status read-back
+    st1 = torch.full((B,), -1, dtype=torch.int32, device=dev())
+    y = layers[0]
+    out1 = bole.bole_tree_verify(y["H0"], y["q"], y["k"], y["v"], y["gate"], par, offs,
+                                 tree_status=st1, validate_gates=True)
+    host, code = bole.bole_read_status(st1)
+    assert host.tolist() == [0, BAD_GATE, 0, 0, 0, 0] and code == bole.BOLE_ERR_BAD_TREE
+    assert torch.equal(out1[int(o[0]):int(o[1])].cpu(), ref[0]["out"][int(o[0]):int(o[1])].cpu())
+
+
+def test_validate_keeps_structural_status(bole):
+    """A tree with a bad parent and a bad gate stays BAD_PARENT; a bad-size tree stays
+    BAD_SIZE; the good trees are unaffected."""
+    base, layers = make(41)
+    parent = base.parent.copy()
+    o = base.node_offsets
+    parent[int(o[2]) + 3] = 5                        # tree 2: node 3 points past itself
+    offs = base.node_offsets.copy()
+    spoil(layers, base, 2, 0, 0, 0.0)
+    spoil(layers, base, 0, 0, 1, -1.0)
+    st = torch.full((base.batch,), -1, dtype=torch.int32, device=dev())
+    y = dict(layers[0], out=None)
+    bole.bole_tree_verify_layers([y], g(parent), g(offs), tree_status=st, validate_gates=True,
+                                 trees_le_32=True)
+    host, code = bole.bole_read_status(st)
+    # tree 3 (40 nodes) and tree 5 (33) exceed the 32-node budget
+    assert host.tolist() == [BAD_GATE, 0, 2, 1, 0, 1] and code == bole.BOLE_ERR_BAD_TREE
+
+
+@pytest.mark.parametrize("vector_gate", [False, True])
+def test_commit_validate_gates(bole, vector_gate):
+    base, layers = make(51, vector_gate, n_layers=2)
+    B = base.batch
+    par, offs = g(base.parent), g(base.node_offsets)
+    ai, al = g(base.accepted_idx), g(base.accepted_len)
+    # bad gates in trees 1 (layer 1) and 4 (layer 0), on nodes off and on the path
+    spoil(layers, base, 1, 1, 0, 0.0, node=int(base.tree_sizes[1]) - 1)
+    spoil(layers, base, 4, 0, 2, float("nan"), node=0)
+    ref = [dict(y, H0=y["H0"].clone()) for y in layers]
+    bole.bole_commit_path_layers(ref, par, offs, ai, al)
+    got = [dict(y, H0=y["H0"].clone()) for y in layers]
+    st = torch.full((B,), -1, dtype=torch.int32, device=dev())
+    pn = torch.full((B, base.max_path), -7, dtype=torch.int32, device=dev())
+    print(f"[case] commit validate vector_gate={vector_gate}", flush=True)
+    bole.bole_commit_path_layers(got, par, offs, ai, al, path_nodes=pn, tree_status=st,
+                                 validate_gates=True)
+    torch.cuda.synchronize()
+    assert st.cpu().tolist() == [0, BAD_GATE, 0, 0, BAD_GATE, 0]
+    pn = pn.cpu()
+    assert (pn[1] == -1).all() and (pn[4] == -1).all()
+    for l in range(2):
+        for b in range(B):
+            if b in (1, 4):
+                assert torch.equal(got[l]["H0"][b].cpu(), layers[l]["H0"][b].cpu()), (l, b)
+            else:
+                assert torch.equal(got[l]["H0"][b].cpu(), ref[l]["H0"][b].cpu()), (l, b)
+    assert int(base.accepted_len[[0, 2, 3, 5]].max()) > 0   # some good tree really commits
+
+
+def test_lazy_validate_gates(bole):
+    """Under the flag the lazy stack equals the two validated calls, statuses included."""
+    prev, players = make(61, n_layers=2)
+    cur, clayers = make(71, n_layers=2, sizes=(5, 64, 18, 9, 32, 1))
+    spoil(players, prev, 2, 1, 3, 0.0)               # previous step: tree 2 keeps its state
+    spoil(clayers, cur, 4, 0, 1, -2.0)               # this step: tree 4 gets NaN rows
+    B = prev.batch
+    pp, po = g(prev.parent), g(prev.node_offsets)
+    ai, al = g(prev.accepted_idx), g(prev.accepted_len)
+    cp, co = g(cur.parent), g(cur.node_offsets)
+    lay = [dict(H0=c["H0"].clone(), q=c["q"], k=c["k"], v=c["v"], gate=c["gate"], prev_k=p["k"],
+                prev_v=p["v"], prev_gate=p["gate"]) for c, p in zip(clayers, players)]
+    pst = torch.full((B,), -1, dtype=torch.int32, device=dev())
+    st = torch.full((B,), -1, dtype=torch.int32, device=dev())
+    bole.bole_tree_verify_lazy_commit_layers(lay, pp, po, ai, al, cp, co, prev_tree_status=pst,
+                                             tree_status=st, validate_gates=True)
+    ref = [dict(H0=c["H0"].clone(), q=c["q"], k=c["k"], v=c["v"], gate=c["gate"], out=None)
+           for c in clayers]
+    pst2 = torch.full((B,), -1, dtype=torch.int32, device=dev())
+    st2 = torch.full((B,), -1, dtype=torch.int32, device=dev())
+    bole.bole_commit_path_layers([dict(y, k=p["k"], v=p["v"], gate=p["gate"])
+                                  for y, p in zip(ref, players)], pp, po, ai, al,
+                                 tree_status=pst2, validate_gates=True)
+    bole.bole_tree_verify_layers(ref, cp, co, tree_status=st2, validate_gates=True)
+    torch.cuda.synchronize()
+    assert pst.cpu().tolist() == pst2.cpu().tolist() == [0, 0, BAD_GATE, 0, 0, 0]
+    assert st.cpu().tolist() == st2.cpu().tolist() == [0, 0, 0, 0, BAD_GATE, 0]
+    for y, r in zip(lay, ref):
+        assert torch.equal(y["H0"].cpu(), r["H0"].cpu())
+        assert torch.equal(y["out"].cpu().nan_to_num(7.0), r["out"].cpu().nan_to_num(7.0))
+
+
+def test_prepare_validate_gates(bole):
+    base, layers = make(81, True)
+    spoil(layers, base, 3, 0, 2, 0.0)
+    st = torch.full((base.batch,), -1, dtype=torch.int32, device=dev())
+    bole.bole_tree_prepare(g(base.parent), g(base.node_offsets), gate=layers[0]["gate"],
+                           tree_status=st, validate_gates=True)
+    host, code = bole.bole_read_status(st)
+    assert host.tolist() == [0, 0, 0, BAD_GATE, 0, 0] and code == bole.BOLE_ERR_BAD_TREE
+
+
+def test_read_status_all_good_and_large_batch(bole):
+    """More than one 256-entry chunk, with and without a host array."""
+    st = torch.zeros(700, dtype=torch.int32, device=dev())
+    host, code = bole.bole_read_status(st)
+    assert code == bole.BOLE_OK and (host == 0).all()
+    st[613] = 3
+    host, code = bole.bole_read_status(st)
+    assert code == bole.BOLE_ERR_BAD_TREE and host[613] == 3 and host.sum() == 3
+    import ctypes
+    assert bole.lib.bole_read_status(ctypes.c_void_p(st.data_ptr()), 700, None,
+                                     bole._stream(None)) == bole.BOLE_ERR_BAD_TREE
+    assert bole.lib.bole_read_status(ctypes.c_void_p(st.data_ptr()), 600, None,
+                                     bole._stream(None)) == bole.BOLE_OK

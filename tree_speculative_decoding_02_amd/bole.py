@@ -13,15 +13,18 @@ import torch  # must be imported before libbole.so: the two share torch's HIP ru
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbole.so")
 
-BOLE_OK, BOLE_ERR_INVALID_VALUE, BOLE_ERR_UNSUPPORTED, BOLE_ERR_HIP = 0, 1, 2, 3
+BOLE_OK, BOLE_ERR_INVALID_VALUE, BOLE_ERR_UNSUPPORTED, BOLE_ERR_HIP, BOLE_ERR_BAD_TREE = 0, 1, 2, 3, 4
 BOLE_TREE_OK, BOLE_TREE_BAD_SIZE, BOLE_TREE_BAD_PARENT, BOLE_TREE_BAD_PATH = 0, 1, 2, 3
+BOLE_TREE_BAD_TOKEN, BOLE_TREE_BAD_GATE = 4, 5
 BOLE_DTYPE_BF16, BOLE_DTYPE_F32 = 0, 1
 BOLE_GATE_SCALAR, BOLE_GATE_VECTOR = 0, 1
 BOLE_FLAG_FORCE_GENERIC = 1
 BOLE_FLAG_TREES_LE_32 = 2
+BOLE_FLAG_VALIDATE_GATES = 4
 MAX_TREE_NODES = 64
 
-EXPORTED = ("bole_max_tree_nodes", "bole_status_string", "bole_check_dims", "bole_tree_verify",
+EXPORTED = ("bole_max_tree_nodes", "bole_status_string", "bole_check_dims",
+            "bole_workspace_bytes", "bole_read_status", "bole_tree_verify",
             "bole_tree_verify_lazy_commit", "bole_tree_verify_layers", "bole_commit_path_layers",
             "bole_tree_verify_lazy_commit_layers", "bole_tree_verify_naive", "bole_commit_path",
             "bole_tree_prepare", "bole_build_tree_workspace_size", "bole_build_tree",
@@ -76,6 +79,10 @@ def _load():
     lib.bole_status_string.argtypes = [ctypes.c_int]
     lib.bole_check_dims.restype = ctypes.c_int
     lib.bole_check_dims.argtypes = [D, I32]
+    lib.bole_workspace_bytes.restype = ctypes.c_size_t
+    lib.bole_workspace_bytes.argtypes = [D]
+    lib.bole_read_status.restype = ctypes.c_int
+    lib.bole_read_status.argtypes = [P, I32, P, P]
     lib.bole_tree_verify.restype = ctypes.c_int
     lib.bole_tree_verify.argtypes = [P, P, P, P, P, P, P, P, D, P, P]
     lib.bole_tree_verify_lazy_commit.restype = ctypes.c_int
@@ -136,12 +143,13 @@ def _need(t, name, dtype=None, device=None):
 
 
 def make_dims(batch, heads, d_k, d_v, total_nodes, factor_dtype, vector_gate, max_path=0,
-              force_generic=False, trees_le_32=False) -> bole_dims_t:
+              force_generic=False, trees_le_32=False, validate_gates=False) -> bole_dims_t:
     fd = {torch.bfloat16: BOLE_DTYPE_BF16, torch.float32: BOLE_DTYPE_F32}.get(factor_dtype)
     if fd is None:
         raise TypeError(f"factor dtype must be bfloat16 or float32, got {factor_dtype}")
     flags = (BOLE_FLAG_FORCE_GENERIC if force_generic else 0) | \
-        (BOLE_FLAG_TREES_LE_32 if trees_le_32 else 0)
+        (BOLE_FLAG_TREES_LE_32 if trees_le_32 else 0) | \
+        (BOLE_FLAG_VALIDATE_GATES if validate_gates else 0)
     return bole_dims_t(batch, heads, d_k, d_v, total_nodes, max_path, fd,
                        BOLE_GATE_VECTOR if vector_gate else BOLE_GATE_SCALAR, flags)
 
@@ -172,10 +180,11 @@ def _factor_dims(H0, q_or_k, v, gate, parent, node_offsets):
 
 
 def bole_tree_verify(H0, q, k, v, gate, parent, node_offsets, out=None, tree_status=None,
-                     stream=None, force_generic=False, trees_le_32=False):
+                     stream=None, force_generic=False, trees_le_32=False, validate_gates=False):
     """out[T, H, d_v] (fp32) = H_i^T q_i for every node, by the parallel closed form.
     trees_le_32: the caller's tree budget is at most 32 nodes (larger trees are reported
-    BOLE_TREE_BAD_SIZE and left untouched)."""
+    BOLE_TREE_BAD_SIZE and left untouched). validate_gates: BOLE_FLAG_VALIDATE_GATES
+    (needs tree_status)."""
     B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
     _need(q, "q", k.dtype, H0.device)
     if tuple(q.shape) != tuple(k.shape):
@@ -189,7 +198,8 @@ def bole_tree_verify(H0, q, k, v, gate, parent, node_offsets, out=None, tree_sta
         _need(tree_status, "tree_status", torch.int32, H0.device)
         if tree_status.numel() < B:
             raise ValueError("tree_status needs B entries")
-    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, force_generic, trees_le_32)
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, force_generic, trees_le_32,
+                     validate_gates)
     _check(lib.bole_tree_verify(_ptr(H0), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(parent),
                                 _ptr(node_offsets), _ptr(out), ctypes.byref(dims),
                                 _ptr(tree_status), _stream(stream)), "bole_tree_verify")
@@ -329,7 +339,8 @@ def bind_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepte
             _need(t, name, torch.int32, H0.device)
     if path_nodes is not None and tuple(path_nodes.shape) != (B, max_path):
         raise ValueError("path_nodes must be [B, max_path]")
-    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, max_path, trees_le_32=trees_le_32)
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, max_path, trees_le_32=trees_le_32,
+                     validate_gates=validate_gates)
     f = bole_factors_t(k.data_ptr(), v.data_ptr(), gate.data_ptr(), parent.data_ptr(),
                        node_offsets.data_ptr())
     args = (_ptr(H0), ctypes.byref(f), _ptr(accepted_idx), _ptr(accepted_len),
@@ -352,7 +363,8 @@ def bind_tree_verify_lazy_commit(H0, prev, prev_accepted_idx, prev_accepted_len,
 
 
 def bole_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepted_len,
-                     path_nodes=None, tree_status=None, stream=None, trees_le_32=False):
+                     path_nodes=None, tree_status=None, stream=None, trees_le_32=False,
+                     validate_gates=False):
     """Commits each tree's accepted path into H0 in place; returns H0."""
     B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
     _need(accepted_idx, "accepted_idx", torch.int32, H0.device)
@@ -365,7 +377,8 @@ def bole_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepte
             _need(t, name, torch.int32, H0.device)
     if path_nodes is not None and tuple(path_nodes.shape) != (B, max_path):
         raise ValueError("path_nodes must be [B, max_path]")
-    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, max_path, trees_le_32=trees_le_32)
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, max_path, trees_le_32=trees_le_32,
+                     validate_gates=validate_gates)
     f = bole_factors_t(k.data_ptr(), v.data_ptr(), gate.data_ptr(), parent.data_ptr(),
                        node_offsets.data_ptr())
     _check(lib.bole_commit_path(_ptr(H0), ctypes.byref(f), _ptr(accepted_idx),
@@ -437,21 +450,22 @@ def _path_args(accepted_idx, accepted_len, path_nodes, B, dev, what=""):
 
 
 def _verify_layers_call(layers, parent, node_offsets, tree_status, stream, force_generic,
-                        trees_le_32):
+                        trees_le_32, validate_gates=False):
     arr, (B, Hh, d_k, d_v, T, vec), _, keep = _layers_args(layers, parent, node_offsets, True)
     dev = layers[0]["H0"].device
-    dims = make_dims(B, Hh, d_k, d_v, T, layers[0]["k"].dtype, vec, 0, force_generic, trees_le_32)
+    dims = make_dims(B, Hh, d_k, d_v, T, layers[0]["k"].dtype, vec, 0, force_generic, trees_le_32,
+                     validate_gates)
     args = (arr, len(layers), _ptr(parent), _ptr(node_offsets), ctypes.byref(dims),
             _status_arg(tree_status, "tree_status", B, dev), _stream(stream))
     return args, keep + [parent, node_offsets, tree_status, dims]
 
 
 def bole_tree_verify_layers(layers, parent, node_offsets, tree_status=None, stream=None,
-                            force_generic=False, trees_le_32=False):
+                            force_generic=False, trees_le_32=False, validate_gates=False):
     """bole_tree_verify on every layer of a stack that shares the trees, in as few
     launches as the kernels allow; returns the list of outs."""
     args, _ = _verify_layers_call(layers, parent, node_offsets, tree_status, stream,
-                                  force_generic, trees_le_32)
+                                  force_generic, trees_le_32, validate_gates)
     _check(lib.bole_tree_verify_layers(*args), "bole_tree_verify_layers")
     return [y["out"] for y in layers]
 
@@ -464,12 +478,12 @@ def bind_tree_verify_layers(layers, parent, node_offsets, tree_status=None, stre
 
 
 def _commit_layers_call(layers, parent, node_offsets, accepted_idx, accepted_len, path_nodes,
-                        tree_status, stream, trees_le_32):
+                        tree_status, stream, trees_le_32, validate_gates=False):
     arr, (B, Hh, d_k, d_v, T, vec), _, keep = _layers_args(layers, parent, node_offsets, False)
     dev = layers[0]["H0"].device
     max_path = _path_args(accepted_idx, accepted_len, path_nodes, B, dev)
     dims = make_dims(B, Hh, d_k, d_v, T, layers[0]["k"].dtype, vec, max_path,
-                     trees_le_32=trees_le_32)
+                     trees_le_32=trees_le_32, validate_gates=validate_gates)
     args = (arr, len(layers), _ptr(parent), _ptr(node_offsets), _ptr(accepted_idx),
             _ptr(accepted_len), ctypes.byref(dims), _ptr(path_nodes),
             _status_arg(tree_status, "tree_status", B, dev), _stream(stream))
@@ -478,10 +492,11 @@ def _commit_layers_call(layers, parent, node_offsets, accepted_idx, accepted_len
 
 
 def bole_commit_path_layers(layers, parent, node_offsets, accepted_idx, accepted_len,
-                            path_nodes=None, tree_status=None, stream=None, trees_le_32=False):
+                            path_nodes=None, tree_status=None, stream=None, trees_le_32=False,
+                            validate_gates=False):
     """bole_commit_path of each layer's k, v, gate along the shared accepted paths."""
     args, _ = _commit_layers_call(layers, parent, node_offsets, accepted_idx, accepted_len,
-                                  path_nodes, tree_status, stream, trees_le_32)
+                                  path_nodes, tree_status, stream, trees_le_32, validate_gates)
     _check(lib.bole_commit_path_layers(*args), "bole_commit_path_layers")
 
 
@@ -494,14 +509,16 @@ def bind_commit_path_layers(layers, parent, node_offsets, accepted_idx, accepted
 
 def _lazy_layers_call(layers, prev_parent, prev_node_offsets, prev_accepted_idx,
                       prev_accepted_len, parent, node_offsets, prev_path_nodes, prev_tree_status,
-                      tree_status, stream, trees_le_32, prev_trees_le_32):
+                      tree_status, stream, trees_le_32, prev_trees_le_32, validate_gates=False):
     arr, (B, Hh, d_k, d_v, T, vec), pT, keep = _layers_args(
         layers, parent, node_offsets, True, prev_parent, prev_node_offsets)
     dev = layers[0]["H0"].device
     max_path = _path_args(prev_accepted_idx, prev_accepted_len, prev_path_nodes, B, dev, "prev_")
     fd = layers[0]["k"].dtype
-    dims = make_dims(B, Hh, d_k, d_v, T, fd, vec, 0, trees_le_32=trees_le_32)
-    pdims = make_dims(B, Hh, d_k, d_v, pT, fd, vec, max_path, trees_le_32=prev_trees_le_32)
+    dims = make_dims(B, Hh, d_k, d_v, T, fd, vec, 0, trees_le_32=trees_le_32,
+                     validate_gates=validate_gates)
+    pdims = make_dims(B, Hh, d_k, d_v, pT, fd, vec, max_path, trees_le_32=prev_trees_le_32,
+                      validate_gates=validate_gates)
     args = (arr, len(layers), _ptr(prev_parent), _ptr(prev_node_offsets), _ptr(prev_accepted_idx),
             _ptr(prev_accepted_len), ctypes.byref(pdims), _ptr(prev_path_nodes),
             _status_arg(prev_tree_status, "prev_tree_status", B, dev), _ptr(parent),
@@ -516,13 +533,14 @@ def bole_tree_verify_lazy_commit_layers(layers, prev_parent, prev_node_offsets,
                                         prev_accepted_idx, prev_accepted_len, parent,
                                         node_offsets, prev_path_nodes=None, prev_tree_status=None,
                                         tree_status=None, stream=None, trees_le_32=False,
-                                        prev_trees_le_32=False):
+                                        prev_trees_le_32=False, validate_gates=False):
     """bole_tree_verify_lazy_commit on every layer of a stack (each layer's prev_k,
-    prev_v, prev_gate along the shared previous path, then its verify); returns the outs."""
+    prev_v, prev_gate along the shared previous path, then its verify); returns the outs.
+    validate_gates sets BOLE_FLAG_VALIDATE_GATES for both steps."""
     args, _ = _lazy_layers_call(layers, prev_parent, prev_node_offsets, prev_accepted_idx,
                                 prev_accepted_len, parent, node_offsets, prev_path_nodes,
                                 prev_tree_status, tree_status, stream, trees_le_32,
-                                prev_trees_le_32)
+                                prev_trees_le_32, validate_gates)
     _check(lib.bole_tree_verify_lazy_commit_layers(*args), "bole_tree_verify_lazy_commit_layers")
     return [y["out"] for y in layers]
 
@@ -653,7 +671,7 @@ def bind_tree_accept(p_ctx, p_node, parent, token, node_offsets, max_path, sampl
 
 
 def bole_tree_prepare(parent, node_offsets, heads=1, d_k=1, gate=None, want_cumlog=False,
-                      tree_status=None, stream=None):
+                      tree_status=None, stream=None, validate_gates=False):
     """Topology export: (depth int32[T], mask int64[T] holding the uint64 bits,
     cumlog float32 [T, H] / [T, H, d_k] or None)."""
     _need(parent, "parent", torch.int32)
@@ -672,8 +690,33 @@ def bole_tree_prepare(parent, node_offsets, heads=1, d_k=1, gate=None, want_cuml
         cum = torch.zeros(tuple(gate.shape), dtype=torch.float32, device=dev)
     if tree_status is not None:
         _need(tree_status, "tree_status", torch.int32, dev)
-    dims = make_dims(B, heads, d_k, 1, T, torch.float32, vec)
+    if validate_gates:
+        _need(gate, "gate", torch.float32, dev)
+        heads = gate.shape[1]
+        d_k = gate.shape[2] if vec else d_k
+    dims = make_dims(B, heads, d_k, 1, T, torch.float32, vec, validate_gates=validate_gates)
     _check(lib.bole_tree_prepare(_ptr(parent), _ptr(node_offsets), _ptr(gate), ctypes.byref(dims),
                                  _ptr(depth), _ptr(mask), _ptr(cum), _ptr(tree_status),
                                  _stream(None)), "bole_tree_prepare")
     return depth, mask, cum
+
+
+# ---- boundary helpers
+
+def bole_workspace_bytes(dims=None) -> int:
+    """Scratch bytes verify, commit and prepare need (always 0)."""
+    return int(lib.bole_workspace_bytes(None if dims is None else ctypes.byref(dims)))
+
+
+def bole_read_status(tree_status, batch=None, stream=None):
+    """Blocks until `stream`'s work is done and returns (host int32 numpy array of the
+    first `batch` statuses, C status: BOLE_OK or BOLE_ERR_BAD_TREE)."""
+    import numpy as np
+    _need(tree_status, "tree_status", torch.int32)
+    B = tree_status.numel() if batch is None else int(batch)
+    host = np.zeros(max(B, 0), np.int32)
+    st = lib.bole_read_status(_ptr(tree_status), B, host.ctypes.data_as(ctypes.c_void_p),
+                              _stream(stream))
+    if st not in (BOLE_OK, BOLE_ERR_BAD_TREE):
+        _check(st, "bole_read_status")
+    return host, st

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "bole")
 LIB = os.path.join(HERE, "libbole.so")
-SOURCES = ["bole_api.hip", "topology.hip", "verify_generic.hip", "verify_mfma.hip", "verify_vec.hip",
+SOURCES = ["bole_api.hip", "topology.hip", "validate.hip", "verify_generic.hip", "verify_mfma.hip", "verify_vec.hip",
            "verify_naive.hip", "commit.hip", "tree_build.hip",
            "tree_accept.hip"]
 ARCH = "gfx950"

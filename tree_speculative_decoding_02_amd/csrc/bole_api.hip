@@ -14,9 +14,41 @@ bole_status_t from_hip(hipError_t e) { return e == hipSuccess ? BOLE_OK : BOLE_E
 
 using bole::kLayersPerLaunch;
 
+// Layers l0 .. l0 + nl - 1 into `out` (nl <= kLayersPerLaunch); with `prev`, each layer's
+// k, v, gate replaced by the previous step's (the commit half of a lazy step).
+int chunk(const bole_layer_t *layers, int num_layers, int l0, bool prev, bole_layer_t *out) {
+    const int nl = num_layers - l0 < kLayersPerLaunch ? num_layers - l0 : kLayersPerLaunch;
+    for (int l = 0; l < nl; ++l) {
+        out[l] = layers[l0 + l];
+        if (prev) {
+            out[l].k = out[l].prev_k;
+            out[l].v = out[l].prev_v;
+            out[l].gate = out[l].prev_gate;
+        }
+    }
+    return nl;
+}
+
+// Gate-domain passes (BOLE_FLAG_VALIDATE_GATES) over every layer, kLayersPerLaunch at a
+// time; kGateReset applies to the first chunk only, so later chunks can only add
+// BOLE_TREE_BAD_GATE.
+hipError_t gate_pass(const bole_layer_t *layers, int num_layers, bool prev, const int32_t *parent,
+                     const int32_t *node_offsets, const bole_dims_t &d, int32_t *tree_status,
+                     int mode, hipStream_t s) {
+    bole_layer_t ch[kLayersPerLaunch];
+    for (int l0 = 0; l0 < num_layers; l0 += kLayersPerLaunch) {
+        const int nl = chunk(layers, num_layers, l0, prev, ch);
+        const hipError_t e = bole::launch_gate_check(ch, nl, parent, node_offsets, d, tree_status,
+                                                     l0 == 0 ? mode : (mode & ~bole::kGateReset), s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // Verify of checked layers, kLayersPerLaunch at a time: matrix cores when they cover
 // every layer of the chunk, else the vector-gate or plain kernel layer by layer. Per-tree
-// outputs come from the first launch only.
+// outputs come from the first launch only. Under BOLE_FLAG_VALIDATE_GATES the gate check
+// follows: every layer's gates, then NaN rows of the trees found bad, in every layer.
 hipError_t dispatch_verify(const bole_layer_t *layers, int num_layers, const int32_t *parent,
                            const int32_t *node_offsets, const bole_dims_t &d,
                            int32_t *tree_status, hipStream_t s) {
@@ -40,32 +72,62 @@ hipError_t dispatch_verify(const bole_layer_t *layers, int num_layers, const int
         }
         if (e != hipSuccess) return e;
     }
+    if (d.flags & BOLE_FLAG_VALIDATE_GATES) {
+        hipError_t e = gate_pass(layers, num_layers, false, parent, node_offsets, d, tree_status,
+                                 bole::kGateDetect, s);
+        if (e == hipSuccess)
+            e = gate_pass(layers, num_layers, false, parent, node_offsets, d, tree_status,
+                          bole::kGateFill, s);
+        return e;
+    }
     return hipSuccess;
 }
 
-hipError_t dispatch_commit(const bole_layer_t *layers, int num_layers, const int32_t *parent,
-                           const int32_t *node_offsets, const int32_t *accepted_idx,
-                           const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
-                           int32_t *tree_status, hipStream_t s) {
+// Commit of checked layers (with `prev`: of the previous step's factors), kLayersPerLaunch
+// at a time. Under BOLE_FLAG_VALIDATE_GATES every tree's gate status over all layers is
+// written first, and the commit kernels keep the state of the trees marked bad.
+hipError_t dispatch_commit(const bole_layer_t *layers, int num_layers, bool prev,
+                           const int32_t *parent, const int32_t *node_offsets,
+                           const int32_t *accepted_idx, const int32_t *accepted_len,
+                           const bole_dims_t &d, int32_t *path_nodes, int32_t *tree_status,
+                           hipStream_t s) {
+    const int32_t *gate_check = nullptr;
+    if (d.flags & BOLE_FLAG_VALIDATE_GATES) {
+        const hipError_t e = gate_pass(layers, num_layers, prev, parent, node_offsets, d,
+                                       tree_status, bole::kGateDetect | bole::kGateReset, s);
+        if (e != hipSuccess) return e;
+        gate_check = tree_status;
+    }
+    bole_layer_t ch[kLayersPerLaunch];
     for (int l0 = 0; l0 < num_layers; l0 += kLayersPerLaunch) {
-        const int nl = num_layers - l0 < kLayersPerLaunch ? num_layers - l0 : kLayersPerLaunch;
-        const hipError_t e = bole::launch_commit(layers + l0, nl, parent, node_offsets,
-                                                 accepted_idx, accepted_len, d,
-                                                 l0 == 0 ? path_nodes : nullptr,
-                                                 l0 == 0 ? tree_status : nullptr, s);
+        const int nl = chunk(layers, num_layers, l0, prev, ch);
+        const hipError_t e = bole::launch_commit(ch, nl, parent, node_offsets, accepted_idx,
+                                                 accepted_len, d, l0 == 0 ? path_nodes : nullptr,
+                                                 l0 == 0 ? tree_status : nullptr, gate_check, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
 // One pass per chunk where the lazy kernel covers it; elsewhere the previous step's
-// commit (on prev_k, prev_v, prev_gate) then this step's verify, chunk by chunk.
+// commit (on prev_k, prev_v, prev_gate) then this step's verify, chunk by chunk. Under
+// BOLE_FLAG_VALIDATE_GATES (either step) the two run as separate calls over the whole
+// stack, each with its gate check.
 hipError_t dispatch_lazy(const bole_layer_t *layers, int num_layers, const bole::PrevPath &prev,
                          const bole_dims_t &pd, const int32_t *parent, const int32_t *node_offsets,
                          const bole_dims_t &d, int32_t *tree_status, hipStream_t s) {
+    if ((d.flags | pd.flags) & BOLE_FLAG_VALIDATE_GATES) {
+        hipError_t e = dispatch_commit(layers, num_layers, true, prev.parent, prev.node_offsets,
+                                       prev.accepted_idx, prev.accepted_len, pd, prev.path_nodes,
+                                       prev.tree_status, s);
+        if (e == hipSuccess)
+            e = dispatch_verify(layers, num_layers, parent, node_offsets, d, tree_status, s);
+        return e;
+    }
+    bole_layer_t pl[kLayersPerLaunch];
     for (int l0 = 0; l0 < num_layers; l0 += kLayersPerLaunch) {
         const bole_layer_t *ch = layers + l0;
-        const int nl = num_layers - l0 < kLayersPerLaunch ? num_layers - l0 : kLayersPerLaunch;
+        const int nl = chunk(layers, num_layers, l0, true, pl);
         bole::PrevPath pp = prev;
         if (l0 > 0) pp.path_nodes = pp.tree_status = nullptr;
         int32_t *ts = l0 == 0 ? tree_status : nullptr;
@@ -73,20 +135,18 @@ hipError_t dispatch_lazy(const bole_layer_t *layers, int num_layers, const bole:
         if (bole::verify_lazy_applies(d, pd, ch, nl)) {
             e = bole::launch_verify_lazy_commit(ch, nl, pp, pd, parent, node_offsets, d, ts, s);
         } else {
-            bole_layer_t pl[kLayersPerLaunch];
-            for (int l = 0; l < nl; ++l) {
-                pl[l] = ch[l];
-                pl[l].k = ch[l].prev_k;
-                pl[l].v = ch[l].prev_v;
-                pl[l].gate = ch[l].prev_gate;
-            }
             e = bole::launch_commit(pl, nl, pp.parent, pp.node_offsets, pp.accepted_idx,
-                                    pp.accepted_len, pd, pp.path_nodes, pp.tree_status, s);
+                                    pp.accepted_len, pd, pp.path_nodes, pp.tree_status, nullptr, s);
             if (e == hipSuccess) e = dispatch_verify(ch, nl, parent, node_offsets, d, ts, s);
         }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// BOLE_FLAG_VALIDATE_GATES reports through tree_status, so it needs one.
+bool validate_ok(const bole_dims_t &d, const int32_t *tree_status) {
+    return !(d.flags & BOLE_FLAG_VALIDATE_GATES) || tree_status != nullptr;
 }
 
 // Host-visible checks shared by the entry points. `need_out`: verify outputs; `distinct`:
@@ -123,6 +183,7 @@ const char *bole_status_string(bole_status_t status) {
         case BOLE_ERR_INVALID_VALUE: return "BOLE_ERR_INVALID_VALUE";
         case BOLE_ERR_UNSUPPORTED: return "BOLE_ERR_UNSUPPORTED";
         case BOLE_ERR_HIP: return "BOLE_ERR_HIP";
+        case BOLE_ERR_BAD_TREE: return "BOLE_ERR_BAD_TREE";
     }
     return "BOLE_ERR_UNKNOWN";
 }
@@ -135,7 +196,8 @@ bole_status_t bole_check_dims(const bole_dims_t *d, int32_t op) {
         return BOLE_ERR_INVALID_VALUE;
     if (d->gate_kind != BOLE_GATE_SCALAR && d->gate_kind != BOLE_GATE_VECTOR)
         return BOLE_ERR_INVALID_VALUE;
-    if (d->flags & ~(BOLE_FLAG_FORCE_GENERIC | BOLE_FLAG_TREES_LE_32)) return BOLE_ERR_INVALID_VALUE;
+    if (d->flags & ~(BOLE_FLAG_FORCE_GENERIC | BOLE_FLAG_TREES_LE_32 | BOLE_FLAG_VALIDATE_GATES))
+        return BOLE_ERR_INVALID_VALUE;
     if (op == kOpCommit && d->max_path < 0) return BOLE_ERR_INVALID_VALUE;
     if (d->d_k > 256 || d->d_v > 256) return BOLE_ERR_UNSUPPORTED;
     if (op == kOpVerify && d->gate_kind == BOLE_GATE_VECTOR && d->d_k > 128)
@@ -144,6 +206,30 @@ bole_status_t bole_check_dims(const bole_dims_t *d, int32_t op) {
     // every packed offset must fit the kernels' 32-bit node indices and 64-bit element offsets
     if ((int64_t)d->batch * d->heads > 0x7fffffffLL) return BOLE_ERR_UNSUPPORTED;
     return BOLE_OK;
+}
+
+size_t bole_workspace_bytes(const bole_dims_t *dims) {
+    (void)dims;
+    return 0;
+}
+
+bole_status_t bole_read_status(const int32_t *tree_status, int32_t batch, int32_t *host_status,
+                               bole_stream_t stream) {
+    if (batch < 0 || (batch > 0 && tree_status == nullptr)) return BOLE_ERR_INVALID_VALUE;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // into the caller's array, or through a small buffer on the stack: nothing allocated
+    int32_t buf[256];
+    bool bad = false;
+    for (int32_t b0 = 0; b0 < batch; b0 += 256) {
+        const int32_t nb = batch - b0 < 256 ? batch - b0 : 256;
+        int32_t *dst = host_status ? host_status + b0 : buf;
+        if (hipMemcpyAsync(dst, tree_status + b0, sizeof(int32_t) * (size_t)nb,
+                           hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return BOLE_ERR_HIP;
+        for (int32_t i = 0; i < nb; ++i) bad = bad || dst[i] != BOLE_TREE_OK;
+    }
+    return bad ? BOLE_ERR_BAD_TREE : BOLE_OK;
 }
 
 bole_status_t bole_tree_verify_layers(const bole_layer_t *layers, int32_t num_layers,
@@ -156,7 +242,7 @@ bole_status_t bole_tree_verify_layers(const bole_layer_t *layers, int32_t num_la
     if (layers == nullptr || num_layers < 1) return BOLE_ERR_INVALID_VALUE;
     if (d.batch == 0) return BOLE_OK;
     if (node_offsets == nullptr || (d.total_nodes > 0 && parent == nullptr) ||
-        !layers_ok(layers, num_layers, d, true, false, nullptr, 2))
+        !layers_ok(layers, num_layers, d, true, false, nullptr, 2) || !validate_ok(d, tree_status))
         return BOLE_ERR_INVALID_VALUE;
     return from_hip(dispatch_verify(layers, num_layers, parent, node_offsets, d, tree_status,
                                     reinterpret_cast<hipStream_t>(stream)));
@@ -193,7 +279,9 @@ bole_status_t bole_tree_verify_lazy_commit_layers(
     if ((d.total_nodes > 0 && parent == nullptr) || (pd.total_nodes > 0 && prev_parent == nullptr))
         return BOLE_ERR_INVALID_VALUE;
     if (pd.max_path > 0 && prev_accepted_idx == nullptr) return BOLE_ERR_INVALID_VALUE;
-    if (!layers_ok(layers, num_layers, d, true, true, &pd, 3)) return BOLE_ERR_INVALID_VALUE;
+    if (!layers_ok(layers, num_layers, d, true, true, &pd, 3) || !validate_ok(d, tree_status) ||
+        !validate_ok(pd, prev_tree_status))
+        return BOLE_ERR_INVALID_VALUE;
     const bole::PrevPath prev = {prev_parent, prev_node_offsets, prev_accepted_idx,
                                  prev_accepted_len, prev_path_nodes, prev_tree_status};
     return from_hip(dispatch_lazy(layers, num_layers, prev, pd, parent, node_offsets, d,
@@ -232,8 +320,17 @@ bole_status_t bole_tree_verify_naive(const float *H0, const void *q, const void 
     if (d.total_nodes > 0 && (q == nullptr || k == nullptr || v == nullptr || gate == nullptr ||
                               parent == nullptr || out == nullptr || states == nullptr))
         return BOLE_ERR_INVALID_VALUE;
-    return from_hip(bole::launch_verify_naive(H0, q, k, v, gate, parent, node_offsets, out, states,
-                                              d, tree_status, reinterpret_cast<hipStream_t>(stream)));
+    if (!validate_ok(d, tree_status)) return BOLE_ERR_INVALID_VALUE;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = bole::launch_verify_naive(H0, q, k, v, gate, parent, node_offsets, out, states,
+                                             d, tree_status, s);
+    if (e == hipSuccess && (d.flags & BOLE_FLAG_VALIDATE_GATES)) {
+        const bole_layer_t y = {const_cast<float *>(H0), q, k, v, gate, out, nullptr, nullptr, nullptr};
+        e = gate_pass(&y, 1, false, parent, node_offsets, d, tree_status, bole::kGateDetect, s);
+        if (e == hipSuccess)
+            e = gate_pass(&y, 1, false, parent, node_offsets, d, tree_status, bole::kGateFill, s);
+    }
+    return from_hip(e);
 }
 
 bole_status_t bole_commit_path_layers(const bole_layer_t *layers, int32_t num_layers,
@@ -249,9 +346,9 @@ bole_status_t bole_commit_path_layers(const bole_layer_t *layers, int32_t num_la
     if (node_offsets == nullptr || accepted_len == nullptr) return BOLE_ERR_INVALID_VALUE;
     if (d.max_path > 0 && accepted_idx == nullptr) return BOLE_ERR_INVALID_VALUE;
     if ((d.total_nodes > 0 && parent == nullptr) ||
-        !layers_ok(layers, num_layers, d, false, false, nullptr, 1))
+        !layers_ok(layers, num_layers, d, false, false, nullptr, 1) || !validate_ok(d, tree_status))
         return BOLE_ERR_INVALID_VALUE;
-    return from_hip(dispatch_commit(layers, num_layers, parent, node_offsets, accepted_idx,
+    return from_hip(dispatch_commit(layers, num_layers, false, parent, node_offsets, accepted_idx,
                                     accepted_len, d, path_nodes, tree_status,
                                     reinterpret_cast<hipStream_t>(stream)));
 }
@@ -281,8 +378,17 @@ bole_status_t bole_tree_prepare(const int32_t *parent, const int32_t *node_offse
     if (node_offsets == nullptr) return BOLE_ERR_INVALID_VALUE;
     if (d.total_nodes > 0 && parent == nullptr) return BOLE_ERR_INVALID_VALUE;
     if (cumlog != nullptr && d.total_nodes > 0 && gate == nullptr) return BOLE_ERR_INVALID_VALUE;
-    return from_hip(bole::launch_prepare(parent, node_offsets, gate, d, depth, mask, cumlog,
-                                         tree_status, reinterpret_cast<hipStream_t>(stream)));
+    const bool validate = (d.flags & BOLE_FLAG_VALIDATE_GATES) != 0;
+    if (validate && (tree_status == nullptr || (d.total_nodes > 0 && gate == nullptr)))
+        return BOLE_ERR_INVALID_VALUE;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = bole::launch_prepare(parent, node_offsets, gate, d, depth, mask, cumlog,
+                                        tree_status, s);
+    if (e == hipSuccess && validate) {
+        const bole_layer_t y = {nullptr, nullptr, nullptr, nullptr, gate, nullptr, nullptr, nullptr, nullptr};
+        e = gate_pass(&y, 1, false, parent, node_offsets, d, tree_status, bole::kGateDetect, s);
+    }
+    return from_hip(e);
 }
 
 size_t bole_build_tree_workspace_size(const bole_build_dims_t *dims) {

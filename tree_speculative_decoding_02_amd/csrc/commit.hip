@@ -35,7 +35,8 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
     const float *__restrict__ gate, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, const int32_t *__restrict__ accepted_idx,
     const int32_t *__restrict__ accepted_len, int32_t *__restrict__ path_nodes,
-    int32_t *__restrict__ tree_status, int H, int DK, int DV, int T, int max_path, int max_n) {
+    int32_t *__restrict__ tree_status, const int32_t *gate_check, int H, int DK, int DV, int T,
+    int max_path, int max_n) {
     __shared__ int s_row[kMaxTree];         // packed row of each path node
     __shared__ float s_a[kMaxTree];         // scalar gate of each path node
     __shared__ int s_len;
@@ -98,6 +99,8 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(
             // empty tree: only a zero-length path is valid
             if (len_raw != 0) st = BOLE_TREE_BAD_PATH;
         }
+        if (st == BOLE_TREE_OK && gate_check && gate_check[b] == BOLE_TREE_BAD_GATE)
+            st = BOLE_TREE_BAD_GATE;
         const bool ok = st == BOLE_TREE_OK;
         const int row = (ok && tid < len) ? tr.lo + x : -1;
         s_row[tid] = row;
@@ -205,8 +208,8 @@ __global__ __launch_bounds__(kCommitThreads) void commit_stream_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, const int32_t *__restrict__ accepted_idx,
     const int32_t *__restrict__ accepted_len, int32_t *__restrict__ path_nodes,
-    int32_t *__restrict__ tree_status, int H, int DK, int DV, int T, int max_path, int max_n,
-    int gpr_log2, int slices, int slice_groups) {
+    int32_t *__restrict__ tree_status, const int32_t *gate_check, int H, int DK, int DV, int T,
+    int max_path, int max_n, int gpr_log2, int slices, int slice_groups) {
     const bole_layer_t &ly = lt.l[blockIdx.y];
     float *const H0 = ly.H0;
     const TF *const k = static_cast<const TF *>(ly.k);
@@ -301,6 +304,11 @@ __global__ __launch_bounds__(kCommitThreads) void commit_stream_kernel(
         } else if (st == BOLE_TREE_OK) {
             if (len_raw != 0) st = BOLE_TREE_BAD_PATH;  // empty tree: only L = 0 is valid
         }
+        // a gate outside its domain (BOLE_FLAG_VALIDATE_GATES): the sequence keeps its
+        // state. The workgroup writing tree_status writes the same decision it reads here,
+        // so every workgroup of the tree decides alike whichever value it reads.
+        if (st == BOLE_TREE_OK && gate_check && gate_check[b] == BOLE_TREE_BAD_GATE)
+            st = BOLE_TREE_BAD_GATE;
         const bool ok = st == BOLE_TREE_OK;
         const int row = (ok && tid < len) ? tr.lo + x : -1;
         s_row[tid] = row;
@@ -395,7 +403,7 @@ template <typename TF, bool VEC>
 static void launch_w(const bole_layer_t *layers, int nl, const int32_t *parent,
                      const int32_t *node_offsets, const int32_t *accepted_idx,
                      const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
-                     int32_t *tree_status, hipStream_t stream) {
+                     int32_t *tree_status, const int32_t *gate_check, hipStream_t stream) {
     const dim3 block(kCommitThreads);
     // streaming kernel: d_v/4 a power of two dividing the block, 16-byte state and factor
     // rows in every layer
@@ -427,7 +435,7 @@ static void launch_w(const bole_layer_t *layers, int nl, const int32_t *parent,
         auto kern = slices > 1 ? commit_stream_kernel<TF, VEC, true> : commit_stream_kernel<TF, VEC, false>;
         kern<<<dim3(U * (unsigned)slices, (unsigned)nl), block, slds, stream>>>(
             lt, parent, node_offsets, accepted_idx, accepted_len, path_nodes, tree_status,
-            d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags),
+            gate_check, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags),
             __builtin_ctz((unsigned)gpr), slices, sg);
         return;
     }
@@ -441,25 +449,25 @@ static void launch_w(const bole_layer_t *layers, int nl, const int32_t *parent,
         if (d.d_v % 4 == 0 && reinterpret_cast<uintptr_t>(y.H0) % 16 == 0)
             commit_kernel<TF, VEC, 4><<<grid, block, lds, stream>>>(
                 y.H0, k, v, y.gate, parent, node_offsets, accepted_idx, accepted_len, pn, ts,
-                d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags));
+                gate_check, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags));
         else
             commit_kernel<TF, VEC, 1><<<grid, block, lds, stream>>>(
                 y.H0, k, v, y.gate, parent, node_offsets, accepted_idx, accepted_len, pn, ts,
-                d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags));
+                gate_check, d.heads, d.d_k, d.d_v, d.total_nodes, d.max_path, max_tree_nodes(d.flags));
     }
 }
 
 hipError_t launch_commit(const bole_layer_t *layers, int nl, const int32_t *parent,
                          const int32_t *node_offsets, const int32_t *accepted_idx,
                          const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
-                         int32_t *tree_status, hipStream_t stream) {
+                         int32_t *tree_status, const int32_t *gate_check, hipStream_t stream) {
     const bool vec = d.gate_kind == BOLE_GATE_VECTOR;
     if (d.factor_dtype == BOLE_DTYPE_F32) {
-        if (vec) launch_w<float, true>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
-        else launch_w<float, false>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
+        if (vec) launch_w<float, true>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, gate_check, stream);
+        else launch_w<float, false>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, gate_check, stream);
     } else {
-        if (vec) launch_w<__bf16, true>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
-        else launch_w<__bf16, false>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, stream);
+        if (vec) launch_w<__bf16, true>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, gate_check, stream);
+        else launch_w<__bf16, false>(layers, nl, parent, node_offsets, accepted_idx, accepted_len, d, path_nodes, tree_status, gate_check, stream);
     }
     return hipGetLastError();
 }

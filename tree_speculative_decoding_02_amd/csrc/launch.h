@@ -65,11 +65,22 @@ hipError_t launch_verify_naive(const float *H0, const void *q, const void *k, co
                                const int32_t *node_offsets, float *out, float *states,
                                const bole_dims_t &d, int32_t *tree_status, hipStream_t stream);
 
-// Commit of each layer's k, v, gate along the shared accepted paths.
+// Commit of each layer's k, v, gate along the shared accepted paths. gate_check (may be
+// NULL): per-tree gate statuses written by a kGateReset pass; a tree marked
+// BOLE_TREE_BAD_GATE there (and otherwise valid) keeps its state and gets that status.
 hipError_t launch_commit(const bole_layer_t *layers, int nl, const int32_t *parent,
                          const int32_t *node_offsets, const int32_t *accepted_idx,
                          const int32_t *accepted_len, const bole_dims_t &d, int32_t *path_nodes,
-                         int32_t *tree_status, hipStream_t stream);
+                         int32_t *tree_status, const int32_t *gate_check, hipStream_t stream);
+
+// Gate-domain check (validate.hip), for BOLE_FLAG_VALIDATE_GATES. Modes: kGateDetect marks
+// structurally valid trees with a non-finite or <= 0 gate BOLE_TREE_BAD_GATE; with
+// kGateReset it also writes BOLE_TREE_OK for every other tree; kGateFill writes NaN over
+// every layer's output rows of the trees marked BOLE_TREE_BAD_GATE.
+enum { kGateDetect = 1, kGateReset = 2, kGateFill = 4 };
+hipError_t launch_gate_check(const bole_layer_t *layers, int num_layers, const int32_t *parent,
+                             const int32_t *node_offsets, const bole_dims_t &d,
+                             int32_t *tree_status, int mode, hipStream_t stream);
 
 // Draft-tree construction (tree_build.hip).
 bool build_dims_ok(const bole_build_dims_t &d);
