@@ -437,12 +437,56 @@ def calibrate_verify_cost(bole, W, wl, dev, stream, timed, sizes=(1, 4, 8, 16, 3
                     "C(N) = 0.1 L_AR + t0 + t1 N, L_AR = t0 + t1"}
 
 
-def config_sweep(dev, reps=20):
-    """Verify and commit on each workload, one layer: the layer's state is copied into 8
-    buffers and the 8 launches of one kind are timed with one event pair (divided by 8).
-    No flags: a caller without a known tree budget takes the general launch. Workloads
-    whose trees have at most 32 nodes are also timed as a caller with that budget runs
-    them (BOLE_FLAG_TREES_LE_32: one launch), under "verify_budget32"."""
+ROTATE_BYTES = 512 * 2 ** 20   # input sets rotated per launch kind: at least this much
+
+
+def sweep_sets(wl, dev, rotate_bytes=ROTATE_BYTES, max_sets=64):
+    """Copies of one workload layer's whole input set (H0, q, k, v, gate, out, trees and
+    paths) on the GPU, enough of them that consecutive launches over the copies read at
+    least `rotate_bytes`: twice the 256 MB last-level cache, so every launch reads its
+    inputs from HBM."""
+    import torch
+    lay = wl.layers[0]
+    tensors = [lay.H0, lay.q, lay.k, lay.v, lay.gate]
+    foot = sum(t.numel() * t.element_size() for t in tensors) + 4 * wl.total_nodes * wl.heads * wl.d_v
+    n = int(min(max_sets, max(1, -(-rotate_bytes // foot))))
+    g = lambda t: t.to(dev).clone()
+    sets = []
+    for _ in range(n):
+        sets.append(dict(H0=g(lay.H0), q=g(lay.q), k=g(lay.k), v=g(lay.v), gate=g(lay.gate),
+                         out=torch.empty((wl.total_nodes, wl.heads, wl.d_v), dtype=torch.float32,
+                                         device=dev),
+                         par=g(torch.from_numpy(wl.parent)), offs=g(torch.from_numpy(wl.node_offsets)),
+                         ai=g(torch.from_numpy(wl.accepted_idx)), al=g(torch.from_numpy(wl.accepted_len))))
+    return sets, foot
+
+
+def time_rotated(fs, stream, reps=20, warm=2):
+    """Median time of one launch (us): the launches `fs` (one per input set) run in turn
+    under one event pair, `reps` times; each time is that span over len(fs)."""
+    import numpy as np
+    import torch
+    for _ in range(warm):
+        for f in fs:
+            f()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        for f in fs:
+            f()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) * 1e3 / len(fs) for a, b in evs]))
+
+
+def config_sweep(dev, reps=20, configs=(1, 2, 3, 4, 5)):
+    """Verify and commit on each workload, one layer. Each launch kind cycles through
+    copies of the whole input set (sweep_sets: at least 512 MB per cycle), so every launch
+    reads cold HBM. No flags: a caller without a known tree budget takes the general
+    launch. Workloads whose trees have at most 32 nodes are also timed as a caller with
+    that budget runs them (BOLE_FLAG_TREES_LE_32), under "verify_budget32"."""
     import numpy as np
     import torch
 
@@ -451,46 +495,34 @@ def config_sweep(dev, reps=20):
     stream = torch.cuda.current_stream()
     names = {1: "tiny_fp32", 2: "mamba2_scalar", 3: "gla_vector", 4: "ragged_large_batch",
              5: "hybrid_stack_one_layer"}
-    for cid in (1, 2, 3, 4, 5):
+    for cid in configs:
         wl = W.make_config(cid, n_layers=1) if cid == 5 else W.make_config(cid)
         lay = wl.layers[0]
-        g = lambda t: t.to(dev)
-        Hs = [g(lay.H0) for _ in range(8)]
-        q, k, v, gate = g(lay.q), g(lay.k), g(lay.v), g(lay.gate)
-        par, offs = g(torch.from_numpy(wl.parent)), g(torch.from_numpy(wl.node_offsets))
-        ai, al = g(torch.from_numpy(wl.accepted_idx)), g(torch.from_numpy(wl.accepted_len))
-        out = torch.empty((wl.total_nodes, wl.heads, wl.d_v), dtype=torch.float32, device=dev)
-        launches = {"verify": [bole.bind_tree_verify(H, q, k, v, gate, par, offs, out,
-                                                     stream=stream) for H in Hs],
-                    "commit": [bole.bind_commit_path(H, k, v, gate, par, offs, ai, al,
-                                                     stream=stream) for H in Hs]}
+        sets, foot = sweep_sets(wl, dev)
+        launches = {"verify": [bole.bind_tree_verify(x["H0"], x["q"], x["k"], x["v"], x["gate"],
+                                                     x["par"], x["offs"], x["out"], stream=stream)
+                               for x in sets],
+                    "commit": [bole.bind_commit_path(x["H0"], x["k"], x["v"], x["gate"], x["par"],
+                                                     x["offs"], x["ai"], x["al"], stream=stream)
+                               for x in sets]}
         s_f = 2 if lay.q.dtype == torch.bfloat16 else 4
         nbytes = {"verify": verify_bytes(wl, s_f), "commit": commit_bytes(wl, s_f)}
         if int(np.diff(wl.node_offsets).max()) <= 32:
             launches["verify_budget32"] = [bole.bind_tree_verify(
-                H, q, k, v, gate, par, offs, out, stream=stream, trees_le_32=True) for H in Hs]
+                x["H0"], x["q"], x["k"], x["v"], x["gate"], x["par"], x["offs"], x["out"],
+                stream=stream, trees_le_32=True) for x in sets]
             nbytes["verify_budget32"] = nbytes["verify"]
         rec = {"kind": "config_sweep", "config": cid, "workload": names[cid], "batch": wl.batch,
                "heads": wl.heads, "d_k": wl.d_k, "d_v": wl.d_v, "total_nodes": wl.total_nodes,
-               "vector_gate": bool(wl.vector_gate), "factor_dtype": str(lay.q.dtype)}
+               "vector_gate": bool(wl.vector_gate), "factor_dtype": str(lay.q.dtype),
+               "input_sets": len(sets), "bytes_per_set": foot}
         for name, fs in launches.items():
-            for _ in range(3):
-                for f in fs:
-                    f()
-            torch.cuda.synchronize()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(reps)]
-            for a, b in evs:
-                a.record(stream)
-                for f in fs:
-                    f()
-                b.record(stream)
-            torch.cuda.synchronize()
-            us = float(np.median([a.elapsed_time(b) * 1e3 / len(fs) for a, b in evs]))
+            us = time_rotated(fs, stream, reps)
             gbs = nbytes[name] / (us * 1e3)
             rec[name] = {"median_us": us, "bytes": nbytes[name], "GB_s": gbs,
                          "frac_hbm_peak": gbs / HBM_PEAK_GBS}
         print(json.dumps(rec), flush=True)
+        del sets, launches
 
 
 def cpu_baseline(wl, min_seconds):

@@ -249,3 +249,25 @@ def test_validate_gates_needs_tree_status():
     assert L.bole_tree_verify_lazy_commit_layers(
         one, 1, 0xa000, 0xb000, 0xc000, 0xd000, ctypes.byref(plain), None, 0xe000, 0xa000,
         0xb000, ctypes.byref(v), None, None) == bole.BOLE_ERR_INVALID_VALUE
+
+
+def test_binding_names_resolve():
+    """Every name a function of the Python binding reads resolves to a parameter, a local,
+    a module global or a builtin (most binding calls need a GPU, so a misspelt or missing
+    name would otherwise surface only there)."""
+    import builtins
+    import symtable
+    path = bole.__file__
+    top = symtable.symtable(open(path).read(), path, "exec")
+    known = set(dir(builtins)) | {s.get_name() for s in top.get_symbols()}
+    missing = []
+
+    def walk(t):
+        for ch in t.get_children():
+            if ch.get_type() == "function":
+                for sym in ch.get_symbols():
+                    if sym.is_global() and sym.get_name() not in known:
+                        missing.append((ch.get_name(), sym.get_name()))
+            walk(ch)
+    walk(top)
+    assert not missing, missing

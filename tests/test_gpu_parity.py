@@ -135,10 +135,10 @@ def test_tree_budget_32_rejects_bigger_trees(bole):
 
 
 def test_config5_all_layers_commit_in_place(bole):
-    """Bench workload: 8 layers, verify then commit in place in every layer; sampled
-    sequences checked against the oracle layer by layer."""
+    """Bench workload: 8 layers, verify then commit in place in every layer; every
+    sequence checked against the oracle layer by layer."""
     wl = W.make_config(5)
-    sample = [0, 1, 17, 40, 63]
+    sample = list(range(wl.batch))
     for layer in range(len(wl.layers)):
         t = to_dev(wl, layer)
         out, st = gpu_verify(bole, t, trees_le_32=True)
@@ -811,3 +811,68 @@ def test_prepare_cumlog(bole):
         ref = oracle.cumlog(wl.layers[0].gate, wl.parent, wl.node_offsets, 3, 16, vec)
         c = cum.double().cpu().numpy()
         assert np.max(np.abs(c - ref) / np.maximum(1.0, np.abs(ref))) < 1e-5
+
+
+PAIR_CASES = [
+    # (name, layers, make_random kwargs): U * layers >= 2048 so the stacked calls take two
+    # units per workgroup, U odd so the last workgroup holds one unit; the single-layer
+    # calls (U < 2048) take one unit per workgroup
+    ("pair_dv64_odd", 3, dict(batch=31, heads=33, d_k=128, d_v=64)),
+    ("pair_dk64_dv32_odd", 3, dict(batch=33, heads=31, d_k=64, d_v=32)),
+]
+
+
+@pytest.mark.parametrize("name,n_layers,kw", PAIR_CASES, ids=[c[0] for c in PAIR_CASES])
+def test_paired_units_equal_single_units(bole, name, n_layers, kw):
+    """Verify (32-node budget) and lazy commit of stacks large enough to pair units in a
+    workgroup: bit for bit the single-layer calls, which do not pair, and within tolerance
+    of the oracle on the first layer."""
+    seed = zlib.crc32(name.encode()) % 10000
+    kw32 = dict(kw, sizes=list(np.random.default_rng(seed).integers(0, 33, size=kw["batch"])))
+    wp, lp = _stack(seed, n_layers, **kw32)
+    wc, lc = _stack(seed + 1, n_layers, **kw32)
+    tp, tc = _tree_dev(wp), _tree_dev(wc)
+    B = wp.batch
+    assert B * kw["heads"] % 2 == 1 and B * kw["heads"] * n_layers >= 2048
+    status = lambda: torch.full((B,), -7, dtype=torch.int32, device=dev())
+    print(f"[case] {name}: verify stack", flush=True)
+    ys = _dev_layers(lc)
+    st_s = status()
+    outs = bole.bole_tree_verify_layers(ys, tc["parent"], tc["offs"], tree_status=st_s,
+                                        trees_le_32=True)
+    for y, o in zip(ys, outs):
+        st_1 = status()
+        o1 = bole.bole_tree_verify(y["H0"], y["q"], y["k"], y["v"], y["gate"], tc["parent"],
+                                   tc["offs"], tree_status=st_1, trees_le_32=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o1) and torch.equal(st_s, st_1)
+    ref, st = oracle.verify_serial(lc[0].H0, lc[0].q, lc[0].k, lc[0].v, lc[0].gate, wc.parent,
+                                   wc.node_offsets, False)
+    assert st_s.cpu().tolist() == st.tolist()
+    assert rel_err_rows(outs[0].double().cpu().numpy(), ref) <= TOL[torch.bfloat16]
+    print(f"[case] {name}: lazy stack", flush=True)
+    ys = _dev_layers(lc, lp)
+    H1 = [y["H0"].clone() for y in ys]
+    pst_s, st_s = status(), status()
+    pn_s = torch.full(tuple(tp["acc_idx"].shape), -7, dtype=torch.int32, device=dev())
+    outs = bole.bole_tree_verify_lazy_commit_layers(
+        ys, tp["parent"], tp["offs"], tp["acc_idx"], tp["acc_len"], tc["parent"], tc["offs"],
+        prev_path_nodes=pn_s, prev_tree_status=pst_s, tree_status=st_s, trees_le_32=True,
+        prev_trees_le_32=True)
+    for y, H, o in zip(ys, H1, outs):
+        pst_1, st_1 = status(), status()
+        pn_1 = torch.empty_like(pn_s)
+        o1 = bole.bole_tree_verify_lazy_commit(
+            H, (y["prev_k"], y["prev_v"], y["prev_gate"], tp["parent"], tp["offs"]),
+            tp["acc_idx"], tp["acc_len"], y["q"], y["k"], y["v"], y["gate"], tc["parent"],
+            tc["offs"], prev_path_nodes=pn_1, prev_tree_status=pst_1, tree_status=st_1,
+            trees_le_32=True, prev_trees_le_32=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y["H0"], H) and torch.equal(o, o1)
+        assert torch.equal(pst_s, pst_1) and torch.equal(st_s, st_1) and torch.equal(pn_s, pn_1)
+    Href, _, _ = oracle.commit_serial(lc[0].H0, lp[0].k, lp[0].v, lp[0].gate, wp.parent,
+                                      wp.node_offsets, wp.accepted_idx, wp.accepted_len, False)
+    oref, _ = oracle.verify_serial(Href, lc[0].q, lc[0].k, lc[0].v, lc[0].gate, wc.parent,
+                                   wc.node_offsets, False)
+    assert rel_err_states(ys[0]["H0"].double().cpu().numpy(), Href) <= TOL[torch.bfloat16]
+    assert rel_err_rows(outs[0].double().cpu().numpy(), oref) <= TOL[torch.bfloat16]

@@ -325,7 +325,8 @@ def bind_tree_verify(H0, q, k, v, gate, parent, node_offsets, out, tree_status=N
 
 
 def bind_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepted_len,
-                     path_nodes=None, tree_status=None, stream=None, trees_le_32=False):
+                     path_nodes=None, tree_status=None, stream=None, trees_le_32=False,
+                     validate_gates=False):
     """Same checks as bole_commit_path, done once; returns a callable that commits into
     H0 in place each time it is called."""
     B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
