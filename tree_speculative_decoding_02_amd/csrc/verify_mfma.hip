@@ -73,12 +73,13 @@ __device__ __forceinline__ void ksplit_body(const bole_layer_t, const int32_t *,
 // workgroup of two wavefronts takes a tree of 33..64 nodes with the row-split body (below)
 // and one of up to 32 nodes on its first wavefront (the second exits); both leave at once,
 // and wave-uniformly, for the trees they do not take, and share one LDS buffer.
-// PAIR (one 64-column group per unit, not FUSED): a workgroup of two wavefronts takes two
-// units, heads 2j and 2j + 1 of one sequence, one per wavefront, each with its own LDS. A
-// node's q, k, v and out rows of two neighbouring heads are adjacent in the token-major
-// layout, so the pair's row pieces form runs twice as long, requested together by one CU.
-template <int DK, int DV, bool LAZY, bool FUSED, bool PAIR>
-__global__ __launch_bounds__(FUSED || PAIR ? 128 : 64, 2) void verify_mfma_tree_kernel(
+// NW > 1 (one 64-column group per unit, not FUSED): a workgroup of NW wavefronts takes NW
+// consecutive units, heads NW j .. NW j + NW - 1 of a sequence, one per wavefront, each with
+// its own LDS. A node's q, k, v and out rows of neighbouring heads are adjacent in the
+// token-major layout, so the group's row pieces form runs NW times as long, requested
+// together by one CU.
+template <int DK, int DV, bool LAZY, bool FUSED, int NW>
+__global__ __launch_bounds__(FUSED ? 128 : 64 * NW, 2) void verify_mfma_tree_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
     int U, int max_n, LazyCommit lc) {
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(FUSED || PAIR ? 128 : 64, 2) void verify_mfma_tree_
     typedef float hvec __attribute__((ext_vector_type(CPL)));
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
     static_assert(!(LAZY && FUSED), "trees of 33..64 nodes follow a lazy commit in their own launch");
-    static_assert(!PAIR || (!FUSED && G == 1), "pairs of units: one column group, one-wavefront body");
+    static_assert(NW == 1 || (!FUSED && G == 1), "unit groups: one column group, one-wavefront body");
     // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR); V rows of the group's columns,
     // row j at [CW j]; lazy commit: k rows and v rows (group columns) of up to kLazyStage
     // path nodes. FUSED: K and V in the buffer the row-split body uses.
@@ -104,11 +105,10 @@ __global__ __launch_bounds__(FUSED || PAIR ? 128 : 64, 2) void verify_mfma_tree_
                                              : ksplit_smem_bytes<DK, DV>())
                                       : 16;
     __shared__ __align__(16) char s_fused[kFusedBytes];
-    constexpr int NW = PAIR ? 2 : 1;        // units (wavefronts) per workgroup
     __shared__ bf16x8 s_k_own[FUSED ? 1 : NW * NN * PPR];
     __shared__ __bf16 s_v_own[FUSED ? 8 : NW * NN * CW];
     __shared__ __bf16 s_pk_all[NW * kLazyStage * DK], s_pv_all[NW * kLazyStage * CW];
-    const int wv = PAIR ? (int)(threadIdx.x >> 6) : 0;  // this wavefront's unit of the pair
+    const int wv = NW > 1 ? (int)(threadIdx.x >> 6) : 0;  // this wavefront's unit of the group
     bf16x8 *const s_k = FUSED ? reinterpret_cast<bf16x8 *>(s_fused) : s_k_own + wv * NN * PPR;
     __bf16 *const s_v = FUSED ? reinterpret_cast<__bf16 *>(s_fused + NN * PPR * 16)
                               : s_v_own + wv * NN * CW;
@@ -130,8 +130,8 @@ __global__ __launch_bounds__(FUSED || PAIR ? 128 : 64, 2) void verify_mfma_tree_
     const int n16 = lane & 15, g = lane >> 4;
     int unit, cg;
     if (G == 1) {
-        unit = PAIR ? 2 * (int)blockIdx.x + wv : (int)blockIdx.x;
-        if (PAIR && unit >= U) return;
+        unit = NW * (int)blockIdx.x + wv;
+        if (NW > 1 && unit >= U) return;
         cg = 0;
     } else {
         const int slot = blockIdx.x >> 3;
@@ -784,9 +784,12 @@ bool verify_mfma_applies(const bole_dims_t &d, const bole_layer_t *layers, int n
     return true;
 }
 
-// Units (sequence x head x layer) from which the one-wavefront kernels take two units per
-// workgroup: below it, one unit per workgroup keeps more CUs busy.
-constexpr uint64_t kPairMinUnits = 2048;
+// Units (sequence x head x layer) from which the one-wavefront kernels take several units
+// per workgroup (kVerifyGroup for verify, kLazyGroup for the lazy commit, measured best):
+// below it, one unit per workgroup keeps more CUs busy.
+constexpr uint64_t kGroupMinUnits = 2048;
+constexpr int kVerifyGroup = 2;
+constexpr int kLazyGroup = 4;
 
 template <int DK, int DV>
 static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *parent,
@@ -798,33 +801,34 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
     // units, each slot G column groups wide, so the groups of a unit share an XCD
     constexpr int G = DV < 64 ? 1 : DV / 64;
     const dim3 grid(G == 1 ? U : ((U + 7) / 8) * 8 * G, (unsigned)nl);
-    // pairs of units once the launch holds enough of them; a small batch keeps one unit per
+    // groups of units once the launch holds enough of them; a small batch keeps one unit per
     // workgroup, so that more CUs take part
-    const bool pair = G == 1 && (uint64_t)U * (uint64_t)nl >= kPairMinUnits;
-    const dim3 pgrid((U + 1) / 2, (unsigned)nl);
+    const bool group = G == 1 && (uint64_t)U * (uint64_t)nl >= kGroupMinUnits;
+    constexpr int NV = G == 1 ? kVerifyGroup : 1, NL = G == 1 ? kLazyGroup : 1;
+    const dim3 vgrid((U + NV - 1) / NV, (unsigned)nl), lgrid((U + NL - 1) / NL, (unsigned)nl);
     LayerTable lt = {};
     for (int l = 0; l < nl; ++l) lt.l[l] = layers[l];
     const LazyCommit none = {};
     const int H = d.heads, T = d.total_nodes;
     if (lazy) {
         // the large trees of this step are verified against the state this launch commits
-        if (pair)
-            verify_mfma_tree_kernel<DK, DV, true, false, G == 1><<<pgrid, dim3(128), 0, stream>>>(
+        if (group)
+            verify_mfma_tree_kernel<DK, DV, true, false, NL><<<lgrid, dim3(64 * NL), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
         else
-            verify_mfma_tree_kernel<DK, DV, true, false, false><<<grid, dim3(64), 0, stream>>>(
+            verify_mfma_tree_kernel<DK, DV, true, false, 1><<<grid, dim3(64), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
         if (max_n > 32)
             verify_mfma_ksplit_kernel<DK, DV><<<grid, dim3(128), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n);
     } else if (max_n > 32) {
-        verify_mfma_tree_kernel<DK, DV, false, true, false><<<grid, dim3(128), 0, stream>>>(
+        verify_mfma_tree_kernel<DK, DV, false, true, 1><<<grid, dim3(128), 0, stream>>>(
             lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
-    } else if (pair) {
-        verify_mfma_tree_kernel<DK, DV, false, false, G == 1><<<pgrid, dim3(128), 0, stream>>>(
+    } else if (group) {
+        verify_mfma_tree_kernel<DK, DV, false, false, NV><<<vgrid, dim3(64 * NV), 0, stream>>>(
             lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
     } else {
-        verify_mfma_tree_kernel<DK, DV, false, false, false><<<grid, dim3(64), 0, stream>>>(
+        verify_mfma_tree_kernel<DK, DV, false, false, 1><<<grid, dim3(64), 0, stream>>>(
             lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
     }
 }
