@@ -395,6 +395,27 @@ BOLE_API bole_status_t bole_build_tree(const float *marginals, const float *cost
                                bole_stream_t stream);
 
 /*
+ * bole_build_tree without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The three launches use a scratch array that the library holds on each GPU
+ * (BOLE_BUILD_NOALLOC_MAX_BYTES, allocated by the code-object loader, kept until the
+ * process ends) instead of the caller's workspace; nothing is allocated or freed here.
+ * Dims whose bole_build_tree_workspace_size exceeds BOLE_BUILD_NOALLOC_MAX_BYTES give
+ * BOLE_ERR_UNSUPPORTED before anything is launched (64 sequences x 8 positions x 128,256
+ * tokens need about 1.1 MB). The stream must belong to the current device. Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race, so serialise them. Nothing in the array needs clearing between calls.
+ * Every other argument, output and error is that of bole_build_tree, and so are the
+ * results, bit for bit.
+ */
+#define BOLE_BUILD_NOALLOC_MAX_BYTES ((size_t)4 << 20)
+BOLE_API bole_status_t bole_build_tree_noalloc(const float *marginals, const float *cost,
+                                               float l_ar, const bole_build_dims_t *dims,
+                                               int32_t *node_offsets, int32_t *parent,
+                                               int32_t *token, float *rho, float *speedup,
+                                               bole_stream_t stream);
+
+/*
  * Tree acceptance: the LLM Primer chapter 9 walkthrough, section 9.1. The target model
  * scores every drafted node in one pass; the walk from the verified context accepts the
  * longest path the target agrees with, and the target's own next token at the first

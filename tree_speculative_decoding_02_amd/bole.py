@@ -28,6 +28,7 @@ EXPORTED = ("bole_max_tree_nodes", "bole_status_string", "bole_check_dims",
             "bole_tree_verify_lazy_commit", "bole_tree_verify_layers", "bole_commit_path_layers",
             "bole_tree_verify_lazy_commit_layers", "bole_tree_verify_naive", "bole_commit_path",
             "bole_tree_prepare", "bole_build_tree_workspace_size", "bole_build_tree",
+            "bole_build_tree_noalloc",
             "bole_tree_accept")
 BOLE_ACCEPT_GREEDY, BOLE_ACCEPT_SAMPLE = 0, 1
 BOLE_BUILD_FIXED_BUDGET = 1
@@ -100,6 +101,8 @@ def _load():
     lib.bole_build_tree_workspace_size.argtypes = [BD]
     lib.bole_build_tree.restype = ctypes.c_int
     lib.bole_build_tree.argtypes = [P, P, ctypes.c_float, P, ctypes.c_size_t, BD, P, P, P, P, P, P]
+    lib.bole_build_tree_noalloc.restype = ctypes.c_int
+    lib.bole_build_tree_noalloc.argtypes = [P, P, ctypes.c_float, BD, P, P, P, P, P, P]
     AD = ctypes.POINTER(bole_accept_dims_t)
     lib.bole_tree_accept.restype = ctypes.c_int
     lib.bole_tree_accept.argtypes = [P, P, P, P, P, P, P, P, P, AD, P, P, P, P, P]
@@ -602,6 +605,40 @@ def bole_build_tree(marginals, cost, l_ar=1.0, n_max=64, fixed=False, workspace=
     capacity B * n_max; node_offsets[B] of them are written), speedup [B]."""
     args, out, _ = _build_call(marginals, cost, l_ar, n_max, fixed, workspace, out, stream)
     _check(lib.bole_build_tree(*args), "bole_build_tree")
+    return out
+
+
+BUILD_NOALLOC_MAX_BYTES = 4 << 20
+
+
+def bole_build_tree_noalloc(marginals, cost, l_ar=1.0, n_max=64, fixed=False, out=None,
+                            stream=None):
+    """bole_build_tree with the library's own scratch array instead of a workspace: the
+    call allocates no device memory (pass `out` to allocate nothing at all). Dims whose
+    workspace would exceed BUILD_NOALLOC_MAX_BYTES raise BoleError (BOLE_ERR_UNSUPPORTED).
+    Calls that overlap on one GPU race on the shared array."""
+    _need(marginals, "marginals", torch.float32)
+    dev = marginals.device
+    if marginals.dim() != 3:
+        raise ValueError("marginals must be [B, depth, vocab]")
+    B, D, V = marginals.shape
+    if cost is not None:
+        _need(cost, "cost", torch.float32, dev)
+        if cost.numel() < n_max:
+            raise ValueError("cost needs n_max entries")
+    dims = bole_build_dims_t(B, D, V, n_max, BOLE_BUILD_FIXED_BUDGET if fixed else 0)
+    if out is None:
+        cap = max(B * n_max, 1)
+        out = {"node_offsets": torch.empty(B + 1, dtype=torch.int32, device=dev),
+               "parent": torch.empty(cap, dtype=torch.int32, device=dev),
+               "token": torch.empty(cap, dtype=torch.int32, device=dev),
+               "rho": torch.empty(cap, dtype=torch.float32, device=dev),
+               "speedup": torch.empty(max(B, 1), dtype=torch.float32, device=dev) if cost is not None else None}
+    _check(lib.bole_build_tree_noalloc(_ptr(marginals), _ptr(cost), ctypes.c_float(l_ar),
+                                       ctypes.byref(dims), _ptr(out["node_offsets"]),
+                                       _ptr(out["parent"]), _ptr(out["token"]),
+                                       _ptr(out.get("rho")), _ptr(out.get("speedup")),
+                                       _stream(stream)), "bole_build_tree_noalloc")
     return out
 
 

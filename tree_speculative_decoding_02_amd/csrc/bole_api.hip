@@ -396,11 +396,10 @@ size_t bole_build_tree_workspace_size(const bole_build_dims_t *dims) {
     return bole::build_workspace_bytes(*dims);
 }
 
-bole_status_t bole_build_tree(const float *marginals, const float *cost, float l_ar,
-                              void *workspace, size_t workspace_bytes,
-                              const bole_build_dims_t *dims, int32_t *node_offsets,
-                              int32_t *parent, int32_t *token, float *rho, float *speedup,
-                              bole_stream_t stream) {
+// Checks shared by the two builder entry points (everything but the workspace).
+static bole_status_t build_args_ok(const float *marginals, const float *cost, float l_ar,
+                            const bole_build_dims_t *dims, const int32_t *node_offsets,
+                            const int32_t *parent, const int32_t *token, const float *speedup) {
     if (dims == nullptr) return BOLE_ERR_INVALID_VALUE;
     const bole_build_dims_t &d = *dims;
     if (d.batch < 0 || d.vocab < 1 || d.n_max < 1 || d.depth < 1 ||
@@ -413,6 +412,34 @@ bole_status_t bole_build_tree(const float *marginals, const float *cost, float l
         return BOLE_ERR_INVALID_VALUE;
     if (cost == nullptr && (!fixed || speedup != nullptr)) return BOLE_ERR_INVALID_VALUE;
     if (!fixed && !(l_ar > 0.f && l_ar < 3.4e38f)) return BOLE_ERR_INVALID_VALUE;
+    return BOLE_OK;
+}
+
+bole_status_t bole_build_tree_noalloc(const float *marginals, const float *cost, float l_ar,
+                                      const bole_build_dims_t *dims, int32_t *node_offsets,
+                                      int32_t *parent, int32_t *token, float *rho,
+                                      float *speedup, bole_stream_t stream) {
+    const bole_status_t st =
+        build_args_ok(marginals, cost, l_ar, dims, node_offsets, parent, token, speedup);
+    if (st != BOLE_OK || dims->batch == 0) return st;
+    static_assert(bole::kBuildScratchBytes == BOLE_BUILD_NOALLOC_MAX_BYTES, "header limit");
+    if (bole::build_workspace_bytes(*dims) > bole::kBuildScratchBytes) return BOLE_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    if (bole::build_scratch(&ws) != hipSuccess) return BOLE_ERR_HIP;
+    return from_hip(bole::launch_build_tree(marginals, cost, l_ar, ws, *dims, node_offsets,
+                                            parent, token, rho, speedup,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+bole_status_t bole_build_tree(const float *marginals, const float *cost, float l_ar,
+                              void *workspace, size_t workspace_bytes,
+                              const bole_build_dims_t *dims, int32_t *node_offsets,
+                              int32_t *parent, int32_t *token, float *rho, float *speedup,
+                              bole_stream_t stream) {
+    const bole_status_t st =
+        build_args_ok(marginals, cost, l_ar, dims, node_offsets, parent, token, speedup);
+    if (st != BOLE_OK || dims->batch == 0) return st;
+    const bole_build_dims_t &d = *dims;
     if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0 ||
         workspace_bytes < bole::build_workspace_bytes(d))
         return BOLE_ERR_INVALID_VALUE;

@@ -85,6 +85,10 @@ hipError_t launch_gate_check(const bole_layer_t *layers, int num_layers, const i
 // Draft-tree construction (tree_build.hip).
 bool build_dims_ok(const bole_build_dims_t &d);
 size_t build_workspace_bytes(const bole_build_dims_t &d);
+// The library-held workspace of bole_build_tree_noalloc on the current GPU (its device
+// address, looked up on the first call on that GPU).
+constexpr size_t kBuildScratchBytes = (size_t)4 << 20;
+hipError_t build_scratch(void **out);
 hipError_t launch_build_tree(const float *marginals, const float *cost, float l_ar,
                              void *workspace, const bole_build_dims_t &d, int32_t *node_offsets,
                              int32_t *parent, int32_t *token, float *rho, float *speedup,

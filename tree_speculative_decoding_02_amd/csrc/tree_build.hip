@@ -13,6 +13,7 @@
 // Only the top 64 tokens of a position can ever be used: one parent's children are
 // inserted in rank order and a tree has at most 64 nodes.
 #include <algorithm>
+#include <mutex>
 
 #include "bole_device.h"
 #include "launch.h"
@@ -598,6 +599,35 @@ bool build_dims_ok(const bole_build_dims_t &d) {
 }
 
 size_t build_workspace_bytes(const bole_build_dims_t &d) { return build_layout(d).total; }
+
+// Scratch of bole_build_tree_noalloc: the workspace of the three launches, held by the
+// library instead of the caller. Every GPU the library runs on has its own copy until the
+// process ends. The kernels write every byte they later read (slice lists padded to 64
+// entries, per-sequence counts, the kept nodes), so nothing is cleared between calls; two
+// calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) char scratch[kBuildScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+
+hipError_t build_scratch(void **out) {
+    static std::mutex mu;
+    static void *ptrs[kMaxScratchDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptrs[dev] == nullptr) {
+        // the name `scratch` stands for a host-side handle: the device address is looked
+        // up once per GPU, with that GPU current, and used for every launch after
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_build_tree(const float *marginals, const float *cost, float l_ar,
                              void *workspace, const bole_build_dims_t &d, int32_t *node_offsets,
