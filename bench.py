@@ -157,6 +157,13 @@ def main():
     print(f"[bench] workload {wl.name}: B={wl.batch} layers={L} H={wl.heads} d_k={wl.d_k} "
           f"d_v={wl.d_v} T={wl.total_nodes}", file=sys.stderr, flush=True)
     g = lambda t: t.to(dev)
+    # transient memory per layer, measured: what Bole keeps per node between verify and
+    # commit is the factors (k, v, gate) and no workspace (bole_workspace_bytes = 0)
+    torch.cuda.synchronize()
+    m0 = torch.cuda.memory_allocated(dev)
+    kept = [g(wl.layers[0].k), g(wl.layers[0].v), g(wl.layers[0].gate)]
+    bole_kept_bytes = torch.cuda.memory_allocated(dev) - m0 + bole.bole_workspace_bytes()
+    del kept
     parent = torch.from_numpy(wl.parent).to(dev)
     offs = torch.from_numpy(wl.node_offsets).to(dev)
     acc_idx = torch.from_numpy(wl.accepted_idx).to(dev)
@@ -270,7 +277,8 @@ def main():
         "wall_ms_per_step": 1e3 * wall / args.steps,
         "transient_bytes_per_layer": {"naive_state_per_node": naive,
                                       "bole_factors": bole_transient,
-                                      "reduction": 1.0 - bole_transient / naive},
+                                      "bole_measured": bole_kept_bytes,
+                                      "reduction": 1.0 - bole_kept_bytes / naive},
     }
     if args.per_layer_forms:
         v1 = [bole.bind_tree_verify(y["H0"], y["q"], y["k"], y["v"], y["gate"], parent, offs,
@@ -526,29 +534,54 @@ def config_sweep(dev, reps=20, configs=(1, 2, 3, 4, 5)):
 
 
 def cpu_baseline(wl, min_seconds):
-    """fp64 CPU oracle (serial walk per node) on whole steps of the same workload:
-    verify of all 8 layers then commit of all 8 layers, repeated until at least
-    min_seconds have passed. Inputs are widened to fp64 before the clock starts."""
+    """The fp64 CPU oracle (serial walk per node) on the same workload: verify of every
+    layer, then commit of every layer, as one step. Run with every core of this process's
+    affinity set and with one thread, three samples each, the median reported. All-core
+    samples are whole steps, repeated to about min_seconds / 6 each; one-thread samples
+    are one layer each, scaled to a step (layers are alike in cost). Inputs are widened to
+    fp64 before the clock starts."""
     import numpy as np
 
     import oracle
+    L = len(wl.layers)
     lays = [[oracle.f64(t) for t in (l.H0, l.q, l.k, l.v, l.gate)] for l in wl.layers]
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        for H0, q, k, v, gate in lays:
+
+    def step(layers):
+        for H0, q, k, v, gate in layers:
             oracle.verify_serial(H0, q, k, v, gate, wl.parent, wl.node_offsets, False)
-        for H0, q, k, v, gate in lays:
+        for H0, q, k, v, gate in layers:
             oracle.commit_serial(H0, k, v, gate, wl.parent, wl.node_offsets, wl.accepted_idx,
                                  wl.accepted_len, False)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
-    return {"value": reps * wl.total_nodes / el, "unit": "draft nodes/s",
-            "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{reps} whole step(s) of the same workload (8-layer verify + commit, "
-                      f"{wl.total_nodes} nodes x {wl.heads} heads per layer), fp64, "
-                      f"{el:.1f} s"}
+
+    cores = len(os.sched_getaffinity(0))
+    out = {}
+    for threads in (cores, 1):
+        oracle.set_threads(threads)
+        used = oracle.threads()
+        samples, total = [], 0.0
+        for _ in range(3):
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                step(lays if threads > 1 else lays[:1])
+                reps += 1
+                el = time.perf_counter() - t0
+                if threads == 1 or el >= min_seconds / 6:
+                    break
+            total += el
+            samples.append(el / reps * (1 if threads > 1 else L))
+        out[threads] = (float(np.median(samples)), used, total)
+    oracle.set_threads(cores)
+    t_all, used_all, s_all = out[cores]
+    t_one, _, s_one = out[1]
+    return {"value": wl.total_nodes / t_all, "unit": "draft nodes/s", "cores": used_all,
+            "kind": "oracle",
+            "sample": f"verify + commit of {L} layers ({wl.total_nodes} nodes x {wl.heads} "
+                      f"heads per layer), fp64: median of 3 samples of whole steps on "
+                      f"{used_all} threads ({s_all:.1f} s in all), and of 3 one-layer samples "
+                      f"on 1 thread scaled to a step ({s_one:.1f} s in all)",
+            "ms_per_step": 1e3 * t_all,
+            "one_thread": {"value": wl.total_nodes / t_one, "ms_per_step": 1e3 * t_one},
+            "affinity_cores": cores}
 
 
 if __name__ == "__main__":

@@ -32,6 +32,8 @@ def configure(lib):
                                          _p, _p, _p, _p, _p, _i64, _p, _p]
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = _int
+    lib.oracle_set_threads.argtypes = [_int]
+    lib.oracle_set_threads.restype = None
     for f in (lib.oracle_topology, lib.oracle_cumlog, lib.oracle_verify_serial,
               lib.oracle_commit_serial):
         f.restype = _int
@@ -50,6 +52,12 @@ def _load():
 def threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's parallel loops from now on (timing only: every result is
+    computed per (sequence, head) and does not depend on the thread count)."""
+    _load().oracle_set_threads(int(n))
 
 
 def f64(x) -> np.ndarray:

@@ -57,6 +57,9 @@ enum { OR_OK = 0, OR_BAD_SIZE = 1, OR_BAD_PARENT = 2, OR_BAD_PATH = 3 };
 /* Number of OpenMP threads the parallel loops below use. */
 int oracle_threads(void) { return omp_get_max_threads(); }
 
+/* Threads for the parallel loops that follow (n >= 1); timing only, results do not depend on it. */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* Structural check of tree b: size first, then every parent link. */
 static int or_tree_check(int64_t b, const int32_t *node_offsets, int64_t total_nodes,
                          const int32_t *parent)

@@ -876,3 +876,37 @@ def test_paired_units_equal_single_units(bole, name, n_layers, kw):
                                    wc.node_offsets, False)
     assert rel_err_states(ys[0]["H0"].double().cpu().numpy(), Href) <= TOL[torch.bfloat16]
     assert rel_err_rows(outs[0].double().cpu().numpy(), oref) <= TOL[torch.bfloat16]
+
+
+def test_fused_pairs_equal_single_units(bole):
+    """Verify without a tree budget (every size up to 64 nodes in one launch) on a stack
+    large enough to take two units per workgroup (an even head count): bit for bit the
+    single-layer calls, which take one unit per workgroup, and within tolerance of the
+    oracle on the first layer; bad trees among them keep their statuses."""
+    kw = dict(batch=33, heads=32, d_k=128, d_v=64, kind="random")
+    wc, lc = _stack(4242, 2, **kw)
+    parent = wc.parent.copy()
+    o = wc.node_offsets
+    big = next(b for b in range(wc.batch) if o[b + 1] - o[b] > 40)
+    parent[o[big] + 35] = 40                       # a bad parent in a large tree
+    tc = _tree_dev(wc)
+    tc["parent"] = torch.from_numpy(parent).to(dev())
+    assert wc.batch * kw["heads"] * 2 >= 2048 and wc.batch * kw["heads"] < 2048
+    status = lambda: torch.full((wc.batch,), -7, dtype=torch.int32, device=dev())
+    print("[case] fused pairs: verify stack", flush=True)
+    ys = _dev_layers(lc)
+    st_s = status()
+    outs = bole.bole_tree_verify_layers(ys, tc["parent"], tc["offs"], tree_status=st_s)
+    for y, out in zip(ys, outs):
+        st_1 = status()
+        o1 = bole.bole_tree_verify(y["H0"], y["q"], y["k"], y["v"], y["gate"], tc["parent"],
+                                   tc["offs"], tree_status=st_1)
+        torch.cuda.synchronize()
+        assert torch.equal(out.nan_to_num(7.0), o1.nan_to_num(7.0)) and torch.equal(st_s, st_1)
+    ref, st = oracle.verify_serial(lc[0].H0, lc[0].q, lc[0].k, lc[0].v, lc[0].gate, parent,
+                                   wc.node_offsets, False)
+    assert st_s.cpu().tolist() == st.tolist() and st[big] == 2
+    good = np.concatenate([np.arange(o[b], o[b + 1]) for b in range(wc.batch) if st[b] == 0])
+    assert rel_err_rows(outs[0].double().cpu().numpy()[good], ref[good]) <= TOL[torch.bfloat16]
+    bad_rows = outs[0][int(o[big]):int(o[big + 1])]
+    assert torch.isnan(bad_rows).all()

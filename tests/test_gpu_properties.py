@@ -1,0 +1,124 @@
+"""Properties of the HIP path that the mathematics fixes, checked on the GPU itself (the
+same properties pin the oracle on the CPU): invariance under a topological relabelling
+of the tree, homogeneity in (H0, v), additivity in H0, a vector gate with equal channels
+against the scalar gate, and identical siblings. Each compares GPU outputs with GPU
+outputs through the C ABI, so a kernel-only mistake that the oracle comparison could
+absorb within its tolerance still has to keep these relations."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests.helpers import rel_err_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bole():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tree_speculative_decoding_02_amd import bole as b
+    return b
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def g(x):
+    return (torch.from_numpy(np.ascontiguousarray(x)) if isinstance(x, np.ndarray) else x).to(dev())
+
+
+def run(bole, H0, q, k, v, gate, parent, offs, **kw):
+    out = bole.bole_tree_verify(g(H0), g(q), g(k), g(v), g(gate), g(parent), g(offs), **kw)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def relabel(rng, parent):
+    """A random topological order of a tree: new index of each node, and the new parent
+    array (a node is placed only after its parent)."""
+    n = len(parent)
+    placed, order = set(), []
+    ready = [i for i in range(n) if parent[i] < 0]
+    while ready:
+        i = ready.pop(rng.integers(len(ready)))
+        order.append(i)
+        placed.add(i)
+        ready += [j for j in range(n) if parent[j] == i]
+    new_of = np.empty(n, np.int64)
+    new_of[order] = np.arange(n)
+    new_parent = np.array([-1 if parent[i] < 0 else new_of[parent[i]] for i in order], np.int32)
+    return new_of, new_parent
+
+
+@pytest.mark.parametrize("vector_gate,sizes", [(False, [32, 17, 5, 64]), (True, [64, 9, 31, 2])])
+def test_relabelling_invariance(bole, vector_gate, sizes):
+    wl = W.make_random(901, batch=len(sizes), heads=3, d_k=128, d_v=64, sizes=sizes,
+                       kind="random", vector_gate=vector_gate)
+    lay = wl.layers[0]
+    rng = np.random.default_rng(5)
+    perm = np.arange(wl.total_nodes)              # new packed row of each old row
+    par2 = wl.parent.copy()
+    for b in range(wl.batch):
+        lo, hi = wl.node_offsets[b], wl.node_offsets[b + 1]
+        new_of, new_par = relabel(rng, wl.parent[lo:hi])
+        perm[lo:hi] = lo + new_of
+        par2[lo:hi] = new_par
+    inv = np.argsort(perm)                        # old row held by each new row
+    sel = lambda t: t[torch.from_numpy(inv)]
+    a = run(bole, lay.H0, lay.q, lay.k, lay.v, lay.gate, wl.parent, wl.node_offsets)
+    b2 = run(bole, lay.H0, sel(lay.q), sel(lay.k), sel(lay.v), sel(lay.gate), par2,
+             wl.node_offsets)
+    assert rel_err_rows(b2.numpy(), a[torch.from_numpy(inv)].numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("vector_gate", [False, True])
+def test_homogeneity_and_additivity(bole, vector_gate):
+    """verify(2 H0, 2 v) = 2 verify(H0, v) exactly (scaling by 2 is exact throughout), and
+    verify(H0a + H0b, v) = verify(H0a, v) + verify(H0b, 0) to rounding."""
+    wl = W.make_random(902, batch=5, heads=2, d_k=128, d_v=64, sizes=[33, 20, 64, 1, 12],
+                       kind="random", vector_gate=vector_gate)
+    lay = wl.layers[0]
+    a = run(bole, lay.H0, lay.q, lay.k, lay.v, lay.gate, wl.parent, wl.node_offsets)
+    a2 = run(bole, 2 * lay.H0, lay.q, lay.k, 2 * lay.v, lay.gate, wl.parent, wl.node_offsets)
+    assert torch.equal(a2, 2 * a)
+    Hb = W.make_random(903, batch=5, heads=2, d_k=128, d_v=64, sizes=[33, 20, 64, 1, 12]).layers[0].H0
+    Hs = (lay.H0.double() + Hb.double()).float()
+    s = run(bole, Hs, lay.q, lay.k, lay.v, lay.gate, wl.parent, wl.node_offsets)
+    zb = run(bole, Hb, lay.q, lay.k, torch.zeros_like(lay.v), lay.gate, wl.parent,
+             wl.node_offsets)
+    sa = run(bole, lay.H0, lay.q, lay.k, lay.v, lay.gate, wl.parent, wl.node_offsets)
+    assert rel_err_rows(s.numpy(), (sa + zb).numpy()) <= 5e-5
+
+
+def test_equal_channel_vector_gate_equals_scalar_gate(bole):
+    """A per-channel gate with every channel equal to the scalar gate (vector-gate
+    kernel) against the scalar gate (scalar kernel): two different kernels, one result."""
+    wl = W.make_random(904, batch=6, heads=4, d_k=128, d_v=64, sizes=[32, 64, 7, 40, 1, 20],
+                       kind="random")
+    lay = wl.layers[0]
+    gvec = lay.gate[:, :, None].expand(-1, -1, 128).contiguous()
+    s = run(bole, lay.H0, lay.q, lay.k, lay.v, lay.gate, wl.parent, wl.node_offsets)
+    vv = run(bole, lay.H0, lay.q, lay.k, lay.v, gvec, wl.parent, wl.node_offsets)
+    assert rel_err_rows(vv.numpy(), s.numpy()) <= 1e-4
+
+
+def test_identical_siblings_have_identical_outputs(bole):
+    """Two siblings with the same q, k, v and gate have the same state, so the same
+    output (to rounding: their self terms sit at different tile positions)."""
+    wl = W.make_random(905, batch=2, heads=3, d_k=128, d_v=64, sizes=[40, 20], kind="random")
+    lay = wl.layers[0]
+    q, k, v, gate = (t.clone() for t in (lay.q, lay.k, lay.v, lay.gate))
+    parent = wl.parent.copy()
+    pairs = []
+    for b, (x, y) in enumerate(((5, 37), (3, 19))):
+        lo = wl.node_offsets[b]
+        parent[lo + y] = parent[lo + x]            # y becomes x's sibling (parent < x < y)
+        for t in (q, k, v, gate):
+            t[lo + y] = t[lo + x]
+        pairs.append((lo + x, lo + y))
+    out = run(bole, lay.H0, q, k, v, gate, parent, wl.node_offsets)
+    for x, y in pairs:
+        assert rel_err_rows(out[y].numpy(), out[x].numpy()) <= 1e-5

@@ -1,4 +1,4 @@
-// mfma_util.h - gfx950 matrix-core, memory and wait helpers shared by the verify kernels.
+// mfma_util.h - gfx950 matrix-core and memory helpers shared by the verify kernels.
 #pragma once
 
 #include "bole_device.h"
@@ -17,29 +17,11 @@ __device__ __forceinline__ bf16x8 load16(const __bf16 *p) {
     return *reinterpret_cast<const bf16x8 *>(p);
 }
 
-// 16-byte global -> LDS copy that bypasses registers (global_load_lds_dwordx4).
-// Lane l's 16 bytes land at lds_wave_base + 16 * l; lds_wave_base must be
-// wave-uniform.
-__device__ __forceinline__ void dma16(const void *src, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(
-        (__attribute__((address_space(1))) void *)(const_cast<void *>(src)),
-        (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
-}
-
 // Streaming forms for data that is read or written exactly once: the non-temporal
 // cache policy keeps it from displacing lines that other waves still use.
 __device__ __forceinline__ bf16x8 load16_stream(const __bf16 *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p));
 }
-
-__device__ __forceinline__ void dma16_stream(const void *src, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(
-        (__attribute__((address_space(1))) void *)(const_cast<void *>(src)),
-        (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, /*non-temporal*/ 2);
-}
-
-// Waits until every memory operation this wave issued (DMA into LDS included) is done.
-__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 // v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], and
 // C rows 4(l/16) + r of column l%16.

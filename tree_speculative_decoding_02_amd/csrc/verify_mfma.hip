@@ -67,19 +67,21 @@ template <int DK, int DV>
 constexpr int ksplit_smem_bytes();
 template <int DK, int DV>
 __device__ __forceinline__ void ksplit_body(const bole_layer_t, const int32_t *, const int32_t *,
-                                            int32_t *, int, int, int, int, char *);
+                                            int32_t *, int, int, int, int, char *, int, int);
 
-// FUSED: every tree size in one launch, for a caller without a budget of 32 nodes. A
-// workgroup of two wavefronts takes a tree of 33..64 nodes with the row-split body (below)
-// and one of up to 32 nodes on its first wavefront (the second exits); both leave at once,
-// and wave-uniformly, for the trees they do not take, and share one LDS buffer.
+// FUSED: every tree size in one launch, for a caller without a budget of 32 nodes. Each
+// unit of the workgroup has two wavefronts and an LDS region of its own: a tree of 33..64
+// nodes takes the row-split body (below) on both, one of up to 32 nodes the one-wavefront
+// body on the first (the second exits); both leave at once, and wave-uniformly, for the
+// trees they do not take. With NW = 2 a workgroup of four wavefronts takes heads 2j and
+// 2j + 1 of one sequence (so one tree, and the row-split barriers of both units match).
 // NW > 1 (one 64-column group per unit, not FUSED): a workgroup of NW wavefronts takes NW
 // consecutive units, heads NW j .. NW j + NW - 1 of a sequence, one per wavefront, each with
 // its own LDS. A node's q, k, v and out rows of neighbouring heads are adjacent in the
 // token-major layout, so the group's row pieces form runs NW times as long, requested
 // together by one CU.
 template <int DK, int DV, bool LAZY, bool FUSED, int NW>
-__global__ __launch_bounds__(FUSED ? 128 : 64 * NW, 2) void verify_mfma_tree_kernel(
+__global__ __launch_bounds__(FUSED ? 128 * NW : 64 * NW, 2) void verify_mfma_tree_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
     int U, int max_n, LazyCommit lc) {
@@ -95,29 +97,31 @@ __global__ __launch_bounds__(FUSED ? 128 : 64 * NW, 2) void verify_mfma_tree_ker
     typedef float hvec __attribute__((ext_vector_type(CPL)));
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
     static_assert(!(LAZY && FUSED), "trees of 33..64 nodes follow a lazy commit in their own launch");
-    static_assert(NW == 1 || (!FUSED && G == 1), "unit groups: one column group, one-wavefront body");
+    static_assert(NW == 1 || G == 1, "unit groups: one column group per unit");
+    static_assert(!FUSED || NW <= 2, "fused unit groups: at most two units");
     // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR); V rows of the group's columns,
     // row j at [CW j]; lazy commit: k rows and v rows (group columns) of up to kLazyStage
     // path nodes. FUSED: K and V in the buffer the row-split body uses.
     constexpr int kLazyStage = LAZY ? 8 : 1;
-    constexpr int kFusedBytes = FUSED ? (NN * PPR * 16 + NN * CW * 2 > ksplit_smem_bytes<DK, DV>()
-                                             ? NN * PPR * 16 + NN * CW * 2
-                                             : ksplit_smem_bytes<DK, DV>())
-                                      : 16;
+    static_assert(NN * PPR * 16 + NN * CW * 2 <= ksplit_smem_bytes<DK, DV>(), "fused LDS region");
+    constexpr int kFusedBytes = FUSED ? NW * ksplit_smem_bytes<DK, DV>() : 16;
     __shared__ __align__(16) char s_fused[kFusedBytes];
     __shared__ bf16x8 s_k_own[FUSED ? 1 : NW * NN * PPR];
     __shared__ __bf16 s_v_own[FUSED ? 8 : NW * NN * CW];
     __shared__ __bf16 s_pk_all[NW * kLazyStage * DK], s_pv_all[NW * kLazyStage * CW];
-    const int wv = NW > 1 ? (int)(threadIdx.x >> 6) : 0;  // this wavefront's unit of the group
-    bf16x8 *const s_k = FUSED ? reinterpret_cast<bf16x8 *>(s_fused) : s_k_own + wv * NN * PPR;
-    __bf16 *const s_v = FUSED ? reinterpret_cast<__bf16 *>(s_fused + NN * PPR * 16)
+    // this wavefront's unit of the group (FUSED: two wavefronts per unit)
+    const int wv = NW > 1 ? (int)(threadIdx.x >> (FUSED ? 7 : 6)) : 0;
+    char *const s_unit = s_fused + (FUSED ? wv * ksplit_smem_bytes<DK, DV>() : 0);
+    bf16x8 *const s_k = FUSED ? reinterpret_cast<bf16x8 *>(s_unit) : s_k_own + wv * NN * PPR;
+    __bf16 *const s_v = FUSED ? reinterpret_cast<__bf16 *>(s_unit + NN * PPR * 16)
                               : s_v_own + wv * NN * CW;
     __bf16 *const s_pk = s_pk_all + wv * kLazyStage * DK;
     __bf16 *const s_pv = s_pv_all + wv * kLazyStage * CW;
     const bole_layer_t &ly = lt.l[blockIdx.y];
     if constexpr (FUSED) {
-        ksplit_body<DK, DV>(ly, parent, node_offsets, tree_status, H, T, U, max_n, s_fused);
-        if (threadIdx.x >= 64) return;
+        ksplit_body<DK, DV>(ly, parent, node_offsets, tree_status, H, T, U, max_n, s_unit,
+                            NW * (int)blockIdx.x + wv, (int)((threadIdx.x >> 6) & 1));
+        if (threadIdx.x & 64) return;  // the second wavefront of each unit
     }
     float *const H0 = ly.H0;                // written only by the lazy commit
     const __bf16 *const q = static_cast<const __bf16 *>(ly.q);
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(FUSED ? 128 : 64 * NW, 2) void verify_mfma_tree_ker
     int unit, cg;
     if (G == 1) {
         unit = NW * (int)blockIdx.x + wv;
-        if (NW > 1 && unit >= U) return;
+        if (unit >= U) return;
         cg = 0;
     } else {
         const int slot = blockIdx.x >> 3;
@@ -487,7 +491,7 @@ template <int DK, int DV>
 __device__ __forceinline__ void ksplit_body(
     const bole_layer_t ly, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
-    int U, int max_n, char *smem) {
+    int U, int max_n, char *smem, int unit_g1, int w_in) {
     constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
     constexpr int CPL = CW / 16;            // columns per lane: 4 or 2
     constexpr int G = DV / CW;              // column groups per unit
@@ -513,11 +517,12 @@ __device__ __forceinline__ void ksplit_body(
     float *const out = ly.out;
 
     const int lane = lane_id();
-    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
+    const int w = __builtin_amdgcn_readfirstlane(w_in);  // wavefront of the unit, 0 or 1
     const int n16 = lane & 15, g = lane >> 4;
     int unit, cg;
     if (G == 1) {
-        unit = blockIdx.x;
+        unit = unit_g1;
+        if (unit >= U) return;  // uniform over the unit's two wavefronts
         cg = 0;
     } else {
         const int slot = blockIdx.x >> 3;
@@ -528,7 +533,7 @@ __device__ __forceinline__ void ksplit_body(
     const int b = unit / H, h = unit - b * H;
     const int c0 = cg * CW;
     const bool first = blockIdx.y == 0 && h == 0 && cg == 0;
-    const bool writer = tree_status != nullptr && first && threadIdx.x == 0;
+    const bool writer = tree_status != nullptr && first && w == 0 && lane_id() == 0;
 
     const TreeRange tr = tree_range(node_offsets, b, T, max_n);
     if (tr.status != BOLE_TREE_OK || tr.n <= 32) return;
@@ -755,7 +760,8 @@ __global__ __launch_bounds__(128, 3) void verify_mfma_ksplit_kernel(
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
     int U, int max_n) {
     __shared__ __align__(16) char smem[ksplit_smem_bytes<DK, DV>()];
-    ksplit_body<DK, DV>(lt.l[blockIdx.y], parent, node_offsets, tree_status, H, T, U, max_n, smem);
+    ksplit_body<DK, DV>(lt.l[blockIdx.y], parent, node_offsets, tree_status, H, T, U, max_n, smem,
+                        (int)blockIdx.x, (int)(threadIdx.x >> 6));
 }
 
 static bool shape_ok(const bole_dims_t &d) {
@@ -822,8 +828,14 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
             verify_mfma_ksplit_kernel<DK, DV><<<grid, dim3(128), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n);
     } else if (max_n > 32) {
-        verify_mfma_tree_kernel<DK, DV, false, true, 1><<<grid, dim3(128), 0, stream>>>(
-            lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
+        // two units per workgroup only when they always share a tree (an even head count)
+        if (group && H % 2 == 0)
+            verify_mfma_tree_kernel<DK, DV, false, true, G == 1 ? 2 : 1><<<
+                dim3(G == 1 ? (U + 1) / 2 : grid.x, (unsigned)nl), dim3(G == 1 ? 256 : 128), 0, stream>>>(
+                lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
+        else
+            verify_mfma_tree_kernel<DK, DV, false, true, 1><<<grid, dim3(128), 0, stream>>>(
+                lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
     } else if (group) {
         verify_mfma_tree_kernel<DK, DV, false, false, NV><<<vgrid, dim3(64 * NV), 0, stream>>>(
             lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
