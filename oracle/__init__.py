@@ -43,9 +43,10 @@ def configure(lib):
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("BOLE_ORACLE_LIB", _build.LIB)  # another build, e.g. sanitized
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        _lib = configure(ctypes.CDLL(_build.LIB))
+        _lib = configure(ctypes.CDLL(path))
     return _lib
 
 

@@ -61,10 +61,13 @@ def test_check_dims_rejects(field, value, op, want):
     assert bole.lib.bole_check_dims(ctypes.byref(_dims(**{field: value})), op) == want
 
 
-def test_vector_gate_width_limit():
-    d = _dims(gate_kind=bole.BOLE_GATE_VECTOR, d_k=256)
-    assert bole.lib.bole_check_dims(ctypes.byref(d), 0) == bole.BOLE_ERR_UNSUPPORTED
-    assert bole.lib.bole_check_dims(ctypes.byref(d), 1) == bole.BOLE_OK
+def test_vector_gate_widths():
+    """Vector gates are taken at every width up to 256, by every operation."""
+    for op in (0, 1, 2):
+        d = _dims(gate_kind=bole.BOLE_GATE_VECTOR, d_k=256)
+        assert bole.lib.bole_check_dims(ctypes.byref(d), op) == bole.BOLE_OK
+        d = _dims(gate_kind=bole.BOLE_GATE_VECTOR, d_k=257)
+        assert bole.lib.bole_check_dims(ctypes.byref(d), op) == bole.BOLE_ERR_UNSUPPORTED
 
 
 def test_null_dims_and_pointers_rejected_without_launch():

@@ -209,6 +209,9 @@ EDGE = [
     ("vector_gate_dk64_dv128", dict(batch=4, heads=3, d_k=64, d_v=128, sizes=[64, 17, 33, 1], vector_gate=True, kind="bestfirst")),
     ("vector_gate_dk128_dv32", dict(batch=4, heads=3, d_k=128, d_v=32, sizes=[48, 64, 5, 31], vector_gate=True, kind="deep", max_path=64)),
     ("vector_gate_dk64_dv256", dict(batch=3, heads=2, d_k=64, d_v=256, sizes=[64, 49, 16], vector_gate=True, kind="bestfirst")),
+    # vector gates at d_k = 256 (the vector-ALU kernel, 64 KB of per-channel decay in LDS)
+    ("vector_gate_dk256", dict(batch=3, heads=2, d_k=256, d_v=64, sizes=[64, 21, 40], vector_gate=True, kind="deep", max_path=64)),
+    ("vector_gate_dk256_dv256_fp32", dict(batch=2, heads=2, d_k=256, d_v=256, sizes=[33, 64], vector_gate=True, factor_dtype=torch.float32, max_path=64)),
     # gates above 1 (allowed: any finite positive decay): cumulative log-decays turn
     # positive along a path, and the vector kernel's mid-range offset M with them
     ("growing_gates_scalar", dict(batch=4, heads=2, d_k=128, d_v=64, sizes=[64, 40, 33, 17], kind="chain", gate_scale=2.5, max_path=64)),

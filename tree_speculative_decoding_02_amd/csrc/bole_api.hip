@@ -200,8 +200,6 @@ bole_status_t bole_check_dims(const bole_dims_t *d, int32_t op) {
         return BOLE_ERR_INVALID_VALUE;
     if (op == kOpCommit && d->max_path < 0) return BOLE_ERR_INVALID_VALUE;
     if (d->d_k > 256 || d->d_v > 256) return BOLE_ERR_UNSUPPORTED;
-    if (op == kOpVerify && d->gate_kind == BOLE_GATE_VECTOR && d->d_k > 128)
-        return BOLE_ERR_UNSUPPORTED;
     if (op == kOpCommit && d->max_path > bole::kMaxTreeNodesHost) return BOLE_ERR_UNSUPPORTED;
     // every packed offset must fit the kernels' 32-bit node indices and 64-bit element offsets
     if ((int64_t)d->batch * d->heads > 0x7fffffffLL) return BOLE_ERR_UNSUPPORTED;

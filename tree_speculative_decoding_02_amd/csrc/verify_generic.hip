@@ -4,8 +4,9 @@
 // Closed Form"), for any supported shape:
 //     o_i = D_i (H_0^T q_i) + sum_{j on path(i)} D_{j->i} (q_i . k_j) v_j
 // channel by channel for vector gates. All nodes are done in parallel; no per-node
-// state is formed. It covers fp32 factors, vector gates, and any d_k/d_v up to 256
-// (vector gates: d_k up to 128). The matrix-core kernel in verify_mfma.hip serves the
+// state is formed. It covers fp32 factors, vector gates, and any d_k/d_v up to 256 (a
+// vector gate's per-channel cumulative log-decay takes 64 d_k floats of LDS: 64 KB at
+// d_k = 256, within gfx950's 160 KB). The matrix-core kernel in verify_mfma.hip serves the
 // bf16 scalar-gate shapes that matter for throughput. This one is the fp32-accurate
 // baseline and the fallback.
 //
