@@ -96,6 +96,8 @@ def parse():
     ap.add_argument("--config-sweep", action="store_true",
                     help="instead of the benchmark, time verify and commit on each of the five "
                          "workloads (one JSON line each)")
+    ap.add_argument("--sweep-configs", default="1,2,3,4,5",
+                    help="workloads the sweep covers (comma-separated ids)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration), then "
                          "time it five times")
@@ -150,7 +152,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.config_sweep:
-        config_sweep(dev)
+        config_sweep(dev, configs=tuple(int(c) for c in args.sweep_configs.split(",")))
         return
     wl = W.make_config(5)
     L = len(wl.layers)
