@@ -20,8 +20,8 @@ resident in HBM before the timed region starts. The 8 layers hold 1 GB, four tim
 The program prints one JSON line:
   - value: draft nodes verified (and committed) through the whole stack per second;
   - roofline: for the step's kernel, its algorithmic bytes per launch over its average
-    launch time (HIP events on the launch stream around each launch), against the
-    8 TB/s HBM peak;
+    launch time (one HIP event pair on the launch stream around the timed steps, which
+    hold nothing but back-to-back launches), against the 8 TB/s HBM peak;
   - cpu_baseline: the fp64 CPU oracle timed on this host on whole steps of the same
     workload.
 """
@@ -189,54 +189,57 @@ def main():
     cstack = bole.bind_commit_path_layers(layers, parent, offs, acc_idx, acc_len, **kw)
 
     def timed(groups, steps, warmup):
-        """Runs `steps` steps of the launch groups; returns (ms per step from one event
-        pair around all steps, per-group span of each step in ms, wall seconds)."""
-        for _ in range(warmup):
-            for grp in groups:
-                for f in grp:
-                    f()
-        torch.cuda.synchronize()
-        recs = [[ev() for _ in range(len(groups) + 1)] for _ in range(steps)]
-        t0, t1 = ev(), ev()
+        """Runs `steps` steps of the launch groups (a step runs every group once, in
+        order); returns (ms per step, average ms of each group's launches, wall seconds).
+        Every time is one event pair around back-to-back launches with nothing between
+        them (an event between two launches costs the stream several microseconds): the
+        step time around all steps, and a group's time around `steps` runs of that group
+        alone (with one group, the step time itself)."""
+        def run(gs, n):
+            for _ in range(n):
+                for grp in gs:
+                    for f in grp:
+                        f()
+
+        def span(gs, n):
+            t0, t1 = ev(), ev()
+            torch.cuda.synchronize()
+            t0.record(stream)
+            run(gs, n)
+            t1.record(stream)
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / n
+
+        run(groups, warmup)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
-        t0.record(stream)
-        for r in recs:
-            # one event pair per launch group: an event between two launches costs the
-            # stream several microseconds
-            r[0].record(stream)
-            for j, grp in enumerate(groups):
-                for f in grp:
-                    f()
-                r[j + 1].record(stream)
-        t1.record(stream)
-        torch.cuda.synchronize()
+        ms = span(groups, steps)
         wall = time.perf_counter() - w0
-        spans = np.array([[r[j].elapsed_time(r[j + 1]) for j in range(len(groups))] for r in recs])
-        return t0.elapsed_time(t1) / steps, spans, wall
+        if len(groups) == 1:
+            return ms, [ms], wall
+        return ms, [span([grp], steps) for grp in groups], wall
 
     # headline: the lazy step, one launch for the stack
-    ms_per_step, l_spans, wall = timed([[lazy]], args.steps, args.warmup)
+    ms_per_step, l_ms, wall = timed([[lazy]], args.steps, args.warmup)
     # the same work in two passes, one launch each for the stack
-    tp_ms, tp_spans, _ = timed([[vstack], [cstack]], args.steps, args.warmup)
+    tp_ms, tp_group_ms, _ = timed([[vstack], [cstack]], args.steps, args.warmup)
 
     nodes = wl.total_nodes
     lb, vb, cb = lazy_bytes(wl), verify_bytes(wl), commit_bytes(wl)
 
-    def kernel_rec(span_ms, nbytes, what):
-        us = 1e3 * float(np.mean(span_ms))
+    def kernel_rec(launch_ms, nbytes, what):
+        us = 1e3 * launch_ms
         gbs = L * nbytes / (us * 1e3)
-        return {"avg_us_per_launch": us, "median_us_per_launch": 1e3 * float(np.median(span_ms)),
-                "layers_per_launch": L, "avg_us_per_layer": us / L,
+        return {"avg_us_per_launch": us, "layers_per_launch": L, "avg_us_per_layer": us / L,
                 "bytes_per_launch": L * nbytes, "bytes_per_layer": nbytes, "GB_s": gbs,
                 "frac_hbm_peak": gbs / HBM_PEAK_GBS, "what": what}
 
     kernels = {
-        "lazy": kernel_rec(l_spans[:, 0], lb, "verify_mfma_tree_kernel<128,64,1,lazy>: previous "
+        "lazy": kernel_rec(l_ms[0], lb, "verify_mfma_tree_kernel<128,64,1,lazy>: previous "
                            "path committed into H0, this tree verified, 8 layers"),
-        "verify": kernel_rec(tp_spans[:, 0], vb, "verify_mfma_tree_kernel<128,64,1>: two-pass "
+        "verify": kernel_rec(tp_group_ms[0], vb, "verify_mfma_tree_kernel<128,64,1>: two-pass "
                              "form, verify of 8 layers"),
-        "commit": kernel_rec(tp_spans[:, 1], cb, "commit_stream_kernel<bf16,scalar>: two-pass "
+        "commit": kernel_rec(tp_group_ms[1], cb, "commit_stream_kernel<bf16,scalar>: two-pass "
                              "form, commit of 8 layers"),
     }
     kd = kernels["lazy"]
@@ -317,13 +320,13 @@ def main():
         cost = torch.tensor([0.1 * l_ar + t0 + t1 * n for n in range(1, nb + 1)],
                             dtype=torch.float32, device=dev)
         build = bole.bind_build_tree(marg, cost, l_ar, n_max=nb, stream=stream)
-        b_ms, b_spans, _ = timed([[build]], args.steps, args.warmup)
-        b_us = 1e3 * float(np.mean(b_spans[:, 0]))
+        b_ms, _, _ = timed([[build]], args.steps, args.warmup)
+        b_us = 1e3 * b_ms
         b_bytes = Bb * Db * Vb * 4   # the marginals, read once; the rest is < 0.1 %
         torch.cuda.synchronize()
         n_kept = build.out["node_offsets"][-1].item()
         result["tree_builder"] = {
-            "avg_us_per_call": b_us, "median_us_per_call": 1e3 * float(np.median(b_spans[:, 0])),
+            "avg_us_per_call": b_us,
             "bytes_per_call": b_bytes, "GB_s": b_bytes / (b_us * 1e3),
             "frac_hbm_peak": b_bytes / (b_us * 1e3) / HBM_PEAK_GBS, "nodes_kept": n_kept,
             "topk_kernel_traffic": recorded_traffic("topk"),
@@ -346,12 +349,11 @@ def main():
             f = bole.bind_tree_accept(p_ctx, p_node, parent, tok, offs, wl.max_path,
                                       sample=mode == "sample", q_ctx=q_ctx, q_node=q_node,
                                       u_node=u_node, u_bonus=u_bonus, stream=stream)
-            _, spans, _ = timed([[f]], args.steps, args.warmup)
+            a_ms, _, _ = timed([[f]], args.steps, args.warmup)
             torch.cuda.synchronize()
             lens = f.out["accepted_len"][:wl.batch].cpu().numpy()
-            us = 1e3 * float(np.mean(spans[:, 0]))
-            rec = {"avg_us_per_call": us, "median_us_per_call": 1e3 * float(np.median(spans[:, 0])),
-                   "mean_accepted_len": float(lens.mean())}
+            us = 1e3 * a_ms
+            rec = {"avg_us_per_call": us, "mean_accepted_len": float(lens.mean())}
             if mode == "greedy":
                 # the walk reads one target row per visited node (the path and its end)
                 nb = int((lens + 1).sum()) * Va * 4
