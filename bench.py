@@ -228,6 +228,8 @@ def main():
         us = 1e3 * launch_ms
         gbs = L * nbytes / (us * 1e3)
         return {"avg_us_per_launch": us, "layers_per_launch": L, "avg_us_per_layer": us / L,
+                # the draft nodes of one layer (every head) over one layer's share of the time
+                "layer_nodes_per_s": wl.total_nodes / (us / L * 1e-6),
                 "bytes_per_launch": L * nbytes, "bytes_per_layer": nbytes, "GB_s": gbs,
                 "frac_hbm_peak": gbs / HBM_PEAK_GBS, "what": what}
 
@@ -532,6 +534,9 @@ def config_sweep(dev, reps=20, configs=(1, 2, 3, 4, 5)):
             gbs = nbytes[name] / (us * 1e3)
             rec[name] = {"median_us": us, "bytes": nbytes[name], "GB_s": gbs,
                          "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+            if name.startswith("verify"):
+                # draft nodes verified per second, every head of the layer
+                rec[name]["nodes_per_s"] = wl.total_nodes / (us * 1e-6)
         print(json.dumps(rec), flush=True)
         del sets, launches
 
