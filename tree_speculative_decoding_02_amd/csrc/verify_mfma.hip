@@ -9,11 +9,12 @@
 //
 // Trees of 1..32 nodes take one wavefront per sequence, head and 64-column group; trees
 // of 33..64 nodes take two wavefronts that split H_0's rows. A batch that may hold larger
-// trees runs both in one fused launch (after a lazy commit, the larger trees take a launch
+// trees runs both in one fused launch (in the lazy form, the larger trees take a launch
 // of their own); each launch covers up to 16 layers that share the trees
-// (blockIdx.y = layer). The LAZY instantiation first applies the previous
-// step's accepted path to H_0 (section 2's restore) and writes it back, in the same pass
-// over H_0. H_0 goes from HBM straight into MFMA operand registers with
+// (blockIdx.y = layer). The LAZY instantiations (one wavefront, and the row split) first
+// apply the previous step's accepted path to H_0 (section 2's restore) and write it back,
+// in the same pass over H_0: each unit is committed by the body that verifies its tree.
+// H_0 goes from HBM straight into MFMA operand registers with
 // row-contiguous 16-byte loads, so a wavefront needs only 12 KB of LDS (K and V) and
 // eight of them fit on a CU: the whole benchmark batch is in flight at once. fp32
 // operands (H_0, W) are split into bf16 hi + lo (two products, about 16 mantissa bits),
@@ -65,9 +66,10 @@ struct LazyCommit {
 // (statuses, path rows) are written by layer 0 only.
 template <int DK, int DV>
 constexpr int ksplit_smem_bytes();
-template <int DK, int DV>
+template <int DK, int DV, bool LAZY>
 __device__ __forceinline__ void ksplit_body(const bole_layer_t, const int32_t *, const int32_t *,
-                                            int32_t *, int, int, int, int, char *, int, int);
+                                            int32_t *, int, int, int, int, char *, int, int,
+                                            const LazyCommit &, __bf16 *);
 
 // FUSED: every tree size in one launch, for a caller without a budget of 32 nodes. Each
 // unit of the workgroup has two wavefronts and an LDS region of its own: a tree of 33..64
@@ -119,8 +121,9 @@ __global__ __launch_bounds__(FUSED ? 128 * NW : 64 * NW, 2) void verify_mfma_tre
     __bf16 *const s_pv = s_pv_all + wv * kLazyStage * CW;
     const bole_layer_t &ly = lt.l[blockIdx.y];
     if constexpr (FUSED) {
-        ksplit_body<DK, DV>(ly, parent, node_offsets, tree_status, H, T, U, max_n, s_unit,
-                            NW * (int)blockIdx.x + wv, (int)((threadIdx.x >> 6) & 1));
+        ksplit_body<DK, DV, false>(ly, parent, node_offsets, tree_status, H, T, U, max_n, s_unit,
+                                   NW * (int)blockIdx.x + wv, (int)((threadIdx.x >> 6) & 1), lc,
+                                   nullptr);
         if (threadIdx.x & 64) return;  // the second wavefront of each unit
     }
     float *const H0 = ly.H0;                // written only by the lazy commit
@@ -154,7 +157,10 @@ __global__ __launch_bounds__(FUSED ? 128 * NW : 64 * NW, 2) void verify_mfma_tre
         if (writer) tree_status[b] = tr.status;
         do_verify = false;
     } else if (tr.n > 32) {
-        do_verify = false;  // the two-wavefront kernel's
+        // the row-split kernel's; after a lazy commit that kernel also commits the
+        // previous path for the unit, in the same pass over H_0
+        if (LAZY) return;
+        do_verify = false;
     } else if (tr.n == 0) {
         if (writer) tree_status[b] = BOLE_TREE_OK;
         do_verify = false;
@@ -486,12 +492,22 @@ constexpr int ksplit_smem_bytes() {
     return 64 * (DK / 8) * 16 + 64 * (DV < 64 ? DV : 64) * 2;
 }
 
-// Both wavefronts of a 128-thread workgroup; smem holds ksplit_smem_bytes bytes.
+// LAZY: the unit's state first takes the previous step's accepted path, with the rules and
+// outputs of bole_commit_path (as in the one-wavefront lazy body), each wavefront updating
+// and writing back the H_0 rows it holds; the tree is then verified against the new state.
+// Path factors are staged kLazyStage path nodes at a time in `lsmem`, this wavefront's own
+// kLazyStage * (DK / 2 + CW) bf16: the k elements of its rows and the v columns.
 template <int DK, int DV>
+constexpr int ksplit_lazy_smem_elems() {
+    return 8 * (DK / 2 + (DV < 64 ? DV : 64));
+}
+
+// Both wavefronts of a 128-thread workgroup; smem holds ksplit_smem_bytes bytes.
+template <int DK, int DV, bool LAZY>
 __device__ __forceinline__ void ksplit_body(
     const bole_layer_t ly, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
-    int U, int max_n, char *smem, int unit_g1, int w_in) {
+    int U, int max_n, char *smem, int unit_g1, int w_in, const LazyCommit &lc, __bf16 *lsmem) {
     constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
     constexpr int CPL = CW / 16;            // columns per lane: 4 or 2
     constexpr int G = DV / CW;              // column groups per unit
@@ -546,7 +562,38 @@ __device__ __forceinline__ void ksplit_body(
     const __bf16 *ku = k + (size_t)lo * rq + (size_t)h * DK;
     const __bf16 *vu = v + (size_t)lo * rv + (size_t)h * DV + c0;
     float *ou = out + (size_t)lo * rv + (size_t)h * DV + c0;
-    const float *hu = ly.H0 + (size_t)unit * DK * DV + c0;
+    float *hu = ly.H0 + (size_t)unit * DK * DV + c0;  // written only by the lazy commit
+
+    // lazy commit, first: the previous tree's offsets, its parent links and the path
+    // indices (lane m: path position m; lx: the path node of each factor chunk this lane
+    // stages first). A chunk is 16 bytes of a path node's k elements on this wavefront's
+    // rows, or of its v row's group columns.
+    constexpr int kStage = 8;               // path nodes staged at a time
+    constexpr int DKH = DK / 2;             // k elements of this wavefront's rows
+    constexpr int LCK = DKH / 8, LCV = CW / 8, LCPN = LCK + LCV;
+    constexpr int LCH = LAZY ? (kStage * LCPN + 63) / 64 : 1;
+    static_assert(!LAZY || ksplit_lazy_smem_elems<DK, DV>() == kStage * (DKH + CW), "staging");
+    TreeRange ptr = {0, 0, BOLE_TREE_OK};
+    int plen_raw = 0;
+    bool plikely = false;
+    int lx[LCH];
+    int lpx = -1, lpp = -1;
+    if constexpr (LAZY) {
+        ptr = tree_range(lc.node_offsets, b, lc.T, lc.max_n);
+        plen_raw = lc.accepted_len[b];
+        plikely = ptr.status == BOLE_TREE_OK && plen_raw > 0 && plen_raw <= lc.max_path &&
+                  plen_raw <= ptr.n;
+        const int32_t *acc_b = lc.accepted_idx + (size_t)b * lc.max_path;
+#pragma unroll
+        for (int u = 0; u < LCH; ++u) {
+            const int m = (lane + 64 * u) / LCPN;
+            lx[u] = (plikely && m < plen_raw) ? acc_b[m] : 0;
+        }
+        if (ptr.status == BOLE_TREE_OK && ptr.n > 0) {
+            lpp = lane < ptr.n ? lc.parent[ptr.lo + lane] : -1;
+            if (lane < plen_raw && plen_raw <= lc.max_path) lpx = acc_b[lane];
+        }
+    }
 
     // ---- 1. issue every load. Relative node tile r: r < 2 is own tile 2w + r, r >= 2
     // the other wavefront's tile 2(1 - w) + r - 2.
@@ -584,9 +631,117 @@ __device__ __forceinline__ void ksplit_body(
     for (int s = 0; s < HSW; ++s)
         hreg[s] = __builtin_nontemporal_load(reinterpret_cast<const hvec *>(
             hu + ((uint32_t)(32 * (w * KH + (s >> 3)) + 8 * g + (s & 7)) * DV + CPL * n16)));
+    // lazy commit: the factor chunks of the first kStage path nodes, issued behind H_0 and
+    // held in registers until the path is validated; rows clamped into the previous tree,
+    // which its offsets check keeps inside [0, T)
+    bf16x8 pf[LCH];
+    if constexpr (LAZY) {
+        if (plikely) {
+            const int mc0 = min(kStage, plen_raw);
+#pragma unroll
+            for (int u = 0; u < LCH; ++u) {
+                const int c = lane + 64 * u;
+                const int m = c / LCPN, part = c - m * LCPN;
+                if (m < mc0) {
+                    const size_t prow = (size_t)(ptr.lo + min(max(lx[u], 0), ptr.n - 1)) * H + h;
+                    pf[u] = part < LCK
+                                ? load16(static_cast<const __bf16 *>(ly.prev_k) + prow * DK +
+                                         w * DKH + 8 * part)
+                                : load16(static_cast<const __bf16 *>(ly.prev_v) + prow * DV + c0 +
+                                         8 * (part - LCK));
+                }
+            }
+        }
+    }
 #pragma unroll
     for (int u = 0; u < KL; ++u)
         if ((64 / PPR) * (w + 2 * u) < rows) s_k[64 * (w + 2 * u) + lane] = kst[u];
+
+    // ---- lazy commit: validate the previous path, stage its factors, update this
+    // wavefront's H_0 rows in registers and write them back (both wavefronts validate;
+    // the first writes the per-tree outputs)
+    if constexpr (LAZY) {
+        const bool lfirst = first && w == 0;
+        int st = ptr.status, plen = 0;
+        float pa = 1.f;  // lane m: scalar gate of path node m
+        if (st == BOLE_TREE_OK && ptr.n > 0) {
+            const int pn = ptr.n;
+            const bool len_ok = plen_raw >= 0 && plen_raw <= lc.max_path;
+            const int x = lane < plen_raw ? lpx : -1;
+            if (__any(lane < pn && (lpp < -1 || lpp >= lane))) {
+                st = BOLE_TREE_BAD_PARENT;
+            } else if (!len_ok) {
+                st = BOLE_TREE_BAD_PATH;
+            } else {
+                const int px = __shfl(lpp, (x >= 0 && x < pn) ? x : 0, 64);
+                const int prev_raw = __shfl(x, lane > 0 ? lane - 1 : 0, 64);
+                const int prev = lane == 0 ? -1 : prev_raw;
+                const bool bad = lane < plen_raw && (x < 0 || x >= pn || px != prev);
+                if (__any(bad)) st = BOLE_TREE_BAD_PATH;
+                else plen = plen_raw;
+            }
+            if (plen > 0 && lane < plen) pa = ly.prev_gate[(size_t)(ptr.lo + x) * H + h];
+            const int row = (st == BOLE_TREE_OK && lane < plen) ? ptr.lo + x : -1;
+            if (lfirst) {
+                if (lane == 0 && lc.tree_status) lc.tree_status[b] = st;
+                if (lc.path_nodes && lane < lc.max_path) lc.path_nodes[(size_t)b * lc.max_path + lane] = row;
+            }
+        } else {
+            if (st == BOLE_TREE_OK && plen_raw != 0) st = BOLE_TREE_BAD_PATH;  // empty tree
+            if (lfirst) {
+                if (lane == 0 && lc.tree_status) lc.tree_status[b] = st;
+                if (lc.path_nodes && lane < lc.max_path) lc.path_nodes[(size_t)b * lc.max_path + lane] = -1;
+            }
+        }
+        if (plen > 0) {
+            __bf16 *const s_pk = lsmem, *const s_pv = lsmem + kStage * DKH;
+            for (int m0 = 0; m0 < plen; m0 += kStage) {
+                const int mc = min(kStage, plen - m0);
+#pragma unroll
+                for (int u = 0; u < LCH; ++u) {
+                    const int c = lane + 64 * u;
+                    const int m = c / LCPN, part = c - m * LCPN;
+                    // every lane takes part in the shuffle; only m < mc use the result
+                    const int xs = __shfl(lpx, min(m0 + m, 63), 64);
+                    if (m < mc) {
+                        bf16x8 chunk;
+                        if (m0 == 0) {
+                            chunk = pf[u];  // prefetched: plen == plen_raw here
+                        } else {
+                            const size_t prow = (size_t)(ptr.lo + min(max(xs, 0), ptr.n - 1)) * H + h;
+                            chunk = part < LCK
+                                        ? load16(static_cast<const __bf16 *>(ly.prev_k) + prow * DK +
+                                                 w * DKH + 8 * part)
+                                        : load16(static_cast<const __bf16 *>(ly.prev_v) + prow * DV +
+                                                 c0 + 8 * (part - LCK));
+                        }
+                        if (part < LCK)
+                            *reinterpret_cast<bf16x8 *>(s_pk + m * DKH + 8 * part) = chunk;
+                        else
+                            *reinterpret_cast<bf16x8 *>(s_pv + m * CW + 8 * (part - LCK)) = chunk;
+                    }
+                }
+                for (int m = 0; m < mc; ++m) {
+                    const float a = readlane_f(pa, m0 + m);
+                    const vvec vv = *reinterpret_cast<const vvec *>(s_pv + m * CW + CPL * n16);
+#pragma unroll
+                    for (int tl = 0; tl < KH; ++tl) {
+                        const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(s_pk + m * DKH + 32 * tl + 8 * g);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+#pragma unroll
+                            for (int c = 0; c < CPL; ++c)
+                                hreg[8 * tl + e][c] = a * hreg[8 * tl + e][c] +
+                                                      static_cast<float>(kk[e]) * static_cast<float>(vv[c]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < HSW; ++s)
+                __builtin_nontemporal_store(hreg[s], reinterpret_cast<hvec *>(
+                    hu + ((uint32_t)(32 * (w * KH + (s >> 3)) + 8 * g + (s & 7)) * DV + CPL * n16)));
+        }
+    }
 
     // ---- 2. topology and base-2 cumulative decay (both wavefronts, same result)
     const float lg2 = lane < n ? __builtin_amdgcn_logf(g_raw) : 0.f;
@@ -754,14 +909,16 @@ __device__ __forceinline__ void ksplit_body(
         }
 }
 
-template <int DK, int DV>
-__global__ __launch_bounds__(128, 3) void verify_mfma_ksplit_kernel(
+template <int DK, int DV, bool LAZY>
+__global__ __launch_bounds__(128, LAZY ? 2 : 3) void verify_mfma_ksplit_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
-    int U, int max_n) {
+    int U, int max_n, LazyCommit lc) {
     __shared__ __align__(16) char smem[ksplit_smem_bytes<DK, DV>()];
-    ksplit_body<DK, DV>(lt.l[blockIdx.y], parent, node_offsets, tree_status, H, T, U, max_n, smem,
-                        (int)blockIdx.x, (int)(threadIdx.x >> 6));
+    __shared__ __align__(16) __bf16 s_lazy[LAZY ? 2 * ksplit_lazy_smem_elems<DK, DV>() : 8];
+    ksplit_body<DK, DV, LAZY>(lt.l[blockIdx.y], parent, node_offsets, tree_status, H, T, U, max_n,
+                              smem, (int)blockIdx.x, (int)(threadIdx.x >> 6), lc,
+                              s_lazy + (LAZY ? (threadIdx.x >> 6) * ksplit_lazy_smem_elems<DK, DV>() : 0));
 }
 
 static bool shape_ok(const bole_dims_t &d) {
@@ -825,8 +982,8 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
             verify_mfma_tree_kernel<DK, DV, true, false, 1><<<grid, dim3(64), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
         if (max_n > 32)
-            verify_mfma_ksplit_kernel<DK, DV><<<grid, dim3(128), 0, stream>>>(
-                lt, parent, node_offsets, tree_status, H, T, (int)U, max_n);
+            verify_mfma_ksplit_kernel<DK, DV, true><<<grid, dim3(128), 0, stream>>>(
+                lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
     } else if (max_n > 32) {
         // two units per workgroup only when they always share a tree (an even head count)
         if (group && H % 2 == 0)
