@@ -193,3 +193,59 @@ def test_read_status_all_good_and_large_batch(bole):
                                      bole._stream(None)) == bole.BOLE_ERR_BAD_TREE
     assert bole.lib.bole_read_status(ctypes.c_void_p(st.data_ptr()), 600, None,
                                      bole._stream(None)) == bole.BOLE_OK
+
+
+def test_single_layer_lazy_and_bound_calls_validate_gates(bole):
+    """The single-layer lazy call and the bound launchers take the flag as the stacked
+    calls do: the same statuses and results as the stack of one layer."""
+    prev, players = make(91, n_layers=1)
+    cur, clayers = make(93, n_layers=1, sizes=(5, 64, 18, 9, 32, 1))
+    spoil(players, prev, 0, 0, 2, 0.0)
+    spoil(clayers, cur, 3, 0, 1, float("nan"))
+    B = prev.batch
+    pp, po = g(prev.parent), g(prev.node_offsets)
+    ai, al = g(prev.accepted_idx), g(prev.accepted_len)
+    cp, co = g(cur.parent), g(cur.node_offsets)
+    p, c = players[0], clayers[0]
+    runs = []
+    for form in ("stack", "single", "bound"):
+        H = c["H0"].clone()
+        pst = torch.full((B,), -1, dtype=torch.int32, device=dev())
+        st = torch.full((B,), -1, dtype=torch.int32, device=dev())
+        out = torch.empty((c["q"].shape[0], 4, 64), dtype=torch.float32, device=dev())
+        if form == "stack":
+            y = dict(H0=H, q=c["q"], k=c["k"], v=c["v"], gate=c["gate"], prev_k=p["k"],
+                     prev_v=p["v"], prev_gate=p["gate"], out=out)
+            bole.bole_tree_verify_lazy_commit_layers([y], pp, po, ai, al, cp, co,
+                                                     prev_tree_status=pst, tree_status=st,
+                                                     validate_gates=True)
+        else:
+            args = (H, (p["k"], p["v"], p["gate"], pp, po), ai, al, c["q"], c["k"], c["v"],
+                    c["gate"], cp, co)
+            kw = dict(prev_tree_status=pst, tree_status=st, validate_gates=True)
+            if form == "single":
+                bole.bole_tree_verify_lazy_commit(*args, out=out, **kw)
+            else:
+                bole.bind_tree_verify_lazy_commit(*args, out, **kw)()
+        torch.cuda.synchronize()
+        runs.append((H.cpu(), out.cpu().nan_to_num(7.0), pst.cpu().tolist(), st.cpu().tolist()))
+    assert runs[0][2] == [BAD_GATE, 0, 0, 0, 0, 0] and runs[0][3] == [0, 0, 0, BAD_GATE, 0, 0]
+    for r in runs[1:]:
+        assert torch.equal(r[0], runs[0][0]) and torch.equal(r[1], runs[0][1])
+        assert r[2] == runs[0][2] and r[3] == runs[0][3]
+    # the bound verify and commit launchers
+    st = torch.full((B,), -1, dtype=torch.int32, device=dev())
+    out = torch.empty((c["q"].shape[0], 4, 64), dtype=torch.float32, device=dev())
+    bole.bind_tree_verify(c["H0"], c["q"], c["k"], c["v"], c["gate"], cp, co, out,
+                          tree_status=st, validate_gates=True)()
+    y = dict(H0=c["H0"], q=c["q"], k=c["k"], v=c["v"], gate=c["gate"], out=out)
+    st2 = torch.full((B,), -1, dtype=torch.int32, device=dev())
+    bole.bind_tree_verify_layers([y], cp, co, tree_status=st2, validate_gates=True)()
+    H = p["H0"].clone()
+    pst = torch.full((B,), -1, dtype=torch.int32, device=dev())
+    bole.bind_commit_path_layers([dict(H0=H, k=p["k"], v=p["v"], gate=p["gate"])], pp, po, ai,
+                                 al, tree_status=pst, validate_gates=True)()
+    torch.cuda.synchronize()
+    assert st.cpu().tolist() == st2.cpu().tolist() == [0, 0, 0, BAD_GATE, 0, 0]
+    assert pst.cpu().tolist() == [BAD_GATE, 0, 0, 0, 0, 0]
+    assert torch.equal(H[0].cpu(), p["H0"][0].cpu())

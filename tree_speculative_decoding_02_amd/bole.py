@@ -240,7 +240,7 @@ def bole_tree_verify_naive(H0, q, k, v, gate, parent, node_offsets, out=None, st
 
 def _lazy_args(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate, parent,
                node_offsets, out, prev_path_nodes, prev_tree_status, tree_status, stream,
-               trees_le_32, prev_trees_le_32):
+               trees_le_32, prev_trees_le_32, validate_gates=False):
     pk, pv, pgate, pparent, poffs = prev
     B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
     pB, pH, pdk, pdv, pT, pvec = _factor_dims(H0, pk, pv, pgate, pparent, poffs)
@@ -266,8 +266,10 @@ def _lazy_args(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate, pa
             _need(t, name, torch.int32, H0.device)
     if prev_path_nodes is not None and tuple(prev_path_nodes.shape) != (B, max_path):
         raise ValueError("prev_path_nodes must be [B, max_path]")
-    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, trees_le_32=trees_le_32)
-    pdims = make_dims(B, Hh, d_k, d_v, pT, k.dtype, vec, max_path, trees_le_32=prev_trees_le_32)
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, trees_le_32=trees_le_32,
+                     validate_gates=validate_gates)
+    pdims = make_dims(B, Hh, d_k, d_v, pT, k.dtype, vec, max_path, trees_le_32=prev_trees_le_32,
+                      validate_gates=validate_gates)
     f = bole_factors_t(pk.data_ptr(), pv.data_ptr(), pgate.data_ptr(), pparent.data_ptr(),
                        poffs.data_ptr())
     args = (_ptr(H0), ctypes.byref(f), _ptr(prev_accepted_idx), _ptr(prev_accepted_len),
@@ -282,14 +284,15 @@ def _lazy_args(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate, pa
 def bole_tree_verify_lazy_commit(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate,
                                  parent, node_offsets, out=None, prev_path_nodes=None,
                                  prev_tree_status=None, tree_status=None, stream=None,
-                                 trees_le_32=False, prev_trees_le_32=False):
+                                 trees_le_32=False, prev_trees_le_32=False, validate_gates=False):
     """Commits the previous step's accepted path into H0 and verifies this step's tree
     against the result, in one pass over H0. prev = (k, v, gate, parent, node_offsets)
     of the previous step. Same result as bole_commit_path(previous step) followed by
-    bole_tree_verify(this step); returns out."""
+    bole_tree_verify(this step); returns out. validate_gates sets
+    BOLE_FLAG_VALIDATE_GATES for both steps."""
     out, args, _ = _lazy_args(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate,
                               parent, node_offsets, out, prev_path_nodes, prev_tree_status,
-                              tree_status, stream, trees_le_32, prev_trees_le_32)
+                              tree_status, stream, trees_le_32, prev_trees_le_32, validate_gates)
     _check(lib.bole_tree_verify_lazy_commit(*args), "bole_tree_verify_lazy_commit")
     return out
 
@@ -308,7 +311,7 @@ class _Bound:
 
 
 def bind_tree_verify(H0, q, k, v, gate, parent, node_offsets, out, tree_status=None,
-                     stream=None, force_generic=False, trees_le_32=False):
+                     stream=None, force_generic=False, trees_le_32=False, validate_gates=False):
     """Same checks as bole_tree_verify, done once; returns a callable that launches the
     verify on these buffers each time it is called (for tight launch loops)."""
     B, Hh, d_k, d_v, T, vec = _factor_dims(H0, k, v, gate, parent, node_offsets)
@@ -320,7 +323,8 @@ def bind_tree_verify(H0, q, k, v, gate, parent, node_offsets, out, tree_status=N
         _need(tree_status, "tree_status", torch.int32, H0.device)
         if tree_status.numel() < B:
             raise ValueError("tree_status needs B entries")
-    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, force_generic, trees_le_32)
+    dims = make_dims(B, Hh, d_k, d_v, T, k.dtype, vec, 0, force_generic, trees_le_32,
+                     validate_gates)
     args = (_ptr(H0), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(parent), _ptr(node_offsets),
             _ptr(out), ctypes.byref(dims), _ptr(tree_status), _stream(stream))
     return _Bound(lib.bole_tree_verify, "bole_tree_verify", args,
@@ -357,12 +361,12 @@ def bind_commit_path(H0, k, v, gate, parent, node_offsets, accepted_idx, accepte
 def bind_tree_verify_lazy_commit(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate,
                                  parent, node_offsets, out, prev_path_nodes=None,
                                  prev_tree_status=None, tree_status=None, stream=None,
-                                 trees_le_32=False, prev_trees_le_32=False):
+                                 trees_le_32=False, prev_trees_le_32=False, validate_gates=False):
     """Same checks as bole_tree_verify_lazy_commit, done once; returns a callable that
     launches it on these buffers each time it is called."""
     _, args, keep = _lazy_args(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate,
                                parent, node_offsets, out, prev_path_nodes, prev_tree_status,
-                               tree_status, stream, trees_le_32, prev_trees_le_32)
+                               tree_status, stream, trees_le_32, prev_trees_le_32, validate_gates)
     return _Bound(lib.bole_tree_verify_lazy_commit, "bole_tree_verify_lazy_commit", args, keep)
 
 
@@ -475,9 +479,9 @@ def bole_tree_verify_layers(layers, parent, node_offsets, tree_status=None, stre
 
 
 def bind_tree_verify_layers(layers, parent, node_offsets, tree_status=None, stream=None,
-                            force_generic=False, trees_le_32=False):
+                            force_generic=False, trees_le_32=False, validate_gates=False):
     args, keep = _verify_layers_call(layers, parent, node_offsets, tree_status, stream,
-                                     force_generic, trees_le_32)
+                                     force_generic, trees_le_32, validate_gates)
     return _Bound(lib.bole_tree_verify_layers, "bole_tree_verify_layers", args, keep)
 
 
@@ -505,9 +509,10 @@ def bole_commit_path_layers(layers, parent, node_offsets, accepted_idx, accepted
 
 
 def bind_commit_path_layers(layers, parent, node_offsets, accepted_idx, accepted_len,
-                            path_nodes=None, tree_status=None, stream=None, trees_le_32=False):
+                            path_nodes=None, tree_status=None, stream=None, trees_le_32=False,
+                            validate_gates=False):
     args, keep = _commit_layers_call(layers, parent, node_offsets, accepted_idx, accepted_len,
-                                     path_nodes, tree_status, stream, trees_le_32)
+                                     path_nodes, tree_status, stream, trees_le_32, validate_gates)
     return _Bound(lib.bole_commit_path_layers, "bole_commit_path_layers", args, keep)
 
 
@@ -553,11 +558,11 @@ def bind_tree_verify_lazy_commit_layers(layers, prev_parent, prev_node_offsets,
                                         prev_accepted_idx, prev_accepted_len, parent,
                                         node_offsets, prev_path_nodes=None, prev_tree_status=None,
                                         tree_status=None, stream=None, trees_le_32=False,
-                                        prev_trees_le_32=False):
+                                        prev_trees_le_32=False, validate_gates=False):
     args, keep = _lazy_layers_call(layers, prev_parent, prev_node_offsets, prev_accepted_idx,
                                    prev_accepted_len, parent, node_offsets, prev_path_nodes,
                                    prev_tree_status, tree_status, stream, trees_le_32,
-                                   prev_trees_le_32)
+                                   prev_trees_le_32, validate_gates)
     return _Bound(lib.bole_tree_verify_lazy_commit_layers, "bole_tree_verify_lazy_commit_layers",
                   args, keep)
 
