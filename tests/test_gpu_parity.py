@@ -666,6 +666,64 @@ def test_lazy_commit_large_current_trees(bole, d_k, d_v):
     assert rel_err_rows(ob[good].astype(np.float64), oref[good]) <= TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("d_k,d_v", [(128, 128), (128, 64), (64, 32), (64, 256), (128, 32)])
+def test_lazy_commit_vector_gates(bole, d_k, d_v):
+    """Per-channel gates take the vector-gate kernel's one-pass form: good and bad previous
+    paths (bad parent, not a chain, too long, on an empty tree, longer than one staging
+    round of 4 nodes) under current trees that are empty, bad, small and large, against
+    the two separate calls and the oracle."""
+    sizes = [3, 2, 3, 2, 1, 0, 4, 40, 12]
+    wp = W.make_random(35, batch=9, heads=2, d_k=d_k, d_v=d_v, sizes=sizes, max_path=40,
+                       vector_gate=True)
+    wp.parent = np.concatenate([np.array([-1, 0, 0, -1, 1, -1, 0, 1, -1, 0, -1, -1, 0, 1, 2],
+                                         np.int32),
+                                np.arange(-1, 39, dtype=np.int32),
+                                np.array([-1, 0, 1, 2, 3, 4, 5, 6, 0, 8, 9, 10], np.int32)])
+    wp.node_offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    wp.accepted_idx[:] = -1
+    wp.accepted_len[:] = [2, 1, 2, 1, 17, 1, 3, 37, 7]
+    wp.accepted_idx[0, :2] = [0, 2]
+    wp.accepted_idx[1, :1] = [0]
+    wp.accepted_idx[2, :2] = [0, 2]       # parent[2] == 1 in tree 2: not a chain
+    wp.accepted_idx[3, :1] = [0]
+    wp.parent[wp.node_offsets[3] + 1] = 5  # previous tree 3: a parent past the node
+    wp.accepted_idx[4, :1] = [0]          # length 17 on 1 node: too long
+    wp.accepted_idx[5, :1] = [0]          # a path on an empty tree
+    wp.accepted_idx[6, :3] = [0, 1, 2]
+    wp.accepted_idx[7, :37] = np.arange(37)   # ten staging rounds
+    wp.accepted_idx[8, :7] = np.arange(7)     # two staging rounds
+    cur_sizes = [0, 5, 64, 20, 33, 1, 40, 2, 9]   # tree 0: nothing to verify, a path to commit
+    wc = W.make_random(36, batch=9, heads=2, d_k=d_k, d_v=d_v, sizes=cur_sizes, kind="deep",
+                       vector_gate=True)
+    wc.parent = wc.parent.copy()
+    wc.parent[wc.node_offsets[6] + 30] = 31   # current tree 6: a node its own child
+    tp, tc = to_dev(wp), to_dev(wc)
+    print(f"[case] lazy vector gates d_k={d_k} d_v={d_v}", flush=True)
+    (Ha, oa, psa, pna, sa), (Hb, ob, psb, pnb, sb) = _lazy_vs_separate(bole, tp, tc)
+    assert psa.tolist() == [0, 2, 3, 2, 3, 3, 0, 0, 0]
+    assert sa.tolist() == [0, 0, 0, 0, 0, 0, 2, 0, 0]
+    np.testing.assert_array_equal(psb, psa)
+    np.testing.assert_array_equal(pnb, pna)
+    np.testing.assert_array_equal(sb, sa)
+    H0 = wp.layers[0].H0.numpy()
+    for b in (1, 2, 3, 4, 5):
+        np.testing.assert_array_equal(Hb[b], H0[b])
+    assert rel_err_states(Hb, Ha) <= 1e-6
+    bad = np.arange(wc.node_offsets[6], wc.node_offsets[7])
+    assert np.isnan(ob[bad]).all() and np.isnan(oa[bad]).all()
+    good = np.setdiff1d(np.arange(ob.shape[0]), bad)
+    assert rel_err_rows(ob[good].astype(np.float64), oa[good].astype(np.float64)) <= 1e-5
+    Href, pn_ref, st_ref = oracle.commit_serial(wp.layers[0].H0, wp.layers[0].k, wp.layers[0].v,
+                                                wp.layers[0].gate, wp.parent, wp.node_offsets,
+                                                wp.accepted_idx, wp.accepted_len, True)
+    assert st_ref.tolist() == psb.tolist()
+    np.testing.assert_array_equal(pn_ref, pnb)
+    oref, _ = oracle.verify_serial(Href, wc.layers[0].q, wc.layers[0].k, wc.layers[0].v,
+                                   wc.layers[0].gate, wc.parent, wc.node_offsets, True)
+    assert rel_err_states(Hb.astype(np.float64), Href) <= TOL[torch.bfloat16]
+    assert rel_err_rows(ob[good].astype(np.float64), oref[good]) <= TOL[torch.bfloat16]
+
+
 def test_lazy_commit_decode_loop(bole):
     """Three steps run eagerly (verify, commit, verify, commit, ...) and lazily (verify,
     then verify with the previous commit folded in, and a final commit)."""

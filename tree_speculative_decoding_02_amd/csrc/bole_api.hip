@@ -131,9 +131,18 @@ hipError_t dispatch_lazy(const bole_layer_t *layers, int num_layers, const bole:
         bole::PrevPath pp = prev;
         if (l0 > 0) pp.path_nodes = pp.tree_status = nullptr;
         int32_t *ts = l0 == 0 ? tree_status : nullptr;
-        hipError_t e;
+        hipError_t e = hipSuccess;
+        bool vec = true;  // the vector-gate kernel's one-pass form, layer by layer
+        for (int l = 0; l < nl; ++l) vec = vec && bole::verify_vec_lazy_applies(d, pd, ch[l]);
         if (bole::verify_lazy_applies(d, pd, ch, nl)) {
             e = bole::launch_verify_lazy_commit(ch, nl, pp, pd, parent, node_offsets, d, ts, s);
+        } else if (vec) {
+            for (int l = 0; l < nl && e == hipSuccess; ++l) {
+                bole::PrevPath pv = pp;  // per-tree outputs from the chunk's first layer
+                if (l > 0) pv.path_nodes = pv.tree_status = nullptr;
+                e = bole::launch_verify_vec_lazy(ch[l], pv, pd, parent, node_offsets, d,
+                                                 l == 0 ? ts : nullptr, s);
+            }
         } else {
             e = bole::launch_commit(pl, nl, pp.parent, pp.node_offsets, pp.accepted_idx,
                                     pp.accepted_len, pd, pp.path_nodes, pp.tree_status, nullptr, s);

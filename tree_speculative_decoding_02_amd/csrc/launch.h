@@ -51,6 +51,15 @@ hipError_t launch_verify_vec(const float *H0, const void *q, const void *k, cons
                              const int32_t *node_offsets, float *out, const bole_dims_t &d,
                              int32_t *tree_status, hipStream_t stream);
 
+// The vector-gate kernel with the previous step's commit folded in (one layer); applies when
+// the verify does and the previous step's factors have the same shapes and 16-byte rows.
+bool verify_vec_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const bole_layer_t &y);
+
+hipError_t launch_verify_vec_lazy(const bole_layer_t &y, const PrevPath &prev,
+                                  const bole_dims_t &pd, const int32_t *parent,
+                                  const int32_t *node_offsets, const bole_dims_t &d,
+                                  int32_t *tree_status, hipStream_t stream);
+
 // True when the one-pass lazy commit + verify kernel covers this pair of steps.
 bool verify_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const bole_layer_t *layers,
                          int nl);

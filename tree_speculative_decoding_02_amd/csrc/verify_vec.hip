@@ -38,6 +38,15 @@ namespace bole {
 
 constexpr int kVecThreads = 256;
 
+// The previous step's tree, accepted path and factors (of one layer), for LAZY.
+struct VecLazy {
+    const int32_t *parent, *node_offsets, *accepted_idx, *accepted_len;
+    int32_t *path_nodes, *tree_status;
+    const __bf16 *k, *v;
+    const float *gate;
+    int T, max_path, max_n;
+};
+
 // One step of a wavefront-wide running minimum and maximum over DPP lane moves: lanes
 // that the move gives no source keep their own values (the identities +inf and -inf).
 template <int CTRL, int ROW_MASK>
@@ -50,12 +59,20 @@ __device__ __forceinline__ void range_dpp_step(float &mn, float &mx) {
                                                  ninf, __builtin_bit_cast(int, mx), CTRL, ROW_MASK, 0xf, false)));
 }
 
-template <int DK, int DV>
+// LAZY: the unit's H_0 slice first takes the previous step's accepted path, with the
+// rules and outputs of bole_commit_path (vector gates: H <- diag(g) H + k v^T per path
+// node): wavefront 0 validates the path beside the topology, the path factors (gate
+// and k rows, the group's v columns) go through the V table's LDS space kStage nodes at
+// a time before V needs it, and each thread updates the H_0 rows it holds and writes them
+// back, just before they become matrix operands. A unit whose tree of this step is bad or
+// empty is committed all the same.
+template <int DK, int DV, bool LAZY>
 __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
-    const float *__restrict__ H0, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
+    float *__restrict__ H0, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     const __bf16 *__restrict__ v, const float *__restrict__ gate,
     const int32_t *__restrict__ parent, const int32_t *__restrict__ node_offsets,
-    float *__restrict__ out, int32_t *__restrict__ tree_status, int H, int T, int U, int max_n) {
+    float *__restrict__ out, int32_t *__restrict__ tree_status, int H, int T, int U, int max_n,
+    VecLazy lz) {
     constexpr int N = kMaxTree;             // node rows staged (tree nodes; the rest clamped)
     constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
     constexpr int CPL = CW / 16;            // columns per lane in the products
@@ -81,6 +98,8 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     __shared__ int s_anc[6][N];                                    // 2^r-th ancestor (or -1)
     __shared__ int s_info[2];                                      // status, doubling rounds
     __shared__ float s_red[4][2];                                  // per wave: min, max of LG
+    __shared__ int s_pinfo[2];                                     // LAZY: path status, length
+    __shared__ int s_prow[LAZY ? 64 : 1];                          // LAZY: path rows
     float *s_lg = s_big;
     __bf16 *s_k = reinterpret_cast<__bf16 *>(s_big + N * DK);
     __bf16 *s_h0b = reinterpret_cast<__bf16 *>(s_big);  // H_0 slice, hi then lo tables
@@ -101,15 +120,138 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     const bool writer = tree_status != nullptr && h == 0 && cg == 0 && tid == 0;
 
     const TreeRange tr = tree_range(node_offsets, b, T, max_n);
-    if (tr.status != BOLE_TREE_OK) {
+    float *const hu = H0 + (size_t)unit * DK * DV + c0;
+    const int hrg = tid >> 4, hn = tid & 15;  // H_0 slice: rows 8 hrg .., columns CPL*hn ..
+
+    // ---- LAZY: the previous step's path. Its offsets and length, then (wavefront 0) its
+    // parent links and indices; thread t stages chunk t of the first kStage path nodes, a
+    // 16-byte piece of a node's gate row, k row or v columns (16 * t bytes into the stage).
+    constexpr int kStage = 4;
+    constexpr int SGC = DK / 4, SKC = DK / 8, SVC = CW / 8, CPN = SGC + SKC + SVC;
+    constexpr int SB = 16 * CPN;            // stage bytes per path node
+    static_assert(!LAZY || (kStage * CPN <= kVecThreads && kStage * SB <= N * CW * 2),
+                  "path staging");
+    TreeRange ptr = {0, 0, BOLE_TREE_OK};
+    int plen_raw = 0, lx = 0, lpx = -1, lpp = -1;
+    bool plikely = false;
+    if constexpr (LAZY) {
+        ptr = tree_range(lz.node_offsets, b, lz.T, lz.max_n);
+        plen_raw = lz.accepted_len[b];
+        plikely = ptr.status == BOLE_TREE_OK && plen_raw > 0 && plen_raw <= lz.max_path &&
+                  plen_raw <= ptr.n;
+        const int32_t *acc_b = lz.accepted_idx + (size_t)b * lz.max_path;
+        if (plikely && tid / CPN < min(kStage, plen_raw)) lx = acc_b[tid / CPN];
+        if (wave == 0 && ptr.status == BOLE_TREE_OK && ptr.n > 0) {
+            lpp = lane < ptr.n ? lz.parent[ptr.lo + lane] : -1;
+            if (lane < plen_raw && plen_raw <= lz.max_path) lpx = acc_b[lane];
+        }
+    }
+    // chunk c of path node `row` (a row of the previous step's factors)
+    auto path_chunk = [&](int row, int c) -> u32x4 {
+        const size_t r = (size_t)row * H + h;
+        const void *p = c < SGC ? static_cast<const void *>(lz.gate + r * DK + 4 * c)
+                      : c < SGC + SKC ? static_cast<const void *>(lz.k + r * DK + 8 * (c - SGC))
+                                      : static_cast<const void *>(lz.v + r * DV + c0 +
+                                                                  8 * (c - SGC - SKC));
+        return *reinterpret_cast<const u32x4 *>(p);
+    };
+    u32x4 pf = {0u, 0u, 0u, 0u};
+    auto prefetch = [&]() {
+        if (plikely && tid / CPN < min(kStage, plen_raw))
+            pf = path_chunk(ptr.lo + min(max(lx, 0), ptr.n - 1), tid % CPN);
+    };
+    // wavefront 0: the path checks of the commit, its per-tree outputs, and the path
+    // (length, rows) for every thread
+    auto validate = [&]() {
+        int st = ptr.status, plen = 0, row = -1;
+        if (st == BOLE_TREE_OK && ptr.n > 0) {
+            const int pn = ptr.n;
+            const bool len_ok = plen_raw >= 0 && plen_raw <= lz.max_path;
+            const int x = lane < plen_raw ? lpx : -1;
+            if (__any(lane < pn && (lpp < -1 || lpp >= lane))) {
+                st = BOLE_TREE_BAD_PARENT;
+            } else if (!len_ok) {
+                st = BOLE_TREE_BAD_PATH;
+            } else {
+                const int px = __shfl(lpp, (x >= 0 && x < pn) ? x : 0, 64);
+                const int prev_raw = __shfl(x, lane > 0 ? lane - 1 : 0, 64);
+                const int prev = lane == 0 ? -1 : prev_raw;
+                const bool bad = lane < plen_raw && (x < 0 || x >= pn || px != prev);
+                if (__any(bad)) st = BOLE_TREE_BAD_PATH;
+                else plen = plen_raw;
+            }
+            row = (st == BOLE_TREE_OK && lane < plen) ? ptr.lo + x : -1;
+        } else if (st == BOLE_TREE_OK && plen_raw != 0) {
+            st = BOLE_TREE_BAD_PATH;  // a path on an empty tree
+        }
+        s_prow[lane] = row;
+        if (lane == 0) {
+            s_pinfo[0] = st;
+            s_pinfo[1] = plen;
+        }
+        if (h == 0 && cg == 0) {
+            if (lane == 0 && lz.tree_status) lz.tree_status[b] = st;
+            if (lz.path_nodes && lane < lz.max_path) lz.path_nodes[(size_t)b * lz.max_path + lane] = row;
+        }
+    };
+    // every thread, after the barrier that publishes the path: the path applied to the
+    // H_0 rows this thread holds (rh), kStage nodes at a time, then the rows written back
+    auto commit = [&](hvec *rh) {
+        const int plen = s_pinfo[1];
+        if (plen == 0) return;  // uniform: nothing to commit, H_0 stays as it is
+        char *const stage = reinterpret_cast<char *>(s_v);
+        for (int m0 = 0; m0 < plen; m0 += kStage) {
+            const int mc = min(kStage, plen - m0);
+            if (tid / CPN < mc) {
+                const u32x4 x = m0 == 0 ? pf : path_chunk(s_prow[m0 + tid / CPN], tid % CPN);
+                *reinterpret_cast<u32x4 *>(stage + 16 * tid) = x;
+            }
+            __syncthreads();
+            if (hrg < HRG) {
+                for (int m = 0; m < mc; ++m) {
+                    const char *nb = stage + m * SB;
+                    const float4 ga = *reinterpret_cast<const float4 *>(nb + 32 * hrg);
+                    const float4 gb = *reinterpret_cast<const float4 *>(nb + 32 * hrg + 16);
+                    const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(nb + 4 * DK + 16 * hrg);
+                    const vvec vv = *reinterpret_cast<const vvec *>(nb + 6 * DK + 2 * CPL * hn);
+                    const float g8[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c)
+                            rh[e][c] = g8[e] * rh[e][c] +
+                                       static_cast<float>(kk[e]) * static_cast<float>(vv[c]);
+                }
+            }
+            __syncthreads();  // read before the next round, or V, takes the space
+        }
+        if (hrg < HRG) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                __builtin_nontemporal_store(
+                    rh[e], reinterpret_cast<hvec *>(hu + ((uint32_t)(8 * hrg + e) * DV + CPL * hn)));
+        }
+    };
+
+    if (tr.status != BOLE_TREE_OK || tr.n == 0) {
         if (writer) tree_status[b] = tr.status;
+        if constexpr (LAZY) {
+            // nothing to verify: the commit alone
+            hvec rh[8];
+            if (hrg < HRG) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    rh[e] = __builtin_nontemporal_load(reinterpret_cast<const hvec *>(
+                        hu + ((uint32_t)(8 * hrg + e) * DV + CPL * hn)));
+            }
+            prefetch();
+            if (wave == 0) validate();
+            __syncthreads();
+            commit(rh);
+        }
         return;
     }
     const int lo = tr.lo, n = tr.n;
-    if (n == 0) {
-        if (writer) tree_status[b] = BOLE_TREE_OK;
-        return;
-    }
     const int last = n - 1;
     const uint32_t rq = (uint32_t)H * DK, rv = (uint32_t)H * DV;
     const __bf16 *qu = q + (size_t)lo * rq + (size_t)h * DK;
@@ -117,7 +259,6 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     const float *gu = gate + (size_t)lo * rq + (size_t)h * DK;
     const __bf16 *vu = v + (size_t)lo * rv + (size_t)h * DV + c0;
     float *ou = out + (size_t)lo * rv + (size_t)h * DV + c0;
-    const float *hu = H0 + (size_t)unit * DK * DV + c0;
     const int n16 = lane & 15, g4 = lane >> 4;
     const int pi = tid >> 2, psub = tid & 3;  // pair-weight node and channel quarter
 
@@ -144,7 +285,6 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         qf[t] = load16(qu + ((uint32_t)min(16 * wave + n16, last) * rq + 32 * t + 8 * g4));
     // H_0: thread (hrg, hn) = (tid / 16, tid % 16) loads rows 8 hrg .. 8 hrg + 7 of the
     // slice, columns CPL*hn .. (the B-operand rows and columns of one lane)
-    const int hrg = tid >> 4, hn = tid & 15;
     if (hrg < HRG) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -157,6 +297,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         rvv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
             vu + ((uint32_t)min(P / VP, last) * rv + 8 * (P % VP))));
     }
+    if constexpr (LAZY) prefetch();
 
     // ---- 1. topology and doubling pointers (wavefront 0); log2 of the gate rows and
     // the K rows to LDS. W needs no clearing: the exact path writes every (node, path
@@ -177,6 +318,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
             s_info[1] = rounds;
         }
         if (writer) tree_status[b] = topo.bad;
+        if constexpr (LAZY) validate();
     }
     float4 lgv[GPT];  // this thread's gate entries: row (tid + 256u) / GP, channels 4*(.. % GP)
 #pragma unroll
@@ -195,6 +337,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     __syncthreads();
 
     if (s_info[0] != BOLE_TREE_OK) {
+        if constexpr (LAZY) commit(rh);
         for (int e = tid; e < n * CW; e += kVecThreads)
             ou[(uint32_t)(e / CW) * rv + (e % CW)] = __builtin_nanf("");
         return;
@@ -390,6 +533,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
             }
     }
     __syncthreads();  // LG and K are dead: the H_0 slice takes their space
+    if constexpr (LAZY) commit(rh);
 
     // ---- 4. H_0 and V to LDS. H_0 is split hi + lo once here, into two bf16 tables in
     // B-operand order: the 16 bytes at [(rg CPL + c) 16 + n] hold rows 8rg .. 8rg + 7 of
@@ -492,34 +636,84 @@ bool verify_vec_applies(const bole_dims_t &d, const void *H0, const void *q, con
     return ((uint64_t)d.batch * (uint64_t)d.heads + 8) * groups < (1ull << 30);
 }
 
+// lz: the lazy commit (H0 is then written), else nullptr (H0 is only read)
 template <int DK, int DV>
-static void launch_vec_shape(const float *H0, const void *q, const void *k, const void *v,
+static void launch_vec_shape(float *H0, const void *q, const void *k, const void *v,
                              const float *gate, const int32_t *parent,
                              const int32_t *node_offsets, float *out, const bole_dims_t &d,
-                             int32_t *tree_status, hipStream_t stream) {
+                             int32_t *tree_status, hipStream_t stream, const VecLazy *lz) {
     constexpr int G = DV < 64 ? 1 : DV / 64;
     const unsigned U = (unsigned)d.batch * (unsigned)d.heads;
     const unsigned grid = G == 1 ? U : ((U + 7) / 8) * 8 * G;
-    verify_vec_kernel<DK, DV><<<dim3(grid), dim3(kVecThreads), 0, stream>>>(
-        H0, static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
-        static_cast<const __bf16 *>(v), gate, parent, node_offsets, out, tree_status, d.heads,
-        d.total_nodes, (int)U, max_tree_nodes(d.flags));
+    const auto qb = static_cast<const __bf16 *>(q);
+    const auto kb = static_cast<const __bf16 *>(k);
+    const auto vb = static_cast<const __bf16 *>(v);
+    if (lz)
+        verify_vec_kernel<DK, DV, true><<<dim3(grid), dim3(kVecThreads), 0, stream>>>(
+            H0, qb, kb, vb, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
+            (int)U, max_tree_nodes(d.flags), *lz);
+    else
+        verify_vec_kernel<DK, DV, false><<<dim3(grid), dim3(kVecThreads), 0, stream>>>(
+            H0, qb, kb, vb, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
+            (int)U, max_tree_nodes(d.flags), VecLazy{});
 }
 
-hipError_t launch_verify_vec(const float *H0, const void *q, const void *k, const void *v,
+static hipError_t launch_vec(float *H0, const void *q, const void *k, const void *v,
                              const float *gate, const int32_t *parent,
                              const int32_t *node_offsets, float *out, const bole_dims_t &d,
-                             int32_t *tree_status, hipStream_t stream) {
+                             int32_t *tree_status, hipStream_t stream, const VecLazy *lz) {
 #define BOLE_VEC_CASE(DKV, DVV)                                                                \
     if (d.d_k == DKV && d.d_v == DVV) {                                                         \
         launch_vec_shape<DKV, DVV>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, \
-                                   stream);                                                     \
+                                   stream, lz);                                                 \
         return hipGetLastError();                                                               \
     }
     BOLE_VEC_CASE(64, 32) BOLE_VEC_CASE(64, 64) BOLE_VEC_CASE(64, 128) BOLE_VEC_CASE(64, 256)
     BOLE_VEC_CASE(128, 32) BOLE_VEC_CASE(128, 64) BOLE_VEC_CASE(128, 128) BOLE_VEC_CASE(128, 256)
 #undef BOLE_VEC_CASE
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_verify_vec(const float *H0, const void *q, const void *k, const void *v,
+                             const float *gate, const int32_t *parent,
+                             const int32_t *node_offsets, float *out, const bole_dims_t &d,
+                             int32_t *tree_status, hipStream_t stream) {
+    // the verify-only instantiation never writes H0
+    return launch_vec(const_cast<float *>(H0), q, k, v, gate, parent, node_offsets, out, d,
+                      tree_status, stream, nullptr);
+}
+
+bool verify_vec_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const bole_layer_t &y) {
+    if (!verify_vec_applies(d, y.H0, y.q, y.k, y.v, y.gate, y.out)) return false;
+    // the previous step's factors: same layout and shapes, 16-byte rows
+    if (pd.factor_dtype != d.factor_dtype || pd.gate_kind != d.gate_kind || pd.d_k != d.d_k ||
+        pd.d_v != d.d_v || pd.heads != d.heads || pd.batch != d.batch)
+        return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(y.prev_k) |
+                        reinterpret_cast<uintptr_t>(y.prev_v) |
+                        reinterpret_cast<uintptr_t>(y.prev_gate);
+    return a % 16 == 0;
+}
+
+hipError_t launch_verify_vec_lazy(const bole_layer_t &y, const PrevPath &prev,
+                                  const bole_dims_t &pd, const int32_t *parent,
+                                  const int32_t *node_offsets, const bole_dims_t &d,
+                                  int32_t *tree_status, hipStream_t stream) {
+    VecLazy lz;
+    lz.parent = prev.parent;
+    lz.node_offsets = prev.node_offsets;
+    lz.accepted_idx = prev.accepted_idx;
+    lz.accepted_len = prev.accepted_len;
+    lz.path_nodes = prev.path_nodes;
+    lz.tree_status = prev.tree_status;
+    lz.k = static_cast<const __bf16 *>(y.prev_k);
+    lz.v = static_cast<const __bf16 *>(y.prev_v);
+    lz.gate = y.prev_gate;
+    lz.T = pd.total_nodes;
+    lz.max_path = pd.max_path;
+    lz.max_n = max_tree_nodes(pd.flags);
+    return launch_vec(y.H0, y.q, y.k, y.v, y.gate, parent, node_offsets, y.out, d, tree_status,
+                      stream, &lz);
 }
 
 }  // namespace bole
