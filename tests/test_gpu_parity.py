@@ -791,6 +791,8 @@ LAYER_CASES = [
                                      sizes=[64, 20, 40, 0], max_path=64, kind="deep")),
     ("seventeen_layers", 17, dict(batch=3, heads=2, d_k=64, d_v=32)),
     ("vector_gate", 3, dict(batch=3, heads=2, d_k=128, d_v=64, vector_gate=True)),
+    # two launches of up to 16 layers, two column groups per unit
+    ("vector_gate_17_layers", 17, dict(batch=3, heads=2, d_k=64, d_v=128, vector_gate=True)),
     ("fp32", 2, dict(batch=3, heads=2, d_k=64, d_v=64, factor_dtype=torch.float32)),
 ]
 

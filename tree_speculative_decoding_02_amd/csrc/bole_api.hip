@@ -45,9 +45,10 @@ hipError_t gate_pass(const bole_layer_t *layers, int num_layers, bool prev, cons
     return hipSuccess;
 }
 
-// Verify of checked layers, kLayersPerLaunch at a time: matrix cores when they cover
-// every layer of the chunk, else the vector-gate or plain kernel layer by layer. Per-tree
-// outputs come from the first launch only. Under BOLE_FLAG_VALIDATE_GATES the gate check
+// Verify of checked layers, kLayersPerLaunch at a time: the scalar-gate or vector-gate
+// matrix-core kernel when it covers every layer of the chunk (one launch), else the
+// vector-gate or plain kernel layer by layer. Per-tree outputs come from the first launch
+// only. Under BOLE_FLAG_VALIDATE_GATES the gate check
 // follows: every layer's gates, then NaN rows of the trees found bad, in every layer.
 hipError_t dispatch_verify(const bole_layer_t *layers, int num_layers, const int32_t *parent,
                            const int32_t *node_offsets, const bole_dims_t &d,
@@ -57,15 +58,21 @@ hipError_t dispatch_verify(const bole_layer_t *layers, int num_layers, const int
         const int nl = num_layers - l0 < kLayersPerLaunch ? num_layers - l0 : kLayersPerLaunch;
         int32_t *ts = l0 == 0 ? tree_status : nullptr;
         hipError_t e = hipSuccess;
+        bool vec = true;
+        for (int l = 0; l < nl; ++l) {
+            const bole_layer_t &y = ch[l];
+            vec = vec && bole::verify_vec_applies(d, y.H0, y.q, y.k, y.v, y.gate, y.out);
+        }
         if (bole::verify_mfma_applies(d, ch, nl)) {
             e = bole::launch_verify_mfma(ch, nl, parent, node_offsets, d, ts, s);
+        } else if (vec) {
+            e = bole::launch_verify_vec(ch, nl, parent, node_offsets, d, ts, s);
         } else {
             for (int l = 0; l < nl && e == hipSuccess; ++l) {
                 const bole_layer_t &y = ch[l];
                 int32_t *tl = l == 0 ? ts : nullptr;
                 e = bole::verify_vec_applies(d, y.H0, y.q, y.k, y.v, y.gate, y.out)
-                        ? bole::launch_verify_vec(y.H0, y.q, y.k, y.v, y.gate, parent,
-                                                  node_offsets, y.out, d, tl, s)
+                        ? bole::launch_verify_vec(&y, 1, parent, node_offsets, d, tl, s)
                         : bole::launch_verify_generic(y.H0, y.q, y.k, y.v, y.gate, parent,
                                                       node_offsets, y.out, d, tl, s);
             }
@@ -132,17 +139,12 @@ hipError_t dispatch_lazy(const bole_layer_t *layers, int num_layers, const bole:
         if (l0 > 0) pp.path_nodes = pp.tree_status = nullptr;
         int32_t *ts = l0 == 0 ? tree_status : nullptr;
         hipError_t e = hipSuccess;
-        bool vec = true;  // the vector-gate kernel's one-pass form, layer by layer
+        bool vec = true;  // the vector-gate kernel's one-pass form covers every layer
         for (int l = 0; l < nl; ++l) vec = vec && bole::verify_vec_lazy_applies(d, pd, ch[l]);
         if (bole::verify_lazy_applies(d, pd, ch, nl)) {
             e = bole::launch_verify_lazy_commit(ch, nl, pp, pd, parent, node_offsets, d, ts, s);
         } else if (vec) {
-            for (int l = 0; l < nl && e == hipSuccess; ++l) {
-                bole::PrevPath pv = pp;  // per-tree outputs from the chunk's first layer
-                if (l > 0) pv.path_nodes = pv.tree_status = nullptr;
-                e = bole::launch_verify_vec_lazy(ch[l], pv, pd, parent, node_offsets, d,
-                                                 l == 0 ? ts : nullptr, s);
-            }
+            e = bole::launch_verify_vec_lazy(ch, nl, pp, pd, parent, node_offsets, d, ts, s);
         } else {
             e = bole::launch_commit(pl, nl, pp.parent, pp.node_offsets, pp.accepted_idx,
                                     pp.accepted_len, pd, pp.path_nodes, pp.tree_status, nullptr, s);

@@ -46,16 +46,16 @@ hipError_t launch_verify_mfma(const bole_layer_t *layers, int nl, const int32_t 
 bool verify_vec_applies(const bole_dims_t &d, const void *H0, const void *q, const void *k,
                         const void *v, const void *gate, const void *out);
 
-hipError_t launch_verify_vec(const float *H0, const void *q, const void *k, const void *v,
-                             const float *gate, const int32_t *parent,
-                             const int32_t *node_offsets, float *out, const bole_dims_t &d,
+hipError_t launch_verify_vec(const bole_layer_t *layers, int nl, const int32_t *parent,
+                             const int32_t *node_offsets, const bole_dims_t &d,
                              int32_t *tree_status, hipStream_t stream);
 
-// The vector-gate kernel with the previous step's commit folded in (one layer); applies when
-// the verify does and the previous step's factors have the same shapes and 16-byte rows.
+// The vector-gate kernel with the previous step's commit folded in; applies to a layer
+// when its verify does and the previous step's factors have the same shapes and 16-byte
+// rows.
 bool verify_vec_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const bole_layer_t &y);
 
-hipError_t launch_verify_vec_lazy(const bole_layer_t &y, const PrevPath &prev,
+hipError_t launch_verify_vec_lazy(const bole_layer_t *layers, int nl, const PrevPath &prev,
                                   const bole_dims_t &pd, const int32_t *parent,
                                   const int32_t *node_offsets, const bole_dims_t &d,
                                   int32_t *tree_status, hipStream_t stream);

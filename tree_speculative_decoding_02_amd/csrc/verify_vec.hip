@@ -38,12 +38,11 @@ namespace bole {
 
 constexpr int kVecThreads = 256;
 
-// The previous step's tree, accepted path and factors (of one layer), for LAZY.
+// The previous step's tree and accepted path, for LAZY (each layer's prev_k, prev_v and
+// prev_gate are its factors).
 struct VecLazy {
     const int32_t *parent, *node_offsets, *accepted_idx, *accepted_len;
     int32_t *path_nodes, *tree_status;
-    const __bf16 *k, *v;
-    const float *gate;
     int T, max_path, max_n;
 };
 
@@ -66,13 +65,13 @@ __device__ __forceinline__ void range_dpp_step(float &mn, float &mx) {
 // a time before V needs it, and each thread updates the H_0 rows it holds and writes them
 // back, just before they become matrix operands. A unit whose tree of this step is bad or
 // empty is committed all the same.
+// Layer blockIdx.y of the table; every layer runs the same trees, and the per-tree
+// outputs (statuses, path rows) are written by layer 0 only.
 template <int DK, int DV, bool LAZY>
 __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
-    float *__restrict__ H0, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
-    const __bf16 *__restrict__ v, const float *__restrict__ gate,
-    const int32_t *__restrict__ parent, const int32_t *__restrict__ node_offsets,
-    float *__restrict__ out, int32_t *__restrict__ tree_status, int H, int T, int U, int max_n,
-    VecLazy lz) {
+    const LayerTable lt, const int32_t *__restrict__ parent,
+    const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
+    int U, int max_n, VecLazy lz) {
     constexpr int N = kMaxTree;             // node rows staged (tree nodes; the rest clamped)
     constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
     constexpr int CPL = CW / 16;            // columns per lane in the products
@@ -117,7 +116,15 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     }
     const int b = unit / H, h = unit - b * H;
     const int c0 = cg * CW;
-    const bool writer = tree_status != nullptr && h == 0 && cg == 0 && tid == 0;
+    const bool first = blockIdx.y == 0 && h == 0 && cg == 0;  // writes the per-tree outputs
+    const bool writer = tree_status != nullptr && first && tid == 0;
+    const bole_layer_t &ly = lt.l[blockIdx.y];
+    float *const H0 = ly.H0;  // written only by the lazy commit
+    const __bf16 *const q = static_cast<const __bf16 *>(ly.q);
+    const __bf16 *const k = static_cast<const __bf16 *>(ly.k);
+    const __bf16 *const v = static_cast<const __bf16 *>(ly.v);
+    const float *const gate = ly.gate;
+    float *const out = ly.out;
 
     const TreeRange tr = tree_range(node_offsets, b, T, max_n);
     float *const hu = H0 + (size_t)unit * DK * DV + c0;
@@ -149,10 +156,13 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     // chunk c of path node `row` (a row of the previous step's factors)
     auto path_chunk = [&](int row, int c) -> u32x4 {
         const size_t r = (size_t)row * H + h;
-        const void *p = c < SGC ? static_cast<const void *>(lz.gate + r * DK + 4 * c)
-                      : c < SGC + SKC ? static_cast<const void *>(lz.k + r * DK + 8 * (c - SGC))
-                                      : static_cast<const void *>(lz.v + r * DV + c0 +
-                                                                  8 * (c - SGC - SKC));
+        const void *p =
+            c < SGC ? static_cast<const void *>(ly.prev_gate + r * DK + 4 * c)
+            : c < SGC + SKC
+                ? static_cast<const void *>(static_cast<const __bf16 *>(ly.prev_k) + r * DK +
+                                            8 * (c - SGC))
+                : static_cast<const void *>(static_cast<const __bf16 *>(ly.prev_v) + r * DV + c0 +
+                                            8 * (c - SGC - SKC));
         return *reinterpret_cast<const u32x4 *>(p);
     };
     u32x4 pf = {0u, 0u, 0u, 0u};
@@ -189,7 +199,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
             s_pinfo[0] = st;
             s_pinfo[1] = plen;
         }
-        if (h == 0 && cg == 0) {
+        if (first) {
             if (lane == 0 && lz.tree_status) lz.tree_status[b] = st;
             if (lz.path_nodes && lane < lz.max_path) lz.path_nodes[(size_t)b * lz.max_path + lane] = row;
         }
@@ -636,36 +646,33 @@ bool verify_vec_applies(const bole_dims_t &d, const void *H0, const void *q, con
     return ((uint64_t)d.batch * (uint64_t)d.heads + 8) * groups < (1ull << 30);
 }
 
+// nl <= kLayersPerLaunch layers sharing their trees, one launch (blockIdx.y = layer);
 // lz: the lazy commit (H0 is then written), else nullptr (H0 is only read)
 template <int DK, int DV>
-static void launch_vec_shape(float *H0, const void *q, const void *k, const void *v,
-                             const float *gate, const int32_t *parent,
-                             const int32_t *node_offsets, float *out, const bole_dims_t &d,
+static void launch_vec_shape(const bole_layer_t *layers, int nl, const int32_t *parent,
+                             const int32_t *node_offsets, const bole_dims_t &d,
                              int32_t *tree_status, hipStream_t stream, const VecLazy *lz) {
     constexpr int G = DV < 64 ? 1 : DV / 64;
     const unsigned U = (unsigned)d.batch * (unsigned)d.heads;
-    const unsigned grid = G == 1 ? U : ((U + 7) / 8) * 8 * G;
-    const auto qb = static_cast<const __bf16 *>(q);
-    const auto kb = static_cast<const __bf16 *>(k);
-    const auto vb = static_cast<const __bf16 *>(v);
+    const dim3 grid(G == 1 ? U : ((U + 7) / 8) * 8 * G, (unsigned)nl);
+    LayerTable lt = {};
+    for (int l = 0; l < nl; ++l) lt.l[l] = layers[l];
     if (lz)
-        verify_vec_kernel<DK, DV, true><<<dim3(grid), dim3(kVecThreads), 0, stream>>>(
-            H0, qb, kb, vb, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
-            (int)U, max_tree_nodes(d.flags), *lz);
+        verify_vec_kernel<DK, DV, true><<<grid, dim3(kVecThreads), 0, stream>>>(
+            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U,
+            max_tree_nodes(d.flags), *lz);
     else
-        verify_vec_kernel<DK, DV, false><<<dim3(grid), dim3(kVecThreads), 0, stream>>>(
-            H0, qb, kb, vb, gate, parent, node_offsets, out, tree_status, d.heads, d.total_nodes,
-            (int)U, max_tree_nodes(d.flags), VecLazy{});
+        verify_vec_kernel<DK, DV, false><<<grid, dim3(kVecThreads), 0, stream>>>(
+            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U,
+            max_tree_nodes(d.flags), VecLazy{});
 }
 
-static hipError_t launch_vec(float *H0, const void *q, const void *k, const void *v,
-                             const float *gate, const int32_t *parent,
-                             const int32_t *node_offsets, float *out, const bole_dims_t &d,
+static hipError_t launch_vec(const bole_layer_t *layers, int nl, const int32_t *parent,
+                             const int32_t *node_offsets, const bole_dims_t &d,
                              int32_t *tree_status, hipStream_t stream, const VecLazy *lz) {
 #define BOLE_VEC_CASE(DKV, DVV)                                                                \
     if (d.d_k == DKV && d.d_v == DVV) {                                                         \
-        launch_vec_shape<DKV, DVV>(H0, q, k, v, gate, parent, node_offsets, out, d, tree_status, \
-                                   stream, lz);                                                 \
+        launch_vec_shape<DKV, DVV>(layers, nl, parent, node_offsets, d, tree_status, stream, lz); \
         return hipGetLastError();                                                               \
     }
     BOLE_VEC_CASE(64, 32) BOLE_VEC_CASE(64, 64) BOLE_VEC_CASE(64, 128) BOLE_VEC_CASE(64, 256)
@@ -674,13 +681,10 @@ static hipError_t launch_vec(float *H0, const void *q, const void *k, const void
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_verify_vec(const float *H0, const void *q, const void *k, const void *v,
-                             const float *gate, const int32_t *parent,
-                             const int32_t *node_offsets, float *out, const bole_dims_t &d,
+hipError_t launch_verify_vec(const bole_layer_t *layers, int nl, const int32_t *parent,
+                             const int32_t *node_offsets, const bole_dims_t &d,
                              int32_t *tree_status, hipStream_t stream) {
-    // the verify-only instantiation never writes H0
-    return launch_vec(const_cast<float *>(H0), q, k, v, gate, parent, node_offsets, out, d,
-                      tree_status, stream, nullptr);
+    return launch_vec(layers, nl, parent, node_offsets, d, tree_status, stream, nullptr);
 }
 
 bool verify_vec_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const bole_layer_t &y) {
@@ -695,7 +699,7 @@ bool verify_vec_lazy_applies(const bole_dims_t &d, const bole_dims_t &pd, const 
     return a % 16 == 0;
 }
 
-hipError_t launch_verify_vec_lazy(const bole_layer_t &y, const PrevPath &prev,
+hipError_t launch_verify_vec_lazy(const bole_layer_t *layers, int nl, const PrevPath &prev,
                                   const bole_dims_t &pd, const int32_t *parent,
                                   const int32_t *node_offsets, const bole_dims_t &d,
                                   int32_t *tree_status, hipStream_t stream) {
@@ -706,14 +710,10 @@ hipError_t launch_verify_vec_lazy(const bole_layer_t &y, const PrevPath &prev,
     lz.accepted_len = prev.accepted_len;
     lz.path_nodes = prev.path_nodes;
     lz.tree_status = prev.tree_status;
-    lz.k = static_cast<const __bf16 *>(y.prev_k);
-    lz.v = static_cast<const __bf16 *>(y.prev_v);
-    lz.gate = y.prev_gate;
     lz.T = pd.total_nodes;
     lz.max_path = pd.max_path;
     lz.max_n = max_tree_nodes(pd.flags);
-    return launch_vec(y.H0, y.q, y.k, y.v, y.gate, parent, node_offsets, y.out, d, tree_status,
-                      stream, &lz);
+    return launch_vec(layers, nl, parent, node_offsets, d, tree_status, stream, &lz);
 }
 
 }  // namespace bole
