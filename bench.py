@@ -525,9 +525,16 @@ def config_sweep(dev, reps=20, configs=(1, 2, 3, 4, 5)):
                                for x in sets],
                     "commit": [bole.bind_commit_path(x["H0"], x["k"], x["v"], x["gate"], x["par"],
                                                      x["offs"], x["ai"], x["al"], stream=stream)
-                               for x in sets]}
+                               for x in sets],
+                    # one decode step in one call: the set's own path committed (as the
+                    # previous step's) and its tree verified against the new state
+                    "lazy": [bole.bind_tree_verify_lazy_commit(
+                        x["H0"], (x["k"], x["v"], x["gate"], x["par"], x["offs"]), x["ai"],
+                        x["al"], x["q"], x["k"], x["v"], x["gate"], x["par"], x["offs"], x["out"],
+                        stream=stream) for x in sets]}
         s_f = 2 if lay.q.dtype == torch.bfloat16 else 4
-        nbytes = {"verify": verify_bytes(wl, s_f), "commit": commit_bytes(wl, s_f)}
+        nbytes = {"verify": verify_bytes(wl, s_f), "commit": commit_bytes(wl, s_f),
+                  "lazy": lazy_bytes(wl, s_f)}
         if int(np.diff(wl.node_offsets).max()) <= 32:
             launches["verify_budget32"] = [bole.bind_tree_verify(
                 x["H0"], x["q"], x["k"], x["v"], x["gate"], x["par"], x["offs"], x["out"],
@@ -547,6 +554,46 @@ def config_sweep(dev, reps=20, configs=(1, 2, 3, 4, 5)):
                 rec[name]["nodes_per_s"] = wl.total_nodes / (us * 1e-6)
         print(json.dumps(rec), flush=True)
         del sets, launches
+    if 3 in configs:
+        vector_stack(dev, stream, reps)
+
+
+def vector_stack(dev, stream, reps, n_layers=8):
+    """8 layers of workload 3's shape (16 sequences x 16 heads, d_k = d_v = 128,
+    per-channel gates, 64-node trees) sharing one tree per sequence: the verify stack and
+    the lazy stack, one launch each (8 layers x 46 MB of inputs, read cold)."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from tree_speculative_decoding_02_amd import bole
+    wl = W.make_config(3)
+    kw = dict(batch=wl.batch, heads=wl.heads, d_k=wl.d_k, d_v=wl.d_v,
+              sizes=np.diff(wl.node_offsets).tolist(), kind="bestfirst", vector_gate=True)
+    lays = [wl.layers[0]] + [W.make_random(5300 + l, **kw).layers[0] for l in range(n_layers - 1)]
+    g = lambda t: t.to(dev)
+    par, offs = g(torch.from_numpy(wl.parent)), g(torch.from_numpy(wl.node_offsets))
+    ai, al = g(torch.from_numpy(wl.accepted_idx)), g(torch.from_numpy(wl.accepted_len))
+    layers = []
+    for l in lays:
+        y = dict(H0=g(l.H0), q=g(l.q), k=g(l.k), v=g(l.v), gate=g(l.gate),
+                 out=torch.empty((wl.total_nodes, wl.heads, wl.d_v), dtype=torch.float32,
+                                 device=dev))
+        y.update(prev_k=y["k"], prev_v=y["v"], prev_gate=y["gate"])
+        layers.append(y)
+    fv = bole.bind_tree_verify_layers(layers, par, offs, stream=stream)
+    fl = bole.bind_tree_verify_lazy_commit_layers(layers, par, offs, ai, al, par, offs,
+                                                  stream=stream)
+    rec = {"kind": "vector_stack", "workload": "gla_vector x 8 layers", "layers": n_layers,
+           "batch": wl.batch, "heads": wl.heads, "d_k": wl.d_k, "d_v": wl.d_v,
+           "total_nodes": wl.total_nodes}
+    for name, f, nb in (("verify", fv, verify_bytes(wl)), ("lazy", fl, lazy_bytes(wl))):
+        us = time_rotated([f] * 4, stream, reps)
+        gbs = n_layers * nb / (us * 1e3)
+        rec[name] = {"median_us": us, "bytes": n_layers * nb, "GB_s": gbs,
+                     "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+                     "nodes_per_s": n_layers * wl.total_nodes / (us * 1e-6)}
+    print(json.dumps(rec), flush=True)
 
 
 def cpu_baseline(wl, min_seconds):

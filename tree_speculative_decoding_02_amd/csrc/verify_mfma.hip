@@ -9,11 +9,11 @@
 //
 // Trees of 1..32 nodes take one wavefront per sequence, head and 64-column group; trees
 // of 33..64 nodes take two wavefronts that split H_0's rows. A batch that may hold larger
-// trees runs both in one fused launch (in the lazy form, the larger trees take a launch
-// of their own); each launch covers up to 16 layers that share the trees
-// (blockIdx.y = layer). The LAZY instantiations (one wavefront, and the row split) first
-// apply the previous step's accepted path to H_0 (section 2's restore) and write it back,
-// in the same pass over H_0: each unit is committed by the body that verifies its tree.
+// trees runs both in one fused launch; each launch covers up to 16 layers that share the
+// trees (blockIdx.y = layer). The LAZY instantiations first apply the previous step's
+// accepted path to H_0 (section 2's restore) and write it back, in the same pass over
+// H_0: each unit is committed by the body (one wavefront, or the row split) that
+// verifies its tree.
 // H_0 goes from HBM straight into MFMA operand registers with
 // row-contiguous 16-byte loads, so a wavefront needs only 12 KB of LDS (K and V) and
 // eight of them fit on a CU: the whole benchmark batch is in flight at once. fp32
@@ -28,7 +28,7 @@
 namespace bole {
 
 // Trees of 1..32 nodes (and the status of every tree except those of 33..64 nodes, which
-// the two-wavefront kernel below takes): one wavefront per (sequence, head, 64-column
+// the two-wavefront body below takes): one wavefront per (sequence, head, 64-column
 // group) covers the tree's 32 node rows as two 16-node tiles. 16x16 matrix-core tiles
 // throughout: lane = (n, g) with n = lane % 16, g = lane / 16.
 //
@@ -66,12 +66,15 @@ struct LazyCommit {
 // (statuses, path rows) are written by layer 0 only.
 template <int DK, int DV>
 constexpr int ksplit_smem_bytes();
+template <int DK, int DV>
+constexpr int ksplit_lazy_smem_elems();
 template <int DK, int DV, bool LAZY>
 __device__ __forceinline__ void ksplit_body(const bole_layer_t, const int32_t *, const int32_t *,
                                             int32_t *, int, int, int, int, char *, int, int,
                                             const LazyCommit &, __bf16 *);
 
-// FUSED: every tree size in one launch, for a caller without a budget of 32 nodes. Each
+// FUSED: every tree size in one launch, for a caller without a budget of 32 nodes (with
+// LAZY, each body also commits the units whose trees it verifies). Each
 // unit of the workgroup has two wavefronts and an LDS region of its own: a tree of 33..64
 // nodes takes the row-split body (below) on both, one of up to 32 nodes the one-wavefront
 // body on the first (the second exits); both leave at once, and wave-uniformly, for the
@@ -98,7 +101,6 @@ __global__ __launch_bounds__(FUSED ? 128 * NW : 64 * NW, 2) void verify_mfma_tre
     constexpr int VPR = CW / 8;             // 16-byte pieces per V row (of this group's columns)
     typedef float hvec __attribute__((ext_vector_type(CPL)));
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
-    static_assert(!(LAZY && FUSED), "trees of 33..64 nodes follow a lazy commit in their own launch");
     static_assert(NW == 1 || G == 1, "unit groups: one column group per unit");
     static_assert(!FUSED || NW <= 2, "fused unit groups: at most two units");
     // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR); V rows of the group's columns,
@@ -111,6 +113,9 @@ __global__ __launch_bounds__(FUSED ? 128 * NW : 64 * NW, 2) void verify_mfma_tre
     __shared__ bf16x8 s_k_own[FUSED ? 1 : NW * NN * PPR];
     __shared__ __bf16 s_v_own[FUSED ? 8 : NW * NN * CW];
     __shared__ __bf16 s_pk_all[NW * kLazyStage * DK], s_pv_all[NW * kLazyStage * CW];
+    // FUSED and LAZY: the row-split body's path staging, one region per wavefront
+    __shared__ __align__(16) __bf16
+        s_lzk[FUSED && LAZY ? 2 * NW * ksplit_lazy_smem_elems<DK, DV>() : 8];
     // this wavefront's unit of the group (FUSED: two wavefronts per unit)
     const int wv = NW > 1 ? (int)(threadIdx.x >> (FUSED ? 7 : 6)) : 0;
     char *const s_unit = s_fused + (FUSED ? wv * ksplit_smem_bytes<DK, DV>() : 0);
@@ -121,9 +126,10 @@ __global__ __launch_bounds__(FUSED ? 128 * NW : 64 * NW, 2) void verify_mfma_tre
     __bf16 *const s_pv = s_pv_all + wv * kLazyStage * CW;
     const bole_layer_t &ly = lt.l[blockIdx.y];
     if constexpr (FUSED) {
-        ksplit_body<DK, DV, false>(ly, parent, node_offsets, tree_status, H, T, U, max_n, s_unit,
-                                   NW * (int)blockIdx.x + wv, (int)((threadIdx.x >> 6) & 1), lc,
-                                   nullptr);
+        ksplit_body<DK, DV, LAZY>(ly, parent, node_offsets, tree_status, H, T, U, max_n, s_unit,
+                                  NW * (int)blockIdx.x + wv, (int)((threadIdx.x >> 6) & 1), lc,
+                                  LAZY ? s_lzk + (threadIdx.x >> 6) * ksplit_lazy_smem_elems<DK, DV>()
+                                       : nullptr);
         if (threadIdx.x & 64) return;  // the second wavefront of each unit
     }
     float *const H0 = ly.H0;                // written only by the lazy commit
@@ -157,8 +163,8 @@ __global__ __launch_bounds__(FUSED ? 128 * NW : 64 * NW, 2) void verify_mfma_tre
         if (writer) tree_status[b] = tr.status;
         do_verify = false;
     } else if (tr.n > 32) {
-        // the row-split kernel's; after a lazy commit that kernel also commits the
-        // previous path for the unit, in the same pass over H_0
+        // the row-split body's, which in the lazy form also commits the unit's previous
+        // path, in the same pass over H_0
         if (LAZY) return;
         do_verify = false;
     } else if (tr.n == 0) {
@@ -909,18 +915,6 @@ __device__ __forceinline__ void ksplit_body(
         }
 }
 
-template <int DK, int DV, bool LAZY>
-__global__ __launch_bounds__(128, LAZY ? 2 : 3) void verify_mfma_ksplit_kernel(
-    const LayerTable lt, const int32_t *__restrict__ parent,
-    const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
-    int U, int max_n, LazyCommit lc) {
-    __shared__ __align__(16) char smem[ksplit_smem_bytes<DK, DV>()];
-    __shared__ __align__(16) __bf16 s_lazy[LAZY ? 2 * ksplit_lazy_smem_elems<DK, DV>() : 8];
-    ksplit_body<DK, DV, LAZY>(lt.l[blockIdx.y], parent, node_offsets, tree_status, H, T, U, max_n,
-                              smem, (int)blockIdx.x, (int)(threadIdx.x >> 6), lc,
-                              s_lazy + (LAZY ? (threadIdx.x >> 6) * ksplit_lazy_smem_elems<DK, DV>() : 0));
-}
-
 static bool shape_ok(const bole_dims_t &d) {
     if (d.flags & BOLE_FLAG_FORCE_GENERIC) return false;
     if (d.factor_dtype != BOLE_DTYPE_BF16 || d.gate_kind != BOLE_GATE_SCALAR) return false;
@@ -973,16 +967,22 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
     for (int l = 0; l < nl; ++l) lt.l[l] = layers[l];
     const LazyCommit none = {};
     const int H = d.heads, T = d.total_nodes;
-    if (lazy) {
-        // the large trees of this step are verified against the state this launch commits
+    if (lazy && max_n > 32) {
+        // every tree size in one launch, as the fused verify below, each body committing
+        // the units whose trees it verifies
+        if (group && H % 2 == 0)
+            verify_mfma_tree_kernel<DK, DV, true, true, G == 1 ? 2 : 1><<<
+                dim3(G == 1 ? (U + 1) / 2 : grid.x, (unsigned)nl), dim3(G == 1 ? 256 : 128), 0, stream>>>(
+                lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
+        else
+            verify_mfma_tree_kernel<DK, DV, true, true, 1><<<grid, dim3(128), 0, stream>>>(
+                lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
+    } else if (lazy) {
         if (group)
             verify_mfma_tree_kernel<DK, DV, true, false, NL><<<lgrid, dim3(64 * NL), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
         else
             verify_mfma_tree_kernel<DK, DV, true, false, 1><<<grid, dim3(64), 0, stream>>>(
-                lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
-        if (max_n > 32)
-            verify_mfma_ksplit_kernel<DK, DV, true><<<grid, dim3(128), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
     } else if (max_n > 32) {
         // two units per workgroup only when they always share a tree (an even head count)
