@@ -221,7 +221,8 @@ def main():
     # the same work in two passes, one launch each for the stack
     tp_ms, tp_group_ms, _ = timed([[vstack], [cstack]], args.steps, args.warmup)
     # the lazy step for a caller that states no tree budget: trees of up to 64 nodes may
-    # come, so a row-split launch follows (its workgroups find 32-node trees and leave)
+    # come, so the fused launch runs (two wavefronts per unit, the second idle for trees
+    # of up to 32 nodes)
     lazy_any = bole.bind_tree_verify_lazy_commit_layers(layers, parent, offs, acc_idx, acc_len,
                                                         parent, offs, stream=stream)
     la_ms, _, _ = timed([[lazy_any]], args.steps, args.warmup)
@@ -283,7 +284,7 @@ def main():
                                  "launches_per_step": 2},
             "lazy_commit_stacked_no_tree_budget": {"ms_per_step": la_ms,
                                                    "value": nodes / (la_ms * 1e-3),
-                                                   "launches_per_step": 2},
+                                                   "launches_per_step": 1},
         },
         "hbm_GB_s_step": L * lb / (ms_per_step * 1e6),
         "wall_ms_per_step": 1e3 * wall / args.steps,
