@@ -541,6 +541,11 @@ def config_sweep(dev, reps=20, configs=(1, 2, 3, 4, 5)):
                 x["H0"], x["q"], x["k"], x["v"], x["gate"], x["par"], x["offs"], x["out"],
                 stream=stream, trees_le_32=True) for x in sets]
             nbytes["verify_budget32"] = nbytes["verify"]
+            launches["lazy_budget32"] = [bole.bind_tree_verify_lazy_commit(
+                x["H0"], (x["k"], x["v"], x["gate"], x["par"], x["offs"]), x["ai"], x["al"],
+                x["q"], x["k"], x["v"], x["gate"], x["par"], x["offs"], x["out"], stream=stream,
+                trees_le_32=True, prev_trees_le_32=True) for x in sets]
+            nbytes["lazy_budget32"] = nbytes["lazy"]
         rec = {"kind": "config_sweep", "config": cid, "workload": names[cid], "batch": wl.batch,
                "heads": wl.heads, "d_k": wl.d_k, "d_v": wl.d_v, "total_nodes": wl.total_nodes,
                "vector_gate": bool(wl.vector_gate), "factor_dtype": str(lay.q.dtype),
