@@ -213,17 +213,21 @@ BOLE_API bole_status_t bole_tree_verify(const float *H0, const void *q, const vo
  * restore runs, and nothing reads the committed state before the next step's verify. The accepted path of a step is known only after
  * that step's verify, so its commit can ride on the next step's verify; H0 is then read
  * once and written once per step instead of read twice and written once.
- * The result is exactly that of
+ * The result is that of
  *     bole_commit_path(H0, prev, prev_accepted_idx, prev_accepted_len, prev_dims,
  *                      prev_path_nodes, prev_tree_status, stream);
  *     bole_tree_verify(H0, q, k, v, gate, parent, node_offsets, out, dims, tree_status,
  *                      stream);
- * and every argument follows those two calls. prev_dims describes the previous step
+ * with the same statuses and path rows, and states and outputs equal to fp32 rounding
+ * (the same products and sums, which the two forms' kernels may contract differently).
+ * Every argument follows those two calls. prev_dims describes the previous step
  * (its total_nodes, max_path and flags); batch, heads, d_k, d_v, factor_dtype and
  * gate_kind must equal those of dims (else BOLE_ERR_INVALID_VALUE). On exit H0 holds
  * the state after the previous step's accepted tokens: the state the next call, or a
- * final bole_commit_path of the last step, starts from. Shapes the one-pass kernel does
- * not cover run as the two calls above.
+ * final bole_commit_path of the last step, starts from. The one-pass kernels cover bf16
+ * factors with scalar or per-channel gates, d_k 64 or 128, d_v 32..256 and 16-byte
+ * aligned rows, every tree size up to 64 nodes; any other shape, and a call under
+ * BOLE_FLAG_VALIDATE_GATES, runs as the two calls above.
  */
 BOLE_API bole_status_t bole_tree_verify_lazy_commit(
     float *H0, const bole_factors_t *prev, const int32_t *prev_accepted_idx,
