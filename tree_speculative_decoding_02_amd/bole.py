@@ -288,7 +288,7 @@ def bole_tree_verify_lazy_commit(H0, prev, prev_accepted_idx, prev_accepted_len,
     """Commits the previous step's accepted path into H0 and verifies this step's tree
     against the result, in one pass over H0. prev = (k, v, gate, parent, node_offsets)
     of the previous step. Same result as bole_commit_path(previous step) followed by
-    bole_tree_verify(this step); returns out. validate_gates sets
+    bole_tree_verify(this step), to fp32 rounding; returns out. validate_gates sets
     BOLE_FLAG_VALIDATE_GATES for both steps."""
     out, args, _ = _lazy_args(H0, prev, prev_accepted_idx, prev_accepted_len, q, k, v, gate,
                               parent, node_offsets, out, prev_path_nodes, prev_tree_status,
