@@ -1028,3 +1028,58 @@ def test_fused_pairs_equal_single_units(bole):
     assert rel_err_rows(outs[0].double().cpu().numpy()[good], ref[good]) <= TOL[torch.bfloat16]
     bad_rows = outs[0][int(o[big]):int(o[big + 1])]
     assert torch.isnan(bad_rows).all()
+
+
+def test_fused_lazy_pairs_equal_single_units(bole):
+    """The lazy stack without a tree budget on a stack large enough to take two units per
+    workgroup (an even head count): every tree size up to 64 nodes in one fused launch,
+    each body committing the units it verifies. Bit for bit the single-layer calls, which
+    take one unit per workgroup; within tolerance of the oracle on the first layer; a bad
+    previous path and a bad current tree keep their statuses."""
+    kw = dict(batch=33, heads=32, d_k=128, d_v=64, kind="random")
+    wp, lp = _stack(4343, 2, **kw)
+    wc, lc = _stack(4344, 2, **kw)
+    o = wc.node_offsets
+    parent = wc.parent.copy()
+    big = next(b for b in range(wc.batch) if o[b + 1] - o[b] > 40)
+    parent[o[big] + 37] = 39                      # a bad parent in a large current tree
+    acc = wp.accepted_idx.copy()
+    bp = next(b for b in range(wp.batch) if wp.accepted_len[b] >= 2)
+    acc[bp, 1] = acc[bp, 0]                       # previous path bp: not a chain
+    tp, tc = _tree_dev(wp), _tree_dev(wc)
+    tc["parent"] = torch.from_numpy(parent).to(dev())
+    tp["acc_idx"] = torch.from_numpy(acc).to(dev())
+    assert wc.batch * kw["heads"] * 2 >= 2048 and wc.batch * kw["heads"] < 2048
+    B = wc.batch
+    status = lambda: torch.full((B,), -7, dtype=torch.int32, device=dev())
+    print("[case] fused lazy pairs: lazy stack", flush=True)
+    ys = _dev_layers(lc, lp)
+    H1 = [y["H0"].clone() for y in ys]
+    pst_s, st_s = status(), status()
+    pn_s = torch.full(tuple(tp["acc_idx"].shape), -7, dtype=torch.int32, device=dev())
+    outs = bole.bole_tree_verify_lazy_commit_layers(
+        ys, tp["parent"], tp["offs"], tp["acc_idx"], tp["acc_len"], tc["parent"], tc["offs"],
+        prev_path_nodes=pn_s, prev_tree_status=pst_s, tree_status=st_s)
+    for y, H, out in zip(ys, H1, outs):
+        pst_1, st_1 = status(), status()
+        pn_1 = torch.empty_like(pn_s)
+        o1 = bole.bole_tree_verify_lazy_commit(
+            H, (y["prev_k"], y["prev_v"], y["prev_gate"], tp["parent"], tp["offs"]),
+            tp["acc_idx"], tp["acc_len"], y["q"], y["k"], y["v"], y["gate"], tc["parent"],
+            tc["offs"], prev_path_nodes=pn_1, prev_tree_status=pst_1, tree_status=st_1)
+        torch.cuda.synchronize()
+        assert torch.equal(y["H0"], H)
+        assert torch.equal(out.nan_to_num(7.0), o1.nan_to_num(7.0))
+        assert torch.equal(pst_s, pst_1) and torch.equal(st_s, st_1) and torch.equal(pn_s, pn_1)
+    Href, pn_ref, pst_ref = oracle.commit_serial(lc[0].H0, lp[0].k, lp[0].v, lp[0].gate,
+                                                 wp.parent, wp.node_offsets, acc,
+                                                 wp.accepted_len, False)
+    oref, st_ref = oracle.verify_serial(Href, lc[0].q, lc[0].k, lc[0].v, lc[0].gate, parent,
+                                        wc.node_offsets, False)
+    assert pst_s.cpu().tolist() == pst_ref.tolist() and pst_ref[bp] == 3
+    assert st_s.cpu().tolist() == st_ref.tolist() and st_ref[big] == 2
+    np.testing.assert_array_equal(pn_s.cpu().numpy(), pn_ref)
+    assert rel_err_states(ys[0]["H0"].double().cpu().numpy(), Href) <= TOL[torch.bfloat16]
+    good = np.concatenate([np.arange(o[b], o[b + 1]) for b in range(B) if st_ref[b] == 0])
+    assert rel_err_rows(outs[0].double().cpu().numpy()[good], oref[good]) <= TOL[torch.bfloat16]
+    assert torch.isnan(outs[0][int(o[big]):int(o[big + 1])]).all()
