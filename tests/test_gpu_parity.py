@@ -793,6 +793,9 @@ LAYER_CASES = [
     ("vector_gate", 3, dict(batch=3, heads=2, d_k=128, d_v=64, vector_gate=True)),
     # two launches of up to 16 layers, two column groups per unit
     ("vector_gate_17_layers", 17, dict(batch=3, heads=2, d_k=64, d_v=128, vector_gate=True)),
+    # a stack long enough for one column group per workgroup, against single-layer calls
+    # short enough for two per workgroup: the two forms agree bit for bit
+    ("vector_gate_group_forms", 3, dict(batch=16, heads=16, d_k=128, d_v=128, vector_gate=True)),
     ("fp32", 2, dict(batch=3, heads=2, d_k=64, d_v=64, factor_dtype=torch.float32)),
 ]
 

@@ -10,26 +10,28 @@
 //  - the H_0 term runs on bf16 matrix cores with the decayed query 2^{LG_i} * q_i
 //    (fp32, split hi + lo) as the A operand and H_0 (split hi + lo) as the B operand:
 //    three products per tile (hi.hi, hi.lo, lo.hi);
-//  - the intra-tree term touches only ancestor pairs (a node has depth-many), on the
-//    vector ALU: each pair's weight is one 128-channel sum with exact exponents
-//    LG_i - LG_j <= 0, so no factor can overflow.
+//  - the intra-tree term runs on matrix cores too when the tree's LG range allows it
+//    (w_ij as the dot product of q_i 2^{LG_i - M} and k_j 2^{M - LG_j}, M the range's
+//    midpoint); otherwise each ancestor pair's weight is a 128-channel sum on the vector
+//    ALU with exact exponents LG_i - LG_j <= 0, so no factor can overflow.
 //
-// One 256-thread workgroup per (sequence, head, 64-column group), trees of up to 64
-// nodes. Every input is staged through registers with plain 16-byte loads issued in the
-// order of use (parent, gate, K, Q fragments, then H_0 and V), so the
-// H_0 and V loads stay in flight while the first phases compute, and each phase waits
-// only for what it reads:
+// One 256-thread workgroup per (sequence, head, 64-column group), or, for a verify launch
+// short enough to be resident at once, one 512-thread workgroup per two column groups;
+// trees of up to 64 nodes; up to 16 layers per launch. Every input is staged through
+// registers with plain 16-byte loads issued in the order of use (parent, gate, K, Q
+// fragments, then H_0 and V), so the H_0 and V loads stay in flight while the first
+// phases compute, and each phase waits only for what it reads:
 //  1. wavefront 0 builds the topology; the gate and K rows go to LDS;
 //  2. gate -> log2 -> root-first cumulative sums LG by pointer doubling: each thread
 //     keeps its own entries in registers, and round r adds the sum held at the node's
 //     2^r-th ancestor (ceil(log2 depth) rounds, one barrier pair each);
-//  3. pair weights w_ij for every ancestor pair, four lanes per node; each wavefront
-//     then builds its decayed-query operands (hi + lo) for one 16-node tile;
+//  3. the LG range; pair weights (exact path) or key operands and S tiles (factored
+//     path); each wavefront builds its decayed-query operands for one 16-node tile;
 //  4. H_0 and V go to LDS, H_0 reusing the space of the LG and K tables;
 //  5. H_0 term (v_mfma_f32_16x16x32_bf16, B operands read as 16-byte rows: lane (n, g)
 //     takes columns CPL*n ..), the intra term accumulated into the same registers, and
 //     the rows stored.
-// About 72 KB of LDS at d_k = 128, so two workgroups share a CU.
+// About 74 KB of LDS at d_k = 128 (two workgroups per CU), 98 KB for a pair.
 #include "bole_device.h"
 #include "launch.h"
 #include "mfma_util.h"
@@ -37,6 +39,9 @@
 namespace bole {
 
 constexpr int kVecThreads = 256;
+// launches of at most this many one-column-group workgroups (two per CU on 256 CUs) take
+// the two-group form (see launch_vec_shape)
+constexpr uint64_t kVecPairMaxWorkgroups = 512;
 
 // The previous step's tree and accepted path, for LAZY (each layer's prev_k, prev_v and
 // prev_gate are its factors).
@@ -67,55 +72,68 @@ __device__ __forceinline__ void range_dpp_step(float &mn, float &mx) {
 // empty is committed all the same.
 // Layer blockIdx.y of the table; every layer runs the same trees, and the per-tree
 // outputs (statuses, path rows) are written by layer 0 only.
-template <int DK, int DV, bool LAZY>
-__global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
+// CG = 2 (d_v a multiple of 128): one 512-thread workgroup takes two 64-column groups of a
+// unit, so the work that does not depend on the columns (topology, LG, pair weights, query
+// and key operands, S tiles) is done once for both; threads 256 h .. 256 h + 255 take
+// group h's H_0 rows, V columns and products, and waves w and w + 4 share node tile w.
+template <int DK, int DV, bool LAZY, int CG>
+__global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
     int U, int max_n, VecLazy lz) {
     constexpr int N = kMaxTree;             // node rows staged (tree nodes; the rest clamped)
-    constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
+    constexpr int NT = kVecThreads * CG;    // threads per workgroup
+    constexpr int CW = DV < 64 ? DV : 64;   // state columns per column group
+    constexpr int CGW = CW * CG;            // state columns per workgroup
     constexpr int CPL = CW / 16;            // columns per lane in the products
     constexpr int G = DV / CW;              // column groups per unit
+    constexpr int GS = G / CG;              // workgroups per unit
+    static_assert(CG == 1 || (CG == 2 && G % 2 == 0), "column groups per workgroup");
     constexpr int KT = DK / 32;             // k-steps of the 16x16x32 products
     constexpr int CH = DK / 4;              // channels per lane in the pair weights
     // 16-byte pieces per thread of each staged table
-    constexpr int GP = DK / 4, GPT = N * GP / kVecThreads;    // gate rows, fp32
-    constexpr int KP = DK / 8, KPT = N * KP / kVecThreads;    // K rows, bf16
-    constexpr int HRG = DK / 8;                                // H_0 slice: 8-row groups
-    constexpr int VP = CW / 8, VPT = N * VP / kVecThreads;    // V rows, bf16
+    constexpr int GP = DK / 4, GPT = N * GP / NT;     // gate rows, fp32
+    constexpr int KP = DK / 8, KPT = N * KP / NT;     // K rows, bf16
+    constexpr int HRG = DK / 8;                       // H_0 slice: 8-row groups
+    constexpr int VP = CGW / 8, VPT = N * VP / NT;    // V rows (the workgroup's columns), bf16
     static_assert(GPT >= 1 && KPT >= 1 && VPT >= 1 && HRG * 16 <= kVecThreads, "staging split");
     typedef float hvec __attribute__((ext_vector_type(CPL)));
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    // phase A: LG (N x DK fp32) then K (N x DK bf16); phase B: the H_0 slice (DK x CW, as
-    // bf16 hi and lo tables)
-    constexpr int kBig = (N * DK + N * DK / 2) > DK * CW ? (N * DK + N * DK / 2) : DK * CW;
+    // phase A: LG (N x DK fp32) then K (N x DK bf16); phase B: each column group's H_0
+    // slice (DK x CW, as bf16 hi and lo tables)
+    constexpr int kBig =
+        (N * DK + N * DK / 2) > CG * DK * CW ? (N * DK + N * DK / 2) : CG * DK * CW;
     __shared__ __attribute__((aligned(16))) float s_big[kBig];
-    __shared__ __attribute__((aligned(16))) __bf16 s_v[N * CW];   // V rows, the group's columns
+    __shared__ __attribute__((aligned(16))) __bf16 s_v[N * CGW];  // V rows, the columns
     __shared__ float s_w[N * N];                                   // w_ij at [N i + j]
     __shared__ uint64_t s_mask[N];
     __shared__ int s_anc[6][N];                                    // 2^r-th ancestor (or -1)
     __shared__ int s_info[2];                                      // status, doubling rounds
-    __shared__ float s_red[4][2];                                  // per wave: min, max of LG
+    __shared__ float s_red[NT / 64][2];                            // per wave: min, max of LG
     __shared__ int s_pinfo[2];                                     // LAZY: path status, length
     __shared__ int s_prow[LAZY ? 64 : 1];                          // LAZY: path rows
     float *s_lg = s_big;
     __bf16 *s_k = reinterpret_cast<__bf16 *>(s_big + N * DK);
-    __bf16 *s_h0b = reinterpret_cast<__bf16 *>(s_big);  // H_0 slice, hi then lo tables
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int tw = wave & 3;                // node tile of this wavefront's products
+    const int hf = tid / kVecThreads;       // column group of this thread within the workgroup
+    const int tl = tid - hf * kVecThreads;  // thread index within its column group
+    // this thread's column group's H_0 slice: its hi table, then its lo table
+    __bf16 *const s_h0g = reinterpret_cast<__bf16 *>(s_big) + hf * 2 * DK * CW;
     int unit, cg;
-    if (G == 1) {
+    if (GS == 1) {
         unit = blockIdx.x;
         cg = 0;
     } else {
         const int slot = blockIdx.x >> 3;
-        cg = slot % G;
-        unit = (slot / G) * 8 + (blockIdx.x & 7);
+        cg = slot % GS;
+        unit = (slot / GS) * 8 + (blockIdx.x & 7);
         if (unit >= U) return;
     }
     const int b = unit / H, h = unit - b * H;
-    const int c0 = cg * CW;
+    const int c0 = cg * CGW;
     const bool first = blockIdx.y == 0 && h == 0 && cg == 0;  // writes the per-tree outputs
     const bool writer = tree_status != nullptr && first && tid == 0;
     const bole_layer_t &ly = lt.l[blockIdx.y];
@@ -127,17 +145,17 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     float *const out = ly.out;
 
     const TreeRange tr = tree_range(node_offsets, b, T, max_n);
-    float *const hu = H0 + (size_t)unit * DK * DV + c0;
-    const int hrg = tid >> 4, hn = tid & 15;  // H_0 slice: rows 8 hrg .., columns CPL*hn ..
+    // H_0 slice of this thread's column group: rows 8 hrg .., columns CPL*hn ..
+    float *const hu = H0 + (size_t)unit * DK * DV + c0 + hf * CW;
+    const int hrg = tl >> 4, hn = tl & 15;
 
     // ---- LAZY: the previous step's path. Its offsets and length, then (wavefront 0) its
     // parent links and indices; thread t stages chunk t of the first kStage path nodes, a
     // 16-byte piece of a node's gate row, k row or v columns (16 * t bytes into the stage).
     constexpr int kStage = 4;
-    constexpr int SGC = DK / 4, SKC = DK / 8, SVC = CW / 8, CPN = SGC + SKC + SVC;
+    constexpr int SGC = DK / 4, SKC = DK / 8, SVC = CGW / 8, CPN = SGC + SKC + SVC;
     constexpr int SB = 16 * CPN;            // stage bytes per path node
-    static_assert(!LAZY || (kStage * CPN <= kVecThreads && kStage * SB <= N * CW * 2),
-                  "path staging");
+    static_assert(!LAZY || (kStage * CPN <= NT && kStage * SB <= N * CGW * 2), "path staging");
     TreeRange ptr = {0, 0, BOLE_TREE_OK};
     int plen_raw = 0, lx = 0, lpx = -1, lpp = -1;
     bool plikely = false;
@@ -223,7 +241,8 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
                     const float4 ga = *reinterpret_cast<const float4 *>(nb + 32 * hrg);
                     const float4 gb = *reinterpret_cast<const float4 *>(nb + 32 * hrg + 16);
                     const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(nb + 4 * DK + 16 * hrg);
-                    const vvec vv = *reinterpret_cast<const vvec *>(nb + 6 * DK + 2 * CPL * hn);
+                    const vvec vv =
+                        *reinterpret_cast<const vvec *>(nb + 6 * DK + 2 * (hf * CW + CPL * hn));
                     const float g8[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
@@ -270,30 +289,31 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     const __bf16 *vu = v + (size_t)lo * rv + (size_t)h * DV + c0;
     float *ou = out + (size_t)lo * rv + (size_t)h * DV + c0;
     const int n16 = lane & 15, g4 = lane >> 4;
-    const int pi = tid >> 2, psub = tid & 3;  // pair-weight node and channel quarter
+    // pair-weight node and channel quarter (the exact path runs on the first 256 threads)
+    const int pi = tl >> 2, psub = tl & 3;
 
-    // ---- issue every load, in order of use. Piece P = tid + 256u of a table with PP
+    // ---- issue every load, in order of use. Piece P = tid + NT u of a table with PP
     // pieces per row is row P / PP, piece P % PP (rows past the tree repeat its last row).
     const int p_raw = wave == 0 ? parent[lo + min(lane, last)] : -1;
     u32x4 rg[GPT], rk[KPT], rvv[VPT];
     hvec rh[8];
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
-        const int P = tid + kVecThreads * u;
+        const int P = tid + NT * u;
         rg[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
             gu + ((uint32_t)min(P / GP, last) * rq + 4 * (P % GP))));
     }
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-        const int P = tid + kVecThreads * u;
+        const int P = tid + NT * u;
         rk[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
             ku + ((uint32_t)min(P / KP, last) * rq + 8 * (P % KP))));
     }
-    bf16x8 qf[KT];      // Q fragments: row 16*wave + n, channels 32t + 8g .. +7
+    bf16x8 qf[KT];      // Q fragments: row 16*tw + n, channels 32t + 8g .. +7
 #pragma unroll
     for (int t = 0; t < KT; ++t)
-        qf[t] = load16(qu + ((uint32_t)min(16 * wave + n16, last) * rq + 32 * t + 8 * g4));
-    // H_0: thread (hrg, hn) = (tid / 16, tid % 16) loads rows 8 hrg .. 8 hrg + 7 of the
+        qf[t] = load16(qu + ((uint32_t)min(16 * tw + n16, last) * rq + 32 * t + 8 * g4));
+    // H_0: thread (hrg, hn) of column group hf loads rows 8 hrg .. 8 hrg + 7 of the group's
     // slice, columns CPL*hn .. (the B-operand rows and columns of one lane)
     if (hrg < HRG) {
 #pragma unroll
@@ -303,7 +323,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-        const int P = tid + kVecThreads * u;
+        const int P = tid + NT * u;
         rvv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
             vu + ((uint32_t)min(P / VP, last) * rv + 8 * (P % VP))));
     }
@@ -333,7 +353,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     float4 lgv[GPT];  // this thread's gate entries: row (tid + 256u) / GP, channels 4*(.. % GP)
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
-        const int P = tid + kVecThreads * u;
+        const int P = tid + NT * u;
         const float4 x = __builtin_bit_cast(float4, rg[u]);
         lgv[u] = make_float4(__builtin_amdgcn_logf(x.x), __builtin_amdgcn_logf(x.y),
                              __builtin_amdgcn_logf(x.z), __builtin_amdgcn_logf(x.w));
@@ -341,15 +361,15 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     }
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-        const int P = tid + kVecThreads * u;
+        const int P = tid + NT * u;
         *reinterpret_cast<u32x4 *>(s_k + (P / KP) * DK + 8 * (P % KP)) = rk[u];
     }
     __syncthreads();
 
     if (s_info[0] != BOLE_TREE_OK) {
         if constexpr (LAZY) commit(rh);
-        for (int e = tid; e < n * CW; e += kVecThreads)
-            ou[(uint32_t)(e / CW) * rv + (e % CW)] = __builtin_nanf("");
+        for (int e = tid; e < n * CGW; e += NT)
+            ou[(uint32_t)(e / CGW) * rv + (e % CGW)] = __builtin_nanf("");
         return;
     }
 
@@ -360,7 +380,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         bool moved[GPT];  // entries whose 2^r-th ancestor exists; only they change
 #pragma unroll
         for (int u = 0; u < GPT; ++u) {
-            const int P = tid + kVecThreads * u;
+            const int P = tid + NT * u;
             const int a = s_anc[r][P / GP];
             moved[u] = a >= 0;
             if (moved[u]) {
@@ -374,7 +394,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < GPT; ++u) {
-            const int P = tid + kVecThreads * u;
+            const int P = tid + NT * u;
             if (moved[u])
                 *reinterpret_cast<float4 *>(s_lg + (P / GP) * DK + 4 * (P % GP)) = lgv[u];
         }
@@ -388,7 +408,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     float lmin = __builtin_inff(), lmax = -__builtin_inff();
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
-        if ((tid + kVecThreads * u) / GP < n) {
+        if ((tid + NT * u) / GP < n) {
             lmin = fminf(lmin, fminf(fminf(lgv[u].x, lgv[u].y), fminf(lgv[u].z, lgv[u].w)));
             lmax = fmaxf(lmax, fmaxf(fmaxf(lgv[u].x, lgv[u].y), fmaxf(lgv[u].z, lgv[u].w)));
         }
@@ -404,14 +424,18 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         s_red[wave][1] = lmax;
     }
     __syncthreads();
-    const float lo_lg = fminf(fminf(s_red[0][0], s_red[1][0]), fminf(s_red[2][0], s_red[3][0]));
-    const float hi_lg = fmaxf(fmaxf(s_red[0][1], s_red[1][1]), fmaxf(s_red[2][1], s_red[3][1]));
+    float lo_lg = s_red[0][0], hi_lg = s_red[0][1];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) {
+        lo_lg = fminf(lo_lg, s_red[w][0]);
+        hi_lg = fmaxf(hi_lg, s_red[w][1]);
+    }
     const float M = 0.5f * (lo_lg + hi_lg);
     const bool factored = hi_lg - lo_lg <= 120.f && M >= -100.f;
 
     // ---- 3 (exact path). pair weights w_ij = sum_c q_i[c] k_j[c] 2^{LG_i[c] - LG_j[c]},
     // j on path(i); four lanes per node, CH channels each, summed across the four
-    if (!factored) {
+    if (!factored && tid < kVecThreads) {
         const uint64_t mi = pi < n ? s_mask[pi] : 0ull;
         bf16x8 qp[CH / 8];  // query channels CH*psub .. of node pi, loaded only on this path
 #pragma unroll
@@ -454,12 +478,12 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
             if (psub == 0) s_w[pi * N + j] = acc;
         }
     }
-    // query operands of node tile `wave`: 2^{LG_i[c] - off} q_i[c], split hi + lo, with
+    // query operands of node tile tw: 2^{LG_i[c] - off} q_i[c], split hi + lo, with
     // off = M on the factored path (the H_0 term is scaled back by 2^M) and 0 otherwise
     const float off = factored ? M : 0.f;
     bf16x8 ah[KT], al[KT];
     {
-        const int qi = min(16 * wave + n16, last);
+        const int qi = min(16 * tw + n16, last);
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
             const float *lgq = s_lg + qi * DK + 32 * t + 8 * g4;
@@ -475,7 +499,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
             }
         }
     }
-    // ---- 3 (factored path). S^T tiles (jt, it = wave) = B_jt . A_it^T over channels, with
+    // ---- 3 (factored path). S^T tiles (jt, it = tw) = B_jt . A_it^T over channels, with
     // B_j = k_j 2^{M - LG_j} (split hi + lo; three products), masked to ancestors. Their
     // accumulator layout (lane (n, g) holds j = 16jt + 4g + r for node i = 16it + n) is the
     // A operand of W.V over the ancestor tile pair (2p, 2p+1): contraction index 8g + e
@@ -493,7 +517,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < GPT; ++u) {
-            const int P = tid + kVecThreads * u;
+            const int P = tid + NT * u;
             const int row = P / GP, c = 4 * (P % GP);
             const b4 kk = *reinterpret_cast<const b4 *>(s_k + row * DK + c);
             const float lg[4] = {lgv[u].x, lgv[u].y, lgv[u].z, lgv[u].w};
@@ -510,12 +534,12 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
             *reinterpret_cast<b4 *>(s_bl + at) = ll;
         }
         __syncthreads();
-        const uint64_t mi = s_mask[16 * wave + n16];
+        const uint64_t mi = s_mask[16 * tw + n16];
         float w[4][4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             f32x4 st = {0.f, 0.f, 0.f, 0.f};
-            if (jt <= wave) {
+            if (jt <= tw) {
                 const int j = 16 * jt + n16;
 #pragma unroll
                 for (int t = 0; t < KT; ++t) {
@@ -529,7 +553,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int j = 16 * jt + 4 * g4 + r;
-                w[jt][r] = (jt <= wave && ((mi >> j) & 1ull)) ? st[r] : 0.f;
+                w[jt][r] = (jt <= tw && ((mi >> j) & 1ull)) ? st[r] : 0.f;
             }
         }
 #pragma unroll
@@ -561,18 +585,19 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
                 ll[e] = xl;
             }
             const int at = ((hrg * CPL + c) * 16 + hn) * 8;
-            *reinterpret_cast<bf16x8 *>(s_h0b + at) = hh;
-            *reinterpret_cast<bf16x8 *>(s_h0b + DK * CW + at) = ll;
+            *reinterpret_cast<bf16x8 *>(s_h0g + at) = hh;
+            *reinterpret_cast<bf16x8 *>(s_h0g + DK * CW + at) = ll;
         }
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-        const int P = tid + kVecThreads * u;
-        *reinterpret_cast<u32x4 *>(s_v + (P / VP) * CW + 8 * (P % VP)) = rvv[u];
+        const int P = tid + NT * u;
+        *reinterpret_cast<u32x4 *>(s_v + (P / VP) * CGW + 8 * (P % VP)) = rvv[u];
     }
     __syncthreads();
 
-    // ---- 5. H_0 term for node tile `wave`, then the intra term, then the rows
+    // ---- 5. H_0 term for node tile tw and this thread's column group, then the intra
+    // term, then the rows
     f32x4 acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -581,7 +606,7 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const int at = (((4 * t + g4) * CPL + c) * 16 + n16) * 8;
-            const bf16x8 bh = load16(s_h0b + at), bl = load16(s_h0b + DK * CW + at);
+            const bf16x8 bh = load16(s_h0g + at), bl = load16(s_h0g + DK * CW + at);
             acc[c] = mfma16_bf16(ah[t], bh, acc[c]);
             acc[c] = mfma16_bf16(ah[t], bl, acc[c]);
             acc[c] = mfma16_bf16(al[t], bh, acc[c]);
@@ -594,12 +619,12 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
         // W.V: V operand for column tile c, element e = V[32p + j(e)][CPL*n + c]
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            if (2 * p > wave) break;
+            if (2 * p > tw) break;
             bf16x8 vb[CPL];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int j = 32 * p + (e < 4 ? 4 * g4 + e : 12 + 4 * g4 + e);
-                const vvec x = *reinterpret_cast<const vvec *>(s_v + j * CW + CPL * n16);
+                const vvec x = *reinterpret_cast<const vvec *>(s_v + j * CGW + hf * CW + CPL * n16);
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) vb[c][e] = x[c];
             }
@@ -612,21 +637,22 @@ __global__ __launch_bounds__(kVecThreads) void verify_vec_kernel(
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int i = 16 * wave + 4 * g4 + r;
+        const int i = 16 * tw + 4 * g4 + r;
         if (i >= n) continue;
         uint64_t rest = factored ? 0ull : s_mask[i];
         while (rest) {
             const int j = __ffsll((unsigned long long)rest) - 1;
             rest &= rest - 1;
             const float w = s_w[i * N + j];
-            const vvec vv = *reinterpret_cast<const vvec *>(s_v + j * CW + CPL * n16);
+            const vvec vv = *reinterpret_cast<const vvec *>(s_v + j * CGW + hf * CW + CPL * n16);
 #pragma unroll
             for (int c = 0; c < CPL; ++c) acc[c][r] += w * static_cast<float>(vv[c]);
         }
         hvec o;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) o[c] = acc[c][r];
-        __builtin_nontemporal_store(o, reinterpret_cast<hvec *>(ou + ((uint32_t)i * rv + CPL * n16)));
+        __builtin_nontemporal_store(
+            o, reinterpret_cast<hvec *>(ou + ((uint32_t)i * rv + hf * CW + CPL * n16)));
     }
 }
 
@@ -654,17 +680,34 @@ static void launch_vec_shape(const bole_layer_t *layers, int nl, const int32_t *
                              int32_t *tree_status, hipStream_t stream, const VecLazy *lz) {
     constexpr int G = DV < 64 ? 1 : DV / 64;
     const unsigned U = (unsigned)d.batch * (unsigned)d.heads;
-    const dim3 grid(G == 1 ? U : ((U + 7) / 8) * 8 * G, (unsigned)nl);
     LayerTable lt = {};
     for (int l = 0; l < nl; ++l) lt.l[l] = layers[l];
+    const int mn = max_tree_nodes(d.flags);
+    const VecLazy none = {};
+    // Verify takes two column groups per workgroup when the launch is short enough for all
+    // of its one-group workgroups to be resident at once (two per CU): each workgroup's
+    // chain is then the launch's time, and the pair does its column-independent work once
+    // (workload 3: 17.8 -> 16.3 us). Longer launches keep one group per workgroup: two
+    // workgroups per CU overlap one unit's products with another's loads, which one
+    // 8-wavefront workgroup does less (8-layer stacks 2-3% slower as pairs), and so does
+    // the lazy form, whose commit rounds the pair does not shorten (0.4 us slower).
+    const unsigned slots1 = G == 1 ? U : ((U + 7) / 8) * 8 * G;
+    if constexpr (G % 2 == 0) {
+        if (!lz && (uint64_t)slots1 * (uint64_t)nl <= kVecPairMaxWorkgroups) {
+            constexpr int GS = G / 2;
+            const dim3 grid(GS == 1 ? U : ((U + 7) / 8) * 8 * GS, (unsigned)nl);
+            verify_vec_kernel<DK, DV, false, 2><<<grid, dim3(2 * kVecThreads), 0, stream>>>(
+                lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, mn, none);
+            return;
+        }
+    }
+    const dim3 grid(slots1, (unsigned)nl);
     if (lz)
-        verify_vec_kernel<DK, DV, true><<<grid, dim3(kVecThreads), 0, stream>>>(
-            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U,
-            max_tree_nodes(d.flags), *lz);
+        verify_vec_kernel<DK, DV, true, 1><<<grid, dim3(kVecThreads), 0, stream>>>(
+            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, mn, *lz);
     else
-        verify_vec_kernel<DK, DV, false><<<grid, dim3(kVecThreads), 0, stream>>>(
-            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U,
-            max_tree_nodes(d.flags), VecLazy{});
+        verify_vec_kernel<DK, DV, false, 1><<<grid, dim3(kVecThreads), 0, stream>>>(
+            lt, parent, node_offsets, tree_status, d.heads, d.total_nodes, (int)U, mn, none);
 }
 
 static hipError_t launch_vec(const bole_layer_t *layers, int nl, const int32_t *parent,
