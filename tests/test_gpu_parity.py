@@ -1086,3 +1086,50 @@ def test_fused_lazy_pairs_equal_single_units(bole):
     good = np.concatenate([np.arange(o[b], o[b + 1]) for b in range(B) if st_ref[b] == 0])
     assert rel_err_rows(outs[0].double().cpu().numpy()[good], oref[good]) <= TOL[torch.bfloat16]
     assert torch.isnan(outs[0][int(o[big]):int(o[big + 1])]).all()
+
+
+def test_packed_fused_verify_equals_sub_batches(bole):
+    """Verify without a tree budget on a stack large enough for the packed fused launch (a
+    head count divisible by 4): 150 sequences, so the slot search spans three groups of 64
+    offsets, with trees of every size up to 64 nodes, a bad parent in a large tree and a
+    last tree that runs past the node count. Bit for bit the single-layer calls on batches
+    of 50 sequences (too few units to be packed), and within tolerance of the oracle."""
+    kw = dict(batch=150, heads=16, d_k=128, d_v=64, kind="random",
+              sizes=[(37 * i) % 65 for i in range(150)])
+    wc, lc = _stack(5151, 2, **kw)
+    o = wc.node_offsets.copy()
+    B, Hh, T = wc.batch, kw["heads"], wc.total_nodes
+    sizes = np.diff(o)
+    assert (sizes > 32).sum() >= 10 and (sizes <= 32).sum() >= 10 and (sizes == 0).any()
+    parent = wc.parent.copy()
+    big = next(b for b in range(B) if sizes[b] > 40)
+    parent[o[big] + 37] = 39                      # a bad parent in a large tree
+    o[B] = T + 1                                  # the last tree ends past the last node
+    tc = dict(parent=torch.from_numpy(parent).to(dev()), offs=torch.from_numpy(o).to(dev()))
+    assert B * Hh * 2 >= 2048 and 50 * Hh < 2048 and Hh % 4 == 0
+    ys = _dev_layers(lc)
+    for y in ys:   # rows of a tree reported bad keep what they held
+        y["out"] = torch.full((T, Hh, kw["d_v"]), 5.0, dtype=torch.float32, device=dev())
+    st = torch.full((B,), -7, dtype=torch.int32, device=dev())
+    print("[case] packed fused verify: 150 x 16, 2 layers", flush=True)
+    outs = bole.bole_tree_verify_layers(ys, tc["parent"], tc["offs"], tree_status=st)
+    torch.cuda.synchronize()
+    for li, (y, out) in enumerate(zip(ys, outs)):
+        for s0 in range(0, B, 50):
+            s1 = min(s0 + 50, B)
+            r0, r1 = int(o[s0]), min(int(o[s1]), T)
+            offs = torch.from_numpy(o[s0:s1 + 1] - o[s0]).to(dev())
+            st1 = torch.full((s1 - s0,), -7, dtype=torch.int32, device=dev())
+            o1 = bole.bole_tree_verify(y["H0"][s0:s1], y["q"][r0:r1], y["k"][r0:r1],
+                                       y["v"][r0:r1], y["gate"][r0:r1], tc["parent"][r0:r1],
+                                       offs, tree_status=st1, out=torch.full_like(out[r0:r1], 5.0))
+            torch.cuda.synchronize()
+            assert torch.equal(out[r0:r1].nan_to_num(7.0), o1.nan_to_num(7.0)), (li, s0)
+            assert torch.equal(st[s0:s1], st1), (li, s0)
+        oref, st_ref = oracle.verify_serial(lc[li].H0, lc[li].q, lc[li].k, lc[li].v,
+                                            lc[li].gate, parent, o, False)
+        assert st.cpu().tolist() == st_ref.tolist()
+        assert st_ref[big] == 2 and st_ref[B - 1] == 1
+        good = np.concatenate([np.arange(o[b], o[b + 1]) for b in range(B) if st_ref[b] == 0])
+        assert rel_err_rows(out.double().cpu().numpy()[good], oref[good]) <= TOL[torch.bfloat16]
+        assert (out[int(o[B - 1]):] == 5.0).all()

@@ -71,7 +71,61 @@ constexpr int ksplit_lazy_smem_elems();
 template <int DK, int DV, bool LAZY>
 __device__ __forceinline__ void ksplit_body(const bole_layer_t, const int32_t *, const int32_t *,
                                             int32_t *, int, int, int, int, char *, int, int,
-                                            const LazyCommit &, __bf16 *);
+                                            const LazyCommit &, __bf16 *, const TreeRange *);
+
+// Packed fused launch (FUSED, NW = 4, a head count divisible by 4): wavefront slots are
+// dealt to the units in sequence order, two to each unit whose tree has 33..64 nodes and
+// one to every other unit, four slots per workgroup. Each sequence's units take a multiple
+// of four slots, so a workgroup holds units of one sequence only: four one-wavefront units
+// or two row-split units. Every wavefront finds its slot's sequence from the tree offsets
+// of all sequences (a running count of large trees, one ballot per 64 sequences); the
+// grid is sized for the case of every tree large, and workgroups past the last slot exit.
+struct PackSlot {
+    int b;          // sequence, -1 past the last slot
+    int r;          // slot within the sequence's slots
+    bool large;     // a tree of 33..64 nodes (two slots per unit)
+    TreeRange tr;   // the sequence's tree range, as tree_range() gives it
+};
+
+__device__ __forceinline__ PackSlot pack_locate(const int32_t *__restrict__ node_offsets, int B,
+                                                int H, int T, int max_n, int s) {
+    const int lane = lane_id();
+    int base = 0;   // slots of the sequences before this chunk of 64
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int b = c0 + lane;
+        int lo = 0, hi = 0;
+        if (b < B) {
+            lo = node_offsets[b];
+            hi = node_offsets[b + 1];
+        }
+        const bool bad = lo < 0 || hi < lo || hi > T || hi - lo > max_n;
+        const uint64_t lm = __ballot(b < B && !bad && hi - lo > 32);
+        // first slot of sequence b: H per sequence before it, H more per large one
+        const int before = (int)__builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(lm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)lm, 0u));
+        const int start = base + H * (lane + before);
+        const int total = H * (min(64, B - c0) + (int)__popcll(lm));
+        if (s < base + total) {
+            // the sequences starting at or before s are a prefix of the chunk's lanes
+            const int bl = (int)__popcll(__ballot(b < B && start <= s)) - 1;
+            PackSlot p;
+            p.b = c0 + bl;
+            p.r = s - __builtin_amdgcn_readlane(start, bl);
+            p.large = (lm >> bl) & 1;
+            p.tr.lo = __builtin_amdgcn_readlane(lo, bl);
+            p.tr.n = __builtin_amdgcn_readlane(hi, bl) - p.tr.lo;
+            p.tr.status = __builtin_amdgcn_readlane(bad ? (int)BOLE_TREE_BAD_SIZE : (int)BOLE_TREE_OK, bl);
+            return p;
+        }
+        base += total;
+    }
+    PackSlot p;
+    p.b = -1;
+    p.r = 0;
+    p.large = false;
+    p.tr = {0, 0, BOLE_TREE_OK};
+    return p;
+}
 
 // FUSED: every tree size in one launch, for a caller without a budget of 32 nodes (with
 // LAZY, each body also commits the units whose trees it verifies). Each
@@ -80,13 +134,14 @@ __device__ __forceinline__ void ksplit_body(const bole_layer_t, const int32_t *,
 // body on the first (the second exits); both leave at once, and wave-uniformly, for the
 // trees they do not take. With NW = 2 a workgroup of four wavefronts takes heads 2j and
 // 2j + 1 of one sequence (so one tree, and the row-split barriers of both units match).
+// FUSED with NW = 4: the packed launch (above), 256 threads.
 // NW > 1 (one 64-column group per unit, not FUSED): a workgroup of NW wavefronts takes NW
 // consecutive units, heads NW j .. NW j + NW - 1 of a sequence, one per wavefront, each with
 // its own LDS. A node's q, k, v and out rows of neighbouring heads are adjacent in the
 // token-major layout, so the group's row pieces form runs NW times as long, requested
 // together by one CU.
 template <int DK, int DV, bool LAZY, bool FUSED, int NW>
-__global__ __launch_bounds__(FUSED ? 128 * NW : 64 * NW, 2) void verify_mfma_tree_kernel(
+__global__ __launch_bounds__(FUSED ? (NW == 4 ? 256 : 128 * NW) : 64 * NW, 2) void verify_mfma_tree_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
     int U, int max_n, LazyCommit lc) {
@@ -102,34 +157,51 @@ __global__ __launch_bounds__(FUSED ? 128 * NW : 64 * NW, 2) void verify_mfma_tre
     typedef float hvec __attribute__((ext_vector_type(CPL)));
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
     static_assert(NW == 1 || G == 1, "unit groups: one column group per unit");
-    static_assert(!FUSED || NW <= 2, "fused unit groups: at most two units");
+    constexpr bool PACK = FUSED && NW == 4;
+    static_assert(!FUSED || NW <= 2 || PACK, "fused unit groups: two units, or packed");
+    static_assert(!PACK || G == 1, "packed launch: one column group per unit");
     // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR); V rows of the group's columns,
     // row j at [CW j]; lazy commit: k rows and v rows (group columns) of up to kLazyStage
     // path nodes. FUSED: K and V in the buffer the row-split body uses.
     constexpr int kLazyStage = LAZY ? 8 : 1;
     static_assert(NN * PPR * 16 + NN * CW * 2 <= ksplit_smem_bytes<DK, DV>(), "fused LDS region");
-    constexpr int kFusedBytes = FUSED ? NW * ksplit_smem_bytes<DK, DV>() : 16;
+    // PACK: two row-split regions, or four one-wavefront regions of half the size
+    static_assert(2 * (NN * PPR * 16 + NN * CW * 2) == ksplit_smem_bytes<DK, DV>(), "packed regions");
+    constexpr int kFusedBytes = FUSED ? (PACK ? 2 : NW) * ksplit_smem_bytes<DK, DV>() : 16;
     __shared__ __align__(16) char s_fused[kFusedBytes];
     __shared__ bf16x8 s_k_own[FUSED ? 1 : NW * NN * PPR];
     __shared__ __bf16 s_v_own[FUSED ? 8 : NW * NN * CW];
     __shared__ __bf16 s_pk_all[NW * kLazyStage * DK], s_pv_all[NW * kLazyStage * CW];
     // FUSED and LAZY: the row-split body's path staging, one region per wavefront
     __shared__ __align__(16) __bf16
-        s_lzk[FUSED && LAZY ? 2 * NW * ksplit_lazy_smem_elems<DK, DV>() : 8];
-    // this wavefront's unit of the group (FUSED: two wavefronts per unit)
-    const int wv = NW > 1 ? (int)(threadIdx.x >> (FUSED ? 7 : 6)) : 0;
-    char *const s_unit = s_fused + (FUSED ? wv * ksplit_smem_bytes<DK, DV>() : 0);
+        s_lzk[FUSED && LAZY ? (PACK ? 4 : 2 * NW) * ksplit_lazy_smem_elems<DK, DV>() : 8];
+    // this wavefront's unit of the group (FUSED, not packed: two wavefronts per unit)
+    const int wv = NW > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> (FUSED && !PACK ? 7 : 6))) : 0;
+    char *const s_unit = s_fused + (PACK ? wv * (ksplit_smem_bytes<DK, DV>() / 2)
+                                        : FUSED ? wv * ksplit_smem_bytes<DK, DV>() : 0);
     bf16x8 *const s_k = FUSED ? reinterpret_cast<bf16x8 *>(s_unit) : s_k_own + wv * NN * PPR;
     __bf16 *const s_v = FUSED ? reinterpret_cast<__bf16 *>(s_unit + NN * PPR * 16)
                               : s_v_own + wv * NN * CW;
     __bf16 *const s_pk = s_pk_all + wv * kLazyStage * DK;
     __bf16 *const s_pv = s_pv_all + wv * kLazyStage * CW;
     const bole_layer_t &ly = lt.l[blockIdx.y];
-    if constexpr (FUSED) {
+    PackSlot ps = {0, 0, false, {0, 0, BOLE_TREE_OK}};
+    if constexpr (PACK) {
+        ps = pack_locate(node_offsets, U / H, H, T, max_n, 4 * (int)blockIdx.x + wv);
+        if (ps.b < 0) return;  // past the last slot: the whole workgroup
+        if (ps.large) {
+            ksplit_body<DK, DV, LAZY>(ly, parent, node_offsets, tree_status, H, T, U, max_n,
+                                      s_fused + (wv >> 1) * ksplit_smem_bytes<DK, DV>(),
+                                      ps.b * H + (ps.r >> 1), ps.r & 1, lc,
+                                      LAZY ? s_lzk + wv * ksplit_lazy_smem_elems<DK, DV>() : nullptr,
+                                      &ps.tr);
+            return;
+        }
+    } else if constexpr (FUSED) {
         ksplit_body<DK, DV, LAZY>(ly, parent, node_offsets, tree_status, H, T, U, max_n, s_unit,
                                   NW * (int)blockIdx.x + wv, (int)((threadIdx.x >> 6) & 1), lc,
                                   LAZY ? s_lzk + (threadIdx.x >> 6) * ksplit_lazy_smem_elems<DK, DV>()
-                                       : nullptr);
+                                       : nullptr, nullptr);
         if (threadIdx.x & 64) return;  // the second wavefront of each unit
     }
     float *const H0 = ly.H0;                // written only by the lazy commit
@@ -142,7 +214,10 @@ __global__ __launch_bounds__(FUSED ? 128 * NW : 64 * NW, 2) void verify_mfma_tre
     const int lane = lane_id();
     const int n16 = lane & 15, g = lane >> 4;
     int unit, cg;
-    if (G == 1) {
+    if (PACK) {
+        unit = ps.b * H + ps.r;
+        cg = 0;
+    } else if (G == 1) {
         unit = NW * (int)blockIdx.x + wv;
         if (unit >= U) return;
         cg = 0;
@@ -157,7 +232,7 @@ __global__ __launch_bounds__(FUSED ? 128 * NW : 64 * NW, 2) void verify_mfma_tre
     const bool first = blockIdx.y == 0 && h == 0 && cg == 0;  // writes the per-tree outputs
     const bool writer = tree_status != nullptr && first && lane == 0;
 
-    const TreeRange tr = tree_range(node_offsets, b, T, max_n);
+    const TreeRange tr = PACK ? ps.tr : tree_range(node_offsets, b, T, max_n);
     bool do_verify = true;
     if (tr.status != BOLE_TREE_OK) {
         if (writer) tree_status[b] = tr.status;
@@ -508,12 +583,14 @@ constexpr int ksplit_lazy_smem_elems() {
     return 8 * (DK / 2 + (DV < 64 ? DV : 64));
 }
 
-// Both wavefronts of a 128-thread workgroup; smem holds ksplit_smem_bytes bytes.
+// Both wavefronts of a 128-thread workgroup (or a pair of a packed one); smem holds
+// ksplit_smem_bytes bytes. `known`: the tree range of the unit's sequence, else read here.
 template <int DK, int DV, bool LAZY>
 __device__ __forceinline__ void ksplit_body(
     const bole_layer_t ly, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
-    int U, int max_n, char *smem, int unit_g1, int w_in, const LazyCommit &lc, __bf16 *lsmem) {
+    int U, int max_n, char *smem, int unit_g1, int w_in, const LazyCommit &lc, __bf16 *lsmem,
+    const TreeRange *known) {
     constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
     constexpr int CPL = CW / 16;            // columns per lane: 4 or 2
     constexpr int G = DV / CW;              // column groups per unit
@@ -557,7 +634,7 @@ __device__ __forceinline__ void ksplit_body(
     const bool first = blockIdx.y == 0 && h == 0 && cg == 0;
     const bool writer = tree_status != nullptr && first && w == 0 && lane_id() == 0;
 
-    const TreeRange tr = tree_range(node_offsets, b, T, max_n);
+    const TreeRange tr = known ? *known : tree_range(node_offsets, b, T, max_n);
     if (tr.status != BOLE_TREE_OK || tr.n <= 32) return;
     const int n = tr.n;
     const int lo = tr.lo, last = n - 1;
@@ -947,6 +1024,8 @@ bool verify_mfma_applies(const bole_dims_t &d, const bole_layer_t *layers, int n
 constexpr uint64_t kGroupMinUnits = 2048;
 constexpr int kVerifyGroup = 2;
 constexpr int kLazyGroup = 4;
+// Sequences up to which the fused launch is packed (every wavefront reads all tree offsets)
+constexpr int kPackMaxSeq = 1024;
 
 template <int DK, int DV>
 static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *parent,
@@ -967,10 +1046,16 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
     for (int l = 0; l < nl; ++l) lt.l[l] = layers[l];
     const LazyCommit none = {};
     const int H = d.heads, T = d.total_nodes;
+    // the packed fused launch: slots for every unit taking two, so half a workgroup per unit
+    const bool pack = group && G == 1 && H % 4 == 0 && d.batch <= kPackMaxSeq;
+    const dim3 pgrid(U / 2, (unsigned)nl);
     if (lazy && max_n > 32) {
         // every tree size in one launch, as the fused verify below, each body committing
         // the units whose trees it verifies
-        if (group && H % 2 == 0)
+        if (pack)
+            verify_mfma_tree_kernel<DK, DV, true, true, G == 1 ? 4 : 1><<<pgrid, dim3(256), 0, stream>>>(
+                lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
+        else if (group && H % 2 == 0)
             verify_mfma_tree_kernel<DK, DV, true, true, G == 1 ? 2 : 1><<<
                 dim3(G == 1 ? (U + 1) / 2 : grid.x, (unsigned)nl), dim3(G == 1 ? 256 : 128), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
@@ -986,7 +1071,10 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
     } else if (max_n > 32) {
         // two units per workgroup only when they always share a tree (an even head count)
-        if (group && H % 2 == 0)
+        if (pack)
+            verify_mfma_tree_kernel<DK, DV, false, true, G == 1 ? 4 : 1><<<pgrid, dim3(256), 0, stream>>>(
+                lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
+        else if (group && H % 2 == 0)
             verify_mfma_tree_kernel<DK, DV, false, true, G == 1 ? 2 : 1><<<
                 dim3(G == 1 ? (U + 1) / 2 : grid.x, (unsigned)nl), dim3(G == 1 ? 256 : 128), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
