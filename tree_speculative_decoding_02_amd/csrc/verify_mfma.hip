@@ -73,11 +73,11 @@ __device__ __forceinline__ void ksplit_body(const bole_layer_t, const int32_t *,
                                             int32_t *, int, int, int, int, char *, int, int,
                                             const LazyCommit &, __bf16 *, const TreeRange *);
 
-// Packed fused launch (FUSED, NW = 4, a head count divisible by 4): wavefront slots are
-// dealt to the units in sequence order, two to each unit whose tree has 33..64 nodes and
-// one to every other unit, four slots per workgroup. Each sequence's units take a multiple
-// of four slots, so a workgroup holds units of one sequence only: four one-wavefront units
-// or two row-split units. Every wavefront finds its slot's sequence from the tree offsets
+// Packed fused launch (FUSED, NW = 4 or 8 slots, a head count divisible by NW): wavefront
+// slots are dealt to the units in sequence order, two to each unit whose tree has 33..64
+// nodes and one to every other unit, NW slots per workgroup. Each sequence's units take a
+// multiple of NW slots, so a workgroup holds units of one sequence only: NW one-wavefront
+// units or NW / 2 row-split units. Every wavefront finds its slot's sequence from the tree offsets
 // of all sequences (a running count of large trees, one ballot per 64 sequences); the
 // grid is sized for the case of every tree large, and workgroups past the last slot exit.
 struct PackSlot {
@@ -134,14 +134,14 @@ __device__ __forceinline__ PackSlot pack_locate(const int32_t *__restrict__ node
 // body on the first (the second exits); both leave at once, and wave-uniformly, for the
 // trees they do not take. With NW = 2 a workgroup of four wavefronts takes heads 2j and
 // 2j + 1 of one sequence (so one tree, and the row-split barriers of both units match).
-// FUSED with NW = 4: the packed launch (above), 256 threads.
+// FUSED with NW = 4 or 8: the packed launch (above), 64 NW threads.
 // NW > 1 (one 64-column group per unit, not FUSED): a workgroup of NW wavefronts takes NW
 // consecutive units, heads NW j .. NW j + NW - 1 of a sequence, one per wavefront, each with
 // its own LDS. A node's q, k, v and out rows of neighbouring heads are adjacent in the
 // token-major layout, so the group's row pieces form runs NW times as long, requested
 // together by one CU.
 template <int DK, int DV, bool LAZY, bool FUSED, int NW>
-__global__ __launch_bounds__(FUSED ? (NW == 4 ? 256 : 128 * NW) : 64 * NW, 2) void verify_mfma_tree_kernel(
+__global__ __launch_bounds__(FUSED && NW <= 2 ? 128 * NW : 64 * NW, 2) void verify_mfma_tree_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
     int U, int max_n, LazyCommit lc) {
@@ -157,24 +157,24 @@ __global__ __launch_bounds__(FUSED ? (NW == 4 ? 256 : 128 * NW) : 64 * NW, 2) vo
     typedef float hvec __attribute__((ext_vector_type(CPL)));
     typedef __bf16 vvec __attribute__((ext_vector_type(CPL)));
     static_assert(NW == 1 || G == 1, "unit groups: one column group per unit");
-    constexpr bool PACK = FUSED && NW == 4;
-    static_assert(!FUSED || NW <= 2 || PACK, "fused unit groups: two units, or packed");
+    constexpr bool PACK = FUSED && NW >= 4;
+    static_assert(!FUSED || NW <= 2 || NW == 4 || NW == 8, "fused unit groups: two units, or packed");
     static_assert(!PACK || G == 1, "packed launch: one column group per unit");
     // K rows: piece p of row j at slot j*PPR + (p ^ j%PPR); V rows of the group's columns,
     // row j at [CW j]; lazy commit: k rows and v rows (group columns) of up to kLazyStage
     // path nodes. FUSED: K and V in the buffer the row-split body uses.
     constexpr int kLazyStage = LAZY ? 8 : 1;
     static_assert(NN * PPR * 16 + NN * CW * 2 <= ksplit_smem_bytes<DK, DV>(), "fused LDS region");
-    // PACK: two row-split regions, or four one-wavefront regions of half the size
+    // PACK: NW / 2 row-split regions, or NW one-wavefront regions of half the size
     static_assert(2 * (NN * PPR * 16 + NN * CW * 2) == ksplit_smem_bytes<DK, DV>(), "packed regions");
-    constexpr int kFusedBytes = FUSED ? (PACK ? 2 : NW) * ksplit_smem_bytes<DK, DV>() : 16;
+    constexpr int kFusedBytes = FUSED ? (PACK ? NW / 2 : NW) * ksplit_smem_bytes<DK, DV>() : 16;
     __shared__ __align__(16) char s_fused[kFusedBytes];
     __shared__ bf16x8 s_k_own[FUSED ? 1 : NW * NN * PPR];
     __shared__ __bf16 s_v_own[FUSED ? 8 : NW * NN * CW];
     __shared__ __bf16 s_pk_all[NW * kLazyStage * DK], s_pv_all[NW * kLazyStage * CW];
     // FUSED and LAZY: the row-split body's path staging, one region per wavefront
     __shared__ __align__(16) __bf16
-        s_lzk[FUSED && LAZY ? (PACK ? 4 : 2 * NW) * ksplit_lazy_smem_elems<DK, DV>() : 8];
+        s_lzk[FUSED && LAZY ? (PACK ? NW : 2 * NW) * ksplit_lazy_smem_elems<DK, DV>() : 8];
     // this wavefront's unit of the group (FUSED, not packed: two wavefronts per unit)
     const int wv = NW > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> (FUSED && !PACK ? 7 : 6))) : 0;
     char *const s_unit = s_fused + (PACK ? wv * (ksplit_smem_bytes<DK, DV>() / 2)
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(FUSED ? (NW == 4 ? 256 : 128 * NW) : 64 * NW, 2) vo
     const bole_layer_t &ly = lt.l[blockIdx.y];
     PackSlot ps = {0, 0, false, {0, 0, BOLE_TREE_OK}};
     if constexpr (PACK) {
-        ps = pack_locate(node_offsets, U / H, H, T, max_n, 4 * (int)blockIdx.x + wv);
+        ps = pack_locate(node_offsets, U / H, H, T, max_n, NW * (int)blockIdx.x + wv);
         if (ps.b < 0) return;  // past the last slot: the whole workgroup
         if (ps.large) {
             ksplit_body<DK, DV, LAZY>(ly, parent, node_offsets, tree_status, H, T, U, max_n,
@@ -1024,8 +1024,10 @@ bool verify_mfma_applies(const bole_dims_t &d, const bole_layer_t *layers, int n
 constexpr uint64_t kGroupMinUnits = 2048;
 constexpr int kVerifyGroup = 2;
 constexpr int kLazyGroup = 4;
-// Sequences up to which the fused launch is packed (every wavefront reads all tree offsets)
+// Sequences up to which the fused launch is packed (every wavefront reads all tree offsets),
+// and its wavefront slots per workgroup (eight, one workgroup per CU, measured slower)
 constexpr int kPackMaxSeq = 1024;
+constexpr int kPackSlots = 4;
 
 template <int DK, int DV>
 static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *parent,
@@ -1047,13 +1049,13 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
     const LazyCommit none = {};
     const int H = d.heads, T = d.total_nodes;
     // the packed fused launch: slots for every unit taking two, so half a workgroup per unit
-    const bool pack = group && G == 1 && H % 4 == 0 && d.batch <= kPackMaxSeq;
-    const dim3 pgrid(U / 2, (unsigned)nl);
+    const bool pack = group && G == 1 && H % kPackSlots == 0 && d.batch <= kPackMaxSeq;
+    const dim3 pgrid(2 * U / kPackSlots, (unsigned)nl), pblock(64 * kPackSlots);
     if (lazy && max_n > 32) {
         // every tree size in one launch, as the fused verify below, each body committing
         // the units whose trees it verifies
         if (pack)
-            verify_mfma_tree_kernel<DK, DV, true, true, G == 1 ? 4 : 1><<<pgrid, dim3(256), 0, stream>>>(
+            verify_mfma_tree_kernel<DK, DV, true, true, G == 1 ? kPackSlots : 1><<<pgrid, pblock, 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
         else if (group && H % 2 == 0)
             verify_mfma_tree_kernel<DK, DV, true, true, G == 1 ? 2 : 1><<<
@@ -1072,7 +1074,7 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
     } else if (max_n > 32) {
         // two units per workgroup only when they always share a tree (an even head count)
         if (pack)
-            verify_mfma_tree_kernel<DK, DV, false, true, G == 1 ? 4 : 1><<<pgrid, dim3(256), 0, stream>>>(
+            verify_mfma_tree_kernel<DK, DV, false, true, G == 1 ? kPackSlots : 1><<<pgrid, pblock, 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
         else if (group && H % 2 == 0)
             verify_mfma_tree_kernel<DK, DV, false, true, G == 1 ? 2 : 1><<<
