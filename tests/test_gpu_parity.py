@@ -999,13 +999,23 @@ def test_paired_units_equal_single_units(bole, name, n_layers, kw):
     assert rel_err_rows(outs[0].double().cpu().numpy(), oref) <= TOL[torch.bfloat16]
 
 
-def test_fused_pairs_equal_single_units(bole):
+FUSED_GROUP_CASES = [
+    # (name, make_random kwargs): two layers hold >= 2048 units, one layer fewer. A head
+    # count divisible by 4 takes the packed launch (four small-tree or two large-tree units
+    # per workgroup); 2 mod 4 takes two units (neighbouring heads) per workgroup
+    ("packed", dict(batch=33, heads=32, d_k=128, d_v=64, kind="random")),
+    ("packed_dk64_dv32", dict(batch=33, heads=32, d_k=64, d_v=32, kind="random")),
+    ("pairs_heads_2_mod_4", dict(batch=31, heads=34, d_k=128, d_v=64, kind="random")),
+]
+
+
+@pytest.mark.parametrize("name,kw", FUSED_GROUP_CASES, ids=[c[0] for c in FUSED_GROUP_CASES])
+def test_fused_pairs_equal_single_units(bole, name, kw):
     """Verify without a tree budget (every size up to 64 nodes in one launch) on a stack
-    large enough to take two units per workgroup (an even head count): bit for bit the
+    large enough to group units per workgroup (an even head count): bit for bit the
     single-layer calls, which take one unit per workgroup, and within tolerance of the
     oracle on the first layer; bad trees among them keep their statuses."""
-    kw = dict(batch=33, heads=32, d_k=128, d_v=64, kind="random")
-    wc, lc = _stack(4242, 2, **kw)
+    wc, lc = _stack(4242 + zlib.crc32(name.encode()) % 1000, 2, **kw)
     parent = wc.parent.copy()
     o = wc.node_offsets
     big = next(b for b in range(wc.batch) if o[b + 1] - o[b] > 40)
@@ -1014,7 +1024,7 @@ def test_fused_pairs_equal_single_units(bole):
     tc["parent"] = torch.from_numpy(parent).to(dev())
     assert wc.batch * kw["heads"] * 2 >= 2048 and wc.batch * kw["heads"] < 2048
     status = lambda: torch.full((wc.batch,), -7, dtype=torch.int32, device=dev())
-    print("[case] fused pairs: verify stack", flush=True)
+    print(f"[case] fused groups {name}: verify stack", flush=True)
     ys = _dev_layers(lc)
     st_s = status()
     outs = bole.bole_tree_verify_layers(ys, tc["parent"], tc["offs"], tree_status=st_s)
@@ -1033,15 +1043,16 @@ def test_fused_pairs_equal_single_units(bole):
     assert torch.isnan(bad_rows).all()
 
 
-def test_fused_lazy_pairs_equal_single_units(bole):
-    """The lazy stack without a tree budget on a stack large enough to take two units per
+@pytest.mark.parametrize("name,kw", FUSED_GROUP_CASES, ids=[c[0] for c in FUSED_GROUP_CASES])
+def test_fused_lazy_pairs_equal_single_units(bole, name, kw):
+    """The lazy stack without a tree budget on a stack large enough to group units per
     workgroup (an even head count): every tree size up to 64 nodes in one fused launch,
     each body committing the units it verifies. Bit for bit the single-layer calls, which
     take one unit per workgroup; within tolerance of the oracle on the first layer; a bad
     previous path and a bad current tree keep their statuses."""
-    kw = dict(batch=33, heads=32, d_k=128, d_v=64, kind="random")
-    wp, lp = _stack(4343, 2, **kw)
-    wc, lc = _stack(4344, 2, **kw)
+    seed = 4343 + zlib.crc32(name.encode()) % 1000
+    wp, lp = _stack(seed, 2, **kw)
+    wc, lc = _stack(seed + 1, 2, **kw)
     o = wc.node_offsets
     parent = wc.parent.copy()
     big = next(b for b in range(wc.batch) if o[b + 1] - o[b] > 40)
@@ -1055,7 +1066,7 @@ def test_fused_lazy_pairs_equal_single_units(bole):
     assert wc.batch * kw["heads"] * 2 >= 2048 and wc.batch * kw["heads"] < 2048
     B = wc.batch
     status = lambda: torch.full((B,), -7, dtype=torch.int32, device=dev())
-    print("[case] fused lazy pairs: lazy stack", flush=True)
+    print(f"[case] fused lazy groups {name}: lazy stack", flush=True)
     ys = _dev_layers(lc, lp)
     H1 = [y["H0"].clone() for y in ys]
     pst_s, st_s = status(), status()
