@@ -503,6 +503,57 @@ def time_rotated(fs, stream, reps=20, warm=2):
     return float(np.median([a.elapsed_time(b) * 1e3 / len(fs) for a, b in evs]))
 
 
+def probe_lib():
+    """The memory-only reference kernels (libbole_probe.so, built with the library)."""
+    import ctypes
+    import os
+
+    from tree_speculative_decoding_02_amd import bole
+    path = os.path.join(os.path.dirname(bole.LIB_PATH), "libbole_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    common = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 5
+    lib.probe_verify_traffic_scalar.argtypes = common + [ctypes.c_int, ctypes.c_void_p]
+    lib.probe_verify_traffic_vector.argtypes = common + [ctypes.c_void_p]
+    return lib
+
+
+def traffic_reference(lib, wl, sets, stream, verify_us, nbytes, reps):
+    """A memory-only launch that moves exactly the verify's bytes, in the same pieces, on
+    the same cold input sets: the time this access pattern takes by itself. Scalar gates:
+    the best of 1, 2 and 4 units per workgroup. None for shapes it does not take."""
+    import ctypes
+
+    import torch
+    vec = bool(wl.vector_gate)
+    if wl.layers[0].q.dtype != torch.bfloat16 or wl.d_k != 128 or wl.d_v != (128 if vec else 64):
+        return None
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(stream.cuda_stream)
+
+    def launch(x, nu):
+        args = (P(x["H0"]), P(x["q"]), P(x["k"]), P(x["v"]), P(x["gate"]), P(x["out"]),
+                P(x["offs"]), wl.batch, wl.heads, wl.d_k, wl.d_v, wl.total_nodes)
+        rc = (lib.probe_verify_traffic_vector(*args, st) if vec
+              else lib.probe_verify_traffic_scalar(*args, nu, st))
+        if rc != 0:
+            raise RuntimeError(f"traffic probe failed: {rc}")
+
+    best = None
+    for nu in ((1,) if vec else (1, 2, 4)):
+        us = time_rotated([lambda x=x: launch(x, nu) for x in sets], stream, reps)
+        if best is None or us < best[0]:
+            best = (us, nu)
+    us, nu = best
+    return {"median_us": us, "GB_s": nbytes / (us * 1e3),
+            "frac_hbm_peak": nbytes / (us * 1e3) / HBM_PEAK_GBS,
+            "verify_rate_of_reference": us / verify_us,
+            "units_per_workgroup": nu if not vec else 1,
+            "what": "memory-only kernel moving the verify's bytes in the same row pieces "
+                    "(no arithmetic), the same cold input sets"}
+
+
 def config_sweep(dev, reps=20, configs=(1, 2, 3, 4, 5)):
     """Verify and commit on each workload, one layer. Each launch kind cycles through
     copies of the whole input set (sweep_sets: at least 512 MB per cycle), so every launch
@@ -515,6 +566,7 @@ def config_sweep(dev, reps=20, configs=(1, 2, 3, 4, 5)):
     import workloads as W
     from tree_speculative_decoding_02_amd import bole
     stream = torch.cuda.current_stream()
+    plib = probe_lib()
     names = {1: "tiny_fp32", 2: "mamba2_scalar", 3: "gla_vector", 4: "ragged_large_batch",
              5: "hybrid_stack_one_layer"}
     for cid in configs:
@@ -558,6 +610,10 @@ def config_sweep(dev, reps=20, configs=(1, 2, 3, 4, 5)):
             if name.startswith("verify"):
                 # draft nodes verified per second, every head of the layer
                 rec[name]["nodes_per_s"] = wl.total_nodes / (us * 1e-6)
+        ref = traffic_reference(plib, wl, sets, stream, rec["verify"]["median_us"],
+                                nbytes["verify"], reps)
+        if ref is not None:
+            rec["verify_traffic_reference"] = ref
         print(json.dumps(rec), flush=True)
         del sets, launches
     if 3 in configs:

@@ -1,6 +1,7 @@
 """Build step for libbole.so: compiles the HIP sources in csrc/ for gfx950 with hipcc
 and links them into a shared library next to this file (in-tree, so it ships with the
-repository snapshot)."""
+repository snapshot). Also builds libbole_probe.so, the benchmark's memory-only reference
+kernels (not part of the library)."""
 import concurrent.futures
 import os
 import shutil
@@ -11,6 +12,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "bole")
 LIB = os.path.join(HERE, "libbole.so")
+PROBE_LIB = os.path.join(HERE, "libbole_probe.so")
+PROBE_SOURCES = ["pattern_probe.hip"]
 SOURCES = ["bole_api.hip", "topology.hip", "validate.hip", "verify_generic.hip", "verify_mfma.hip", "verify_vec.hip",
            "verify_naive.hip", "commit.hip", "tree_build.hip",
            "tree_accept.hip"]
@@ -43,18 +46,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libbole.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
            "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libbole.so and libbole_probe.so; returns the
+    path of libbole.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

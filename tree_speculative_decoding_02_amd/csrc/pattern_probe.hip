@@ -1,0 +1,214 @@
+// Memory-only reference kernels for the benchmark: each moves exactly the bytes of one
+// tree verify (the closed form of the Bole page, section "Tree-structured verification"),
+// in the same pieces and with the same workgroup shape, and computes nothing. The time of
+// such a launch is what this access pattern costs on its own; the verify kernels are
+// measured against it. Not part of the library's API (a separate shared object that only
+// the benchmark loads).
+//
+// Scalar gates (d_k = 128, d_v = 64): per unit (sequence, head) the 32 KB H_0 slice, the
+// tree's q and k rows (256-byte pieces, rows H * 256 bytes apart), v rows (128 bytes) and
+// gate scalars are read, then the out rows (256 bytes) written; 128 threads per unit, NU
+// units (neighbouring heads) per workgroup.
+// Vector gates (d_k = d_v = 128): per unit the 64 KB H_0 slice, the tree's gate rows
+// (512-byte pieces), k, q and v rows (256 bytes) are read and the out rows (512 bytes)
+// written; one 512-thread workgroup per unit.
+//
+// Every load is issued before the first is used; the values are folded into one register
+// and stored as the output rows, so no load can be dropped.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#define PROBE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Tree {
+    int lo, n;
+};
+
+// the sequence's tree, or n = 0 when its offsets are not a tree of 1..64 nodes in [0, T)
+__device__ __forceinline__ Tree tree_of(const int32_t *offs, int b, int T) {
+    const int lo = offs[b], hi = offs[b + 1];
+    const bool ok = lo >= 0 && hi > lo && hi <= T && hi - lo <= 64;
+    return Tree{lo, ok ? hi - lo : 0};
+}
+
+template <int NU>
+__global__ __launch_bounds__(128 * NU) void scalar_traffic(const float *__restrict__ H0,
+                                                           const uint16_t *__restrict__ q,
+                                                           const uint16_t *__restrict__ k,
+                                                           const uint16_t *__restrict__ v,
+                                                           const float *__restrict__ gate,
+                                                           float *__restrict__ out,
+                                                           const int32_t *__restrict__ offs,
+                                                           int H, int U, int T) {
+    constexpr int DK = 128, DV = 64;
+    const int tid = threadIdx.x & 127;
+    const int unit = NU * (int)blockIdx.x + (int)(threadIdx.x >> 7);
+    if (unit >= U) return;
+    const int b = unit / H, h = unit - b * H;
+    const Tree tr = tree_of(offs, b, T);
+    if (tr.n == 0) return;
+    const int n = tr.n;
+    const uint32_t rq = (uint32_t)H * DK, rv = (uint32_t)H * DV;
+    const uint16_t *qu = q + (size_t)tr.lo * rq + (size_t)h * DK;
+    const uint16_t *ku = k + (size_t)tr.lo * rq + (size_t)h * DK;
+    const uint16_t *vu = v + (size_t)tr.lo * rv + (size_t)h * DV;
+    const float *hu = H0 + (size_t)unit * DK * DV;
+    u32x4 r[37];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)  // H_0: 2048 pieces of 16 bytes
+        r[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hu + 4 * (tid + 128 * u)));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // q and k: 16 pieces per row, the tree's rows only
+        const int p = tid + 128 * u;
+        r[16 + u] = u32x4{0u, 0u, 0u, 0u};
+        r[24 + u] = u32x4{0u, 0u, 0u, 0u};
+        if (p / 16 < n) {
+            r[16 + u] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(qu + (uint32_t)(p / 16) * rq + 8 * (p % 16)));
+            r[24 + u] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(ku + (uint32_t)(p / 16) * rq + 8 * (p % 16)));
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // v: 8 pieces per row
+        const int p = tid + 128 * u;
+        r[32 + u] = u32x4{0u, 0u, 0u, 0u};
+        if (p / 8 < n)
+            r[32 + u] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(vu + (uint32_t)(p / 8) * rv + 8 * (p % 8)));
+    }
+    const float gv = tid < n ? gate[(size_t)(tr.lo + tid) * H + h] : 0.f;
+    r[36] = u32x4{__float_as_uint(gv), 0u, 0u, 0u};
+    u32x4 acc = r[0];
+#pragma unroll
+    for (int u = 1; u < 37; ++u) acc ^= r[u];
+    float *ou = out + (size_t)tr.lo * rv + (size_t)h * DV;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // out: 16 pieces per row
+        const int p = tid + 128 * u;
+        if (p / 16 < n)
+            __builtin_nontemporal_store(
+                acc, reinterpret_cast<u32x4 *>(ou + (uint32_t)(p / 16) * rv + 4 * (p % 16)));
+    }
+}
+
+__global__ __launch_bounds__(512) void vector_traffic(const float *__restrict__ H0,
+                                                      const uint16_t *__restrict__ q,
+                                                      const uint16_t *__restrict__ k,
+                                                      const uint16_t *__restrict__ v,
+                                                      const float *__restrict__ gate,
+                                                      float *__restrict__ out,
+                                                      const int32_t *__restrict__ offs, int H,
+                                                      int T) {
+    constexpr int DK = 128, DV = 128, NT = 512;
+    const int unit = blockIdx.x, b = unit / H, h = unit - b * H, tid = threadIdx.x;
+    const Tree tr = tree_of(offs, b, T);
+    if (tr.n == 0) return;
+    const int n = tr.n, last = n - 1;
+    const uint32_t rq = (uint32_t)H * DK, rv = (uint32_t)H * DV;
+    const float *gu = gate + (size_t)tr.lo * rq + (size_t)h * DK;
+    const uint16_t *ku = k + (size_t)tr.lo * rq + (size_t)h * DK;
+    const uint16_t *qu = q + (size_t)tr.lo * rq + (size_t)h * DK;
+    const uint16_t *vu = v + (size_t)tr.lo * rv + (size_t)h * DV;
+    const float *hu = H0 + (size_t)unit * DK * DV;
+    u32x4 r[18];
+    // rows past the tree repeat its last row, as the verify's staging does
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // gate: 32 pieces per row
+        const int p = tid + NT * u;
+        r[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(gu + (uint32_t)min(p / 32, last) * rq + 4 * (p % 32)));
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // k and q: 16 pieces per row
+        const int p = tid + NT * u;
+        r[4 + u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(ku + (uint32_t)min(p / 16, last) * rq + 8 * (p % 16)));
+        r[6 + u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(qu + (uint32_t)min(p / 16, last) * rq + 8 * (p % 16)));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // H_0: 4096 pieces
+        const int p = tid + NT * u;
+        r[8 + u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hu + 4 * p));
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // v: 16 pieces per row
+        const int p = tid + NT * u;
+        r[16 + u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(vu + (uint32_t)min(p / 16, last) * rv + 8 * (p % 16)));
+    }
+    u32x4 acc = r[0];
+#pragma unroll
+    for (int u = 1; u < 18; ++u) acc ^= r[u];
+    float *ou = out + (size_t)tr.lo * rv + (size_t)h * DV;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // out: 32 pieces per row
+        const int p = tid + NT * u;
+        if (p / 32 < n)
+            __builtin_nontemporal_store(
+                acc, reinterpret_cast<u32x4 *>(ou + (uint32_t)(p / 32) * rv + 4 * (p % 32)));
+    }
+}
+
+bool aligned16(const void *a, const void *b, const void *c, const void *d, const void *e) {
+    return ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+             reinterpret_cast<uintptr_t>(c) | reinterpret_cast<uintptr_t>(d) |
+             reinterpret_cast<uintptr_t>(e)) & 15u) == 0;
+}
+
+}  // namespace
+
+// Scalar-gate verify traffic. H0 [B, H, 128, 64] fp32, q and k [T, H, 128] bf16, v [T, H, 64]
+// bf16, gate [T, H] fp32, out [T, H, 64] fp32 (written with arbitrary values),
+// node_offsets [B + 1], all device pointers, 16-byte aligned. units_per_workgroup: 1, 2 or 4.
+// Returns 0, -1 for a shape or alignment it does not take, or the launch's hipError_t.
+PROBE_API int probe_verify_traffic_scalar(const float *H0, const void *q, const void *k,
+                                          const void *v, const float *gate, float *out,
+                                          const int32_t *node_offsets, int batch, int heads,
+                                          int d_k, int d_v, int total_nodes,
+                                          int units_per_workgroup, hipStream_t stream) {
+    if (d_k != 128 || d_v != 64 || batch < 0 || heads <= 0 || total_nodes < 0) return -1;
+    if (!aligned16(H0, q, k, v, out)) return -1;
+    const int U = batch * heads;
+    if (U == 0) return 0;
+    const auto *qq = static_cast<const uint16_t *>(q);
+    const auto *kk = static_cast<const uint16_t *>(k);
+    const auto *vv = static_cast<const uint16_t *>(v);
+    switch (units_per_workgroup) {
+        case 1:
+            scalar_traffic<1><<<U, 128, 0, stream>>>(H0, qq, kk, vv, gate, out, node_offsets, heads, U, total_nodes);
+            break;
+        case 2:
+            scalar_traffic<2><<<(U + 1) / 2, 256, 0, stream>>>(H0, qq, kk, vv, gate, out, node_offsets, heads, U, total_nodes);
+            break;
+        case 4:
+            scalar_traffic<4><<<(U + 3) / 4, 512, 0, stream>>>(H0, qq, kk, vv, gate, out, node_offsets, heads, U, total_nodes);
+            break;
+        default:
+            return -1;
+    }
+    return (int)hipGetLastError();
+}
+
+// Vector-gate verify traffic: H0 [B, H, 128, 128] fp32, q and k [T, H, 128] bf16, v
+// [T, H, 128] bf16, gate [T, H, 128] fp32, out [T, H, 128] fp32; otherwise as above.
+PROBE_API int probe_verify_traffic_vector(const float *H0, const void *q, const void *k,
+                                          const void *v, const float *gate, float *out,
+                                          const int32_t *node_offsets, int batch, int heads,
+                                          int d_k, int d_v, int total_nodes, hipStream_t stream) {
+    if (d_k != 128 || d_v != 128 || batch < 0 || heads <= 0 || total_nodes < 0) return -1;
+    if (!aligned16(H0, q, k, v, out) || (reinterpret_cast<uintptr_t>(gate) & 15u)) return -1;
+    const int U = batch * heads;
+    if (U == 0) return 0;
+    vector_traffic<<<U, 512, 0, stream>>>(H0, static_cast<const uint16_t *>(q),
+                                          static_cast<const uint16_t *>(k),
+                                          static_cast<const uint16_t *>(v), gate, out,
+                                          node_offsets, heads, total_nodes);
+    return (int)hipGetLastError();
+}
