@@ -37,6 +37,21 @@ def test_library_exports_every_declared_symbol():
     assert not leaked, leaked
 
 
+def test_probe_library_is_separate_and_exports_its_two_kernels():
+    """The benchmark's memory-only reference kernels live in their own library: it
+    exports exactly its two launchers, and libbole.so exports neither."""
+    path = os.path.join(os.path.dirname(bole.LIB_PATH), "libbole_probe.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    probes = {line.split()[-1] for line in out.splitlines() if "probe_" in line}
+    assert probes == {"probe_verify_traffic_scalar", "probe_verify_traffic_vector"}
+    main = subprocess.run(["nm", "-D", "--defined-only", bole.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    assert "probe_" not in main
+    lib = ctypes.CDLL(path)
+    assert lib.probe_verify_traffic_scalar and lib.probe_verify_traffic_vector
+
+
 def _dims(**kw):
     d = bole.make_dims(4, 8, 128, 64, 100, torch.bfloat16, False, 8)
     for k, v in kw.items():

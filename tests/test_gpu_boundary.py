@@ -249,3 +249,44 @@ def test_single_layer_lazy_and_bound_calls_validate_gates(bole):
     assert st.cpu().tolist() == st2.cpu().tolist() == [0, 0, 0, BAD_GATE, 0, 0]
     assert pst.cpu().tolist() == [BAD_GATE, 0, 0, 0, 0, 0]
     assert torch.equal(H[0].cpu(), p["H0"][0].cpu())
+
+
+@pytest.mark.parametrize("vector", [False, True])
+def test_traffic_probe_writes_exactly_the_tree_rows(vector):
+    """The benchmark's memory-only reference (libbole_probe.so) writes every out row of
+    every valid tree and no other row: rows of a bad tree, of an empty tree and past the
+    last tree keep their values."""
+    import ctypes
+    import os
+
+    from tree_speculative_decoding_02_amd import bole as b
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(b.LIB_PATH), "libbole_probe.so"))
+    d = torch.device("cuda:0")
+    B, H, dk = 6, 4, 128
+    dv = 128 if vector else 64
+    offs = np.array([0, 64, 64, 97, 98, 130, 132], dtype=np.int32)  # tree 1 empty
+    offs_bad = offs.copy()
+    offs_bad[5] = 300                                      # trees 4 and 5: bad range
+    T = int(offs[-1]) + 3                                  # 3 rows past the last tree
+    H0 = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=d) + 1.0
+    q = torch.ones((T, H, dk), dtype=torch.bfloat16, device=d)
+    k, v = q.clone(), torch.ones((T, H, dv), dtype=torch.bfloat16, device=d)
+    gate = torch.ones((T, H, dk) if vector else (T, H), dtype=torch.float32, device=d)
+    out = torch.full((T, H, dv), 7.0, dtype=torch.float32, device=d)
+    o = torch.from_numpy(offs_bad).to(d)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = [P(H0), P(q), P(k), P(v), P(gate), P(out), P(o), ctypes.c_int(B), ctypes.c_int(H),
+            ctypes.c_int(dk), ctypes.c_int(dv), ctypes.c_int(T)]
+    print(f"[case] traffic probe, vector={vector}", flush=True)
+    if vector:
+        rc = lib.probe_verify_traffic_vector(*args, ctypes.c_void_p(0))
+    else:
+        rc = lib.probe_verify_traffic_scalar(*args, ctypes.c_int(2), ctypes.c_void_p(0))
+    torch.cuda.synchronize()
+    assert rc == 0
+    written = (out != 7.0).any(dim=2).all(dim=1).cpu().numpy()
+    untouched = (out == 7.0).all(dim=2).all(dim=1).cpu().numpy()
+    want = np.zeros(T, dtype=bool)
+    for t in (0, 2, 3):                                    # the valid non-empty trees
+        want[offs[t]:offs[t + 1]] = True
+    assert (written == want).all() and (untouched == ~want).all()
