@@ -481,11 +481,25 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
     // query operands of node tile tw: 2^{LG_i[c] - off} q_i[c], split hi + lo, with
     // off = M on the factored path (the H_0 term is scaled back by 2^M) and 0 otherwise
     const float off = factored ? M : 0.f;
+    // CG = 2 on the factored path: waves w and w + 4 (same node tile) each build half of
+    // the tile's k-steps (column group h: k-steps h KT/2 ..) and hand them to the other
+    // through LDS, in the V table (group 0's halves) and the pair-weight table (group
+    // 1's), both unused on this path until V is staged
+    const bool share = CG == 2 && !LAZY && factored;
+    constexpr int KH2 = KT / 2;
+    static_assert(CG == 1 || (4 * 2 * KH2 * 64 * 16 <= N * CGW * 2 && 4 * 2 * KH2 * 64 * 16 <= N * N * 4),
+                  "operand exchange regions");
+    bf16x8 *const x_own = reinterpret_cast<bf16x8 *>(hf == 0 ? static_cast<void *>(s_v) : static_cast<void *>(s_w)) +
+                          tw * 2 * KH2 * 64;
+    const bf16x8 *const x_other =
+        reinterpret_cast<const bf16x8 *>(hf == 0 ? static_cast<void *>(s_w) : static_cast<void *>(s_v)) +
+        tw * 2 * KH2 * 64;
     bf16x8 ah[KT], al[KT];
     {
         const int qi = min(16 * tw + n16, last);
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
+            if (share && (t / KH2) != hf) continue;  // the partner's k-step
             const float *lgq = s_lg + qi * DK + 32 * t + 8 * g4;
             const float4 x0 = *reinterpret_cast<const float4 *>(lgq);
             const float4 x1 = *reinterpret_cast<const float4 *>(lgq + 4);
@@ -496,6 +510,10 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
                 split_bf16(static_cast<float>(qf[t][e]) * __builtin_amdgcn_exp2f(lq[e] - off), xh, xl);
                 ah[t][e] = xh;
                 al[t][e] = xl;
+            }
+            if (share) {
+                x_own[(2 * (t % KH2)) * 64 + lane] = ah[t];
+                x_own[(2 * (t % KH2) + 1) * 64 + lane] = al[t];
             }
         }
     }
@@ -515,6 +533,14 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
         __bf16 *s_bh = reinterpret_cast<__bf16 *>(s_big);
         __bf16 *s_bl = s_bh + N * DK;
         __syncthreads();
+        if (share) {
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                if ((t / KH2) == hf) continue;
+                ah[t] = x_other[(2 * (t % KH2)) * 64 + lane];
+                al[t] = x_other[(2 * (t % KH2) + 1) * 64 + lane];
+            }
+        }
 #pragma unroll
         for (int u = 0; u < GPT; ++u) {
             const int P = tid + NT * u;
@@ -539,7 +565,9 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             f32x4 st = {0.f, 0.f, 0.f, 0.f};
-            if (jt <= tw) {
+            // CG = 2: each of waves w and w + 4 takes one ancestor tile pair (column group
+            // h: tiles 2h and 2h + 1), the other's weights come through LDS
+            if (jt <= tw && !(share && (jt >> 1) != hf)) {
                 const int j = 16 * jt + n16;
 #pragma unroll
                 for (int t = 0; t < KT; ++t) {
@@ -565,8 +593,28 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
                 wh[p][e] = xh;
                 wl[p][e] = xl;
             }
+        if (share && 2 * hf <= tw) {
+            // this wave's pair into the pair-weight table (its operand halves there were
+            // read before the last barrier)
+            bf16x8 *const wx = reinterpret_cast<bf16x8 *>(s_w) + wave * 128;
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                if (p == hf) {
+                    wx[lane] = wh[p];
+                    wx[64 + lane] = wl[p];
+                }
+        }
     }
     __syncthreads();  // LG and K are dead: the H_0 slice takes their space
+    if (share && 2 * (1 - hf) <= tw) {
+        const bf16x8 *const wx = reinterpret_cast<const bf16x8 *>(s_w) + (wave ^ 4) * 128;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            if (p != hf) {
+                wh[p] = wx[lane];
+                wl[p] = wx[64 + lane];
+            }
+    }
     if constexpr (LAZY) commit(rh);
 
     // ---- 4. H_0 and V to LDS. H_0 is split hi + lo once here, into two bf16 tables in
