@@ -19,8 +19,8 @@
 // short enough to be resident at once, one 512-thread workgroup per two column groups;
 // trees of up to 64 nodes; up to 16 layers per launch. Every input is staged through
 // registers with plain 16-byte loads issued in the order of use (parent, gate, K, Q
-// fragments, then H_0 and V), so the H_0 and V loads stay in flight while the first
-// phases compute, and each phase waits only for what it reads:
+// fragments; H_0 and V once the gate rows have landed), so the H_0 and V loads stay in
+// flight while the first phases compute, and each phase waits only for what it reads:
 //  1. wavefront 0 builds the topology; the gate and K rows go to LDS;
 //  2. gate -> log2 -> root-first cumulative sums LG by pointer doubling: each thread
 //     keeps its own entries in registers, and round r adds the sum held at the node's
@@ -292,8 +292,9 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
     // pair-weight node and channel quarter (the exact path runs on the first 256 threads)
     const int pi = tl >> 2, psub = tl & 3;
 
-    // ---- issue every load, in order of use. Piece P = tid + NT u of a table with PP
-    // pieces per row is row P / PP, piece P % PP (rows past the tree repeat its last row).
+    // ---- issue the loads in order of use (H_0 and V a little later, below). Piece
+    // P = tid + NT u of a table with PP pieces per row is row P / PP, piece P % PP (rows
+    // past the tree repeat its last row).
     const int p_raw = wave == 0 ? parent[lo + min(lane, last)] : -1;
     u32x4 rg[GPT], rk[KPT], rvv[VPT];
     hvec rh[8];
@@ -314,19 +315,25 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
     for (int t = 0; t < KT; ++t)
         qf[t] = load16(qu + ((uint32_t)min(16 * tw + n16, last) * rq + 32 * t + 8 * g4));
     // H_0: thread (hrg, hn) of column group hf loads rows 8 hrg .. 8 hrg + 7 of the group's
-    // slice, columns CPL*hn .. (the B-operand rows and columns of one lane)
-    if (hrg < HRG) {
+    // slice, columns CPL*hn .. (the B-operand rows and columns of one lane); then V. Both
+    // are needed last, and are issued once the gate rows have landed (with LAZY, once the
+    // first barrier has passed): the gate, K and Q rows that the tree-only phases wait for
+    // then reach the workgroup sooner (workload 3: verify 15.6 -> 15.35 us, lazy step
+    // 20.8 -> 19.9 us, 8 layers of lazy steps 108.8 -> 105.8 us).
+    auto issue_h0_v = [&]() {
+        if (hrg < HRG) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            rh[e] = __builtin_nontemporal_load(
-                reinterpret_cast<const hvec *>(hu + ((uint32_t)(8 * hrg + e) * DV + CPL * hn)));
-    }
+            for (int e = 0; e < 8; ++e)
+                rh[e] = __builtin_nontemporal_load(
+                    reinterpret_cast<const hvec *>(hu + ((uint32_t)(8 * hrg + e) * DV + CPL * hn)));
+        }
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-        const int P = tid + NT * u;
-        rvv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-            vu + ((uint32_t)min(P / VP, last) * rv + 8 * (P % VP))));
-    }
+        for (int u = 0; u < VPT; ++u) {
+            const int P = tid + NT * u;
+            rvv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                vu + ((uint32_t)min(P / VP, last) * rv + 8 * (P % VP))));
+        }
+    };
     if constexpr (LAZY) prefetch();
 
     // ---- 1. topology and doubling pointers (wavefront 0); log2 of the gate rows and
@@ -359,12 +366,14 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
                              __builtin_amdgcn_logf(x.z), __builtin_amdgcn_logf(x.w));
         *reinterpret_cast<float4 *>(s_lg + (P / GP) * DK + 4 * (P % GP)) = lgv[u];
     }
+    if constexpr (!LAZY) issue_h0_v();
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
         const int P = tid + NT * u;
         *reinterpret_cast<u32x4 *>(s_k + (P / KP) * DK + 8 * (P % KP)) = rk[u];
     }
     __syncthreads();
+    if constexpr (LAZY) issue_h0_v();
 
     if (s_info[0] != BOLE_TREE_OK) {
         if constexpr (LAZY) commit(rh);
