@@ -1144,3 +1144,54 @@ def test_packed_fused_verify_equals_sub_batches(bole):
         good = np.concatenate([np.arange(o[b], o[b + 1]) for b in range(B) if st_ref[b] == 0])
         assert rel_err_rows(out.double().cpu().numpy()[good], oref[good]) <= TOL[torch.bfloat16]
         assert (out[int(o[B - 1]):] == 5.0).all()
+
+
+def test_half_column_groups_equal_full_groups(bole):
+    """Under the 32-node budget a launch of at most 256 units at d_v = 64 takes two 32-column
+    groups per unit; a longer launch (the same layer twice) takes one 64-column group. Both
+    give the same outputs, statuses and committed states, to fp32 rounding, and both are
+    within the bars of the oracle."""
+    kw = dict(batch=8, heads=32, d_k=128, d_v=64,
+              sizes=[32, 7, 0, 32, 1, 19, 32, 25])
+    wp, lp = _stack(7171, 1, **kw)
+    wc, lc = _stack(7172, 1, **kw)
+    tp, tc = _tree_dev(wp), _tree_dev(wc)
+    B = wc.batch
+    st = lambda: torch.full((B,), -7, dtype=torch.int32, device=dev())
+    print("[case] half-column groups: verify", flush=True)
+    y1 = _dev_layers(lc)[0]
+    s1 = st()
+    o1 = bole.bole_tree_verify(y1["H0"], y1["q"], y1["k"], y1["v"], y1["gate"], tc["parent"],
+                               tc["offs"], tree_status=s1, trees_le_32=True)
+    ys = _dev_layers(lc + lc)
+    s2 = st()
+    o2 = bole.bole_tree_verify_layers(ys, tc["parent"], tc["offs"], tree_status=s2, trees_le_32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    scale = float(o2[0].abs().max())
+    assert float((o1 - o2[0]).abs().max()) <= 1e-6 * scale
+    assert torch.equal(o2[0], o2[1])
+    ref, sref = oracle.verify_serial(lc[0].H0, lc[0].q, lc[0].k, lc[0].v, lc[0].gate, wc.parent,
+                                     wc.node_offsets, False)
+    assert s1.cpu().tolist() == sref.tolist()
+    assert rel_err_rows(o1.double().cpu().numpy(), ref) <= TOL[torch.bfloat16]
+    print("[case] half-column groups: lazy step", flush=True)
+    y1 = _dev_layers(lc, lp)[0]
+    ps1, s1 = st(), st()
+    o1 = bole.bole_tree_verify_lazy_commit(
+        y1["H0"], (y1["prev_k"], y1["prev_v"], y1["prev_gate"], tp["parent"], tp["offs"]),
+        tp["acc_idx"], tp["acc_len"], y1["q"], y1["k"], y1["v"], y1["gate"], tc["parent"],
+        tc["offs"], prev_tree_status=ps1, tree_status=s1, trees_le_32=True, prev_trees_le_32=True)
+    ys = _dev_layers(lc + lc, lp + lp)
+    ps2, s2 = st(), st()
+    o2 = bole.bole_tree_verify_lazy_commit_layers(
+        ys, tp["parent"], tp["offs"], tp["acc_idx"], tp["acc_len"], tc["parent"], tc["offs"],
+        prev_tree_status=ps2, tree_status=s2, trees_le_32=True, prev_trees_le_32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(ps1, ps2)
+    hs = float(ys[0]["H0"].abs().max())
+    assert float((y1["H0"] - ys[0]["H0"]).abs().max()) <= 1e-6 * hs
+    assert float((o1 - o2[0]).abs().max()) <= 1e-6 * float(o2[0].abs().max())
+    Href, _, _ = oracle.commit_serial(lc[0].H0, lp[0].k, lp[0].v, lp[0].gate, wp.parent,
+                                      wp.node_offsets, wp.accepted_idx, wp.accepted_len, False)
+    assert rel_err_states(y1["H0"].double().cpu().numpy(), Href) <= TOL[torch.bfloat16]

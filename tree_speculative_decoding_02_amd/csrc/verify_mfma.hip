@@ -64,11 +64,13 @@ struct LazyCommit {
 
 // Layer blockIdx.y of the table; every layer runs the same trees. Per-tree outputs
 // (statuses, path rows) are written by layer 0 only.
-template <int DK, int DV>
+// CWM: the most state columns a workgroup (a unit's column group) takes, 64, or 32 for
+// launches too short to fill the chip (two column groups per unit at d_v = 64)
+template <int DK, int DV, int CWM>
 constexpr int ksplit_smem_bytes();
-template <int DK, int DV>
+template <int DK, int DV, int CWM>
 constexpr int ksplit_lazy_smem_elems();
-template <int DK, int DV, bool LAZY>
+template <int DK, int DV, bool LAZY, int CWM>
 __device__ __forceinline__ void ksplit_body(const bole_layer_t, const int32_t *, const int32_t *,
                                             int32_t *, int, int, int, int, char *, int, int,
                                             const LazyCommit &, __bf16 *, const TreeRange *);
@@ -140,14 +142,14 @@ __device__ __forceinline__ PackSlot pack_locate(const int32_t *__restrict__ node
 // its own LDS. A node's q, k, v and out rows of neighbouring heads are adjacent in the
 // token-major layout, so the group's row pieces form runs NW times as long, requested
 // together by one CU.
-template <int DK, int DV, bool LAZY, bool FUSED, int NW>
+template <int DK, int DV, bool LAZY, bool FUSED, int NW, int CWM>
 __global__ __launch_bounds__(FUSED && NW <= 2 ? 128 * NW : 64 * NW, 2) void verify_mfma_tree_kernel(
     const LayerTable lt, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
     int U, int max_n, LazyCommit lc) {
     constexpr int NN = 32;                  // node rows staged
     constexpr int NT = 2;                   // 16-node tiles
-    constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
+    constexpr int CW = DV < CWM ? DV : CWM; // state columns per workgroup
     constexpr int CPL = CW / 16;            // columns per lane: 4 or 2
     constexpr int G = DV / CW;              // column groups per unit
     constexpr int KT = DK / 32;             // k-steps of the bf16 products
@@ -164,21 +166,21 @@ __global__ __launch_bounds__(FUSED && NW <= 2 ? 128 * NW : 64 * NW, 2) void veri
     // row j at [CW j]; lazy commit: k rows and v rows (group columns) of up to kLazyStage
     // path nodes. FUSED: K and V in the buffer the row-split body uses.
     constexpr int kLazyStage = LAZY ? 8 : 1;
-    static_assert(NN * PPR * 16 + NN * CW * 2 <= ksplit_smem_bytes<DK, DV>(), "fused LDS region");
+    static_assert(NN * PPR * 16 + NN * CW * 2 <= ksplit_smem_bytes<DK, DV, CWM>(), "fused LDS region");
     // PACK: NW / 2 row-split regions, or NW one-wavefront regions of half the size
-    static_assert(2 * (NN * PPR * 16 + NN * CW * 2) == ksplit_smem_bytes<DK, DV>(), "packed regions");
-    constexpr int kFusedBytes = FUSED ? (PACK ? NW / 2 : NW) * ksplit_smem_bytes<DK, DV>() : 16;
+    static_assert(2 * (NN * PPR * 16 + NN * CW * 2) == ksplit_smem_bytes<DK, DV, CWM>(), "packed regions");
+    constexpr int kFusedBytes = FUSED ? (PACK ? NW / 2 : NW) * ksplit_smem_bytes<DK, DV, CWM>() : 16;
     __shared__ __align__(16) char s_fused[kFusedBytes];
     __shared__ bf16x8 s_k_own[FUSED ? 1 : NW * NN * PPR];
     __shared__ __bf16 s_v_own[FUSED ? 8 : NW * NN * CW];
     __shared__ __bf16 s_pk_all[NW * kLazyStage * DK], s_pv_all[NW * kLazyStage * CW];
     // FUSED and LAZY: the row-split body's path staging, one region per wavefront
     __shared__ __align__(16) __bf16
-        s_lzk[FUSED && LAZY ? (PACK ? NW : 2 * NW) * ksplit_lazy_smem_elems<DK, DV>() : 8];
+        s_lzk[FUSED && LAZY ? (PACK ? NW : 2 * NW) * ksplit_lazy_smem_elems<DK, DV, CWM>() : 8];
     // this wavefront's unit of the group (FUSED, not packed: two wavefronts per unit)
     const int wv = NW > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> (FUSED && !PACK ? 7 : 6))) : 0;
-    char *const s_unit = s_fused + (PACK ? wv * (ksplit_smem_bytes<DK, DV>() / 2)
-                                        : FUSED ? wv * ksplit_smem_bytes<DK, DV>() : 0);
+    char *const s_unit = s_fused + (PACK ? wv * (ksplit_smem_bytes<DK, DV, CWM>() / 2)
+                                        : FUSED ? wv * ksplit_smem_bytes<DK, DV, CWM>() : 0);
     bf16x8 *const s_k = FUSED ? reinterpret_cast<bf16x8 *>(s_unit) : s_k_own + wv * NN * PPR;
     __bf16 *const s_v = FUSED ? reinterpret_cast<__bf16 *>(s_unit + NN * PPR * 16)
                               : s_v_own + wv * NN * CW;
@@ -190,17 +192,17 @@ __global__ __launch_bounds__(FUSED && NW <= 2 ? 128 * NW : 64 * NW, 2) void veri
         ps = pack_locate(node_offsets, U / H, H, T, max_n, NW * (int)blockIdx.x + wv);
         if (ps.b < 0) return;  // past the last slot: the whole workgroup
         if (ps.large) {
-            ksplit_body<DK, DV, LAZY>(ly, parent, node_offsets, tree_status, H, T, U, max_n,
-                                      s_fused + (wv >> 1) * ksplit_smem_bytes<DK, DV>(),
+            ksplit_body<DK, DV, LAZY, CWM>(ly, parent, node_offsets, tree_status, H, T, U, max_n,
+                                      s_fused + (wv >> 1) * ksplit_smem_bytes<DK, DV, CWM>(),
                                       ps.b * H + (ps.r >> 1), ps.r & 1, lc,
-                                      LAZY ? s_lzk + wv * ksplit_lazy_smem_elems<DK, DV>() : nullptr,
+                                      LAZY ? s_lzk + wv * ksplit_lazy_smem_elems<DK, DV, CWM>() : nullptr,
                                       &ps.tr);
             return;
         }
     } else if constexpr (FUSED) {
-        ksplit_body<DK, DV, LAZY>(ly, parent, node_offsets, tree_status, H, T, U, max_n, s_unit,
+        ksplit_body<DK, DV, LAZY, CWM>(ly, parent, node_offsets, tree_status, H, T, U, max_n, s_unit,
                                   NW * (int)blockIdx.x + wv, (int)((threadIdx.x >> 6) & 1), lc,
-                                  LAZY ? s_lzk + (threadIdx.x >> 6) * ksplit_lazy_smem_elems<DK, DV>()
+                                  LAZY ? s_lzk + (threadIdx.x >> 6) * ksplit_lazy_smem_elems<DK, DV, CWM>()
                                        : nullptr, nullptr);
         if (threadIdx.x & 64) return;  // the second wavefront of each unit
     }
@@ -568,9 +570,9 @@ __global__ __launch_bounds__(FUSED && NW <= 2 ? 128 * NW : 64 * NW, 2) void veri
 // (wave-uniform); K and V rows are staged per pair of tiles, clamped into the tree, so
 // every V row that a masked (zero) weight meets is finite. Every other tree, and the
 // status of out-of-range trees, is the one-wavefront kernel's.
-template <int DK, int DV>
+template <int DK, int DV, int CWM>
 constexpr int ksplit_smem_bytes() {
-    return 64 * (DK / 8) * 16 + 64 * (DV < 64 ? DV : 64) * 2;
+    return 64 * (DK / 8) * 16 + 64 * (DV < CWM ? DV : CWM) * 2;
 }
 
 // LAZY: the unit's state first takes the previous step's accepted path, with the rules and
@@ -578,20 +580,20 @@ constexpr int ksplit_smem_bytes() {
 // and writing back the H_0 rows it holds; the tree is then verified against the new state.
 // Path factors are staged kLazyStage path nodes at a time in `lsmem`, this wavefront's own
 // kLazyStage * (DK / 2 + CW) bf16: the k elements of its rows and the v columns.
-template <int DK, int DV>
+template <int DK, int DV, int CWM>
 constexpr int ksplit_lazy_smem_elems() {
-    return 8 * (DK / 2 + (DV < 64 ? DV : 64));
+    return 8 * (DK / 2 + (DV < CWM ? DV : CWM));
 }
 
 // Both wavefronts of a 128-thread workgroup (or a pair of a packed one); smem holds
 // ksplit_smem_bytes bytes. `known`: the tree range of the unit's sequence, else read here.
-template <int DK, int DV, bool LAZY>
+template <int DK, int DV, bool LAZY, int CWM>
 __device__ __forceinline__ void ksplit_body(
     const bole_layer_t ly, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ node_offsets, int32_t *__restrict__ tree_status, int H, int T,
     int U, int max_n, char *smem, int unit_g1, int w_in, const LazyCommit &lc, __bf16 *lsmem,
     const TreeRange *known) {
-    constexpr int CW = DV < 64 ? DV : 64;   // state columns per workgroup
+    constexpr int CW = DV < CWM ? DV : CWM; // state columns per workgroup
     constexpr int CPL = CW / 16;            // columns per lane: 4 or 2
     constexpr int G = DV / CW;              // column groups per unit
     constexpr int KT = DK / 32;             // k-steps of the bf16 products
@@ -655,7 +657,7 @@ __device__ __forceinline__ void ksplit_body(
     constexpr int DKH = DK / 2;             // k elements of this wavefront's rows
     constexpr int LCK = DKH / 8, LCV = CW / 8, LCPN = LCK + LCV;
     constexpr int LCH = LAZY ? (kStage * LCPN + 63) / 64 : 1;
-    static_assert(!LAZY || ksplit_lazy_smem_elems<DK, DV>() == kStage * (DKH + CW), "staging");
+    static_assert(!LAZY || ksplit_lazy_smem_elems<DK, DV, CWM>() == kStage * (DKH + CW), "staging");
     TreeRange ptr = {0, 0, BOLE_TREE_OK};
     int plen_raw = 0;
     bool plikely = false;
@@ -1028,16 +1030,23 @@ constexpr int kLazyGroup = 4;
 // and its wavefront slots per workgroup (eight, one workgroup per CU, measured slower)
 constexpr int kPackMaxSeq = 1024;
 constexpr int kPackSlots = 4;
+// Launches of at most this many units (sequence x head x layer) at d_v = 64, under the
+// 32-node budget, take two 32-column groups per unit: twice the workgroups, each with half
+// the H_0 slice and half the products, for batches too small to fill the chip. Measured
+// (32-node trees, cold): 64 units 5.4 -> 4.8 us, 256 units 6.4 -> 6.2 us and their lazy
+// step 10.4 -> 9.5 us; but 512 units 8.5 -> 8.8 us, and 256 units of 64-node trees (no
+// budget, the row-split body) 8.9 -> 9.3 us, so neither takes it.
+constexpr uint64_t kHalfColumnsMaxUnits = 256;
 
-template <int DK, int DV>
-static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *parent,
-                         const int32_t *node_offsets, const bole_dims_t &d, int32_t *tree_status,
-                         hipStream_t stream, const LazyCommit *lazy) {
+template <int DK, int DV, int CWM>
+static void launch_shape_cw(const bole_layer_t *layers, int nl, const int32_t *parent,
+                            const int32_t *node_offsets, const bole_dims_t &d,
+                            int32_t *tree_status, hipStream_t stream, const LazyCommit *lazy) {
     const unsigned U = (unsigned)d.batch * (unsigned)d.heads;
     const int max_n = max_tree_nodes(d.flags);
-    // one workgroup per (unit, 64-column group, layer): G > 1: ceil(U / 8) slots of 8
-    // units, each slot G column groups wide, so the groups of a unit share an XCD
-    constexpr int G = DV < 64 ? 1 : DV / 64;
+    // one workgroup per (unit, column group, layer): G > 1: ceil(U / 8) slots of 8 units,
+    // each slot G column groups wide, so the groups of a unit share an XCD
+    constexpr int G = DV < CWM ? 1 : DV / CWM;
     const dim3 grid(G == 1 ? U : ((U + 7) / 8) * 8 * G, (unsigned)nl);
     // groups of units once the launch holds enough of them; a small batch keeps one unit per
     // workgroup, so that more CUs take part
@@ -1055,41 +1064,55 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
         // every tree size in one launch, as the fused verify below, each body committing
         // the units whose trees it verifies
         if (pack)
-            verify_mfma_tree_kernel<DK, DV, true, true, G == 1 ? kPackSlots : 1><<<pgrid, pblock, 0, stream>>>(
+            verify_mfma_tree_kernel<DK, DV, true, true, G == 1 ? kPackSlots : 1, CWM><<<pgrid, pblock, 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
         else if (group && H % 2 == 0)
-            verify_mfma_tree_kernel<DK, DV, true, true, G == 1 ? 2 : 1><<<
+            verify_mfma_tree_kernel<DK, DV, true, true, G == 1 ? 2 : 1, CWM><<<
                 dim3(G == 1 ? (U + 1) / 2 : grid.x, (unsigned)nl), dim3(G == 1 ? 256 : 128), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
         else
-            verify_mfma_tree_kernel<DK, DV, true, true, 1><<<grid, dim3(128), 0, stream>>>(
+            verify_mfma_tree_kernel<DK, DV, true, true, 1, CWM><<<grid, dim3(128), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
     } else if (lazy) {
         if (group)
-            verify_mfma_tree_kernel<DK, DV, true, false, NL><<<lgrid, dim3(64 * NL), 0, stream>>>(
+            verify_mfma_tree_kernel<DK, DV, true, false, NL, CWM><<<lgrid, dim3(64 * NL), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
         else
-            verify_mfma_tree_kernel<DK, DV, true, false, 1><<<grid, dim3(64), 0, stream>>>(
+            verify_mfma_tree_kernel<DK, DV, true, false, 1, CWM><<<grid, dim3(64), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, *lazy);
     } else if (max_n > 32) {
         // two units per workgroup only when they always share a tree (an even head count)
         if (pack)
-            verify_mfma_tree_kernel<DK, DV, false, true, G == 1 ? kPackSlots : 1><<<pgrid, pblock, 0, stream>>>(
+            verify_mfma_tree_kernel<DK, DV, false, true, G == 1 ? kPackSlots : 1, CWM><<<pgrid, pblock, 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
         else if (group && H % 2 == 0)
-            verify_mfma_tree_kernel<DK, DV, false, true, G == 1 ? 2 : 1><<<
+            verify_mfma_tree_kernel<DK, DV, false, true, G == 1 ? 2 : 1, CWM><<<
                 dim3(G == 1 ? (U + 1) / 2 : grid.x, (unsigned)nl), dim3(G == 1 ? 256 : 128), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
         else
-            verify_mfma_tree_kernel<DK, DV, false, true, 1><<<grid, dim3(128), 0, stream>>>(
+            verify_mfma_tree_kernel<DK, DV, false, true, 1, CWM><<<grid, dim3(128), 0, stream>>>(
                 lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
     } else if (group) {
-        verify_mfma_tree_kernel<DK, DV, false, false, NV><<<vgrid, dim3(64 * NV), 0, stream>>>(
+        verify_mfma_tree_kernel<DK, DV, false, false, NV, CWM><<<vgrid, dim3(64 * NV), 0, stream>>>(
             lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
     } else {
-        verify_mfma_tree_kernel<DK, DV, false, false, 1><<<grid, dim3(64), 0, stream>>>(
+        verify_mfma_tree_kernel<DK, DV, false, false, 1, CWM><<<grid, dim3(64), 0, stream>>>(
             lt, parent, node_offsets, tree_status, H, T, (int)U, max_n, none);
     }
+}
+
+template <int DK, int DV>
+static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *parent,
+                         const int32_t *node_offsets, const bole_dims_t &d, int32_t *tree_status,
+                         hipStream_t stream, const LazyCommit *lazy) {
+    if constexpr (DV == 64) {
+        const uint64_t units = (uint64_t)d.batch * (uint64_t)d.heads * (uint64_t)nl;
+        if (units <= kHalfColumnsMaxUnits && max_tree_nodes(d.flags) <= 32) {
+            launch_shape_cw<DK, DV, 32>(layers, nl, parent, node_offsets, d, tree_status, stream, lazy);
+            return;
+        }
+    }
+    launch_shape_cw<DK, DV, 64>(layers, nl, parent, node_offsets, d, tree_status, stream, lazy);
 }
 
 template <int DK>
