@@ -483,11 +483,14 @@ def sweep_sets(wl, dev, rotate_bytes=ROTATE_BYTES, max_sets=64):
     return sets, foot
 
 
-def time_rotated(fs, stream, reps=20, warm=2):
+def time_rotated(fs, stream, reps=20, warm=2, min_launches=100, min_warm=20):
     """Median time of one launch (us): the launches `fs` (one per input set) run in turn
-    under one event pair, `reps` times; each time is that span over len(fs)."""
+    under one event pair, `reps` times; each time is that span over len(fs). At least
+    `min_launches` timed launches after at least `min_warm` untimed ones."""
     import numpy as np
     import torch
+    reps = max(reps, -(-min_launches // len(fs)))
+    warm = max(warm, -(-min_warm // len(fs)))
     for _ in range(warm):
         for f in fs:
             f()
