@@ -7,10 +7,12 @@
 // L_i is the root-first sum of log2 a over path(i). Only per-node factors are read
 // (section 2, "Token-Level Factor Encoding"); no per-node state exists anywhere.
 //
-// Trees of 1..32 nodes take one wavefront per sequence, head and 64-column group; trees
-// of 33..64 nodes take two wavefronts that split H_0's rows. A batch that may hold larger
-// trees runs both in one fused launch; each launch covers up to 16 layers that share the
-// trees (blockIdx.y = layer). The LAZY instantiations first apply the previous step's
+// Trees of 1..32 nodes take one wavefront per sequence, head and column group (64 state
+// columns; 32 in short launches under the 32-node budget); trees of 33..64 nodes take
+// two wavefronts that split H_0's rows. A batch that may hold larger trees runs both in
+// one fused launch, packed (four small-tree or two large-tree units per workgroup) when
+// the head count allows; each launch covers up to 16 layers that share the trees
+// (blockIdx.y = layer). The LAZY instantiations first apply the previous step's
 // accepted path to H_0 (section 2's restore) and write it back, in the same pass over
 // H_0: each unit is committed by the body (one wavefront, or the row split) that
 // verifies its tree.
@@ -33,11 +35,12 @@ namespace bole {
 // throughout: lane = (n, g) with n = lane % 16, g = lane / 16.
 //
 // H_0 term, all v_mfma_f32_16x16x32_bf16. The H_0 slice is loaded straight into
-// registers with row-contiguous 16-byte loads: load s = 8t + e gives lane (n, g) row
-// 32t + 8g + e, columns 4n .. 4n+3, and one load instruction covers 4 full rows. Over
-// the 8 loads of k-step t, lane (n, g) then holds rows 32t + 8g .. +7 of each of its
-// columns: exactly the B operand of a 16x16x32 product whose output column n stands
-// for state column 4n + c. H_0 never goes through LDS. It is split bf16 hi + lo (two
+// registers with row-contiguous loads: load s = 8t + e gives lane (n, g) row
+// 32t + 8g + e, columns CPL n .. CPL n + CPL - 1 (CPL = 4 for 64 columns, 16 bytes; 2 for
+// 32), and one load instruction covers 4 full rows of the group. Over the 8 loads of
+// k-step t, lane (n, g) then holds rows 32t + 8g .. +7 of each of its columns: exactly
+// the B operand of a 16x16x32 product whose output column n stands for state column
+// CPL n + c. H_0 never goes through LDS. It is split bf16 hi + lo (two
 // products, about 16 mantissa bits); the A operand is the bf16 Q fragment of the same
 // k-step, shared with the intra-tree term.
 //
@@ -51,7 +54,7 @@ namespace bole {
 //    32p + 16 + 4g + e - 4 (e >= 4); V is gathered from LDS in the same order;
 //  - W = S * 2^{L_i - L_j} on ancestors, selected to 0 elsewhere, split bf16 hi + lo.
 // Both terms land in one accumulator layout: lane (n, g) holds node 16it + 4g + r,
-// state columns 4n .. 4n+3 across its four tiles, stored as one 16-byte write per row.
+// state columns CPL n .. across its CPL tiles, stored as one write per row.
 // Read-once and write-once streams carry the non-temporal cache policy.
 // The previous step's tree and accepted path, for the lazy-commit form (LAZY): the kernel
 // first applies that path (with the layer's prev_k, prev_v, prev_gate) to H_0 in
