@@ -226,6 +226,9 @@ def main():
     lazy_any = bole.bind_tree_verify_lazy_commit_layers(layers, parent, offs, acc_idx, acc_len,
                                                         parent, offs, stream=stream)
     la_ms, _, _ = timed([[lazy_any]], args.steps, args.warmup)
+    # the memory-only reference for the lazy step: the same bytes in the same pieces
+    ref_launch = lazy_traffic_launch(probe_lib(), layers, wl, offs, acc_idx, acc_len, stream)
+    ref_ms, _, _ = timed([[ref_launch]], args.steps, args.warmup)
 
     nodes = wl.total_nodes
     lb, vb, cb = lazy_bytes(wl), verify_bytes(wl), commit_bytes(wl)
@@ -248,6 +251,13 @@ def main():
                              "form, commit of 8 layers"),
     }
     kd = kernels["lazy"]
+    ref_gbs = L * lb / (ref_ms * 1e6)
+    lazy_reference = {"avg_us_per_launch": 1e3 * ref_ms, "GB_s": ref_gbs,
+                      "frac_hbm_peak": ref_gbs / HBM_PEAK_GBS,
+                      "lazy_rate_of_reference": ref_ms / l_ms[0],
+                      "what": "memory-only kernel moving exactly the lazy launch's bytes (8 "
+                              "layers: H0 read and written back, path and tree rows, out) in "
+                              "the same row pieces, no arithmetic"}
     naive = wl.heads * wl.total_nodes * wl.d_k * wl.d_v * 4
     bole_transient = sum(int(layers[0][n].numel() * layers[0][n].element_size())
                          for n in ("k", "v", "gate"))
@@ -286,6 +296,7 @@ def main():
                                                    "value": nodes / (la_ms * 1e-3),
                                                    "launches_per_step": 1},
         },
+        "lazy_traffic_reference": lazy_reference,
         "hbm_GB_s_step": L * lb / (ms_per_step * 1e6),
         "wall_ms_per_step": 1e3 * wall / args.steps,
         "transient_bytes_per_layer": {"naive_state_per_node": naive,
@@ -519,7 +530,35 @@ def probe_lib():
     common = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 5
     lib.probe_verify_traffic_scalar.argtypes = common + [ctypes.c_int, ctypes.c_void_p]
     lib.probe_verify_traffic_vector.argtypes = common + [ctypes.c_void_p]
+    lib.probe_lazy_traffic_scalar.argtypes = ([ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 4
+                                              + [ctypes.c_int] * 7 + [ctypes.c_void_p])
     return lib
+
+
+def lazy_traffic_launch(lib, layers, wl, parent_offs, acc_idx, acc_len, stream):
+    """A launcher for the memory-only kernel that moves exactly the lazy step's bytes for
+    the layer stack (the same stack, trees and paths; the previous step's tree is this
+    step's, as in the benchmark). H0 is written back unchanged; out gets arbitrary values."""
+    import ctypes
+
+    class ProbeLayer(ctypes.Structure):
+        _fields_ = [(n, ctypes.c_void_p) for n in ("H0", "q", "k", "v", "gate", "out", "prev_k",
+                                                   "prev_v", "prev_gate")]
+    arr = (ProbeLayer * len(layers))()
+    for i, y in enumerate(layers):
+        for n, _ in ProbeLayer._fields_:
+            setattr(arr[i], n, y[n].data_ptr())
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = (arr, len(layers), P(parent_offs), P(parent_offs), P(acc_idx), P(acc_len), wl.batch,
+            wl.heads, wl.d_k, wl.d_v, wl.total_nodes, wl.total_nodes, int(acc_idx.shape[1]),
+            ctypes.c_void_p(stream.cuda_stream))
+
+    def launch():
+        rc = lib.probe_lazy_traffic_scalar(*args)
+        if rc != 0:
+            raise RuntimeError(f"lazy traffic probe failed: {rc}")
+    launch.keep = arr
+    return launch
 
 
 def traffic_reference(lib, wl, sets, stream, verify_us, nbytes, reps):

@@ -290,3 +290,38 @@ def test_traffic_probe_writes_exactly_the_tree_rows(vector):
     for t in (0, 2, 3):                                    # the valid non-empty trees
         want[offs[t]:offs[t + 1]] = True
     assert (written == want).all() and (untouched == ~want).all()
+
+
+def test_lazy_traffic_probe_keeps_the_state():
+    """The lazy-step memory-only reference writes every H0 slice back unchanged and the
+    out rows of every valid tree, on a two-layer stack with paths of several lengths."""
+    import ctypes
+    import os
+
+    import bench
+    from tree_speculative_decoding_02_amd import bole as b
+    d = torch.device("cuda:0")
+    wl = W.make_random(909, batch=5, heads=4, d_k=128, d_v=64, sizes=[32, 9, 0, 64, 17])
+    g = lambda x: torch.as_tensor(np.ascontiguousarray(x)).to(d)
+    layers = []
+    for l in range(2):
+        lay = wl.layers[0] if l == 0 else W.make_random(910, batch=5, heads=4, d_k=128, d_v=64,
+                                                           sizes=[32, 9, 0, 64, 17]).layers[0]
+        y = dict(H0=lay.H0.to(d).clone(), q=lay.q.to(d), k=lay.k.to(d), v=lay.v.to(d),
+                 gate=lay.gate.to(d),
+                 out=torch.full((wl.total_nodes, 4, 64), 7.0, dtype=torch.float32, device=d))
+        y.update(prev_k=y["k"], prev_v=y["v"], prev_gate=y["gate"])
+        layers.append(y)
+    H_before = [y["H0"].clone() for y in layers]
+    offs, ai, al = g(wl.node_offsets), g(wl.accepted_idx), g(wl.accepted_len)
+    st = torch.cuda.current_stream()
+    print("[case] lazy traffic probe, 2 layers", flush=True)
+    launch = bench.lazy_traffic_launch(bench.probe_lib(), layers, wl, offs, ai, al, st)
+    launch()
+    torch.cuda.synchronize()
+    for y, H in zip(layers, H_before):
+        assert torch.equal(y["H0"], H)
+        written = (y["out"] != 7.0).any(dim=2).all(dim=1).cpu().numpy()
+        untouched = (y["out"] == 7.0).all(dim=2).all(dim=1).cpu().numpy()
+        assert written.all() and not untouched.any()   # every row belongs to a valid tree
+    assert int(wl.accepted_len.max()) > 0
