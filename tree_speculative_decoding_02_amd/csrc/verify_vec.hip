@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
     constexpr int SB = 16 * CPN;            // stage bytes per path node
     static_assert(!LAZY || (kStage * CPN <= NT && kStage * SB <= N * CGW * 2), "path staging");
     TreeRange ptr = {0, 0, BOLE_TREE_OK};
-    int plen_raw = 0, lx = 0, lpx = -1, lpp = -1;
+    int plen_raw = 0, lx = 0, lx2 = 0, lpx = -1, lpp = -1;
     bool plikely = false;
     if constexpr (LAZY) {
         ptr = tree_range(lz.node_offsets, b, lz.T, lz.max_n);
@@ -166,6 +166,7 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
                   plen_raw <= ptr.n;
         const int32_t *acc_b = lz.accepted_idx + (size_t)b * lz.max_path;
         if (plikely && tid / CPN < min(kStage, plen_raw)) lx = acc_b[tid / CPN];
+        if (plikely && tid / CPN < min(kStage, plen_raw - kStage)) lx2 = acc_b[kStage + tid / CPN];
         if (wave == 0 && ptr.status == BOLE_TREE_OK && ptr.n > 0) {
             lpp = lane < ptr.n ? lz.parent[ptr.lo + lane] : -1;
             if (lane < plen_raw && plen_raw <= lz.max_path) lpx = acc_b[lane];
@@ -183,10 +184,13 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
                                             8 * (c - SGC - SKC));
         return *reinterpret_cast<const u32x4 *>(p);
     };
-    u32x4 pf = {0u, 0u, 0u, 0u};
+    // the chunks of the first two rounds of kStage path nodes, loaded with the other inputs
+    u32x4 pf = {0u, 0u, 0u, 0u}, pf2 = {0u, 0u, 0u, 0u};
     auto prefetch = [&]() {
         if (plikely && tid / CPN < min(kStage, plen_raw))
             pf = path_chunk(ptr.lo + min(max(lx, 0), ptr.n - 1), tid % CPN);
+        if (plikely && tid / CPN < min(kStage, plen_raw - kStage))
+            pf2 = path_chunk(ptr.lo + min(max(lx2, 0), ptr.n - 1), tid % CPN);
     };
     // wavefront 0: the path checks of the commit, its per-tree outputs, and the path
     // (length, rows) for every thread
@@ -231,7 +235,9 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
         for (int m0 = 0; m0 < plen; m0 += kStage) {
             const int mc = min(kStage, plen - m0);
             if (tid / CPN < mc) {
-                const u32x4 x = m0 == 0 ? pf : path_chunk(s_prow[m0 + tid / CPN], tid % CPN);
+                const u32x4 x = m0 == 0 ? pf
+                                : m0 == kStage ? pf2
+                                               : path_chunk(s_prow[m0 + tid / CPN], tid % CPN);
                 *reinterpret_cast<u32x4 *>(stage + 16 * tid) = x;
             }
             __syncthreads();
