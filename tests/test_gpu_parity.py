@@ -1195,3 +1195,37 @@ def test_half_column_groups_equal_full_groups(bole):
     Href, _, _ = oracle.commit_serial(lc[0].H0, lp[0].k, lp[0].v, lp[0].gate, wp.parent,
                                       wp.node_offsets, wp.accepted_idx, wp.accepted_len, False)
     assert rel_err_states(y1["H0"].double().cpu().numpy(), Href) <= TOL[torch.bfloat16]
+
+
+def test_packed_launch_sequence_limit(bole):
+    """The packed fused launch takes batches of at most 1024 sequences (every wavefront
+    reads all tree offsets); 1025 sequences take the two-units-per-workgroup launch. The
+    first 1024 sequences come out bit for bit the same either way, at the smallest head
+    count the packed launch takes (4), and a sample of sequences matches the oracle."""
+    sizes = [(1, 2, 33, 40, 64, 0, 31, 17, 48)[i % 9] for i in range(1025)]
+    wl = W.make_random(9191, batch=1025, heads=4, d_k=128, d_v=64, sizes=sizes, kind="random")
+    t = to_dev(wl)
+    o = wl.node_offsets
+    T1024 = int(o[1024])
+    print("[case] packed launch limit: 1025 and 1024 sequences x 4 heads", flush=True)
+    st_full = torch.full((1025,), -7, dtype=torch.int32, device=dev())
+    out_full = bole.bole_tree_verify(t["H0"], t["q"], t["k"], t["v"], t["gate"], t["parent"],
+                                     t["offs"], tree_status=st_full)
+    st_pk = torch.full((1024,), -7, dtype=torch.int32, device=dev())
+    out_pk = bole.bole_tree_verify(t["H0"][:1024], t["q"][:T1024], t["k"][:T1024],
+                                   t["v"][:T1024], t["gate"][:T1024], t["parent"][:T1024],
+                                   t["offs"][:1025], tree_status=st_pk)
+    torch.cuda.synchronize()
+    assert torch.equal(out_full[:T1024], out_pk) and torch.equal(st_full[:1024], st_pk)
+    assert (st_full == 0).all()
+    # the oracle on every 64th sequence (and the last)
+    lay = wl.layers[0]
+    for b in list(range(0, 1025, 64)) + [1024]:
+        lo, hi = int(o[b]), int(o[b + 1])
+        if hi == lo:
+            continue
+        ref, st = oracle.verify_serial(lay.H0[b:b + 1], lay.q[lo:hi], lay.k[lo:hi], lay.v[lo:hi],
+                                       lay.gate[lo:hi], wl.parent[lo:hi],
+                                       np.array([0, hi - lo], dtype=np.int32), False)
+        assert st.tolist() == [0]
+        assert rel_err_rows(out_full[lo:hi].double().cpu().numpy(), ref) <= TOL[torch.bfloat16], b
