@@ -656,6 +656,19 @@ def config_sweep(dev, reps=20, configs=(1, 2, 3, 4, 5)):
                                 nbytes["verify"], reps)
         if ref is not None:
             rec["verify_traffic_reference"] = ref
+        if ref is not None and not wl.vector_gate:
+            # the lazy step's bytes, moved by the memory-only kernel on the same sets
+            lfs = [lazy_traffic_launch(plib, [dict(H0=x["H0"], q=x["q"], k=x["k"], v=x["v"],
+                                                   gate=x["gate"], out=x["out"], prev_k=x["k"],
+                                                   prev_v=x["v"], prev_gate=x["gate"])],
+                                       wl, x["offs"], x["ai"], x["al"], stream) for x in sets]
+            lus = time_rotated(lfs, stream, reps)
+            lgbs = nbytes["lazy"] / (lus * 1e3)
+            rec["lazy_traffic_reference"] = {
+                "median_us": lus, "GB_s": lgbs, "frac_hbm_peak": lgbs / HBM_PEAK_GBS,
+                "lazy_rate_of_reference": lus / rec["lazy"]["median_us"],
+                "what": "memory-only kernel moving the lazy step's bytes (H0 read and written "
+                        "back, path and tree rows, out) in the same row pieces"}
         print(json.dumps(rec), flush=True)
         del sets, launches
     if 3 in configs:
