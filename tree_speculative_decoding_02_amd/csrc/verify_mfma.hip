@@ -140,7 +140,9 @@ __device__ __forceinline__ PackSlot pack_locate(const int32_t *__restrict__ node
 // trees they do not take. With NW = 2 a workgroup of four wavefronts takes heads 2j and
 // 2j + 1 of one sequence (so one tree, and the row-split barriers of both units match).
 // FUSED with NW = 4 or 8: the packed launch (above), 64 NW threads.
-// NW > 1 (one 64-column group per unit, not FUSED): a workgroup of NW wavefronts takes NW
+// CWM: the most state columns a workgroup takes (64, or 32 for two column groups per unit
+// at d_v = 64).
+// NW > 1 (one column group per unit, not FUSED): a workgroup of NW wavefronts takes NW
 // consecutive units, heads NW j .. NW j + NW - 1 of a sequence, one per wavefront, each with
 // its own LDS. A node's q, k, v and out rows of neighbouring heads are adjacent in the
 // token-major layout, so the group's row pieces form runs NW times as long, requested
