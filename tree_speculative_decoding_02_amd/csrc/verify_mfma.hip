@@ -692,7 +692,10 @@ __device__ __forceinline__ void ksplit_body(
     const float g_raw = gate[(size_t)lo * H + h + node * (uint32_t)H];
     // qa[r][tl]: Q fragment of relative tile r at this wavefront's k-step w*KH + tl;
     // qb[r][tl] (loaded after the H_0 term, which does not need it): own tile r at the
-    // other wavefront's k-step (1 - w)*KH + tl
+    // other wavefront's k-step (1 - w)*KH + tl. The other wavefront's tiles (r >= 2) are
+    // read again there, as its qb: they take plain loads, which leave the lines in L2 for
+    // that second read (streaming loads did not, and it went to HBM: 64-node trees 74.0
+    // -> 65.2 us, the ragged batch 51.4 -> 47.2 us)
     bf16x8 qa[4][KH], qb[2][KH];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -701,7 +704,9 @@ __device__ __forceinline__ void ksplit_body(
 #pragma unroll
         for (int tl = 0; tl < KH; ++tl) {
             qa[r][tl] = bf16x8{};
-            if (ti < ntl) qa[r][tl] = load16_stream(qrow + 32 * (w * KH + tl));
+            if (ti < ntl)
+                qa[r][tl] = r >= 2 ? load16(qrow + 32 * (w * KH + tl))
+                                   : load16_stream(qrow + 32 * (w * KH + tl));
         }
     }
     // K: load s = w + 2u fills LDS slots 64s .. 64s+63 (rows (64/PPR)s ..); V: load s,
