@@ -304,17 +304,22 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
     const int p_raw = wave == 0 ? parent[lo + min(lane, last)] : -1;
     u32x4 rg[GPT], rk[KPT], rvv[VPT];
     hvec rh[8];
+    // gate and K rows: with several workgroups per unit (GS > 1) each of them reads the
+    // unit's rows, so plain loads, which leave the lines in L2 for the others (8-layer
+    // stacks of workload 3's shape: verify 105 -> 99 us); one workgroup per unit streams them
+    auto row16 = [&](const void *p) -> u32x4 {
+        return GS > 1 ? *reinterpret_cast<const u32x4 *>(p)
+                      : __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    };
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
         const int P = tid + NT * u;
-        rg[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-            gu + ((uint32_t)min(P / GP, last) * rq + 4 * (P % GP))));
+        rg[u] = row16(gu + ((uint32_t)min(P / GP, last) * rq + 4 * (P % GP)));
     }
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
         const int P = tid + NT * u;
-        rk[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-            ku + ((uint32_t)min(P / KP, last) * rq + 8 * (P % KP))));
+        rk[u] = row16(ku + ((uint32_t)min(P / KP, last) * rq + 8 * (P % KP)));
     }
     bf16x8 qf[KT];      // Q fragments: row 16*tw + n, channels 32t + 8g .. +7
 #pragma unroll
