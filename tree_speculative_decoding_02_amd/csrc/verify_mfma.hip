@@ -305,19 +305,21 @@ __global__ __launch_bounds__(FUSED && NW <= 2 ? 128 * NW : 64 * NW, 2) void veri
     // takes row (64/VPR)s + l/VPR, piece l % VPR.
     constexpr int KL = NN * PPR / 64, VL = NN * VPR / 64;
     bf16x8 kst[KL], vst[VL];
+    // q and k rows: with several column groups per unit (G > 1) every group's workgroup
+    // reads them, so plain loads, which leave the lines in L2 for the others
+    auto qk16 = [](const __bf16 *p) { return G > 1 ? load16(p) : load16_stream(p); };
     if (do_verify) {
 #pragma unroll
         for (int it = 0; it < NT; ++it)
 #pragma unroll
             for (int t = 0; t < KT; ++t)
-                qf[it][t] = load16_stream(
-                    qu + ((uint32_t)min(16 * it + n16, last) * rq + 32 * t + 8 * g));
+                qf[it][t] = qk16(qu + ((uint32_t)min(16 * it + n16, last) * rq + 32 * t + 8 * g));
 #pragma unroll
         for (int u = 0; u < KL; ++u) {
             const int s = u;
             const int j = (64 / PPR) * s + lane / PPR;
             const int pc = (lane % PPR) ^ (j % PPR);
-            kst[u] = load16_stream(ku + ((uint32_t)min(j, last) * rq + 8 * pc));
+            kst[u] = qk16(ku + ((uint32_t)min(j, last) * rq + 8 * pc));
         }
 #pragma unroll
         for (int u = 0; u < VL; ++u) {
@@ -705,8 +707,8 @@ __device__ __forceinline__ void ksplit_body(
         for (int tl = 0; tl < KH; ++tl) {
             qa[r][tl] = bf16x8{};
             if (ti < ntl)
-                qa[r][tl] = r >= 2 ? load16(qrow + 32 * (w * KH + tl))
-                                   : load16_stream(qrow + 32 * (w * KH + tl));
+                qa[r][tl] = (r >= 2 || G > 1) ? load16(qrow + 32 * (w * KH + tl))
+                                              : load16_stream(qrow + 32 * (w * KH + tl));
         }
     }
     // K: load s = w + 2u fills LDS slots 64s .. 64s+63 (rows (64/PPR)s ..); V: load s,
@@ -718,7 +720,10 @@ __device__ __forceinline__ void ksplit_body(
         const int s = w + 2 * u;
         const int j = (64 / PPR) * s + lane / PPR;
         const int pc = (lane % PPR) ^ (j % PPR);
-        if ((64 / PPR) * s < rows) kst[u] = load16_stream(ku + ((uint32_t)min(j, last) * rq + 8 * pc));
+        // (G > 1: every column group's workgroup reads these rows, as the q rows)
+        if ((64 / PPR) * s < rows)
+            kst[u] = G > 1 ? load16(ku + ((uint32_t)min(j, last) * rq + 8 * pc))
+                           : load16_stream(ku + ((uint32_t)min(j, last) * rq + 8 * pc));
     }
     // H_0 rows of this wavefront: load s = 8tl + e, lane (n, g): row 32(w*KH + tl) + 8g + e
     hvec hreg[HSW];
@@ -885,7 +890,9 @@ __device__ __forceinline__ void ksplit_body(
 #pragma unroll
         for (int tl = 0; tl < KH; ++tl) {
             qb[r][tl] = bf16x8{};
-            if (ti < ntl) qb[r][tl] = load16_stream(qrow + 32 * ((1 - w) * KH + tl));
+            if (ti < ntl)
+                qb[r][tl] = G > 1 ? load16(qrow + 32 * ((1 - w) * KH + tl))
+                                  : load16_stream(qrow + 32 * ((1 - w) * KH + tl));
         }
     }
     // V rows, needed only by the intra-tree term and staged after the swap in the region
