@@ -42,10 +42,21 @@ struct AcceptArgs {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
+// A 16-byte piece of a row: KEEP (sampling, which reads a node's rows again within the
+// call) a plain load that leaves the lines in the caches, else a streaming load (greedy
+// reads each row once; plain loads there were slower: 75 -> 91 us cold, while sampling
+// went 300 -> 251 us).
+template <bool KEEP>
+__device__ __forceinline__ f4 piece(const float *p) {
+    return KEEP ? *reinterpret_cast<const f4 *>(p)
+                : __builtin_nontemporal_load(reinterpret_cast<const f4 *>(p));
+}
+
 // Elements y .. y+3 of an fp32 row (y a multiple of 4; values past V are unspecified):
 // one 16-byte load when the row allows it.
+template <bool KEEP>
 __device__ __forceinline__ f4 load4(const float *row, int y, int V, bool vec) {
-    if (vec) return __builtin_nontemporal_load(reinterpret_cast<const f4 *>(row + min(y, V - 4)));
+    if (vec) return piece<KEEP>(row + min(y, V - 4));
     f4 x;
 #pragma unroll
     for (int c = 0; c < 4; ++c) x[c] = row[min(y + c, V - 1)];
@@ -58,7 +69,7 @@ __device__ __forceinline__ f4 load4(const float *row, int y, int V, bool vec) {
 // 0 for a sum): every loaded value is then used unconditionally, so the compiler keeps
 // the batch of loads in flight together instead of moving a load under a per-element
 // branch.
-template <typename F>
+template <bool KEEP, typename F>
 __device__ __forceinline__ void row_pass(const float *row, int V, bool vec, F f, float pad) {
     const int t = threadIdx.x;
     if (vec) {
@@ -68,7 +79,7 @@ __device__ __forceinline__ void row_pass(const float *row, int V, bool vec, F f,
 #pragma unroll
             for (int u = 0; u < kAcceptBatch; ++u) {
                 const int y = y0 + u * step;
-                x[u] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(row + min(y, V - 4)));
+                x[u] = piece<KEEP>(row + min(y, V - 4));
             }
 #pragma unroll
             for (int u = 0; u < kAcceptBatch; ++u) {
@@ -95,7 +106,7 @@ __device__ __forceinline__ void row_pass(const float *row, int V, bool vec, F f,
 // Calls f(y, p(y), q(y)) for the elements of two fp32 rows this thread owns, in
 // increasing y; kAcceptBatch / 4 16-byte loads of each row in flight. Positions past the
 // rows get p = q = 0 (f must then add nothing), for the reason given above.
-template <typename F>
+template <bool KEEP, typename F>
 __device__ __forceinline__ void row_pass2(const float *prow, const float *qrow, int V, bool vec,
                                           F f) {
     constexpr int NB = kAcceptBatch / 4;
@@ -104,8 +115,8 @@ __device__ __forceinline__ void row_pass2(const float *prow, const float *qrow, 
         f4 px[NB], qx[NB];
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-            px[u] = load4(prow, y0 + u * step, V, vec);
-            qx[u] = load4(qrow, y0 + u * step, V, vec);
+            px[u] = load4<KEEP>(prow, y0 + u * step, V, vec);
+            qx[u] = load4<KEEP>(qrow, y0 + u * step, V, vec);
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
@@ -162,7 +173,7 @@ constexpr int kTileBatch = kAcceptBatch / 4;
 
 // VP, VQ: the target rows (p), the draft rows (q) take 16-byte loads. As template
 // constants they leave no branch between the loads of a batch.
-template <bool VP, bool VQ>
+template <bool VP, bool VQ, bool KEEP>
 __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs a) {
     __shared__ double s_red[kAcceptWaves];
     __shared__ double s_tw[kAcceptWaves][kTileGroup];
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
             // ---- greedy: argmax of the target row
             float bv = -__builtin_huge_valf();
             int bi = 0x7fffffff;
-            row_pass(prow, V, VP, [&](int y, float x) {
+            row_pass<KEEP>(prow, V, VP, [&](int y, float x) {
                 if (x > bv) {  // y increases: a tie keeps the earlier id
                     bv = x;
                     bi = y;
@@ -294,7 +305,7 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
             C = C / Zp + 1.0 / Zq;
             Zq = Zq - (double)qx;
             double part = 0.0;
-            row_pass2(prow, qrow, V, VP && VQ,
+            row_pass2<KEEP>(prow, qrow, V, VP && VQ,
                       [&](int, float py, float qy) { part += residual(py, qy, A, C); });
             Zp = block_sum_d(part, s_red);
             ++k;
@@ -314,7 +325,7 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
         double total = Zp;
         if (!withq) {
             double part = 0.0;
-            row_pass(prow, V, VP, [&](int, float x) { part += (double)x; }, 0.f);
+            row_pass<KEEP>(prow, V, VP, [&](int, float x) { part += (double)x; }, 0.f);
             total = block_sum_d(part, s_red);
         }
         const double thr = (double)a.u_bonus[b] * total;
@@ -332,8 +343,8 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
 #pragma unroll
                 for (int u = 0; u < kTileBatch; ++u) {
                     const int y = (g0 + j0 + u) * kTile + 4 * t;
-                    pv[u] = load4(prow, y, V, VP);
-                    qv[u] = withq ? load4(qrow, y, V, VQ) : f4{0.f, 0.f, 0.f, 0.f};
+                    pv[u] = load4<KEEP>(prow, y, V, VP);
+                    qv[u] = withq ? load4<KEEP>(qrow, y, V, VQ) : f4{0.f, 0.f, 0.f, 0.f};
                 }
 #pragma unroll
                 for (int u = 0; u < kTileBatch; ++u) {
@@ -367,8 +378,8 @@ __global__ __launch_bounds__(kAcceptThreads) void tree_accept_kernel(AcceptArgs 
         }
         if (tile >= 0) {
             const int y = tile * kTile + 4 * t;
-            const f4 pv = load4(prow, y, V, VP);
-            const f4 qv = withq ? load4(qrow, y, V, VQ) : f4{0.f, 0.f, 0.f, 0.f};
+            const f4 pv = load4<KEEP>(prow, y, V, VP);
+            const f4 qv = withq ? load4<KEEP>(qrow, y, V, VQ) : f4{0.f, 0.f, 0.f, 0.f};
             double e[4], sv = 0.0;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -445,10 +456,16 @@ hipError_t launch_tree_accept(const float *p_ctx, const float *p_node, const flo
     a.vecq = d.vocab % 4 == 0 && q_ctx && q_node &&
              ((reinterpret_cast<uintptr_t>(q_ctx) | reinterpret_cast<uintptr_t>(q_node)) % 16) == 0;
     const dim3 grid((unsigned)d.batch), block(kAcceptThreads);
-    if (a.vec && a.vecq) tree_accept_kernel<true, true><<<grid, block, 0, stream>>>(a);
-    else if (a.vec) tree_accept_kernel<true, false><<<grid, block, 0, stream>>>(a);
-    else if (a.vecq) tree_accept_kernel<false, true><<<grid, block, 0, stream>>>(a);
-    else tree_accept_kernel<false, false><<<grid, block, 0, stream>>>(a);
+    if (a.mode == BOLE_ACCEPT_SAMPLE) {
+        if (a.vec && a.vecq) tree_accept_kernel<true, true, true><<<grid, block, 0, stream>>>(a);
+        else if (a.vec) tree_accept_kernel<true, false, true><<<grid, block, 0, stream>>>(a);
+        else if (a.vecq) tree_accept_kernel<false, true, true><<<grid, block, 0, stream>>>(a);
+        else tree_accept_kernel<false, false, true><<<grid, block, 0, stream>>>(a);
+    } else {
+        // greedy reads no draft rows
+        if (a.vec) tree_accept_kernel<true, false, false><<<grid, block, 0, stream>>>(a);
+        else tree_accept_kernel<false, false, false><<<grid, block, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 
