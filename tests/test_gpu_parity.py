@@ -1147,10 +1147,10 @@ def test_packed_fused_verify_equals_sub_batches(bole):
 
 
 def test_half_column_groups_equal_full_groups(bole):
-    """Under the 32-node budget a launch of at most 256 units at d_v = 64 takes two 32-column
-    groups per unit; a longer launch (the same layer twice) takes one 64-column group. Both
-    give the same outputs, statuses and committed states, to fp32 rounding, and both are
-    within the bars of the oracle."""
+    """Under the 32-node budget a launch of at most 512 units at d_v = 64 takes two 32-column
+    groups per unit; a longer launch (the same layer three times, 768 units) takes one
+    64-column group. Both give the same outputs, statuses and committed states, to fp32
+    rounding, and both are within the bars of the oracle."""
     kw = dict(batch=8, heads=32, d_k=128, d_v=64,
               sizes=[32, 7, 0, 32, 1, 19, 32, 25])
     wp, lp = _stack(7171, 1, **kw)
@@ -1163,7 +1163,8 @@ def test_half_column_groups_equal_full_groups(bole):
     s1 = st()
     o1 = bole.bole_tree_verify(y1["H0"], y1["q"], y1["k"], y1["v"], y1["gate"], tc["parent"],
                                tc["offs"], tree_status=s1, trees_le_32=True)
-    ys = _dev_layers(lc + lc)
+    ys = _dev_layers(lc + lc + lc)
+    assert wc.batch * kw["heads"] * 3 > 512
     s2 = st()
     o2 = bole.bole_tree_verify_layers(ys, tc["parent"], tc["offs"], tree_status=s2, trees_le_32=True)
     torch.cuda.synchronize()
@@ -1182,7 +1183,7 @@ def test_half_column_groups_equal_full_groups(bole):
         y1["H0"], (y1["prev_k"], y1["prev_v"], y1["prev_gate"], tp["parent"], tp["offs"]),
         tp["acc_idx"], tp["acc_len"], y1["q"], y1["k"], y1["v"], y1["gate"], tc["parent"],
         tc["offs"], prev_tree_status=ps1, tree_status=s1, trees_le_32=True, prev_trees_le_32=True)
-    ys = _dev_layers(lc + lc, lp + lp)
+    ys = _dev_layers(lc + lc + lc, lp + lp + lp)
     ps2, s2 = st(), st()
     o2 = bole.bole_tree_verify_lazy_commit_layers(
         ys, tp["parent"], tp["offs"], tp["acc_idx"], tp["acc_len"], tc["parent"], tc["offs"],

@@ -1047,13 +1047,16 @@ constexpr int kLazyGroup = 4;
 // and its wavefront slots per workgroup (eight, one workgroup per CU, measured slower)
 constexpr int kPackMaxSeq = 1024;
 constexpr int kPackSlots = 4;
-// Launches of at most this many units (sequence x head x layer) at d_v = 64, under the
-// 32-node budget, take two 32-column groups per unit: twice the workgroups, each with half
-// the H_0 slice and half the products, for batches too small to fill the chip. Measured
-// (32-node trees, cold): 64 units 5.4 -> 4.8 us, 256 units 6.4 -> 6.2 us and their lazy
-// step 10.4 -> 9.5 us; but 512 units 8.5 -> 8.8 us, and 256 units of 64-node trees (no
-// budget, the row-split body) 8.9 -> 9.3 us, so neither takes it.
+// Launches of at most this many units (sequence x head x layer) at d_v = 64 take two
+// 32-column groups per unit: twice the workgroups, each with half the H_0 slice and half
+// the products, for batches too small to fill the chip (the groups of a unit share its q
+// and k rows through L2). Measured (cold): 256 units of 32-node trees 6.4 -> 5.9 us, their
+// lazy step 10.4 -> 9.8 us, 128 units of 64-node trees 7.7 -> 6.7 us, 256 of them
+// unchanged. At 512 units, 32-node trees gain (8.4 -> 8.0 us) but 64-node trees lose
+// (12.3 -> 12.5-13.3 us), so the larger limit holds only under the 32-node budget; at 1,024
+// units both lose.
 constexpr uint64_t kHalfColumnsMaxUnits = 256;
+constexpr uint64_t kHalfColumnsMaxUnitsBudget32 = 512;
 
 template <int DK, int DV, int CWM>
 static void launch_shape_cw(const bole_layer_t *layers, int nl, const int32_t *parent,
@@ -1124,7 +1127,9 @@ static void launch_shape(const bole_layer_t *layers, int nl, const int32_t *pare
                          hipStream_t stream, const LazyCommit *lazy) {
     if constexpr (DV == 64) {
         const uint64_t units = (uint64_t)d.batch * (uint64_t)d.heads * (uint64_t)nl;
-        if (units <= kHalfColumnsMaxUnits && max_tree_nodes(d.flags) <= 32) {
+        const uint64_t limit = max_tree_nodes(d.flags) <= 32 ? kHalfColumnsMaxUnitsBudget32
+                                                              : kHalfColumnsMaxUnits;
+        if (units <= limit) {
             launch_shape_cw<DK, DV, 32>(layers, nl, parent, node_offsets, d, tree_status, stream, lazy);
             return;
         }
