@@ -8,7 +8,7 @@
 // (section 2, "Token-Level Factor Encoding"); no per-node state exists anywhere.
 //
 // Trees of 1..32 nodes take one wavefront per sequence, head and column group (64 state
-// columns; 32 in short launches under the 32-node budget); trees of 33..64 nodes take
+// columns; 32 in short launches); trees of 33..64 nodes take
 // two wavefronts that split H_0's rows. A batch that may hold larger trees runs both in
 // one fused launch, packed (four small-tree or two large-tree units per workgroup) when
 // the head count allows; each launch covers up to 16 layers that share the trees
