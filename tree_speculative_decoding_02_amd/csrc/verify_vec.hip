@@ -22,9 +22,10 @@
 // fragments; H_0 and V once the gate rows have landed), so the H_0 and V loads stay in
 // flight while the first phases compute, and each phase waits only for what it reads:
 //  1. wavefront 0 builds the topology; the gate and K rows go to LDS;
-//  2. gate -> log2 -> root-first cumulative sums LG by pointer doubling: each thread
-//     keeps its own entries in registers, and round r adds the sum held at the node's
-//     2^r-th ancestor (ceil(log2 depth) rounds, one barrier pair each);
+//  2. gate -> log2 -> root-first cumulative sums LG by pointer doubling across lanes:
+//     lane = node, each wavefront holds a slice of the channels in registers, and round
+//     r adds the sums held by the node's 2^r-th ancestor, read from its lane
+//     (ceil(log2 depth) rounds, no barriers);
 //  3. the LG range; pair weights (exact path) or key operands and S tiles (factored
 //     path); each wavefront builds its decayed-query operands for one 16-node tile;
 //  4. H_0 and V go to LDS, H_0 reusing the space of the LG and K tables;
@@ -297,6 +298,10 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
     const int n16 = lane & 15, g4 = lane >> 4;
     // pair-weight node and channel quarter (the exact path runs on the first 256 threads)
     const int pi = tl >> 2, psub = tl & 3;
+    // LG table: row `row`, 16-byte chunk `ch` (channels 4 ch ..) lies at chunk ch ^ (row mod
+    // NCL) of the row, so that 16 lanes reading one chunk of 16 rows fall on distinct banks
+    constexpr int NCL = DK / 4;
+    auto lgx = [](int row, int ch) { return row * DK + 4 * (ch ^ (row & (NCL - 1))); };
 
     // ---- issue the loads in order of use (H_0 and V a little later, below). Piece
     // P = tid + NT u of a table with PP pieces per row is row P / PP, piece P % PP (rows
@@ -368,14 +373,13 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
         if (writer) tree_status[b] = topo.bad;
         if constexpr (LAZY) validate();
     }
-    float4 lgv[GPT];  // this thread's gate entries: row (tid + 256u) / GP, channels 4*(.. % GP)
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
         const int P = tid + NT * u;
         const float4 x = __builtin_bit_cast(float4, rg[u]);
-        lgv[u] = make_float4(__builtin_amdgcn_logf(x.x), __builtin_amdgcn_logf(x.y),
-                             __builtin_amdgcn_logf(x.z), __builtin_amdgcn_logf(x.w));
-        *reinterpret_cast<float4 *>(s_lg + (P / GP) * DK + 4 * (P % GP)) = lgv[u];
+        *reinterpret_cast<float4 *>(s_lg + lgx(P / GP, P % GP)) =
+            make_float4(__builtin_amdgcn_logf(x.x), __builtin_amdgcn_logf(x.y),
+                        __builtin_amdgcn_logf(x.z), __builtin_amdgcn_logf(x.w));
     }
     if constexpr (!LAZY) issue_h0_v();
 #pragma unroll
@@ -393,44 +397,49 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
         return;
     }
 
-    // ---- 2. LG by pointer doubling: after round r an entry holds the sum over the
-    // node's 2^{r+1} nearest path nodes (or its whole path)
+    // ---- 2. LG by pointer doubling across lanes: wavefront w holds chunks CPW w .. CPW w
+    // + CPW - 1 of every node's row (lane = node) in registers, and round r adds the sums
+    // held by each node's 2^r-th ancestor, read from its lane (ds_bpermute): after round r
+    // an entry holds the sum over the node's 2^{r+1} nearest path nodes (or its whole
+    // path). Every lane reads the sums of the previous round, so no round needs a barrier;
+    // each wavefront writes its chunks back, and the range's barrier publishes them.
+    constexpr int CPW = NCL / (NT / 64);
+    static_assert(NCL % (NT / 64) == 0, "LG chunks per wavefront");
+    float4 lv[CPW];
+#pragma unroll
+    for (int x = 0; x < CPW; ++x)
+        lv[x] = *reinterpret_cast<const float4 *>(s_lg + lgx(lane, CPW * wave + x));
     const int rounds = s_info[1];
     for (int r = 0; r < rounds; ++r) {
-        bool moved[GPT];  // entries whose 2^r-th ancestor exists; only they change
+        const int a = s_anc[r][lane];
+        const int src = (a >= 0 ? a : lane) << 2;
+        auto pull = [&](float &y) {
+            const float t = __builtin_bit_cast(
+                float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, y)));
+            y = a >= 0 ? y + t : y;
+        };
 #pragma unroll
-        for (int u = 0; u < GPT; ++u) {
-            const int P = tid + NT * u;
-            const int a = s_anc[r][P / GP];
-            moved[u] = a >= 0;
-            if (moved[u]) {
-                const float4 x = *reinterpret_cast<const float4 *>(s_lg + a * DK + 4 * (P % GP));
-                lgv[u].x += x.x;
-                lgv[u].y += x.y;
-                lgv[u].z += x.z;
-                lgv[u].w += x.w;
-            }
+        for (int x = 0; x < CPW; ++x) {
+            pull(lv[x].x);
+            pull(lv[x].y);
+            pull(lv[x].z);
+            pull(lv[x].w);
         }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < GPT; ++u) {
-            const int P = tid + NT * u;
-            if (moved[u])
-                *reinterpret_cast<float4 *>(s_lg + (P / GP) * DK + 4 * (P % GP)) = lgv[u];
-        }
-        if (r + 1 < rounds) __syncthreads();  // the last round's barrier is the range's
     }
+#pragma unroll
+    for (int x = 0; x < CPW; ++x)
+        *reinterpret_cast<float4 *>(s_lg + lgx(lane, CPW * wave + x)) = lv[x];
 
     // ---- LG range of the tree. With M its midpoint, q_i 2^{LG_i - M} and k_j 2^{M - LG_j}
     // stay within 2^{+-60} when the range is at most 120, and w_ij is then their dot
     // product: the intra term runs on matrix cores. Otherwise (very deep or very strongly
     // decayed trees) each ancestor pair is summed with its exact exponent.
     float lmin = __builtin_inff(), lmax = -__builtin_inff();
+    if (lane < n) {
 #pragma unroll
-    for (int u = 0; u < GPT; ++u) {
-        if ((tid + NT * u) / GP < n) {
-            lmin = fminf(lmin, fminf(fminf(lgv[u].x, lgv[u].y), fminf(lgv[u].z, lgv[u].w)));
-            lmax = fmaxf(lmax, fmaxf(fmaxf(lgv[u].x, lgv[u].y), fmaxf(lgv[u].z, lgv[u].w)));
+        for (int x = 0; x < CPW; ++x) {
+            lmin = fminf(lmin, fminf(fminf(lv[x].x, lv[x].y), fminf(lv[x].z, lv[x].w)));
+            lmax = fmaxf(lmax, fmaxf(fmaxf(lv[x].x, lv[x].y), fmaxf(lv[x].z, lv[x].w)));
         }
     }
     range_dpp_step<0x111, 0xf>(lmin, lmax);  // row_shr:1
@@ -466,10 +475,10 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
         for (int u = 0; u < CH / 8; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) qv[8 * u + e] = static_cast<float>(qp[u][e]);
-        const float *lgi = s_lg + min(pi, last) * DK + CH * psub;
+        const int ri = min(pi, last);
 #pragma unroll
         for (int c = 0; c < CH; c += 4) {
-            const float4 x = *reinterpret_cast<const float4 *>(lgi + c);
+            const float4 x = *reinterpret_cast<const float4 *>(s_lg + lgx(ri, (CH * psub + c) / 4));
             li[c] = x.x;
             li[c + 1] = x.y;
             li[c + 2] = x.z;
@@ -479,14 +488,14 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
         while (rest) {  // the same ancestors for the four lanes of a node
             const int j = __ffsll((unsigned long long)rest) - 1;
             rest &= rest - 1;
-            const float *lgj = s_lg + j * DK + CH * psub;
             const __bf16 *kj = s_k + j * DK + CH * psub;
             float acc = 0.f;
 #pragma unroll
             for (int c = 0; c < CH; c += 8) {
                 const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(kj + c);
-                const float4 x0 = *reinterpret_cast<const float4 *>(lgj + c);
-                const float4 x1 = *reinterpret_cast<const float4 *>(lgj + c + 4);
+                const float4 x0 = *reinterpret_cast<const float4 *>(s_lg + lgx(j, (CH * psub + c) / 4));
+                const float4 x1 =
+                    *reinterpret_cast<const float4 *>(s_lg + lgx(j, (CH * psub + c) / 4 + 1));
                 const float lj[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -520,9 +529,8 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
             if (share && (t / KH2) != hf) continue;  // the partner's k-step
-            const float *lgq = s_lg + qi * DK + 32 * t + 8 * g4;
-            const float4 x0 = *reinterpret_cast<const float4 *>(lgq);
-            const float4 x1 = *reinterpret_cast<const float4 *>(lgq + 4);
+            const float4 x0 = *reinterpret_cast<const float4 *>(s_lg + lgx(qi, 8 * t + 2 * g4));
+            const float4 x1 = *reinterpret_cast<const float4 *>(s_lg + lgx(qi, 8 * t + 2 * g4 + 1));
             const float lq[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -552,6 +560,12 @@ __global__ __launch_bounds__(kVecThreads * CG) void verify_vec_kernel(
         typedef __bf16 b4 __attribute__((ext_vector_type(4)));
         __bf16 *s_bh = reinterpret_cast<__bf16 *>(s_big);
         __bf16 *s_bl = s_bh + N * DK;
+        float4 lgv[GPT];  // LG entries of this thread's key factors: row P / GP, chunk P % GP
+#pragma unroll
+        for (int u = 0; u < GPT; ++u) {
+            const int P = tid + NT * u;
+            lgv[u] = *reinterpret_cast<const float4 *>(s_lg + lgx(P / GP, P % GP));
+        }
         __syncthreads();
         if (share) {
 #pragma unroll
