@@ -189,6 +189,9 @@ EDGE = [
     ("fp32_vector", dict(batch=3, heads=2, d_k=64, d_v=64, vector_gate=True, factor_dtype=torch.float32)),
     ("extreme_gates_scalar", dict(batch=4, heads=2, d_k=128, d_v=64, sizes=[64, 64, 30, 10], kind="deep", gate_shift=6.0, max_path=64)),
     ("extreme_gates_vector", dict(batch=3, heads=2, d_k=64, d_v=64, sizes=[64, 20, 64], kind="deep", vector_gate=True, gate_shift=6.0, max_path=64)),
+    # the same gates where two column groups share a workgroup (exact pair sums there too)
+    ("extreme_gates_vector_dv128", dict(batch=3, heads=2, d_k=128, d_v=128, sizes=[64, 20, 64], kind="deep", vector_gate=True, gate_shift=6.0, max_path=64)),
+    ("extreme_gates_vector_dk64_dv256", dict(batch=3, heads=2, d_k=64, d_v=256, sizes=[64, 33, 5], kind="deep", vector_gate=True, gate_shift=6.0, max_path=64)),
     ("single_nodes", dict(batch=6, heads=5, d_k=128, d_v=64, sizes=[1] * 6)),
     ("dk128_dv32", dict(batch=4, heads=3, d_k=128, d_v=32)),
     ("dk64_dv64", dict(batch=4, heads=3, d_k=64, d_v=64, sizes=[32, 17, 16, 5])),
