@@ -61,7 +61,7 @@ CASES = [
     ("many_ties", 4, 5, 20000, 64, dict(grid=2.0 ** -12), 0.05),
     ("flat_logits_many_ties", 2, 3, 50000, 64, dict(logit_std=0.0), 0.05),
     # nearly flat rows: the top keys lie within the threshold search's 16-bit resolution,
-    # so compactions keep many candidates (and may take the block-wide extraction path)
+    # so compactions keep many candidates (and may take the extraction path)
     ("near_flat_logits", 2, 3, 60000, 64, dict(logit_std=0.002), 0.05),
     ("slightly_flat_logits", 2, 3, 60000, 64, dict(logit_std=0.05), 0.05),
     ("vocab_10", 3, 3, 10, 64, {}, 0.01),
@@ -80,6 +80,35 @@ def test_build_tree_matches_oracle(bole, name, B, D, V, n_max, mk, alpha):
     if name == "flat_logits_many_ties":
         # uniform rows: every element ties, the ranks go by token id
         assert out["token"][:3].cpu().tolist() == [0, 1, 2]
+
+
+@pytest.mark.parametrize("order", ["ascending", "descending", "one_block"])
+def test_top_values_in_one_part_of_a_slice(bole, order):
+    """Rows whose largest probabilities all lie in one stretch of the vocabulary (sorted
+    rows, or one block of 1,000 tokens holding them): the top-64 step's threshold then
+    comes from one part of each slice while the others see only small values."""
+    B, D, V = 3, 4, 40000
+    m = W.make_marginals(81, B, D, V)
+    if order == "ascending":
+        m = np.sort(m, axis=-1)
+    elif order == "descending":
+        m = -np.sort(-m, axis=-1)
+    else:
+        # the 1,000 largest of each row moved, in random order, to tokens 17,000 .. 17,999
+        for b in range(B):
+            for d in range(D):
+                r = m[b, d]
+                top = np.argsort(-r, kind="stable")[:1000]
+                rest = np.setdiff1d(np.arange(V), top)
+                rng = np.random.default_rng(b * 100 + d)
+                row = np.empty_like(r)
+                row[17000:18000] = rng.permutation(r[top])
+                others = rest.copy()
+                rng.shuffle(others)
+                row[np.r_[0:17000, 18000:V]] = r[others]
+                m[b, d] = row
+    print(f"[case] top values {order} B={B} D={D} V={V}", flush=True)
+    run_and_compare(bole, np.ascontiguousarray(m), primer_cost(64), 64)
 
 
 def test_fixed_budget_without_cost(bole):

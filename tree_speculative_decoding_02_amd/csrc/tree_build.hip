@@ -22,7 +22,6 @@ namespace bole {
 
 constexpr int kTopK = 64;
 constexpr int kBuildThreads = 256;
-constexpr int kGatherCap = 1024;                         // candidates sorted in LDS
 constexpr int kMaxDepth = 32;
 constexpr int kMaxBudget = 64;
 
@@ -76,180 +75,182 @@ __device__ __forceinline__ void wave_merge64(uint32_t &k, int &i, uint32_t nk, i
 // ---- 1. top 64 of one vocabulary slice of one (sequence, position) row
 //
 // The workgroup streams its slice [lo, hi) in chunks of kChunk elements, the next chunk's
-// loads in flight while the current one is filtered: thread t holds elements
-// c0 + (j * 256 + t) * W + c (j < kChunkPerThread / W, c < W) as orderable keys. Only
-// elements at or above a running threshold theta are gathered into an LDS candidate
-// buffer. theta starts as the smallest, over the wavefronts, of the wavefront's 16th
-// largest thread maximum in the first chunk (at least 64 elements reach it), and rises
-// after the first chunk and whenever the buffer passes half full: it becomes the 64th
-// largest buffered key resolved to its top kThetaBits bits (a bitwise search, one barrier
-// a bit), and the candidates below it are dropped. theta never exceeds the 64th largest
-// key seen so far, so the buffer always holds the top 64. The
-// last step counts each candidate's rank and writes ranks below 64 in place. If one
-// chunk leaves more than kGatherCap candidates (many equal values at theta), 64 rounds
-// of block-wide extraction over the slice, read again, give the same list.
+// loads in flight while the current one is filtered, and each wavefront keeps candidates
+// of its own: wavefront w holds, of the chunk at c0, the elements c0 + kSub w + (64 j + l) W
+// + c of lane l (j < kChunkPerThread / W, c < W) as orderable keys, and gathers those at or
+// above a running threshold theta into its own LDS buffer (slots from a ballot; the count
+// is the same in every lane, so no atomics).
+//  - theta starts as the smallest, over the wavefronts, of each wavefront's 16th largest
+//    lane maximum in the first chunk (a 32-step ballot search; at least 64 elements reach
+//    it), the one barrier before the end.
+//  - A wavefront whose buffer passes half full raises theta to its 64th largest buffered
+//    key resolved to its top kThetaBits bits (a bitwise search), drops the candidates below
+//    it and publishes it in LDS; every wavefront takes the largest published value before
+//    each chunk. Each such value is at most the 64th largest key seen in the slice, so the
+//    slice's top 64 always stay in the buffers; a value read while it is being raised is
+//    an earlier, smaller one, which is as safe, so these exchanges need no barrier.
+//  - At the end each wavefront ranks its candidates and writes its best 64 to LDS, and
+//    wavefront 0 merges the four lists.
+// A wavefront whose buffer overflows (many keys equal to theta, such as uniform rows) takes
+// 64 rounds of extraction over its own elements, read again. (A first version shared one
+// buffer per workgroup, with a barrier per chunk and one per bit of each threshold search:
+// 57.8 us for the benchmark's 512 rows x 128,256.)
 constexpr int kChunkPerThread = 16;
-constexpr int kThetaBits = 16;  // key bits resolved by a compaction's threshold search
+constexpr int kThetaBits = 16;  // key bits resolved by a threshold search
 constexpr int kChunk = kBuildThreads * kChunkPerThread;  // 4096 elements
+constexpr int kSub = 64 * kChunkPerThread;              // 1024: a wavefront's part of a chunk
+constexpr int kWaveCap = 512;                           // candidates per wavefront
+
+// The 64th largest of the wavefront's J x W values per lane, resolved to its top
+// kThetaBits bits and never above it (0 when fewer than 64 values are nonzero).
+template <int J, int W, typename VT>
+__device__ __forceinline__ uint32_t wave_theta64(const VT (&v)[J]) {
+    uint32_t th = 0u;
+    for (int bit = 31; bit >= 32 - kThetaBits; --bit) {
+        const uint32_t cand = th | (1u << bit);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int e = 0; e < W; ++e) c += __popcll(__ballot(v[j][e] >= cand));
+        if (c >= kTopK) th = cand;
+    }
+    return th;
+}
 
 template <int W>
 __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
     const float *__restrict__ marginals, uint2 *__restrict__ lists, int V, int S, int slice_len) {
     constexpr int J = kChunkPerThread / W;
+    constexpr int R = kWaveCap / 64;  // buffer entries per lane
     typedef uint32_t uv __attribute__((ext_vector_type(W)));
-    __shared__ uint32_t s_k[2][kGatherCap];
-    __shared__ int s_i[2][kGatherCap];
-    __shared__ int s_cnt[2];
-    __shared__ uint32_t s_th4[4];
-    __shared__ int s_wc[2][4];
-    __shared__ uint32_t s_rk[4];
-    __shared__ int s_ri[4];
+    __shared__ uint32_t s_k[4][kWaveCap];
+    __shared__ int s_i[4][kWaveCap];
+    __shared__ uint32_t s_lk[4][kTopK];  // each wavefront's best 64, in rank order
+    __shared__ int s_li[4][kTopK];
+    __shared__ uint32_t s_th4[4];        // first chunk: each wavefront's 16th largest lane maximum
+    __shared__ uint32_t s_theta[4];      // each wavefront's published threshold
     const int t = threadIdx.x, lane = lane_id(), wave = t >> 6;
     const size_t row = blockIdx.x / S;
     const int slice = blockIdx.x - (int)row * S;
     const int lo = slice * slice_len, hi = min(V, lo + slice_len);
     const float *src = marginals + row * (size_t)V;
     uint2 *dst = lists + (size_t)blockIdx.x * kTopK;
+    uint32_t *const bk_s = s_k[wave];
+    int *const bi_s = s_i[wave];
 
+    // first element of load j of this lane, in this wavefront's part of the chunk at c0
+    auto elem = [&](int c0, int j) { return c0 + kSub * wave + (j * 64 + lane) * W; };
     // a chunk's raw bits (addresses clamped into the row)
     auto load = [&](int c0, uv (&x)[J]) {
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int e = c0 + (j * kBuildThreads + t) * W;
-            x[j] = __builtin_nontemporal_load(reinterpret_cast<const uv *>(src + (uint32_t)min(e, V - W)));
-        }
+        for (int j = 0; j < J; ++j)
+            x[j] = __builtin_nontemporal_load(
+                reinterpret_cast<const uv *>(src + (uint32_t)min(elem(c0, j), V - W)));
     };
-    // the keys of a chunk in place (0 outside the slice: only the last chunk masks), and
-    // the thread's largest
+    // the keys in place (0 outside the slice: only the last chunk masks), and the lane's
+    // largest
     auto keys = [&](int c0, uv (&x)[J]) -> uint32_t {
         uint32_t mx = 0u;
-        if (c0 + kChunk <= hi) {
+        const bool whole = c0 + kChunk <= hi;
 #pragma unroll
-            for (int j = 0; j < J; ++j)
+        for (int j = 0; j < J; ++j)
 #pragma unroll
-                for (int c = 0; c < W; ++c) {
-                    x[j][c] = bits2key(x[j][c]);
-                    mx = max(mx, x[j][c]);
-                }
-        } else {
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int e = c0 + (j * kBuildThreads + t) * W;
-#pragma unroll
-                for (int c = 0; c < W; ++c) {
-                    x[j][c] = e + c < hi ? bits2key(x[j][c]) : 0u;
-                    mx = max(mx, x[j][c]);
-                }
+            for (int c = 0; c < W; ++c) {
+                x[j][c] = (whole || elem(c0, j) + c < hi) ? bits2key(x[j][c]) : 0u;
+                mx = max(mx, x[j][c]);
             }
-        }
         return mx;
     };
 
-    int buf = 0;
-    if (t == 0) s_cnt[0] = 0;
+    int cnt = 0;  // candidates in this wavefront's buffer (the same in every lane)
+    uint32_t theta = 1u;
+    // gathers the keys >= theta of one chunk part; the count goes on past the capacity
+    // (the entries past it are not written), which marks an overflow
+    auto gather = [&](int c0, uv (&x)[J], uint32_t mx) {
+        if (!__ballot(mx >= theta)) return;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            int sbase = elem(c0, j);
+            asm volatile("" : "+v"(sbase));  // recomputed per load, not held in registers
+#pragma unroll
+            for (int c = 0; c < W; ++c) {
+                const bool take = x[j][c] >= theta;
+                const uint64_t m = __ballot(take);
+                if (m) {
+                    const int slot = cnt + (int)__builtin_amdgcn_mbcnt_hi(
+                                               (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    if (take && slot < kWaveCap) {
+                        bk_s[slot] = x[j][c];
+                        bi_s[slot] = sbase + c;
+                    }
+                    cnt += (int)__popcll(m);
+                }
+            }
+        }
+    };
+    // theta <- max(theta, the 64th largest buffered key resolved to kThetaBits bits); the
+    // candidates below it are dropped (read into registers first, so in place)
+    // (the kept entries move only toward the front: entry r of each lane is read before any
+    // write reaches its slot)
+    auto compact = [&]() {
+        uint32_t bk[R][1];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int x2 = lane + 64 * r;
+            bk[r][0] = x2 < cnt ? bk_s[x2] : 0u;
+        }
+        theta = max(theta, wave_theta64<R, 1>(bk));
+        if (lane == 0) s_theta[wave] = theta;
+        int nc = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int x2 = lane + 64 * r;
+            const bool keep = bk[r][0] >= theta;
+            const int ix = keep ? bi_s[x2] : 0;
+            const uint64_t m = __ballot(keep);
+            const int slot = nc + (int)__builtin_amdgcn_mbcnt_hi(
+                                      (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (keep) {
+                bk_s[slot] = bk[r][0];
+                bi_s[slot] = ix;
+            }
+            nc += (int)__popcll(m);
+        }
+        cnt = nc;
+    };
+    // one chunk part: false when the buffer overflowed
+    auto step = [&](int c0, uv (&x)[J], uint32_t mx) -> bool {
+        theta = max(max(theta, max(s_theta[0], s_theta[1])), max(s_theta[2], s_theta[3]));
+        gather(c0, x, mx);
+        if (cnt > kWaveCap) return false;
+        if (cnt > kWaveCap / 2) compact();
+        return true;
+    };
+
     uv A[J], B2[J];  // two chunk buffers, alternating
     load(lo, A);
     if (lo + kChunk < hi) load(lo + kChunk, B2);
     uint32_t mx0 = keys(lo, A);
     {
-        // the wavefront's 16th largest thread maximum in the first chunk, bit by bit
+        // the wavefront's 16th largest lane maximum in the first chunk, bit by bit
         uint32_t th = 0u;
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = th | (1u << bit);
             if (__popcll(__ballot(mx0 >= cand)) >= 16) th = cand;
         }
-        if (lane == 0) s_th4[wave] = th;
+        if (lane == 0) {
+            s_th4[wave] = th;
+            s_theta[wave] = 1u;
+        }
     }
     __syncthreads();
     // >= 1: a key at or above it is never the empty key
-    uint32_t theta = max(1u, min(min(s_th4[0], s_th4[1]), min(s_th4[2], s_th4[3])));
-
+    theta = max(1u, min(min(s_th4[0], s_th4[1]), min(s_th4[2], s_th4[3])));
     bool overflow = false;
-    // filters one chunk (keys already formed): gather, then compact when the buffer is
-    // half full (or past 2 x 64 at the slice's end); false when the buffer overflowed
-    auto filter = [&](int c0, uv (&x)[J], uint32_t mx) -> bool {
-        if (__ballot(mx >= theta)) {
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                int sbase = c0 + (j * kBuildThreads + t) * W;
-                asm volatile("" : "+v"(sbase));  // recomputed per slab, not held in registers
-#pragma unroll
-                for (int c = 0; c < W; ++c) {
-                    const bool take = x[j][c] >= theta;
-                    const uint64_t m = __ballot(take);
-                    if (m) {
-                        const int first = __builtin_ctzll(m);
-                        int base = 0;
-                        if (lane == first) base = atomicAdd(&s_cnt[buf], __popcll(m));
-                        base = __builtin_amdgcn_readlane(base, first);
-                        const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                                    (uint32_t)(m >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                        if (take && slot < kGatherCap) {
-                            s_k[buf][slot] = x[j][c];
-                            s_i[buf][slot] = sbase + c;
-                        }
-                    }
-                }
-            }
-        }
-        __syncthreads();
-        const int cnt = s_cnt[buf];
-        if (cnt > kGatherCap) return false;
-        if (cnt > kGatherCap / 2 || (c0 == lo && cnt > kTopK) ||
-            (c0 + kChunk >= hi && cnt > 2 * kTopK)) {
-            // theta <- the 64th largest buffered key, resolved to its top kThetaBits bits
-            // (so never above it: the buffer keeps the top 64, plus the few keys that share
-            // that prefix below them; the final ranks are exact either way); keep the
-            // candidates >= it
-            uint32_t bk[kGatherCap / kBuildThreads];
-#pragma unroll
-            for (int r = 0; r < kGatherCap / kBuildThreads; ++r) {
-                const int x2 = t + r * kBuildThreads;
-                bk[r] = x2 < cnt ? s_k[buf][x2] : 0u;
-            }
-            uint32_t th = 0u;
-            for (int bit = 31; bit >= 32 - kThetaBits; --bit) {
-                const uint32_t cand = th | (1u << bit);
-                int wc = 0;
-#pragma unroll
-                for (int r = 0; r < kGatherCap / kBuildThreads; ++r) wc += __popcll(__ballot(bk[r] >= cand));
-                if (lane == 0) s_wc[bit & 1][wave] = wc;
-                __syncthreads();
-                if (s_wc[bit & 1][0] + s_wc[bit & 1][1] + s_wc[bit & 1][2] + s_wc[bit & 1][3] >= kTopK)
-                    th = cand;
-            }
-            theta = max(theta, th);
-            if (t == 0) s_cnt[buf ^ 1] = 0;
-            __syncthreads();
-#pragma unroll
-            for (int r = 0; r < kGatherCap / kBuildThreads; ++r) {
-                const int x2 = t + r * kBuildThreads;
-                const bool keep = x2 < cnt && bk[r] >= theta;
-                const uint64_t m = __ballot(keep);
-                if (m) {
-                    const int first = __builtin_ctzll(m);
-                    int base = 0;
-                    if (lane == first) base = atomicAdd(&s_cnt[buf ^ 1], __popcll(m));
-                    base = __builtin_amdgcn_readlane(base, first);
-                    const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                                (uint32_t)(m >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    if (keep) {
-                        s_k[buf ^ 1][slot] = bk[r];
-                        s_i[buf ^ 1][slot] = s_i[buf][x2];
-                    }
-                }
-            }
-            __syncthreads();
-            buf ^= 1;
-        }
-        return true;
-    };
-
     for (int c0 = lo; c0 < hi; c0 += 2 * kChunk) {
         // chunk c0 in A (keys formed), chunk c0 + kChunk in flight in B2
-        if (!filter(c0, A, mx0)) {
+        if (!step(c0, A, mx0)) {
             overflow = true;
             break;
         }
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
         if (c1 >= hi) break;
         if (c1 + kChunk < hi) load(c1 + kChunk, A);
         const uint32_t mx1 = keys(c1, B2);
-        if (!filter(c1, B2, mx1)) {
+        if (!step(c1, B2, mx1)) {
             overflow = true;
             break;
         }
@@ -267,60 +268,67 @@ __global__ __launch_bounds__(kBuildThreads) void topk_slice_kernel(
     }
 
     if (!overflow) {
-        // each candidate's rank is the number of better candidates ((key, index) pairs
-        // are distinct, so ranks are too); ranks below 64 are written in place
-        const int cnt = s_cnt[buf];
-        for (int x = t; x < cnt; x += kBuildThreads) {
-            const uint32_t kx = s_k[buf][x];
-            const int ix = s_i[buf][x];
+        if (cnt > 2 * kTopK) compact();  // a short ranking
+        // each candidate's rank is the number of better ones ((key, index) pairs are
+        // distinct, so ranks are too)
+        for (int x = lane; x < cnt; x += 64) {
+            const uint32_t kx = bk_s[x];
+            const int ix = bi_s[x];
             int rank = 0;
-            for (int y = 0; y < cnt; ++y) rank += better(s_k[buf][y], s_i[buf][y], kx, ix) ? 1 : 0;
-            if (rank < kTopK) dst[rank] = make_uint2(kx, (uint32_t)ix);
+            for (int y = 0; y < cnt; ++y) rank += better(bk_s[y], bi_s[y], kx, ix) ? 1 : 0;
+            if (rank < kTopK) {
+                s_lk[wave][rank] = kx;
+                s_li[wave][rank] = ix;
+            }
         }
-        for (int r = cnt + t; r < kTopK; r += kBuildThreads) dst[r] = make_uint2(0u, 0x7fffffffu);
-        return;
+        for (int r = cnt + lane; r < kTopK; r += 64) {
+            s_lk[wave][r] = 0u;
+            s_li[wave][r] = 0x7fffffff;
+        }
+    } else {
+        // many ties: 64 rounds, each taking the best of this wavefront's elements not yet
+        // taken (ranking after the last one taken), read again
+        uint32_t lk = 0xffffffffu;
+        int li = -1;
+        for (int r = 0; r < kTopK; ++r) {
+            uint32_t bk2 = 0u;
+            int bi = 0x7fffffff;
+            for (int c0 = lo; c0 < hi; c0 += kChunk)
+                for (int j = 0; j < J; ++j)
+                    for (int c = 0; c < W; ++c) {
+                        const int e = elem(c0, j) + c;
+                        if (e < hi) {
+                            const uint32_t k = bits2key(__float_as_uint(src[e]));
+                            if (better(lk, li, k, e) && better(k, e, bk2, bi)) {
+                                bk2 = k;
+                                bi = e;
+                            }
+                        }
+                    }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const uint32_t pk = __shfl_xor(bk2, off, 64);
+                const int pi = __shfl_xor(bi, off, 64);
+                if (better(pk, pi, bk2, bi)) {
+                    bk2 = pk;
+                    bi = pi;
+                }
+            }
+            if (lane == 0) {
+                s_lk[wave][r] = bk2;
+                s_li[wave][r] = bk2 ? bi : 0x7fffffff;
+            }
+            lk = bk2;
+            li = bi;
+        }
     }
-
-    // many ties: 64 rounds, each taking the best element not yet taken (ranking after the
-    // last one taken), over the slice read again
-    uint32_t lk = 0xffffffffu;
-    int li = -1;
-    for (int r = 0; r < kTopK; ++r) {
-        uint32_t bk2 = 0u;
-        int bi = 0x7fffffff;
-        for (int e = lo + t; e < hi; e += kBuildThreads) {
-            const uint32_t k = bits2key(__float_as_uint(src[e]));
-            if (better(lk, li, k, e) && better(k, e, bk2, bi)) {
-                bk2 = k;
-                bi = e;
-            }
-        }
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t k = s_lk[0][lane];
+        int i = s_li[0][lane];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const uint32_t pk = __shfl_xor(bk2, off, 64);
-            const int pi = __shfl_xor(bi, off, 64);
-            if (better(pk, pi, bk2, bi)) {
-                bk2 = pk;
-                bi = pi;
-            }
-        }
-        if (lane == 0) {
-            s_rk[wave] = bk2;
-            s_ri[wave] = bi;
-        }
-        __syncthreads();
-        bk2 = s_rk[0];
-        bi = s_ri[0];
-#pragma unroll
-        for (int w = 1; w < 4; ++w)
-            if (better(s_rk[w], s_ri[w], bk2, bi)) {
-                bk2 = s_rk[w];
-                bi = s_ri[w];
-            }
-        __syncthreads();
-        if (t == 0) dst[r] = make_uint2(bk2, (uint32_t)(bk2 ? bi : 0x7fffffff));
-        lk = bk2;
-        li = bi;
+        for (int w = 1; w < 4; ++w) wave_merge64(k, i, s_lk[w][lane], s_li[w][lane]);
+        dst[lane] = make_uint2(k, (uint32_t)i);
     }
 }
 
