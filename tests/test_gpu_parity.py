@@ -325,8 +325,13 @@ def test_empty_batch_and_empty_trees(bole):
     torch.cuda.synchronize()
 
 
-def test_determinism(bole):
-    wl = W.make_config(2)
+@pytest.mark.parametrize("cid", [2, 3, 4], ids=["mamba2", "gla_vector", "ragged_fused"])
+def test_determinism(bole, cid):
+    """Two calls on the same inputs give bit-identical outputs and states: the scalar
+    one-wavefront launch, the vector-gate kernel (two column groups sharing their operands
+    through LDS) and the fused launch (row-split partial sums swapped through LDS)."""
+    wl = W.make_config(cid, n_layers=1)
+    print(f"[case] determinism config {cid}", flush=True)
     t = to_dev(wl)
     a, _ = gpu_verify(bole, t)
     b, _ = gpu_verify(bole, t)
