@@ -532,13 +532,16 @@ def probe_lib():
     lib.probe_verify_traffic_vector.argtypes = common + [ctypes.c_void_p]
     lib.probe_lazy_traffic_scalar.argtypes = ([ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 4
                                               + [ctypes.c_int] * 7 + [ctypes.c_void_p])
+    lib.probe_lazy_traffic_vector.argtypes = lib.probe_lazy_traffic_scalar.argtypes
     return lib
 
 
 def lazy_traffic_launch(lib, layers, wl, parent_offs, acc_idx, acc_len, stream):
     """A launcher for the memory-only kernel that moves exactly the lazy step's bytes for
     the layer stack (the same stack, trees and paths; the previous step's tree is this
-    step's, as in the benchmark). H0 is written back unchanged; out gets arbitrary values."""
+    step's, as in the benchmark), in the lazy launch's shape for scalar gates (d_k = 128,
+    d_v = 64) or per-channel gates (d_k = d_v = 128). H0 is written back unchanged; out
+    gets arbitrary values."""
     import ctypes
 
     class ProbeLayer(ctypes.Structure):
@@ -553,8 +556,10 @@ def lazy_traffic_launch(lib, layers, wl, parent_offs, acc_idx, acc_len, stream):
             wl.heads, wl.d_k, wl.d_v, wl.total_nodes, wl.total_nodes, int(acc_idx.shape[1]),
             ctypes.c_void_p(stream.cuda_stream))
 
+    probe = lib.probe_lazy_traffic_vector if wl.vector_gate else lib.probe_lazy_traffic_scalar
+
     def launch():
-        rc = lib.probe_lazy_traffic_scalar(*args)
+        rc = probe(*args)
         if rc != 0:
             raise RuntimeError(f"lazy traffic probe failed: {rc}")
     launch.keep = arr
@@ -656,7 +661,7 @@ def config_sweep(dev, reps=20, configs=(1, 2, 3, 4, 5)):
                                 nbytes["verify"], reps)
         if ref is not None:
             rec["verify_traffic_reference"] = ref
-        if ref is not None and not wl.vector_gate:
+        if ref is not None:
             # the lazy step's bytes, moved by the memory-only kernel on the same sets
             lfs = [lazy_traffic_launch(plib, [dict(H0=x["H0"], q=x["q"], k=x["k"], v=x["v"],
                                                    gate=x["gate"], out=x["out"], prev_k=x["k"],

@@ -39,19 +39,19 @@ def test_library_exports_every_declared_symbol():
 
 def test_probe_library_is_separate_and_exports_its_launchers():
     """The benchmark's memory-only reference kernels live in their own library: it
-    exports exactly its three launchers, and libbole.so exports none of them."""
+    exports exactly its four launchers, and libbole.so exports none of them."""
     path = os.path.join(os.path.dirname(bole.LIB_PATH), "libbole_probe.so")
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
                          check=True).stdout
     probes = {line.split()[-1] for line in out.splitlines() if "probe_" in line}
     assert probes == {"probe_verify_traffic_scalar", "probe_verify_traffic_vector",
-                      "probe_lazy_traffic_scalar"}
+                      "probe_lazy_traffic_scalar", "probe_lazy_traffic_vector"}
     main = subprocess.run(["nm", "-D", "--defined-only", bole.LIB_PATH], capture_output=True,
                           text=True, check=True).stdout
     assert "probe_" not in main
     lib = ctypes.CDLL(path)
     assert lib.probe_verify_traffic_scalar and lib.probe_verify_traffic_vector
-    assert lib.probe_lazy_traffic_scalar
+    assert lib.probe_lazy_traffic_scalar and lib.probe_lazy_traffic_vector
 
 
 def _dims(**kw):

@@ -292,6 +292,37 @@ def test_traffic_probe_writes_exactly_the_tree_rows(vector):
     assert (written == want).all() and (untouched == ~want).all()
 
 
+def test_vector_lazy_traffic_probe_keeps_the_state():
+    """The per-channel-gate lazy-step reference (d_k = d_v = 128) writes every H0 slice back
+    unchanged and every column of the out rows of every valid tree, on a two-layer stack."""
+    import bench
+    d = torch.device("cuda:0")
+    kw = dict(batch=5, heads=3, d_k=128, d_v=128, sizes=[64, 9, 0, 33, 17], vector_gate=True)
+    wl = W.make_random(911, **kw)
+    g = lambda x: torch.as_tensor(np.ascontiguousarray(x)).to(d)
+    layers = []
+    for l in range(2):
+        lay = wl.layers[0] if l == 0 else W.make_random(912, **kw).layers[0]
+        y = dict(H0=lay.H0.to(d).clone(), q=lay.q.to(d), k=lay.k.to(d), v=lay.v.to(d),
+                 gate=lay.gate.to(d),
+                 out=torch.full((wl.total_nodes, 3, 128), 7.0, dtype=torch.float32, device=d))
+        y.update(prev_k=y["k"], prev_v=y["v"], prev_gate=y["gate"])
+        layers.append(y)
+    H_before = [y["H0"].clone() for y in layers]
+    offs, ai, al = g(wl.node_offsets), g(wl.accepted_idx), g(wl.accepted_len)
+    st = torch.cuda.current_stream()
+    print("[case] vector lazy traffic probe, 2 layers", flush=True)
+    launch = bench.lazy_traffic_launch(bench.probe_lib(), layers, wl, offs, ai, al, st)
+    launch()
+    torch.cuda.synchronize()
+    for y, H in zip(layers, H_before):
+        assert torch.equal(y["H0"], H)
+        # each column group writes its half of every row: no 64-column half left untouched
+        halves = y["out"].reshape(wl.total_nodes, 3, 2, 64)
+        assert (halves != 7.0).any(dim=3).all()
+    assert int(wl.accepted_len.max()) > 0
+
+
 def test_lazy_traffic_probe_keeps_the_state():
     """The lazy-step memory-only reference writes every H0 slice back unchanged and the
     out rows of every valid tree, on a two-layer stack with paths of several lengths."""

@@ -270,6 +270,107 @@ __global__ __launch_bounds__(256) void lazy_traffic(const ProbeTable t,
     }
 }
 
+// Lazy-step traffic with per-channel gates (d_k = d_v = 128), in the vector-gate kernel's
+// lazy launch shape: one 256-thread workgroup per (unit, 64-column group), the two groups
+// of a unit 8 workgroups apart (slots of 8 units). Each reads its 32 KB half of the H_0
+// slice, the path's gate and k rows and its half of their v rows, and the tree's gate, q and
+// k rows and its half of the v rows; it writes its H_0 half back (the values read) when the
+// path is not empty, then its half of the out rows. The rows both groups read take plain
+// loads, as in the kernel, so the second read can come from L2. blockIdx.y = layer.
+__global__ __launch_bounds__(256) void vector_lazy_traffic(const ProbeTable t,
+                                                           const int32_t *__restrict__ offs,
+                                                           const int32_t *__restrict__ poffs,
+                                                           const int32_t *__restrict__ acc_idx,
+                                                           const int32_t *__restrict__ acc_len,
+                                                           int max_path, int H, int U, int T, int PT) {
+    constexpr int DK = 128, DV = 128, CW = 64, NT = 256;
+    constexpr int PPN = DK / 4 + DK / 8 + CW / 8;  // path pieces per node: gate, k, v half
+    const ProbeLayer &ly = t.l[blockIdx.y];
+    const int tid = threadIdx.x;
+    const int slot = blockIdx.x >> 3, cg = slot & 1;
+    const int unit = (slot >> 1) * 8 + (blockIdx.x & 7);
+    if (unit >= U) return;
+    const int b = unit / H, h = unit - b * H;
+    const int c0 = cg * CW;
+    const Tree tr = tree_of(offs, b, T);
+    const Tree pt = tree_of(poffs, b, PT);
+    const int L0 = acc_len[b];
+    const int L = (pt.n > 0 && L0 > 0 && L0 <= max_path && L0 <= pt.n) ? L0 : 0;
+    const int32_t *ai = acc_idx + (size_t)b * max_path;
+    const uint32_t rq = (uint32_t)H * DK, rv = (uint32_t)H * DV;
+    float *hu = ly.H0 + (size_t)unit * DK * DV + c0;
+    u32x4 hr[8], r[18];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // the H_0 half: row p / 16, piece p % 16
+        const int p = tid + NT * u;
+        hr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hu + (uint32_t)(p / 16) * DV + 4 * (p % 16)));
+    }
+    u32x4 pacc = u32x4{0u, 0u, 0u, 0u};
+    for (int p = tid; p < L * PPN; p += NT) {  // the path's pieces
+        const int m = p / PPN, part = p % PPN;
+        const int x = ai[m];
+        if (x >= 0 && x < pt.n) {
+            const size_t row = (size_t)(pt.lo + x) * H + h;
+            pacc ^= part < DK / 4
+                        ? *reinterpret_cast<const u32x4 *>(ly.prev_gate + row * DK + 4 * part)
+                    : part < DK / 4 + DK / 8
+                        ? *reinterpret_cast<const u32x4 *>(ly.prev_k + row * DK + 8 * (part - DK / 4))
+                        : __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                              ly.prev_v + row * DV + c0 + 8 * (part - DK / 4 - DK / 8)));
+        }
+    }
+    const int n = tr.n;
+    const float *gu = ly.gate + (size_t)tr.lo * rq + (size_t)h * DK;
+    const uint16_t *qu = ly.q + (size_t)tr.lo * rq + (size_t)h * DK;
+    const uint16_t *ku = ly.k + (size_t)tr.lo * rq + (size_t)h * DK;
+    const uint16_t *vu = ly.v + (size_t)tr.lo * rv + (size_t)h * DV + c0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // gate: 32 pieces per row
+        const int p = tid + NT * u;
+        r[u] = p / 32 < n ? *reinterpret_cast<const u32x4 *>(gu + (uint32_t)(p / 32) * rq + 4 * (p % 32))
+                          : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // q and k: 16 pieces per row
+        const int p = tid + NT * u;
+        const bool in = p / 16 < n;
+        r[8 + u] = in ? *reinterpret_cast<const u32x4 *>(qu + (uint32_t)(p / 16) * rq + 8 * (p % 16))
+                      : u32x4{0u, 0u, 0u, 0u};
+        r[12 + u] = in ? *reinterpret_cast<const u32x4 *>(ku + (uint32_t)(p / 16) * rq + 8 * (p % 16))
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // the v half: 8 pieces per row
+        const int p = tid + NT * u;
+        r[16 + u] = p / 8 < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                                    vu + (uint32_t)(p / 8) * rv + 8 * (p % 8)))
+                              : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (L > 0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            // the values read, made opaque to the compiler (a store of a value just loaded
+            // from the same address would otherwise be dropped)
+            const int p = tid + NT * u;
+            u32x4 x = hr[u];
+            asm volatile("" : "+v"(x));
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(hu + (uint32_t)(p / 16) * DV + 4 * (p % 16)));
+        }
+    }
+    u32x4 acc = pacc;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= hr[u];
+#pragma unroll
+    for (int u = 0; u < 18; ++u) acc ^= r[u];
+    float *ou = ly.out + (size_t)tr.lo * rv + (size_t)h * DV + c0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // the out half: 16 pieces per row
+        const int p = tid + NT * u;
+        if (p / 16 < n)
+            __builtin_nontemporal_store(acc, reinterpret_cast<u32x4 *>(ou + (uint32_t)(p / 16) * rv + 4 * (p % 16)));
+    }
+}
+
 bool aligned16(const void *a, const void *b, const void *c, const void *d, const void *e) {
     return ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
              reinterpret_cast<uintptr_t>(c) | reinterpret_cast<uintptr_t>(d) |
@@ -354,5 +455,31 @@ PROBE_API int probe_lazy_traffic_scalar(const ProbeLayer *layers, int nl,
     lazy_traffic<<<dim3((U + 1) / 2, nl), 256, 0, stream>>>(t, node_offsets, prev_offsets,
                                                             accepted_idx, accepted_len, max_path,
                                                             heads, U, total_nodes, prev_total_nodes);
+    return (int)hipGetLastError();
+}
+
+// Lazy-step traffic with per-channel gates, nl <= 16 layers sharing the trees and paths, one
+// launch: as probe_lazy_traffic_scalar with d_k = d_v = 128 and gate, prev_gate [T, H, 128]
+// fp32 (H0 [B, H, 128, 128], q and k [T, H, 128], v [T, H, 128], out [T, H, 128]).
+PROBE_API int probe_lazy_traffic_vector(const ProbeLayer *layers, int nl,
+                                        const int32_t *node_offsets, const int32_t *prev_offsets,
+                                        const int32_t *accepted_idx, const int32_t *accepted_len,
+                                        int batch, int heads, int d_k, int d_v, int total_nodes,
+                                        int prev_total_nodes, int max_path, hipStream_t stream) {
+    if (d_k != 128 || d_v != 128 || batch < 0 || heads <= 0 || nl < 1 || nl > kProbeLayers ||
+        max_path < 1 || max_path > 64 || total_nodes < 0 || prev_total_nodes < 0)
+        return -1;
+    ProbeTable t = {};
+    for (int l = 0; l < nl; ++l) {
+        const ProbeLayer &y = layers[l];
+        if (!aligned16(y.H0, y.q, y.k, y.v, y.out) || !aligned16(y.prev_k, y.prev_v, y.gate, y.prev_gate, y.H0))
+            return -1;
+        t.l[l] = y;
+    }
+    const int U = batch * heads;
+    if (U == 0) return 0;
+    vector_lazy_traffic<<<dim3(((U + 7) / 8) * 16, nl), 256, 0, stream>>>(
+        t, node_offsets, prev_offsets, accepted_idx, accepted_len, max_path, heads, U, total_nodes,
+        prev_total_nodes);
     return (int)hipGetLastError();
 }
