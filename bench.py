@@ -715,6 +715,14 @@ def vector_stack(dev, stream, reps, n_layers=8):
         rec[name] = {"median_us": us, "bytes": n_layers * nb, "GB_s": gbs,
                      "frac_hbm_peak": gbs / HBM_PEAK_GBS,
                      "nodes_per_s": n_layers * wl.total_nodes / (us * 1e-6)}
+    # the stack's lazy-step bytes moved by the memory-only kernel, one launch of 8 layers
+    lref = lazy_traffic_launch(probe_lib(), layers, wl, offs, ai, al, stream)
+    lus = time_rotated([lref] * 4, stream, reps)
+    lgbs = rec["lazy"]["bytes"] / (lus * 1e3)
+    rec["lazy_traffic_reference"] = {
+        "median_us": lus, "GB_s": lgbs, "frac_hbm_peak": lgbs / HBM_PEAK_GBS,
+        "lazy_rate_of_reference": lus / rec["lazy"]["median_us"],
+        "what": "memory-only kernel moving the lazy stack's bytes in the same row pieces"}
     print(json.dumps(rec), flush=True)
 
 
