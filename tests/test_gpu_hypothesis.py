@@ -40,3 +40,50 @@ def test_drawn_workloads_meet_the_oracle_bars(bole, data):
     wl = W.make_random(seed, batch=B, heads=H, d_k=dk, d_v=dv, sizes=sizes, kind=kind,
                        vector_gate=vec, factor_dtype=dtype, max_path=64, gate_shift=shift)
     check_workload(bole, wl, paths=("auto",))
+
+
+@settings(max_examples=25, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.function_scoped_fixture, HealthCheck.too_slow])
+@given(st.data())
+def test_drawn_lazy_steps_match_two_calls_and_the_oracle(bole, data):
+    """The one-pass decode step (the previous step's commit folded into this step's
+    verify) on drawn previous trees, accepted paths and current trees: statuses and path
+    rows as the two separate calls, bit for bit; states within 1e-6 and outputs within
+    1e-5 of them; and within the bars of the oracle's commit then verify."""
+    import numpy as np
+
+    import oracle
+    from tests.helpers import rel_err_rows, rel_err_states
+    from tests.test_gpu_parity import TOL, _lazy_vs_separate, to_dev
+    B = data.draw(st.integers(1, 5), label="batch")
+    H = data.draw(st.integers(1, 3), label="heads")
+    vec = data.draw(st.booleans(), label="vector_gate")
+    dk = data.draw(st.sampled_from([64, 128]), label="d_k")
+    dv = data.draw(st.sampled_from([32, 64, 128]), label="d_v")
+    dtype = data.draw(st.sampled_from([torch.bfloat16, torch.bfloat16, torch.float32]), label="dtype")
+    prev_sizes = data.draw(st.lists(st.integers(0, 64), min_size=B, max_size=B), label="prev_sizes")
+    cur_sizes = data.draw(st.lists(st.integers(0, 64), min_size=B, max_size=B), label="cur_sizes")
+    kinds = ["random", "chain", "deep", "bestfirst"]
+    kp, kc = data.draw(st.sampled_from(kinds), label="prev_kind"), data.draw(st.sampled_from(kinds), label="cur_kind")
+    seed = data.draw(st.integers(0, 10 ** 6), label="seed")
+    le32 = max(prev_sizes) <= 32 and data.draw(st.booleans(), label="prev_trees_le_32")
+    print(f"[case] drawn lazy B={B} H={H} vec={vec} dk={dk} dv={dv} dtype={dtype} prev={prev_sizes} "
+          f"{kp} cur={cur_sizes} {kc} le32={le32} seed={seed}", flush=True)
+    common = dict(batch=B, heads=H, d_k=dk, d_v=dv, vector_gate=vec, factor_dtype=dtype, max_path=64)
+    wp = W.make_random(seed, sizes=prev_sizes, kind=kp, **common)
+    wc = W.make_random(seed + 1, sizes=cur_sizes, kind=kc, **common)
+    tp, tc = to_dev(wp), to_dev(wc)
+    (Ha, oa, psa, pna, sa), (Hb, ob, psb, pnb, sb) = _lazy_vs_separate(bole, tp, tc, prev_trees_le_32=le32)
+    np.testing.assert_array_equal(psb, psa)
+    np.testing.assert_array_equal(pnb, pna)
+    np.testing.assert_array_equal(sb, sa)
+    assert rel_err_states(Hb.astype(np.float64), Ha.astype(np.float64)) <= 1e-6
+    assert rel_err_rows(ob.astype(np.float64), oa.astype(np.float64)) <= 1e-5
+    lp, lc = wp.layers[0], wc.layers[0]
+    Href, pnref, pstref = oracle.commit_serial(lp.H0, lp.k, lp.v, lp.gate, wp.parent, wp.node_offsets,
+                                               wp.accepted_idx, wp.accepted_len, vec)
+    oref, stref = oracle.verify_serial(Href, lc.q, lc.k, lc.v, lc.gate, wc.parent, wc.node_offsets, vec)
+    assert psb.tolist() == pstref.tolist() and sb.tolist() == stref.tolist()
+    np.testing.assert_array_equal(pnb, pnref)
+    assert rel_err_states(Hb.astype(np.float64), Href) <= TOL[dtype]
+    assert rel_err_rows(ob.astype(np.float64), oref) <= TOL[dtype]
