@@ -87,3 +87,56 @@ def test_drawn_lazy_steps_match_two_calls_and_the_oracle(bole, data):
     np.testing.assert_array_equal(pnb, pnref)
     assert rel_err_states(Hb.astype(np.float64), Href) <= TOL[dtype]
     assert rel_err_rows(ob.astype(np.float64), oref) <= TOL[dtype]
+
+
+@settings(max_examples=25, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.function_scoped_fixture, HealthCheck.too_slow])
+@given(st.data())
+def test_drawn_builder_inputs_match_the_oracle(bole, data):
+    """The draft-tree builder on drawn marginals: vocabularies from 1 token up and around
+    the 4,096-token chunks, flat, tied and peaked rows, any budget, with and without a cost
+    table; trees, tokens, path scores and speedups bit for bit the oracle's."""
+    from tests.test_gpu_tree_build import primer_cost, run_and_compare
+    B = data.draw(st.integers(1, 6), label="batch")
+    D = data.draw(st.integers(1, 8), label="depth")
+    V = data.draw(st.one_of(st.sampled_from([1, 2, 10, 63, 64, 65, 4095, 4096, 4097, 8192, 12289]),
+                            st.integers(1, 40000)), label="vocab")
+    n_max = data.draw(st.integers(1, 64), label="n_max")
+    std = data.draw(st.sampled_from([0.0, 0.01, 0.5, 2.0, 4.0]), label="logit_std")
+    grid = data.draw(st.sampled_from([None, None, 2.0 ** -10, 2.0 ** -14]), label="grid")
+    alpha = data.draw(st.sampled_from([0.0, 0.02, 0.1]), label="alpha")
+    fixed = data.draw(st.booleans(), label="fixed")
+    seed = data.draw(st.integers(0, 10 ** 6), label="seed")
+    print(f"[case] drawn builder B={B} D={D} V={V} n_max={n_max} std={std} grid={grid} "
+          f"alpha={alpha} fixed={fixed} seed={seed}", flush=True)
+    m = W.make_marginals(seed, B, D, V, logit_std=std, grid=grid)
+    run_and_compare(bole, m, None if fixed else primer_cost(n_max, alpha), n_max, fixed=fixed)
+
+
+@settings(max_examples=25, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.function_scoped_fixture, HealthCheck.too_slow])
+@given(st.data())
+def test_drawn_trees_accept_as_the_oracle(bole, data):
+    """Tree acceptance on drawn trees, vocabularies, path limits, agreement and peakedness,
+    greedy and sampling: statuses equal; accepted paths, lengths and bonus tokens bit for
+    bit wherever the oracle's smallest decision margin is clear (every greedy tree)."""
+    import numpy as np
+
+    from tests.test_gpu_tree_accept import make_case, run
+    B = data.draw(st.integers(1, 6), label="batch")
+    sizes = data.draw(st.lists(st.integers(0, 64), min_size=B, max_size=B), label="sizes")
+    kind = data.draw(st.sampled_from(["random", "chain", "star", "deep", "bestfirst"]), label="kind")
+    V = data.draw(st.one_of(st.sampled_from([64, 65, 4096, 4097, 131073]), st.integers(64, 40000)), label="vocab")
+    max_path = data.draw(st.integers(1, 64), label="max_path")
+    sample = data.draw(st.booleans(), label="sample")
+    agree = data.draw(st.sampled_from([0.0, 0.7, 1.0]), label="agree")
+    peaked = data.draw(st.sampled_from([0.5, 2.0, 4.0]), label="peaked")
+    seed = data.draw(st.integers(0, 10 ** 6), label="seed")
+    print(f"[case] drawn accept B={B} sizes={sizes} {kind} V={V} max_path={max_path} sample={sample} "
+          f"agree={agree} peaked={peaked} seed={seed}", flush=True)
+    c = make_case(seed, B, V, sizes, kind, agree=agree, peaked=peaked)
+    got, ref = run(bole, c, max_path, sample)
+    np.testing.assert_array_equal(got["status"], ref["status"])
+    clear = ref["margin"] > 1e-9 if sample else np.ones(B, bool)
+    for k in ("accepted_idx", "accepted_len", "bonus"):
+        np.testing.assert_array_equal(got[k][clear], ref[k][clear], err_msg=k)
