@@ -1,6 +1,7 @@
 """GPU parity on workloads drawn by hypothesis: the batch, head count, tree sizes and kinds,
-widths, gate kind, factor dtype and decay strength are all drawn (derandomised, so every
-run draws the same cases), and each workload must meet the oracle's bars through the C
+widths, gate kind, factor dtype, decay strength and gate range are all drawn
+(derandomised, so every run draws the same cases), and each workload must meet the
+oracle's bars through the C
 ABI: statuses, path gathers and topology bit-exact, outputs and committed states within
 2e-3 (bf16 factors) or 1e-5 (fp32), normwise per row and per (sequence, head)."""
 import pytest
@@ -34,11 +35,15 @@ def test_drawn_workloads_meet_the_oracle_bars(bole, data):
     sizes = data.draw(st.lists(st.integers(0, 64), min_size=B, max_size=B), label="sizes")
     dtype = data.draw(st.sampled_from([torch.bfloat16, torch.float32]), label="dtype")
     shift = data.draw(st.sampled_from([0.0, 0.0, 3.0]), label="gate_shift")
+    # gates up to about 2.5 (state growing along a path), or all exactly 1
+    scale = data.draw(st.sampled_from([1.0, 1.0, 2.5]), label="gate_scale")
+    value = data.draw(st.sampled_from([None, None, None, 1.0]), label="gate_value")
     seed = data.draw(st.integers(0, 10 ** 6), label="seed")
     print(f"[case] drawn B={B} H={H} vec={vec} dk={dk} dv={dv} kind={kind} sizes={sizes} "
-          f"dtype={dtype} shift={shift} seed={seed}", flush=True)
+          f"dtype={dtype} shift={shift} scale={scale} value={value} seed={seed}", flush=True)
     wl = W.make_random(seed, batch=B, heads=H, d_k=dk, d_v=dv, sizes=sizes, kind=kind,
-                       vector_gate=vec, factor_dtype=dtype, max_path=64, gate_shift=shift)
+                       vector_gate=vec, factor_dtype=dtype, max_path=64, gate_shift=shift,
+                       gate_scale=scale, gate_value=value)
     check_workload(bole, wl, paths=("auto",))
 
 
