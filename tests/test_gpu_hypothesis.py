@@ -1,9 +1,9 @@
 """GPU parity on workloads drawn by hypothesis: the batch, head count, tree sizes and kinds,
 widths, gate kind, factor dtype, decay strength and gate range are all drawn
 (derandomised, so every run draws the same cases), and each workload must meet the
-oracle's bars through the C
-ABI: statuses, path gathers and topology bit-exact, outputs and committed states within
-2e-3 (bf16 factors) or 1e-5 (fp32), normwise per row and per (sequence, head)."""
+oracle's bars through the C ABI: statuses, path gathers and topology bit-exact, outputs and
+committed states within 2e-3 (bf16 factors) or 1e-5 (fp32), normwise per row and per
+(sequence, head)."""
 import pytest
 import torch
 from hypothesis import HealthCheck, given, settings, strategies as st
