@@ -145,3 +145,27 @@ def test_drawn_trees_accept_as_the_oracle(bole, data):
     clear = ref["margin"] > 1e-9 if sample else np.ones(B, bool)
     for k in ("accepted_idx", "accepted_len", "bonus"):
         np.testing.assert_array_equal(got[k][clear], ref[k][clear], err_msg=k)
+
+
+@settings(max_examples=15, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.function_scoped_fixture, HealthCheck.too_slow])
+@given(st.data())
+def test_drawn_layer_stacks_equal_layer_by_layer(bole, data):
+    """Layer stacks (verify, commit and the lazy step, up to 20 layers, so past one
+    launch's 16) on drawn shapes and trees: bit for bit the single-layer calls on every
+    layer, and the lazy stack within the oracle's bars."""
+    from tests.test_gpu_parity import test_layer_stack_equals_layer_by_layer
+    n_layers = data.draw(st.integers(1, 20), label="layers")
+    B = data.draw(st.integers(1, 5), label="batch")
+    kw = dict(batch=B, heads=data.draw(st.integers(1, 4), label="heads"),
+              d_k=data.draw(st.sampled_from([64, 128]), label="d_k"),
+              d_v=data.draw(st.sampled_from([32, 64, 128]), label="d_v"),
+              sizes=data.draw(st.lists(st.integers(0, 64), min_size=B, max_size=B), label="sizes"),
+              kind=data.draw(st.sampled_from(["random", "chain", "deep", "bestfirst"]), label="kind"),
+              vector_gate=data.draw(st.booleans(), label="vector_gate"),
+              factor_dtype=data.draw(st.sampled_from([torch.bfloat16, torch.bfloat16, torch.float32]),
+                                     label="dtype"),
+              max_path=64)
+    name = f"drawn_stack_{data.draw(st.integers(0, 10 ** 6), label='name')}"
+    print(f"[case] drawn stack {name} layers={n_layers} {kw}", flush=True)
+    test_layer_stack_equals_layer_by_layer(bole, name, n_layers, kw)
