@@ -4,9 +4,21 @@ widths, gate kind, factor dtype, decay strength and gate range are all drawn
 oracle's bars through the C ABI: statuses, path gathers and topology bit-exact, outputs and
 committed states within 2e-3 (bf16 factors) or 1e-5 (fp32), normwise per row and per
 (sequence, head)."""
+import os
+
 import pytest
 import torch
 from hypothesis import HealthCheck, given, settings, strategies as st
+
+# BOLE_DRAWS=n: n times as many cases, drawn afresh on each run (a wider search than the
+# fixed cases the suite runs by default)
+_SCALE = int(os.environ.get("BOLE_DRAWS", "0"))
+
+
+def drawn(n):
+    return settings(max_examples=n * max(1, _SCALE), deadline=None, derandomize=_SCALE == 0,
+                    database=None,
+                    suppress_health_check=[HealthCheck.function_scoped_fixture, HealthCheck.too_slow])
 
 import workloads as W
 from tests.test_gpu_parity import check_workload
@@ -22,8 +34,7 @@ def bole():
     return b
 
 
-@settings(max_examples=30, deadline=None, derandomize=True, database=None,
-          suppress_health_check=[HealthCheck.function_scoped_fixture, HealthCheck.too_slow])
+@drawn(30)
 @given(st.data())
 def test_drawn_workloads_meet_the_oracle_bars(bole, data):
     B = data.draw(st.integers(1, 6), label="batch")
@@ -47,8 +58,7 @@ def test_drawn_workloads_meet_the_oracle_bars(bole, data):
     check_workload(bole, wl, paths=("auto",))
 
 
-@settings(max_examples=25, deadline=None, derandomize=True, database=None,
-          suppress_health_check=[HealthCheck.function_scoped_fixture, HealthCheck.too_slow])
+@drawn(25)
 @given(st.data())
 def test_drawn_lazy_steps_match_two_calls_and_the_oracle(bole, data):
     """The one-pass decode step (the previous step's commit folded into this step's
@@ -94,8 +104,7 @@ def test_drawn_lazy_steps_match_two_calls_and_the_oracle(bole, data):
     assert rel_err_rows(ob.astype(np.float64), oref) <= TOL[dtype]
 
 
-@settings(max_examples=25, deadline=None, derandomize=True, database=None,
-          suppress_health_check=[HealthCheck.function_scoped_fixture, HealthCheck.too_slow])
+@drawn(25)
 @given(st.data())
 def test_drawn_builder_inputs_match_the_oracle(bole, data):
     """The draft-tree builder on drawn marginals: vocabularies from 1 token up and around
@@ -118,8 +127,7 @@ def test_drawn_builder_inputs_match_the_oracle(bole, data):
     run_and_compare(bole, m, None if fixed else primer_cost(n_max, alpha), n_max, fixed=fixed)
 
 
-@settings(max_examples=25, deadline=None, derandomize=True, database=None,
-          suppress_health_check=[HealthCheck.function_scoped_fixture, HealthCheck.too_slow])
+@drawn(25)
 @given(st.data())
 def test_drawn_trees_accept_as_the_oracle(bole, data):
     """Tree acceptance on drawn trees, vocabularies, path limits, agreement and peakedness,
@@ -147,8 +155,7 @@ def test_drawn_trees_accept_as_the_oracle(bole, data):
         np.testing.assert_array_equal(got[k][clear], ref[k][clear], err_msg=k)
 
 
-@settings(max_examples=15, deadline=None, derandomize=True, database=None,
-          suppress_health_check=[HealthCheck.function_scoped_fixture, HealthCheck.too_slow])
+@drawn(15)
 @given(st.data())
 def test_drawn_layer_stacks_equal_layer_by_layer(bole, data):
     """Layer stacks (verify, commit and the lazy step, up to 20 layers, so past one
