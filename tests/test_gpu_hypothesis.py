@@ -55,7 +55,9 @@ def test_drawn_workloads_meet_the_oracle_bars(bole, data):
     wl = W.make_random(seed, batch=B, heads=H, d_k=dk, d_v=dv, sizes=sizes, kind=kind,
                        vector_gate=vec, factor_dtype=dtype, max_path=64, gate_shift=shift,
                        gate_scale=scale, gate_value=value)
-    check_workload(bole, wl, paths=("auto",))
+    # the caller's 32-node budget (its own launch shapes) when every tree fits it
+    le32 = max(sizes) <= 32 and data.draw(st.booleans(), label="trees_le_32")
+    check_workload(bole, wl, paths=("auto",), trees_le_32=le32)
 
 
 @drawn(25)
