@@ -1,7 +1,8 @@
 """Properties of the HIP path that the mathematics fixes, checked on the GPU itself (the
 same properties pin the oracle on the CPU): invariance under a topological relabelling
 of the tree, homogeneity in (H0, v), additivity in H0, a vector gate with equal channels
-against the scalar gate, and identical siblings. Each compares GPU outputs with GPU
+against the scalar gate, identical siblings, and a new leaf that leaves every other output
+as it was. Each compares GPU outputs with GPU
 outputs through the C ABI, so a kernel-only mistake that the oracle comparison could
 absorb within its tolerance still has to keep these relations."""
 import numpy as np
@@ -122,3 +123,33 @@ def test_identical_siblings_have_identical_outputs(bole):
     out = run(bole, lay.H0, q, k, v, gate, parent, wl.node_offsets)
     for x, y in pairs:
         assert rel_err_rows(out[y].numpy(), out[x].numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("vector_gate", [False, True])
+def test_a_new_leaf_changes_no_other_output(bole, vector_gate):
+    """A node's output depends on its own root path only, so a leaf appended to a tree
+    leaves every other node's output as it was (to rounding). The sizes cross the size
+    classes the kernels dispatch on: 32 -> 33 nodes (one-wavefront to row-split body),
+    63 -> 64 (the largest tree), 0 -> 1 (an empty tree gains a node) and 16 -> 17."""
+    sizes = [32, 63, 0, 16]
+    wl = W.make_random(906, batch=len(sizes), heads=3, d_k=128, d_v=64, sizes=sizes,
+                       kind="random", vector_gate=vector_gate)
+    lay = wl.layers[0]
+    rng = np.random.default_rng(7)
+    base = run(bole, lay.H0, lay.q, lay.k, lay.v, lay.gate, wl.parent, wl.node_offsets)
+    ref = W.make_random(907, batch=len(sizes), heads=3, d_k=128, d_v=64, sizes=[1] * len(sizes),
+                        kind="random", vector_gate=vector_gate).layers[0]
+    q, k, v, gate = lay.q, lay.k, lay.v, lay.gate
+    parent, offs = wl.parent.copy(), wl.node_offsets.copy()
+    keep = np.arange(wl.total_nodes)               # new packed row of each old row
+    for b in reversed(range(len(sizes))):          # later trees first: earlier offsets hold
+        hi, n = int(offs[b + 1]), sizes[b]
+        p_leaf = int(rng.integers(-1, n))          # under any node of the tree or the context
+        ins = lambda t, x: torch.cat([t[:hi], x[b:b + 1], t[hi:]])
+        q, k, v, gate = ins(q, ref.q), ins(k, ref.k), ins(v, ref.v), ins(gate, ref.gate)
+        parent = np.concatenate([parent[:hi], [p_leaf], parent[hi:]]).astype(np.int32)
+        offs[b + 1:] += 1
+        keep[keep >= hi] += 1
+    out = run(bole, lay.H0, q, k, v, gate, parent, offs)
+    assert out.shape[0] == wl.total_nodes + len(sizes)
+    assert rel_err_rows(out[torch.from_numpy(keep)].numpy(), base.numpy()) <= 1e-4
