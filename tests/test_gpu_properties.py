@@ -2,9 +2,9 @@
 same properties pin the oracle on the CPU): invariance under a topological relabelling
 of the tree, homogeneity in (H0, v), additivity in H0, a vector gate with equal channels
 against the scalar gate, identical siblings, and a new leaf that leaves every other output
-as it was. Each compares GPU outputs with GPU
-outputs through the C ABI, so a kernel-only mistake that the oracle comparison could
-absorb within its tolerance still has to keep these relations."""
+as it was. Each compares GPU outputs with GPU outputs through the C ABI, so a kernel-only
+mistake that the oracle comparison could absorb within its tolerance still has to keep
+these relations."""
 import numpy as np
 import pytest
 import torch
