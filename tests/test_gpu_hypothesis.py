@@ -178,3 +178,49 @@ def test_drawn_layer_stacks_equal_layer_by_layer(bole, data):
     name = f"drawn_stack_{data.draw(st.integers(0, 10 ** 6), label='name')}"
     print(f"[case] drawn stack {name} layers={n_layers} {kw}", flush=True)
     test_layer_stack_equals_layer_by_layer(bole, name, n_layers, kw)
+
+
+@drawn(15)
+@given(st.data())
+def test_drawn_new_leaves_change_no_other_output(bole, data):
+    """Leaves appended to drawn trees (any tree, under any node or the context) leave every
+    other node's output as it was: within twice the oracle's bar, the bound that both
+    calls meeting that bar implies, whichever size class or path each call takes."""
+    import numpy as np
+
+    from tests.helpers import rel_err_rows
+    from tests.test_gpu_parity import TOL
+    from tests.test_gpu_properties import run
+    B = data.draw(st.integers(1, 5), label="batch")
+    kw = dict(batch=B, heads=data.draw(st.integers(1, 3), label="heads"),
+              d_k=data.draw(st.sampled_from([64, 128]), label="d_k"),
+              d_v=data.draw(st.sampled_from([32, 64, 128]), label="d_v"),
+              vector_gate=data.draw(st.booleans(), label="vector_gate"),
+              factor_dtype=data.draw(st.sampled_from([torch.bfloat16, torch.bfloat16, torch.float32]),
+                                     label="dtype"))
+    sizes = data.draw(st.lists(st.integers(0, 63), min_size=B, max_size=B), label="sizes")
+    grow = data.draw(st.lists(st.booleans(), min_size=B, max_size=B), label="grow")
+    kind = data.draw(st.sampled_from(["random", "chain", "star", "deep", "bestfirst"]), label="kind")
+    seed = data.draw(st.integers(0, 10 ** 6), label="seed")
+    print(f"[case] drawn new leaves sizes={sizes} grow={grow} {kind} {kw} seed={seed}", flush=True)
+    wl = W.make_random(seed, sizes=sizes, kind=kind, **kw)
+    lay = wl.layers[0]
+    ref = W.make_random(seed + 1, sizes=[1] * B, kind="random", **kw).layers[0]
+    base = run(bole, lay.H0, lay.q, lay.k, lay.v, lay.gate, wl.parent, wl.node_offsets)
+    q, k, v, gate = lay.q, lay.k, lay.v, lay.gate
+    parent, offs = wl.parent.copy(), wl.node_offsets.copy()
+    keep = np.arange(wl.total_nodes)               # new packed row of each old row
+    for b in reversed(range(B)):                   # later trees first: earlier offsets hold
+        if not grow[b]:
+            continue
+        hi = int(offs[b + 1])
+        p_leaf = data.draw(st.integers(-1, sizes[b] - 1), label=f"leaf_parent_{b}")
+        ins = lambda t, x: torch.cat([t[:hi], x[b:b + 1], t[hi:]])
+        q, k, v, gate = ins(q, ref.q), ins(k, ref.k), ins(v, ref.v), ins(gate, ref.gate)
+        parent = np.concatenate([parent[:hi], [p_leaf], parent[hi:]]).astype(np.int32)
+        offs[b + 1:] += 1
+        keep[keep >= hi] += 1
+    out = run(bole, lay.H0, q, k, v, gate, parent, offs)
+    assert out.shape[0] == wl.total_nodes + sum(grow)
+    assert rel_err_rows(out[torch.from_numpy(keep)].double().numpy(), base.double().numpy()) \
+        <= 2 * TOL[kw["factor_dtype"]]
