@@ -570,11 +570,14 @@ struct BuildLayout {
     int S, slice_len;
 };
 
-// Slices per row: about 2048 workgroups in all, each slice at least 8192 elements and a
-// multiple of the chunk.
+// Slices per row: about 1024 workgroups in all, each slice at least 8192 elements and a
+// multiple of the chunk. At 64 x 8 rows of 128,256 tokens that is two slices per row, four
+// workgroups per CU, all resident at once: the whole call took 74.3-74.9 us against 80.0
+// with four slices per row (part of that grid ran as a second, partial round), 80.9-81.4
+// with one, and 82-91 with three, five or eight.
 static void slices_for(const bole_build_dims_t &d, int &S, int &slice_len) {
     const int64_t rows = (int64_t)d.batch * d.depth;
-    const int64_t by_grid = rows > 0 ? (2048 + rows - 1) / rows : 1;
+    const int64_t by_grid = rows > 0 ? (1024 + rows - 1) / rows : 1;
     const int64_t by_size = ((int64_t)d.vocab + 8191) / 8192;
     const int64_t want = std::max<int64_t>(1, std::min(by_grid, by_size));
     int64_t len = ((int64_t)d.vocab + want - 1) / want;
